@@ -1,0 +1,11 @@
+"""fp64 CPU oracle for the KLA operator.
+
+TEST INFRASTRUCTURE ONLY: imported by the test-suite, the smoke check and the
+benchmark's CPU-baseline leg, never by the product path.  It shares no code
+with the HIP kernels or their binding.
+"""
+
+from .kla_oracle import kla_decode_step, kla_forward, kla_recurrence
+from .kla_chunk_oracle import kla_chunkwise
+
+__all__ = ["kla_recurrence", "kla_forward", "kla_decode_step", "kla_chunkwise"]
