@@ -1,0 +1,92 @@
+// kla_api.cpp -- the C ABI declared in include/kla.h.
+//
+// Every argument is validated on the host before the first HIP call, so the
+// error paths run (and are tested) on machines without a GPU.  After
+// validation the call only enqueues kernels on the caller's stream.
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/kla.h"
+#include "kla_internal.h"
+
+namespace {
+
+bool misaligned(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+bool bad_eps(float eps) { return !std::isfinite(eps) || eps < 0.f; }
+
+kla_status_t from_hip(hipError_t e) { return e == hipSuccess ? KLA_OK : KLA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int kla_abi_version(void) { return KLA_ABI_VERSION; }
+
+const char *kla_status_str(kla_status_t s) {
+  switch (s) {
+    case KLA_OK: return "ok";
+    case KLA_ERR_NULL: return "a required pointer is NULL";
+    case KLA_ERR_SHAPE: return "invalid or inconsistent sizes";
+    case KLA_ERR_DTYPE: return "unknown dtype";
+    case KLA_ERR_UNSUPPORTED: return "shape/dtype/chunk combination not compiled";
+    case KLA_ERR_SEQLENS: return "cu_seqlens must be non-decreasing from 0 to T";
+    case KLA_ERR_EPS: return "eps must be finite and >= 0";
+    case KLA_ERR_ALIGN: return "data pointers must be 16-byte aligned";
+    case KLA_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+kla_status_t kla_decode_step(const void *q, const void *k, const void *v, const void *g,
+                             const void *eta, float eps, float *state, void *o, int N, int H,
+                             int dk, int dv, kla_dtype_t dtype, void *stream) {
+  if (dtype != KLA_DT_BF16 && dtype != KLA_DT_F32) return KLA_ERR_DTYPE;
+  if (N < 0 || H <= 0 || dk <= 0 || dv <= 0) return KLA_ERR_SHAPE;
+  if (bad_eps(eps)) return KLA_ERR_EPS;
+  if (!kla::decode_supported(dtype, dk, dv)) return KLA_ERR_UNSUPPORTED;
+  if (N == 0) return KLA_OK;
+  if (!q || !k || !v || !g || !eta || !state || !o) return KLA_ERR_NULL;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(g) || misaligned(eta) ||
+      misaligned(state) || misaligned(o))
+    return KLA_ERR_ALIGN;
+  if ((long long)N * H > 0x7fffffffLL) return KLA_ERR_SHAPE;
+  kla::DecodeArgs a{q, k, v, g, eta, eps, state, o, N, H, dk, dv, (int)dtype};
+  return from_hip(kla::launch_decode(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
+kla_status_t kla_chunk_fwd(const void *q, const void *k, const void *v, const void *g,
+                           const void *eta, float eps, const float *initial_state, void *o,
+                           float *final_state, const int32_t *cu_seqlens,
+                           const int32_t *cu_seqlens_host, int num_seqs, int B, int H, int T,
+                           int dk, int dv, int chunk, kla_dtype_t dtype, void *stream) {
+  if (dtype != KLA_DT_BF16 && dtype != KLA_DT_F32) return KLA_ERR_DTYPE;
+  if (B < 0 || H <= 0 || T < 0 || dk <= 0 || dv <= 0 || chunk <= 0 || num_seqs < 0)
+    return KLA_ERR_SHAPE;
+  if (bad_eps(eps)) return KLA_ERR_EPS;
+  if (!kla::chunk_supported(dtype, dk, dv, chunk)) return KLA_ERR_UNSUPPORTED;
+  if (cu_seqlens == nullptr) {
+    if (cu_seqlens_host != nullptr) return KLA_ERR_NULL;
+    if (num_seqs != B) return KLA_ERR_SHAPE;
+  } else {
+    if (cu_seqlens_host == nullptr) return KLA_ERR_NULL;
+    if (B != 1) return KLA_ERR_SHAPE;
+    if (cu_seqlens_host[0] != 0 || cu_seqlens_host[num_seqs] != T) return KLA_ERR_SEQLENS;
+    for (int n = 0; n < num_seqs; ++n)
+      if (cu_seqlens_host[n + 1] < cu_seqlens_host[n]) return KLA_ERR_SEQLENS;
+    if (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) return KLA_ERR_ALIGN;
+  }
+  if ((long long)num_seqs * H * ((dv + 15) / 16) > 0x7fffffffLL) return KLA_ERR_SHAPE;
+  if ((long long)B * H * T > (1LL << 40)) return KLA_ERR_SHAPE;
+  if (num_seqs == 0) return KLA_OK;
+  // token tensors are only dereferenced when there are tokens
+  if ((long long)B * T > 0 && (!q || !k || !v || !g || !eta || !o)) return KLA_ERR_NULL;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(g) || misaligned(eta) ||
+      misaligned(o) || misaligned(initial_state) || misaligned(final_state))
+    return KLA_ERR_ALIGN;
+  kla::ChunkArgs a{q,        k,         v,  g, eta, eps, initial_state, o, final_state,
+                   cu_seqlens, num_seqs, B, H, T, dk,  dv,  chunk,         (int)dtype};
+  return from_hip(kla::launch_chunk_fwd(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

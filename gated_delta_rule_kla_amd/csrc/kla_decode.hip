@@ -1,0 +1,187 @@
+// kla_decode.hip -- single-token KLA decode step for gfx950.
+//
+// One recurrent step per (sequence, head):
+//   alpha = exp(g), beta = eta / (||k||^2 + eps)
+//   y_k = S^T k, y_q = S^T q           (one pass over the old state)
+//   e   = v - alpha y_k
+//   o   = alpha y_q + beta (k.q) e     (= S_new^T q without a second pass)
+//   S   = alpha S + beta k e^T         (written back in place)
+// This is the update of "Resumen Técnico: Atención Lineal Kaczmarz (KLA)"
+// (gist.science/es/paper/2605.08587), §"La Regla de Actualización KLA",
+// with the decayed state alpha S and the readout o = S_new^T q.
+//
+// The step is HBM-bound (0.75 flop per byte): the fp32 state is read once and
+// written once with 16-byte accesses and held in VGPRs in between.  One
+// workgroup owns one (sequence, head) state of DK x DV floats; each thread
+// holds a float4 column slice of RPT rows.  Threads of one row group cover one
+// full row, so each load/store instruction of a wave touches whole contiguous
+// rows.  Partial dot products are reduced across row groups with lane
+// shuffles inside a wave and through LDS across waves.
+#include "kla_common.h"
+#include "kla_internal.h"
+
+namespace kla {
+
+constexpr int decode_threads(int dk, int dv) {
+  return dk * dv / 64 < 64 ? 64 : (dk * dv / 64 > 1024 ? 1024 : dk * dv / 64);
+}
+
+template <int DK, int DV>
+struct DecodeShape {
+  static constexpr int TPR = DV / 4;                        // threads per row
+  static constexpr int NT = decode_threads(DK, DV);         // ~64 state floats per thread
+  static constexpr int RG = NT / TPR;                       // row groups
+  static constexpr int RPT = DK / RG;                       // rows per thread
+  static constexpr int NW = NT / 64;                        // waves
+  static_assert(TPR <= 64 && RG * TPR == NT && RPT * RG == DK, "decode tiling");
+};
+
+template <typename E, int DK, int DV>
+__global__ __launch_bounds__(decode_threads(DK, DV)) void kla_decode_kernel(
+    const E *__restrict__ q, const E *__restrict__ k, const E *__restrict__ v,
+    const E *__restrict__ g, const E *__restrict__ eta, float eps, float *__restrict__ state,
+    E *__restrict__ o) {
+  using Sh = DecodeShape<DK, DV>;
+  constexpr int TPR = Sh::TPR, RG = Sh::RG, RPT = Sh::RPT, NW = Sh::NW;
+  constexpr int NRED = 10;  // y_k[4], y_q[4], k.k, k.q
+
+  __shared__ float s_k[DK];
+  __shared__ float s_q[DK];
+  __shared__ float s_red[NW > 1 ? NW : 1][TPR][NRED];
+
+  const size_t nh = blockIdx.x;
+  const int t = threadIdx.x;
+  const int cg = t % TPR;  // column group: columns 4cg .. 4cg+3
+  const int rg = t / TPR;  // row group: rows rg + RG p
+
+  for (int i = t; i < DK; i += Sh::NT) {
+    s_k[i] = Elem<E>::to_f32(k[nh * DK + i]);
+    s_q[i] = Elem<E>::to_f32(q[nh * DK + i]);
+  }
+
+  float *S = state + nh * (size_t)(DK * DV);
+  f32x4 s[RPT];
+#pragma unroll
+  for (int p = 0; p < RPT; ++p)
+    s[p] = *reinterpret_cast<const f32x4 *>(S + (size_t)(rg + RG * p) * DV + 4 * cg);
+
+  float vv[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) vv[c] = Elem<E>::to_f32(v[nh * DV + 4 * cg + c]);
+  const float alpha = __expf(Elem<E>::to_f32(g[nh]));
+  const float et = Elem<E>::to_f32(eta[nh]);
+
+  __syncthreads();
+
+  float red[NRED];
+#pragma unroll
+  for (int i = 0; i < NRED; ++i) red[i] = 0.f;
+#pragma unroll
+  for (int p = 0; p < RPT; ++p) {
+    const float kr = s_k[rg + RG * p], qr = s_q[rg + RG * p];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      red[c] = fmaf(s[p][c], kr, red[c]);
+      red[4 + c] = fmaf(s[p][c], qr, red[4 + c]);
+    }
+    red[8] = fmaf(kr, kr, red[8]);
+    red[9] = fmaf(kr, qr, red[9]);
+  }
+  // reduce over the row groups inside the wave (lanes TPR apart)
+#pragma unroll
+  for (int off = TPR; off < 64; off <<= 1) {
+#pragma unroll
+    for (int i = 0; i < NRED; ++i) red[i] += __shfl_xor(red[i], off);
+  }
+  if constexpr (NW > 1) {
+    const int lane = t & 63, w = t >> 6;
+    if (lane < TPR) {
+#pragma unroll
+      for (int i = 0; i < NRED; ++i) s_red[w][lane][i] = red[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < NRED; ++i) {
+      float acc = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) acc += s_red[ww][cg][i];
+      red[i] = acc;
+    }
+  }
+
+  const float beta = et / (red[8] + eps);
+  const float bkq = beta * red[9];
+  float e[4], oo[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    e[c] = vv[c] - alpha * red[c];
+    oo[c] = alpha * red[4 + c] + bkq * e[c];
+  }
+#pragma unroll
+  for (int p = 0; p < RPT; ++p) {
+    const float bk = beta * s_k[rg + RG * p];
+    f32x4 n;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) n[c] = fmaf(alpha, s[p][c], bk * e[c]);
+    *reinterpret_cast<f32x4 *>(S + (size_t)(rg + RG * p) * DV + 4 * cg) = n;
+  }
+  if (rg == 0) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) o[nh * DV + 4 * cg + c] = Elem<E>::from_f32(oo[c]);
+  }
+}
+
+template <typename E, int DK, int DV>
+static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t st) {
+  const unsigned nblk = (unsigned)((size_t)a.N * a.H);
+  hipLaunchKernelGGL((kla_decode_kernel<E, DK, DV>), dim3(nblk), dim3(DecodeShape<DK, DV>::NT), 0,
+                     st, (const E *)a.q, (const E *)a.k, (const E *)a.v, (const E *)a.g,
+                     (const E *)a.eta, a.eps, a.state, (E *)a.o);
+  return hipGetLastError();
+}
+
+static int dim_index(int d) {
+  switch (d) {
+    case 16: return 0;
+    case 32: return 1;
+    case 64: return 2;
+    case 128: return 3;
+    case 256: return 4;
+    default: return -1;
+  }
+}
+
+bool decode_supported(int dtype, int dk, int dv) {
+  return (dtype == 0 || dtype == 1) && dim_index(dk) >= 0 && dim_index(dv) >= 0;
+}
+
+template <typename E, int DK>
+static hipError_t dispatch_dv(const DecodeArgs &a, hipStream_t st) {
+  switch (a.dv) {
+    case 16: return launch_decode_t<E, DK, 16>(a, st);
+    case 32: return launch_decode_t<E, DK, 32>(a, st);
+    case 64: return launch_decode_t<E, DK, 64>(a, st);
+    case 128: return launch_decode_t<E, DK, 128>(a, st);
+    case 256: return launch_decode_t<E, DK, 256>(a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename E>
+static hipError_t dispatch_dk(const DecodeArgs &a, hipStream_t st) {
+  switch (a.dk) {
+    case 16: return dispatch_dv<E, 16>(a, st);
+    case 32: return dispatch_dv<E, 32>(a, st);
+    case 64: return dispatch_dv<E, 64>(a, st);
+    case 128: return dispatch_dv<E, 128>(a, st);
+    case 256: return dispatch_dv<E, 256>(a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t st) {
+  if (a.dtype == 0) return dispatch_dk<bf16>(a, st);
+  return dispatch_dk<float>(a, st);
+}
+
+}  // namespace kla

@@ -1,0 +1,193 @@
+"""Thin ctypes binding over libkla.so (include/kla.h).
+
+Argument marshalling only: shape/dtype checks, output allocation with torch
+and the current HIP stream.  Every step of the operator runs in the HIP
+kernels; there is no fallback.  If libkla.so is missing the call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = ["chunk_fwd", "decode_step", "lib", "lib_path", "KlaError",
+           "KLA_DT_BF16", "KLA_DT_F32"]
+
+KLA_DT_BF16 = 0
+KLA_DT_F32 = 1
+_DTYPES = {torch.bfloat16: KLA_DT_BF16, torch.float32: KLA_DT_F32}
+
+_LIB: Optional[ctypes.CDLL] = None
+
+
+def lib_path() -> str:
+    return os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkla.so")
+
+
+class KlaError(RuntimeError):
+    """A negative kla_status_t returned by the library."""
+
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed: {msg} (status {status})")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libkla.so once.  torch is imported first so that the library binds
+    to the HIP runtime torch already mapped (same soname)."""
+    global _LIB
+    if _LIB is None:
+        path = lib_path()
+        if not os.path.exists(path):
+            raise RuntimeError(
+                f"{path} is not built: run `python -c 'import __graft_entry__ as g; g.build()'` "
+                "(or python gated_delta_rule_kla_amd/build.py)")
+        L = ctypes.CDLL(path)
+        vp, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+        L.kla_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, f32, vp, vp, vp, vp, vp,
+                                    i32, i32, i32, i32, i32, i32, i32, i32, vp]
+        L.kla_chunk_fwd.restype = i32
+        L.kla_decode_step.argtypes = [vp, vp, vp, vp, vp, f32, vp, vp,
+                                      i32, i32, i32, i32, i32, vp]
+        L.kla_decode_step.restype = i32
+        L.kla_status_str.argtypes = [i32]
+        L.kla_status_str.restype = ctypes.c_char_p
+        L.kla_abi_version.argtypes = []
+        L.kla_abi_version.restype = i32
+        _LIB = L
+    return _LIB
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise KlaError(fn, status, lib().kla_status_str(status).decode())
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, shape, device) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def chunk_fwd(
+    q: torch.Tensor,
+    k: torch.Tensor,
+    v: torch.Tensor,
+    g: torch.Tensor,
+    eta: torch.Tensor,
+    eps: float = 1e-6,
+    initial_state: Optional[torch.Tensor] = None,
+    cu_seqlens: Optional[torch.Tensor] = None,
+    chunk: int = 64,
+    output_final_state: bool = True,
+    cu_seqlens_host: Optional[torch.Tensor] = None,
+    out: Optional[torch.Tensor] = None,
+    final_state: Optional[torch.Tensor] = None,
+) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """KLA chunkwise prefill (kla_chunk_fwd).
+
+    q, k: [B, H, T, dk]; v: [B, H, T, dv]; g, eta: [B, H, T]; all bf16 or all
+    fp32 on one GPU.  initial_state: [N, H, dk, dv] fp32 or None.  cu_seqlens:
+    int32 [N + 1] on the GPU (B must be 1) or None.  Returns (o, final_state).
+    ``final_state`` may be passed as the same tensor as ``initial_state`` to
+    update it in place.
+    """
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("kla.chunk_fwd needs GPU tensors")
+    dtype = q.dtype
+    if dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {dtype}")
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    _need(q, "q", dtype, (B, H, T, dk), dev)
+    _need(k, "k", dtype, (B, H, T, dk), dev)
+    _need(v, "v", dtype, (B, H, T, dv), dev)
+    _need(g, "g", dtype, (B, H, T), dev)
+    _need(eta, "eta", dtype, (B, H, T), dev)
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, (cu_seqlens.numel(),), dev)
+        if cu_seqlens_host is None:
+            cu_seqlens_host = cu_seqlens.cpu()
+        cu_seqlens_host = cu_seqlens_host.to(torch.int32).contiguous()
+        if cu_seqlens_host.numel() != cu_seqlens.numel():
+            raise ValueError("cu_seqlens_host does not mirror cu_seqlens")
+        N = cu_seqlens.numel() - 1
+    else:
+        N = B
+    if initial_state is not None:
+        _need(initial_state, "initial_state", torch.float32, (N, H, dk, dv), dev)
+    if out is None:
+        out = torch.empty((B, H, T, dv), dtype=dtype, device=dev)
+    else:
+        _need(out, "out", dtype, (B, H, T, dv), dev)
+    if output_final_state and final_state is None:
+        final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    if final_state is not None:
+        _need(final_state, "final_state", torch.float32, (N, H, dk, dv), dev)
+    host_ptr = None if cu_seqlens_host is None else cu_seqlens_host.data_ptr()
+    st = lib().kla_chunk_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(eta), float(eps),
+        _ptr(initial_state), _ptr(out), _ptr(final_state),
+        _ptr(cu_seqlens), host_ptr, N, B, H, T, dk, dv, int(chunk), _DTYPES[dtype],
+        _stream(dev))
+    _check("kla_chunk_fwd", st)
+    return out, final_state
+
+
+def decode_step(
+    q: torch.Tensor,
+    k: torch.Tensor,
+    v: torch.Tensor,
+    g: torch.Tensor,
+    eta: torch.Tensor,
+    eps: float,
+    state: torch.Tensor,
+    out: Optional[torch.Tensor] = None,
+) -> torch.Tensor:
+    """One KLA recurrent step (kla_decode_step); ``state`` is updated in place.
+
+    q, k: [N, H, dk]; v: [N, H, dv]; g, eta: [N, H]; state: [N, H, dk, dv] fp32.
+    Returns o [N, H, dv].
+    """
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("kla.decode_step needs GPU tensors")
+    dtype = q.dtype
+    if dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {dtype}")
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    _need(q, "q", dtype, (N, H, dk), dev)
+    _need(k, "k", dtype, (N, H, dk), dev)
+    _need(v, "v", dtype, (N, H, dv), dev)
+    _need(g, "g", dtype, (N, H), dev)
+    _need(eta, "eta", dtype, (N, H), dev)
+    _need(state, "state", torch.float32, (N, H, dk, dv), dev)
+    if out is None:
+        out = torch.empty((N, H, dv), dtype=dtype, device=dev)
+    else:
+        _need(out, "out", dtype, (N, H, dv), dev)
+    st = lib().kla_decode_step(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(eta), float(eps), _ptr(state), _ptr(out),
+        N, H, dk, dv, _DTYPES[dtype], _stream(dev))
+    _check("kla_decode_step", st)
+    return out

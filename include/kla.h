@@ -1,0 +1,145 @@
+/*
+ * kla.h -- C ABI of the MI355X (gfx950) Kaczmarz Linear Attention operator.
+ *
+ * The operator.  Per sequence and head, with q_t, k_t in R^dk, v_t in R^dv and
+ * state S_t in R^{dk x dv}:
+ *
+ *     alpha_t = exp(g_t)                           (g = log-decay, g <= 0)
+ *     beta_t  = eta_t / (||k_t||_2^2 + eps)         Kaczmarz step
+ *     e_t     = v_t - (alpha_t S_{t-1})^T k_t       residual against the decayed state
+ *     S_t     = alpha_t S_{t-1} + beta_t k_t e_t^T
+ *     o_t     = S_t^T q_t
+ *
+ * Source: "Resumen Técnico: Atención Lineal Kaczmarz (KLA)",
+ * gist.science/es/paper/2605.08587 -- §"Derivación Teórica" (the write is the
+ * projection of the decayed state onto {S : S^T k_t = v_t}), §"La Regla de
+ * Actualización KLA" (beta_t and the update), §"Implementación" (state shape
+ * dk x dv; the gates and the chunkwise block solver of Gated DeltaNet are kept,
+ * only B = Diag(beta) changes).  The decay form exp(g_t) and the readout
+ * o_t = S_t^T q_t (post-update state, no 1/sqrt(dk) scale) are the plainest
+ * reading of the pages, which only name "decay gates" and the recurrent state.
+ *
+ * Conventions common to every entry point
+ *   - Every data pointer is DEVICE memory (allocated by the caller, e.g. with
+ *     PyTorch) unless its comment says "host".  The library allocates no
+ *     device memory and keeps no state between calls.
+ *   - Tensors are dense and contiguous, row-major, in the layouts stated per
+ *     argument.  All data pointers must be 16-byte aligned (cu_seqlens:
+ *     4-byte).
+ *   - q, k, v, g, eta and o share one element type (kla_dtype_t); states are
+ *     always fp32.  Accumulation is fp32.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Calls only enqueue work and return; kernel faults surface at the
+ *     caller's next synchronisation.  Calls on different streams are
+ *     independent and thread-safe.
+ *   - Errors: a negative kla_status_t.  All argument validation is done on
+ *     the host BEFORE any HIP call, so it also runs on a machine without a
+ *     GPU; a failing HIP launch returns KLA_ERR_HIP.  Nothing is printed and
+ *     no exception crosses the ABI.  On error nothing has been enqueued.
+ */
+#ifndef KLA_H
+#define KLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KLA_DT_BF16 = 0, /* bfloat16 inputs/outputs: the production path, bf16 MFMA   */
+    KLA_DT_F32 = 1   /* fp32 inputs/outputs: the debug build, fp32 MFMA           */
+} kla_dtype_t;
+
+typedef enum {
+    KLA_OK = 0,
+    KLA_ERR_NULL = -1,        /* a required pointer is NULL                      */
+    KLA_ERR_SHAPE = -2,       /* a size is negative/zero or inconsistent         */
+    KLA_ERR_DTYPE = -3,       /* unknown kla_dtype_t                             */
+    KLA_ERR_UNSUPPORTED = -4, /* valid but not compiled: see supported shapes    */
+    KLA_ERR_SEQLENS = -5,     /* cu_seqlens not 0 = c0 <= c1 <= ... <= cN = T    */
+    KLA_ERR_EPS = -6,         /* eps < 0, NaN or infinite                        */
+    KLA_ERR_ALIGN = -8,       /* a data pointer is not 16-byte aligned           */
+    KLA_ERR_HIP = -9          /* the HIP runtime rejected a launch               */
+} kla_status_t;
+
+/*
+ * kla_chunk_fwd -- chunkwise-parallel prefill (the block solver).
+ *
+ * Computes o_t for every token and the final state of every sequence, using
+ * per chunk of `chunk` tokens: B = Diag(beta), the unit-lower-triangular solve
+ * T = (I + strictly-lower(B K K^T, decay-weighted))^-1, T applied to the chunk,
+ * a sequential scan of the state over chunks, and the causal intra-chunk
+ * output (§"Implementación" above: the block solver with only B changed).
+ * The result equals the token recurrence up to rounding and does not depend
+ * on `chunk`.
+ *
+ *   q, k      [B, H, T, dk]  dtype
+ *   v         [B, H, T, dv]  dtype
+ *   g, eta    [B, H, T]      dtype; g is the log-decay (alpha = exp(g)),
+ *                            eta the relaxation gate (used as given)
+ *   eps       fp32 scalar >= 0 (finite)
+ *   initial_state  [N, H, dk, dv] fp32 (dv contiguous), or NULL = zeros
+ *   o         [B, H, T, dv]  dtype, written for every token
+ *   final_state    [N, H, dk, dv] fp32, or NULL = not written.  May alias
+ *                  initial_state (each tile is read before it is written);
+ *                  no other aliasing is allowed.
+ *   cu_seqlens     device int32 [N + 1] or NULL.  NULL: N = B and batch row b
+ *                  is sequence b.  Otherwise B must be 1 and sequence n is
+ *                  tokens [cu[n], cu[n+1]) of that row (packed varlen);
+ *                  empty sequences are allowed (their final state = initial).
+ *   cu_seqlens_host  host mirror of cu_seqlens (required iff cu_seqlens is
+ *                  given): validated here.  The kernels also clamp every range
+ *                  to [0, T], so a device array that disagrees with the mirror
+ *                  cannot cause an out-of-bounds access.
+ *   num_seqs  N (must equal B when cu_seqlens is NULL)
+ *
+ * Supported: dtype BF16 with chunk 64, dk 128, dv a multiple of 32 in
+ * [32, 256]; dtype F32 with chunk 16 and dk in {16, 32, 64, 128}, or chunk 64
+ * and dk in {16, 32}, dv a multiple of 16 in [16, 256].  Anything else returns
+ * KLA_ERR_UNSUPPORTED.
+ */
+kla_status_t kla_chunk_fwd(const void *q, const void *k, const void *v,
+                           const void *g, const void *eta, float eps,
+                           const float *initial_state, void *o, float *final_state,
+                           const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
+                           int num_seqs, int B, int H, int T, int dk, int dv, int chunk,
+                           kla_dtype_t dtype, void *stream);
+
+/*
+ * kla_decode_step -- one recurrent step for N sequences x H heads.
+ *
+ * The token update of §"La Regla de Actualización KLA" applied once per
+ * (sequence, head); the state is read once from HBM and written once, and
+ * o = S_new^T q is formed from the same pass as alpha S_old^T q +
+ * beta (k.q) e.
+ *
+ *   q, k    [N, H, dk]  dtype
+ *   v       [N, H, dv]  dtype
+ *   g, eta  [N, H]      dtype
+ *   eps     fp32 scalar >= 0 (finite)
+ *   state   [N, H, dk, dv] fp32, updated IN PLACE
+ *   o       [N, H, dv]  dtype
+ *
+ * Supported: dk, dv in {16, 32, 64, 128, 256}, either dtype.
+ */
+kla_status_t kla_decode_step(const void *q, const void *k, const void *v,
+                             const void *g, const void *eta, float eps,
+                             float *state, void *o,
+                             int N, int H, int dk, int dv,
+                             kla_dtype_t dtype, void *stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char *kla_status_str(kla_status_t s);
+
+/* ABI version of this header (incremented on any incompatible change). */
+int kla_abi_version(void);
+
+#define KLA_ABI_VERSION 1
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KLA_H */

@@ -1,0 +1,131 @@
+"""The C ABI on a host without a GPU: it loads, exports every symbol the header
+declares, and rejects bad arguments with the documented status codes before
+any HIP call (no compute call is made here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from gated_delta_rule_kla_amd import kla
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kla.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(kla.lib_path()),
+                                reason="libkla.so not built (run __graft_entry__.build())")
+
+OK, E_NULL, E_SHAPE, E_DTYPE, E_UNSUP, E_SEQ, E_EPS, E_ALIGN, E_HIP = 0, -1, -2, -3, -4, -5, -6, -8, -9
+FAKE = 0x7F0000000000  # never dereferenced: every case below fails validation first
+
+
+def _declared():
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(kla_[a-z_0-9]+)\s*\(", txt)))
+
+
+def test_exports_every_declared_symbol():
+    L = kla.lib()
+    names = _declared()
+    assert set(names) >= {"kla_chunk_fwd", "kla_decode_step", "kla_status_str", "kla_abi_version"}
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_abi_version_matches_header():
+    v = int(re.search(r"#define KLA_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
+    assert kla.lib().kla_abi_version() == v
+
+
+def test_status_strings():
+    L = kla.lib()
+    for s in (OK, E_NULL, E_SHAPE, E_DTYPE, E_UNSUP, E_SEQ, E_EPS, E_ALIGN, E_HIP, -77):
+        txt = L.kla_status_str(s)
+        assert isinstance(txt, bytes) and len(txt) > 0
+
+
+def _chunk(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, eta=FAKE, eps=1e-6, s0=None, o=FAKE, sf=FAKE,
+             cu=None, cuh=None, N=2, B=2, H=4, T=100, dk=128, dv=128, chunk=64, dtype=0)
+    a.update(kw)
+    return kla.lib().kla_chunk_fwd(a["q"], a["k"], a["v"], a["g"], a["eta"], a["eps"], a["s0"],
+                                   a["o"], a["sf"], a["cu"], a["cuh"], a["N"], a["B"], a["H"],
+                                   a["T"], a["dk"], a["dv"], a["chunk"], a["dtype"], None)
+
+
+def _decode(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, eta=FAKE, eps=1e-6, S=FAKE, o=FAKE,
+             N=3, H=2, dk=128, dv=128, dtype=0)
+    a.update(kw)
+    return kla.lib().kla_decode_step(a["q"], a["k"], a["v"], a["g"], a["eta"], a["eps"], a["S"],
+                                     a["o"], a["N"], a["H"], a["dk"], a["dv"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=7), E_DTYPE),
+    (dict(H=0), E_SHAPE),
+    (dict(T=-1), E_SHAPE),
+    (dict(N=3), E_SHAPE),                        # N must equal B without cu_seqlens
+    (dict(eps=-1.0), E_EPS),
+    (dict(eps=float("nan")), E_EPS),
+    (dict(eps=float("inf")), E_EPS),
+    (dict(dk=96), E_UNSUP),
+    (dict(dv=24), E_UNSUP),
+    (dict(chunk=32), E_UNSUP),
+    (dict(dtype=1, chunk=64, dk=128), E_UNSUP),  # fp32 debug build: chunk 64 needs dk <= 32
+    (dict(q=None), E_NULL),
+    (dict(o=None), E_NULL),
+    (dict(k=FAKE + 8), E_ALIGN),
+    (dict(sf=FAKE + 4), E_ALIGN),
+    (dict(cu=FAKE), E_NULL),                     # device cu_seqlens without the host mirror
+])
+def test_chunk_fwd_rejects(kw, code):
+    assert _chunk(**kw) == code
+
+
+def test_chunk_fwd_seqlens_validation():
+    def host(vals):
+        arr = (ctypes.c_int32 * len(vals))(*vals)
+        return arr, ctypes.addressof(arr)
+    keep, h = host([0, 30, 20, 100])             # decreasing
+    assert _chunk(cu=FAKE, cuh=h, N=3, B=1) == E_SEQ
+    keep, h = host([0, 30, 60, 90])              # does not end at T = 100
+    assert _chunk(cu=FAKE, cuh=h, N=3, B=1) == E_SEQ
+    keep, h = host([5, 30, 60, 100])             # does not start at 0
+    assert _chunk(cu=FAKE, cuh=h, N=3, B=1) == E_SEQ
+    keep, h = host([0, 30, 60, 100])
+    assert _chunk(cu=FAKE, cuh=h, N=3, B=2) == E_SHAPE   # varlen needs B == 1
+    assert _chunk(cu=FAKE + 2, cuh=h, N=3, B=1) == E_ALIGN
+
+
+def test_chunk_fwd_nothing_to_do():
+    # zero sequences: valid, returns without touching the GPU
+    assert _chunk(N=0, B=0) == OK
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=2), E_DTYPE),
+    (dict(H=0), E_SHAPE),
+    (dict(N=-1), E_SHAPE),
+    (dict(eps=-0.5), E_EPS),
+    (dict(dk=48), E_UNSUP),
+    (dict(dv=512), E_UNSUP),
+    (dict(S=None), E_NULL),
+    (dict(v=FAKE + 2), E_ALIGN),
+])
+def test_decode_rejects(kw, code):
+    assert _decode(**kw) == code
+
+
+def test_decode_zero_sequences_is_noop():
+    assert _decode(N=0) == OK
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 1, 4, 16)
+    with pytest.raises(ValueError):
+        kla.chunk_fwd(x, x, x, x[..., 0], x[..., 0])
+    with pytest.raises(ValueError):
+        kla.decode_step(x[0], x[0], x[0], x[0, :, 0], x[0, :, 0], 1e-6, x)

@@ -1,0 +1,236 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Criterion (per output tensor): max|gpu - ref| / max|ref| <= 2e-2 for bf16
+inputs with fp32 accumulation, <= 1e-4 for the fp32 debug build.  Small cases
+span several chunks and a ragged tail and are compared element by element;
+the full-size workloads (the launch configuration the benchmark times) are
+compared on sampled heads, which the oracle computes on their own.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from gated_delta_rule_kla_amd import inputs, kla
+from oracle import kla_decode_step, kla_forward
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+DEV = torch.device("cuda:0")
+TOL = {torch.bfloat16: 2e-2, torch.float32: 1e-4}
+f = inputs.to_f64
+
+
+def rel_err(got, ref):
+    got, ref = np.asarray(got, dtype=np.float64), np.asarray(ref, dtype=np.float64)
+    assert np.isfinite(got).all(), "non-finite GPU output"
+    return float(np.abs(got - ref).max() / np.abs(ref).max())
+
+
+def run_prefill(x, final_alias=False, chunk=None):
+    s0 = None if x.initial_state is None else x.initial_state.to(DEV)
+    cu = None if x.cu_seqlens is None else x.cu_seqlens.to(DEV)
+    fs = s0 if final_alias else None
+    o, S = kla.chunk_fwd(x.q.to(DEV), x.k.to(DEV), x.v.to(DEV), x.g.to(DEV), x.eta.to(DEV),
+                         x.eps, s0, cu, chunk=chunk or x.chunk, cu_seqlens_host=x.cu_seqlens,
+                         final_state=fs)
+    torch.cuda.synchronize()
+    return o.cpu(), S.cpu()
+
+
+def oracle_prefill(x, heads=None):
+    cu = None if x.cu_seqlens is None else x.cu_seqlens.tolist()
+    return kla_forward(f(x.q), f(x.k), f(x.v), f(x.g), f(x.eta), x.eps,
+                       f(x.initial_state), cu_seqlens=cu, heads=heads)
+
+
+def check_prefill(x, **kw):
+    o, S = run_prefill(x, **kw)
+    o_r, S_r = oracle_prefill(x)
+    tol = TOL[x.q.dtype]
+    eo, es = rel_err(f(o), o_r), rel_err(f(S), S_r)
+    print(f"{x.name}: err_o={eo:.3e} err_S={es:.3e} tol={tol}")
+    assert eo <= tol and es <= tol, (eo, es)
+    return o, S
+
+
+# ---------------------------------------------------------------- decode ----
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("dk,dv", [(128, 128), (16, 16), (64, 256), (256, 32), (32, 16)])
+def test_decode_small(dtype, dk, dv):
+    d = inputs.make_decode(N=3, H=2, dk=dk, dv=dv, steps=4, dtype=dtype, seed=dk + dv)
+    st = d.state.to(DEV)
+    S_r = f(d.state)
+    for s in range(4):
+        o = kla.decode_step(d.q[s].to(DEV), d.k[s].to(DEV), d.v[s].to(DEV), d.g[s].to(DEV),
+                            d.eta[s].to(DEV), d.eps, st)
+        o_r, S_r = kla_decode_step(f(d.q[s]), f(d.k[s]), f(d.v[s]), f(d.g[s]), f(d.eta[s]), d.eps, S_r)
+        assert rel_err(f(o), o_r) <= TOL[dtype]
+    torch.cuda.synchronize()
+    assert rel_err(f(st), S_r) <= TOL[dtype]
+
+
+# --------------------------------------------------------------- prefill ----
+
+def test_prefill_tiny_fp32_workload():
+    """The tiny fp32 workload: B=1 H=1 T=256 dk=dv=16 chunk 16, to 1e-4."""
+    check_prefill(inputs.prefill_config(0))
+
+
+@pytest.mark.parametrize("dk,dv,T", [(32, 48, 333), (16, 16, 64), (32, 32, 1)])
+def test_prefill_fp32_chunk64(dk, dv, T):
+    x = inputs.make_prefill(B=2, H=2, T=T, dk=dk, dv=dv, chunk=64, dtype=torch.float32,
+                            s0_std=0.3, seed=T, name=f"fp32-c64-{dk}x{dv}-T{T}")
+    check_prefill(x)
+
+
+@pytest.mark.parametrize("dk", [16, 64, 128])
+def test_prefill_fp32_chunk16(dk):
+    x = inputs.make_prefill(B=1, H=3, T=100, dk=dk, dv=32, chunk=16, dtype=torch.float32,
+                            s0_std=0.1, seed=dk, name=f"fp32-c16-dk{dk}")
+    check_prefill(x)
+
+
+def test_prefill_chunk_size_invariance_fp32():
+    x = inputs.make_prefill(B=1, H=2, T=150, dk=32, dv=32, chunk=64, dtype=torch.float32,
+                            s0_std=0.1, seed=5, name="inv")
+    o64, S64 = run_prefill(x, chunk=64)
+    o16, S16 = run_prefill(x, chunk=16)
+    assert rel_err(f(o16), f(o64)) <= 1e-4 and rel_err(f(S16), f(S64)) <= 1e-4
+
+
+@pytest.mark.parametrize("B,H,T,dk,dv", [
+    (1, 2, 300, 128, 128),     # one scan wave per workgroup, ragged tail
+    (4, 16, 200, 128, 128),    # 256 workgroups -> two scan waves per workgroup
+    (1, 2, 273, 128, 256),     # wide values
+    (2, 2, 129, 64, 64),       # dk 64
+    (1, 1, 64, 128, 32),       # exactly one chunk
+    (1, 1, 7, 128, 128),       # shorter than one chunk
+])
+def test_prefill_bf16(B, H, T, dk, dv):
+    x = inputs.make_prefill(B=B, H=H, T=T, dk=dk, dv=dv, chunk=64, s0_std=0.02, seed=B * H + T,
+                            name=f"bf16-{B}x{H}x{T}-{dk}x{dv}")
+    check_prefill(x)
+
+
+def test_prefill_bf16_heavy_tailed_keys_slow_decay():
+    """The long-context regime: key scale exp(N(0,1)), g = -0.1 softplus, eta ~ sigmoid(N(1,1))."""
+    x = inputs.make_prefill(B=1, H=2, T=1000, dk=128, dv=128, chunk=64, sigma_k=1.0,
+                            g_scale=0.1, eta_mu=1.0, seed=11, name="heavy")
+    check_prefill(x)
+
+
+def test_prefill_varlen_with_empty_and_tiny_sequences():
+    x = inputs.make_prefill(H=3, dk=128, dv=128, chunk=64, s0_std=0.02,
+                            lengths=[0, 1, 63, 64, 65, 200, 17, 0], seed=12, name="varlen")
+    check_prefill(x)
+
+
+def test_prefill_no_initial_state_and_no_tokens():
+    x = inputs.make_prefill(H=2, dk=128, dv=64, chunk=64, lengths=[0, 0], seed=13, name="empty")
+    o, S = run_prefill(x)
+    assert o.numel() == 0 and torch.count_nonzero(S) == 0
+
+
+def test_prefill_final_state_aliases_initial_state():
+    x = inputs.make_prefill(B=2, H=2, T=150, dk=128, dv=128, chunk=64, s0_std=0.05, seed=14,
+                            name="alias")
+    o, S = run_prefill(x, final_alias=True)
+    o_r, S_r = oracle_prefill(x)
+    assert rel_err(f(o), o_r) <= 2e-2 and rel_err(f(S), S_r) <= 2e-2
+
+
+def test_prefill_deterministic():
+    x = inputs.make_prefill(B=1, H=4, T=257, dk=128, dv=128, chunk=64, seed=15)
+    o1, S1 = run_prefill(x)
+    o2, S2 = run_prefill(x)
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+def test_prefill_then_decode_continues_the_sequence():
+    x = inputs.make_prefill(B=2, H=2, T=140, dk=128, dv=128, chunk=64, seed=16)
+    head = inputs.PrefillInputs(x.q[:, :, :130].contiguous(), x.k[:, :, :130].contiguous(),
+                                x.v[:, :, :130].contiguous(), x.g[:, :, :130].contiguous(),
+                                x.eta[:, :, :130].contiguous(), x.eps, None, None, 64)
+    _, S = run_prefill(head)
+    st = S.to(DEV)
+    outs = []
+    for t in range(130, 140):
+        outs.append(kla.decode_step(x.q[:, :, t].contiguous().to(DEV), x.k[:, :, t].contiguous().to(DEV),
+                                    x.v[:, :, t].contiguous().to(DEV), x.g[:, :, t].contiguous().to(DEV),
+                                    x.eta[:, :, t].contiguous().to(DEV), x.eps, st).cpu())
+    torch.cuda.synchronize()
+    o_r, S_r = oracle_prefill(x)
+    assert rel_err(f(torch.stack(outs, 2)), o_r[:, :, 130:]) <= 2e-2
+    assert rel_err(f(st), S_r) <= 2e-2
+
+
+# ------------------------------------------- full-size workloads, sampled ----
+
+def _sampled(x, o, S, pairs, dv_cols=None):
+    """Compare (sequence n, head h) pairs against the oracle run on just them."""
+    worst_o = worst_s = 0.0
+    cu = None if x.cu_seqlens is None else x.cu_seqlens.tolist()
+    for n, h in pairs:
+        if cu is None:
+            b, t0, t1 = n, 0, x.q.shape[2]
+        else:
+            b, t0, t1 = 0, cu[n], cu[n + 1]
+        cols = slice(None) if dv_cols is None else dv_cols
+        s0 = None if x.initial_state is None else f(x.initial_state[n:n + 1, h:h + 1, :, cols])
+        o_r, S_r = kla_forward(f(x.q[b:b + 1, h:h + 1, t0:t1]), f(x.k[b:b + 1, h:h + 1, t0:t1]),
+                               f(x.v[b:b + 1, h:h + 1, t0:t1, cols]), f(x.g[b:b + 1, h:h + 1, t0:t1]),
+                               f(x.eta[b:b + 1, h:h + 1, t0:t1]), x.eps, s0)
+        worst_o = max(worst_o, rel_err(f(o[b, h, t0:t1, cols]), o_r[0, 0]))
+        worst_s = max(worst_s, rel_err(f(S[n, h, :, cols]), S_r[0, 0]))
+    print(f"{x.name}: sampled err_o={worst_o:.3e} err_S={worst_s:.3e}")
+    assert worst_o <= 2e-2 and worst_s <= 2e-2, (worst_o, worst_s)
+
+
+def test_full_prefill_workload_b4_h16_t4096():
+    x = inputs.prefill_config(1)
+    o, S = run_prefill(x)
+    _sampled(x, o, S, [(0, 0), (3, 15), (1, 7)])
+
+
+def test_full_long_context_workload_t65536_dv256():
+    x = inputs.prefill_config(2)
+    o, S = run_prefill(x)
+    # columns are independent, so the oracle may run on a slice of them
+    _sampled(x, o, S, [(0, 0), (0, 9)], dv_cols=slice(96, 128))
+    assert np.isfinite(f(S)).all()
+
+
+def test_full_varlen_workload_32_sequences_h32():
+    x = inputs.prefill_config(4)
+    o, S = run_prefill(x)
+    L = np.diff(x.cu_seqlens.numpy())
+    longest, shortest = int(np.argmax(L)), int(np.argmin(L))
+    _sampled(x, o, S, [(longest, 0), (shortest, 31), (5, 17)])
+
+
+def test_full_decode_workload_256x16_512_steps():
+    d = inputs.decode_config()
+    pairs = [(0, 0), (255, 15), (100, 3)]
+    st = d.state.to(DEV)
+    q, k, v, g, eta = (t.to(DEV) for t in (d.q, d.k, d.v, d.g, d.eta))
+    outs = []
+    for s in range(d.q.shape[0]):
+        o = kla.decode_step(q[s], k[s], v[s], g[s], eta[s], d.eps, st)
+        outs.append(torch.stack([o[n, h] for n, h in pairs]))
+    torch.cuda.synchronize()
+    outs = f(torch.stack(outs).cpu())  # [steps, pairs, dv]
+    for i, (n, h) in enumerate(pairs):
+        S_r = f(d.state[n:n + 1, h:h + 1])
+        o_all = []
+        for s in range(d.q.shape[0]):
+            o_r, S_r = kla_decode_step(f(d.q[s, n:n + 1, h:h + 1]), f(d.k[s, n:n + 1, h:h + 1]),
+                                       f(d.v[s, n:n + 1, h:h + 1]), f(d.g[s, n:n + 1, h:h + 1]),
+                                       f(d.eta[s, n:n + 1, h:h + 1]), d.eps, S_r)
+            o_all.append(o_r[0, 0])
+        eo = rel_err(outs[:, i], np.stack(o_all))
+        es = rel_err(f(st[n, h].cpu()), S_r[0, 0])
+        print(f"decode ({n},{h}): err_o={eo:.3e} err_S={es:.3e}")
+        assert eo <= 2e-2 and es <= 2e-2
