@@ -33,17 +33,17 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published (no sparsity)
 
 
-def prefill_algorithmic(B, H, T, dk, dv, C, n_states_read, n_states_written):
+def prefill_algorithmic(B, H, T, dk, dv, C, n_states_read, n_states_written, N):
     """Fixed-formula work of one prefill call (independent of the implementation).
 
     flops per token-head: 2C(3dk + 2dv) + 6 dk dv  (dense chunk form: K K^T,
       Q K^T, T applied to the chunk, K S, Q S, P U~, K^T U~)
     bytes per token-head: q, k, v, g, eta read and o written once (bf16),
-      plus 4 dk dv per state read or written.
+      plus 4 dk dv per state read or written (N sequences x H heads).
     """
     th = B * H * T
     flops = th * (2 * C * (3 * dk + 2 * dv) + 6 * dk * dv)
-    byts = th * (2 * (2 * dk + dv) + 2 * 2 + 2 * dv) + 4 * dk * dv * H * (n_states_read + n_states_written)
+    byts = th * (2 * (2 * dk + dv) + 2 * 2 + 2 * dv) + 4 * dk * dv * N * H * (n_states_read + n_states_written)
     return flops, byts
 
 
@@ -51,6 +51,24 @@ def decode_algorithmic(N, H, dk, dv):
     """Bytes of one decode step: state read + written (fp32), q/k/v/g/eta read, o written (bf16)."""
     per_head = 8 * dk * dv + 2 * (2 * dk + dv) + 2 * 2 + 2 * dv
     return N * H * per_head, N * H * 6 * dk * dv
+
+
+def recorded_traffic(profile_md, kernel_src):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, or None
+    when the kernel source has changed since those counters were taken."""
+    import hashlib
+    try:
+        txt = open(os.path.join(ROOT, "profiles", profile_md)).read()
+        src = open(os.path.join(ROOT, kernel_src), "rb").read()
+    except OSError:
+        return None
+    fields = dict(line.split(": ", 1) for line in txt.splitlines() if ": " in line and line[:1].isalpha())
+    if fields.get("kernel_source_sha256", "").strip() != hashlib.sha256(src).hexdigest():
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def time_launches(fn, steps, stream):
@@ -89,7 +107,7 @@ def bench_prefill(steps, warmup):
         step(i)
     per, wall = time_launches(step, steps, stream)
     ms = sum(per) / len(per)
-    flops, byts = prefill_algorithmic(B, H, T, dk, dv, x.chunk, 0, 1)
+    flops, byts = prefill_algorithmic(B, H, T, dk, dv, x.chunk, 0, 1, B)
     return dict(ms=ms, wall_ms=wall * 1e3 / steps, per=per, tokens=B * T, flops=flops, bytes=byts,
                 dims=(B, H, T, dk, dv, x.chunk))
 
@@ -119,9 +137,10 @@ def bench_decode(steps_total=512, warmup=64):
                 steps=steps_total)
 
 
-def cpu_baseline(rows=2):
+def cpu_baseline(rows=4):
     """The fp64 oracle, as it stands, on batch rows [0, rows) of the prefill
-    workload (all 16 heads, all 4096 tokens), single-threaded BLAS."""
+    workload (all 16 heads, all 4096 tokens), single-threaded BLAS.  With the
+    default rows=4 the sample is the whole workload (a few seconds of CPU)."""
     from threadpoolctl import threadpool_limits
 
     from gated_delta_rule_kla_amd import inputs
@@ -188,7 +207,9 @@ def main():
                        "global_batch": B, "seq_len": T, "heads": H, "dk": dk, "dv": dv, "chunk": C},
             "tflops": tfl, "mfma_frac": tfl / BF16_PEAK_TFLOPS,
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                         "frac": gbs / HBM_PEAK_GBS,
+                         "traffic": recorded_traffic("kla_chunk_kernel_prefill_b4_h16_t4096_hbm.md",
+                                                     "gated_delta_rule_kla_amd/csrc/kla_chunk.hip"),
                          "kernel": "kla_chunk_kernel<bf16,64,128,2>",
                          "algorithmic_bytes_per_launch": p["bytes"],
                          "algorithmic_flops_per_launch": p["flops"],
@@ -205,7 +226,9 @@ def main():
                "ms_per_step": d["ms"], "wall_ms_per_step": d["wall_ms"], "GB/s": gbs,
                "tokens/s": d["N"] / sec,
                "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                            "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                            "frac": gbs / HBM_PEAK_GBS,
+                            "traffic": recorded_traffic("kla_decode_kernel_n256_h16_hbm.md",
+                                                        "gated_delta_rule_kla_amd/csrc/kla_decode.hip"),
                             "kernel": "kla_decode_kernel<bf16,128,128>",
                             "algorithmic_bytes_per_launch": d["bytes"]}}
         if args.mode == "decode":
