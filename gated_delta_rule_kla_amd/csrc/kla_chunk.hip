@@ -112,6 +112,13 @@ template <> struct Ops<bf16> {
   static __device__ __forceinline__ Grp a_row(const bf16 *row, int kb, int g) {
     return *reinterpret_cast<const bf16x8 *>(row + kb + 8 * g);
   }
+  // the same group read from a naturally ordered row in global memory
+  static __device__ __forceinline__ Grp ldg_grp(const bf16 *row, int kb, int g) {
+    const bf16x4 lo = *reinterpret_cast<const bf16x4 *>(row + kb + 4 * g);
+    const bf16x4 hi = *reinterpret_cast<const bf16x4 *>(row + kb + 16 + 4 * g);
+    return Grp{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
+  static __device__ __forceinline__ Grp zero_grp() { return zero(); }
   // A group of M^T: rows c16 + (l&15) of M^T, contraction rows kb..kb+31 of M,
   // from M stored row-major (grouped columns) -- two transposing LDS reads
   static __device__ __forceinline__ Grp a_trans(const bf16 *M, int ld, int kb, int c16, int lane) {
@@ -153,6 +160,10 @@ template <> struct Ops<float> {
   static __device__ __forceinline__ Grp a_row(const float *row, int kb, int g) {
     return *reinterpret_cast<const f32x4 *>(row + kb + 4 * g);
   }
+  static __device__ __forceinline__ Grp ldg_grp(const float *row, int kb, int g) {
+    return *reinterpret_cast<const f32x4 *>(row + kb + 4 * g);
+  }
+  static __device__ __forceinline__ Grp zero_grp() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
   static __device__ __forceinline__ Grp a_trans(const float *M, int ld, int kb, int c16, int lane) {
     const int g = lane >> 4, li = lane & 15;
     Grp r;
@@ -228,49 +239,83 @@ __device__ __forceinline__ float wave_inclusive_scan(float v) {
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // ---------------------------------------------------------------------------
-// LDS plan
+// Roles and LDS plan
 // ---------------------------------------------------------------------------
-template <typename E, int C, int DK, int NBW>
+// Waves of a workgroup.  Iteration i (one barrier each, i = -2 .. nch) has
+//   CHAIN  scan chunk i        OUTPUT  chunk i-1       PWAVE[2]  P of chunk i
+//   TSOLVE T' of chunk i+1     VLOAD   V of chunk i+1  GRAM[2]   chunk i+2
+enum Role { CHAIN = 0, OUTPUT = 1, GRAM0 = 2, GRAM1 = 3, TSOLVE = 4, PW0 = 5, PW1 = 6, VLOAD = 7 };
+constexpr int kWaves = 8;
+
+// lower-triangular 16x16 tile (rt, st), st <= rt, in row-major order; the two
+// Gram waves and the two P waves each take one half of the list
+__host__ __device__ constexpr int tile_index(int rt, int st) { return rt * (rt + 1) / 2 + st; }
+__host__ __device__ constexpr int tile_part(int NB, int rt, int st) {
+  return tile_index(rt, st) < (NB * (NB + 1) / 2 + 1) / 2 ? 0 : 1;
+}
+__host__ __device__ constexpr bool part_uses_row(int NB, int part, int rt) {
+  for (int st = 0; st <= rt; ++st)
+    if (tile_part(NB, rt, st) == part) return true;
+  return false;
+}
+// diagonal blocks owned by a Gram wave, in order
+__host__ __device__ constexpr int part_diag_count(int NB, int part) {
+  int n = 0;
+  for (int b = 0; b < NB; ++b) n += (tile_part(NB, b, b) == part);
+  return n;
+}
+__host__ __device__ constexpr int part_diag_block(int NB, int part, int k) {
+  for (int b = 0; b < NB; ++b)
+    if (tile_part(NB, b, b) == part && k-- == 0) return b;
+  return -1;
+}
+
+template <typename E, int C, int DK, int NCT>
 struct ChunkShape {
-  static constexpr int NB = C / 16;           // 16-row blocks per chunk
-  static constexpr int DVT = 16 * NBW;        // state columns per workgroup
-  static constexpr int NWAVES = NBW + 2;      // scan waves + K wave + Q wave
-  static constexpr int NT = 64 * NWAVES;
+  static constexpr int NB = C / 16;            // 16-row blocks per chunk
+  static constexpr int DVT = 16 * NCT;         // state columns per workgroup
+  static constexpr int NT = 64 * kWaves;
   static constexpr int PAD = 16 / (int)sizeof(E);
-  static constexpr int LDK = DK + PAD;        // pitch of K and Q rows (grouped columns)
-  static constexpr int LDC = C + PAD;         // pitch of T' and P rows (grouped columns) and of A
-  static constexpr int LDV = DVT + PAD;       // pitch of V slice rows (natural)
-  static constexpr int LDD = 20;              // fp32 pitch of 16-wide diagonal blocks
-  static constexpr int KSTEPS = DK / Ops<E>::KSTEP;
-  // shared double buffer (elements of E, then floats)
+  static constexpr int LDK = DK + PAD;         // K rows (grouped columns)
+  static constexpr int LDC = C + PAD;          // T' and P rows (grouped columns)
+  static constexpr int LDV = DVT + PAD;        // V slice rows (natural)
+  static constexpr int LDA = 16 + PAD;         // rows of one 16x16 off-diagonal A block
+  static constexpr int LDD = 20;               // fp32 16-wide rows of diagonal blocks
+  static constexpr int KG = Ops<E>::KG;
+  static constexpr int NOFF = NB * (NB - 1) / 2;
+  static constexpr int MAXD = (NB + 1) / 2;    // diagonal blocks per Gram wave
+  // sizes in bytes
+  static constexpr int K_SLOT = C * LDK * (int)sizeof(E);
+  static constexpr int V_SLOT = C * LDV * (int)sizeof(E);
+  static constexpr int TP_SLOT = C * LDC * (int)sizeof(E);
+  static constexpr int P_SLOT = C * LDC * (int)sizeof(E);
+  static constexpr int SU_S = NCT * (DK / KG) * 64 * 16;   // S start groups, 16 B per lane
+  static constexpr int SU_U = NCT * (C / KG) * 64 * 16;    // U~ groups
+  static constexpr int SU_SLOT = SU_S + SU_U;
+  static constexpr int A_SLOT = (NOFF > 0 ? NOFF : 1) * 16 * LDA * (int)sizeof(E);
+  static constexpr int TD_SLOT = NB * 16 * LDD * 4;        // T diagonal blocks, transposed, fp32
+  static constexpr int VEC_SLOT = 4 * C * 4;               // gamma, Gam, d, beta
+  static constexpr int GPRIV = MAXD * 16 * LDD * 4 + NB * 64 * 4 + 2 * C * 4;  // At blocks, norm partials, gamma/beta
+  static constexpr int OT_BYTES = (sizeof(E) == 2 ? NCT : 0) * 16 * LDC * (int)sizeof(E);
+  // offsets
   static constexpr int OFF_K = 0;
-  static constexpr int OFF_Q = OFF_K + C * LDK;
-  static constexpr int OFF_V = OFF_Q + C * LDK;
-  static constexpr int OFF_TP = OFF_V + C * LDV;
-  static constexpr int OFF_P = OFF_TP + C * LDC;
-  static constexpr int BUF_E = OFF_P + C * LDC;
-  static constexpr int BUF_F = 2 * C;         // Gam[C], d[C]
-  static constexpr int BUF_BYTES = BUF_E * (int)sizeof(E) + BUF_F * 4;
-  // K wave private
-  static constexpr int A_BYTES = C * LDC * (int)sizeof(E);       // A, row-major (natural), E
-  static constexpr int ATD_BYTES = NB * 16 * LDD * 4;            // A diagonal blocks, transposed, fp32
-  static constexpr int TD_BYTES = NB * 16 * LDD * 4;             // T diagonal blocks, fp32
-  // producer waves' private per-row vectors: K wave gamma[C], beta[C],
-  // norm partials [NB][4][16]; Q wave gamma[C]
-  static constexpr int VEC_BYTES = (3 * C + NB * 64) * 4;
-  // scan wave private: O^T staging (16 columns x C rows) for row-contiguous stores
-  static constexpr int OT_BYTES = 16 * LDC * (int)sizeof(E);
-  static constexpr int OFF_KW = 2 * BUF_BYTES;
-  static constexpr int OFF_VEC = OFF_KW + A_BYTES + ATD_BYTES + TD_BYTES;
-  static constexpr int OFF_OT = OFF_VEC + VEC_BYTES;
-  static constexpr int BYTES = OFF_OT + NBW * OT_BYTES;
+  static constexpr int OFF_V = OFF_K + 3 * K_SLOT;
+  static constexpr int OFF_TP = OFF_V + 2 * V_SLOT;
+  static constexpr int OFF_P = OFF_TP + 2 * TP_SLOT;
+  static constexpr int OFF_SU = OFF_P + 2 * P_SLOT;
+  static constexpr int OFF_A = OFF_SU + 2 * SU_SLOT;
+  static constexpr int OFF_TD = OFF_A + 2 * A_SLOT;
+  static constexpr int OFF_VEC = OFF_TD + 2 * TD_SLOT;
+  static constexpr int OFF_GP = OFF_VEC + 4 * VEC_SLOT;
+  static constexpr int OFF_OT = OFF_GP + 2 * GPRIV;
+  static constexpr int BYTES = OFF_OT + OT_BYTES;
 
   static_assert(C == 16 || C == 64, "chunk");
-  static_assert(C % Ops<E>::KG == 0 && DK % Ops<E>::KG == 0 && DK % Ops<E>::KSTEP == 0, "dk");
-  static_assert(BUF_BYTES % 16 == 0 && A_BYTES % 16 == 0 && VEC_BYTES % 16 == 0 && OT_BYTES % 16 == 0,
-                "lds align");
+  static_assert(C % KG == 0 && DK % KG == 0 && DK % Ops<E>::KSTEP == 0, "dk");
+  static_assert(K_SLOT % 16 == 0 && V_SLOT % 16 == 0 && TP_SLOT % 16 == 0 && A_SLOT % 16 == 0 &&
+                    GPRIV % 16 == 0 && VEC_SLOT % 16 == 0 && OT_BYTES % 16 == 0, "lds align");
   static_assert((LDK * (int)sizeof(E)) % 16 == 0 && (LDC * (int)sizeof(E)) % 16 == 0 &&
-                    (LDV * (int)sizeof(E)) % 16 == 0, "row align");
+                    (LDV * (int)sizeof(E)) % 16 == 0 && (LDA * (int)sizeof(E)) % 8 == 0, "row align");
   static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
@@ -287,14 +332,17 @@ struct ChunkParams {
 // ---------------------------------------------------------------------------
 // the kernel
 // ---------------------------------------------------------------------------
-template <typename E, int C, int DK, int NBW>
-__global__ __launch_bounds__(64 * (NBW + 2)) void kla_chunk_kernel(ChunkParams p) {
-  using Sh = ChunkShape<E, C, DK, NBW>;
+template <typename E, int C, int DK, int NCT>
+__global__ __launch_bounds__(64 * kWaves) void kla_chunk_kernel(ChunkParams p) {
+  using Sh = ChunkShape<E, C, DK, NCT>;
   using O = Ops<E>;
   using Nat = typename O::Nat;
   using Grp = typename O::Grp;
-  constexpr int NB = Sh::NB, DVT = Sh::DVT, LDK = Sh::LDK, LDC = Sh::LDC, LDV = Sh::LDV, LDD = Sh::LDD;
-  constexpr int KSTEP = O::KSTEP, VPL = O::VPL, KSTEPS = Sh::KSTEPS, KG = O::KG, TPG = KG / 16;
+  constexpr int NB = Sh::NB, DVT = Sh::DVT, LDK = Sh::LDK, LDC = Sh::LDC, LDV = Sh::LDV;
+  constexpr int LDA = Sh::LDA, LDD = Sh::LDD;
+  constexpr int KSTEP = O::KSTEP, VPL = O::VPL, KSTEPS = DK / KSTEP, KG = O::KG, TPG = KG / 16;
+  constexpr int NQG = DK / KG;  // contraction groups over dk
+  constexpr int NCG = C / KG;   // contraction groups over the chunk
 
   __shared__ __attribute__((aligned(16))) char smem[Sh::BYTES];
 
@@ -326,168 +374,131 @@ __global__ __launch_bounds__(64 * (NBW + 2)) void kla_chunk_kernel(ChunkParams p
   const E *geta = static_cast<const E *>(p.eta);
   E *go = static_cast<E *>(p.o);
   const int dv = p.dv;
+  auto nrow_of = [&](int c) { return min(C, len - c * C); };
+  auto tok0_of = [&](int c) { return row0 + (size_t)c * C; };
 
-  auto bufE = [&](int i) { return reinterpret_cast<E *>(smem + i * Sh::BUF_BYTES); };
-  auto bufF = [&](int i) {
-    return reinterpret_cast<float *>(smem + i * Sh::BUF_BYTES + Sh::BUF_E * (int)sizeof(E));
+  // ---- LDS views -------------------------------------------------------------
+  auto sK = [&](int c) { return reinterpret_cast<E *>(smem + Sh::OFF_K + (c % 3) * Sh::K_SLOT); };
+  auto sV = [&](int c) { return reinterpret_cast<E *>(smem + Sh::OFF_V + (c & 1) * Sh::V_SLOT); };
+  auto sTp = [&](int c) { return reinterpret_cast<E *>(smem + Sh::OFF_TP + (c & 1) * Sh::TP_SLOT); };
+  auto sP = [&](int c) { return reinterpret_cast<E *>(smem + Sh::OFF_P + (c & 1) * Sh::P_SLOT); };
+  auto sSuS = [&](int c) { return reinterpret_cast<Grp *>(smem + Sh::OFF_SU + (c & 1) * Sh::SU_SLOT); };
+  auto sSuU = [&](int c) {
+    return reinterpret_cast<Grp *>(smem + Sh::OFF_SU + (c & 1) * Sh::SU_SLOT + Sh::SU_S);
   };
+  auto sA = [&](int c) { return reinterpret_cast<E *>(smem + Sh::OFF_A + (c & 1) * Sh::A_SLOT); };
+  auto sTd = [&](int c) { return reinterpret_cast<float *>(smem + Sh::OFF_TD + (c & 1) * Sh::TD_SLOT); };
+  // per-chunk row vectors: gamma, Gam = exp(gamma), d = exp(gamma_C - gamma), beta
+  auto sVec = [&](int c) { return reinterpret_cast<float *>(smem + Sh::OFF_VEC + (c & 3) * Sh::VEC_SLOT); };
 
   // strictly-upper 16x16 blocks of T' and P are zero and never rewritten
   for (int i = threadIdx.x; i < 2 * C * C; i += Sh::NT) {
     const int bi = i / (C * C), rr = (i / C) % C, ss = i % C;
     if ((rr >> 4) < (ss >> 4)) {
-      bufE(bi)[Sh::OFF_TP + rr * LDC + O::perm(ss)] = Elem<E>::from_f32(0.f);
-      bufE(bi)[Sh::OFF_P + rr * LDC + O::perm(ss)] = Elem<E>::from_f32(0.f);
+      sTp(bi)[rr * LDC + O::perm(ss)] = Elem<E>::from_f32(0.f);
+      sP(bi)[rr * LDC + O::perm(ss)] = Elem<E>::from_f32(0.f);
     }
   }
 
-  // ---- per-row vectors of the producer waves (private LDS) -------------------
-  float *sGamK = reinterpret_cast<float *>(smem + Sh::OFF_VEC);
-  float *sBetaK = sGamK + C;
-  float *sNrmK = sGamK + 2 * C;
-  float *sGamQ = sNrmK + NB * 64;
-
-  if (wave < NBW) {
-    // ======================= scan wave: 16 state columns =====================
-    f32x4 accS[DK / 16];
-    const int col0 = jt * DVT + 16 * wave;     // first of this wave's 16 state columns
-    const int col = col0 + li;                  // this lane's state column
-    E *sOt = reinterpret_cast<E *>(smem + Sh::OFF_OT + wave * Sh::OT_BYTES);
+  if (wave == CHAIN) {
+    // =================== chain: the sequential state scan ====================
+    // S (DK rows x DVT columns, fp32) lives in the accumulators for the whole
+    // sequence: accS[ct][it] is the 16x16 tile (rows 16 it.., columns 16 ct..).
+    f32x4 accS[NCT][DK / 16];
     const size_t sbase = (size_t)nh * DK * (size_t)dv;
 #pragma unroll
-    for (int it = 0; it < DK / 16; ++it) {
+    for (int ct = 0; ct < NCT; ++ct) {
+      const int col = jt * DVT + 16 * ct + li;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = 16 * it + 4 * lg + j;
-        accS[it][j] = p.s0 ? p.s0[sbase + (size_t)r * dv + col] : 0.f;
-      }
+      for (int it = 0; it < DK / 16; ++it)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          accS[ct][it][j] = p.s0 ? p.s0[sbase + (size_t)(16 * it + 4 * lg + j) * dv + col] : 0.f;
     }
     __syncthreads();
-    for (int c = 0; c < nch; ++c) {
-      const int cur = c & 1;
-      const E *sK = bufE(cur) + Sh::OFF_K;
-      const E *sQ = bufE(cur) + Sh::OFF_Q;
-      const E *sV = bufE(cur) + Sh::OFF_V;
-      const E *sTp = bufE(cur) + Sh::OFF_TP;
-      const E *sP = bufE(cur) + Sh::OFF_P;
-      const float *sGam = bufF(cur);
-      const float *sD = bufF(cur) + C;
-
-      // Every S-independent left operand of this chunk is read up front, so the
-      // LDS latency overlaps the MFMA chain instead of stalling each step.
-      Grp kA[NB][DK / KG], qA[NB][DK / KG];
+    for (int i = -2; i <= nch; ++i) {
+      if (i >= 0 && i < nch) {
+        const int c = i;
+        const E *K = sK(c);
+        const E *V = sV(c);
+        const E *Tp = sTp(c);
+        const float *vec = sVec(c);
+        Grp *suS = sSuS(c);
+        Grp *suU = sSuU(c);
+        // S as right operands, straight from the accumulators; also handed to
+        // the output wave (it needs the chunk's start state)
+        Grp sb[NCT][NQG];
 #pragma unroll
-      for (int rt = 0; rt < NB; ++rt) {
+        for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-        for (int q = 0; q < DK / KG; ++q) {
-          kA[rt][q] = O::a_row(sK + (16 * rt + li) * LDK, q * KG, lg);
-          qA[rt][q] = O::a_row(sQ + (16 * rt + li) * LDK, q * KG, lg);
-        }
-      }
-      f32x4 gm[NB], dd[NB], vv[NB];
-#pragma unroll
-      for (int rt = 0; rt < NB; ++rt) {
-        gm[rt] = *reinterpret_cast<const f32x4 *>(sGam + 16 * rt + 4 * lg);
-        dd[rt] = *reinterpret_cast<const f32x4 *>(sD + 16 * rt + 4 * lg);
-        vv[rt] = O::col4(sV, LDV, 16 * rt, 16 * wave, lane);
-      }
-      Grp tA[NB][C / KG], pA[NB][C / KG];
-#pragma unroll
-      for (int rt = 0; rt < NB; ++rt) {
-#pragma unroll
-        for (int q = 0; q * KG < 16 * (rt + 1); ++q) {
-          tA[rt][q] = O::a_row(sTp + (16 * rt + li) * LDC, q * KG, lg);
-          pA[rt][q] = O::a_row(sP + (16 * rt + li) * LDC, q * KG, lg);
-        }
-      }
-      Grp ktA[DK / 16][C / KG];
-#pragma unroll
-      for (int it = 0; it < DK / 16; ++it) {
-#pragma unroll
-        for (int q = 0; q < C / KG; ++q) ktA[it][q] = O::a_trans(sK, LDK, q * KG, 16 * it, lane);
-      }
-      const float gC = sGam[C - 1];
-
-      // S as right operands, straight from the accumulators
-      Grp sb[DK / KG];
-#pragma unroll
-      for (int q = 0; q < DK / KG; ++q) sb[q] = O::b_from_d(&accS[q * TPG]);
-      // K S and Q S
-      f32x4 aK[NB], aQ[NB];
-#pragma unroll
-      for (int rt = 0; rt < NB; ++rt) {
-        aK[rt] = aQ[rt] = zero4();
-#pragma unroll
-        for (int q = 0; q < DK / KG; ++q) {
-          aK[rt] = O::mma_grp(kA[rt][q], sb[q], aK[rt]);
-          aQ[rt] = O::mma_grp(qA[rt][q], sb[q], aQ[rt]);
-        }
-      }
-      // X = V - Diag(Gam) K S;  O starts as Diag(Gam) Q S
-      f32x4 xv[NB];
-#pragma unroll
-      for (int rt = 0; rt < NB; ++rt) {
-        xv[rt] = vv[rt] - gm[rt] * aK[rt];
-        aQ[rt] = gm[rt] * aQ[rt];
-      }
-      Grp xb[C / KG];
-#pragma unroll
-      for (int q = 0; q < C / KG; ++q) xb[q] = O::b_from_d(&xv[q * TPG]);
-      // U~ = T' X   (T' lower triangular: skip the zero groups)
-      f32x4 u[NB], du[NB];
-#pragma unroll
-      for (int rt = 0; rt < NB; ++rt) {
-        u[rt] = zero4();
-#pragma unroll
-        for (int q = 0; q * KG < 16 * (rt + 1); ++q) u[rt] = O::mma_grp(tA[rt][q], xb[q], u[rt]);
-        du[rt] = dd[rt] * u[rt];
-      }
-      Grp ub[C / KG], dub[C / KG];
-#pragma unroll
-      for (int q = 0; q < C / KG; ++q) {
-        ub[q] = O::b_from_d(&u[q * TPG]);
-        dub[q] = O::b_from_d(&du[q * TPG]);
-      }
-      // S <- Gam_C S + K^T Diag(d) U~   (issued before O: it is the chain)
-#pragma unroll
-      for (int it = 0; it < DK / 16; ++it) {
-        accS[it] = gC * accS[it];
-#pragma unroll
-        for (int q = 0; q < C / KG; ++q) accS[it] = O::mma_grp(ktA[it][q], dub[q], accS[it]);
-      }
-      // O += P U~ ; write the valid rows
-      const int nrow = min(C, len - c * C);
-      const size_t tok0 = row0 + (size_t)c * C;
-#pragma unroll
-      for (int rt = 0; rt < NB; ++rt) {
-#pragma unroll
-        for (int q = 0; q * KG < 16 * (rt + 1); ++q) aQ[rt] = O::mma_grp(pA[rt][q], ub[q], aQ[rt]);
-      }
-      if constexpr (sizeof(E) == 2) {
-        // stage O^T (4 rows of one column per lane = one 8-byte write), read it
-        // back transposed (4 columns of one row per lane) and store 8 bytes
-#pragma unroll
-        for (int rt = 0; rt < NB; ++rt) {
-          bf16x4 ob;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) ob[j] = (bf16)aQ[rt][j];
-          *reinterpret_cast<bf16x4 *>(sOt + li * LDC + 16 * rt + 4 * lg) = ob;
-        }
-        const int x = (lane >> 2) & 3, a = lane & 3;
-#pragma unroll
-        for (int rt = 0; rt < NB; ++rt) {
-          const bf16x4 rowv =
-              __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(sOt + (4 * lg + x) * LDC + 16 * rt + 4 * a));
-          const int r = 16 * rt + li;
-          if (r < nrow) *reinterpret_cast<bf16x4 *>(go + (tok0 + r) * (size_t)dv + col0 + 4 * lg) = rowv;
-        }
-      } else {
+          for (int q = 0; q < NQG; ++q) {
+            sb[ct][q] = O::b_from_d(&accS[ct][q * TPG]);
+            suS[(ct * NQG + q) * 64 + lane] = sb[ct][q];
+          }
+        // K S
+        f32x4 x[NCT][NB];
 #pragma unroll
         for (int rt = 0; rt < NB; ++rt) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int r = 16 * rt + 4 * lg + j;
-            if (r < nrow) go[(tok0 + r) * (size_t)dv + col] = Elem<E>::from_f32(aQ[rt][j]);
+          for (int ct = 0; ct < NCT; ++ct) x[ct][rt] = zero4();
+#pragma unroll
+          for (int q = 0; q < NQG; ++q) {
+            const Grp a = O::a_row(K + (16 * rt + li) * LDK, q * KG, lg);
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) x[ct][rt] = O::mma_grp(a, sb[ct][q], x[ct][rt]);
+          }
+        }
+        // X = V - Diag(Gam) K S
+#pragma unroll
+        for (int rt = 0; rt < NB; ++rt) {
+          const f32x4 gm = *reinterpret_cast<const f32x4 *>(vec + C + 16 * rt + 4 * lg);
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct) x[ct][rt] = O::col4(V, LDV, 16 * rt, 16 * ct, lane) - gm * x[ct][rt];
+        }
+        Grp xb[NCT][NCG];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+          for (int q = 0; q < NCG; ++q) xb[ct][q] = O::b_from_d(&x[ct][q * TPG]);
+        // U~ = T' X   (T' lower triangular: skip the zero groups)
+        f32x4 u[NCT][NB];
+#pragma unroll
+        for (int rt = 0; rt < NB; ++rt) {
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct) u[ct][rt] = zero4();
+#pragma unroll
+          for (int q = 0; q * KG < 16 * (rt + 1); ++q) {
+            const Grp a = O::a_row(Tp + (16 * rt + li) * LDC, q * KG, lg);
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) u[ct][rt] = O::mma_grp(a, xb[ct][q], u[ct][rt]);
+          }
+        }
+        // U~ groups for the output wave; Diag(d) U~ groups for the update
+        Grp dub[NCT][NCG];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+          for (int q = 0; q < NCG; ++q) {
+            suU[(ct * NCG + q) * 64 + lane] = O::b_from_d(&u[ct][q * TPG]);
+            f32x4 du[TPG];
+#pragma unroll
+            for (int tt = 0; tt < TPG; ++tt) {
+              const int r16 = 16 * (q * TPG + tt);
+              du[tt] = *reinterpret_cast<const f32x4 *>(vec + 2 * C + r16 + 4 * lg) * u[ct][q * TPG + tt];
+            }
+            dub[ct][q] = O::b_from_d(du);
+          }
+        // S <- Gam_C S + K^T Diag(d) U~
+        const float gC = vec[C + C - 1];
+#pragma unroll
+        for (int it = 0; it < DK / 16; ++it) {
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct) accS[ct][it] = gC * accS[ct][it];
+#pragma unroll
+          for (int q = 0; q < NCG; ++q) {
+            const Grp a = O::a_trans(K, LDK, q * KG, 16 * it, lane);
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) accS[ct][it] = O::mma_grp(a, dub[ct][q], accS[ct][it]);
           }
         }
       }
@@ -495,25 +506,120 @@ __global__ __launch_bounds__(64 * (NBW + 2)) void kla_chunk_kernel(ChunkParams p
     }
     if (p.sfin) {
 #pragma unroll
-      for (int it = 0; it < DK / 16; ++it) {
+      for (int ct = 0; ct < NCT; ++ct) {
+        const int col = jt * DVT + 16 * ct + li;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int r = 16 * it + 4 * lg + j;
-          p.sfin[sbase + (size_t)r * dv + col] = accS[it][j];
-        }
+        for (int it = 0; it < DK / 16; ++it)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) p.sfin[sbase + (size_t)(16 * it + 4 * lg + j) * dv + col] = accS[ct][it][j];
       }
     }
-  } else if (wave == NBW) {
-    // ======================= K wave ==========================================
-    // The chunk's raw inputs are fetched one chunk ahead into registers: the
-    // loads for chunk c+1 are issued at the end of producing chunk c and land
-    // while the wave waits at the barrier.  Rows past the sequence end load a
-    // clamped (valid) row and are zeroed after arrival.
+  } else if (wave == OUTPUT) {
+    // =================== output: O = Diag(Gam) Q S + P U~ =====================
+    // Runs one chunk behind the chain; Q comes straight from global memory in
+    // grouped column order, fetched one iteration ahead.
+    Grp qreg[NB][NQG];
+    auto fetch = [&](int c) {
+      const int nrow = nrow_of(c);
+      const size_t tok0 = tok0_of(c);
+#pragma unroll
+      for (int rt = 0; rt < NB; ++rt) {
+        const E *row = gq + (tok0 + min(16 * rt + li, nrow - 1)) * DK;
+#pragma unroll
+        for (int q = 0; q < NQG; ++q) qreg[rt][q] = O::ldg_grp(row, q * KG, lg);
+      }
+    };
+    E *sOt = reinterpret_cast<E *>(smem + Sh::OFF_OT);
+    __syncthreads();
+    for (int i = -2; i <= nch; ++i) {
+      if (i >= 1 && i <= nch) {
+        const int c = i - 1;
+        const int nrow = nrow_of(c);
+        const size_t tok0 = tok0_of(c);
+        const E *Pm = sP(c);
+        const Grp *suS = sSuS(c);
+        const Grp *suU = sSuU(c);
+        const float *vec = sVec(c);
+#pragma unroll
+        for (int rt = 0; rt < NB; ++rt)
+          if (16 * rt + li >= nrow)
+#pragma unroll
+            for (int q = 0; q < NQG; ++q) qreg[rt][q] = O::zero_grp();
+        f32x4 ao[NCT][NB];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+          Grp sb[NQG];
+#pragma unroll
+          for (int q = 0; q < NQG; ++q) sb[q] = suS[(ct * NQG + q) * 64 + lane];
+#pragma unroll
+          for (int rt = 0; rt < NB; ++rt) {
+            ao[ct][rt] = zero4();
+#pragma unroll
+            for (int q = 0; q < NQG; ++q) ao[ct][rt] = O::mma_grp(qreg[rt][q], sb[q], ao[ct][rt]);
+          }
+        }
+#pragma unroll
+        for (int rt = 0; rt < NB; ++rt) {
+          const f32x4 gm = *reinterpret_cast<const f32x4 *>(vec + C + 16 * rt + 4 * lg);
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct) ao[ct][rt] = gm * ao[ct][rt];
+        }
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+          Grp ub[NCG];
+#pragma unroll
+          for (int q = 0; q < NCG; ++q) ub[q] = suU[(ct * NCG + q) * 64 + lane];
+#pragma unroll
+          for (int rt = 0; rt < NB; ++rt)
+#pragma unroll
+            for (int q = 0; q * KG < 16 * (rt + 1); ++q)
+              ao[ct][rt] = O::mma_grp(O::a_row(Pm + (16 * rt + li) * LDC, q * KG, lg), ub[q], ao[ct][rt]);
+        }
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+          const int col0 = jt * DVT + 16 * ct;
+          if constexpr (sizeof(E) == 2) {
+            // stage O^T (4 rows of one column = one 8-byte write per lane), read
+            // it back transposed (4 columns of one row) and store 8 bytes
+            E *st = sOt + ct * 16 * LDC;
+#pragma unroll
+            for (int rt = 0; rt < NB; ++rt) {
+              bf16x4 ob;
+#pragma unroll
+              for (int j = 0; j < 4; ++j) ob[j] = (bf16)ao[ct][rt][j];
+              *reinterpret_cast<bf16x4 *>(st + li * LDC + 16 * rt + 4 * lg) = ob;
+            }
+            const int x = (lane >> 2) & 3, a = lane & 3;
+            bf16x4 rows[NB];
+#pragma unroll
+            for (int rt = 0; rt < NB; ++rt)
+              rows[rt] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(st + (4 * lg + x) * LDC + 16 * rt + 4 * a));
+#pragma unroll
+            for (int rt = 0; rt < NB; ++rt)
+              if (16 * rt + li < nrow)
+                *reinterpret_cast<bf16x4 *>(go + (tok0 + 16 * rt + li) * (size_t)dv + col0 + 4 * lg) = rows[rt];
+          } else {
+#pragma unroll
+            for (int rt = 0; rt < NB; ++rt)
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const int r = 16 * rt + 4 * lg + j;
+                if (r < nrow) go[(tok0 + r) * (size_t)dv + col0 + li] = Elem<E>::from_f32(ao[ct][rt][j]);
+              }
+          }
+        }
+      }
+      if (i >= 0 && i < nch) fetch(i);
+      lds_barrier();
+    }
+  } else if (wave == GRAM0 || wave == GRAM1) {
+    // =================== Gram waves: chunk i+2 ================================
+    const int part = wave - GRAM0;
     Nat kop[NB][KSTEPS];
     E kg_raw = Elem<E>::from_f32(0.f), ke_raw = Elem<E>::from_f32(0.f);
     auto fetch = [&](int c) {
-      const int nrow = min(C, len - c * C);
-      const size_t tok0 = row0 + (size_t)c * C;
+      const int nrow = nrow_of(c);
+      const size_t tok0 = tok0_of(c);
 #pragma unroll
       for (int rt = 0; rt < NB; ++rt) {
         const int r = min(16 * rt + li, nrow - 1);
@@ -524,63 +630,70 @@ __global__ __launch_bounds__(64 * (NBW + 2)) void kla_chunk_kernel(ChunkParams p
       kg_raw = gg[tok0 + lr];
       ke_raw = geta[tok0 + lr];
     };
-    E *sA = reinterpret_cast<E *>(smem + Sh::OFF_KW);
-    float *sAtd = reinterpret_cast<float *>(smem + Sh::OFF_KW + Sh::A_BYTES);
-    float *sTd = reinterpret_cast<float *>(smem + Sh::OFF_KW + Sh::A_BYTES + Sh::ATD_BYTES);
+    char *gp = smem + Sh::OFF_GP + part * Sh::GPRIV;
+    float *sAtd = reinterpret_cast<float *>(gp);                       // [MAXD][16][LDD]
+    float *sNrm = sAtd + Sh::MAXD * 16 * LDD;                          // [NB][4][16]
+    float *sGam = sNrm + NB * 64;                                      // [C]
+    float *sBet = sGam + C;                                            // [C]
 
-    auto produce = [&](int c, int nb) {
-      E *sK = bufE(nb) + Sh::OFF_K;
-      E *sTp = bufE(nb) + Sh::OFF_TP;
-      float *sF = bufF(nb);
-      const int nrow = min(C, len - c * C);
-      // K rows to LDS (grouped columns) for the scan waves
+    auto produce = [&](int c) {
+      const int nrow = nrow_of(c);
+      E *K = sK(c);
+      E *Ablk = sA(c);
+      float *Td = sTd(c);
+      float *vec = sVec(c);
 #pragma unroll
       for (int rt = 0; rt < NB; ++rt) {
         const int r = 16 * rt + li;
 #pragma unroll
         for (int kq = 0; kq < KSTEPS; ++kq) {
           if (r >= nrow) kop[rt][kq] = O::zero();
-          O::st_nat(sK + r * LDK, kq, lg, kop[rt][kq]);
+          // K rows for the chain and P waves (half the row tiles each)
+          if ((rt < (NB + 1) / 2) == (part == 0)) O::st_nat(K + r * LDK, kq, lg, kop[rt][kq]);
         }
       }
-      // fused ||k_r||^2: lane holds a quarter of row 16rt + li; the four
-      // quarters are summed through LDS by lane r
+      // fused ||k_r||^2: lane holds a quarter of row 16rt + li; lane r sums the
+      // four quarters of its row through LDS
 #pragma unroll
       for (int rt = 0; rt < NB; ++rt) {
         float sq = 0.f;
 #pragma unroll
         for (int kq = 0; kq < KSTEPS; ++kq) sq += O::sumsq(kop[rt][kq]);
-        sNrmK[(rt * 4 + lg) * 16 + li] = sq;
+        sNrm[(rt * 4 + lg) * 16 + li] = sq;
       }
       const float gam = wave_inclusive_scan((lane < nrow) ? Elem<E>::to_f32(kg_raw) : 0.f);
       float nr = 0.f;
       if (lane < C) {
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) nr += sNrmK[((lane >> 4) * 4 + q4) * 16 + li];
+        for (int q4 = 0; q4 < 4; ++q4) nr += sNrm[((lane >> 4) * 4 + q4) * 16 + li];
       }
       // beta of rows beyond the sequence end is 0 (not 0/0 when eps = 0)
       const float beta = (lane < nrow) ? Elem<E>::to_f32(ke_raw) / (nr + p.eps) : 0.f;
       const float gamC = lane_value(gam, C - 1);
       if (lane < C) {
-        sGamK[lane] = gam;
-        sBetaK[lane] = beta;
-        sF[lane] = __expf(gam);             // Gam_r
-        sF[C + lane] = __expf(gamC - gam);  // d_r
+        sGam[lane] = gam;
+        sBet[lane] = beta;
+        if (part == 0) {
+          vec[lane] = gam;
+          vec[C + lane] = __expf(gam);             // Gam_r
+          vec[2 * C + lane] = __expf(gamC - gam);  // d_r
+          vec[3 * C + lane] = beta;
+        }
       }
-      // per-lane row (r = 16 rt + 4 lg + j) and column (s = 16 st + li) gate values
       f32x4 gr4[NB], br4[NB];
       float gs1[NB];
 #pragma unroll
       for (int rt = 0; rt < NB; ++rt) {
-        gr4[rt] = *reinterpret_cast<const f32x4 *>(sGamK + 16 * rt + 4 * lg);
-        br4[rt] = *reinterpret_cast<const f32x4 *>(sBetaK + 16 * rt + 4 * lg);
-        gs1[rt] = sGamK[16 * rt + li];
+        gr4[rt] = *reinterpret_cast<const f32x4 *>(sGam + 16 * rt + 4 * lg);
+        br4[rt] = *reinterpret_cast<const f32x4 *>(sBet + 16 * rt + 4 * lg);
+        gs1[rt] = sGam[16 * rt + li];
       }
-      // Gram tiles K K^T (lower, incl. diagonal) and A
+      // this wave's Gram tiles and A = beta_r (K K^T)_rs exp(gamma_r - gamma_s), r > s
 #pragma unroll
       for (int rt = 0; rt < NB; ++rt) {
 #pragma unroll
         for (int st = 0; st <= rt; ++st) {
+          if (tile_part(NB, rt, st) != part) continue;
           f32x4 acc = zero4();
 #pragma unroll
           for (int kq = 0; kq < KSTEPS; ++kq) acc = O::mma(kop[rt][kq], kop[st][kq], acc);
@@ -593,42 +706,80 @@ __global__ __launch_bounds__(64 * (NBW + 2)) void kla_chunk_kernel(ChunkParams p
             av[j] = (r > s) ? br4[rt][j] * acc[j] * dec : 0.f;
           }
           if (st < rt) {
+            E *blk = Ablk + (rt * (rt - 1) / 2 + st) * 16 * LDA;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) sA[(16 * rt + 4 * lg + j) * LDC + s] = Elem<E>::from_f32(av[j]);
+            for (int j = 0; j < 4; ++j) blk[(4 * lg + j) * LDA + li] = Elem<E>::from_f32(av[j]);
           } else {
-            // diagonal block, stored transposed: At[s'][r']
-            *reinterpret_cast<f32x4 *>(sAtd + rt * 16 * LDD + li * LDD + 4 * lg) = av;
+            // own diagonal block, stored transposed: At[s'][r']
+            int dl = 0;
+#pragma unroll
+            for (int kk = 0; kk < Sh::MAXD; ++kk)
+              if (part_diag_block(NB, part, kk) == rt) dl = kk;
+            *reinterpret_cast<f32x4 *>(sAtd + dl * 16 * LDD + li * LDD + 4 * lg) = av;
           }
         }
       }
-      // diagonal blocks of T = (I + A)^-1: lane = (block lg, column li);
-      // the block (stored transposed) is read whole before the substitution
-      if (lg < NB) {
-        float x[16];
-        f32x4 at[16][4];
+      // own diagonal blocks of T = (I + A)^-1 by column-parallel forward
+      // substitution in fp32: lane = (local block lg, column li)
+      constexpr int ND0 = part_diag_count(NB, 0), ND1 = part_diag_count(NB, 1);
+      const int nd = part == 0 ? ND0 : ND1;
+      if (lg < nd) {
+        int bb = 0;
+#pragma unroll
+        for (int kk = 0; kk < Sh::MAXD; ++kk)
+          if (kk == lg) bb = part_diag_block(NB, part, kk);
         const float *At = sAtd + lg * 16 * LDD;
-#pragma unroll
-        for (int s = 0; s < 15; ++s)
-#pragma unroll
-          for (int qd = 0; qd < 4; ++qd)
-            if (4 * qd + 3 > s) at[s][qd] = *reinterpret_cast<const f32x4 *>(At + s * LDD + 4 * qd);
+        float x[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) x[r] = (r == li) ? 1.f : 0.f;
 #pragma unroll
         for (int s = 0; s < 15; ++s) {
+          f32x4 colv[4];
 #pragma unroll
-          for (int r = s + 1; r < 16; ++r) x[r] = fmaf(-at[s][r >> 2][r & 3], x[s], x[r]);
+          for (int qd = 0; qd < 4; ++qd)
+            if (4 * qd + 3 > s) colv[qd] = *reinterpret_cast<const f32x4 *>(At + s * LDD + 4 * qd);
+#pragma unroll
+          for (int r = s + 1; r < 16; ++r) x[r] = fmaf(-colv[r >> 2][r & 3], x[s], x[r]);
         }
-        float *Td = sTd + lg * 16 * LDD;
+        // T_bb transposed: row li of T^T = column li of T
+        float *dst = Td + (bb * 16 + li) * LDD;
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd)
+          *reinterpret_cast<f32x4 *>(dst + 4 * qd) = f32x4{x[4 * qd], x[4 * qd + 1], x[4 * qd + 2], x[4 * qd + 3]};
+      }
+    };
+
+    if (nch > 0) fetch(0);
+    __syncthreads();
+    for (int i = -2; i <= nch; ++i) {
+      const int c = i + 2;
+      if (c >= 0 && c < nch) {
+        produce(c);
+        if (c + 1 < nch) fetch(c + 1);
+      }
+      lds_barrier();
+    }
+  } else if (wave == TSOLVE) {
+    // =================== T' of chunk i+1 ======================================
+    // T' = T Diag(beta); diagonal blocks of T come from the Gram waves, the
+    // off-diagonal blocks are built level by level: T_ij = -T_ii sum_m A_im T_mj
+    auto solve = [&](int c) {
+      E *Tp = sTp(c);
+      const E *Ablk = sA(c);
+      const float *Td = sTd(c);
+      const float *beta = sVec(c) + 3 * C;
+      // diagonal blocks: lane = (block lg, column li)
+      if (lg < NB) {
+        const float *src = Td + (lg * 16 + li) * LDD;
+        const float bs = beta[16 * lg + li];
         const int pc = O::perm(16 * lg + li);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          Td[r * LDD + li] = x[r];
-          // T' = T Diag(beta): column 16 lg + li scaled by that row's beta (= this lane's)
-          sTp[(16 * lg + r) * LDC + pc] = Elem<E>::from_f32(x[r] * beta);
+        for (int qd = 0; qd < 4; ++qd) {
+          const f32x4 t4 = *reinterpret_cast<const f32x4 *>(src + 4 * qd);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) Tp[(16 * lg + 4 * qd + e) * LDC + pc] = Elem<E>::from_f32(t4[e] * bs);
         }
       }
-      // off-diagonal blocks, level by level: T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj
       if constexpr (NB > 1) {
         f32x4 Toff[NB][NB];
 #pragma unroll
@@ -640,140 +791,134 @@ __global__ __launch_bounds__(64 * (NBW + 2)) void kla_chunk_kernel(ChunkParams p
 #pragma unroll
             for (int m = j; m < i; ++m) {
               float a[4], bb[4];
-              const f32x4 a4 = load4(sA + (16 * i + li) * LDC + 16 * m + 4 * lg);
+              const f32x4 a4 = load4(Ablk + (i * (i - 1) / 2 + m) * 16 * LDA + li * LDA + 4 * lg);
 #pragma unroll
               for (int e = 0; e < 4; ++e) a[e] = a4[e];
               if (m == j) {
+                // B operand T_jj[4lg + e][li] = T_jj^T[li][4lg + e]
+                const f32x4 t4 = *reinterpret_cast<const f32x4 *>(Td + (j * 16 + li) * LDD + 4 * lg);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) bb[e] = sTd[j * 16 * LDD + (4 * lg + e) * LDD + li];
+                for (int e = 0; e < 4; ++e) bb[e] = t4[e];
               } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) bb[e] = Toff[m][j][e];
               }
               y = Mm16<E>::mma(a, bb, y);
             }
+            // A operand T_ii[li][4lg + e] = T_ii^T[4lg + e][li]
             float a[4], bb[4];
-            const f32x4 t4 = *reinterpret_cast<const f32x4 *>(sTd + i * 16 * LDD + li * LDD + 4 * lg);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              a[e] = t4[e];
+              a[e] = Td[(i * 16 + 4 * lg + e) * LDD + li];
               bb[e] = y[e];
             }
             const f32x4 t = Mm16<E>::mma(a, bb, zero4());
             Toff[i][j] = -t;
-            const float bs = sBetaK[16 * j + li];
+            const float bs = beta[16 * j + li];
             const int pc = O::perm(16 * j + li);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) sTp[(16 * i + 4 * lg + e) * LDC + pc] = Elem<E>::from_f32(-t[e] * bs);
+            for (int e = 0; e < 4; ++e) Tp[(16 * i + 4 * lg + e) * LDC + pc] = Elem<E>::from_f32(-t[e] * bs);
           }
         }
       }
-      if (c + 1 < nch) fetch(c + 1);
     };
-
-    if (nch > 0) {
-      fetch(0);
-      produce(0, 0);
-    }
     __syncthreads();
-    for (int c = 0; c < nch; ++c) {
-      if (c + 1 < nch) produce(c + 1, (c + 1) & 1);
+    for (int i = -2; i <= nch; ++i) {
+      if (i + 1 >= 0 && i + 1 < nch) solve(i + 1);
       lds_barrier();
     }
-  } else {
-    // ======================= Q wave ==========================================
-    constexpr int V16 = 16 / (int)sizeof(E);  // elements per 16-byte piece
-    constexpr int PPR = DVT / V16;            // 16-byte pieces per V row slice
-    constexpr int NVP = (C * PPR + 63) / 64;  // V pieces per lane
-    Nat qop[NB][KSTEPS], kop[NB][KSTEPS];
-    uint4 vreg[NVP];
-    E qg_raw = Elem<E>::from_f32(0.f);
-    const size_t vcol0 = (size_t)jt * DVT;
+  } else if (wave == PW0 || wave == PW1) {
+    // =================== P waves: causal scores of chunk i ====================
+    const int part = wave - PW0;
+    Grp qreg[NB][NQG];
     auto fetch = [&](int c) {
-      const int nrow = min(C, len - c * C);
-      const size_t tok0 = row0 + (size_t)c * C;
+      const int nrow = nrow_of(c);
+      const size_t tok0 = tok0_of(c);
 #pragma unroll
       for (int rt = 0; rt < NB; ++rt) {
-        const int r = min(16 * rt + li, nrow - 1);
+        if (!part_uses_row(NB, part, rt)) continue;
+        const E *row = gq + (tok0 + min(16 * rt + li, nrow - 1)) * DK;
 #pragma unroll
-        for (int kq = 0; kq < KSTEPS; ++kq) {
-          qop[rt][kq] = O::ldg(gq + (tok0 + r) * DK + kq * KSTEP + lg * VPL);
-          kop[rt][kq] = O::ldg(gk + (tok0 + r) * DK + kq * KSTEP + lg * VPL);
-        }
+        for (int q = 0; q < NQG; ++q) qreg[rt][q] = O::ldg_grp(row, q * KG, lg);
       }
-#pragma unroll
-      for (int i = 0; i < NVP; ++i) {
-        const int pc = min(lane + 64 * i, C * PPR - 1);
-        const int r = min(pc / PPR, nrow - 1), cq = pc % PPR;
-        vreg[i] = ldg16(gv + (tok0 + r) * (size_t)dv + vcol0 + cq * V16);
-      }
-      qg_raw = gg[tok0 + min(lane, nrow - 1)];
     };
-
-    auto produce = [&](int c, int nb) {
-      E *sQ = bufE(nb) + Sh::OFF_Q;
-      E *sV = bufE(nb) + Sh::OFF_V;
-      E *sP = bufE(nb) + Sh::OFF_P;
-      const int nrow = min(C, len - c * C);
-#pragma unroll
-      for (int rt = 0; rt < NB; ++rt) {
-        const int r = 16 * rt + li;
-#pragma unroll
-        for (int kq = 0; kq < KSTEPS; ++kq) {
-          if (r >= nrow) {
-            qop[rt][kq] = O::zero();
-            kop[rt][kq] = O::zero();
-          }
-          O::st_nat(sQ + r * LDK, kq, lg, qop[rt][kq]);
-        }
-      }
-      // V slice [C x DVT], row-major
-#pragma unroll
-      for (int i = 0; i < NVP; ++i) {
-        const int pc = lane + 64 * i;
-        if (pc < C * PPR) {
-          const int r = pc / PPR, cq = pc % PPR;
-          const uint4 u = (r < nrow) ? vreg[i] : make_uint4(0u, 0u, 0u, 0u);
-          *reinterpret_cast<uint4 *>(sV + r * LDV + cq * V16) = u;
-        }
-      }
-      const float gam = wave_inclusive_scan((lane < nrow) ? Elem<E>::to_f32(qg_raw) : 0.f);
-      if (lane < C) sGamQ[lane] = gam;
+    auto produce = [&](int c) {
+      const int nrow = nrow_of(c);
+      const E *K = sK(c);
+      E *Pm = sP(c);
+      const float *gamv = sVec(c);
       f32x4 gr4[NB];
       float gs1[NB];
 #pragma unroll
       for (int rt = 0; rt < NB; ++rt) {
-        gr4[rt] = *reinterpret_cast<const f32x4 *>(sGamQ + 16 * rt + 4 * lg);
-        gs1[rt] = sGamQ[16 * rt + li];
+        gr4[rt] = *reinterpret_cast<const f32x4 *>(gamv + 16 * rt + 4 * lg);
+        gs1[rt] = gamv[16 * rt + li];
       }
-      // causal scores P = (Q K^T) weighted by exp(gamma_r - gamma_s), r >= s
 #pragma unroll
       for (int rt = 0; rt < NB; ++rt) {
+        if (!part_uses_row(NB, part, rt)) continue;
+        if (16 * rt + li >= nrow)
+#pragma unroll
+          for (int q = 0; q < NQG; ++q) qreg[rt][q] = O::zero_grp();
 #pragma unroll
         for (int st = 0; st <= rt; ++st) {
+          if (tile_part(NB, rt, st) != part) continue;
           f32x4 acc = zero4();
 #pragma unroll
-          for (int kq = 0; kq < KSTEPS; ++kq) acc = O::mma(qop[rt][kq], kop[st][kq], acc);
+          for (int q = 0; q < NQG; ++q) acc = O::mma_grp(qreg[rt][q], O::a_row(K + (16 * st + li) * LDK, q * KG, lg), acc);
           const int s = 16 * st + li;
           const int pc = O::perm(s);
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int r = 16 * rt + 4 * lg + j;
             const float val = (r >= s) ? acc[j] * __expf(gr4[rt][j] - gs1[st]) : 0.f;
-            sP[r * LDC + pc] = Elem<E>::from_f32(val);
+            Pm[r * LDC + pc] = Elem<E>::from_f32(val);
           }
         }
       }
-      if (c + 1 < nch) fetch(c + 1);
     };
-
-    if (nch > 0) {
-      fetch(0);
-      produce(0, 0);
-    }
     __syncthreads();
-    for (int c = 0; c < nch; ++c) {
-      if (c + 1 < nch) produce(c + 1, (c + 1) & 1);
+    for (int i = -2; i <= nch; ++i) {
+      if (i >= 0 && i < nch) produce(i);
+      if (i + 1 >= 0 && i + 1 < nch) fetch(i + 1);
+      lds_barrier();
+    }
+  } else {
+    // =================== V loader: V slice of chunk i+1 =======================
+    constexpr int V16 = 16 / (int)sizeof(E);  // elements per 16-byte piece
+    constexpr int PPR = DVT / V16;            // 16-byte pieces per V row slice
+    constexpr int NVP = (C * PPR + 63) / 64;  // pieces per lane
+    uint4 vreg[NVP];
+    const size_t vcol0 = (size_t)jt * DVT;
+    auto fetch = [&](int c) {
+      const int nrow = nrow_of(c);
+      const size_t tok0 = tok0_of(c);
+#pragma unroll
+      for (int k = 0; k < NVP; ++k) {
+        const int pc = min(lane + 64 * k, C * PPR - 1);
+        const int r = min(pc / PPR, nrow - 1), cq = pc % PPR;
+        vreg[k] = ldg16(gv + (tok0 + r) * (size_t)dv + vcol0 + cq * V16);
+      }
+    };
+    auto store = [&](int c) {
+      const int nrow = nrow_of(c);
+      E *V = sV(c);
+#pragma unroll
+      for (int k = 0; k < NVP; ++k) {
+        const int pc = lane + 64 * k;
+        if (pc < C * PPR) {
+          const int r = pc / PPR, cq = pc % PPR;
+          *reinterpret_cast<uint4 *>(V + r * LDV + cq * V16) = (r < nrow) ? vreg[k] : make_uint4(0u, 0u, 0u, 0u);
+        }
+      }
+    };
+    if (nch > 0) fetch(0);
+    __syncthreads();
+    for (int i = -2; i <= nch; ++i) {
+      if (i + 1 >= 0 && i + 1 < nch) {
+        store(i + 1);
+        if (i + 2 < nch) fetch(i + 2);
+      }
       lds_barrier();
     }
   }
@@ -782,9 +927,9 @@ __global__ __launch_bounds__(64 * (NBW + 2)) void kla_chunk_kernel(ChunkParams p
 // ---------------------------------------------------------------------------
 // host-side dispatch
 // ---------------------------------------------------------------------------
-template <typename E, int C, int DK, int NBW>
+template <typename E, int C, int DK, int NCT>
 static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t st) {
-  using Sh = ChunkShape<E, C, DK, NBW>;
+  using Sh = ChunkShape<E, C, DK, NCT>;
   ChunkParams p;
   p.q = a.q;
   p.k = a.k;
@@ -803,7 +948,7 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t st) {
   const long long nblk = (long long)a.num_seqs * a.H * p.n_tiles;
   p.remap = (nblk % 8 == 0) ? 1 : 0;
   if (nblk == 0) return hipSuccess;
-  hipLaunchKernelGGL((kla_chunk_kernel<E, C, DK, NBW>), dim3((unsigned)nblk), dim3(Sh::NT), 0, st, p);
+  hipLaunchKernelGGL((kla_chunk_kernel<E, C, DK, NCT>), dim3((unsigned)nblk), dim3(Sh::NT), 0, st, p);
   return hipGetLastError();
 }
 
@@ -819,16 +964,16 @@ bool chunk_supported(int dtype, int dk, int dv, int chunk) {
   return false;
 }
 
-// Column slice width: 32 columns (2 scan waves) when that still gives at
-// least one workgroup per CU, else 16 (more workgroups, more redundant
-// S-independent work per column).
-static bool use_two_scan_waves(const ChunkArgs &a) {
+// Column slice width: 32 columns (two column tiles per workgroup) when that
+// still gives at least one workgroup per CU, else 16 (more workgroups, more
+// redundant S-independent work per column).
+static bool use_two_column_tiles(const ChunkArgs &a) {
   return a.dv % 32 == 0 && (long long)a.num_seqs * a.H * (a.dv / 32) >= 256;
 }
 
 hipError_t launch_chunk_fwd(const ChunkArgs &a, hipStream_t st) {
   if (a.dtype == 0) {
-    const bool two = use_two_scan_waves(a);
+    const bool two = use_two_column_tiles(a);
     if (a.dk == 128) return two ? launch_chunk_t<bf16, 64, 128, 2>(a, st) : launch_chunk_t<bf16, 64, 128, 1>(a, st);
     if (a.dk == 64) return two ? launch_chunk_t<bf16, 64, 64, 2>(a, st) : launch_chunk_t<bf16, 64, 64, 1>(a, st);
     return hipErrorInvalidValue;
