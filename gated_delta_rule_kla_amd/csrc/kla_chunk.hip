@@ -23,27 +23,29 @@
 // applied before the exponential.
 //
 // Mapping onto the chip.  One workgroup owns one (sequence, head, slice of
-// DVT = 16 NBW state columns) and walks that sequence's chunks in order.  The
-// state slice never leaves the chip: it lives in MFMA accumulators of the NBW
-// "scan" waves (16 columns each, fp32) for the whole sequence.  Two
-// "producer" waves build the S-independent data of chunk c+1 while the scan
-// waves consume chunk c (double-buffered LDS, one barrier per chunk):
-//   * the K wave: K (16-byte loads straight into MFMA operand layout,
-//     prefetched one chunk ahead), the fused ||k||^2 reduction and beta, the
-//     gate scan, K K^T on MFMA, A, and the 64x64 unit-lower-triangular solve
-//     done blockwise: the four 16x16 diagonal blocks by column-parallel
-//     forward substitution in fp32 (lane = block x column), the off-diagonal
-//     blocks by 16x16x16 MFMA products T_ij = -T_ii sum_m A_im T_mj;
-//   * the Q wave: Q and the V slice, Q K^T on MFMA and the causal tile P.
-// The scan waves never round-trip their own data through LDS: every right
-// operand (S, X, U~, Diag(d) U~) is fed to the next MFMA straight from the
-// accumulator registers, by ordering each instruction's contraction index
-// the way the accumulator layout holds it (see Ops below).  The matching left
-// operands (K, Q, T', P rows) are stored by the producers with their columns
-// permuted into that order, so each is one 16-byte LDS read; K^T and the V
-// slice are read from row-major tiles with gfx950's transposing LDS read.
+// DVT = 16 NCT state columns) and walks that sequence's chunks in order.  The
+// state slice never leaves the chip: it lives in the MFMA accumulators of the
+// chain wave (fp32) for the whole sequence.  Seven role-specialised waves form
+// a software pipeline over the chunks with one LDS-only barrier per step (see
+// "Roles and LDS plan" below): the S-independent work of a chunk -- gate scan,
+// ||k||^2 and beta, K K^T and A (Gram waves), the blockwise triangular solve
+// for T' (T-solve wave) -- runs two and one steps ahead of the chain, and the
+// P waves form the causal scores and the output rows.
+//
+// Every K and Q row is read with coalesced 16-byte buffer loads and goes
+// through LDS into the MFMA operand layout: loads that give each lane its own
+// row (the operand layout) cost the texture-address unit four times more.
+// The chain never round-trips its own data through LDS: every right operand
+// (S, X, U~, Diag(d) U~) is fed to the next MFMA straight from the accumulator
+// registers, by ordering each instruction's contraction index the way the
+// accumulator layout holds it (see Ops below); the matching left operands (K
+// and Q rows) are stored with their columns permuted into that order, and K^T,
+// T' (stored transposed) and the V slice are read with gfx950's transposing
+// LDS read.
 #include "kla_common.h"
 #include "kla_internal.h"
+
+#include <type_traits>
 
 namespace kla {
 
@@ -80,10 +82,14 @@ template <> struct Ops<bf16> {
     for (int x = 0; x < 8; ++x) r[x] = (bf16)0.f;
     return r;
   }
+  // sum of squares of the 8 values: bf16 products are exact in fp32
   static __device__ __forceinline__ float sumsq(Nat v) {
     float s = 0.f;
 #pragma unroll
-    for (int x = 0; x < 8; ++x) s = fmaf((float)v[x], (float)v[x], s);
+    for (int x = 0; x < 4; ++x) {
+      const bf16x2 pr = {v[2 * x], v[2 * x + 1]};
+      s = __builtin_amdgcn_fdot2_f32_bf16(pr, pr, s, false);
+    }
     return s;
   }
   // column position inside a row stored in grouped order: inside each block of
@@ -97,6 +103,10 @@ template <> struct Ops<bf16> {
     const bf16x4 lo = {v[0], v[1], v[2], v[3]}, hi = {v[4], v[5], v[6], v[7]};
     *reinterpret_cast<bf16x4 *>(row + perm(c0)) = lo;
     *reinterpret_cast<bf16x4 *>(row + perm(c0 + 4)) = hi;
+  }
+  // store one 16-byte piece (natural columns 8m .. 8m+7) into a grouped row
+  static __device__ __forceinline__ void st_piece(bf16 *row, int m, uint4 v) {
+    st_nat(row, m >> 2, m & 3, __builtin_bit_cast(Nat, v));
   }
   // B group from the D tiles of rows kb..kb+31
   static __device__ __forceinline__ Grp b_from_d(const f32x4 *d) {
@@ -156,6 +166,9 @@ template <> struct Ops<float> {
   static __device__ __forceinline__ float sumsq(Nat v) { return v * v; }
   static __device__ __forceinline__ int perm(int c) { return c; }
   static __device__ __forceinline__ void st_nat(float *row, int kq, int g, Nat v) { row[kq * 4 + g] = v; }
+  static __device__ __forceinline__ void st_piece(float *row, int m, uint4 v) {
+    *reinterpret_cast<f32x4 *>(row + 4 * m) = __builtin_bit_cast(f32x4, v);
+  }
   static __device__ __forceinline__ Grp b_from_d(const f32x4 *d) { return d[0]; }
   static __device__ __forceinline__ Grp a_row(const float *row, int kb, int g) {
     return *reinterpret_cast<const f32x4 *>(row + kb + 4 * g);
@@ -186,30 +199,39 @@ template <> struct Ops<float> {
 template <typename E> struct Mm16;
 
 template <> struct Mm16<bf16> {
-  static __device__ __forceinline__ f32x4 mma(const float *a, const float *b, f32x4 c) {
-    bf16x4 av, bv;
-#pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      av[x] = (bf16)a[x];
-      bv[x] = (bf16)b[x];
-    }
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bv, c, 0, 0, 0);
+  typedef bf16x4 Op;
+  // left operand of a 16x16 block stored transposed (Mt[k][row]): one
+  // transposing LDS read gives lane l the entries [l&15][4(l>>4) .. +3]
+  static __device__ __forceinline__ Op ld_t(const bf16 *Mt, int ld, int lane) {
+    const int g = lane >> 4, x = (lane >> 2) & 3, a = lane & 3;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(Mt + (4 * g + x) * ld + 4 * a));
+  }
+  static __device__ __forceinline__ Op cvt(f32x4 v) { return Op{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]}; }
+  static __device__ __forceinline__ f32x4 mma(Op a, Op b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
   }
 };
 
 template <> struct Mm16<float> {
-  static __device__ __forceinline__ f32x4 mma(const float *a, const float *b, f32x4 c) {
+  typedef f32x4 Op;
+  static __device__ __forceinline__ Op ld_t(const float *Mt, int ld, int lane) {
+    const int g = lane >> 4, li = lane & 15;
+    return Op{Mt[(4 * g) * ld + li], Mt[(4 * g + 1) * ld + li], Mt[(4 * g + 2) * ld + li], Mt[(4 * g + 3) * ld + li]};
+  }
+  static __device__ __forceinline__ Op cvt(f32x4 v) { return v; }
+  static __device__ __forceinline__ f32x4 mma(Op a, Op b, f32x4 c) {
 #pragma unroll
     for (int x = 0; x < 4; ++x) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[x], b[x], c, 0, 0, 0);
     return c;
   }
 };
 
-__device__ __forceinline__ f32x4 load4(const bf16 *p) {
-  bf16x4 b = *reinterpret_cast<const bf16x4 *>(p);
-  return f32x4{(float)b[0], (float)b[1], (float)b[2], (float)b[3]};
+// four consecutive elements from fp32
+__device__ __forceinline__ void store4(bf16 *p, f32x4 v) {
+  *reinterpret_cast<bf16x4 *>(p) = bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
 }
-__device__ __forceinline__ f32x4 load4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
+__device__ __forceinline__ void store4(float *p, f32x4 v) { *reinterpret_cast<f32x4 *>(p) = v; }
+
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
 // Inclusive prefix sum over the 64 lanes of a wave: Hillis-Steele with DPP
@@ -241,34 +263,37 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 // ---------------------------------------------------------------------------
 // Roles and LDS plan
 // ---------------------------------------------------------------------------
-// Waves of a workgroup.  Iteration i (one barrier each, i = -2 .. nch) has
-//   CHAIN  scan chunk i        OUTPUT  chunk i-1       PWAVE[2]  P of chunk i
-//   TSOLVE T' of chunk i+1     VLOAD   V of chunk i+1  GRAM[2]   chunk i+2
-enum Role { CHAIN = 0, OUTPUT = 1, GRAM0 = 2, GRAM1 = 3, TSOLVE = 4, PW0 = 5, PW1 = 6, VLOAD = 7 };
-constexpr int kWaves = 8;
+// Waves of a workgroup.  Step i (one barrier each, i = -2 .. nch) has
+//   CHAIN    the state scan of chunk i
+//   PW[2]    causal scores and Diag(Gam) Q S of chunk i; output of chunk i-1
+//   TSOLVE   T' of chunk i+1
+//   GRAM[2]  gate scan, ||k||^2, beta and A of chunk i+2
+//   VLOAD    the V slice of chunk i+1
+// Waves w and w+4 share a SIMD, so the order pairs heavy roles with light
+// ones and leaves the T' solve (a long dependency chain) a SIMD of its own.
+enum Role { CHAIN = 0, PW0 = 1, PW1 = 2, TSOLVE = 3, VLOAD = 4, GRAM0 = 5, GRAM1 = 6 };
+constexpr int kWaves = 7;
 
-// lower-triangular 16x16 tile (rt, st), st <= rt, in row-major order; the two
-// Gram waves and the two P waves each take one half of the list
-__host__ __device__ constexpr int tile_index(int rt, int st) { return rt * (rt + 1) / 2 + st; }
-__host__ __device__ constexpr int tile_part(int NB, int rt, int st) {
-  return tile_index(rt, st) < (NB * (NB + 1) / 2 + 1) / 2 ? 0 : 1;
+// The 16-row blocks of a chunk are split between the two Gram waves and, the
+// same way, between the two P waves: part 0 owns the first and the last block,
+// part 1 the ones in between.  A wave handles the lower-triangular tiles
+// (rt, st <= rt) of the row blocks rt it owns (5 of the 10 tiles each for a
+// 64-token chunk), so the diagonal tiles -- and with them ||k_r||^2 and
+// beta_r -- of all its rows are its own.  Chunks of 16 (one block) leave
+// part 1 idle.
+__host__ __device__ constexpr bool owns_block(int NB, int part, int rt) {
+  return (rt == 0 || rt == NB - 1) ? part == 0 : part == 1;
 }
-__host__ __device__ constexpr bool part_uses_row(int NB, int part, int rt) {
-  for (int st = 0; st <= rt; ++st)
-    if (tile_part(NB, rt, st) == part) return true;
-  return false;
-}
-// diagonal blocks owned by a Gram wave, in order
-__host__ __device__ constexpr int part_diag_count(int NB, int part) {
-  int n = 0;
-  for (int b = 0; b < NB; ++b) n += (tile_part(NB, b, b) == part);
-  return n;
-}
-__host__ __device__ constexpr int part_diag_block(int NB, int part, int k) {
-  for (int b = 0; b < NB; ++b)
-    if (tile_part(NB, b, b) == part && k-- == 0) return b;
-  return -1;
-}
+template <int NB, int PART>
+struct OwnBlocks {  // the blocks a part owns, in order
+  static constexpr int N = PART == 0 ? (NB > 1 ? 2 : 1) : NB - 2;
+  static __host__ __device__ constexpr int at(int k) { return PART == 0 ? (k == 0 ? 0 : NB - 1) : 1 + k; }
+};
+template <int NB, int PART>
+struct GramBlocks {  // the blocks a Gram wave reads: 0 .. (largest owned block)
+  static constexpr int N = PART == 0 ? NB : NB - 1;
+  static __host__ __device__ constexpr int at(int k) { return k; }
+};
 
 template <typename E, int C, int DK, int NCT>
 struct ChunkShape {
@@ -276,47 +301,93 @@ struct ChunkShape {
   static constexpr int DVT = 16 * NCT;         // state columns per workgroup
   static constexpr int NT = 64 * kWaves;
   static constexpr int PAD = 16 / (int)sizeof(E);
-  static constexpr int LDK = DK + PAD;         // K rows (grouped columns)
-  static constexpr int LDC = C + PAD;          // T' and P rows (grouped columns)
+  static constexpr int LDK = DK + PAD;         // K and Q rows (grouped columns)
+  static constexpr int LDC = C + PAD;          // T'^T rows (grouped columns)
   static constexpr int LDV = DVT + PAD;        // V slice rows (natural)
-  static constexpr int LDA = 16 + PAD;         // rows of one 16x16 off-diagonal A block
+  static constexpr int LDA = 16 + PAD;         // rows of one 16x16 off-diagonal A^T block
   static constexpr int LDD = 20;               // fp32 16-wide rows of diagonal blocks
   static constexpr int KG = Ops<E>::KG;
   static constexpr int NOFF = NB * (NB - 1) / 2;
-  static constexpr int MAXD = (NB + 1) / 2;    // diagonal blocks per Gram wave
+  static constexpr int MAXOWN = NB > 1 ? 2 : 1;        // row blocks per P wave
+  static constexpr int LOS = MAXOWN * 16 + PAD;        // rows of O^T staging
   // sizes in bytes
   static constexpr int K_SLOT = C * LDK * (int)sizeof(E);
   static constexpr int V_SLOT = C * LDV * (int)sizeof(E);
   static constexpr int TP_SLOT = C * LDC * (int)sizeof(E);
-  static constexpr int P_SLOT = C * LDC * (int)sizeof(E);
-  static constexpr int SU_S = NCT * (DK / KG) * 64 * 16;   // S start groups, 16 B per lane
+  static constexpr int SU_S = NCT * (DK / KG) * 64 * 16;   // chunk-start S groups, 16 B per lane
   static constexpr int SU_U = NCT * (C / KG) * 64 * 16;    // U~ groups
   static constexpr int SU_SLOT = SU_S + SU_U;
   static constexpr int A_SLOT = (NOFF > 0 ? NOFF : 1) * 16 * LDA * (int)sizeof(E);
-  static constexpr int TD_SLOT = NB * 16 * LDD * 4;        // T diagonal blocks, transposed, fp32
+  static constexpr int TD_SLOT = NB * 16 * LDD * 4;        // diagonal blocks (A, then T), transposed, fp32
   static constexpr int VEC_SLOT = 4 * C * 4;               // gamma, Gam, d, beta
-  static constexpr int GPRIV = MAXD * 16 * LDD * 4 + NB * 64 * 4 + 2 * C * 4;  // At blocks, norm partials, gamma/beta
-  static constexpr int OT_BYTES = (sizeof(E) == 2 ? NCT : 0) * 16 * LDC * (int)sizeof(E);
+  static constexpr int GPRIV = 3 * C * 4;                  // per Gram wave: gamma, ||k||^2, beta
+  static constexpr int QST = MAXOWN * 16 * LDK * (int)sizeof(E);   // per P wave: its Q rows
+  static constexpr int OST = (sizeof(E) == 2 ? DVT * LOS : 0) * (int)sizeof(E);  // per P wave: O^T staging
+  static constexpr int GE_SLOT = 2 * C * 4;                // g and eta of a chunk, fp32
   // offsets
   static constexpr int OFF_K = 0;
   static constexpr int OFF_V = OFF_K + 3 * K_SLOT;
   static constexpr int OFF_TP = OFF_V + 2 * V_SLOT;
-  static constexpr int OFF_P = OFF_TP + 2 * TP_SLOT;
-  static constexpr int OFF_SU = OFF_P + 2 * P_SLOT;
+  static constexpr int OFF_SU = OFF_TP + 2 * TP_SLOT;
   static constexpr int OFF_A = OFF_SU + 2 * SU_SLOT;
   static constexpr int OFF_TD = OFF_A + 2 * A_SLOT;
   static constexpr int OFF_VEC = OFF_TD + 2 * TD_SLOT;
-  static constexpr int OFF_GP = OFF_VEC + 4 * VEC_SLOT;
-  static constexpr int OFF_OT = OFF_GP + 2 * GPRIV;
-  static constexpr int BYTES = OFF_OT + OT_BYTES;
+  static constexpr int OFF_GP = OFF_VEC + 3 * VEC_SLOT;
+  static constexpr int OFF_QS = OFF_GP + 2 * GPRIV;
+  static constexpr int OFF_OS = OFF_QS + 2 * QST;
+  static constexpr int OFF_GE = OFF_OS + 2 * OST;
+  static constexpr int BYTES = OFF_GE + 2 * GE_SLOT;
 
   static_assert(C == 16 || C == 64, "chunk");
   static_assert(C % KG == 0 && DK % KG == 0 && DK % Ops<E>::KSTEP == 0, "dk");
   static_assert(K_SLOT % 16 == 0 && V_SLOT % 16 == 0 && TP_SLOT % 16 == 0 && A_SLOT % 16 == 0 &&
-                    GPRIV % 16 == 0 && VEC_SLOT % 16 == 0 && OT_BYTES % 16 == 0, "lds align");
+                    GPRIV % 16 == 0 && VEC_SLOT % 16 == 0 && QST % 16 == 0 && OST % 16 == 0, "lds align");
   static_assert((LDK * (int)sizeof(E)) % 16 == 0 && (LDC * (int)sizeof(E)) % 16 == 0 &&
-                    (LDV * (int)sizeof(E)) % 16 == 0 && (LDA * (int)sizeof(E)) % 8 == 0, "row align");
+                    (LDV * (int)sizeof(E)) % 16 == 0 && (LDA * (int)sizeof(E)) % 8 == 0 &&
+                    (LOS * (int)sizeof(E)) % 8 == 0, "row align");
   static_assert(BYTES <= 160 * 1024, "LDS budget");
+};
+
+// Raw buffer resource over bytes [0, n) of p: loads at offsets >= n return 0
+// (that is how rows past the end of a sequence read as zero rows).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *p, int n) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, n, 0x00020000);
+}
+__device__ __forceinline__ uint4 buffer_ld16(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// Coalesced loads of whole K or Q rows of one chunk: lane l takes the 16-byte
+// pieces l, l + 64, ... of the listed row blocks, so consecutive lanes read
+// consecutive bytes of a row (a wave instruction touches 4 rows of 256 B
+// rather than 16 rows).  The rows then go through LDS into the MFMA operand
+// layout, where each lane holds one row.
+template <typename E, int DK, class BL>
+struct RowLoad {
+  static constexpr int RB = DK * (int)sizeof(E);   // bytes per row
+  static constexpr int PPR = RB / 16;              // 16-byte pieces per row
+  static constexpr int RPJ = 64 / PPR;             // rows per wave instruction
+  static constexpr int NPL = BL::N * 16 / RPJ;     // instructions (pieces per lane)
+  static_assert(PPR >= 4 && 64 % PPR == 0, "row size");
+  uint4 r[NPL > 0 ? NPL : 1];
+  // list row of piece j of this lane: RPJ j + lane / PPR; chunk row:
+  static __device__ __forceinline__ int chunk_row(int j, int lane) {
+    return 16 * BL::at((RPJ * j) >> 4) + ((RPJ * j) & 15) + lane / PPR;
+  }
+  // chunk rows start at `rows`; rows >= nrow read as zero
+  __device__ __forceinline__ void issue(const E *rows, int nrow, int lane) {
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(rows, nrow * RB);
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) r[j] = buffer_ld16(rs, chunk_row(j, lane) * RB + (lane % PPR) * 16);
+  }
+  // store the rows in grouped column order; list row lr / chunk row cr goes
+  // to row dst_row(lr, cr) of dst
+  template <class RowMap>
+  __device__ __forceinline__ void put(E *dst, int ld, int lane, RowMap dst_row) const {
+#pragma unroll
+    for (int j = 0; j < NPL; ++j)
+      Ops<E>::st_piece(dst + dst_row(RPJ * j + lane / PPR, chunk_row(j, lane)) * ld, lane % PPR, r[j]);
+  }
 };
 
 struct ChunkParams {
@@ -336,11 +407,10 @@ template <typename E, int C, int DK, int NCT>
 __global__ __launch_bounds__(64 * kWaves) void kla_chunk_kernel(ChunkParams p) {
   using Sh = ChunkShape<E, C, DK, NCT>;
   using O = Ops<E>;
-  using Nat = typename O::Nat;
   using Grp = typename O::Grp;
   constexpr int NB = Sh::NB, DVT = Sh::DVT, LDK = Sh::LDK, LDC = Sh::LDC, LDV = Sh::LDV;
-  constexpr int LDA = Sh::LDA, LDD = Sh::LDD;
-  constexpr int KSTEP = O::KSTEP, VPL = O::VPL, KSTEPS = DK / KSTEP, KG = O::KG, TPG = KG / 16;
+  constexpr int LDA = Sh::LDA, LDD = Sh::LDD, LOS = Sh::LOS;
+  constexpr int KG = O::KG, TPG = KG / 16;
   constexpr int NQG = DK / KG;  // contraction groups over dk
   constexpr int NCG = C / KG;   // contraction groups over the chunk
 
@@ -376,12 +446,25 @@ __global__ __launch_bounds__(64 * kWaves) void kla_chunk_kernel(ChunkParams p) {
   const int dv = p.dv;
   auto nrow_of = [&](int c) { return min(C, len - c * C); };
   auto tok0_of = [&](int c) { return row0 + (size_t)c * C; };
+  // a prefetch past the last chunk re-reads the last chunk
+  auto clampc = [&](int c) { return min(max(c, 0), nch - 1); };
+
+  if (nch == 0) {
+    // empty sequence: the final state is the initial state
+    if (p.sfin) {
+      const size_t sbase = (size_t)nh * DK * (size_t)dv;
+      for (int e = threadIdx.x; e < DK * DVT; e += Sh::NT) {
+        const size_t off = sbase + (size_t)(e / DVT) * dv + (size_t)jt * DVT + (e % DVT);
+        p.sfin[off] = p.s0 ? p.s0[off] : 0.f;
+      }
+    }
+    return;
+  }
 
   // ---- LDS views -------------------------------------------------------------
   auto sK = [&](int c) { return reinterpret_cast<E *>(smem + Sh::OFF_K + (c % 3) * Sh::K_SLOT); };
   auto sV = [&](int c) { return reinterpret_cast<E *>(smem + Sh::OFF_V + (c & 1) * Sh::V_SLOT); };
   auto sTp = [&](int c) { return reinterpret_cast<E *>(smem + Sh::OFF_TP + (c & 1) * Sh::TP_SLOT); };
-  auto sP = [&](int c) { return reinterpret_cast<E *>(smem + Sh::OFF_P + (c & 1) * Sh::P_SLOT); };
   auto sSuS = [&](int c) { return reinterpret_cast<Grp *>(smem + Sh::OFF_SU + (c & 1) * Sh::SU_SLOT); };
   auto sSuU = [&](int c) {
     return reinterpret_cast<Grp *>(smem + Sh::OFF_SU + (c & 1) * Sh::SU_SLOT + Sh::SU_S);
@@ -389,15 +472,15 @@ __global__ __launch_bounds__(64 * kWaves) void kla_chunk_kernel(ChunkParams p) {
   auto sA = [&](int c) { return reinterpret_cast<E *>(smem + Sh::OFF_A + (c & 1) * Sh::A_SLOT); };
   auto sTd = [&](int c) { return reinterpret_cast<float *>(smem + Sh::OFF_TD + (c & 1) * Sh::TD_SLOT); };
   // per-chunk row vectors: gamma, Gam = exp(gamma), d = exp(gamma_C - gamma), beta
-  auto sVec = [&](int c) { return reinterpret_cast<float *>(smem + Sh::OFF_VEC + (c & 3) * Sh::VEC_SLOT); };
+  auto sVec = [&](int c) { return reinterpret_cast<float *>(smem + Sh::OFF_VEC + (c % 3) * Sh::VEC_SLOT); };
+  // g (0 past the sequence end) and eta of a chunk's rows, staged by the V loader
+  auto sGE = [&](int c) { return reinterpret_cast<float *>(smem + Sh::OFF_GE + (c & 1) * Sh::GE_SLOT); };
 
-  // strictly-upper 16x16 blocks of T' and P are zero and never rewritten
+  // strictly-upper 16x16 blocks of T' (strictly-lower ones of the stored
+  // T'^T) are zero and never rewritten
   for (int i = threadIdx.x; i < 2 * C * C; i += Sh::NT) {
     const int bi = i / (C * C), rr = (i / C) % C, ss = i % C;
-    if ((rr >> 4) < (ss >> 4)) {
-      sTp(bi)[rr * LDC + O::perm(ss)] = Elem<E>::from_f32(0.f);
-      sP(bi)[rr * LDC + O::perm(ss)] = Elem<E>::from_f32(0.f);
-    }
+    if ((rr >> 4) > (ss >> 4)) sTp(bi)[rr * LDC + O::perm(ss)] = Elem<E>::from_f32(0.f);
   }
 
   if (wave == CHAIN) {
@@ -415,26 +498,29 @@ __global__ __launch_bounds__(64 * kWaves) void kla_chunk_kernel(ChunkParams p) {
         for (int j = 0; j < 4; ++j)
           accS[ct][it][j] = p.s0 ? p.s0[sbase + (size_t)(16 * it + 4 * lg + j) * dv + col] : 0.f;
     }
+    // chunk-start S as right operands, straight from the accumulators; also
+    // published for the P waves (their Q S of that chunk)
+    Grp sb[NCT][NQG];
+    auto publish = [&](int c) {
+      Grp *suS = sSuS(c);
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int q = 0; q < NQG; ++q) {
+          sb[ct][q] = O::b_from_d(&accS[ct][q * TPG]);
+          suS[(ct * NQG + q) * 64 + lane] = sb[ct][q];
+        }
+    };
     __syncthreads();
     for (int i = -2; i <= nch; ++i) {
+      if (i == -1) publish(0);
       if (i >= 0 && i < nch) {
         const int c = i;
         const E *K = sK(c);
         const E *V = sV(c);
-        const E *Tp = sTp(c);
+        const E *TpT = sTp(c);
         const float *vec = sVec(c);
-        Grp *suS = sSuS(c);
         Grp *suU = sSuU(c);
-        // S as right operands, straight from the accumulators; also handed to
-        // the output wave (it needs the chunk's start state)
-        Grp sb[NCT][NQG];
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-          for (int q = 0; q < NQG; ++q) {
-            sb[ct][q] = O::b_from_d(&accS[ct][q * TPG]);
-            suS[(ct * NQG + q) * 64 + lane] = sb[ct][q];
-          }
         // K S
         f32x4 x[NCT][NB];
 #pragma unroll
@@ -460,7 +546,8 @@ __global__ __launch_bounds__(64 * kWaves) void kla_chunk_kernel(ChunkParams p) {
         for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
           for (int q = 0; q < NCG; ++q) xb[ct][q] = O::b_from_d(&x[ct][q * TPG]);
-        // U~ = T' X   (T' lower triangular: skip the zero groups)
+        // U~ = T' X   (T' lower triangular: skip the zero groups; T' is stored
+        // transposed)
         f32x4 u[NCT][NB];
 #pragma unroll
         for (int rt = 0; rt < NB; ++rt) {
@@ -468,12 +555,12 @@ __global__ __launch_bounds__(64 * kWaves) void kla_chunk_kernel(ChunkParams p) {
           for (int ct = 0; ct < NCT; ++ct) u[ct][rt] = zero4();
 #pragma unroll
           for (int q = 0; q * KG < 16 * (rt + 1); ++q) {
-            const Grp a = O::a_row(Tp + (16 * rt + li) * LDC, q * KG, lg);
+            const Grp a = O::a_trans(TpT, LDC, q * KG, 16 * rt, lane);
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) u[ct][rt] = O::mma_grp(a, xb[ct][q], u[ct][rt]);
           }
         }
-        // U~ groups for the output wave; Diag(d) U~ groups for the update
+        // U~ groups for the P waves; Diag(d) U~ groups for the update
         Grp dub[NCT][NCG];
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct)
@@ -501,6 +588,7 @@ __global__ __launch_bounds__(64 * kWaves) void kla_chunk_kernel(ChunkParams p) {
             for (int ct = 0; ct < NCT; ++ct) accS[ct][it] = O::mma_grp(a, dub[ct][q], accS[ct][it]);
           }
         }
+        if (c + 1 < nch) publish(c + 1);
       }
       lds_barrier();
     }
@@ -514,272 +602,324 @@ __global__ __launch_bounds__(64 * kWaves) void kla_chunk_kernel(ChunkParams p) {
           for (int j = 0; j < 4; ++j) p.sfin[sbase + (size_t)(16 * it + 4 * lg + j) * dv + col] = accS[ct][it][j];
       }
     }
-  } else if (wave == OUTPUT) {
-    // =================== output: O = Diag(Gam) Q S + P U~ =====================
-    // Runs one chunk behind the chain; Q comes straight from global memory in
-    // grouped column order, fetched one iteration ahead.
-    Grp qreg[NB][NQG];
-    auto fetch = [&](int c) {
-      const int nrow = nrow_of(c);
-      const size_t tok0 = tok0_of(c);
+  } else if (wave == PW0 || wave == PW1) {
+    // =================== P waves: scores and output rows ======================
+    // For its row blocks rt, a P wave forms the causal scores of chunk i as
+    // P^T = K Q^T (the accumulator layout of P^T is exactly the left-operand
+    // layout P needs in P U~, so P stays in registers), and Diag(Gam) Q S with
+    // the chunk-start state; one step later, when the chain has U~, it adds
+    // P U~ and writes those output rows.
+    auto pwave = [&](auto part_c) {
+      constexpr int part = decltype(part_c)::value;
+      using BL = OwnBlocks<NB, part>;
+      constexpr int NOWN = BL::N;
+      constexpr int NOW1 = NOWN > 0 ? NOWN : 1;
+      RowLoad<E, DK, BL> qin;
+      E *sQ = reinterpret_cast<E *>(smem + Sh::OFF_QS + part * Sh::QST);
+      E *sO = reinterpret_cast<E *>(smem + Sh::OFF_OS + part * Sh::OST);
+      f32x4 ao[NCT][NOW1];  // output rows of the pending chunk
+      Grp pa[NOW1][NCG];    // its P rows as left operands
+      qin.issue(gq + tok0_of(0) * DK, nrow_of(0), lane);
+      __syncthreads();
+      for (int i = -2; i <= nch; ++i) {
+        // chunk i first, then the output of chunk i-1: its stores then drain
+        // while this wave waits at the barrier
+        f32x4 ao_n[NCT][NOW1];
+        Grp pa_n[NOW1][NCG];
+        if (NOWN > 0 && i >= 0 && i < nch) {
+          // ---- chunk i: P rows and Diag(Gam) Q S ----
+          const int c = i;
+          const int nrow = nrow_of(c);
+          qin.put(sQ, LDK, lane, [](int lr, int) { return lr; });
+          qin.issue(gq + tok0_of(clampc(c + 1)) * DK, nrow_of(clampc(c + 1)), lane);
+          const E *K = sK(c);
+          const float *vec = sVec(c);
+          const Grp *suS = sSuS(c);
+          Grp qa[NOW1][NQG];
 #pragma unroll
-      for (int rt = 0; rt < NB; ++rt) {
-        const E *row = gq + (tok0 + min(16 * rt + li, nrow - 1)) * DK;
+          for (int k = 0; k < NOWN; ++k)
 #pragma unroll
-        for (int q = 0; q < NQG; ++q) qreg[rt][q] = O::ldg_grp(row, q * KG, lg);
-      }
-    };
-    E *sOt = reinterpret_cast<E *>(smem + Sh::OFF_OT);
-    __syncthreads();
-    for (int i = -2; i <= nch; ++i) {
-      if (i >= 1 && i <= nch) {
-        const int c = i - 1;
-        const int nrow = nrow_of(c);
-        const size_t tok0 = tok0_of(c);
-        const E *Pm = sP(c);
-        const Grp *suS = sSuS(c);
-        const Grp *suU = sSuU(c);
-        const float *vec = sVec(c);
+            for (int q = 0; q < NQG; ++q) qa[k][q] = O::a_row(sQ + (16 * k + li) * LDK, q * KG, lg);
+          // P^T tiles: D[s][r] = K_s . q_r, lane column r = 16 rt + li, rows s = 16 st + 4 lg + j
+          f32x4 pt[NOW1][NB];
 #pragma unroll
-        for (int rt = 0; rt < NB; ++rt)
-          if (16 * rt + li >= nrow)
+          for (int st = 0; st < NB; ++st) {
+            if (st > BL::at(NOWN - 1)) continue;
+            Grp kb[NQG];
 #pragma unroll
-            for (int q = 0; q < NQG; ++q) qreg[rt][q] = O::zero_grp();
-        f32x4 ao[NCT][NB];
+            for (int q = 0; q < NQG; ++q) kb[q] = O::a_row(K + (16 * st + li) * LDK, q * KG, lg);
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-          Grp sb[NQG];
+            for (int k = 0; k < NOWN; ++k) {
+              if (st > BL::at(k)) continue;
+              pt[k][st] = zero4();
 #pragma unroll
-          for (int q = 0; q < NQG; ++q) sb[q] = suS[(ct * NQG + q) * 64 + lane];
+              for (int q = 0; q < NQG; ++q) pt[k][st] = O::mma_grp(kb[q], qa[k][q], pt[k][st]);
+            }
+          }
+          // decay and causal mask, then the P rows as left-operand groups
 #pragma unroll
-          for (int rt = 0; rt < NB; ++rt) {
-            ao[ct][rt] = zero4();
+          for (int k = 0; k < NOWN; ++k) {
+            const int rt = BL::at(k);
+            const float gr = vec[16 * rt + li];
 #pragma unroll
-            for (int q = 0; q < NQG; ++q) ao[ct][rt] = O::mma_grp(qreg[rt][q], sb[q], ao[ct][rt]);
+            for (int st = 0; st <= rt; ++st) {
+              const f32x4 gs = *reinterpret_cast<const f32x4 *>(vec + 16 * st + 4 * lg);
+#pragma unroll
+              for (int j = 0; j < 4; ++j)
+                pt[k][st][j] = (st < rt || 4 * lg + j <= li) ? pt[k][st][j] * __expf(gr - gs[j]) : 0.f;
+            }
+#pragma unroll
+            for (int q = 0; q * KG < 16 * (rt + 1); ++q) {
+              f32x4 tl[TPG];
+#pragma unroll
+              for (int tt = 0; tt < TPG; ++tt) tl[tt] = (q * TPG + tt <= rt) ? pt[k][q * TPG + tt] : zero4();
+              pa_n[k][q] = O::b_from_d(tl);
+            }
+          }
+          // Diag(Gam) Q S
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct) {
+            Grp sbq[NQG];
+#pragma unroll
+            for (int q = 0; q < NQG; ++q) sbq[q] = suS[(ct * NQG + q) * 64 + lane];
+#pragma unroll
+            for (int k = 0; k < NOWN; ++k) {
+              ao_n[ct][k] = zero4();
+#pragma unroll
+              for (int q = 0; q < NQG; ++q) ao_n[ct][k] = O::mma_grp(qa[k][q], sbq[q], ao_n[ct][k]);
+            }
+          }
+#pragma unroll
+          for (int k = 0; k < NOWN; ++k) {
+            const f32x4 gm = *reinterpret_cast<const f32x4 *>(vec + C + 16 * BL::at(k) + 4 * lg);
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) ao_n[ct][k] = gm * ao_n[ct][k];
           }
         }
+        if (NOWN > 0 && i >= 1 && i <= nch) {
+          // ---- output of chunk i-1: O = Diag(Gam) Q S + P U~ ----
+          const int c = i - 1;
+          const int nrow = nrow_of(c);
+          const size_t tok0 = tok0_of(c);
+          const Grp *suU = sSuU(c);
 #pragma unroll
-        for (int rt = 0; rt < NB; ++rt) {
-          const f32x4 gm = *reinterpret_cast<const f32x4 *>(vec + C + 16 * rt + 4 * lg);
+          for (int ct = 0; ct < NCT; ++ct) {
+            Grp ub[NCG];
 #pragma unroll
-          for (int ct = 0; ct < NCT; ++ct) ao[ct][rt] = gm * ao[ct][rt];
-        }
+            for (int q = 0; q < NCG; ++q) ub[q] = suU[(ct * NCG + q) * 64 + lane];
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-          Grp ub[NCG];
+            for (int k = 0; k < NOWN; ++k) {
+              const int rt = BL::at(k);
 #pragma unroll
-          for (int q = 0; q < NCG; ++q) ub[q] = suU[(ct * NCG + q) * 64 + lane];
-#pragma unroll
-          for (int rt = 0; rt < NB; ++rt)
-#pragma unroll
-            for (int q = 0; q * KG < 16 * (rt + 1); ++q)
-              ao[ct][rt] = O::mma_grp(O::a_row(Pm + (16 * rt + li) * LDC, q * KG, lg), ub[q], ao[ct][rt]);
-        }
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-          const int col0 = jt * DVT + 16 * ct;
+              for (int q = 0; q * KG < 16 * (rt + 1); ++q) ao[ct][k] = O::mma_grp(pa[k][q], ub[q], ao[ct][k]);
+            }
+          }
           if constexpr (sizeof(E) == 2) {
             // stage O^T (4 rows of one column = one 8-byte write per lane), read
             // it back transposed (4 columns of one row) and store 8 bytes
-            E *st = sOt + ct * 16 * LDC;
 #pragma unroll
-            for (int rt = 0; rt < NB; ++rt) {
-              bf16x4 ob;
+            for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-              for (int j = 0; j < 4; ++j) ob[j] = (bf16)ao[ct][rt][j];
-              *reinterpret_cast<bf16x4 *>(st + li * LDC + 16 * rt + 4 * lg) = ob;
-            }
+              for (int k = 0; k < NOWN; ++k) {
+                bf16x4 ob;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) ob[j] = (bf16)ao[ct][k][j];
+                *reinterpret_cast<bf16x4 *>(sO + (16 * ct + li) * LOS + 16 * k + 4 * lg) = ob;
+              }
             const int x = (lane >> 2) & 3, a = lane & 3;
-            bf16x4 rows[NB];
 #pragma unroll
-            for (int rt = 0; rt < NB; ++rt)
-              rows[rt] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(st + (4 * lg + x) * LDC + 16 * rt + 4 * a));
+            for (int ct = 0; ct < NCT; ++ct) {
+              bf16x4 rows[NOW1];
 #pragma unroll
-            for (int rt = 0; rt < NB; ++rt)
-              if (16 * rt + li < nrow)
-                *reinterpret_cast<bf16x4 *>(go + (tok0 + 16 * rt + li) * (size_t)dv + col0 + 4 * lg) = rows[rt];
+              for (int k = 0; k < NOWN; ++k)
+                rows[k] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                    (lds_bf16x4 *)(sO + (16 * ct + 4 * lg + x) * LOS + 16 * k + 4 * a));
+#pragma unroll
+              for (int k = 0; k < NOWN; ++k) {
+                const int r = 16 * BL::at(k) + li;
+                if (r < nrow)
+                  *reinterpret_cast<bf16x4 *>(go + (tok0 + r) * (size_t)dv + jt * DVT + 16 * ct + 4 * lg) = rows[k];
+              }
+            }
           } else {
 #pragma unroll
-            for (int rt = 0; rt < NB; ++rt)
+            for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                const int r = 16 * rt + 4 * lg + j;
-                if (r < nrow) go[(tok0 + r) * (size_t)dv + col0 + li] = Elem<E>::from_f32(ao[ct][rt][j]);
-              }
+              for (int k = 0; k < NOWN; ++k)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                  const int r = 16 * BL::at(k) + 4 * lg + j;
+                  if (r < nrow) go[(tok0 + r) * (size_t)dv + jt * DVT + 16 * ct + li] = Elem<E>::from_f32(ao[ct][k][j]);
+                }
           }
         }
+        if (NOWN > 0 && i >= 0 && i < nch) {
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+            for (int k = 0; k < NOWN; ++k) ao[ct][k] = ao_n[ct][k];
+#pragma unroll
+          for (int k = 0; k < NOWN; ++k)
+#pragma unroll
+            for (int q = 0; q < NCG; ++q) pa[k][q] = pa_n[k][q];
+        }
+        lds_barrier();
       }
-      if (i >= 0 && i < nch) fetch(i);
-      lds_barrier();
-    }
+    };
+    if (wave == PW0)
+      pwave(std::integral_constant<int, 0>{});
+    else
+      pwave(std::integral_constant<int, 1>{});
   } else if (wave == GRAM0 || wave == GRAM1) {
     // =================== Gram waves: chunk i+2 ================================
-    const int part = wave - GRAM0;
-    Nat kop[NB][KSTEPS];
-    E kg_raw = Elem<E>::from_f32(0.f), ke_raw = Elem<E>::from_f32(0.f);
-    auto fetch = [&](int c) {
-      const int nrow = nrow_of(c);
-      const size_t tok0 = tok0_of(c);
+    auto gram = [&](auto part_c) {
+      constexpr int part = decltype(part_c)::value;
+      using BL = GramBlocks<NB, part>;
+      using OB = OwnBlocks<NB, part>;
+      RowLoad<E, DK, BL> kin;
+      auto issue = [&](int c) { kin.issue(gk + tok0_of(c) * DK, nrow_of(c), lane); };
+      float *gp = reinterpret_cast<float *>(smem + Sh::OFF_GP + part * Sh::GPRIV);
+      float *sGam = gp;          // [C]
+      float *sNrm = gp + C;      // [C]
+      float *sBet = gp + 2 * C;  // [C]
+      issue(0);
+      __syncthreads();
+      for (int i = -2; i <= nch; ++i) {
+        const int c = i + 2;
+        if (OB::N > 0 && c >= 0 && c < nch) {
+          const int nrow = nrow_of(c);
+          E *K = sK(c);
+          E *Ablk = sA(c);
+          float *Td = sTd(c);
+          float *vec = sVec(c);
+          // the chunk's K rows into the ring (rows both Gram waves read are
+          // written by both, with identical values), then the next chunk's loads
+          kin.put(K, LDK, lane, [](int, int row) { return row; });
+          issue(clampc(c + 1));
+          const float *ge = sGE(c);
+          const float gl = (lane < C) ? ge[lane] : 0.f;
+          const float el = (lane < C) ? ge[C + lane] : 0.f;
+          Grp kb[BL::N > 0 ? BL::N : 1][NQG];
 #pragma unroll
-      for (int rt = 0; rt < NB; ++rt) {
-        const int r = min(16 * rt + li, nrow - 1);
+          for (int k = 0; k < BL::N; ++k)
 #pragma unroll
-        for (int kq = 0; kq < KSTEPS; ++kq) kop[rt][kq] = O::ldg(gk + (tok0 + r) * DK + kq * KSTEP + lg * VPL);
+            for (int q = 0; q < NQG; ++q) kb[k][q] = O::a_row(K + (16 * k + li) * LDK, q * KG, lg);
+          // Gram tiles of the owned rows
+          f32x4 G[NB][NB];
+#pragma unroll
+          for (int rt = 0; rt < NB; ++rt) {
+            if (!owns_block(NB, part, rt)) continue;
+#pragma unroll
+            for (int st = 0; st <= rt; ++st) {
+              G[rt][st] = zero4();
+#pragma unroll
+              for (int q = 0; q < NQG; ++q) G[rt][st] = O::mma_grp(kb[rt][q], kb[st][q], G[rt][st]);
+            }
+            // ||k_r||^2 of row 16 rt + li sits on the diagonal of tile (rt, rt):
+            // lane group li >> 2, element li & 3
+            const f32x4 d = G[rt][rt];
+            const int j = li & 3;
+            const float nr = j == 0 ? d[0] : j == 1 ? d[1] : j == 2 ? d[2] : d[3];
+            if (lg == (li >> 2)) sNrm[16 * rt + li] = nr;
+          }
+          // gate scan and beta (lane = chunk row); beta of rows beyond the
+          // sequence end is 0 (not 0/0 when eps = 0)
+          const float gam = wave_inclusive_scan(gl);
+          const float gamC = lane_value(gam, C - 1);
+          if (lane < C) {
+            sGam[lane] = gam;
+            if (part == 0) {
+              vec[lane] = gam;
+              vec[C + lane] = __expf(gam);             // Gam_r
+              vec[2 * C + lane] = __expf(gamC - gam);  // d_r
+            }
+            if (owns_block(NB, part, lane >> 4)) {
+              const float beta = (lane < nrow) ? el / (sNrm[lane] + p.eps) : 0.f;
+              sBet[lane] = beta;
+              vec[3 * C + lane] = beta;
+            }
+          }
+          // A = beta_r (K K^T)_rs exp(gamma_r - gamma_s), r > s
+#pragma unroll
+          for (int rt = 0; rt < NB; ++rt) {
+            if (!owns_block(NB, part, rt)) continue;
+            const f32x4 gr4 = *reinterpret_cast<const f32x4 *>(sGam + 16 * rt + 4 * lg);
+            const f32x4 br4 = *reinterpret_cast<const f32x4 *>(sBet + 16 * rt + 4 * lg);
+#pragma unroll
+            for (int st = 0; st <= rt; ++st) {
+              const float gs = sGam[16 * st + li];
+              const f32x4 acc = G[rt][st];
+              f32x4 av;
+              if (st < rt) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) av[j] = br4[j] * acc[j] * __expf(gr4[j] - gs);
+                // off-diagonal block, stored transposed: A^T[s'][r']
+                store4(Ablk + (rt * (rt - 1) / 2 + st) * 16 * LDA + li * LDA + 4 * lg, av);
+              } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                  const bool below = 4 * lg + j > li;
+                  const float dec = below ? __expf(gr4[j] - gs) : 0.f;
+                  av[j] = below ? br4[j] * acc[j] * dec : 0.f;
+                }
+                // diagonal block, fp32, stored transposed (At[s'][r']) for the solve
+                *reinterpret_cast<f32x4 *>(Td + (rt * 16 + li) * LDD + 4 * lg) = av;
+              }
+            }
+          }
+        }
+        lds_barrier();
       }
-      const int lr = min(lane, nrow - 1);
-      kg_raw = gg[tok0 + lr];
-      ke_raw = geta[tok0 + lr];
     };
-    char *gp = smem + Sh::OFF_GP + part * Sh::GPRIV;
-    float *sAtd = reinterpret_cast<float *>(gp);                       // [MAXD][16][LDD]
-    float *sNrm = sAtd + Sh::MAXD * 16 * LDD;                          // [NB][4][16]
-    float *sGam = sNrm + NB * 64;                                      // [C]
-    float *sBet = sGam + C;                                            // [C]
-
-    auto produce = [&](int c) {
-      const int nrow = nrow_of(c);
-      E *K = sK(c);
-      E *Ablk = sA(c);
+    if (wave == GRAM0)
+      gram(std::integral_constant<int, 0>{});
+    else
+      gram(std::integral_constant<int, 1>{});
+  } else if (wave == TSOLVE) {
+    // =================== T' of chunk i+1 ======================================
+    // T' = T Diag(beta), T = (I + A)^-1, stored transposed (row s of T'^T is
+    // column s of T') with grouped columns, so a lane writes 4 consecutive
+    // entries at once; the chain reads it with transposing LDS reads.
+    auto solve = [&](int c) {
+      using M = Mm16<E>;
+      E *TpT = sTp(c);
+      const E *Ablk = sA(c);
       float *Td = sTd(c);
-      float *vec = sVec(c);
-#pragma unroll
-      for (int rt = 0; rt < NB; ++rt) {
-        const int r = 16 * rt + li;
-#pragma unroll
-        for (int kq = 0; kq < KSTEPS; ++kq) {
-          if (r >= nrow) kop[rt][kq] = O::zero();
-          // K rows for the chain and P waves (half the row tiles each)
-          if ((rt < (NB + 1) / 2) == (part == 0)) O::st_nat(K + r * LDK, kq, lg, kop[rt][kq]);
-        }
-      }
-      // fused ||k_r||^2: lane holds a quarter of row 16rt + li; lane r sums the
-      // four quarters of its row through LDS
-#pragma unroll
-      for (int rt = 0; rt < NB; ++rt) {
-        float sq = 0.f;
-#pragma unroll
-        for (int kq = 0; kq < KSTEPS; ++kq) sq += O::sumsq(kop[rt][kq]);
-        sNrm[(rt * 4 + lg) * 16 + li] = sq;
-      }
-      const float gam = wave_inclusive_scan((lane < nrow) ? Elem<E>::to_f32(kg_raw) : 0.f);
-      float nr = 0.f;
-      if (lane < C) {
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) nr += sNrm[((lane >> 4) * 4 + q4) * 16 + li];
-      }
-      // beta of rows beyond the sequence end is 0 (not 0/0 when eps = 0)
-      const float beta = (lane < nrow) ? Elem<E>::to_f32(ke_raw) / (nr + p.eps) : 0.f;
-      const float gamC = lane_value(gam, C - 1);
-      if (lane < C) {
-        sGam[lane] = gam;
-        sBet[lane] = beta;
-        if (part == 0) {
-          vec[lane] = gam;
-          vec[C + lane] = __expf(gam);             // Gam_r
-          vec[2 * C + lane] = __expf(gamC - gam);  // d_r
-          vec[3 * C + lane] = beta;
-        }
-      }
-      f32x4 gr4[NB], br4[NB];
-      float gs1[NB];
-#pragma unroll
-      for (int rt = 0; rt < NB; ++rt) {
-        gr4[rt] = *reinterpret_cast<const f32x4 *>(sGam + 16 * rt + 4 * lg);
-        br4[rt] = *reinterpret_cast<const f32x4 *>(sBet + 16 * rt + 4 * lg);
-        gs1[rt] = sGam[16 * rt + li];
-      }
-      // this wave's Gram tiles and A = beta_r (K K^T)_rs exp(gamma_r - gamma_s), r > s
-#pragma unroll
-      for (int rt = 0; rt < NB; ++rt) {
-#pragma unroll
-        for (int st = 0; st <= rt; ++st) {
-          if (tile_part(NB, rt, st) != part) continue;
-          f32x4 acc = zero4();
-#pragma unroll
-          for (int kq = 0; kq < KSTEPS; ++kq) acc = O::mma(kop[rt][kq], kop[st][kq], acc);
-          const int s = 16 * st + li;
-          f32x4 av;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int r = 16 * rt + 4 * lg + j;
-            const float dec = (r > s) ? __expf(gr4[rt][j] - gs1[st]) : 0.f;
-            av[j] = (r > s) ? br4[rt][j] * acc[j] * dec : 0.f;
-          }
-          if (st < rt) {
-            E *blk = Ablk + (rt * (rt - 1) / 2 + st) * 16 * LDA;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) blk[(4 * lg + j) * LDA + li] = Elem<E>::from_f32(av[j]);
-          } else {
-            // own diagonal block, stored transposed: At[s'][r']
-            int dl = 0;
-#pragma unroll
-            for (int kk = 0; kk < Sh::MAXD; ++kk)
-              if (part_diag_block(NB, part, kk) == rt) dl = kk;
-            *reinterpret_cast<f32x4 *>(sAtd + dl * 16 * LDD + li * LDD + 4 * lg) = av;
-          }
-        }
-      }
-      // own diagonal blocks of T = (I + A)^-1 by column-parallel forward
-      // substitution in fp32: lane = (local block lg, column li)
-      constexpr int ND0 = part_diag_count(NB, 0), ND1 = part_diag_count(NB, 1);
-      const int nd = part == 0 ? ND0 : ND1;
-      if (lg < nd) {
-        int bb = 0;
-#pragma unroll
-        for (int kk = 0; kk < Sh::MAXD; ++kk)
-          if (kk == lg) bb = part_diag_block(NB, part, kk);
-        const float *At = sAtd + lg * 16 * LDD;
+      const float *beta = sVec(c) + 3 * C;
+      // diagonal blocks T_bb = (I + A_bb)^-1 by column-parallel forward
+      // substitution in fp32: lane = (block lg, column li).  A_bb arrives
+      // transposed (row s of At = column s of A); row s+1 is read while row s
+      // is applied.  T_bb replaces it, also transposed.
+      if (lg < NB) {
+        float *At = Td + lg * 16 * LDD;
         float x[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) x[r] = (r == li) ? 1.f : 0.f;
+        f32x4 cur[4], nxt[4];
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) cur[qd] = *reinterpret_cast<const f32x4 *>(At + 4 * qd);
 #pragma unroll
         for (int s = 0; s < 15; ++s) {
-          f32x4 colv[4];
+          if (s + 1 < 15) {
 #pragma unroll
-          for (int qd = 0; qd < 4; ++qd)
-            if (4 * qd + 3 > s) colv[qd] = *reinterpret_cast<const f32x4 *>(At + s * LDD + 4 * qd);
+            for (int qd = 0; qd < 4; ++qd)
+              if (4 * qd + 3 > s + 1) nxt[qd] = *reinterpret_cast<const f32x4 *>(At + (s + 1) * LDD + 4 * qd);
+          }
 #pragma unroll
-          for (int r = s + 1; r < 16; ++r) x[r] = fmaf(-colv[r >> 2][r & 3], x[s], x[r]);
+          for (int r = s + 1; r < 16; ++r) x[r] = fmaf(-cur[r >> 2][r & 3], x[s], x[r]);
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd) cur[qd] = nxt[qd];
         }
-        // T_bb transposed: row li of T^T = column li of T
-        float *dst = Td + (bb * 16 + li) * LDD;
-#pragma unroll
-        for (int qd = 0; qd < 4; ++qd)
-          *reinterpret_cast<f32x4 *>(dst + 4 * qd) = f32x4{x[4 * qd], x[4 * qd + 1], x[4 * qd + 2], x[4 * qd + 3]};
-      }
-    };
-
-    if (nch > 0) fetch(0);
-    __syncthreads();
-    for (int i = -2; i <= nch; ++i) {
-      const int c = i + 2;
-      if (c >= 0 && c < nch) {
-        produce(c);
-        if (c + 1 < nch) fetch(c + 1);
-      }
-      lds_barrier();
-    }
-  } else if (wave == TSOLVE) {
-    // =================== T' of chunk i+1 ======================================
-    // T' = T Diag(beta); diagonal blocks of T come from the Gram waves, the
-    // off-diagonal blocks are built level by level: T_ij = -T_ii sum_m A_im T_mj
-    auto solve = [&](int c) {
-      E *Tp = sTp(c);
-      const E *Ablk = sA(c);
-      const float *Td = sTd(c);
-      const float *beta = sVec(c) + 3 * C;
-      // diagonal blocks: lane = (block lg, column li)
-      if (lg < NB) {
-        const float *src = Td + (lg * 16 + li) * LDD;
+        float *dst = At + li * LDD;
         const float bs = beta[16 * lg + li];
-        const int pc = O::perm(16 * lg + li);
 #pragma unroll
         for (int qd = 0; qd < 4; ++qd) {
-          const f32x4 t4 = *reinterpret_cast<const f32x4 *>(src + 4 * qd);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) Tp[(16 * lg + 4 * qd + e) * LDC + pc] = Elem<E>::from_f32(t4[e] * bs);
+          const f32x4 t4 = {x[4 * qd], x[4 * qd + 1], x[4 * qd + 2], x[4 * qd + 3]};
+          *reinterpret_cast<f32x4 *>(dst + 4 * qd) = t4;
+          store4(TpT + (16 * lg + li) * LDC + O::perm(16 * lg + 4 * qd), bs * t4);
         }
       }
+      // off-diagonal blocks level by level: T_ij = -T_ii sum_m A_im T_mj
       if constexpr (NB > 1) {
         f32x4 Toff[NB][NB];
 #pragma unroll
@@ -790,34 +930,20 @@ __global__ __launch_bounds__(64 * kWaves) void kla_chunk_kernel(ChunkParams p) {
             f32x4 y = zero4();
 #pragma unroll
             for (int m = j; m < i; ++m) {
-              float a[4], bb[4];
-              const f32x4 a4 = load4(Ablk + (i * (i - 1) / 2 + m) * 16 * LDA + li * LDA + 4 * lg);
-#pragma unroll
-              for (int e = 0; e < 4; ++e) a[e] = a4[e];
-              if (m == j) {
-                // B operand T_jj[4lg + e][li] = T_jj^T[li][4lg + e]
-                const f32x4 t4 = *reinterpret_cast<const f32x4 *>(Td + (j * 16 + li) * LDD + 4 * lg);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) bb[e] = t4[e];
-              } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) bb[e] = Toff[m][j][e];
-              }
-              y = Mm16<E>::mma(a, bb, y);
+              // A_im[li][4lg + e] (block stored transposed); B operand T_mj[4lg + e][li]
+              const typename M::Op a = M::ld_t(Ablk + (i * (i - 1) / 2 + m) * 16 * LDA, LDA, lane);
+              const f32x4 bt = (m == j) ? *reinterpret_cast<const f32x4 *>(Td + (j * 16 + li) * LDD + 4 * lg)
+                                        : Toff[m][j];
+              y = M::mma(a, M::cvt(bt), y);
             }
             // A operand T_ii[li][4lg + e] = T_ii^T[4lg + e][li]
-            float a[4], bb[4];
+            f32x4 ti;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              a[e] = Td[(i * 16 + 4 * lg + e) * LDD + li];
-              bb[e] = y[e];
-            }
-            const f32x4 t = Mm16<E>::mma(a, bb, zero4());
-            Toff[i][j] = -t;
-            const float bs = beta[16 * j + li];
-            const int pc = O::perm(16 * j + li);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) Tp[(16 * i + 4 * lg + e) * LDC + pc] = Elem<E>::from_f32(-t[e] * bs);
+            for (int e = 0; e < 4; ++e) ti[e] = Td[(i * 16 + 4 * lg + e) * LDD + li];
+            const f32x4 t = -M::mma(M::cvt(ti), M::cvt(y), zero4());
+            Toff[i][j] = t;
+            // T'^T[16 j + li][16 i + 4 lg + e] = T_ij[4 lg + e][li] beta_(16 j + li)
+            store4(TpT + (16 * j + li) * LDC + O::perm(16 * i + 4 * lg), beta[16 * j + li] * t);
           }
         }
       }
@@ -825,62 +951,6 @@ __global__ __launch_bounds__(64 * kWaves) void kla_chunk_kernel(ChunkParams p) {
     __syncthreads();
     for (int i = -2; i <= nch; ++i) {
       if (i + 1 >= 0 && i + 1 < nch) solve(i + 1);
-      lds_barrier();
-    }
-  } else if (wave == PW0 || wave == PW1) {
-    // =================== P waves: causal scores of chunk i ====================
-    const int part = wave - PW0;
-    Grp qreg[NB][NQG];
-    auto fetch = [&](int c) {
-      const int nrow = nrow_of(c);
-      const size_t tok0 = tok0_of(c);
-#pragma unroll
-      for (int rt = 0; rt < NB; ++rt) {
-        if (!part_uses_row(NB, part, rt)) continue;
-        const E *row = gq + (tok0 + min(16 * rt + li, nrow - 1)) * DK;
-#pragma unroll
-        for (int q = 0; q < NQG; ++q) qreg[rt][q] = O::ldg_grp(row, q * KG, lg);
-      }
-    };
-    auto produce = [&](int c) {
-      const int nrow = nrow_of(c);
-      const E *K = sK(c);
-      E *Pm = sP(c);
-      const float *gamv = sVec(c);
-      f32x4 gr4[NB];
-      float gs1[NB];
-#pragma unroll
-      for (int rt = 0; rt < NB; ++rt) {
-        gr4[rt] = *reinterpret_cast<const f32x4 *>(gamv + 16 * rt + 4 * lg);
-        gs1[rt] = gamv[16 * rt + li];
-      }
-#pragma unroll
-      for (int rt = 0; rt < NB; ++rt) {
-        if (!part_uses_row(NB, part, rt)) continue;
-        if (16 * rt + li >= nrow)
-#pragma unroll
-          for (int q = 0; q < NQG; ++q) qreg[rt][q] = O::zero_grp();
-#pragma unroll
-        for (int st = 0; st <= rt; ++st) {
-          if (tile_part(NB, rt, st) != part) continue;
-          f32x4 acc = zero4();
-#pragma unroll
-          for (int q = 0; q < NQG; ++q) acc = O::mma_grp(qreg[rt][q], O::a_row(K + (16 * st + li) * LDK, q * KG, lg), acc);
-          const int s = 16 * st + li;
-          const int pc = O::perm(s);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int r = 16 * rt + 4 * lg + j;
-            const float val = (r >= s) ? acc[j] * __expf(gr4[rt][j] - gs1[st]) : 0.f;
-            Pm[r * LDC + pc] = Elem<E>::from_f32(val);
-          }
-        }
-      }
-    };
-    __syncthreads();
-    for (int i = -2; i <= nch; ++i) {
-      if (i >= 0 && i < nch) produce(i);
-      if (i + 1 >= 0 && i + 1 < nch) fetch(i + 1);
       lds_barrier();
     }
   } else {
@@ -891,34 +961,50 @@ __global__ __launch_bounds__(64 * kWaves) void kla_chunk_kernel(ChunkParams p) {
     uint4 vreg[NVP];
     const size_t vcol0 = (size_t)jt * DVT;
     auto fetch = [&](int c) {
-      const int nrow = nrow_of(c);
-      const size_t tok0 = tok0_of(c);
+      const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(gv + tok0_of(c) * dv, nrow_of(c) * dv * (int)sizeof(E));
 #pragma unroll
       for (int k = 0; k < NVP; ++k) {
         const int pc = min(lane + 64 * k, C * PPR - 1);
-        const int r = min(pc / PPR, nrow - 1), cq = pc % PPR;
-        vreg[k] = ldg16(gv + (tok0 + r) * (size_t)dv + vcol0 + cq * V16);
+        const int r = pc / PPR, cq = pc % PPR;
+        vreg[k] = buffer_ld16(rs, (r * dv + (int)vcol0 + cq * V16) * (int)sizeof(E));
       }
     };
     auto store = [&](int c) {
-      const int nrow = nrow_of(c);
       E *V = sV(c);
 #pragma unroll
       for (int k = 0; k < NVP; ++k) {
         const int pc = lane + 64 * k;
         if (pc < C * PPR) {
           const int r = pc / PPR, cq = pc % PPR;
-          *reinterpret_cast<uint4 *>(V + r * LDV + cq * V16) = (r < nrow) ? vreg[k] : make_uint4(0u, 0u, 0u, 0u);
+          *reinterpret_cast<uint4 *>(V + r * LDV + cq * V16) = vreg[k];
         }
       }
     };
-    if (nch > 0) fetch(0);
+    // g and eta of chunk c are staged at step c-3 (the Gram waves use them at
+    // step c-2); chunk 0 before the loop
+    E graw = Elem<E>::from_f32(0.f), eraw = Elem<E>::from_f32(0.f);
+    auto fetch_ge = [&](int c) {
+      const int lr = min(lane, nrow_of(c) - 1);
+      graw = gg[tok0_of(c) + lr];
+      eraw = geta[tok0_of(c) + lr];
+    };
+    auto store_ge = [&](int c) {
+      float *ge = sGE(c);
+      if (lane < C) {
+        ge[lane] = (lane < nrow_of(c)) ? Elem<E>::to_f32(graw) : 0.f;
+        ge[C + lane] = Elem<E>::to_f32(eraw);
+      }
+    };
+    fetch_ge(0);
+    store_ge(0);
+    fetch_ge(clampc(1));
+    fetch(0);
     __syncthreads();
     for (int i = -2; i <= nch; ++i) {
-      if (i + 1 >= 0 && i + 1 < nch) {
-        store(i + 1);
-        if (i + 2 < nch) fetch(i + 2);
-      }
+      if (i + 1 >= 0 && i + 1 < nch) store(i + 1);
+      if (i + 3 < nch) store_ge(i + 3);
+      fetch(clampc(i + 2));
+      fetch_ge(clampc(i + 4));
       lds_barrier();
     }
   }

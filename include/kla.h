@@ -95,9 +95,9 @@ typedef enum {
  *                  cannot cause an out-of-bounds access.
  *   num_seqs  N (must equal B when cu_seqlens is NULL)
  *
- * Supported: dtype BF16 with chunk 64, dk 128, dv a multiple of 32 in
- * [32, 256]; dtype F32 with chunk 16 and dk in {16, 32, 64, 128}, or chunk 64
- * and dk in {16, 32}, dv a multiple of 16 in [16, 256].  Anything else returns
+ * Supported: dtype BF16 with chunk 64 and dk in {64, 128}; dtype F32 with
+ * chunk 16 and dk in {16, 32, 64, 128}, or chunk 64 and dk in {16, 32}; for
+ * both, dv a multiple of 16 in [16, 256].  Anything else returns
  * KLA_ERR_UNSUPPORTED.
  */
 kla_status_t kla_chunk_fwd(const void *q, const void *k, const void *v,
