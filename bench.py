@@ -72,20 +72,21 @@ def recorded_traffic(profile_md, kernel_src):
 
 
 def time_launches(fn, steps, stream):
-    """Per-launch durations (ms) from HIP events recorded on the launch stream."""
+    """Mean duration (ms) of one call over `steps` back-to-back calls, from two
+    HIP events recorded on the launch stream around all of them (no event
+    between calls, so the GPU runs the calls as it would in a loop), and the
+    host wall time of the same region."""
     import torch
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    a.record(stream)
     for i in range(steps):
-        evs[i][0].record(stream)
         fn(i)
-        evs[i][1].record(stream)
+    b.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per = [a.elapsed_time(b) for a, b in evs]
-    return per, wall
+    return a.elapsed_time(b) / steps, wall
 
 
 def bench_prefill(steps, warmup):
@@ -98,17 +99,17 @@ def bench_prefill(steps, warmup):
     q, k, v, g, eta = (t.to(dev) for t in (x.q, x.k, x.v, x.g, x.eta))
     o = torch.empty((B, H, T, dv), dtype=q.dtype, device=dev)
     S = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    ws = torch.empty(kla.chunk_workspace_bytes(B, H, T, dk, dv, x.chunk, q.dtype), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
     def step(_i):
-        kla.chunk_fwd(q, k, v, g, eta, x.eps, None, None, chunk=x.chunk, out=o, final_state=S)
+        kla.chunk_fwd(q, k, v, g, eta, x.eps, None, None, chunk=x.chunk, out=o, final_state=S, workspace=ws)
 
     for i in range(warmup):
         step(i)
-    per, wall = time_launches(step, steps, stream)
-    ms = sum(per) / len(per)
+    ms, wall = time_launches(step, steps, stream)
     flops, byts = prefill_algorithmic(B, H, T, dk, dv, x.chunk, 0, 1, B)
-    return dict(ms=ms, wall_ms=wall * 1e3 / steps, per=per, tokens=B * T, flops=flops, bytes=byts,
+    return dict(ms=ms, wall_ms=wall * 1e3 / steps, tokens=B * T, flops=flops, bytes=byts,
                 dims=(B, H, T, dk, dv, x.chunk))
 
 
@@ -130,8 +131,7 @@ def bench_decode(steps_total=512, warmup=64):
 
     for i in range(warmup):
         step(i % steps_total)
-    per, wall = time_launches(step, steps_total, stream)
-    ms = sum(per) / len(per)
+    ms, wall = time_launches(step, steps_total, stream)
     byts, flops = decode_algorithmic(N, H, dk, dv)
     return dict(ms=ms, wall_ms=wall * 1e3 / steps_total, bytes=byts, flops=flops, N=N, H=H, dk=dk, dv=dv,
                 steps=steps_total)

@@ -2,7 +2,8 @@
 
 Each translation unit is compiled to an object in parallel, then linked into
 gated_delta_rule_kla_amd/libkla.so.  Packed-fp32 instruction selection is
-switched off for device code (-packed-fp32-ops).
+switched off for device code (-packed-fp32-ops), and so is the promotion of
+per-lane arrays into LDS (the kernels size their LDS themselves).
 """
 
 from __future__ import annotations
@@ -33,6 +34,7 @@ def _flags():
     return [
         f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-mllvm", "-disable-promote-alloca-to-lds",
         "-I", os.path.join(ROOT, "include"), "-I", CSRC,
         "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
     ]

@@ -33,6 +33,7 @@ const char *kla_status_str(kla_status_t s) {
     case KLA_ERR_SEQLENS: return "cu_seqlens must be non-decreasing from 0 to T";
     case KLA_ERR_EPS: return "eps must be finite and >= 0";
     case KLA_ERR_ALIGN: return "data pointers must be 16-byte aligned";
+    case KLA_ERR_WORKSPACE: return "workspace missing or smaller than kla_chunk_workspace_bytes()";
     case KLA_ERR_HIP: return "HIP runtime error";
   }
   return "unknown status";
@@ -55,11 +56,15 @@ kla_status_t kla_decode_step(const void *q, const void *k, const void *v, const 
   return from_hip(kla::launch_decode(a, reinterpret_cast<hipStream_t>(stream)));
 }
 
-kla_status_t kla_chunk_fwd(const void *q, const void *k, const void *v, const void *g,
-                           const void *eta, float eps, const float *initial_state, void *o,
-                           float *final_state, const int32_t *cu_seqlens,
-                           const int32_t *cu_seqlens_host, int num_seqs, int B, int H, int T,
-                           int dk, int dv, int chunk, kla_dtype_t dtype, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Shape, dtype, eps and cu_seqlens checks shared by kla_chunk_fwd and
+// kla_chunk_workspace_bytes.
+kla_status_t check_chunk_shapes(float eps, const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
+                                int num_seqs, int B, int H, int T, int dk, int dv, int chunk,
+                                kla_dtype_t dtype) {
   if (dtype != KLA_DT_BF16 && dtype != KLA_DT_F32) return KLA_ERR_DTYPE;
   if (B < 0 || H <= 0 || T < 0 || dk <= 0 || dv <= 0 || chunk <= 0 || num_seqs < 0)
     return KLA_ERR_SHAPE;
@@ -78,14 +83,54 @@ kla_status_t kla_chunk_fwd(const void *q, const void *k, const void *v, const vo
   }
   if ((long long)num_seqs * H * ((dv + 15) / 16) > 0x7fffffffLL) return KLA_ERR_SHAPE;
   if ((long long)B * H * T > (1LL << 40)) return KLA_ERR_SHAPE;
+  // workspace slots per head (see kla_chunk.hip): a grid dimension and int-indexed
+  const long long slots = cu_seqlens ? (long long)T / chunk + num_seqs + 1
+                                     : (long long)B * ((T + (long long)chunk - 1) / chunk);
+  if (slots > 0x7fffffffLL) return KLA_ERR_SHAPE;
+  return KLA_OK;
+}
+
+kla::ChunkArgs chunk_args(const void *q, const void *k, const void *v, const void *g, const void *eta,
+                          float eps, const float *initial_state, void *o, float *final_state,
+                          const int32_t *cu_seqlens, int num_seqs, int B, int H, int T, int dk, int dv,
+                          int chunk, kla_dtype_t dtype, void *workspace) {
+  return kla::ChunkArgs{q,          k,        v, g, eta, eps, initial_state, o, final_state,
+                        cu_seqlens, num_seqs, B, H, T,   dk,  dv,            chunk, (int)dtype, workspace};
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kla_chunk_workspace_bytes(const int32_t *cu_seqlens, const int32_t *cu_seqlens_host, int num_seqs,
+                                 int B, int H, int T, int dk, int dv, int chunk, kla_dtype_t dtype) {
+  if (check_chunk_shapes(0.f, cu_seqlens, cu_seqlens_host, num_seqs, B, H, T, dk, dv, chunk, dtype) != KLA_OK)
+    return 0;
+  if (num_seqs == 0 || (long long)B * T == 0) return 0;
+  return kla::chunk_workspace_bytes(chunk_args(nullptr, nullptr, nullptr, nullptr, nullptr, 0.f, nullptr,
+                                               nullptr, nullptr, cu_seqlens, num_seqs, B, H, T, dk, dv, chunk,
+                                               dtype, nullptr));
+}
+
+kla_status_t kla_chunk_fwd(const void *q, const void *k, const void *v, const void *g,
+                           const void *eta, float eps, const float *initial_state, void *o,
+                           float *final_state, const int32_t *cu_seqlens,
+                           const int32_t *cu_seqlens_host, int num_seqs, int B, int H, int T,
+                           int dk, int dv, int chunk, void *workspace, size_t workspace_bytes,
+                           kla_dtype_t dtype, void *stream) {
+  const kla_status_t st =
+      check_chunk_shapes(eps, cu_seqlens, cu_seqlens_host, num_seqs, B, H, T, dk, dv, chunk, dtype);
+  if (st != KLA_OK) return st;
   if (num_seqs == 0) return KLA_OK;
   // token tensors are only dereferenced when there are tokens
   if ((long long)B * T > 0 && (!q || !k || !v || !g || !eta || !o)) return KLA_ERR_NULL;
   if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(g) || misaligned(eta) ||
-      misaligned(o) || misaligned(initial_state) || misaligned(final_state))
+      misaligned(o) || misaligned(initial_state) || misaligned(final_state) || misaligned(workspace))
     return KLA_ERR_ALIGN;
-  kla::ChunkArgs a{q,        k,         v,  g, eta, eps, initial_state, o, final_state,
-                   cu_seqlens, num_seqs, B, H, T, dk,  dv,  chunk,         (int)dtype};
+  const kla::ChunkArgs a = chunk_args(q, k, v, g, eta, eps, initial_state, o, final_state, cu_seqlens, num_seqs,
+                                      B, H, T, dk, dv, chunk, dtype, workspace);
+  const size_t need = (long long)B * T > 0 ? kla::chunk_workspace_bytes(a) : 0;
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return KLA_ERR_WORKSPACE;
   return from_hip(kla::launch_chunk_fwd(a, reinterpret_cast<hipStream_t>(stream)));
 }
 

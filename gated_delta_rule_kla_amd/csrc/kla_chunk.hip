@@ -261,26 +261,27 @@ __device__ __forceinline__ float wave_inclusive_scan(float v) {
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // ---------------------------------------------------------------------------
-// Roles and LDS plan
+// Two kernels
 // ---------------------------------------------------------------------------
-// Waves of a workgroup.  Step i (one barrier each, i = -2 .. nch) has
-//   CHAIN    the state scan of chunk i
-//   PW[2]    causal scores and Diag(Gam) Q S of chunk i; output of chunk i-1
-//   TSOLVE   T' of chunk i+1
-//   GRAM[2]  gate scan, ||k||^2, beta and A of chunk i+2
-//   VLOAD    the V slice of chunk i+1
-// Waves w and w+4 share a SIMD, so the order pairs heavy roles with light
-// ones and leaves the T' solve (a long dependency chain) a SIMD of its own.
-enum Role { CHAIN = 0, PW0 = 1, PW1 = 2, TSOLVE = 3, VLOAD = 4, GRAM0 = 5, GRAM1 = 6 };
-constexpr int kWaves = 7;
+// kla_chunk_prep_kernel: the S-independent work of every chunk, all chunks in
+// parallel (a workgroup pipelines a run of consecutive chunks of one head):
+// gate scan, ||k||^2 and beta, K K^T and A, T = (I + A)^-1, T' = T Diag(beta),
+// and the causal scores P = (Q K^T) . exp(gamma_r - gamma_s) (r >= s).  It
+// writes T'^T, the row vectors gamma, Gam, d and P into a workspace, laid out
+// exactly as the scan kernel holds them in LDS and registers.
+//
+// kla_chunk_kernel: one workgroup per (sequence, head, slice of state
+// columns), the chunks of the sequence in order -- the state scan and the
+// output.  Because T' and P are computed once per chunk and head, the column
+// slices of a head no longer each redo them.
 
-// The 16-row blocks of a chunk are split between the two Gram waves and, the
-// same way, between the two P waves: part 0 owns the first and the last block,
-// part 1 the ones in between.  A wave handles the lower-triangular tiles
-// (rt, st <= rt) of the row blocks rt it owns (5 of the 10 tiles each for a
-// 64-token chunk), so the diagonal tiles -- and with them ||k_r||^2 and
-// beta_r -- of all its rows are its own.  Chunks of 16 (one block) leave
-// part 1 idle.
+// The 16-row blocks of a chunk are split between two waves (two Gram waves in
+// the prep kernel, two P waves in the scan kernel): part 0 owns the first and
+// the last block, part 1 the ones in between.  A wave handles the
+// lower-triangular tiles (rt, st <= rt) of the row blocks rt it owns (5 of the
+// 10 tiles each for a 64-token chunk), so the diagonal tiles -- and with them
+// ||k_r||^2 and beta_r -- of all its rows are its own.  Chunks of 16 (one
+// block) leave part 1 idle.
 __host__ __device__ constexpr bool owns_block(int NB, int part, int rt) {
   return (rt == 0 || rt == NB - 1) ? part == 0 : part == 1;
 }
@@ -289,63 +290,53 @@ struct OwnBlocks {  // the blocks a part owns, in order
   static constexpr int N = PART == 0 ? (NB > 1 ? 2 : 1) : NB - 2;
   static __host__ __device__ constexpr int at(int k) { return PART == 0 ? (k == 0 ? 0 : NB - 1) : 1 + k; }
 };
-template <int NB, int PART>
-struct GramBlocks {  // the blocks a Gram wave reads: 0 .. (largest owned block)
-  static constexpr int N = PART == 0 ? NB : NB - 1;
+
+template <int NB>
+struct AllBlocks {
+  static constexpr int N = NB;
   static __host__ __device__ constexpr int at(int k) { return k; }
 };
 
-template <typename E, int C, int DK, int NCT>
-struct ChunkShape {
-  static constexpr int NB = C / 16;            // 16-row blocks per chunk
-  static constexpr int DVT = 16 * NCT;         // state columns per workgroup
-  static constexpr int NT = 64 * kWaves;
+// Layout of the per-chunk data the prep kernel hands to the scan kernel: the
+// T'^T image (zero blocks and pads included), the row vectors gamma, Gam, d
+// (fp32), then the causal scores P in left-operand groups.  Row block rt of P
+// has ceil(16 (rt + 1) / KG) groups (the columns up to its diagonal), 64 lanes
+// x 16 bytes each.
+template <typename E, int C>
+struct TpLayout {
   static constexpr int PAD = 16 / (int)sizeof(E);
-  static constexpr int LDK = DK + PAD;         // K and Q rows (grouped columns)
-  static constexpr int LDC = C + PAD;          // T'^T rows (grouped columns)
-  static constexpr int LDV = DVT + PAD;        // V slice rows (natural)
-  static constexpr int LDA = 16 + PAD;         // rows of one 16x16 off-diagonal A^T block
-  static constexpr int LDD = 20;               // fp32 16-wide rows of diagonal blocks
+  static constexpr int LDC = C + PAD;                      // T'^T rows (grouped columns)
   static constexpr int KG = Ops<E>::KG;
-  static constexpr int NOFF = NB * (NB - 1) / 2;
-  static constexpr int MAXOWN = NB > 1 ? 2 : 1;        // row blocks per P wave
-  static constexpr int LOS = MAXOWN * 16 + PAD;        // rows of O^T staging
-  // sizes in bytes
-  static constexpr int K_SLOT = C * LDK * (int)sizeof(E);
-  static constexpr int V_SLOT = C * LDV * (int)sizeof(E);
-  static constexpr int TP_SLOT = C * LDC * (int)sizeof(E);
-  static constexpr int SU_S = NCT * (DK / KG) * 64 * 16;   // chunk-start S groups, 16 B per lane
-  static constexpr int SU_U = NCT * (C / KG) * 64 * 16;    // U~ groups
-  static constexpr int SU_SLOT = SU_S + SU_U;
-  static constexpr int A_SLOT = (NOFF > 0 ? NOFF : 1) * 16 * LDA * (int)sizeof(E);
-  static constexpr int TD_SLOT = NB * 16 * LDD * 4;        // diagonal blocks (A, then T), transposed, fp32
-  static constexpr int VEC_SLOT = 4 * C * 4;               // gamma, Gam, d, beta
-  static constexpr int GPRIV = 3 * C * 4;                  // per Gram wave: gamma, ||k||^2, beta
-  static constexpr int QST = MAXOWN * 16 * LDK * (int)sizeof(E);   // per P wave: its Q rows
-  static constexpr int OST = (sizeof(E) == 2 ? DVT * LOS : 0) * (int)sizeof(E);  // per P wave: O^T staging
-  static constexpr int GE_SLOT = 2 * C * 4;                // g and eta of a chunk, fp32
-  // offsets
-  static constexpr int OFF_K = 0;
-  static constexpr int OFF_V = OFF_K + 3 * K_SLOT;
-  static constexpr int OFF_TP = OFF_V + 2 * V_SLOT;
-  static constexpr int OFF_SU = OFF_TP + 2 * TP_SLOT;
-  static constexpr int OFF_A = OFF_SU + 2 * SU_SLOT;
-  static constexpr int OFF_TD = OFF_A + 2 * A_SLOT;
-  static constexpr int OFF_VEC = OFF_TD + 2 * TD_SLOT;
-  static constexpr int OFF_GP = OFF_VEC + 3 * VEC_SLOT;
-  static constexpr int OFF_QS = OFF_GP + 2 * GPRIV;
-  static constexpr int OFF_OS = OFF_QS + 2 * QST;
-  static constexpr int OFF_GE = OFF_OS + 2 * OST;
-  static constexpr int BYTES = OFF_GE + 2 * GE_SLOT;
+  static constexpr int TP_IMG = C * LDC * (int)sizeof(E);
+  static constexpr int VEC3 = 3 * C * 4;
+  static __host__ __device__ constexpr int pgroup(int rt, int q) {
+    int n = q;
+    for (int r = 0; r < rt; ++r) n += (16 * (r + 1) + KG - 1) / KG;
+    return n;
+  }
+  static constexpr int NPG = pgroup(C / 16, 0);
+  static constexpr int OFF_P = TP_IMG + VEC3;
+  static constexpr int BYTES = OFF_P + NPG * 64 * 16;      // workspace bytes per (chunk, head)
+  static_assert(TP_IMG % 16 == 0 && VEC3 % 16 == 0, "align");
+};
 
-  static_assert(C == 16 || C == 64, "chunk");
-  static_assert(C % KG == 0 && DK % KG == 0 && DK % Ops<E>::KSTEP == 0, "dk");
-  static_assert(K_SLOT % 16 == 0 && V_SLOT % 16 == 0 && TP_SLOT % 16 == 0 && A_SLOT % 16 == 0 &&
-                    GPRIV % 16 == 0 && VEC_SLOT % 16 == 0 && QST % 16 == 0 && OST % 16 == 0, "lds align");
-  static_assert((LDK * (int)sizeof(E)) % 16 == 0 && (LDC * (int)sizeof(E)) % 16 == 0 &&
-                    (LDV * (int)sizeof(E)) % 16 == 0 && (LDA * (int)sizeof(E)) % 8 == 0 &&
-                    (LOS * (int)sizeof(E)) % 8 == 0, "row align");
-  static_assert(BYTES <= 160 * 1024, "LDS budget");
+// Workspace slot of chunk c of sequence n: dense batches use n * ceil(T/C) + c;
+// packed sequences use n + floor(t0_n / C) + c, which never collides (each
+// sequence's last slot is below the next sequence's first) and stays below
+// floor(T/C) + N + 1.
+__host__ __device__ inline int slots_per_head(bool varlen, int B, int T, int N, int C) {
+  return varlen ? T / C + N + 1 : B * ((T + C - 1) / C);
+}
+
+struct ChunkParams {
+  const void *q, *k, *v, *g, *eta;
+  float eps;
+  const float *s0;
+  void *o;
+  float *sfin;
+  const int32_t *cu;
+  char *ws;
+  int H, T, dv, n_tiles, remap, nseq, nslot;
 };
 
 // Raw buffer resource over bytes [0, n) of p: loads at offsets >= n return 0
@@ -356,12 +347,23 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *p, int
 __device__ __forceinline__ uint4 buffer_ld16(__amdgpu_buffer_rsrc_t r, int off) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
+// element i as raw bits (0 past the end of the resource); converted where it
+// is used, so that the wait for the load lands there
+__device__ __forceinline__ unsigned short buffer_ld_elem(__amdgpu_buffer_rsrc_t r, int i, const bf16 *) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, 2 * i, 0, 0);
+}
+__device__ __forceinline__ unsigned buffer_ld_elem(__amdgpu_buffer_rsrc_t r, int i, const float *) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, 4 * i, 0, 0);
+}
+__device__ __forceinline__ float elem_bits_to_f32(unsigned short v) { return Elem<bf16>::to_f32(__builtin_bit_cast(bf16, v)); }
+__device__ __forceinline__ float elem_bits_to_f32(unsigned v) { return __builtin_bit_cast(float, v); }
 
 // Coalesced loads of whole K or Q rows of one chunk: lane l takes the 16-byte
 // pieces l, l + 64, ... of the listed row blocks, so consecutive lanes read
 // consecutive bytes of a row (a wave instruction touches 4 rows of 256 B
-// rather than 16 rows).  The rows then go through LDS into the MFMA operand
-// layout, where each lane holds one row.
+// rather than 16 rows; loads that give each lane its own row cost the
+// texture-address unit four times more).  The rows then go through LDS into
+// the MFMA operand layout, where each lane holds one row.
 template <typename E, int DK, class BL>
 struct RowLoad {
   static constexpr int RB = DK * (int)sizeof(E);   // bytes per row
@@ -390,26 +392,521 @@ struct RowLoad {
   }
 };
 
-struct ChunkParams {
-  const void *q, *k, *v, *g, *eta;
-  float eps;
-  const float *s0;
-  void *o;
-  float *sfin;
-  const int32_t *cu;
-  int H, T, dv, n_tiles, remap;
+// NP 16-byte pieces copied from global memory (consecutive lanes, consecutive
+// pieces) into LDS, one step ahead.
+template <int NP>
+struct PieceCopy {
+  static constexpr int NPL = (NP + 63) / 64;
+  u32x4 r[NPL];
+  __device__ __forceinline__ void issue(const void *src, int lane) {
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) r[j] = reinterpret_cast<const u32x4 *>(src)[min(lane + 64 * j, NP - 1)];
+  }
+  __device__ __forceinline__ void put(void *dst, int lane) const {
+#pragma unroll
+    for (int j = 0; j < NPL; ++j)
+      if (NP % 64 == 0 || lane + 64 * j < NP) reinterpret_cast<u32x4 *>(dst)[lane + 64 * j] = r[j];
+  }
+};
+
+// The DVT-column slice of a chunk's V rows (rows past nrow read as zero):
+// 16-byte pieces, consecutive lanes along a row.
+template <typename E, int C, int DVT>
+struct VSliceLoad {
+  static constexpr int V16 = 16 / (int)sizeof(E);  // elements per piece
+  static constexpr int PPR = DVT / V16;            // pieces per row slice
+  static constexpr int NPL = (C * PPR + 63) / 64;  // pieces per lane
+  uint4 r[NPL];
+  __device__ __forceinline__ void issue(const E *rows, int nrow, int dv, int col0, int lane) {
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(rows, nrow * dv * (int)sizeof(E));
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) {
+      const int pc = min(lane + 64 * j, C * PPR - 1);
+      r[j] = buffer_ld16(rs, ((pc / PPR) * dv + col0 + (pc % PPR) * V16) * (int)sizeof(E));
+    }
+  }
+  __device__ __forceinline__ void put(E *V, int ldv, int lane) const {
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) {
+      const int pc = lane + 64 * j;
+      if ((C * PPR) % 64 == 0 || pc < C * PPR) *reinterpret_cast<uint4 *>(V + (pc / PPR) * ldv + (pc % PPR) * V16) = r[j];
+    }
+  }
 };
 
 // ---------------------------------------------------------------------------
-// the kernel
+// prep kernel
 // ---------------------------------------------------------------------------
+// One workgroup per (head, run of kPrepSlots consecutive workspace slots):
+// six role-specialised waves in a pipeline over the run, one LDS-only barrier
+// per step.  Step s (s = -1 .. kPrepSlots) has
+//   PLOAD    K and Q rows, g and eta of slot s+1 into LDS (coalesced loads
+//            issued a step ahead)
+//   PG[2]    slot s: K K^T of the owned rows, ||k||^2, the gate scan, beta,
+//            A, and the owned diagonal blocks T_bb = (I + A_bb)^-1 and of T'^T
+//   PP[2]    slot s: the causal scores of the owned rows (as P^T = K Q^T),
+//            straight to the workspace as left-operand groups
+//   POFFD    slot s-1: the off-diagonal blocks of T and of T' = T Diag(beta)
+//            (the Gram waves wrote the diagonal ones); the T'^T image goes to
+//            the workspace with gamma, Gam, d
+// Waves w and w+4 share a SIMD.
+enum PrepRole { PG0 = 0, PG1 = 1, PP0 = 2, PP1 = 3, POFFD = 4, PLOAD = 5 };
+constexpr int kPrepWaves = 6;
+constexpr int kPrepSlots = 16;  // workspace slots per workgroup
+
+template <typename E, int C, int DK>
+struct PrepShape {
+  static constexpr int NB = C / 16;
+  static constexpr int NT = 64 * kPrepWaves;
+  static constexpr int PAD = 16 / (int)sizeof(E);
+  static constexpr int LDK = DK + PAD;         // K and Q rows (grouped columns)
+  static constexpr int LDC = TpLayout<E, C>::LDC;
+  static constexpr int LDA = 16 + PAD;         // rows of one 16x16 off-diagonal A^T block
+  static constexpr int LDD = 20;               // fp32 16-wide rows of diagonal blocks
+  static constexpr int KG = Ops<E>::KG;
+  static constexpr int NOFF = NB * (NB - 1) / 2;
+  static constexpr int K_SLOT = C * LDK * (int)sizeof(E);
+  static constexpr int GE_SLOT = 2 * C * 4;                // g (0 past the end), eta
+  static constexpr int A_SLOT = (NOFF > 0 ? NOFF : 1) * 16 * LDA * (int)sizeof(E);
+  static constexpr int TD_SLOT = NB * 16 * LDD * 4;        // diagonal blocks (A, then T), transposed, fp32
+  static constexpr int BV_SLOT = 4 * C * 4;                // gamma, Gam, d, beta
+  static constexpr int GP = 3 * C * 4;                     // per Gram wave: gamma, ||k||^2, beta
+  static constexpr int PGAM = C * 4;                       // per P wave: gamma
+  static constexpr int OFF_K = 0;
+  static constexpr int OFF_Q = OFF_K + 2 * K_SLOT;
+  static constexpr int OFF_GE = OFF_Q + 2 * K_SLOT;
+  static constexpr int OFF_A = OFF_GE + 2 * GE_SLOT;
+  static constexpr int OFF_TD = OFF_A + 2 * A_SLOT;
+  static constexpr int OFF_BV = OFF_TD + 2 * TD_SLOT;
+  static constexpr int IMG_SLOT = TpLayout<E, C>::TP_IMG;
+  static constexpr int OFF_IMG = OFF_BV + 2 * BV_SLOT;
+  static constexpr int OFF_GP = OFF_IMG + 2 * IMG_SLOT;
+  static constexpr int OFF_PG = OFF_GP + 2 * GP;
+  static constexpr int OFF_SLOT = OFF_PG + 2 * PGAM;       // per slot: token offset (8 B), rows (4 B), pad
+  static constexpr int BYTES = OFF_SLOT + kPrepSlots * 16;
+  static_assert(K_SLOT % 16 == 0 && A_SLOT % 16 == 0 && TD_SLOT % 16 == 0, "lds align");
+  static_assert(BYTES <= 160 * 1024, "LDS budget");
+};
+
+template <typename E, int C, int DK>
+__global__ __launch_bounds__(64 * kPrepWaves) void kla_chunk_prep_kernel(ChunkParams p) {
+  using Sh = PrepShape<E, C, DK>;
+  using TL = TpLayout<E, C>;
+  using O = Ops<E>;
+  using Grp = typename O::Grp;
+  constexpr int NB = Sh::NB, LDK = Sh::LDK, LDC = Sh::LDC, LDA = Sh::LDA, LDD = Sh::LDD;
+  constexpr int KG = O::KG, TPG = KG / 16, NQG = DK / KG;
+
+  __shared__ __attribute__((aligned(16))) char smem[Sh::BYTES];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int li = lane & 15, lg = lane >> 4;
+  const int h = blockIdx.y;
+  const int slot_base = blockIdx.x * kPrepSlots;
+
+  // ---- the chunk behind each slot of the run: token offset and row count ---
+  // (row count 0: no chunk -- an unused slot or past the end)
+  long long *slot_tok = reinterpret_cast<long long *>(smem + Sh::OFF_SLOT);
+  int *slot_rows = reinterpret_cast<int *>(smem + Sh::OFF_SLOT + 8);
+  if (threadIdx.x < kPrepSlots) {
+    const int slot = slot_base + threadIdx.x;
+    int b = 0, t0 = 0, len = p.T, c = slot;
+    if (p.cu) {
+      // sequence n with n + floor(cu[n] / C) <= slot (strictly increasing in n)
+      int lo = 0, hi = p.nseq - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (mid + min(max(p.cu[mid], 0), p.T) / C <= slot) lo = mid; else hi = mid - 1;
+      }
+      t0 = min(max(p.cu[lo], 0), p.T);
+      len = min(max(p.cu[lo + 1], t0), p.T) - t0;
+      c = slot - (lo + t0 / C);
+    } else {
+      const int nchT = (p.T + C - 1) / C;
+      b = slot / nchT;
+      c = slot % nchT;
+      if (b >= p.nseq) len = 0;
+    }
+    const bool ok = slot < p.nslot && c >= 0 && c * C < len;
+    slot_tok[2 * threadIdx.x] = ((long long)b * p.H + h) * p.T + t0 + (long long)c * C;
+    slot_rows[4 * threadIdx.x] = ok ? min(C, len - c * C) : 0;
+  }
+  // (values read from LDS are per lane to the compiler: make them scalar)
+  auto nrow_of = [&](int s) {
+    return (s >= 0 && s < kPrepSlots) ? __builtin_amdgcn_readfirstlane(slot_rows[4 * s]) : 0;
+  };
+  auto tok_of = [&](int s) {
+    const long long t = slot_tok[2 * min(max(s, 0), kPrepSlots - 1)];
+    const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)t), hi = __builtin_amdgcn_readfirstlane((unsigned)(t >> 32));
+    return (size_t)(((unsigned long long)hi << 32) | lo);
+  };
+  auto ws_of = [&](int s) { return p.ws + ((size_t)h * p.nslot + slot_base + s) * TL::BYTES; };
+
+  auto sK = [&](int s) { return reinterpret_cast<E *>(smem + Sh::OFF_K + (s & 1) * Sh::K_SLOT); };
+  auto sQ = [&](int s) { return reinterpret_cast<E *>(smem + Sh::OFF_Q + (s & 1) * Sh::K_SLOT); };
+  auto sGE = [&](int s) { return reinterpret_cast<float *>(smem + Sh::OFF_GE + (s & 1) * Sh::GE_SLOT); };
+  auto sA = [&](int s) { return reinterpret_cast<E *>(smem + Sh::OFF_A + (s & 1) * Sh::A_SLOT); };
+  auto sTd = [&](int s) { return reinterpret_cast<float *>(smem + Sh::OFF_TD + (s & 1) * Sh::TD_SLOT); };
+  // gamma, Gam = exp(gamma), d = exp(gamma_C - gamma), beta
+  auto sBV = [&](int s) { return reinterpret_cast<float *>(smem + Sh::OFF_BV + (s & 1) * Sh::BV_SLOT); };
+  auto sImg = [&](int s) { return reinterpret_cast<E *>(smem + Sh::OFF_IMG + (s & 1) * Sh::IMG_SLOT); };
+
+  // strictly-upper blocks of T' (strictly-lower ones of the T'^T image) and the
+  // pads are zero and never rewritten
+  for (int i = threadIdx.x; i < 2 * C * LDC; i += Sh::NT) {
+    const int rr = (i / LDC) % C, cc = i % LDC;
+    if (cc >= C || (rr >> 4) > (cc >> 4))
+      sImg(i / (C * LDC))[rr * LDC + (cc < C ? O::perm(cc) : cc)] = Elem<E>::from_f32(0.f);
+  }
+
+  if (wave == PLOAD) {
+    // =================== K, Q, g, eta of slot s+1 ============================
+    RowLoad<E, DK, AllBlocks<NB>> kin, qin;
+    typename std::conditional<sizeof(E) == 2, unsigned short, unsigned>::type graw = 0, eraw = 0;
+    auto issue = [&](int s) {
+      const int nrow = nrow_of(s);
+      const size_t tok = tok_of(s);
+      kin.issue(static_cast<const E *>(p.k) + tok * DK, nrow, lane);
+      qin.issue(static_cast<const E *>(p.q) + tok * DK, nrow, lane);
+      // g and eta of row `lane` (0 past the end; lanes >= C read nothing)
+      const E *gp = static_cast<const E *>(p.g) + tok, *ep = static_cast<const E *>(p.eta) + tok;
+      graw = buffer_ld_elem(buffer_rsrc(gp, nrow * (int)sizeof(E)), lane, gp);
+      eraw = buffer_ld_elem(buffer_rsrc(ep, nrow * (int)sizeof(E)), lane, ep);
+    };
+    __syncthreads();
+    issue(0);
+    for (int s = -1; s <= kPrepSlots; ++s) {
+      if (s + 1 < kPrepSlots) {
+        kin.put(sK(s + 1), LDK, lane, [](int, int row) { return row; });
+        qin.put(sQ(s + 1), LDK, lane, [](int, int row) { return row; });
+        float *ge = sGE(s + 1);
+        if (lane < C) {
+          ge[lane] = elem_bits_to_f32(graw);
+          ge[C + lane] = elem_bits_to_f32(eraw);
+        }
+        issue(s + 2);
+      }
+      lds_barrier();
+    }
+  } else if (wave == PG0 || wave == PG1) {
+    // =================== Gram waves: slot s ==================================
+    auto gram = [&](auto part_c) {
+      constexpr int part = decltype(part_c)::value;
+      using OB = OwnBlocks<NB, part>;
+      constexpr int NREAD = part == 0 ? NB : NB - 1;  // blocks 0 .. largest owned block
+      float *gp = reinterpret_cast<float *>(smem + Sh::OFF_GP + part * Sh::GP);
+      float *sGam = gp, *sNrm = gp + C, *sBet = gp + 2 * C;
+      __syncthreads();
+      for (int s = -1; s <= kPrepSlots; ++s) {
+        const int nrow = nrow_of(s);
+        if (OB::N > 0 && nrow > 0) {
+          const E *K = sK(s);
+          const float *ge = sGE(s);
+          E *Ablk = sA(s);
+          float *Td = sTd(s);
+          float *bv = sBV(s);
+          Grp kb[NREAD > 0 ? NREAD : 1][NQG];
+#pragma unroll
+          for (int k = 0; k < NREAD; ++k)
+#pragma unroll
+            for (int q = 0; q < NQG; ++q) kb[k][q] = O::a_row(K + (16 * k + li) * LDK, q * KG, lg);
+          f32x4 G[NB][NB];
+#pragma unroll
+          for (int rt = 0; rt < NB; ++rt) {
+            if (!owns_block(NB, part, rt)) continue;
+#pragma unroll
+            for (int st = 0; st <= rt; ++st) {
+              G[rt][st] = zero4();
+#pragma unroll
+              for (int q = 0; q < NQG; ++q) G[rt][st] = O::mma_grp(kb[rt][q], kb[st][q], G[rt][st]);
+            }
+            // ||k_r||^2 of row 16 rt + li sits on the diagonal of tile (rt, rt):
+            // lane group li >> 2, element li & 3
+            const f32x4 d = G[rt][rt];
+            const int j = li & 3;
+            const float nr = j == 0 ? d[0] : j == 1 ? d[1] : j == 2 ? d[2] : d[3];
+            if (lg == (li >> 2)) sNrm[16 * rt + li] = nr;
+          }
+          // gate scan and beta (lane = chunk row); beta of rows beyond the
+          // sequence end is 0 (not 0/0 when eps = 0)
+          const float gam = wave_inclusive_scan(lane < C ? ge[lane] : 0.f);
+          const float gamC = lane_value(gam, C - 1);
+          if (lane < C) {
+            sGam[lane] = gam;
+            if (part == 0) {
+              bv[lane] = gam;
+              bv[C + lane] = __expf(gam);             // Gam_r
+              bv[2 * C + lane] = __expf(gamC - gam);  // d_r
+            }
+            if (owns_block(NB, part, lane >> 4)) {
+              const float beta = (lane < nrow) ? ge[C + lane] / (sNrm[lane] + p.eps) : 0.f;
+              sBet[lane] = beta;
+              bv[3 * C + lane] = beta;
+            }
+          }
+          // A = beta_r (K K^T)_rs exp(gamma_r - gamma_s), r > s
+#pragma unroll
+          for (int rt = 0; rt < NB; ++rt) {
+            if (!owns_block(NB, part, rt)) continue;
+            const f32x4 gr4 = *reinterpret_cast<const f32x4 *>(sGam + 16 * rt + 4 * lg);
+            const f32x4 br4 = *reinterpret_cast<const f32x4 *>(sBet + 16 * rt + 4 * lg);
+#pragma unroll
+            for (int st = 0; st <= rt; ++st) {
+              const float gs = sGam[16 * st + li];
+              const f32x4 acc = G[rt][st];
+              f32x4 av;
+              if (st < rt) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) av[j] = br4[j] * acc[j] * __expf(gr4[j] - gs);
+                // off-diagonal block, stored transposed: A^T[s'][r']
+                store4(Ablk + (rt * (rt - 1) / 2 + st) * 16 * LDA + li * LDA + 4 * lg, av);
+              } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                  const bool below = 4 * lg + j > li;
+                  const float dec = below ? __expf(gr4[j] - gs) : 0.f;
+                  av[j] = below ? br4[j] * acc[j] * dec : 0.f;
+                }
+                // diagonal block, fp32, stored transposed (At[s'][r'])
+                *reinterpret_cast<f32x4 *>(Td + (rt * 16 + li) * LDD + 4 * lg) = av;
+              }
+            }
+          }
+          // the owned diagonal blocks T_bb = (I + A_bb)^-1 by column-parallel
+          // forward substitution in fp32: lane = (owned block lg, column li);
+          // T_bb replaces A_bb, also transposed (row li = column li of T_bb)
+          asm volatile("" ::: "memory");  // A_bb (written by other lanes of this wave) before the solve reads it
+          if (lg < OB::N) {
+            const int bb = lg == 0 ? OB::at(0) : OB::at(OB::N > 1 ? 1 : 0);
+            float *At = Td + bb * 16 * LDD;
+            float x[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) x[r] = (r == li) ? 1.f : 0.f;
+            f32x4 cur[4], nxt[4];
+#pragma unroll
+            for (int qd = 0; qd < 4; ++qd) cur[qd] = *reinterpret_cast<const f32x4 *>(At + 4 * qd);
+#pragma unroll
+            for (int s2 = 0; s2 < 15; ++s2) {
+              if (s2 + 1 < 15) {
+#pragma unroll
+                for (int qd = 0; qd < 4; ++qd)
+                  if (4 * qd + 3 > s2 + 1) nxt[qd] = *reinterpret_cast<const f32x4 *>(At + (s2 + 1) * LDD + 4 * qd);
+              }
+#pragma unroll
+              for (int r = s2 + 1; r < 16; ++r) x[r] = fmaf(-cur[r >> 2][r & 3], x[s2], x[r]);
+#pragma unroll
+              for (int qd = 0; qd < 4; ++qd) cur[qd] = nxt[qd];
+            }
+            // T_bb replaces A_bb (transposed, for the off-diagonal blocks); the
+            // diagonal block of the T'^T image is column li of T_bb times beta
+            float *dst = At + li * LDD;
+            E *irow = sImg(s) + (16 * bb + li) * LDC;
+            const float bs = sBet[16 * bb + li];
+#pragma unroll
+            for (int qd = 0; qd < 4; ++qd) {
+              const f32x4 t4 = {x[4 * qd], x[4 * qd + 1], x[4 * qd + 2], x[4 * qd + 3]};
+              *reinterpret_cast<f32x4 *>(dst + 4 * qd) = t4;
+              store4(irow + O::perm(16 * bb + 4 * qd), bs * t4);
+            }
+          }
+        }
+        lds_barrier();
+      }
+    };
+    if (wave == PG0)
+      gram(std::integral_constant<int, 0>{});
+    else
+      gram(std::integral_constant<int, 1>{});
+  } else if (wave == PP0 || wave == PP1) {
+    // =================== P waves: slot s =====================================
+    // P^T = K Q^T: its accumulator layout is the left-operand layout of the P
+    // rows in P U~, so the groups go to the workspace as they are (16 bytes
+    // per lane, consecutive lanes consecutive)
+    auto pwave = [&](auto part_c) {
+      constexpr int part = decltype(part_c)::value;
+      using OB = OwnBlocks<NB, part>;
+      constexpr int NOWN = OB::N;
+      constexpr int NOW1 = NOWN > 0 ? NOWN : 1;
+      float *sGam = reinterpret_cast<float *>(smem + Sh::OFF_PG + part * Sh::PGAM);
+      __syncthreads();
+      for (int s = -1; s <= kPrepSlots; ++s) {
+        const int nrow = nrow_of(s);
+        if (NOWN > 0 && nrow > 0) {
+          const E *K = sK(s);
+          const E *Q = sQ(s);
+          const float *ge = sGE(s);
+          const float gam = wave_inclusive_scan(lane < C ? ge[lane] : 0.f);
+          if (lane < C) sGam[lane] = gam;
+          Grp qa[NOW1][NQG];
+#pragma unroll
+          for (int k = 0; k < NOWN; ++k)
+#pragma unroll
+            for (int q = 0; q < NQG; ++q) qa[k][q] = O::a_row(Q + (16 * OB::at(k) + li) * LDK, q * KG, lg);
+          // P^T tiles: D[s'][r] = K_s' . q_r, lane column r = 16 rt + li, rows s' = 16 st + 4 lg + j
+          f32x4 pt[NOW1][NB];
+#pragma unroll
+          for (int st = 0; st < NB; ++st) {
+            if (st > OB::at(NOWN - 1)) continue;
+            Grp kb[NQG];
+#pragma unroll
+            for (int q = 0; q < NQG; ++q) kb[q] = O::a_row(K + (16 * st + li) * LDK, q * KG, lg);
+#pragma unroll
+            for (int k = 0; k < NOWN; ++k) {
+              if (st > OB::at(k)) continue;
+              pt[k][st] = zero4();
+#pragma unroll
+              for (int q = 0; q < NQG; ++q) pt[k][st] = O::mma_grp(kb[q], qa[k][q], pt[k][st]);
+            }
+          }
+          // decay and causal mask, then the P rows as left-operand groups
+          Grp *wsP = reinterpret_cast<Grp *>(ws_of(s) + TL::OFF_P);
+#pragma unroll
+          for (int k = 0; k < NOWN; ++k) {
+            const int rt = OB::at(k);
+            const float gr = sGam[16 * rt + li];
+#pragma unroll
+            for (int st = 0; st <= rt; ++st) {
+              const f32x4 gs = *reinterpret_cast<const f32x4 *>(sGam + 16 * st + 4 * lg);
+#pragma unroll
+              for (int j = 0; j < 4; ++j)
+                pt[k][st][j] = (st < rt || 4 * lg + j <= li) ? pt[k][st][j] * __expf(gr - gs[j]) : 0.f;
+            }
+#pragma unroll
+            for (int q = 0; q * KG < 16 * (rt + 1); ++q) {
+              f32x4 tl[TPG];
+#pragma unroll
+              for (int tt = 0; tt < TPG; ++tt) tl[tt] = (q * TPG + tt <= rt) ? pt[k][q * TPG + tt] : zero4();
+              wsP[TL::pgroup(rt, q) * 64 + lane] = O::b_from_d(tl);
+            }
+          }
+        }
+        lds_barrier();
+      }
+    };
+    if (wave == PP0)
+      pwave(std::integral_constant<int, 0>{});
+    else
+      pwave(std::integral_constant<int, 1>{});
+  } else {
+    // =================== off-diagonal solve: slot s-1 ========================
+    using M = Mm16<E>;
+    __syncthreads();
+    for (int s = -1; s <= kPrepSlots; ++s) {
+      const int sp = s - 1;
+      if (nrow_of(sp) > 0) {
+        const E *Ablk = sA(sp);
+        const float *Td = sTd(sp);
+        const float *bv = sBV(sp);
+        const float *beta = bv + 3 * C;
+        E *img = sImg(sp);
+        // off-diagonal blocks level by level: T_ij = -T_ii sum_m A_im T_mj
+        if constexpr (NB > 1) {
+          f32x4 Toff[NB][NB];
+#pragma unroll
+          for (int dist = 1; dist < NB; ++dist) {
+#pragma unroll
+            for (int i = dist; i < NB; ++i) {
+              const int j = i - dist;
+              f32x4 y = zero4();
+#pragma unroll
+              for (int m = j; m < i; ++m) {
+                // A_im[li][4lg + e] (block stored transposed); B operand T_mj[4lg + e][li]
+                const typename M::Op a = M::ld_t(Ablk + (i * (i - 1) / 2 + m) * 16 * LDA, LDA, lane);
+                const f32x4 bt = (m == j) ? *reinterpret_cast<const f32x4 *>(Td + (j * 16 + li) * LDD + 4 * lg)
+                                          : Toff[m][j];
+                y = M::mma(a, M::cvt(bt), y);
+              }
+              // A operand T_ii[li][4lg + e] = T_ii^T[4lg + e][li]
+              f32x4 ti;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) ti[e] = Td[(i * 16 + 4 * lg + e) * LDD + li];
+              const f32x4 t = -M::mma(M::cvt(ti), M::cvt(y), zero4());
+              Toff[i][j] = t;
+              // T'^T[16 j + li][16 i + 4 lg + e] = T_ij[4 lg + e][li] beta_(16 j + li)
+              store4(img + (16 * j + li) * LDC + O::perm(16 * i + 4 * lg), beta[16 * j + li] * t);
+            }
+          }
+        }
+        // the T'^T image and gamma, Gam, d to the workspace (16-byte pieces;
+        // all LDS reads first, then the stores)
+        constexpr int NI = TL::TP_IMG / 16, NP = NI + TL::VEC3 / 16, NPL = (NP + 63) / 64;
+        u32x4 *dst = reinterpret_cast<u32x4 *>(ws_of(sp));
+        const u32x4 *im = reinterpret_cast<const u32x4 *>(img);
+        const u32x4 *vs = reinterpret_cast<const u32x4 *>(bv);
+        u32x4 pc[NPL];
+#pragma unroll
+        for (int j = 0; j < NPL; ++j) {
+          const int i = min(lane + 64 * j, NP - 1);
+          pc[j] = i < NI ? im[i] : vs[i - NI];
+        }
+#pragma unroll
+        for (int j = 0; j < NPL; ++j)
+          if (NP % 64 == 0 || lane + 64 * j < NP) dst[lane + 64 * j] = pc[j];
+      }
+      lds_barrier();
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// scan kernel: roles and LDS plan
+// ---------------------------------------------------------------------------
+// Waves of a workgroup.  Step i (one barrier each, i = -1 .. nch) has
+//   CHAIN[2] the state scan of chunk i (half of the state columns each)
+//   PW[2]    Diag(Gam) Q S and the causal scores of chunk i; output of chunk i-1
+//   LOADK    K rows of chunk i+1 into LDS (coalesced loads issued a step ahead)
+//   LOADT    T'^T, gamma/Gam/d, P and the V slice of chunk i+1 into LDS
+// Waves w and w+4 share a SIMD.
+enum Role { CHAIN0 = 0, CHAIN1 = 1, PW0 = 2, PW1 = 3, LOADK = 4, LOADT = 5 };
+constexpr int kWaves = 6;
+
+template <typename E, int C, int DK, int NCT>
+struct ChunkShape {
+  static constexpr int NB = C / 16;            // 16-row blocks per chunk
+  static constexpr int DVT = 16 * NCT;         // state columns per workgroup
+  static constexpr int NCW = (NCT + 1) / 2;    // 16-column tiles per chain wave
+  static constexpr int NT = 64 * kWaves;
+  static constexpr int PAD = 16 / (int)sizeof(E);
+  static constexpr int LDK = DK + PAD;         // K and Q rows (grouped columns)
+  static constexpr int LDC = TpLayout<E, C>::LDC;
+  static constexpr int LDV = DVT + PAD;        // V slice rows (natural)
+  static constexpr int KG = Ops<E>::KG;
+  static constexpr int MAXOWN = NB > 1 ? 2 : 1;        // row blocks per P wave
+  static constexpr int LOS = MAXOWN * 16 + PAD;        // rows of O^T staging
+  // sizes in bytes
+  static constexpr int K_SLOT = C * LDK * (int)sizeof(E);
+  static constexpr int V_SLOT = C * LDV * (int)sizeof(E);
+  static constexpr int TP_SLOT = TpLayout<E, C>::BYTES;    // T'^T image, then gamma, Gam, d
+  static constexpr int SU_S = NCT * (DK / KG) * 64 * 16;   // chunk-start S groups, 16 B per lane
+  static constexpr int SU_U = NCT * (C / KG) * 64 * 16;    // U~ groups
+  static constexpr int SU_SLOT = SU_S + SU_U;
+  static constexpr int QST = MAXOWN * 16 * LDK * (int)sizeof(E);   // per P wave: its Q rows
+  static constexpr int OST = (sizeof(E) == 2 ? DVT * LOS : 0) * (int)sizeof(E);  // per P wave: O^T staging
+  // offsets
+  static constexpr int OFF_K = 0;
+  static constexpr int OFF_V = OFF_K + 2 * K_SLOT;
+  static constexpr int OFF_TP = OFF_V + 2 * V_SLOT;
+  static constexpr int OFF_SU = OFF_TP + 2 * TP_SLOT;
+  static constexpr int OFF_QS = OFF_SU + 2 * SU_SLOT;
+  static constexpr int OFF_OS = OFF_QS + 2 * QST;
+  static constexpr int BYTES = OFF_OS + 2 * OST;
+
+  static_assert(C == 16 || C == 64, "chunk");
+  static_assert(C % KG == 0 && DK % KG == 0 && DK % Ops<E>::KSTEP == 0, "dk");
+  static_assert(K_SLOT % 16 == 0 && V_SLOT % 16 == 0 && TP_SLOT % 16 == 0 && QST % 16 == 0 && OST % 16 == 0,
+                "lds align");
+  static_assert((LDK * (int)sizeof(E)) % 16 == 0 && (LDC * (int)sizeof(E)) % 16 == 0 &&
+                    (LDV * (int)sizeof(E)) % 16 == 0 && (LOS * (int)sizeof(E)) % 8 == 0, "row align");
+  static_assert(BYTES <= 160 * 1024, "LDS budget");
+};
+
 template <typename E, int C, int DK, int NCT>
 __global__ __launch_bounds__(64 * kWaves) void kla_chunk_kernel(ChunkParams p) {
   using Sh = ChunkShape<E, C, DK, NCT>;
+  using TL = TpLayout<E, C>;
   using O = Ops<E>;
   using Grp = typename O::Grp;
-  constexpr int NB = Sh::NB, DVT = Sh::DVT, LDK = Sh::LDK, LDC = Sh::LDC, LDV = Sh::LDV;
-  constexpr int LDA = Sh::LDA, LDD = Sh::LDD, LOS = Sh::LOS;
+  constexpr int NB = Sh::NB, DVT = Sh::DVT, LDK = Sh::LDK, LDC = Sh::LDC, LDV = Sh::LDV, LOS = Sh::LOS;
   constexpr int KG = O::KG, TPG = KG / 16;
   constexpr int NQG = DK / KG;  // contraction groups over dk
   constexpr int NCG = C / KG;   // contraction groups over the chunk
@@ -428,11 +925,14 @@ __global__ __launch_bounds__(64 * kWaves) void kla_chunk_kernel(ChunkParams p) {
   const int nh = L / p.n_tiles;
   const int h = nh % p.H;
   const int n = nh / p.H;
-  int b = n, t0 = 0, t1 = p.T;
+  int b = n, t0 = 0, t1 = p.T, slot0;
   if (p.cu) {
     b = 0;
     t0 = min(max(p.cu[n], 0), p.T);
     t1 = min(max(p.cu[n + 1], t0), p.T);
+    slot0 = n + t0 / C;
+  } else {
+    slot0 = n * ((p.T + C - 1) / C);
   }
   const int len = t1 - t0;
   const int nch = (len + C - 1) / C;
@@ -440,9 +940,8 @@ __global__ __launch_bounds__(64 * kWaves) void kla_chunk_kernel(ChunkParams p) {
   const E *gq = static_cast<const E *>(p.q);
   const E *gk = static_cast<const E *>(p.k);
   const E *gv = static_cast<const E *>(p.v);
-  const E *gg = static_cast<const E *>(p.g);
-  const E *geta = static_cast<const E *>(p.eta);
   E *go = static_cast<E *>(p.o);
+  const char *ws = p.ws + (size_t)h * p.nslot * TL::BYTES;
   const int dv = p.dv;
   auto nrow_of = [&](int c) { return min(C, len - c * C); };
   auto tok0_of = [&](int c) { return row0 + (size_t)c * C; };
@@ -461,37 +960,35 @@ __global__ __launch_bounds__(64 * kWaves) void kla_chunk_kernel(ChunkParams p) {
     return;
   }
 
-  // ---- LDS views -------------------------------------------------------------
-  auto sK = [&](int c) { return reinterpret_cast<E *>(smem + Sh::OFF_K + (c % 3) * Sh::K_SLOT); };
+  // ---- LDS views (chunk c in slot c & 1) --------------------------------------
+  auto sK = [&](int c) { return reinterpret_cast<E *>(smem + Sh::OFF_K + (c & 1) * Sh::K_SLOT); };
   auto sV = [&](int c) { return reinterpret_cast<E *>(smem + Sh::OFF_V + (c & 1) * Sh::V_SLOT); };
   auto sTp = [&](int c) { return reinterpret_cast<E *>(smem + Sh::OFF_TP + (c & 1) * Sh::TP_SLOT); };
+  // per-chunk row vectors: gamma, Gam = exp(gamma), d = exp(gamma_C - gamma)
+  auto sVec = [&](int c) {
+    return reinterpret_cast<float *>(smem + Sh::OFF_TP + (c & 1) * Sh::TP_SLOT + TL::TP_IMG);
+  };
   auto sSuS = [&](int c) { return reinterpret_cast<Grp *>(smem + Sh::OFF_SU + (c & 1) * Sh::SU_SLOT); };
   auto sSuU = [&](int c) {
     return reinterpret_cast<Grp *>(smem + Sh::OFF_SU + (c & 1) * Sh::SU_SLOT + Sh::SU_S);
   };
-  auto sA = [&](int c) { return reinterpret_cast<E *>(smem + Sh::OFF_A + (c & 1) * Sh::A_SLOT); };
-  auto sTd = [&](int c) { return reinterpret_cast<float *>(smem + Sh::OFF_TD + (c & 1) * Sh::TD_SLOT); };
-  // per-chunk row vectors: gamma, Gam = exp(gamma), d = exp(gamma_C - gamma), beta
-  auto sVec = [&](int c) { return reinterpret_cast<float *>(smem + Sh::OFF_VEC + (c % 3) * Sh::VEC_SLOT); };
-  // g (0 past the sequence end) and eta of a chunk's rows, staged by the V loader
-  auto sGE = [&](int c) { return reinterpret_cast<float *>(smem + Sh::OFF_GE + (c & 1) * Sh::GE_SLOT); };
 
-  // strictly-upper 16x16 blocks of T' (strictly-lower ones of the stored
-  // T'^T) are zero and never rewritten
-  for (int i = threadIdx.x; i < 2 * C * C; i += Sh::NT) {
-    const int bi = i / (C * C), rr = (i / C) % C, ss = i % C;
-    if ((rr >> 4) > (ss >> 4)) sTp(bi)[rr * LDC + O::perm(ss)] = Elem<E>::from_f32(0.f);
-  }
-
-  if (wave == CHAIN) {
+  if (wave == CHAIN0 || wave == CHAIN1) {
     // =================== chain: the sequential state scan ====================
-    // S (DK rows x DVT columns, fp32) lives in the accumulators for the whole
-    // sequence: accS[ct][it] is the 16x16 tile (rows 16 it.., columns 16 ct..).
-    f32x4 accS[NCT][DK / 16];
+    // Two chain waves, each with NCW of the workgroup's 16-column tiles (the
+    // columns of S evolve independently; with one tile the second is idle).
+    // Its part of S (DK rows, fp32) lives in the accumulators for the whole
+    // sequence: accS[ct][it] is the 16x16 tile (rows 16 it.., columns
+    // 16 (CT0 + ct)..).
+    auto chain = [&](auto ct0_c) {
+    constexpr int CT0 = decltype(ct0_c)::value;
+    constexpr int NCW = CT0 < NCT ? (NCT - CT0 < Sh::NCW ? NCT - CT0 : Sh::NCW) : 0;
+    constexpr int NCW1 = NCW > 0 ? NCW : 1;
+    f32x4 accS[NCW1][DK / 16];
     const size_t sbase = (size_t)nh * DK * (size_t)dv;
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      const int col = jt * DVT + 16 * ct + li;
+    for (int ct = 0; ct < NCW; ++ct) {
+      const int col = jt * DVT + 16 * (CT0 + ct) + li;
 #pragma unroll
       for (int it = 0; it < DK / 16; ++it)
 #pragma unroll
@@ -500,21 +997,21 @@ __global__ __launch_bounds__(64 * kWaves) void kla_chunk_kernel(ChunkParams p) {
     }
     // chunk-start S as right operands, straight from the accumulators; also
     // published for the P waves (their Q S of that chunk)
-    Grp sb[NCT][NQG];
+    Grp sb[NCW1][NQG];
     auto publish = [&](int c) {
       Grp *suS = sSuS(c);
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct)
+      for (int ct = 0; ct < NCW; ++ct)
 #pragma unroll
         for (int q = 0; q < NQG; ++q) {
           sb[ct][q] = O::b_from_d(&accS[ct][q * TPG]);
-          suS[(ct * NQG + q) * 64 + lane] = sb[ct][q];
+          suS[((CT0 + ct) * NQG + q) * 64 + lane] = sb[ct][q];
         }
     };
     __syncthreads();
-    for (int i = -2; i <= nch; ++i) {
+    for (int i = -1; i <= nch; ++i) {
       if (i == -1) publish(0);
-      if (i >= 0 && i < nch) {
+      if (NCW > 0 && i >= 0 && i < nch) {
         const int c = i;
         const E *K = sK(c);
         const E *V = sV(c);
@@ -522,16 +1019,16 @@ __global__ __launch_bounds__(64 * kWaves) void kla_chunk_kernel(ChunkParams p) {
         const float *vec = sVec(c);
         Grp *suU = sSuU(c);
         // K S
-        f32x4 x[NCT][NB];
+        f32x4 x[NCW1][NB];
 #pragma unroll
         for (int rt = 0; rt < NB; ++rt) {
 #pragma unroll
-          for (int ct = 0; ct < NCT; ++ct) x[ct][rt] = zero4();
+          for (int ct = 0; ct < NCW; ++ct) x[ct][rt] = zero4();
 #pragma unroll
           for (int q = 0; q < NQG; ++q) {
             const Grp a = O::a_row(K + (16 * rt + li) * LDK, q * KG, lg);
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) x[ct][rt] = O::mma_grp(a, sb[ct][q], x[ct][rt]);
+            for (int ct = 0; ct < NCW; ++ct) x[ct][rt] = O::mma_grp(a, sb[ct][q], x[ct][rt]);
           }
         }
         // X = V - Diag(Gam) K S
@@ -539,34 +1036,34 @@ __global__ __launch_bounds__(64 * kWaves) void kla_chunk_kernel(ChunkParams p) {
         for (int rt = 0; rt < NB; ++rt) {
           const f32x4 gm = *reinterpret_cast<const f32x4 *>(vec + C + 16 * rt + 4 * lg);
 #pragma unroll
-          for (int ct = 0; ct < NCT; ++ct) x[ct][rt] = O::col4(V, LDV, 16 * rt, 16 * ct, lane) - gm * x[ct][rt];
+          for (int ct = 0; ct < NCW; ++ct) x[ct][rt] = O::col4(V, LDV, 16 * rt, 16 * (CT0 + ct), lane) - gm * x[ct][rt];
         }
-        Grp xb[NCT][NCG];
+        Grp xb[NCW1][NCG];
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct)
+        for (int ct = 0; ct < NCW; ++ct)
 #pragma unroll
           for (int q = 0; q < NCG; ++q) xb[ct][q] = O::b_from_d(&x[ct][q * TPG]);
         // U~ = T' X   (T' lower triangular: skip the zero groups; T' is stored
         // transposed)
-        f32x4 u[NCT][NB];
+        f32x4 u[NCW1][NB];
 #pragma unroll
         for (int rt = 0; rt < NB; ++rt) {
 #pragma unroll
-          for (int ct = 0; ct < NCT; ++ct) u[ct][rt] = zero4();
+          for (int ct = 0; ct < NCW; ++ct) u[ct][rt] = zero4();
 #pragma unroll
           for (int q = 0; q * KG < 16 * (rt + 1); ++q) {
             const Grp a = O::a_trans(TpT, LDC, q * KG, 16 * rt, lane);
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) u[ct][rt] = O::mma_grp(a, xb[ct][q], u[ct][rt]);
+            for (int ct = 0; ct < NCW; ++ct) u[ct][rt] = O::mma_grp(a, xb[ct][q], u[ct][rt]);
           }
         }
         // U~ groups for the P waves; Diag(d) U~ groups for the update
-        Grp dub[NCT][NCG];
+        Grp dub[NCW1][NCG];
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct)
+        for (int ct = 0; ct < NCW; ++ct)
 #pragma unroll
           for (int q = 0; q < NCG; ++q) {
-            suU[(ct * NCG + q) * 64 + lane] = O::b_from_d(&u[ct][q * TPG]);
+            suU[((CT0 + ct) * NCG + q) * 64 + lane] = O::b_from_d(&u[ct][q * TPG]);
             f32x4 du[TPG];
 #pragma unroll
             for (int tt = 0; tt < TPG; ++tt) {
@@ -580,12 +1077,12 @@ __global__ __launch_bounds__(64 * kWaves) void kla_chunk_kernel(ChunkParams p) {
 #pragma unroll
         for (int it = 0; it < DK / 16; ++it) {
 #pragma unroll
-          for (int ct = 0; ct < NCT; ++ct) accS[ct][it] = gC * accS[ct][it];
+          for (int ct = 0; ct < NCW; ++ct) accS[ct][it] = gC * accS[ct][it];
 #pragma unroll
           for (int q = 0; q < NCG; ++q) {
             const Grp a = O::a_trans(K, LDK, q * KG, 16 * it, lane);
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) accS[ct][it] = O::mma_grp(a, dub[ct][q], accS[ct][it]);
+            for (int ct = 0; ct < NCW; ++ct) accS[ct][it] = O::mma_grp(a, dub[ct][q], accS[ct][it]);
           }
         }
         if (c + 1 < nch) publish(c + 1);
@@ -594,21 +1091,25 @@ __global__ __launch_bounds__(64 * kWaves) void kla_chunk_kernel(ChunkParams p) {
     }
     if (p.sfin) {
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        const int col = jt * DVT + 16 * ct + li;
+      for (int ct = 0; ct < NCW; ++ct) {
+        const int col = jt * DVT + 16 * (CT0 + ct) + li;
 #pragma unroll
         for (int it = 0; it < DK / 16; ++it)
 #pragma unroll
           for (int j = 0; j < 4; ++j) p.sfin[sbase + (size_t)(16 * it + 4 * lg + j) * dv + col] = accS[ct][it][j];
       }
     }
+    };
+    if (wave == CHAIN0)
+      chain(std::integral_constant<int, 0>{});
+    else
+      chain(std::integral_constant<int, Sh::NCW>{});
   } else if (wave == PW0 || wave == PW1) {
-    // =================== P waves: scores and output rows ======================
-    // For its row blocks rt, a P wave forms the causal scores of chunk i as
-    // P^T = K Q^T (the accumulator layout of P^T is exactly the left-operand
-    // layout P needs in P U~, so P stays in registers), and Diag(Gam) Q S with
-    // the chunk-start state; one step later, when the chain has U~, it adds
-    // P U~ and writes those output rows.
+    // =================== P waves: output rows ================================
+    // For its row blocks rt, a P wave forms Diag(Gam) Q S of chunk i with the
+    // chunk-start state and takes that chunk's causal scores P (left-operand
+    // groups from the prep kernel) into registers; one step later, when the
+    // chain has U~, it adds P U~ and writes those output rows.
     auto pwave = [&](auto part_c) {
       constexpr int part = decltype(part_c)::value;
       using BL = OwnBlocks<NB, part>;
@@ -621,7 +1122,7 @@ __global__ __launch_bounds__(64 * kWaves) void kla_chunk_kernel(ChunkParams p) {
       Grp pa[NOW1][NCG];    // its P rows as left operands
       qin.issue(gq + tok0_of(0) * DK, nrow_of(0), lane);
       __syncthreads();
-      for (int i = -2; i <= nch; ++i) {
+      for (int i = -1; i <= nch; ++i) {
         // chunk i first, then the output of chunk i-1: its stores then drain
         // while this wave waits at the barrier
         f32x4 ao_n[NCT][NOW1];
@@ -629,53 +1130,20 @@ __global__ __launch_bounds__(64 * kWaves) void kla_chunk_kernel(ChunkParams p) {
         if (NOWN > 0 && i >= 0 && i < nch) {
           // ---- chunk i: P rows and Diag(Gam) Q S ----
           const int c = i;
-          const int nrow = nrow_of(c);
           qin.put(sQ, LDK, lane, [](int lr, int) { return lr; });
           qin.issue(gq + tok0_of(clampc(c + 1)) * DK, nrow_of(clampc(c + 1)), lane);
-          const E *K = sK(c);
           const float *vec = sVec(c);
           const Grp *suS = sSuS(c);
+          const Grp *sP = reinterpret_cast<const Grp *>(reinterpret_cast<const char *>(sTp(c)) + TL::OFF_P);
+#pragma unroll
+          for (int k = 0; k < NOWN; ++k)
+#pragma unroll
+            for (int q = 0; q * KG < 16 * (BL::at(k) + 1); ++q) pa_n[k][q] = sP[TL::pgroup(BL::at(k), q) * 64 + lane];
           Grp qa[NOW1][NQG];
 #pragma unroll
           for (int k = 0; k < NOWN; ++k)
 #pragma unroll
             for (int q = 0; q < NQG; ++q) qa[k][q] = O::a_row(sQ + (16 * k + li) * LDK, q * KG, lg);
-          // P^T tiles: D[s][r] = K_s . q_r, lane column r = 16 rt + li, rows s = 16 st + 4 lg + j
-          f32x4 pt[NOW1][NB];
-#pragma unroll
-          for (int st = 0; st < NB; ++st) {
-            if (st > BL::at(NOWN - 1)) continue;
-            Grp kb[NQG];
-#pragma unroll
-            for (int q = 0; q < NQG; ++q) kb[q] = O::a_row(K + (16 * st + li) * LDK, q * KG, lg);
-#pragma unroll
-            for (int k = 0; k < NOWN; ++k) {
-              if (st > BL::at(k)) continue;
-              pt[k][st] = zero4();
-#pragma unroll
-              for (int q = 0; q < NQG; ++q) pt[k][st] = O::mma_grp(kb[q], qa[k][q], pt[k][st]);
-            }
-          }
-          // decay and causal mask, then the P rows as left-operand groups
-#pragma unroll
-          for (int k = 0; k < NOWN; ++k) {
-            const int rt = BL::at(k);
-            const float gr = vec[16 * rt + li];
-#pragma unroll
-            for (int st = 0; st <= rt; ++st) {
-              const f32x4 gs = *reinterpret_cast<const f32x4 *>(vec + 16 * st + 4 * lg);
-#pragma unroll
-              for (int j = 0; j < 4; ++j)
-                pt[k][st][j] = (st < rt || 4 * lg + j <= li) ? pt[k][st][j] * __expf(gr - gs[j]) : 0.f;
-            }
-#pragma unroll
-            for (int q = 0; q * KG < 16 * (rt + 1); ++q) {
-              f32x4 tl[TPG];
-#pragma unroll
-              for (int tt = 0; tt < TPG; ++tt) tl[tt] = (q * TPG + tt <= rt) ? pt[k][q * TPG + tt] : zero4();
-              pa_n[k][q] = O::b_from_d(tl);
-            }
-          }
           // Diag(Gam) Q S
 #pragma unroll
           for (int ct = 0; ct < NCT; ++ct) {
@@ -761,7 +1229,7 @@ __global__ __launch_bounds__(64 * kWaves) void kla_chunk_kernel(ChunkParams p) {
 #pragma unroll
           for (int k = 0; k < NOWN; ++k)
 #pragma unroll
-            for (int q = 0; q < NCG; ++q) pa[k][q] = pa_n[k][q];
+            for (int q = 0; q * KG < 16 * (BL::at(k) + 1); ++q) pa[k][q] = pa_n[k][q];
         }
         lds_barrier();
       }
@@ -770,241 +1238,34 @@ __global__ __launch_bounds__(64 * kWaves) void kla_chunk_kernel(ChunkParams p) {
       pwave(std::integral_constant<int, 0>{});
     else
       pwave(std::integral_constant<int, 1>{});
-  } else if (wave == GRAM0 || wave == GRAM1) {
-    // =================== Gram waves: chunk i+2 ================================
-    auto gram = [&](auto part_c) {
-      constexpr int part = decltype(part_c)::value;
-      using BL = GramBlocks<NB, part>;
-      using OB = OwnBlocks<NB, part>;
-      RowLoad<E, DK, BL> kin;
-      auto issue = [&](int c) { kin.issue(gk + tok0_of(c) * DK, nrow_of(c), lane); };
-      float *gp = reinterpret_cast<float *>(smem + Sh::OFF_GP + part * Sh::GPRIV);
-      float *sGam = gp;          // [C]
-      float *sNrm = gp + C;      // [C]
-      float *sBet = gp + 2 * C;  // [C]
-      issue(0);
-      __syncthreads();
-      for (int i = -2; i <= nch; ++i) {
-        const int c = i + 2;
-        if (OB::N > 0 && c >= 0 && c < nch) {
-          const int nrow = nrow_of(c);
-          E *K = sK(c);
-          E *Ablk = sA(c);
-          float *Td = sTd(c);
-          float *vec = sVec(c);
-          // the chunk's K rows into the ring (rows both Gram waves read are
-          // written by both, with identical values), then the next chunk's loads
-          kin.put(K, LDK, lane, [](int, int row) { return row; });
-          issue(clampc(c + 1));
-          const float *ge = sGE(c);
-          const float gl = (lane < C) ? ge[lane] : 0.f;
-          const float el = (lane < C) ? ge[C + lane] : 0.f;
-          Grp kb[BL::N > 0 ? BL::N : 1][NQG];
-#pragma unroll
-          for (int k = 0; k < BL::N; ++k)
-#pragma unroll
-            for (int q = 0; q < NQG; ++q) kb[k][q] = O::a_row(K + (16 * k + li) * LDK, q * KG, lg);
-          // Gram tiles of the owned rows
-          f32x4 G[NB][NB];
-#pragma unroll
-          for (int rt = 0; rt < NB; ++rt) {
-            if (!owns_block(NB, part, rt)) continue;
-#pragma unroll
-            for (int st = 0; st <= rt; ++st) {
-              G[rt][st] = zero4();
-#pragma unroll
-              for (int q = 0; q < NQG; ++q) G[rt][st] = O::mma_grp(kb[rt][q], kb[st][q], G[rt][st]);
-            }
-            // ||k_r||^2 of row 16 rt + li sits on the diagonal of tile (rt, rt):
-            // lane group li >> 2, element li & 3
-            const f32x4 d = G[rt][rt];
-            const int j = li & 3;
-            const float nr = j == 0 ? d[0] : j == 1 ? d[1] : j == 2 ? d[2] : d[3];
-            if (lg == (li >> 2)) sNrm[16 * rt + li] = nr;
-          }
-          // gate scan and beta (lane = chunk row); beta of rows beyond the
-          // sequence end is 0 (not 0/0 when eps = 0)
-          const float gam = wave_inclusive_scan(gl);
-          const float gamC = lane_value(gam, C - 1);
-          if (lane < C) {
-            sGam[lane] = gam;
-            if (part == 0) {
-              vec[lane] = gam;
-              vec[C + lane] = __expf(gam);             // Gam_r
-              vec[2 * C + lane] = __expf(gamC - gam);  // d_r
-            }
-            if (owns_block(NB, part, lane >> 4)) {
-              const float beta = (lane < nrow) ? el / (sNrm[lane] + p.eps) : 0.f;
-              sBet[lane] = beta;
-              vec[3 * C + lane] = beta;
-            }
-          }
-          // A = beta_r (K K^T)_rs exp(gamma_r - gamma_s), r > s
-#pragma unroll
-          for (int rt = 0; rt < NB; ++rt) {
-            if (!owns_block(NB, part, rt)) continue;
-            const f32x4 gr4 = *reinterpret_cast<const f32x4 *>(sGam + 16 * rt + 4 * lg);
-            const f32x4 br4 = *reinterpret_cast<const f32x4 *>(sBet + 16 * rt + 4 * lg);
-#pragma unroll
-            for (int st = 0; st <= rt; ++st) {
-              const float gs = sGam[16 * st + li];
-              const f32x4 acc = G[rt][st];
-              f32x4 av;
-              if (st < rt) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) av[j] = br4[j] * acc[j] * __expf(gr4[j] - gs);
-                // off-diagonal block, stored transposed: A^T[s'][r']
-                store4(Ablk + (rt * (rt - 1) / 2 + st) * 16 * LDA + li * LDA + 4 * lg, av);
-              } else {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                  const bool below = 4 * lg + j > li;
-                  const float dec = below ? __expf(gr4[j] - gs) : 0.f;
-                  av[j] = below ? br4[j] * acc[j] * dec : 0.f;
-                }
-                // diagonal block, fp32, stored transposed (At[s'][r']) for the solve
-                *reinterpret_cast<f32x4 *>(Td + (rt * 16 + li) * LDD + 4 * lg) = av;
-              }
-            }
-          }
-        }
-        lds_barrier();
-      }
-    };
-    if (wave == GRAM0)
-      gram(std::integral_constant<int, 0>{});
-    else
-      gram(std::integral_constant<int, 1>{});
-  } else if (wave == TSOLVE) {
-    // =================== T' of chunk i+1 ======================================
-    // T' = T Diag(beta), T = (I + A)^-1, stored transposed (row s of T'^T is
-    // column s of T') with grouped columns, so a lane writes 4 consecutive
-    // entries at once; the chain reads it with transposing LDS reads.
-    auto solve = [&](int c) {
-      using M = Mm16<E>;
-      E *TpT = sTp(c);
-      const E *Ablk = sA(c);
-      float *Td = sTd(c);
-      const float *beta = sVec(c) + 3 * C;
-      // diagonal blocks T_bb = (I + A_bb)^-1 by column-parallel forward
-      // substitution in fp32: lane = (block lg, column li).  A_bb arrives
-      // transposed (row s of At = column s of A); row s+1 is read while row s
-      // is applied.  T_bb replaces it, also transposed.
-      if (lg < NB) {
-        float *At = Td + lg * 16 * LDD;
-        float x[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) x[r] = (r == li) ? 1.f : 0.f;
-        f32x4 cur[4], nxt[4];
-#pragma unroll
-        for (int qd = 0; qd < 4; ++qd) cur[qd] = *reinterpret_cast<const f32x4 *>(At + 4 * qd);
-#pragma unroll
-        for (int s = 0; s < 15; ++s) {
-          if (s + 1 < 15) {
-#pragma unroll
-            for (int qd = 0; qd < 4; ++qd)
-              if (4 * qd + 3 > s + 1) nxt[qd] = *reinterpret_cast<const f32x4 *>(At + (s + 1) * LDD + 4 * qd);
-          }
-#pragma unroll
-          for (int r = s + 1; r < 16; ++r) x[r] = fmaf(-cur[r >> 2][r & 3], x[s], x[r]);
-#pragma unroll
-          for (int qd = 0; qd < 4; ++qd) cur[qd] = nxt[qd];
-        }
-        float *dst = At + li * LDD;
-        const float bs = beta[16 * lg + li];
-#pragma unroll
-        for (int qd = 0; qd < 4; ++qd) {
-          const f32x4 t4 = {x[4 * qd], x[4 * qd + 1], x[4 * qd + 2], x[4 * qd + 3]};
-          *reinterpret_cast<f32x4 *>(dst + 4 * qd) = t4;
-          store4(TpT + (16 * lg + li) * LDC + O::perm(16 * lg + 4 * qd), bs * t4);
-        }
-      }
-      // off-diagonal blocks level by level: T_ij = -T_ii sum_m A_im T_mj
-      if constexpr (NB > 1) {
-        f32x4 Toff[NB][NB];
-#pragma unroll
-        for (int dist = 1; dist < NB; ++dist) {
-#pragma unroll
-          for (int i = dist; i < NB; ++i) {
-            const int j = i - dist;
-            f32x4 y = zero4();
-#pragma unroll
-            for (int m = j; m < i; ++m) {
-              // A_im[li][4lg + e] (block stored transposed); B operand T_mj[4lg + e][li]
-              const typename M::Op a = M::ld_t(Ablk + (i * (i - 1) / 2 + m) * 16 * LDA, LDA, lane);
-              const f32x4 bt = (m == j) ? *reinterpret_cast<const f32x4 *>(Td + (j * 16 + li) * LDD + 4 * lg)
-                                        : Toff[m][j];
-              y = M::mma(a, M::cvt(bt), y);
-            }
-            // A operand T_ii[li][4lg + e] = T_ii^T[4lg + e][li]
-            f32x4 ti;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) ti[e] = Td[(i * 16 + 4 * lg + e) * LDD + li];
-            const f32x4 t = -M::mma(M::cvt(ti), M::cvt(y), zero4());
-            Toff[i][j] = t;
-            // T'^T[16 j + li][16 i + 4 lg + e] = T_ij[4 lg + e][li] beta_(16 j + li)
-            store4(TpT + (16 * j + li) * LDC + O::perm(16 * i + 4 * lg), beta[16 * j + li] * t);
-          }
-        }
-      }
-    };
+  } else if (wave == LOADK) {
+    // =================== K rows of chunk i+1 ==================================
+    RowLoad<E, DK, AllBlocks<NB>> kin;
+    kin.issue(gk + tok0_of(0) * DK, nrow_of(0), lane);
     __syncthreads();
-    for (int i = -2; i <= nch; ++i) {
-      if (i + 1 >= 0 && i + 1 < nch) solve(i + 1);
+    for (int i = -1; i <= nch; ++i) {
+      if (i + 1 < nch) {
+        kin.put(sK(i + 1), LDK, lane, [](int, int row) { return row; });
+        kin.issue(gk + tok0_of(clampc(i + 2)) * DK, nrow_of(clampc(i + 2)), lane);
+      }
       lds_barrier();
     }
   } else {
-    // =================== V loader: V slice of chunk i+1 =======================
-    constexpr int V16 = 16 / (int)sizeof(E);  // elements per 16-byte piece
-    constexpr int PPR = DVT / V16;            // 16-byte pieces per V row slice
-    constexpr int NVP = (C * PPR + 63) / 64;  // pieces per lane
-    uint4 vreg[NVP];
-    const size_t vcol0 = (size_t)jt * DVT;
+    // =================== T'^T, gamma/Gam/d, P and the V slice of chunk i+1 =====
+    PieceCopy<TL::BYTES / 16> tin;
+    VSliceLoad<E, C, DVT> vin;
     auto fetch = [&](int c) {
-      const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(gv + tok0_of(c) * dv, nrow_of(c) * dv * (int)sizeof(E));
-#pragma unroll
-      for (int k = 0; k < NVP; ++k) {
-        const int pc = min(lane + 64 * k, C * PPR - 1);
-        const int r = pc / PPR, cq = pc % PPR;
-        vreg[k] = buffer_ld16(rs, (r * dv + (int)vcol0 + cq * V16) * (int)sizeof(E));
-      }
+      tin.issue(ws + (size_t)(slot0 + c) * TL::BYTES, lane);
+      vin.issue(gv + tok0_of(c) * dv, nrow_of(c), dv, jt * DVT, lane);
     };
-    auto store = [&](int c) {
-      E *V = sV(c);
-#pragma unroll
-      for (int k = 0; k < NVP; ++k) {
-        const int pc = lane + 64 * k;
-        if (pc < C * PPR) {
-          const int r = pc / PPR, cq = pc % PPR;
-          *reinterpret_cast<uint4 *>(V + r * LDV + cq * V16) = vreg[k];
-        }
-      }
-    };
-    // g and eta of chunk c are staged at step c-3 (the Gram waves use them at
-    // step c-2); chunk 0 before the loop
-    E graw = Elem<E>::from_f32(0.f), eraw = Elem<E>::from_f32(0.f);
-    auto fetch_ge = [&](int c) {
-      const int lr = min(lane, nrow_of(c) - 1);
-      graw = gg[tok0_of(c) + lr];
-      eraw = geta[tok0_of(c) + lr];
-    };
-    auto store_ge = [&](int c) {
-      float *ge = sGE(c);
-      if (lane < C) {
-        ge[lane] = (lane < nrow_of(c)) ? Elem<E>::to_f32(graw) : 0.f;
-        ge[C + lane] = Elem<E>::to_f32(eraw);
-      }
-    };
-    fetch_ge(0);
-    store_ge(0);
-    fetch_ge(clampc(1));
     fetch(0);
     __syncthreads();
-    for (int i = -2; i <= nch; ++i) {
-      if (i + 1 >= 0 && i + 1 < nch) store(i + 1);
-      if (i + 3 < nch) store_ge(i + 3);
-      fetch(clampc(i + 2));
-      fetch_ge(clampc(i + 4));
+    for (int i = -1; i <= nch; ++i) {
+      if (i + 1 < nch) {
+        tin.put(sTp(i + 1), lane);
+        vin.put(sV(i + 1), LDV, lane);
+        fetch(clampc(i + 2));
+      }
       lds_barrier();
     }
   }
@@ -1013,6 +1274,16 @@ __global__ __launch_bounds__(64 * kWaves) void kla_chunk_kernel(ChunkParams p) {
 // ---------------------------------------------------------------------------
 // host-side dispatch
 // ---------------------------------------------------------------------------
+template <typename E, int C>
+static size_t workspace_bytes_t(const ChunkArgs &a) {
+  return (size_t)a.H * slots_per_head(a.cu_seqlens != nullptr, a.B, a.T, a.num_seqs, C) * TpLayout<E, C>::BYTES;
+}
+
+size_t chunk_workspace_bytes(const ChunkArgs &a) {
+  if (a.dtype == 0) return workspace_bytes_t<bf16, 64>(a);
+  return a.chunk == 16 ? workspace_bytes_t<float, 16>(a) : workspace_bytes_t<float, 64>(a);
+}
+
 template <typename E, int C, int DK, int NCT>
 static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t st) {
   using Sh = ChunkShape<E, C, DK, NCT>;
@@ -1027,13 +1298,23 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t st) {
   p.o = a.o;
   p.sfin = a.final_state;
   p.cu = a.cu_seqlens;
+  p.ws = static_cast<char *>(a.workspace);
   p.H = a.H;
   p.T = a.T;
   p.dv = a.dv;
   p.n_tiles = a.dv / Sh::DVT;
+  p.nseq = a.num_seqs;
+  p.nslot = slots_per_head(a.cu_seqlens != nullptr, a.B, a.T, a.num_seqs, C);
   const long long nblk = (long long)a.num_seqs * a.H * p.n_tiles;
   p.remap = (nblk % 8 == 0) ? 1 : 0;
   if (nblk == 0) return hipSuccess;
+  if ((long long)a.B * a.T > 0 && p.nslot > 0) {
+    const unsigned runs = (unsigned)((p.nslot + kPrepSlots - 1) / kPrepSlots);
+    hipLaunchKernelGGL((kla_chunk_prep_kernel<E, C, DK>), dim3(runs, (unsigned)a.H),
+                       dim3(PrepShape<E, C, DK>::NT), 0, st, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL((kla_chunk_kernel<E, C, DK, NCT>), dim3((unsigned)nblk), dim3(Sh::NT), 0, st, p);
   return hipGetLastError();
 }

@@ -13,7 +13,7 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["chunk_fwd", "decode_step", "lib", "lib_path", "KlaError",
+__all__ = ["chunk_fwd", "chunk_workspace_bytes", "decode_step", "lib", "lib_path", "KlaError",
            "KLA_DT_BF16", "KLA_DT_F32"]
 
 KLA_DT_BF16 = 0
@@ -46,10 +46,12 @@ def lib() -> ctypes.CDLL:
                 f"{path} is not built: run `python -c 'import __graft_entry__ as g; g.build()'` "
                 "(or python gated_delta_rule_kla_amd/build.py)")
         L = ctypes.CDLL(path)
-        vp, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+        vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
         L.kla_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, f32, vp, vp, vp, vp, vp,
-                                    i32, i32, i32, i32, i32, i32, i32, i32, vp]
+                                    i32, i32, i32, i32, i32, i32, i32, vp, sz, i32, vp]
         L.kla_chunk_fwd.restype = i32
+        L.kla_chunk_workspace_bytes.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, i32, i32]
+        L.kla_chunk_workspace_bytes.restype = sz
         L.kla_decode_step.argtypes = [vp, vp, vp, vp, vp, f32, vp, vp,
                                       i32, i32, i32, i32, i32, vp]
         L.kla_decode_step.restype = i32
@@ -101,6 +103,7 @@ def chunk_fwd(
     cu_seqlens_host: Optional[torch.Tensor] = None,
     out: Optional[torch.Tensor] = None,
     final_state: Optional[torch.Tensor] = None,
+    workspace: Optional[torch.Tensor] = None,
 ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """KLA chunkwise prefill (kla_chunk_fwd).
 
@@ -108,7 +111,9 @@ def chunk_fwd(
     fp32 on one GPU.  initial_state: [N, H, dk, dv] fp32 or None.  cu_seqlens:
     int32 [N + 1] on the GPU (B must be 1) or None.  Returns (o, final_state).
     ``final_state`` may be passed as the same tensor as ``initial_state`` to
-    update it in place.
+    update it in place.  ``workspace`` (uint8, on the GPU, at least
+    chunk_workspace_bytes(...) bytes) is taken from torch's caching allocator
+    on the current stream when not given.
     """
     dev = q.device
     if dev.type != "cuda":
@@ -144,13 +149,33 @@ def chunk_fwd(
     if final_state is not None:
         _need(final_state, "final_state", torch.float32, (N, H, dk, dv), dev)
     host_ptr = None if cu_seqlens_host is None else cu_seqlens_host.data_ptr()
+    ws_bytes = lib().kla_chunk_workspace_bytes(_ptr(cu_seqlens), host_ptr, N, B, H, T, dk, dv, int(chunk),
+                                               _DTYPES[dtype])
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    elif workspace.device != dev or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor on the inputs' device")
     st = lib().kla_chunk_fwd(
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(eta), float(eps),
         _ptr(initial_state), _ptr(out), _ptr(final_state),
-        _ptr(cu_seqlens), host_ptr, N, B, H, T, dk, dv, int(chunk), _DTYPES[dtype],
-        _stream(dev))
+        _ptr(cu_seqlens), host_ptr, N, B, H, T, dk, dv, int(chunk),
+        _ptr(workspace), workspace.numel(), _DTYPES[dtype], _stream(dev))
     _check("kla_chunk_fwd", st)
     return out, final_state
+
+
+def chunk_workspace_bytes(B: int, H: int, T: int, dk: int, dv: int, chunk: int = 64,
+                          dtype: torch.dtype = torch.bfloat16,
+                          cu_seqlens_host: Optional[torch.Tensor] = None) -> int:
+    """Workspace bytes kla_chunk_fwd needs (kla_chunk_workspace_bytes); 0 for
+    arguments it would reject.  With packed sequences pass the host int32
+    cu_seqlens (B must be 1)."""
+    if cu_seqlens_host is not None:
+        cu = cu_seqlens_host.to(torch.int32).contiguous()
+        # the device pointer is only tested for NULL here
+        return lib().kla_chunk_workspace_bytes(ctypes.c_void_p(16), cu.data_ptr(), cu.numel() - 1, B, H, T,
+                                               dk, dv, int(chunk), _DTYPES[dtype])
+    return lib().kla_chunk_workspace_bytes(None, None, B, B, H, T, dk, dv, int(chunk), _DTYPES[dtype])
 
 
 def decode_step(

@@ -22,7 +22,8 @@
  * Conventions common to every entry point
  *   - Every data pointer is DEVICE memory (allocated by the caller, e.g. with
  *     PyTorch) unless its comment says "host".  The library allocates no
- *     device memory and keeps no state between calls.
+ *     device memory and keeps no state between calls: scratch memory a call
+ *     needs (kla_chunk_fwd's workspace) is passed in by the caller.
  *   - Tensors are dense and contiguous, row-major, in the layouts stated per
  *     argument.  All data pointers must be 16-byte aligned (cu_seqlens:
  *     4-byte).
@@ -60,6 +61,7 @@ typedef enum {
     KLA_ERR_UNSUPPORTED = -4, /* valid but not compiled: see supported shapes    */
     KLA_ERR_SEQLENS = -5,     /* cu_seqlens not 0 = c0 <= c1 <= ... <= cN = T    */
     KLA_ERR_EPS = -6,         /* eps < 0, NaN or infinite                        */
+    KLA_ERR_WORKSPACE = -7,   /* workspace NULL or below kla_chunk_workspace_bytes */
     KLA_ERR_ALIGN = -8,       /* a data pointer is not 16-byte aligned           */
     KLA_ERR_HIP = -9          /* the HIP runtime rejected a launch               */
 } kla_status_t;
@@ -94,6 +96,18 @@ typedef enum {
  *                  to [0, T], so a device array that disagrees with the mirror
  *                  cannot cause an out-of-bounds access.
  *   num_seqs  N (must equal B when cu_seqlens is NULL)
+ *   workspace, workspace_bytes  device scratch of at least
+ *                  kla_chunk_workspace_bytes(...) bytes for the same arguments
+ *                  (16-byte aligned; may be NULL when that size is 0).  Owned
+ *                  by the caller; its contents need no initialisation and are
+ *                  meaningless after the call.  Calls that overlap in time
+ *                  must not share a workspace.
+ *
+ * Two kernels run on `stream`: a prep kernel computes, for every (chunk,
+ * head) in parallel, the S-independent part of the block solver (beta, the
+ * decay weights, K K^T, T, T' = T Diag(beta) and the decayed causal scores
+ * of Q K^T) into the workspace; the scan kernel then walks each sequence's
+ * chunks with the state in registers.
  *
  * Supported: dtype BF16 with chunk 64 and dk in {64, 128}; dtype F32 with
  * chunk 16 and dk in {16, 32, 64, 128}, or chunk 64 and dk in {16, 32}; for
@@ -105,7 +119,18 @@ kla_status_t kla_chunk_fwd(const void *q, const void *k, const void *v,
                            const float *initial_state, void *o, float *final_state,
                            const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
                            int num_seqs, int B, int H, int T, int dk, int dv, int chunk,
+                           void *workspace, size_t workspace_bytes,
                            kla_dtype_t dtype, void *stream);
+
+/*
+ * kla_chunk_workspace_bytes -- device workspace kla_chunk_fwd needs for these
+ * arguments (the same meaning as there; host-only, no HIP call).  16,128
+ * bytes per (64-token chunk, head) in bf16.  Returns 0 when no workspace is
+ * needed (no tokens) and also for arguments kla_chunk_fwd would reject.
+ */
+size_t kla_chunk_workspace_bytes(const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
+                                 int num_seqs, int B, int H, int T, int dk, int dv, int chunk,
+                                 kla_dtype_t dtype);
 
 /*
  * kla_decode_step -- one recurrent step for N sequences x H heads.
@@ -136,7 +161,7 @@ const char *kla_status_str(kla_status_t s);
 /* ABI version of this header (incremented on any incompatible change). */
 int kla_abi_version(void);
 
-#define KLA_ABI_VERSION 1
+#define KLA_ABI_VERSION 2
 
 #ifdef __cplusplus
 }

@@ -16,7 +16,7 @@ HEADER = os.path.join(ROOT, "include", "kla.h")
 pytestmark = pytest.mark.skipif(not os.path.exists(kla.lib_path()),
                                 reason="libkla.so not built (run __graft_entry__.build())")
 
-OK, E_NULL, E_SHAPE, E_DTYPE, E_UNSUP, E_SEQ, E_EPS, E_ALIGN, E_HIP = 0, -1, -2, -3, -4, -5, -6, -8, -9
+OK, E_NULL, E_SHAPE, E_DTYPE, E_UNSUP, E_SEQ, E_EPS, E_WS, E_ALIGN, E_HIP = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9
 FAKE = 0x7F0000000000  # never dereferenced: every case below fails validation first
 
 
@@ -28,7 +28,8 @@ def _declared():
 def test_exports_every_declared_symbol():
     L = kla.lib()
     names = _declared()
-    assert set(names) >= {"kla_chunk_fwd", "kla_decode_step", "kla_status_str", "kla_abi_version"}
+    assert set(names) >= {"kla_chunk_fwd", "kla_chunk_workspace_bytes", "kla_decode_step", "kla_status_str",
+                          "kla_abi_version"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -40,18 +41,27 @@ def test_abi_version_matches_header():
 
 def test_status_strings():
     L = kla.lib()
-    for s in (OK, E_NULL, E_SHAPE, E_DTYPE, E_UNSUP, E_SEQ, E_EPS, E_ALIGN, E_HIP, -77):
+    for s in (OK, E_NULL, E_SHAPE, E_DTYPE, E_UNSUP, E_SEQ, E_EPS, E_WS, E_ALIGN, E_HIP, -77):
         txt = L.kla_status_str(s)
         assert isinstance(txt, bytes) and len(txt) > 0
 
 
+def _ws_bytes(**kw):
+    a = dict(cu=None, cuh=None, N=2, B=2, H=4, T=100, dk=128, dv=128, chunk=64, dtype=0)
+    a.update(kw)
+    return kla.lib().kla_chunk_workspace_bytes(a["cu"], a["cuh"], a["N"], a["B"], a["H"], a["T"], a["dk"],
+                                               a["dv"], a["chunk"], a["dtype"])
+
+
 def _chunk(**kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, eta=FAKE, eps=1e-6, s0=None, o=FAKE, sf=FAKE,
-             cu=None, cuh=None, N=2, B=2, H=4, T=100, dk=128, dv=128, chunk=64, dtype=0)
+             cu=None, cuh=None, N=2, B=2, H=4, T=100, dk=128, dv=128, chunk=64, ws=FAKE,
+             ws_bytes=1 << 40, dtype=0)
     a.update(kw)
     return kla.lib().kla_chunk_fwd(a["q"], a["k"], a["v"], a["g"], a["eta"], a["eps"], a["s0"],
                                    a["o"], a["sf"], a["cu"], a["cuh"], a["N"], a["B"], a["H"],
-                                   a["T"], a["dk"], a["dv"], a["chunk"], a["dtype"], None)
+                                   a["T"], a["dk"], a["dv"], a["chunk"], a["ws"], a["ws_bytes"],
+                                   a["dtype"], None)
 
 
 def _decode(**kw):
@@ -79,6 +89,9 @@ def _decode(**kw):
     (dict(k=FAKE + 8), E_ALIGN),
     (dict(sf=FAKE + 4), E_ALIGN),
     (dict(cu=FAKE), E_NULL),                     # device cu_seqlens without the host mirror
+    (dict(ws=None), E_WS),
+    (dict(ws_bytes=1000), E_WS),                 # two 64-token chunks x 2 sequences x 4 heads need more
+    (dict(ws=FAKE + 8), E_ALIGN),
 ])
 def test_chunk_fwd_rejects(kw, code):
     assert _chunk(**kw) == code
@@ -129,3 +142,45 @@ def test_binding_refuses_cpu_tensors():
         kla.chunk_fwd(x, x, x, x[..., 0], x[..., 0])
     with pytest.raises(ValueError):
         kla.decode_step(x[0], x[0], x[0], x[0, :, 0], x[0, :, 0], 1e-6, x)
+
+
+def test_workspace_bytes():
+    # bf16, chunk 64, per (chunk, head): one 64 x 72 bf16 T'^T image, gamma, Gam, d (3 x 64 fp32)
+    # and the causal scores as 1 + 1 + 2 + 2 left-operand groups of 64 lanes x 16 bytes
+    per = 64 * 72 * 2 + 3 * 64 * 4 + 6 * 64 * 16
+    assert _ws_bytes() == 2 * 4 * 2 * per                  # B=2 rows x ceil(100/64)=2 chunks x H=4
+    assert _ws_bytes(T=128) == 2 * 4 * 2 * per
+    assert _ws_bytes(T=129) == 2 * 4 * 3 * per
+    assert _ws_bytes(T=0) == 0 and _ws_bytes(N=0, B=0) == 0
+    assert _ws_bytes(dk=96) == 0                           # unsupported -> 0
+    # fp32 chunk 16: 16 x 20 fp32 image + 3 x 16 fp32 + one group of scores
+    assert _ws_bytes(dtype=1, chunk=16, dk=32, dv=16) == 2 * 4 * 7 * (16 * 20 * 4 + 3 * 16 * 4 + 64 * 16)
+    # fp32 chunk 64: 64 x 68 fp32 image + 3 x 64 fp32 + 1 + 2 + 3 + 4 groups
+    assert _ws_bytes(dtype=1, chunk=64, dk=32, dv=16) == 2 * 4 * 2 * (64 * 68 * 4 + 3 * 64 * 4 + 10 * 64 * 16)
+    # packed sequences: floor(T / C) + N + 1 slots per head
+    arr = (ctypes.c_int32 * 4)(0, 30, 60, 100)
+    assert _ws_bytes(cu=FAKE, cuh=ctypes.addressof(arr), N=3, B=1) == 4 * (100 // 64 + 3 + 1) * per
+    # the binding's helper agrees
+    assert kla.chunk_workspace_bytes(2, 4, 100, 128, 128) == _ws_bytes()
+    # exactly the reported size is accepted by the validation (then FAKE pointers would be used,
+    # so only check that a size one byte short is rejected)
+    assert _chunk(ws_bytes=_ws_bytes() - 1) == E_WS
+
+
+def test_workspace_slots_never_collide():
+    """The packed-sequence slot of chunk c of sequence n is n + floor(t0_n / C) + c: distinct for all
+    (n, c) and below floor(T / C) + N + 1, for any lengths (brute force over random length mixes)."""
+    import random
+    rng = random.Random(7)
+    C = 64
+    for _ in range(300):
+        N = rng.randint(1, 12)
+        lens = [rng.choice([0, 1, 5, 63, 64, 65, 127, 128, 200, rng.randint(0, 400)]) for _ in range(N)]
+        t0, seen = 0, set()
+        T = sum(lens)
+        for n, L in enumerate(lens):
+            for c in range((L + C - 1) // C):
+                s = n + t0 // C + c
+                assert s not in seen and 0 <= s < T // C + N + 1
+                seen.add(s)
+            t0 += L
