@@ -302,9 +302,18 @@ struct AllBlocks {
 // (fp32), then the causal scores P in left-operand groups.  Row block rt of P
 // has ceil(16 (rt + 1) / KG) groups (the columns up to its diagonal), 64 lanes
 // x 16 bytes each.
+// LDS row padding: 32 bytes.  With 64 four-byte banks, rows 32 bytes apart
+// modulo 256 keep the transposing reads (4 rows x 32 bytes per 16 lanes) and
+// the 16-byte row reads free of bank conflicts for the row lengths used here
+// (measured: 2.9x fewer conflict cycles than 16-byte padding for the K^T reads).
+template <typename E>
+struct LdsPad {
+  static constexpr int V = 32 / (int)sizeof(E);
+};
+
 template <typename E, int C>
 struct TpLayout {
-  static constexpr int PAD = 16 / (int)sizeof(E);
+  static constexpr int PAD = LdsPad<E>::V;
   static constexpr int LDC = C + PAD;                      // T'^T rows (grouped columns)
   static constexpr int KG = Ops<E>::KG;
   static constexpr int TP_IMG = C * LDC * (int)sizeof(E);
@@ -458,10 +467,10 @@ template <typename E, int C, int DK>
 struct PrepShape {
   static constexpr int NB = C / 16;
   static constexpr int NT = 64 * kPrepWaves;
-  static constexpr int PAD = 16 / (int)sizeof(E);
+  static constexpr int PAD = LdsPad<E>::V;
   static constexpr int LDK = DK + PAD;         // K and Q rows (grouped columns)
   static constexpr int LDC = TpLayout<E, C>::LDC;
-  static constexpr int LDA = 16 + PAD;         // rows of one 16x16 off-diagonal A^T block
+  static constexpr int LDA = 16 + 2 * PAD;     // rows of one 16x16 off-diagonal A^T block
   static constexpr int LDD = 20;               // fp32 16-wide rows of diagonal blocks
   static constexpr int KG = Ops<E>::KG;
   static constexpr int NOFF = NB * (NB - 1) / 2;
@@ -854,11 +863,13 @@ __global__ __launch_bounds__(64 * kPrepWaves) void kla_chunk_prep_kernel(ChunkPa
 // Waves of a workgroup.  Step i (one barrier each, i = -1 .. nch) has
 //   CHAIN[2] the state scan of chunk i (half of the state columns each)
 //   PW[2]    Diag(Gam) Q S and the causal scores of chunk i; output of chunk i-1
-//   LOADK    K rows of chunk i+1 into LDS (coalesced loads issued a step ahead)
+//   LOADK    K rows of chunk i+1 into LDS (coalesced loads issued two steps ahead)
 //   LOADT    T'^T, gamma/Gam/d, P and the V slice of chunk i+1 into LDS
-// Waves w and w+4 share a SIMD.
-enum Role { CHAIN0 = 0, CHAIN1 = 1, PW0 = 2, PW1 = 3, LOADK = 4, LOADT = 5 };
-constexpr int kWaves = 6;
+//   LOADQ    Q rows of chunk i+1 into LDS
+// The P waves issue no global loads: their output stores would otherwise sit
+// in the same wait counter as the loads.  Waves w and w+4 share a SIMD.
+enum Role { CHAIN0 = 0, CHAIN1 = 1, PW0 = 2, PW1 = 3, LOADK = 4, LOADT = 5, LOADQ = 6 };
+constexpr int kWaves = 7;
 
 template <typename E, int C, int DK, int NCT>
 struct ChunkShape {
@@ -866,10 +877,12 @@ struct ChunkShape {
   static constexpr int DVT = 16 * NCT;         // state columns per workgroup
   static constexpr int NCW = (NCT + 1) / 2;    // 16-column tiles per chain wave
   static constexpr int NT = 64 * kWaves;
-  static constexpr int PAD = 16 / (int)sizeof(E);
+  static constexpr int PAD = LdsPad<E>::V;
   static constexpr int LDK = DK + PAD;         // K and Q rows (grouped columns)
   static constexpr int LDC = TpLayout<E, C>::LDC;
-  static constexpr int LDV = DVT + PAD;        // V slice rows (natural)
+  // V slice rows (natural); a row length of 32 mod 64 bytes keeps the
+  // transposing reads conflict-free
+  static constexpr int LDV = ((DVT + PAD) * (int)sizeof(E)) % 64 == 32 ? DVT + PAD : DVT + 2 * PAD;
   static constexpr int KG = Ops<E>::KG;
   static constexpr int MAXOWN = NB > 1 ? 2 : 1;        // row blocks per P wave
   static constexpr int LOS = MAXOWN * 16 + PAD;        // rows of O^T staging
@@ -880,20 +893,19 @@ struct ChunkShape {
   static constexpr int SU_S = NCT * (DK / KG) * 64 * 16;   // chunk-start S groups, 16 B per lane
   static constexpr int SU_U = NCT * (C / KG) * 64 * 16;    // U~ groups
   static constexpr int SU_SLOT = SU_S + SU_U;
-  static constexpr int QST = MAXOWN * 16 * LDK * (int)sizeof(E);   // per P wave: its Q rows
   static constexpr int OST = (sizeof(E) == 2 ? DVT * LOS : 0) * (int)sizeof(E);  // per P wave: O^T staging
   // offsets
   static constexpr int OFF_K = 0;
   static constexpr int OFF_V = OFF_K + 2 * K_SLOT;
   static constexpr int OFF_TP = OFF_V + 2 * V_SLOT;
   static constexpr int OFF_SU = OFF_TP + 2 * TP_SLOT;
-  static constexpr int OFF_QS = OFF_SU + 2 * SU_SLOT;
-  static constexpr int OFF_OS = OFF_QS + 2 * QST;
+  static constexpr int OFF_Q = OFF_SU + 2 * SU_SLOT;
+  static constexpr int OFF_OS = OFF_Q + 2 * K_SLOT;
   static constexpr int BYTES = OFF_OS + 2 * OST;
 
   static_assert(C == 16 || C == 64, "chunk");
   static_assert(C % KG == 0 && DK % KG == 0 && DK % Ops<E>::KSTEP == 0, "dk");
-  static_assert(K_SLOT % 16 == 0 && V_SLOT % 16 == 0 && TP_SLOT % 16 == 0 && QST % 16 == 0 && OST % 16 == 0,
+  static_assert(K_SLOT % 16 == 0 && V_SLOT % 16 == 0 && TP_SLOT % 16 == 0 && OST % 16 == 0,
                 "lds align");
   static_assert((LDK * (int)sizeof(E)) % 16 == 0 && (LDC * (int)sizeof(E)) % 16 == 0 &&
                     (LDV * (int)sizeof(E)) % 16 == 0 && (LOS * (int)sizeof(E)) % 8 == 0, "row align");
@@ -947,6 +959,9 @@ __global__ __launch_bounds__(64 * kWaves) void kla_chunk_kernel(ChunkParams p) {
   auto tok0_of = [&](int c) { return row0 + (size_t)c * C; };
   // a prefetch past the last chunk re-reads the last chunk
   auto clampc = [&](int c) { return min(max(c, 0), nch - 1); };
+  // steps run from -1 to iend (an even count: the load waves alternate two
+  // register sets); steps past nch do nothing but the barrier
+  const int iend = nch + (nch & 1);
 
   if (nch == 0) {
     // empty sequence: the final state is the initial state
@@ -962,6 +977,7 @@ __global__ __launch_bounds__(64 * kWaves) void kla_chunk_kernel(ChunkParams p) {
 
   // ---- LDS views (chunk c in slot c & 1) --------------------------------------
   auto sK = [&](int c) { return reinterpret_cast<E *>(smem + Sh::OFF_K + (c & 1) * Sh::K_SLOT); };
+  auto sQ = [&](int c) { return reinterpret_cast<E *>(smem + Sh::OFF_Q + (c & 1) * Sh::K_SLOT); };
   auto sV = [&](int c) { return reinterpret_cast<E *>(smem + Sh::OFF_V + (c & 1) * Sh::V_SLOT); };
   auto sTp = [&](int c) { return reinterpret_cast<E *>(smem + Sh::OFF_TP + (c & 1) * Sh::TP_SLOT); };
   // per-chunk row vectors: gamma, Gam = exp(gamma), d = exp(gamma_C - gamma)
@@ -1009,7 +1025,7 @@ __global__ __launch_bounds__(64 * kWaves) void kla_chunk_kernel(ChunkParams p) {
         }
     };
     __syncthreads();
-    for (int i = -1; i <= nch; ++i) {
+    for (int i = -1; i <= iend; ++i) {
       if (i == -1) publish(0);
       if (NCW > 0 && i >= 0 && i < nch) {
         const int c = i;
@@ -1115,55 +1131,11 @@ __global__ __launch_bounds__(64 * kWaves) void kla_chunk_kernel(ChunkParams p) {
       using BL = OwnBlocks<NB, part>;
       constexpr int NOWN = BL::N;
       constexpr int NOW1 = NOWN > 0 ? NOWN : 1;
-      RowLoad<E, DK, BL> qin;
-      E *sQ = reinterpret_cast<E *>(smem + Sh::OFF_QS + part * Sh::QST);
       E *sO = reinterpret_cast<E *>(smem + Sh::OFF_OS + part * Sh::OST);
       f32x4 ao[NCT][NOW1];  // output rows of the pending chunk
       Grp pa[NOW1][NCG];    // its P rows as left operands
-      qin.issue(gq + tok0_of(0) * DK, nrow_of(0), lane);
       __syncthreads();
-      for (int i = -1; i <= nch; ++i) {
-        // chunk i first, then the output of chunk i-1: its stores then drain
-        // while this wave waits at the barrier
-        f32x4 ao_n[NCT][NOW1];
-        Grp pa_n[NOW1][NCG];
-        if (NOWN > 0 && i >= 0 && i < nch) {
-          // ---- chunk i: P rows and Diag(Gam) Q S ----
-          const int c = i;
-          qin.put(sQ, LDK, lane, [](int lr, int) { return lr; });
-          qin.issue(gq + tok0_of(clampc(c + 1)) * DK, nrow_of(clampc(c + 1)), lane);
-          const float *vec = sVec(c);
-          const Grp *suS = sSuS(c);
-          const Grp *sP = reinterpret_cast<const Grp *>(reinterpret_cast<const char *>(sTp(c)) + TL::OFF_P);
-#pragma unroll
-          for (int k = 0; k < NOWN; ++k)
-#pragma unroll
-            for (int q = 0; q * KG < 16 * (BL::at(k) + 1); ++q) pa_n[k][q] = sP[TL::pgroup(BL::at(k), q) * 64 + lane];
-          Grp qa[NOW1][NQG];
-#pragma unroll
-          for (int k = 0; k < NOWN; ++k)
-#pragma unroll
-            for (int q = 0; q < NQG; ++q) qa[k][q] = O::a_row(sQ + (16 * k + li) * LDK, q * KG, lg);
-          // Diag(Gam) Q S
-#pragma unroll
-          for (int ct = 0; ct < NCT; ++ct) {
-            Grp sbq[NQG];
-#pragma unroll
-            for (int q = 0; q < NQG; ++q) sbq[q] = suS[(ct * NQG + q) * 64 + lane];
-#pragma unroll
-            for (int k = 0; k < NOWN; ++k) {
-              ao_n[ct][k] = zero4();
-#pragma unroll
-              for (int q = 0; q < NQG; ++q) ao_n[ct][k] = O::mma_grp(qa[k][q], sbq[q], ao_n[ct][k]);
-            }
-          }
-#pragma unroll
-          for (int k = 0; k < NOWN; ++k) {
-            const f32x4 gm = *reinterpret_cast<const f32x4 *>(vec + C + 16 * BL::at(k) + 4 * lg);
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) ao_n[ct][k] = gm * ao_n[ct][k];
-          }
-        }
+      for (int i = -1; i <= iend; ++i) {
         if (NOWN > 0 && i >= 1 && i <= nch) {
           // ---- output of chunk i-1: O = Diag(Gam) Q S + P U~ ----
           const int c = i - 1;
@@ -1195,18 +1167,38 @@ __global__ __launch_bounds__(64 * kWaves) void kla_chunk_kernel(ChunkParams p) {
                 *reinterpret_cast<bf16x4 *>(sO + (16 * ct + li) * LOS + 16 * k + 4 * lg) = ob;
               }
             const int x = (lane >> 2) & 3, a = lane & 3;
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) {
-              bf16x4 rows[NOW1];
-#pragma unroll
-              for (int k = 0; k < NOWN; ++k)
-                rows[k] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                    (lds_bf16x4 *)(sO + (16 * ct + 4 * lg + x) * LOS + 16 * k + 4 * a));
+            if constexpr (DVT % 32 == 0) {
+              // lane (row li, piece lg): columns 8 lg .. 8 lg + 7 of the
+              // slice as two transposing reads, one 16-byte store
 #pragma unroll
               for (int k = 0; k < NOWN; ++k) {
-                const int r = 16 * BL::at(k) + li;
-                if (r < nrow)
-                  *reinterpret_cast<bf16x4 *>(go + (tok0 + r) * (size_t)dv + jt * DVT + 16 * ct + 4 * lg) = rows[k];
+#pragma unroll
+                for (int m0 = 0; m0 < DVT / 8; m0 += 4) {
+                  const int m = m0 + lg;
+                  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                      (lds_bf16x4 *)(sO + (8 * m + x) * LOS + 16 * k + 4 * a));
+                  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                      (lds_bf16x4 *)(sO + (8 * m + 4 + x) * LOS + 16 * k + 4 * a));
+                  const int r = 16 * BL::at(k) + li;
+                  if (r < nrow)
+                    *reinterpret_cast<bf16x8 *>(go + (tok0 + r) * (size_t)dv + jt * DVT + 8 * m) =
+                        bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                }
+              }
+            } else {
+#pragma unroll
+              for (int ct = 0; ct < NCT; ++ct) {
+                bf16x4 rows[NOW1];
+#pragma unroll
+                for (int k = 0; k < NOWN; ++k)
+                  rows[k] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                      (lds_bf16x4 *)(sO + (16 * ct + 4 * lg + x) * LOS + 16 * k + 4 * a));
+#pragma unroll
+                for (int k = 0; k < NOWN; ++k) {
+                  const int r = 16 * BL::at(k) + li;
+                  if (r < nrow)
+                    *reinterpret_cast<bf16x4 *>(go + (tok0 + r) * (size_t)dv + jt * DVT + 16 * ct + 4 * lg) = rows[k];
+                }
               }
             }
           } else {
@@ -1222,14 +1214,40 @@ __global__ __launch_bounds__(64 * kWaves) void kla_chunk_kernel(ChunkParams p) {
           }
         }
         if (NOWN > 0 && i >= 0 && i < nch) {
-#pragma unroll
-          for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-            for (int k = 0; k < NOWN; ++k) ao[ct][k] = ao_n[ct][k];
+          // ---- chunk i: P rows and Diag(Gam) Q S ----
+          const int c = i;
+          const E *Q = sQ(c);
+          const float *vec = sVec(c);
+          const Grp *suS = sSuS(c);
+          const Grp *sP = reinterpret_cast<const Grp *>(reinterpret_cast<const char *>(sTp(c)) + TL::OFF_P);
 #pragma unroll
           for (int k = 0; k < NOWN; ++k)
 #pragma unroll
-            for (int q = 0; q * KG < 16 * (BL::at(k) + 1); ++q) pa[k][q] = pa_n[k][q];
+            for (int q = 0; q * KG < 16 * (BL::at(k) + 1); ++q) pa[k][q] = sP[TL::pgroup(BL::at(k), q) * 64 + lane];
+          Grp qa[NOW1][NQG];
+#pragma unroll
+          for (int k = 0; k < NOWN; ++k)
+#pragma unroll
+            for (int q = 0; q < NQG; ++q) qa[k][q] = O::a_row(Q + (16 * BL::at(k) + li) * LDK, q * KG, lg);
+          // Diag(Gam) Q S
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct) {
+            Grp sbq[NQG];
+#pragma unroll
+            for (int q = 0; q < NQG; ++q) sbq[q] = suS[(ct * NQG + q) * 64 + lane];
+#pragma unroll
+            for (int k = 0; k < NOWN; ++k) {
+              ao[ct][k] = zero4();
+#pragma unroll
+              for (int q = 0; q < NQG; ++q) ao[ct][k] = O::mma_grp(qa[k][q], sbq[q], ao[ct][k]);
+            }
+          }
+#pragma unroll
+          for (int k = 0; k < NOWN; ++k) {
+            const f32x4 gm = *reinterpret_cast<const f32x4 *>(vec + C + 16 * BL::at(k) + 4 * lg);
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) ao[ct][k] = gm * ao[ct][k];
+          }
         }
         lds_barrier();
       }
@@ -1240,33 +1258,64 @@ __global__ __launch_bounds__(64 * kWaves) void kla_chunk_kernel(ChunkParams p) {
       pwave(std::integral_constant<int, 1>{});
   } else if (wave == LOADK) {
     // =================== K rows of chunk i+1 ==================================
-    RowLoad<E, DK, AllBlocks<NB>> kin;
-    kin.issue(gk + tok0_of(0) * DK, nrow_of(0), lane);
+    // Two register sets, loads issued two steps ahead (the step alternates
+    // between them, so the set is a compile-time choice).  Stores past the
+    // last chunk rewrite a slot nobody reads any more.
+    RowLoad<E, DK, AllBlocks<NB>> kin[2];
+    kin[0].issue(gk + tok0_of(0) * DK, nrow_of(0), lane);
+    kin[1].issue(gk + tok0_of(clampc(1)) * DK, nrow_of(clampc(1)), lane);
     __syncthreads();
-    for (int i = -1; i <= nch; ++i) {
-      if (i + 1 < nch) {
-        kin.put(sK(i + 1), LDK, lane, [](int, int row) { return row; });
-        kin.issue(gk + tok0_of(clampc(i + 2)) * DK, nrow_of(clampc(i + 2)), lane);
-      }
+    auto step = [&](int i, auto set_c) {
+      constexpr int S = decltype(set_c)::value;
+      kin[S].put(sK(i + 1), LDK, lane, [](int, int row) { return row; });
+      kin[S].issue(gk + tok0_of(clampc(i + 3)) * DK, nrow_of(clampc(i + 3)), lane);
       lds_barrier();
+    };
+    for (int i = -1; i <= iend; i += 2) {
+      step(i, std::integral_constant<int, 0>{});
+      step(i + 1, std::integral_constant<int, 1>{});
+    }
+  } else if (wave == LOADQ) {
+    // =================== Q rows of chunk i+1 (two sets, two steps ahead) ========
+    RowLoad<E, DK, AllBlocks<NB>> qin[2];
+    qin[0].issue(gq + tok0_of(0) * DK, nrow_of(0), lane);
+    qin[1].issue(gq + tok0_of(clampc(1)) * DK, nrow_of(clampc(1)), lane);
+    __syncthreads();
+    auto step = [&](int i, auto set_c) {
+      constexpr int S = decltype(set_c)::value;
+      qin[S].put(sQ(i + 1), LDK, lane, [](int, int row) { return row; });
+      qin[S].issue(gq + tok0_of(clampc(i + 3)) * DK, nrow_of(clampc(i + 3)), lane);
+      lds_barrier();
+    };
+    for (int i = -1; i <= iend; i += 2) {
+      step(i, std::integral_constant<int, 0>{});
+      step(i + 1, std::integral_constant<int, 1>{});
     }
   } else {
     // =================== T'^T, gamma/Gam/d, P and the V slice of chunk i+1 =====
-    PieceCopy<TL::BYTES / 16> tin;
-    VSliceLoad<E, C, DVT> vin;
-    auto fetch = [&](int c) {
-      tin.issue(ws + (size_t)(slot0 + c) * TL::BYTES, lane);
-      vin.issue(gv + tok0_of(c) * dv, nrow_of(c), dv, jt * DVT, lane);
+    // (two sets, two steps ahead, as for K, when the registers allow)
+    using TC = PieceCopy<TL::BYTES / 16>;
+    constexpr int NSET = TC::NPL <= 20 ? 2 : 1;
+    TC tin[NSET];
+    VSliceLoad<E, C, DVT> vin[NSET];
+    auto fetch = [&](int c, auto set_c) {
+      constexpr int S = decltype(set_c)::value;
+      tin[S].issue(ws + (size_t)(slot0 + c) * TL::BYTES, lane);
+      vin[S].issue(gv + tok0_of(c) * dv, nrow_of(c), dv, jt * DVT, lane);
     };
-    fetch(0);
+    fetch(0, std::integral_constant<int, 0>{});
+    if constexpr (NSET == 2) fetch(clampc(1), std::integral_constant<int, NSET - 1>{});
     __syncthreads();
-    for (int i = -1; i <= nch; ++i) {
-      if (i + 1 < nch) {
-        tin.put(sTp(i + 1), lane);
-        vin.put(sV(i + 1), LDV, lane);
-        fetch(clampc(i + 2));
-      }
+    auto step = [&](int i, auto set_c) {
+      constexpr int S = decltype(set_c)::value;
+      tin[S].put(sTp(i + 1), lane);
+      vin[S].put(sV(i + 1), LDV, lane);
+      fetch(clampc(i + 1 + NSET), set_c);
       lds_barrier();
+    };
+    for (int i = -1; i <= iend; i += 2) {
+      step(i, std::integral_constant<int, 0>{});
+      step(i + 1, std::integral_constant<int, NSET - 1>{});
     }
   }
 }
