@@ -297,11 +297,6 @@ struct AllBlocks {
   static __host__ __device__ constexpr int at(int k) { return k; }
 };
 
-// Layout of the per-chunk data the prep kernel hands to the scan kernel: the
-// T'^T image (zero blocks and pads included), the row vectors gamma, Gam, d
-// (fp32), then the causal scores P in left-operand groups.  Row block rt of P
-// has ceil(16 (rt + 1) / KG) groups (the columns up to its diagonal), 64 lanes
-// x 16 bytes each.
 // LDS row padding: 32 bytes.  With 64 four-byte banks, rows 32 bytes apart
 // modulo 256 keep the transposing reads (4 rows x 32 bytes per 16 lanes) and
 // the 16-byte row reads free of bank conflicts for the row lengths used here
@@ -311,21 +306,16 @@ struct LdsPad {
   static constexpr int V = 32 / (int)sizeof(E);
 };
 
+// Layout of the per-chunk data the prep kernel hands to the scan kernel: the
+// T'^T image (zero blocks and pads included), then the row vectors gamma,
+// Gam, d (fp32).
 template <typename E, int C>
 struct TpLayout {
   static constexpr int PAD = LdsPad<E>::V;
   static constexpr int LDC = C + PAD;                      // T'^T rows (grouped columns)
-  static constexpr int KG = Ops<E>::KG;
   static constexpr int TP_IMG = C * LDC * (int)sizeof(E);
   static constexpr int VEC3 = 3 * C * 4;
-  static __host__ __device__ constexpr int pgroup(int rt, int q) {
-    int n = q;
-    for (int r = 0; r < rt; ++r) n += (16 * (r + 1) + KG - 1) / KG;
-    return n;
-  }
-  static constexpr int NPG = pgroup(C / 16, 0);
-  static constexpr int OFF_P = TP_IMG + VEC3;
-  static constexpr int BYTES = OFF_P + NPG * 64 * 16;      // workspace bytes per (chunk, head)
+  static constexpr int BYTES = TP_IMG + VEC3;              // workspace bytes per (chunk, head)
   static_assert(TP_IMG % 16 == 0 && VEC3 % 16 == 0, "align");
 };
 
@@ -346,6 +336,7 @@ struct ChunkParams {
   const int32_t *cu;
   char *ws;
   int H, T, dv, n_tiles, remap, nseq, nslot;
+  int pslots;  // prep kernel: workspace slots per workgroup (1 .. kPrepSlots)
 };
 
 // Raw buffer resource over bytes [0, n) of p: loads at offsets >= n return 0
@@ -446,22 +437,21 @@ struct VSliceLoad {
 // ---------------------------------------------------------------------------
 // prep kernel
 // ---------------------------------------------------------------------------
-// One workgroup per (head, run of kPrepSlots consecutive workspace slots):
-// six role-specialised waves in a pipeline over the run, one LDS-only barrier
-// per step.  Step s (s = -1 .. kPrepSlots) has
-//   PLOAD    K and Q rows, g and eta of slot s+1 into LDS (coalesced loads
-//            issued a step ahead)
+// One workgroup per (head, run of p.pslots <= kPrepSlots consecutive workspace
+// slots):
+// four role-specialised waves in a pipeline over the run, one LDS-only
+// barrier per step.  Step s (s = -1 .. p.pslots) has
+//   PLOAD    K rows, g and eta of slot s+1 into LDS (coalesced loads issued a
+//            step ahead)
 //   PG[2]    slot s: K K^T of the owned rows, ||k||^2, the gate scan, beta,
 //            A, and the owned diagonal blocks T_bb = (I + A_bb)^-1 and of T'^T
-//   PP[2]    slot s: the causal scores of the owned rows (as P^T = K Q^T),
-//            straight to the workspace as left-operand groups
 //   POFFD    slot s-1: the off-diagonal blocks of T and of T' = T Diag(beta)
 //            (the Gram waves wrote the diagonal ones); the T'^T image goes to
 //            the workspace with gamma, Gam, d
-// Waves w and w+4 share a SIMD.
-enum PrepRole { PG0 = 0, PG1 = 1, PP0 = 2, PP1 = 3, POFFD = 4, PLOAD = 5 };
-constexpr int kPrepWaves = 6;
-constexpr int kPrepSlots = 16;  // workspace slots per workgroup
+// One wave per SIMD.
+enum PrepRole { PG0 = 0, PG1 = 1, POFFD = 2, PLOAD = 3 };
+constexpr int kPrepWaves = 4;
+constexpr int kPrepSlots = 16;  // most workspace slots per workgroup
 
 template <typename E, int C, int DK>
 struct PrepShape {
@@ -470,7 +460,7 @@ struct PrepShape {
   static constexpr int PAD = LdsPad<E>::V;
   static constexpr int LDK = DK + PAD;         // K and Q rows (grouped columns)
   static constexpr int LDC = TpLayout<E, C>::LDC;
-  static constexpr int LDA = 16 + 2 * PAD;     // rows of one 16x16 off-diagonal A^T block
+  static constexpr int LDA = 16 + PAD / 2;     // rows of one 16x16 off-diagonal A^T block
   static constexpr int LDD = 20;               // fp32 16-wide rows of diagonal blocks
   static constexpr int KG = Ops<E>::KG;
   static constexpr int NOFF = NB * (NB - 1) / 2;
@@ -480,21 +470,19 @@ struct PrepShape {
   static constexpr int TD_SLOT = NB * 16 * LDD * 4;        // diagonal blocks (A, then T), transposed, fp32
   static constexpr int BV_SLOT = 4 * C * 4;                // gamma, Gam, d, beta
   static constexpr int GP = 3 * C * 4;                     // per Gram wave: gamma, ||k||^2, beta
-  static constexpr int PGAM = C * 4;                       // per P wave: gamma
   static constexpr int OFF_K = 0;
-  static constexpr int OFF_Q = OFF_K + 2 * K_SLOT;
-  static constexpr int OFF_GE = OFF_Q + 2 * K_SLOT;
+  static constexpr int OFF_GE = OFF_K + 2 * K_SLOT;
   static constexpr int OFF_A = OFF_GE + 2 * GE_SLOT;
   static constexpr int OFF_TD = OFF_A + 2 * A_SLOT;
   static constexpr int OFF_BV = OFF_TD + 2 * TD_SLOT;
   static constexpr int IMG_SLOT = TpLayout<E, C>::TP_IMG;
   static constexpr int OFF_IMG = OFF_BV + 2 * BV_SLOT;
   static constexpr int OFF_GP = OFF_IMG + 2 * IMG_SLOT;
-  static constexpr int OFF_PG = OFF_GP + 2 * GP;
-  static constexpr int OFF_SLOT = OFF_PG + 2 * PGAM;       // per slot: token offset (8 B), rows (4 B), pad
+  static constexpr int OFF_SLOT = OFF_GP + 2 * GP;         // per slot: token offset (8 B), rows (4 B), pad
   static constexpr int BYTES = OFF_SLOT + kPrepSlots * 16;
   static_assert(K_SLOT % 16 == 0 && A_SLOT % 16 == 0 && TD_SLOT % 16 == 0, "lds align");
-  static_assert(BYTES <= 160 * 1024, "LDS budget");
+  // bf16: two workgroups per CU (the fp32 debug build may take one)
+  static_assert(BYTES <= (sizeof(E) == 2 ? 80 : 160) * 1024, "LDS budget");
 };
 
 template <typename E, int C, int DK>
@@ -511,13 +499,14 @@ __global__ __launch_bounds__(64 * kPrepWaves) void kla_chunk_prep_kernel(ChunkPa
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int li = lane & 15, lg = lane >> 4;
   const int h = blockIdx.y;
-  const int slot_base = blockIdx.x * kPrepSlots;
+  const int nps = p.pslots;
+  const int slot_base = blockIdx.x * nps;
 
   // ---- the chunk behind each slot of the run: token offset and row count ---
   // (row count 0: no chunk -- an unused slot or past the end)
   long long *slot_tok = reinterpret_cast<long long *>(smem + Sh::OFF_SLOT);
   int *slot_rows = reinterpret_cast<int *>(smem + Sh::OFF_SLOT + 8);
-  if (threadIdx.x < kPrepSlots) {
+  if (threadIdx.x < nps) {
     const int slot = slot_base + threadIdx.x;
     int b = 0, t0 = 0, len = p.T, c = slot;
     if (p.cu) {
@@ -542,17 +531,16 @@ __global__ __launch_bounds__(64 * kPrepWaves) void kla_chunk_prep_kernel(ChunkPa
   }
   // (values read from LDS are per lane to the compiler: make them scalar)
   auto nrow_of = [&](int s) {
-    return (s >= 0 && s < kPrepSlots) ? __builtin_amdgcn_readfirstlane(slot_rows[4 * s]) : 0;
+    return (s >= 0 && s < nps) ? __builtin_amdgcn_readfirstlane(slot_rows[4 * s]) : 0;
   };
   auto tok_of = [&](int s) {
-    const long long t = slot_tok[2 * min(max(s, 0), kPrepSlots - 1)];
+    const long long t = slot_tok[2 * min(max(s, 0), nps - 1)];
     const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)t), hi = __builtin_amdgcn_readfirstlane((unsigned)(t >> 32));
     return (size_t)(((unsigned long long)hi << 32) | lo);
   };
   auto ws_of = [&](int s) { return p.ws + ((size_t)h * p.nslot + slot_base + s) * TL::BYTES; };
 
   auto sK = [&](int s) { return reinterpret_cast<E *>(smem + Sh::OFF_K + (s & 1) * Sh::K_SLOT); };
-  auto sQ = [&](int s) { return reinterpret_cast<E *>(smem + Sh::OFF_Q + (s & 1) * Sh::K_SLOT); };
   auto sGE = [&](int s) { return reinterpret_cast<float *>(smem + Sh::OFF_GE + (s & 1) * Sh::GE_SLOT); };
   auto sA = [&](int s) { return reinterpret_cast<E *>(smem + Sh::OFF_A + (s & 1) * Sh::A_SLOT); };
   auto sTd = [&](int s) { return reinterpret_cast<float *>(smem + Sh::OFF_TD + (s & 1) * Sh::TD_SLOT); };
@@ -570,13 +558,12 @@ __global__ __launch_bounds__(64 * kPrepWaves) void kla_chunk_prep_kernel(ChunkPa
 
   if (wave == PLOAD) {
     // =================== K, Q, g, eta of slot s+1 ============================
-    RowLoad<E, DK, AllBlocks<NB>> kin, qin;
+    RowLoad<E, DK, AllBlocks<NB>> kin;
     typename std::conditional<sizeof(E) == 2, unsigned short, unsigned>::type graw = 0, eraw = 0;
     auto issue = [&](int s) {
       const int nrow = nrow_of(s);
       const size_t tok = tok_of(s);
       kin.issue(static_cast<const E *>(p.k) + tok * DK, nrow, lane);
-      qin.issue(static_cast<const E *>(p.q) + tok * DK, nrow, lane);
       // g and eta of row `lane` (0 past the end; lanes >= C read nothing)
       const E *gp = static_cast<const E *>(p.g) + tok, *ep = static_cast<const E *>(p.eta) + tok;
       graw = buffer_ld_elem(buffer_rsrc(gp, nrow * (int)sizeof(E)), lane, gp);
@@ -584,10 +571,9 @@ __global__ __launch_bounds__(64 * kPrepWaves) void kla_chunk_prep_kernel(ChunkPa
     };
     __syncthreads();
     issue(0);
-    for (int s = -1; s <= kPrepSlots; ++s) {
-      if (s + 1 < kPrepSlots) {
+    for (int s = -1; s <= nps; ++s) {
+      if (s + 1 < nps) {
         kin.put(sK(s + 1), LDK, lane, [](int, int row) { return row; });
-        qin.put(sQ(s + 1), LDK, lane, [](int, int row) { return row; });
         float *ge = sGE(s + 1);
         if (lane < C) {
           ge[lane] = elem_bits_to_f32(graw);
@@ -606,7 +592,7 @@ __global__ __launch_bounds__(64 * kPrepWaves) void kla_chunk_prep_kernel(ChunkPa
       float *gp = reinterpret_cast<float *>(smem + Sh::OFF_GP + part * Sh::GP);
       float *sGam = gp, *sNrm = gp + C, *sBet = gp + 2 * C;
       __syncthreads();
-      for (int s = -1; s <= kPrepSlots; ++s) {
+      for (int s = -1; s <= nps; ++s) {
         const int nrow = nrow_of(s);
         if (OB::N > 0 && nrow > 0) {
           const E *K = sK(s);
@@ -726,81 +712,11 @@ __global__ __launch_bounds__(64 * kPrepWaves) void kla_chunk_prep_kernel(ChunkPa
       gram(std::integral_constant<int, 0>{});
     else
       gram(std::integral_constant<int, 1>{});
-  } else if (wave == PP0 || wave == PP1) {
-    // =================== P waves: slot s =====================================
-    // P^T = K Q^T: its accumulator layout is the left-operand layout of the P
-    // rows in P U~, so the groups go to the workspace as they are (16 bytes
-    // per lane, consecutive lanes consecutive)
-    auto pwave = [&](auto part_c) {
-      constexpr int part = decltype(part_c)::value;
-      using OB = OwnBlocks<NB, part>;
-      constexpr int NOWN = OB::N;
-      constexpr int NOW1 = NOWN > 0 ? NOWN : 1;
-      float *sGam = reinterpret_cast<float *>(smem + Sh::OFF_PG + part * Sh::PGAM);
-      __syncthreads();
-      for (int s = -1; s <= kPrepSlots; ++s) {
-        const int nrow = nrow_of(s);
-        if (NOWN > 0 && nrow > 0) {
-          const E *K = sK(s);
-          const E *Q = sQ(s);
-          const float *ge = sGE(s);
-          const float gam = wave_inclusive_scan(lane < C ? ge[lane] : 0.f);
-          if (lane < C) sGam[lane] = gam;
-          Grp qa[NOW1][NQG];
-#pragma unroll
-          for (int k = 0; k < NOWN; ++k)
-#pragma unroll
-            for (int q = 0; q < NQG; ++q) qa[k][q] = O::a_row(Q + (16 * OB::at(k) + li) * LDK, q * KG, lg);
-          // P^T tiles: D[s'][r] = K_s' . q_r, lane column r = 16 rt + li, rows s' = 16 st + 4 lg + j
-          f32x4 pt[NOW1][NB];
-#pragma unroll
-          for (int st = 0; st < NB; ++st) {
-            if (st > OB::at(NOWN - 1)) continue;
-            Grp kb[NQG];
-#pragma unroll
-            for (int q = 0; q < NQG; ++q) kb[q] = O::a_row(K + (16 * st + li) * LDK, q * KG, lg);
-#pragma unroll
-            for (int k = 0; k < NOWN; ++k) {
-              if (st > OB::at(k)) continue;
-              pt[k][st] = zero4();
-#pragma unroll
-              for (int q = 0; q < NQG; ++q) pt[k][st] = O::mma_grp(kb[q], qa[k][q], pt[k][st]);
-            }
-          }
-          // decay and causal mask, then the P rows as left-operand groups
-          Grp *wsP = reinterpret_cast<Grp *>(ws_of(s) + TL::OFF_P);
-#pragma unroll
-          for (int k = 0; k < NOWN; ++k) {
-            const int rt = OB::at(k);
-            const float gr = sGam[16 * rt + li];
-#pragma unroll
-            for (int st = 0; st <= rt; ++st) {
-              const f32x4 gs = *reinterpret_cast<const f32x4 *>(sGam + 16 * st + 4 * lg);
-#pragma unroll
-              for (int j = 0; j < 4; ++j)
-                pt[k][st][j] = (st < rt || 4 * lg + j <= li) ? pt[k][st][j] * __expf(gr - gs[j]) : 0.f;
-            }
-#pragma unroll
-            for (int q = 0; q * KG < 16 * (rt + 1); ++q) {
-              f32x4 tl[TPG];
-#pragma unroll
-              for (int tt = 0; tt < TPG; ++tt) tl[tt] = (q * TPG + tt <= rt) ? pt[k][q * TPG + tt] : zero4();
-              wsP[TL::pgroup(rt, q) * 64 + lane] = O::b_from_d(tl);
-            }
-          }
-        }
-        lds_barrier();
-      }
-    };
-    if (wave == PP0)
-      pwave(std::integral_constant<int, 0>{});
-    else
-      pwave(std::integral_constant<int, 1>{});
-  } else {
+  } else if (wave == POFFD) {
     // =================== off-diagonal solve: slot s-1 ========================
     using M = Mm16<E>;
     __syncthreads();
-    for (int s = -1; s <= kPrepSlots; ++s) {
+    for (int s = -1; s <= nps; ++s) {
       const int sp = s - 1;
       if (nrow_of(sp) > 0) {
         const E *Ablk = sA(sp);
@@ -864,7 +780,7 @@ __global__ __launch_bounds__(64 * kPrepWaves) void kla_chunk_prep_kernel(ChunkPa
 //   CHAIN[2] the state scan of chunk i (half of the state columns each)
 //   PW[2]    Diag(Gam) Q S and the causal scores of chunk i; output of chunk i-1
 //   LOADK    K rows of chunk i+1 into LDS (coalesced loads issued two steps ahead)
-//   LOADT    T'^T, gamma/Gam/d, P and the V slice of chunk i+1 into LDS
+//   LOADT    T'^T, gamma/Gam/d and the V slice of chunk i+1 into LDS
 //   LOADQ    Q rows of chunk i+1 into LDS
 // The P waves issue no global loads: their output stores would otherwise sit
 // in the same wait counter as the loads.  Waves w and w+4 share a SIMD.
@@ -1121,11 +1037,12 @@ __global__ __launch_bounds__(64 * kWaves) void kla_chunk_kernel(ChunkParams p) {
     else
       chain(std::integral_constant<int, Sh::NCW>{});
   } else if (wave == PW0 || wave == PW1) {
-    // =================== P waves: output rows ================================
-    // For its row blocks rt, a P wave forms Diag(Gam) Q S of chunk i with the
-    // chunk-start state and takes that chunk's causal scores P (left-operand
-    // groups from the prep kernel) into registers; one step later, when the
-    // chain has U~, it adds P U~ and writes those output rows.
+    // =================== P waves: scores and output rows ======================
+    // For its row blocks rt, a P wave forms the causal scores of chunk i as
+    // P^T = K Q^T (the accumulator layout of P^T is exactly the left-operand
+    // layout P needs in P U~, so P stays in registers) and Diag(Gam) Q S with
+    // the chunk-start state; one step later, when the chain has U~, it adds
+    // P U~ and writes those output rows.
     auto pwave = [&](auto part_c) {
       constexpr int part = decltype(part_c)::value;
       using BL = OwnBlocks<NB, part>;
@@ -1217,18 +1134,51 @@ __global__ __launch_bounds__(64 * kWaves) void kla_chunk_kernel(ChunkParams p) {
           // ---- chunk i: P rows and Diag(Gam) Q S ----
           const int c = i;
           const E *Q = sQ(c);
+          const E *K = sK(c);
           const float *vec = sVec(c);
           const Grp *suS = sSuS(c);
-          const Grp *sP = reinterpret_cast<const Grp *>(reinterpret_cast<const char *>(sTp(c)) + TL::OFF_P);
-#pragma unroll
-          for (int k = 0; k < NOWN; ++k)
-#pragma unroll
-            for (int q = 0; q * KG < 16 * (BL::at(k) + 1); ++q) pa[k][q] = sP[TL::pgroup(BL::at(k), q) * 64 + lane];
           Grp qa[NOW1][NQG];
 #pragma unroll
           for (int k = 0; k < NOWN; ++k)
 #pragma unroll
             for (int q = 0; q < NQG; ++q) qa[k][q] = O::a_row(Q + (16 * BL::at(k) + li) * LDK, q * KG, lg);
+          // P^T tiles: D[s][r] = K_s . q_r, lane column r = 16 rt + li, rows s = 16 st + 4 lg + j
+          f32x4 pt[NOW1][NB];
+#pragma unroll
+          for (int st = 0; st < NB; ++st) {
+            if (st > BL::at(NOWN - 1)) continue;
+            Grp kb[NQG];
+#pragma unroll
+            for (int q = 0; q < NQG; ++q) kb[q] = O::a_row(K + (16 * st + li) * LDK, q * KG, lg);
+#pragma unroll
+            for (int k = 0; k < NOWN; ++k) {
+              if (st > BL::at(k)) continue;
+              pt[k][st] = zero4();
+#pragma unroll
+              for (int q = 0; q < NQG; ++q) pt[k][st] = O::mma_grp(kb[q], qa[k][q], pt[k][st]);
+            }
+          }
+          // decay and causal mask; the accumulator layout of P^T is the
+          // left-operand layout of the P rows in P U~
+#pragma unroll
+          for (int k = 0; k < NOWN; ++k) {
+            const int rt = BL::at(k);
+            const float gr = vec[16 * rt + li];
+#pragma unroll
+            for (int st = 0; st <= rt; ++st) {
+              const f32x4 gs = *reinterpret_cast<const f32x4 *>(vec + 16 * st + 4 * lg);
+#pragma unroll
+              for (int j = 0; j < 4; ++j)
+                pt[k][st][j] = (st < rt || 4 * lg + j <= li) ? pt[k][st][j] * __expf(gr - gs[j]) : 0.f;
+            }
+#pragma unroll
+            for (int q = 0; q * KG < 16 * (rt + 1); ++q) {
+              f32x4 tl[TPG];
+#pragma unroll
+              for (int tt = 0; tt < TPG; ++tt) tl[tt] = (q * TPG + tt <= rt) ? pt[k][q * TPG + tt] : zero4();
+              pa[k][q] = O::b_from_d(tl);
+            }
+          }
           // Diag(Gam) Q S
 #pragma unroll
           for (int ct = 0; ct < NCT; ++ct) {
@@ -1292,7 +1242,7 @@ __global__ __launch_bounds__(64 * kWaves) void kla_chunk_kernel(ChunkParams p) {
       step(i + 1, std::integral_constant<int, 1>{});
     }
   } else {
-    // =================== T'^T, gamma/Gam/d, P and the V slice of chunk i+1 =====
+    // =================== T'^T, gamma/Gam/d and the V slice of chunk i+1 ========
     // (two sets, two steps ahead, as for K, when the registers allow)
     using TC = PieceCopy<TL::BYTES / 16>;
     constexpr int NSET = TC::NPL <= 20 ? 2 : 1;
@@ -1358,7 +1308,11 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t st) {
   p.remap = (nblk % 8 == 0) ? 1 : 0;
   if (nblk == 0) return hipSuccess;
   if ((long long)a.B * a.T > 0 && p.nslot > 0) {
-    const unsigned runs = (unsigned)((p.nslot + kPrepSlots - 1) / kPrepSlots);
+    // slots per workgroup: the longest run that still gives two workgroups
+    // per CU (the pipeline is latency-bound; two resident workgroups overlap)
+    const long long work = (long long)p.nslot * a.H;
+    p.pslots = (int)std::min<long long>(kPrepSlots, std::max<long long>(2, work / 512));
+    const unsigned runs = (unsigned)((p.nslot + p.pslots - 1) / p.pslots);
     hipLaunchKernelGGL((kla_chunk_prep_kernel<E, C, DK>), dim3(runs, (unsigned)a.H),
                        dim3(PrepShape<E, C, DK>::NT), 0, st, p);
     const hipError_t e = hipGetLastError();
