@@ -208,9 +208,10 @@ def main():
             "tflops": tfl, "mfma_frac": tfl / BF16_PEAK_TFLOPS,
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": gbs / HBM_PEAK_GBS,
-                         "traffic": recorded_traffic("kla_chunk_kernel_prefill_b4_h16_t4096_hbm.md",
+                         "traffic": recorded_traffic("kla_chunk_fwd_prefill_b4_h16_t4096_hbm.md",
                                                      "gated_delta_rule_kla_amd/csrc/kla_chunk.hip"),
-                         "kernel": "kla_chunk_kernel<bf16,64,128,2>",
+                         "kernel": "kla_chunk_fwd: kla_chunk_prep_kernel<bf16,64,128> then "
+                                   "kla_chunk_kernel<bf16,64,128,2>, timed together per call",
                          "algorithmic_bytes_per_launch": p["bytes"],
                          "algorithmic_flops_per_launch": p["flops"],
                          "note": "arithmetic intensity 172.6 flop/B is below the bf16 ridge "
