@@ -113,6 +113,44 @@ def bench_prefill(steps, warmup):
                 dims=(B, H, T, dk, dv, x.chunk))
 
 
+def bench_gdn(steps, warmup, decode_steps=512):
+    """The same kernels in gated-delta-rule mode (kla_gdn_*: the update
+    coefficient given instead of the Kaczmarz step), on the prefill and decode
+    workloads with unit-length keys: the operator-level form of the pages'
+    KLA-versus-GDN latency comparison."""
+    import torch
+    from gated_delta_rule_kla_amd import inputs, kla
+
+    dev = torch.device("cuda:0")
+    x = inputs.unit_keys(inputs.prefill_config(1))
+    B, H, T, dk, dv = x.dims
+    q, k, v, g, beta = (t.to(dev) for t in (x.q, x.k, x.v, x.g, x.eta))
+    o = torch.empty((B, H, T, dv), dtype=q.dtype, device=dev)
+    S = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    ws = torch.empty(kla.chunk_workspace_bytes(B, H, T, dk, dv, x.chunk, q.dtype), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def pstep(_i):
+        kla.gdn_chunk_fwd(q, k, v, g, beta, None, None, chunk=x.chunk, out=o, final_state=S, workspace=ws)
+
+    for i in range(warmup):
+        pstep(i)
+    p_ms, _ = time_launches(pstep, steps, stream)
+    del q, k, v, g, beta, o, S, ws
+    d = inputs.unit_keys(inputs.decode_config(steps=decode_steps))
+    dq, dk_, dv_, dg, db = (t.to(dev) for t in (d.q, d.k, d.v, d.g, d.eta))
+    st = d.state.to(dev)
+    do = torch.empty((d.q.shape[1], d.q.shape[2], d.v.shape[-1]), dtype=dq.dtype, device=dev)
+
+    def dstep(i):
+        kla.gdn_decode_step(dq[i], dk_[i], dv_[i], dg[i], db[i], st, out=do)
+
+    for i in range(64):
+        dstep(i % decode_steps)
+    d_ms, _ = time_launches(dstep, decode_steps, stream)
+    return dict(prefill_ms=p_ms, decode_ms=d_ms, tokens=B * T)
+
+
 def bench_decode(steps_total=512, warmup=64):
     import torch
     from gated_delta_rule_kla_amd import inputs, kla
@@ -236,6 +274,17 @@ def main():
             out.update({"value": gbs, "unit": "GB/s", "ms_per_step": d["ms"],
                         "config": {"workload": dec["workload"]}, "roofline": dec["roofline"]})
         out["decode"] = dec
+    if args.mode == "all":
+        gd = bench_gdn(args.steps, args.warmup)
+        gdn = {"workload": "the same prefill and decode workloads through kla_gdn_chunk_fwd / "
+                           "kla_gdn_decode_step (update coefficient given; unit-length keys)",
+               "prefill_ms_per_call": gd["prefill_ms"], "prefill_tokens/s": gd["tokens"] / (gd["prefill_ms"] * 1e-3),
+               "decode_ms_per_step": gd["decode_ms"]}
+        if "ms_per_step" in out:
+            gdn["kla_over_gdn_prefill_time"] = out["ms_per_step"] / gd["prefill_ms"]
+        if "decode" in out:
+            gdn["kla_over_gdn_decode_time"] = out["decode"]["ms_per_step"] / gd["decode_ms"]
+        out["gdn"] = gdn
     if args.mode == "all" and not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out))

@@ -17,49 +17,6 @@ bool bad_eps(float eps) { return !std::isfinite(eps) || eps < 0.f; }
 
 kla_status_t from_hip(hipError_t e) { return e == hipSuccess ? KLA_OK : KLA_ERR_HIP; }
 
-}  // namespace
-
-extern "C" {
-
-int kla_abi_version(void) { return KLA_ABI_VERSION; }
-
-const char *kla_status_str(kla_status_t s) {
-  switch (s) {
-    case KLA_OK: return "ok";
-    case KLA_ERR_NULL: return "a required pointer is NULL";
-    case KLA_ERR_SHAPE: return "invalid or inconsistent sizes";
-    case KLA_ERR_DTYPE: return "unknown dtype";
-    case KLA_ERR_UNSUPPORTED: return "shape/dtype/chunk combination not compiled";
-    case KLA_ERR_SEQLENS: return "cu_seqlens must be non-decreasing from 0 to T";
-    case KLA_ERR_EPS: return "eps must be finite and >= 0";
-    case KLA_ERR_ALIGN: return "data pointers must be 16-byte aligned";
-    case KLA_ERR_WORKSPACE: return "workspace missing or smaller than kla_chunk_workspace_bytes()";
-    case KLA_ERR_HIP: return "HIP runtime error";
-  }
-  return "unknown status";
-}
-
-kla_status_t kla_decode_step(const void *q, const void *k, const void *v, const void *g,
-                             const void *eta, float eps, float *state, void *o, int N, int H,
-                             int dk, int dv, kla_dtype_t dtype, void *stream) {
-  if (dtype != KLA_DT_BF16 && dtype != KLA_DT_F32) return KLA_ERR_DTYPE;
-  if (N < 0 || H <= 0 || dk <= 0 || dv <= 0) return KLA_ERR_SHAPE;
-  if (bad_eps(eps)) return KLA_ERR_EPS;
-  if (!kla::decode_supported(dtype, dk, dv)) return KLA_ERR_UNSUPPORTED;
-  if (N == 0) return KLA_OK;
-  if (!q || !k || !v || !g || !eta || !state || !o) return KLA_ERR_NULL;
-  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(g) || misaligned(eta) ||
-      misaligned(state) || misaligned(o))
-    return KLA_ERR_ALIGN;
-  if ((long long)N * H > 0x7fffffffLL) return KLA_ERR_SHAPE;
-  kla::DecodeArgs a{q, k, v, g, eta, eps, state, o, N, H, dk, dv, (int)dtype};
-  return from_hip(kla::launch_decode(a, reinterpret_cast<hipStream_t>(stream)));
-}
-
-}  // extern "C"
-
-namespace {
-
 // Shape, dtype, eps and cu_seqlens checks shared by kla_chunk_fwd and
 // kla_chunk_workspace_bytes.
 kla_status_t check_chunk_shapes(float eps, const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
@@ -93,31 +50,34 @@ kla_status_t check_chunk_shapes(float eps, const int32_t *cu_seqlens, const int3
 kla::ChunkArgs chunk_args(const void *q, const void *k, const void *v, const void *g, const void *eta,
                           float eps, const float *initial_state, void *o, float *final_state,
                           const int32_t *cu_seqlens, int num_seqs, int B, int H, int T, int dk, int dv,
-                          int chunk, kla_dtype_t dtype, void *workspace) {
-  return kla::ChunkArgs{q,          k,        v, g, eta, eps, initial_state, o, final_state,
-                        cu_seqlens, num_seqs, B, H, T,   dk,  dv,            chunk, (int)dtype, workspace};
+                          int chunk, kla_dtype_t dtype, void *workspace, int beta_direct) {
+  return kla::ChunkArgs{q,          k,        v, g, eta, eps, initial_state, o,     final_state,
+                        cu_seqlens, num_seqs, B, H, T,   dk,  dv,            chunk, (int)dtype,
+                        workspace,  beta_direct};
 }
 
-}  // namespace
-
-extern "C" {
-
-size_t kla_chunk_workspace_bytes(const int32_t *cu_seqlens, const int32_t *cu_seqlens_host, int num_seqs,
-                                 int B, int H, int T, int dk, int dv, int chunk, kla_dtype_t dtype) {
-  if (check_chunk_shapes(0.f, cu_seqlens, cu_seqlens_host, num_seqs, B, H, T, dk, dv, chunk, dtype) != KLA_OK)
-    return 0;
-  if (num_seqs == 0 || (long long)B * T == 0) return 0;
-  return kla::chunk_workspace_bytes(chunk_args(nullptr, nullptr, nullptr, nullptr, nullptr, 0.f, nullptr,
-                                               nullptr, nullptr, cu_seqlens, num_seqs, B, H, T, dk, dv, chunk,
-                                               dtype, nullptr));
+kla_status_t decode_impl(const void *q, const void *k, const void *v, const void *g, const void *eta,
+                         float eps, int beta_direct, float *state, void *o, int N, int H, int dk, int dv,
+                         kla_dtype_t dtype, void *stream) {
+  if (dtype != KLA_DT_BF16 && dtype != KLA_DT_F32) return KLA_ERR_DTYPE;
+  if (N < 0 || H <= 0 || dk <= 0 || dv <= 0) return KLA_ERR_SHAPE;
+  if (bad_eps(eps)) return KLA_ERR_EPS;
+  if (!kla::decode_supported(dtype, dk, dv)) return KLA_ERR_UNSUPPORTED;
+  if (N == 0) return KLA_OK;
+  if (!q || !k || !v || !g || !eta || !state || !o) return KLA_ERR_NULL;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(g) || misaligned(eta) ||
+      misaligned(state) || misaligned(o))
+    return KLA_ERR_ALIGN;
+  if ((long long)N * H > 0x7fffffffLL) return KLA_ERR_SHAPE;
+  kla::DecodeArgs a{q, k, v, g, eta, eps, state, o, N, H, dk, dv, (int)dtype, beta_direct};
+  return from_hip(kla::launch_decode(a, reinterpret_cast<hipStream_t>(stream)));
 }
 
-kla_status_t kla_chunk_fwd(const void *q, const void *k, const void *v, const void *g,
-                           const void *eta, float eps, const float *initial_state, void *o,
-                           float *final_state, const int32_t *cu_seqlens,
-                           const int32_t *cu_seqlens_host, int num_seqs, int B, int H, int T,
-                           int dk, int dv, int chunk, void *workspace, size_t workspace_bytes,
-                           kla_dtype_t dtype, void *stream) {
+kla_status_t chunk_fwd_impl(const void *q, const void *k, const void *v, const void *g, const void *eta,
+                            float eps, int beta_direct, const float *initial_state, void *o,
+                            float *final_state, const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
+                            int num_seqs, int B, int H, int T, int dk, int dv, int chunk, void *workspace,
+                            size_t workspace_bytes, kla_dtype_t dtype, void *stream) {
   const kla_status_t st =
       check_chunk_shapes(eps, cu_seqlens, cu_seqlens_host, num_seqs, B, H, T, dk, dv, chunk, dtype);
   if (st != KLA_OK) return st;
@@ -128,10 +88,73 @@ kla_status_t kla_chunk_fwd(const void *q, const void *k, const void *v, const vo
       misaligned(o) || misaligned(initial_state) || misaligned(final_state) || misaligned(workspace))
     return KLA_ERR_ALIGN;
   const kla::ChunkArgs a = chunk_args(q, k, v, g, eta, eps, initial_state, o, final_state, cu_seqlens, num_seqs,
-                                      B, H, T, dk, dv, chunk, dtype, workspace);
+                                      B, H, T, dk, dv, chunk, dtype, workspace, beta_direct);
   const size_t need = (long long)B * T > 0 ? kla::chunk_workspace_bytes(a) : 0;
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return KLA_ERR_WORKSPACE;
   return from_hip(kla::launch_chunk_fwd(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+int kla_abi_version(void) { return KLA_ABI_VERSION; }
+
+const char *kla_status_str(kla_status_t s) {
+  switch (s) {
+    case KLA_OK: return "ok";
+    case KLA_ERR_NULL: return "a required pointer is NULL";
+    case KLA_ERR_SHAPE: return "invalid or inconsistent sizes";
+    case KLA_ERR_DTYPE: return "unknown dtype";
+    case KLA_ERR_UNSUPPORTED: return "shape/dtype/chunk combination not compiled";
+    case KLA_ERR_SEQLENS: return "cu_seqlens must be non-decreasing from 0 to T";
+    case KLA_ERR_EPS: return "eps must be finite and >= 0";
+    case KLA_ERR_ALIGN: return "data pointers must be 16-byte aligned";
+    case KLA_ERR_WORKSPACE: return "workspace missing or smaller than kla_chunk_workspace_bytes()";
+    case KLA_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+size_t kla_chunk_workspace_bytes(const int32_t *cu_seqlens, const int32_t *cu_seqlens_host, int num_seqs,
+                                 int B, int H, int T, int dk, int dv, int chunk, kla_dtype_t dtype) {
+  if (check_chunk_shapes(0.f, cu_seqlens, cu_seqlens_host, num_seqs, B, H, T, dk, dv, chunk, dtype) != KLA_OK)
+    return 0;
+  if (num_seqs == 0 || (long long)B * T == 0) return 0;
+  return kla::chunk_workspace_bytes(chunk_args(nullptr, nullptr, nullptr, nullptr, nullptr, 0.f, nullptr,
+                                               nullptr, nullptr, cu_seqlens, num_seqs, B, H, T, dk, dv, chunk,
+                                               dtype, nullptr, 0));
+}
+
+kla_status_t kla_chunk_fwd(const void *q, const void *k, const void *v, const void *g,
+                           const void *eta, float eps, const float *initial_state, void *o,
+                           float *final_state, const int32_t *cu_seqlens,
+                           const int32_t *cu_seqlens_host, int num_seqs, int B, int H, int T,
+                           int dk, int dv, int chunk, void *workspace, size_t workspace_bytes,
+                           kla_dtype_t dtype, void *stream) {
+  return chunk_fwd_impl(q, k, v, g, eta, eps, 0, initial_state, o, final_state, cu_seqlens, cu_seqlens_host,
+                        num_seqs, B, H, T, dk, dv, chunk, workspace, workspace_bytes, dtype, stream);
+}
+
+kla_status_t kla_gdn_chunk_fwd(const void *q, const void *k, const void *v, const void *g,
+                               const void *beta, const float *initial_state, void *o, float *final_state,
+                               const int32_t *cu_seqlens, const int32_t *cu_seqlens_host, int num_seqs,
+                               int B, int H, int T, int dk, int dv, int chunk, void *workspace,
+                               size_t workspace_bytes, kla_dtype_t dtype, void *stream) {
+  return chunk_fwd_impl(q, k, v, g, beta, 0.f, 1, initial_state, o, final_state, cu_seqlens, cu_seqlens_host,
+                        num_seqs, B, H, T, dk, dv, chunk, workspace, workspace_bytes, dtype, stream);
+}
+
+kla_status_t kla_decode_step(const void *q, const void *k, const void *v, const void *g,
+                             const void *eta, float eps, float *state, void *o, int N, int H,
+                             int dk, int dv, kla_dtype_t dtype, void *stream) {
+  return decode_impl(q, k, v, g, eta, eps, 0, state, o, N, H, dk, dv, dtype, stream);
+}
+
+kla_status_t kla_gdn_decode_step(const void *q, const void *k, const void *v, const void *g,
+                                 const void *beta, float *state, void *o, int N, int H, int dk, int dv,
+                                 kla_dtype_t dtype, void *stream) {
+  return decode_impl(q, k, v, g, beta, 0.f, 1, state, o, N, H, dk, dv, dtype, stream);
 }
 
 }  // extern "C"

@@ -337,6 +337,7 @@ struct ChunkParams {
   char *ws;
   int H, T, dv, n_tiles, remap, nseq, nslot;
   int pslots;  // prep kernel: workspace slots per workgroup (1 .. kPrepSlots)
+  int beta_direct;  // 1: `eta` holds beta itself (gated delta rule); eps unused
 };
 
 // Raw buffer resource over bytes [0, n) of p: loads at offsets >= n return 0
@@ -634,7 +635,8 @@ __global__ __launch_bounds__(64 * kPrepWaves) void kla_chunk_prep_kernel(ChunkPa
               bv[2 * C + lane] = __expf(gamC - gam);  // d_r
             }
             if (owns_block(NB, part, lane >> 4)) {
-              const float beta = (lane < nrow) ? ge[C + lane] / (sNrm[lane] + p.eps) : 0.f;
+              const float beta =
+                  (lane < nrow) ? (p.beta_direct ? ge[C + lane] : ge[C + lane] / (sNrm[lane] + p.eps)) : 0.f;
               sBet[lane] = beta;
               bv[3 * C + lane] = beta;
             }
@@ -1303,6 +1305,7 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t st) {
   p.dv = a.dv;
   p.n_tiles = a.dv / Sh::DVT;
   p.nseq = a.num_seqs;
+  p.beta_direct = a.beta_direct;
   p.nslot = slots_per_head(a.cu_seqlens != nullptr, a.B, a.T, a.num_seqs, C);
   const long long nblk = (long long)a.num_seqs * a.H * p.n_tiles;
   p.remap = (nblk % 8 == 0) ? 1 : 0;

@@ -1,7 +1,8 @@
 // kla_decode.hip -- single-token KLA decode step for gfx950.
 //
 // One recurrent step per (sequence, head):
-//   alpha = exp(g), beta = eta / (||k||^2 + eps)
+//   alpha = exp(g), beta = eta / (||k||^2 + eps)  (or beta = eta as given: the
+//   gated delta rule, whose learned coefficient the Kaczmarz step replaces)
 //   y_k = S^T k, y_q = S^T q           (one pass over the old state)
 //   e   = v - alpha y_k
 //   o   = alpha y_q + beta (k.q) e     (= S_new^T q without a second pass)
@@ -39,7 +40,7 @@ struct DecodeShape {
 template <typename E, int DK, int DV>
 __global__ __launch_bounds__(decode_threads(DK, DV)) void kla_decode_kernel(
     const E *__restrict__ q, const E *__restrict__ k, const E *__restrict__ v,
-    const E *__restrict__ g, const E *__restrict__ eta, float eps, float *__restrict__ state,
+    const E *__restrict__ g, const E *__restrict__ eta, float eps, int beta_direct, float *__restrict__ state,
     E *__restrict__ o) {
   using Sh = DecodeShape<DK, DV>;
   constexpr int TPR = Sh::TPR, RG = Sh::RG, RPT = Sh::RPT, NW = Sh::NW;
@@ -109,7 +110,7 @@ __global__ __launch_bounds__(decode_threads(DK, DV)) void kla_decode_kernel(
     }
   }
 
-  const float beta = et / (red[8] + eps);
+  const float beta = beta_direct ? et : et / (red[8] + eps);
   const float bkq = beta * red[9];
   float e[4], oo[4];
 #pragma unroll
@@ -136,7 +137,7 @@ static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t st) {
   const unsigned nblk = (unsigned)((size_t)a.N * a.H);
   hipLaunchKernelGGL((kla_decode_kernel<E, DK, DV>), dim3(nblk), dim3(DecodeShape<DK, DV>::NT), 0,
                      st, (const E *)a.q, (const E *)a.k, (const E *)a.v, (const E *)a.g,
-                     (const E *)a.eta, a.eps, a.state, (E *)a.o);
+                     (const E *)a.eta, a.eps, a.beta_direct, a.state, (E *)a.o);
   return hipGetLastError();
 }
 

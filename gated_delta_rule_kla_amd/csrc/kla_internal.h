@@ -12,7 +12,8 @@ struct DecodeArgs {
   float *state;
   void *o;
   int N, H, dk, dv;
-  int dtype;  // kla_dtype_t
+  int dtype;        // kla_dtype_t
+  int beta_direct;  // 1: `eta` holds beta itself (gated delta rule); eps unused
 };
 
 struct ChunkArgs {
@@ -25,6 +26,7 @@ struct ChunkArgs {
   int num_seqs, B, H, T, dk, dv, chunk;
   int dtype;        // kla_dtype_t
   void *workspace;  // device, chunk_workspace_bytes(*this) bytes
+  int beta_direct;  // 1: `eta` holds beta itself (gated delta rule); eps unused
 };
 
 // True if a kernel is compiled for this combination.

@@ -23,6 +23,7 @@ values are then rounded once with round-to-nearest-even to the input dtype.
 
 from __future__ import annotations
 
+import dataclasses
 import math
 from dataclasses import dataclass
 from typing import Optional
@@ -197,6 +198,20 @@ def make_decode(
     q, k, v, g, eta = _draw_tokens(rng, (steps, N, H), dk, dv, sigma_k, g_scale, eta_mu, dtype)
     s0 = torch.from_numpy(s0_std * rng.standard_normal((N, H, dk, dv), dtype=np.float32))
     return DecodeInputs(q, k, v, g, eta, _f32(eps), s0, name)
+
+
+def unit_keys(x):
+    """A copy of prefill or decode inputs ``x`` with every key vector scaled to
+    unit length (in fp64 from the rounded keys, then rounded again), for the
+    gated-delta-rule mode: there the update coefficient is given, and keys of
+    length 1 with coefficients in (0, 1) are the regime in which that rule is
+    contractive.  The ``eta`` draws (sigmoid of a normal) then serve as the
+    coefficients beta.  Everything else is shared with ``x``."""
+    k = x.k.to(torch.float64)
+    k = k / torch.linalg.vector_norm(k, dim=-1, keepdim=True).clamp_min(1e-30)
+    out = dataclasses.replace(x, k=k.to(x.k.dtype))
+    out.name = (x.name or "inputs") + "-unitkeys"
+    return out
 
 
 def _log_uniform_lengths(rng, n, lo, hi):

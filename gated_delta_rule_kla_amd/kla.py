@@ -13,8 +13,8 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["chunk_fwd", "chunk_workspace_bytes", "decode_step", "lib", "lib_path", "KlaError",
-           "KLA_DT_BF16", "KLA_DT_F32"]
+__all__ = ["chunk_fwd", "chunk_workspace_bytes", "decode_step", "gdn_chunk_fwd", "gdn_decode_step", "lib",
+           "lib_path", "KlaError", "KLA_DT_BF16", "KLA_DT_F32"]
 
 KLA_DT_BF16 = 0
 KLA_DT_F32 = 1
@@ -55,6 +55,11 @@ def lib() -> ctypes.CDLL:
         L.kla_decode_step.argtypes = [vp, vp, vp, vp, vp, f32, vp, vp,
                                       i32, i32, i32, i32, i32, vp]
         L.kla_decode_step.restype = i32
+        L.kla_gdn_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                        i32, i32, i32, i32, i32, i32, i32, vp, sz, i32, vp]
+        L.kla_gdn_chunk_fwd.restype = i32
+        L.kla_gdn_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
+        L.kla_gdn_decode_step.restype = i32
         L.kla_status_str.argtypes = [i32]
         L.kla_status_str.restype = ctypes.c_char_p
         L.kla_abi_version.argtypes = []
@@ -89,35 +94,11 @@ def _need(t: torch.Tensor, name: str, dtype: torch.dtype, shape, device) -> None
         raise ValueError(f"{name} must be contiguous")
 
 
-def chunk_fwd(
-    q: torch.Tensor,
-    k: torch.Tensor,
-    v: torch.Tensor,
-    g: torch.Tensor,
-    eta: torch.Tensor,
-    eps: float = 1e-6,
-    initial_state: Optional[torch.Tensor] = None,
-    cu_seqlens: Optional[torch.Tensor] = None,
-    chunk: int = 64,
-    output_final_state: bool = True,
-    cu_seqlens_host: Optional[torch.Tensor] = None,
-    out: Optional[torch.Tensor] = None,
-    final_state: Optional[torch.Tensor] = None,
-    workspace: Optional[torch.Tensor] = None,
-) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """KLA chunkwise prefill (kla_chunk_fwd).
-
-    q, k: [B, H, T, dk]; v: [B, H, T, dv]; g, eta: [B, H, T]; all bf16 or all
-    fp32 on one GPU.  initial_state: [N, H, dk, dv] fp32 or None.  cu_seqlens:
-    int32 [N + 1] on the GPU (B must be 1) or None.  Returns (o, final_state).
-    ``final_state`` may be passed as the same tensor as ``initial_state`` to
-    update it in place.  ``workspace`` (uint8, on the GPU, at least
-    chunk_workspace_bytes(...) bytes) is taken from torch's caching allocator
-    on the current stream when not given.
-    """
+def _chunk_call(fn: str, q, k, v, g, coef, eps, initial_state, cu_seqlens, chunk, output_final_state,
+                cu_seqlens_host, out, final_state, workspace):
     dev = q.device
     if dev.type != "cuda":
-        raise ValueError("kla.chunk_fwd needs GPU tensors")
+        raise ValueError(f"kla.{fn} needs GPU tensors")
     dtype = q.dtype
     if dtype not in _DTYPES:
         raise TypeError(f"unsupported dtype {dtype}")
@@ -127,7 +108,7 @@ def chunk_fwd(
     _need(k, "k", dtype, (B, H, T, dk), dev)
     _need(v, "v", dtype, (B, H, T, dv), dev)
     _need(g, "g", dtype, (B, H, T), dev)
-    _need(eta, "eta", dtype, (B, H, T), dev)
+    _need(coef, "eta" if eps is not None else "beta", dtype, (B, H, T), dev)
     if cu_seqlens is not None:
         _need(cu_seqlens, "cu_seqlens", torch.int32, (cu_seqlens.numel(),), dev)
         if cu_seqlens_host is None:
@@ -155,13 +136,66 @@ def chunk_fwd(
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     elif workspace.device != dev or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous uint8 tensor on the inputs' device")
-    st = lib().kla_chunk_fwd(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(eta), float(eps),
-        _ptr(initial_state), _ptr(out), _ptr(final_state),
-        _ptr(cu_seqlens), host_ptr, N, B, H, T, dk, dv, int(chunk),
-        _ptr(workspace), workspace.numel(), _DTYPES[dtype], _stream(dev))
-    _check("kla_chunk_fwd", st)
+    tail = (_ptr(initial_state), _ptr(out), _ptr(final_state), _ptr(cu_seqlens), host_ptr, N, B, H, T, dk, dv,
+            int(chunk), _ptr(workspace), workspace.numel(), _DTYPES[dtype], _stream(dev))
+    if eps is not None:
+        st = lib().kla_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(coef), float(eps), *tail)
+        _check("kla_chunk_fwd", st)
+    else:
+        st = lib().kla_gdn_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(coef), *tail)
+        _check("kla_gdn_chunk_fwd", st)
     return out, final_state
+
+
+def chunk_fwd(
+    q: torch.Tensor,
+    k: torch.Tensor,
+    v: torch.Tensor,
+    g: torch.Tensor,
+    eta: torch.Tensor,
+    eps: float = 1e-6,
+    initial_state: Optional[torch.Tensor] = None,
+    cu_seqlens: Optional[torch.Tensor] = None,
+    chunk: int = 64,
+    output_final_state: bool = True,
+    cu_seqlens_host: Optional[torch.Tensor] = None,
+    out: Optional[torch.Tensor] = None,
+    final_state: Optional[torch.Tensor] = None,
+    workspace: Optional[torch.Tensor] = None,
+) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """KLA chunkwise prefill (kla_chunk_fwd).
+
+    q, k: [B, H, T, dk]; v: [B, H, T, dv]; g, eta: [B, H, T]; all bf16 or all
+    fp32 on one GPU.  initial_state: [N, H, dk, dv] fp32 or None.  cu_seqlens:
+    int32 [N + 1] on the GPU (B must be 1) or None.  Returns (o, final_state).
+    ``final_state`` may be passed as the same tensor as ``initial_state`` to
+    update it in place.  ``workspace`` (uint8, on the GPU, at least
+    chunk_workspace_bytes(...) bytes) is taken from torch's caching allocator
+    on the current stream when not given.
+    """
+    return _chunk_call("chunk_fwd", q, k, v, g, eta, eps, initial_state, cu_seqlens, chunk,
+                       output_final_state, cu_seqlens_host, out, final_state, workspace)
+
+
+def gdn_chunk_fwd(
+    q: torch.Tensor,
+    k: torch.Tensor,
+    v: torch.Tensor,
+    g: torch.Tensor,
+    beta: torch.Tensor,
+    initial_state: Optional[torch.Tensor] = None,
+    cu_seqlens: Optional[torch.Tensor] = None,
+    chunk: int = 64,
+    output_final_state: bool = True,
+    cu_seqlens_host: Optional[torch.Tensor] = None,
+    out: Optional[torch.Tensor] = None,
+    final_state: Optional[torch.Tensor] = None,
+    workspace: Optional[torch.Tensor] = None,
+) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Gated delta rule chunkwise prefill (kla_gdn_chunk_fwd): as chunk_fwd
+    with the update coefficient ``beta`` [B, H, T] given instead of eta, eps."""
+    return _chunk_call("gdn_chunk_fwd", q, k, v, g, beta, None, initial_state, cu_seqlens, chunk,
+                       output_final_state, cu_seqlens_host, out, final_state, workspace)
 
 
 def chunk_workspace_bytes(B: int, H: int, T: int, dk: int, dv: int, chunk: int = 64,
@@ -176,6 +210,35 @@ def chunk_workspace_bytes(B: int, H: int, T: int, dk: int, dv: int, chunk: int =
         return lib().kla_chunk_workspace_bytes(ctypes.c_void_p(16), cu.data_ptr(), cu.numel() - 1, B, H, T,
                                                dk, dv, int(chunk), _DTYPES[dtype])
     return lib().kla_chunk_workspace_bytes(None, None, B, B, H, T, dk, dv, int(chunk), _DTYPES[dtype])
+
+
+def _decode_call(fn, q, k, v, g, coef, eps, state, out):
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError(f"kla.{fn} needs GPU tensors")
+    dtype = q.dtype
+    if dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {dtype}")
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    _need(q, "q", dtype, (N, H, dk), dev)
+    _need(k, "k", dtype, (N, H, dk), dev)
+    _need(v, "v", dtype, (N, H, dv), dev)
+    _need(g, "g", dtype, (N, H), dev)
+    _need(coef, "eta" if eps is not None else "beta", dtype, (N, H), dev)
+    _need(state, "state", torch.float32, (N, H, dk, dv), dev)
+    if out is None:
+        out = torch.empty((N, H, dv), dtype=dtype, device=dev)
+    else:
+        _need(out, "out", dtype, (N, H, dv), dev)
+    tail = (_ptr(state), _ptr(out), N, H, dk, dv, _DTYPES[dtype], _stream(dev))
+    if eps is not None:
+        st = lib().kla_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(coef), float(eps), *tail)
+        _check("kla_decode_step", st)
+    else:
+        st = lib().kla_gdn_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(coef), *tail)
+        _check("kla_gdn_decode_step", st)
+    return out
 
 
 def decode_step(
@@ -193,26 +256,18 @@ def decode_step(
     q, k: [N, H, dk]; v: [N, H, dv]; g, eta: [N, H]; state: [N, H, dk, dv] fp32.
     Returns o [N, H, dv].
     """
-    dev = q.device
-    if dev.type != "cuda":
-        raise ValueError("kla.decode_step needs GPU tensors")
-    dtype = q.dtype
-    if dtype not in _DTYPES:
-        raise TypeError(f"unsupported dtype {dtype}")
-    N, H, dk = q.shape
-    dv = v.shape[-1]
-    _need(q, "q", dtype, (N, H, dk), dev)
-    _need(k, "k", dtype, (N, H, dk), dev)
-    _need(v, "v", dtype, (N, H, dv), dev)
-    _need(g, "g", dtype, (N, H), dev)
-    _need(eta, "eta", dtype, (N, H), dev)
-    _need(state, "state", torch.float32, (N, H, dk, dv), dev)
-    if out is None:
-        out = torch.empty((N, H, dv), dtype=dtype, device=dev)
-    else:
-        _need(out, "out", dtype, (N, H, dv), dev)
-    st = lib().kla_decode_step(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(eta), float(eps), _ptr(state), _ptr(out),
-        N, H, dk, dv, _DTYPES[dtype], _stream(dev))
-    _check("kla_decode_step", st)
-    return out
+    return _decode_call("decode_step", q, k, v, g, eta, eps, state, out)
+
+
+def gdn_decode_step(
+    q: torch.Tensor,
+    k: torch.Tensor,
+    v: torch.Tensor,
+    g: torch.Tensor,
+    beta: torch.Tensor,
+    state: torch.Tensor,
+    out: Optional[torch.Tensor] = None,
+) -> torch.Tensor:
+    """One gated-delta-rule step (kla_gdn_decode_step): as decode_step with the
+    update coefficient ``beta`` [N, H] given; ``state`` is updated in place."""
+    return _decode_call("gdn_decode_step", q, k, v, g, beta, None, state, out)

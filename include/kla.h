@@ -105,9 +105,9 @@ typedef enum {
  *
  * Two kernels run on `stream`: a prep kernel computes, for every (chunk,
  * head) in parallel, the S-independent part of the block solver (beta, the
- * decay weights, K K^T, T, T' = T Diag(beta) and the decayed causal scores
- * of Q K^T) into the workspace; the scan kernel then walks each sequence's
- * chunks with the state in registers.
+ * decay weights, K K^T, T and T' = T Diag(beta)) into the workspace; the
+ * scan kernel then walks each sequence's chunks with the state in registers,
+ * and forms the decayed causal scores of Q K^T and the output.
  *
  * Supported: dtype BF16 with chunk 64 and dk in {64, 128}; dtype F32 with
  * chunk 16 and dk in {16, 32, 64, 128}, or chunk 64 and dk in {16, 32}; for
@@ -124,8 +124,8 @@ kla_status_t kla_chunk_fwd(const void *q, const void *k, const void *v,
 
 /*
  * kla_chunk_workspace_bytes -- device workspace kla_chunk_fwd needs for these
- * arguments (the same meaning as there; host-only, no HIP call).  16,128
- * bytes per (64-token chunk, head) in bf16.  Returns 0 when no workspace is
+ * arguments (the same meaning as there; host-only, no HIP call).  11,008
+ * bytes per (64-token chunk, head) in bf16.  kla_gdn_chunk_fwd needs the same.  Returns 0 when no workspace is
  * needed (no tokens) and also for arguments kla_chunk_fwd would reject.
  */
 size_t kla_chunk_workspace_bytes(const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
@@ -155,13 +155,43 @@ kla_status_t kla_decode_step(const void *q, const void *k, const void *v,
                              int N, int H, int dk, int dv,
                              kla_dtype_t dtype, void *stream);
 
+/*
+ * kla_gdn_chunk_fwd, kla_gdn_decode_step -- the same two operations for the
+ * gated delta rule (Gated DeltaNet), the model KLA modifies: KLA keeps
+ * GDN's state, gates, recurrence and block-parallel algorithm and only
+ * replaces its learned scalar update coefficient with the Kaczmarz step
+ * eta / (||k||^2 + eps) (§"Declaración del Problema", §"Metodología: Atención
+ * Lineal Kaczmarz", §"Implementación").  Here that coefficient is given:
+ *
+ *   beta    [B, H, T] (chunk) or [N, H] (decode), dtype: the update
+ *           coefficient beta_t itself, used as S = alpha S + beta_t k e^T
+ *
+ * in place of eta and eps; every other argument, layout, status code and
+ * supported shape is that of kla_chunk_fwd / kla_decode_step (the same
+ * kernels run; kla_chunk_workspace_bytes sizes the workspace).  With
+ * beta_t = eta_t / (||k_t||^2 + eps) the results equal KLA's.
+ */
+kla_status_t kla_gdn_chunk_fwd(const void *q, const void *k, const void *v,
+                               const void *g, const void *beta,
+                               const float *initial_state, void *o, float *final_state,
+                               const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
+                               int num_seqs, int B, int H, int T, int dk, int dv, int chunk,
+                               void *workspace, size_t workspace_bytes,
+                               kla_dtype_t dtype, void *stream);
+
+kla_status_t kla_gdn_decode_step(const void *q, const void *k, const void *v,
+                                 const void *g, const void *beta,
+                                 float *state, void *o,
+                                 int N, int H, int dk, int dv,
+                                 kla_dtype_t dtype, void *stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *kla_status_str(kla_status_t s);
 
 /* ABI version of this header (incremented on any incompatible change). */
 int kla_abi_version(void);
 
-#define KLA_ABI_VERSION 2
+#define KLA_ABI_VERSION 3
 
 #ifdef __cplusplus
 }

@@ -5,7 +5,9 @@ benchmark's CPU-baseline leg, never by the product path.  It shares no code
 with the HIP kernels or their binding.
 """
 
-from .kla_oracle import kla_decode_step, kla_forward, kla_recurrence
+from .kla_oracle import (gdn_decode_step, gdn_forward, gdn_recurrence, kla_decode_step, kla_forward,
+                         kla_recurrence)
 from .kla_chunk_oracle import kla_chunkwise
 
-__all__ = ["kla_recurrence", "kla_forward", "kla_decode_step", "kla_chunkwise"]
+__all__ = ["kla_recurrence", "kla_forward", "kla_decode_step", "kla_chunkwise", "gdn_recurrence",
+           "gdn_forward", "gdn_decode_step"]

@@ -47,13 +47,16 @@ def kla_chunkwise(
     S0: Optional[np.ndarray],
     chunk: int,
     return_chunks: bool = False,
+    beta_given: Optional[np.ndarray] = None,
 ):
     """Chunkwise KLA for ONE sequence and ONE head in fp64.
 
     q, k: [L, dk]; v: [L, dv]; g, eta: [L]; S0: [dk, dv] or None.  The last
     chunk may be shorter than ``chunk``.  Returns (o [L, dv], S_L) and, with
     ``return_chunks``, a list of per-chunk dicts (beta, gamma, A, T, W, U, Ut,
-    P) for inspecting intermediates.
+    P) for inspecting intermediates.  With ``beta_given`` ([L]) the diagonal
+    coefficients are taken as given (the gated delta rule, whose block solver
+    KLA keeps, [KLA] §"Implementación") and eta, eps are not used.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -69,7 +72,10 @@ def kla_chunkwise(
         c1 = min(c0 + chunk, L)
         n = c1 - c0
         K, Q, V = k[c0:c1], q[c0:c1], v[c0:c1]
-        beta = eta[c0:c1] / (np.sum(K * K, axis=1) + eps)
+        if beta_given is None:
+            beta = eta[c0:c1] / (np.sum(K * K, axis=1) + eps)
+        else:
+            beta = np.asarray(beta_given, dtype=np.float64)[c0:c1]
         gamma = np.cumsum(g[c0:c1])
         Gam = np.exp(gamma)
         lower_incl = np.tril(np.ones((n, n), dtype=bool))

@@ -42,7 +42,8 @@ from typing import Optional, Sequence, Tuple
 
 import numpy as np
 
-__all__ = ["kla_recurrence", "kla_forward", "kla_decode_step"]
+__all__ = ["kla_recurrence", "kla_forward", "kla_decode_step", "gdn_recurrence", "gdn_forward",
+           "gdn_decode_step"]
 
 
 def kla_recurrence(
@@ -95,10 +96,12 @@ def kla_recurrence(
     return o, S
 
 
-def _run_heads(q, k, v, g, eta, eps, S):
+def _run_heads(q, k, v, g, eta, eps, S, beta_given=None):
     """The same recurrence vectorised over a leading head axis (in place on S).
 
     q, k: [H, L, dk]; v: [H, L, dv]; g, eta: [H, L]; S: [H, dk, dv] fp64.
+    With ``beta_given`` ([H, L]) the update coefficient is taken as given
+    (the gated delta rule) and eta, eps are not used.
     Returns o [H, L, dv].
     """
     H, L, _ = k.shape
@@ -106,12 +109,46 @@ def _run_heads(q, k, v, g, eta, eps, S):
     for t in range(L):
         kt = k[:, t, :]                                     # [H, dk]
         alpha = np.exp(g[:, t])                             # [H]
-        beta = eta[:, t] / (np.einsum("hi,hi->h", kt, kt) + eps)
+        if beta_given is None:
+            beta = eta[:, t] / (np.einsum("hi,hi->h", kt, kt) + eps)
+        else:
+            beta = beta_given[:, t]
         S *= alpha[:, None, None]                           # S~ = alpha S
         e = v[:, t, :] - np.einsum("hij,hi->hj", S, kt)     # e = v - S~^T k
         S += beta[:, None, None] * kt[:, :, None] * e[:, None, :]
         o[:, t, :] = np.einsum("hij,hi->hj", S, q[:, t, :])  # o = S^T q
     return o
+
+
+def _forward(q, k, v, g, coef, eps, initial_state, cu_seqlens, heads, beta_given):
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    g = np.asarray(g, dtype=np.float64)
+    coef = np.asarray(coef, dtype=np.float64)
+    B, H, T, dk = k.shape
+    dv = v.shape[3]
+    if cu_seqlens is None:
+        segs = [(b, 0, T) for b in range(B)]
+    else:
+        if B != 1:
+            raise ValueError("packed sequences need B == 1")
+        cu = [int(x) for x in cu_seqlens]
+        segs = [(0, cu[n], cu[n + 1]) for n in range(len(cu) - 1)]
+    hs = list(range(H)) if heads is None else [int(h) for h in heads]
+    o = np.full((B, H, T, dv), np.nan)
+    S_fin = np.full((len(segs), H, dk, dv), np.nan)
+    for n, (b, t0, t1) in enumerate(segs):
+        if initial_state is None:
+            S = np.zeros((len(hs), dk, dv))
+        else:
+            S = np.array(np.asarray(initial_state, dtype=np.float64)[n, hs], copy=True)
+        c = coef[b, hs, t0:t1]
+        o[b, hs, t0:t1] = _run_heads(q[b, hs, t0:t1], k[b, hs, t0:t1], v[b, hs, t0:t1],
+                                     g[b, hs, t0:t1], None if beta_given else c, eps, S,
+                                     beta_given=c if beta_given else None)
+        S_fin[n, hs] = S
+    return o, S_fin
 
 
 def kla_forward(
@@ -136,32 +173,26 @@ def kla_forward(
 
     Returns (o [B, H, T, dv], final states [N, H, dk, dv]).
     """
-    q = np.asarray(q, dtype=np.float64)
-    k = np.asarray(k, dtype=np.float64)
-    v = np.asarray(v, dtype=np.float64)
-    g = np.asarray(g, dtype=np.float64)
-    eta = np.asarray(eta, dtype=np.float64)
-    B, H, T, dk = k.shape
-    dv = v.shape[3]
-    if cu_seqlens is None:
-        segs = [(b, 0, T) for b in range(B)]
-    else:
-        if B != 1:
-            raise ValueError("packed sequences need B == 1")
-        cu = [int(x) for x in cu_seqlens]
-        segs = [(0, cu[n], cu[n + 1]) for n in range(len(cu) - 1)]
-    hs = list(range(H)) if heads is None else [int(h) for h in heads]
-    o = np.full((B, H, T, dv), np.nan)
-    S_fin = np.full((len(segs), H, dk, dv), np.nan)
-    for n, (b, t0, t1) in enumerate(segs):
-        if initial_state is None:
-            S = np.zeros((len(hs), dk, dv))
-        else:
-            S = np.array(np.asarray(initial_state, dtype=np.float64)[n, hs], copy=True)
-        o[b, hs, t0:t1] = _run_heads(q[b, hs, t0:t1], k[b, hs, t0:t1], v[b, hs, t0:t1],
-                                     g[b, hs, t0:t1], eta[b, hs, t0:t1], eps, S)
-        S_fin[n, hs] = S
-    return o, S_fin
+    return _forward(q, k, v, g, eta, eps, initial_state, cu_seqlens, heads, beta_given=False)
+
+
+def gdn_forward(
+    q: np.ndarray,
+    k: np.ndarray,
+    v: np.ndarray,
+    g: np.ndarray,
+    beta: np.ndarray,
+    initial_state: Optional[np.ndarray] = None,
+    cu_seqlens: Optional[Sequence[int]] = None,
+    heads: Optional[Sequence[int]] = None,
+) -> Tuple[np.ndarray, np.ndarray]:
+    """The gated delta rule (Gated DeltaNet) over a batch, fp64: the KLA
+    recurrence with the update coefficient beta_t [B, H, T] given instead of
+    eta_t / (||k_t||^2 + eps).  [KLA] §"Declaración del Problema" and
+    §"Metodología: Atención Lineal Kaczmarz": KLA is GDN with that learned
+    coefficient replaced by the Kaczmarz step; state, gates and recurrence are
+    kept (§"Implementación").  Arguments and results as kla_forward."""
+    return _forward(q, k, v, g, beta, None, initial_state, cu_seqlens, heads, beta_given=True)
 
 
 def kla_decode_step(
@@ -188,3 +219,45 @@ def kla_decode_step(
                    v.reshape(N * H, 1, -1), np.asarray(g, np.float64).reshape(N * H, 1),
                    np.asarray(eta, np.float64).reshape(N * H, 1), eps, S)
     return o.reshape(N, H, -1), S.reshape(N, H, dk, -1)
+
+
+def gdn_decode_step(
+    q: np.ndarray,
+    k: np.ndarray,
+    v: np.ndarray,
+    g: np.ndarray,
+    beta: np.ndarray,
+    state: np.ndarray,
+) -> Tuple[np.ndarray, np.ndarray]:
+    """One gated-delta-rule step for N sequences x H heads, fp64 (beta [N, H]
+    given); as kla_decode_step otherwise."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    N, H, dk = k.shape
+    S = np.array(state, dtype=np.float64, copy=True).reshape(N * H, dk, -1)
+    o = _run_heads(q.reshape(N * H, 1, dk), k.reshape(N * H, 1, dk),
+                   v.reshape(N * H, 1, -1), np.asarray(g, np.float64).reshape(N * H, 1),
+                   None, None, S, beta_given=np.asarray(beta, np.float64).reshape(N * H, 1))
+    return o.reshape(N, H, -1), S.reshape(N, H, dk, -1)
+
+
+def gdn_recurrence(q, k, v, g, beta, S0=None):
+    """Token-by-token gated delta rule for ONE sequence and ONE head, fp64:
+    q, k [L, dk]; v [L, dv]; g, beta [L]; S0 [dk, dv] or None.  Each step:
+    S~ = exp(g_t) S, e = v_t - S~^T k_t, S = S~ + beta_t k_t e^T, o_t = S^T q_t.
+    Returns (o [L, dv], S_L)."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    g = np.asarray(g, dtype=np.float64)
+    beta = np.asarray(beta, dtype=np.float64)
+    L, dk = k.shape
+    S = np.zeros((dk, v.shape[1])) if S0 is None else np.array(S0, dtype=np.float64, copy=True)
+    o = np.empty((L, v.shape[1]))
+    for t in range(L):
+        S_dec = np.exp(g[t]) * S
+        e = v[t] - S_dec.T @ k[t]
+        S = S_dec + beta[t] * np.outer(k[t], e)
+        o[t] = S.T @ q[t]
+    return o, S

@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol():
     L = kla.lib()
     names = _declared()
     assert set(names) >= {"kla_chunk_fwd", "kla_chunk_workspace_bytes", "kla_decode_step", "kla_status_str",
-                          "kla_abi_version"}
+                          "kla_abi_version", "kla_gdn_chunk_fwd", "kla_gdn_decode_step"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -135,6 +135,47 @@ def test_decode_zero_sequences_is_noop():
     assert _decode(N=0) == OK
 
 
+def _gdn_chunk(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, s0=None, o=FAKE, sf=FAKE,
+             cu=None, cuh=None, N=2, B=2, H=4, T=100, dk=128, dv=128, chunk=64, ws=FAKE,
+             ws_bytes=1 << 40, dtype=0)
+    a.update(kw)
+    return kla.lib().kla_gdn_chunk_fwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["s0"], a["o"], a["sf"],
+                                       a["cu"], a["cuh"], a["N"], a["B"], a["H"], a["T"], a["dk"], a["dv"],
+                                       a["chunk"], a["ws"], a["ws_bytes"], a["dtype"], None)
+
+
+def _gdn_decode(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, S=FAKE, o=FAKE, N=3, H=2, dk=128, dv=128, dtype=0)
+    a.update(kw)
+    return kla.lib().kla_gdn_decode_step(a["q"], a["k"], a["v"], a["g"], a["beta"], a["S"], a["o"], a["N"],
+                                         a["H"], a["dk"], a["dv"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=5), E_DTYPE),
+    (dict(T=-3), E_SHAPE),
+    (dict(dk=96), E_UNSUP),
+    (dict(beta=None), E_NULL),
+    (dict(beta=FAKE + 4), E_ALIGN),
+    (dict(ws=None), E_WS),
+    (dict(N=0, B=0), OK),
+])
+def test_gdn_chunk_fwd_rejects(kw, code):
+    assert _gdn_chunk(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=5), E_DTYPE),
+    (dict(dv=24), E_UNSUP),
+    (dict(beta=None), E_NULL),
+    (dict(S=FAKE + 8), E_ALIGN),
+    (dict(N=0), OK),
+])
+def test_gdn_decode_rejects(kw, code):
+    assert _gdn_decode(**kw) == code
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     x = torch.zeros(1, 1, 4, 16)
@@ -142,6 +183,10 @@ def test_binding_refuses_cpu_tensors():
         kla.chunk_fwd(x, x, x, x[..., 0], x[..., 0])
     with pytest.raises(ValueError):
         kla.decode_step(x[0], x[0], x[0], x[0, :, 0], x[0, :, 0], 1e-6, x)
+    with pytest.raises(ValueError):
+        kla.gdn_chunk_fwd(x, x, x, x[..., 0], x[..., 0])
+    with pytest.raises(ValueError):
+        kla.gdn_decode_step(x[0], x[0], x[0], x[0, :, 0], x[0, :, 0], x)
 
 
 def test_workspace_bytes():

@@ -12,7 +12,7 @@ import pytest
 import torch
 
 from gated_delta_rule_kla_amd import inputs, kla
-from oracle import kla_decode_step, kla_forward
+from oracle import gdn_decode_step, gdn_forward, kla_decode_step, kla_forward
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -167,6 +167,75 @@ def test_prefill_then_decode_continues_the_sequence():
     assert rel_err(f(st), S_r) <= 2e-2
 
 
+# --------------------------------------- gated delta rule (beta given) ----
+# The same kernels with the update coefficient taken as given (kla_gdn_*):
+# unit-length keys, beta = the sigmoid draws.
+
+def run_gdn_prefill(x, chunk=None):
+    s0 = None if x.initial_state is None else x.initial_state.to(DEV)
+    cu = None if x.cu_seqlens is None else x.cu_seqlens.to(DEV)
+    o, S = kla.gdn_chunk_fwd(x.q.to(DEV), x.k.to(DEV), x.v.to(DEV), x.g.to(DEV), x.eta.to(DEV), s0, cu,
+                             chunk=chunk or x.chunk, cu_seqlens_host=x.cu_seqlens)
+    torch.cuda.synchronize()
+    return o.cpu(), S.cpu()
+
+
+def check_gdn_prefill(x):
+    o, S = run_gdn_prefill(x)
+    cu = None if x.cu_seqlens is None else x.cu_seqlens.tolist()
+    o_r, S_r = gdn_forward(f(x.q), f(x.k), f(x.v), f(x.g), f(x.eta), f(x.initial_state), cu_seqlens=cu)
+    tol = TOL[x.q.dtype]
+    eo, es = rel_err(f(o), o_r), rel_err(f(S), S_r)
+    print(f"{x.name}: err_o={eo:.3e} err_S={es:.3e} tol={tol}")
+    assert eo <= tol and es <= tol, (eo, es)
+
+
+@pytest.mark.parametrize("B,H,T,dk,dv", [(2, 3, 300, 128, 128), (1, 2, 129, 64, 64), (1, 1, 40, 128, 256)])
+def test_gdn_prefill_bf16(B, H, T, dk, dv):
+    x = inputs.unit_keys(inputs.make_prefill(B=B, H=H, T=T, dk=dk, dv=dv, chunk=64, s0_std=0.02,
+                                             seed=40 + T, name=f"gdn-{B}x{H}x{T}-{dk}x{dv}"))
+    check_gdn_prefill(x)
+
+
+def test_gdn_prefill_varlen():
+    x = inputs.unit_keys(inputs.make_prefill(H=2, dk=128, dv=128, chunk=64, s0_std=0.02,
+                                             lengths=[0, 5, 64, 130, 1], seed=41, name="gdn-varlen"))
+    check_gdn_prefill(x)
+
+
+@pytest.mark.parametrize("chunk,dk", [(16, 16), (16, 128), (64, 32)])
+def test_gdn_prefill_fp32(chunk, dk):
+    x = inputs.unit_keys(inputs.make_prefill(B=1, H=2, T=150, dk=dk, dv=16, chunk=chunk, dtype=torch.float32,
+                                             seed=42 + dk, name=f"gdn-fp32-c{chunk}-dk{dk}"))
+    check_gdn_prefill(x)
+
+
+def test_gdn_with_the_kaczmarz_step_equals_kla():
+    """beta_t = eta_t / (||k_t||^2 + eps), formed on the host in fp32, through the
+    gated-delta-rule entry point gives KLA's result (fp32 debug build)."""
+    x = inputs.make_prefill(B=1, H=2, T=200, dk=32, dv=16, chunk=16, dtype=torch.float32, s0_std=0.05,
+                            seed=43, name="gdn-vs-kla")
+    o_k, S_k = run_prefill(x)
+    beta = (x.eta / ((x.k * x.k).sum(-1) + x.eps)).to(torch.float32)
+    y = inputs.PrefillInputs(x.q, x.k, x.v, x.g, beta, 0.0, x.initial_state, None, 16)
+    o_g, S_g = run_gdn_prefill(y)
+    assert rel_err(f(o_g), f(o_k)) <= 1e-5 and rel_err(f(S_g), f(S_k)) <= 1e-5
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_gdn_decode_small(dtype):
+    d = inputs.unit_keys(inputs.make_decode(N=3, H=2, dk=128, dv=128, steps=4, dtype=dtype, seed=44))
+    st = d.state.to(DEV)
+    S_r = f(d.state)
+    for s in range(4):
+        o = kla.gdn_decode_step(d.q[s].to(DEV), d.k[s].to(DEV), d.v[s].to(DEV), d.g[s].to(DEV),
+                                d.eta[s].to(DEV), st)
+        o_r, S_r = gdn_decode_step(f(d.q[s]), f(d.k[s]), f(d.v[s]), f(d.g[s]), f(d.eta[s]), S_r)
+        assert rel_err(f(o), o_r) <= TOL[dtype]
+    torch.cuda.synchronize()
+    assert rel_err(f(st), S_r) <= TOL[dtype]
+
+
 # ------------------------------------------- full-size workloads, sampled ----
 
 def _sampled(x, o, S, pairs, dv_cols=None):
@@ -193,6 +262,19 @@ def test_full_prefill_workload_b4_h16_t4096():
     x = inputs.prefill_config(1)
     o, S = run_prefill(x)
     _sampled(x, o, S, [(0, 0), (3, 15), (1, 7)])
+
+
+def test_full_gdn_prefill_workload_b4_h16_t4096():
+    x = inputs.unit_keys(inputs.prefill_config(1))
+    o, S = run_gdn_prefill(x)
+    worst_o = worst_s = 0.0
+    for b, h in [(0, 0), (3, 15)]:
+        o_r, S_r = gdn_forward(f(x.q[b:b + 1, h:h + 1]), f(x.k[b:b + 1, h:h + 1]), f(x.v[b:b + 1, h:h + 1]),
+                               f(x.g[b:b + 1, h:h + 1]), f(x.eta[b:b + 1, h:h + 1]))
+        worst_o = max(worst_o, rel_err(f(o[b, h]), o_r[0, 0]))
+        worst_s = max(worst_s, rel_err(f(S[b, h]), S_r[0, 0]))
+    print(f"{x.name}: sampled err_o={worst_o:.3e} err_S={worst_s:.3e}")
+    assert worst_o <= 2e-2 and worst_s <= 2e-2, (worst_o, worst_s)
 
 
 def test_full_long_context_workload_t65536_dv256():
