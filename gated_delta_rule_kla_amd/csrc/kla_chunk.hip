@@ -335,7 +335,8 @@ struct ChunkParams {
   float *sfin;
   const int32_t *cu;
   char *ws;
-  int H, T, dv, n_tiles, remap, nseq, nslot;
+  const int *order;  // packed sequences, longest first (in the workspace), or nullptr
+  int H, T, dv, n_tiles, ngroups, nseq, nslot;
   int pslots;  // prep kernel: workspace slots per workgroup (1 .. kPrepSlots)
   int beta_direct;  // 1: `eta` holds beta itself (gated delta rule); eps unused
 };
@@ -849,12 +850,18 @@ __global__ __launch_bounds__(64 * kWaves) void kla_chunk_kernel(ChunkParams p) {
   const int lg = lane >> 4;  // lane group 0..3
 
   // ---- which (sequence, head, column slice) this workgroup owns ----------
-  int L = blockIdx.x;
-  if (p.remap) L = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
-  const int jt = L % p.n_tiles;
-  const int nh = L / p.n_tiles;
-  const int h = nh % p.H;
-  const int n = nh / p.H;
+  // Workgroups are dispatched in blockIdx order and blockIdx % 8 picks the
+  // XCD.  (sequence, head) groups go round-robin over the XCDs with all
+  // column slices of a group on one XCD (they share K, Q and the workspace
+  // through its L2); packed sequences come longest first (order[]), so the
+  // longest chains start first.  The grid is padded to whole rounds of 8.
+  const int xcd = blockIdx.x & 7, i8 = blockIdx.x >> 3;
+  const int gidx = (i8 / p.n_tiles) * 8 + xcd;
+  if (gidx >= p.ngroups) return;  // padding (uniform per workgroup)
+  const int jt = i8 % p.n_tiles;
+  const int h = gidx % p.H;
+  const int n = p.order ? p.order[gidx / p.H] : gidx / p.H;
+  const int nh = n * p.H + h;  // (sequence, head) index of the state arrays
   int b = n, t0 = 0, t1 = p.T, slot0;
   if (p.cu) {
     b = 0;
@@ -1275,9 +1282,38 @@ __global__ __launch_bounds__(64 * kWaves) void kla_chunk_kernel(ChunkParams p) {
 // ---------------------------------------------------------------------------
 // host-side dispatch
 // ---------------------------------------------------------------------------
+// Packed sequences, longest first: order[rank] = n, rank = the number of
+// sequences longer than n (ties by index).  O(N) per thread, so only run for
+// N <= kMaxOrdered; beyond that the scan takes sequences in index order.
+constexpr int kMaxOrdered = 2048;
+
+__global__ __launch_bounds__(256) void kla_seq_order_kernel(const int32_t *cu, int nseq, int T, int *order) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= nseq) return;
+  auto len = [&](int n) {
+    const int a = min(max(cu[n], 0), T);
+    return min(max(cu[n + 1], a), T) - a;
+  };
+  const int lt = len(t);
+  int rank = 0;
+  for (int m = 0; m < nseq; ++m) {
+    const int lm = len(m);
+    rank += (lm > lt || (lm == lt && m < t)) ? 1 : 0;
+  }
+  order[rank] = t;
+}
+
+template <typename E, int C>
+static size_t order_offset_t(const ChunkArgs &a) {
+  const size_t img = (size_t)a.H * slots_per_head(a.cu_seqlens != nullptr, a.B, a.T, a.num_seqs, C) *
+                     TpLayout<E, C>::BYTES;
+  return (img + 255) / 256 * 256;
+}
+
 template <typename E, int C>
 static size_t workspace_bytes_t(const ChunkArgs &a) {
-  return (size_t)a.H * slots_per_head(a.cu_seqlens != nullptr, a.B, a.T, a.num_seqs, C) * TpLayout<E, C>::BYTES;
+  // per-chunk images, then (packed sequences) the longest-first order
+  return order_offset_t<E, C>(a) + (a.cu_seqlens ? ((size_t)a.num_seqs * 4 + 255) / 256 * 256 : 0);
 }
 
 size_t chunk_workspace_bytes(const ChunkArgs &a) {
@@ -1307,9 +1343,18 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t st) {
   p.nseq = a.num_seqs;
   p.beta_direct = a.beta_direct;
   p.nslot = slots_per_head(a.cu_seqlens != nullptr, a.B, a.T, a.num_seqs, C);
-  const long long nblk = (long long)a.num_seqs * a.H * p.n_tiles;
-  p.remap = (nblk % 8 == 0) ? 1 : 0;
-  if (nblk == 0) return hipSuccess;
+  p.ngroups = a.num_seqs * a.H;
+  p.order = nullptr;
+  const long long nblk = ((long long)p.ngroups + 7) / 8 * 8 * p.n_tiles;
+  if (p.ngroups == 0) return hipSuccess;
+  if (a.cu_seqlens && a.num_seqs > 1 && a.num_seqs <= kMaxOrdered && (long long)a.B * a.T > 0) {
+    int *order = reinterpret_cast<int *>(static_cast<char *>(a.workspace) + order_offset_t<E, C>(a));
+    hipLaunchKernelGGL(kla_seq_order_kernel, dim3((unsigned)((a.num_seqs + 255) / 256)), dim3(256), 0, st,
+                       a.cu_seqlens, a.num_seqs, a.T, order);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    p.order = order;
+  }
   if ((long long)a.B * a.T > 0 && p.nslot > 0) {
     // slots per workgroup: the longest run that still gives two workgroups
     // per CU (the pipeline is latency-bound; two resident workgroups overlap)

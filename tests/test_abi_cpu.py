@@ -202,9 +202,11 @@ def test_workspace_bytes():
     assert _ws_bytes(dtype=1, chunk=16, dk=32, dv=16) == 2 * 4 * 7 * (16 * 24 * 4 + 3 * 16 * 4)
     # fp32 chunk 64: 64 x 72 fp32 image + 3 x 64 fp32
     assert _ws_bytes(dtype=1, chunk=64, dk=32, dv=16) == 2 * 4 * 2 * (64 * 72 * 4 + 3 * 64 * 4)
-    # packed sequences: floor(T / C) + N + 1 slots per head
+    # packed sequences: floor(T / C) + N + 1 slots per head (rounded up to 256 bytes), then the
+    # longest-first sequence order (N int32, rounded up to 256 bytes)
     arr = (ctypes.c_int32 * 4)(0, 30, 60, 100)
-    assert _ws_bytes(cu=FAKE, cuh=ctypes.addressof(arr), N=3, B=1) == 4 * (100 // 64 + 3 + 1) * per
+    img = 4 * (100 // 64 + 3 + 1) * per
+    assert _ws_bytes(cu=FAKE, cuh=ctypes.addressof(arr), N=3, B=1) == (img + 255) // 256 * 256 + 256
     # the binding's helper agrees
     assert kla.chunk_workspace_bytes(2, 4, 100, 128, 128) == _ws_bytes()
     # exactly the reported size is accepted by the validation (then FAKE pointers would be used,
