@@ -803,8 +803,6 @@ struct ChunkShape {
   // transposing reads conflict-free
   static constexpr int LDV = ((DVT + PAD) * (int)sizeof(E)) % 64 == 32 ? DVT + PAD : DVT + 2 * PAD;
   static constexpr int KG = Ops<E>::KG;
-  static constexpr int MAXOWN = NB > 1 ? 2 : 1;        // row blocks per P wave
-  static constexpr int LOS = MAXOWN * 16 + PAD;        // rows of O^T staging
   // sizes in bytes
   static constexpr int K_SLOT = C * LDK * (int)sizeof(E);
   static constexpr int V_SLOT = C * LDV * (int)sizeof(E);
@@ -812,22 +810,20 @@ struct ChunkShape {
   static constexpr int SU_S = NCT * (DK / KG) * 64 * 16;   // chunk-start S groups, 16 B per lane
   static constexpr int SU_U = NCT * (C / KG) * 64 * 16;    // U~ groups
   static constexpr int SU_SLOT = SU_S + SU_U;
-  static constexpr int OST = (sizeof(E) == 2 ? DVT * LOS : 0) * (int)sizeof(E);  // per P wave: O^T staging
   // offsets
   static constexpr int OFF_K = 0;
   static constexpr int OFF_V = OFF_K + 2 * K_SLOT;
   static constexpr int OFF_TP = OFF_V + 2 * V_SLOT;
   static constexpr int OFF_SU = OFF_TP + 2 * TP_SLOT;
   static constexpr int OFF_Q = OFF_SU + 2 * SU_SLOT;
-  static constexpr int OFF_OS = OFF_Q + 2 * K_SLOT;
-  static constexpr int BYTES = OFF_OS + 2 * OST;
+  static constexpr int BYTES = OFF_Q + 2 * K_SLOT;
 
   static_assert(C == 16 || C == 64, "chunk");
   static_assert(C % KG == 0 && DK % KG == 0 && DK % Ops<E>::KSTEP == 0, "dk");
-  static_assert(K_SLOT % 16 == 0 && V_SLOT % 16 == 0 && TP_SLOT % 16 == 0 && OST % 16 == 0,
+  static_assert(K_SLOT % 16 == 0 && V_SLOT % 16 == 0 && TP_SLOT % 16 == 0,
                 "lds align");
   static_assert((LDK * (int)sizeof(E)) % 16 == 0 && (LDC * (int)sizeof(E)) % 16 == 0 &&
-                    (LDV * (int)sizeof(E)) % 16 == 0 && (LOS * (int)sizeof(E)) % 8 == 0, "row align");
+                    (LDV * (int)sizeof(E)) % 16 == 0, "row align");
   static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
@@ -837,7 +833,7 @@ __global__ __launch_bounds__(64 * kWaves) void kla_chunk_kernel(ChunkParams p) {
   using TL = TpLayout<E, C>;
   using O = Ops<E>;
   using Grp = typename O::Grp;
-  constexpr int NB = Sh::NB, DVT = Sh::DVT, LDK = Sh::LDK, LDC = Sh::LDC, LDV = Sh::LDV, LOS = Sh::LOS;
+  constexpr int NB = Sh::NB, DVT = Sh::DVT, LDK = Sh::LDK, LDC = Sh::LDC, LDV = Sh::LDV;
   constexpr int KG = O::KG, TPG = KG / 16;
   constexpr int NQG = DK / KG;  // contraction groups over dk
   constexpr int NCG = C / KG;   // contraction groups over the chunk
@@ -1057,8 +1053,7 @@ __global__ __launch_bounds__(64 * kWaves) void kla_chunk_kernel(ChunkParams p) {
       using BL = OwnBlocks<NB, part>;
       constexpr int NOWN = BL::N;
       constexpr int NOW1 = NOWN > 0 ? NOWN : 1;
-      E *sO = reinterpret_cast<E *>(smem + Sh::OFF_OS + part * Sh::OST);
-      f32x4 ao[NCT][NOW1];  // output rows of the pending chunk
+      f32x4 ao[NCT][NOW1];  // output of the pending chunk, as O^T tiles
       Grp pa[NOW1][NCG];    // its P rows as left operands
       __syncthreads();
       for (int i = -1; i <= iend; ++i) {
@@ -1068,6 +1063,8 @@ __global__ __launch_bounds__(64 * kWaves) void kla_chunk_kernel(ChunkParams p) {
           const int nrow = nrow_of(c);
           const size_t tok0 = tok0_of(c);
           const Grp *suU = sSuU(c);
+          // ao holds O^T tiles (lane: one output row, 4 consecutive columns),
+          // so the rows go straight to memory
 #pragma unroll
           for (int ct = 0; ct < NCT; ++ct) {
             Grp ub[NCG];
@@ -1077,66 +1074,17 @@ __global__ __launch_bounds__(64 * kWaves) void kla_chunk_kernel(ChunkParams p) {
             for (int k = 0; k < NOWN; ++k) {
               const int rt = BL::at(k);
 #pragma unroll
-              for (int q = 0; q * KG < 16 * (rt + 1); ++q) ao[ct][k] = O::mma_grp(pa[k][q], ub[q], ao[ct][k]);
+              for (int q = 0; q * KG < 16 * (rt + 1); ++q) ao[ct][k] = O::mma_grp(ub[q], pa[k][q], ao[ct][k]);
             }
           }
-          if constexpr (sizeof(E) == 2) {
-            // stage O^T (4 rows of one column = one 8-byte write per lane), read
-            // it back transposed (4 columns of one row) and store 8 bytes
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct)
+          for (int k = 0; k < NOWN; ++k) {
+            const int r = 16 * BL::at(k) + li;
+            if (r < nrow) {
+              E *orow = go + (tok0 + r) * (size_t)dv + jt * DVT + 4 * lg;
 #pragma unroll
-              for (int k = 0; k < NOWN; ++k) {
-                bf16x4 ob;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) ob[j] = (bf16)ao[ct][k][j];
-                *reinterpret_cast<bf16x4 *>(sO + (16 * ct + li) * LOS + 16 * k + 4 * lg) = ob;
-              }
-            const int x = (lane >> 2) & 3, a = lane & 3;
-            if constexpr (DVT % 32 == 0) {
-              // lane (row li, piece lg): columns 8 lg .. 8 lg + 7 of the
-              // slice as two transposing reads, one 16-byte store
-#pragma unroll
-              for (int k = 0; k < NOWN; ++k) {
-#pragma unroll
-                for (int m0 = 0; m0 < DVT / 8; m0 += 4) {
-                  const int m = m0 + lg;
-                  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                      (lds_bf16x4 *)(sO + (8 * m + x) * LOS + 16 * k + 4 * a));
-                  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                      (lds_bf16x4 *)(sO + (8 * m + 4 + x) * LOS + 16 * k + 4 * a));
-                  const int r = 16 * BL::at(k) + li;
-                  if (r < nrow)
-                    *reinterpret_cast<bf16x8 *>(go + (tok0 + r) * (size_t)dv + jt * DVT + 8 * m) =
-                        bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                }
-              }
-            } else {
-#pragma unroll
-              for (int ct = 0; ct < NCT; ++ct) {
-                bf16x4 rows[NOW1];
-#pragma unroll
-                for (int k = 0; k < NOWN; ++k)
-                  rows[k] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                      (lds_bf16x4 *)(sO + (16 * ct + 4 * lg + x) * LOS + 16 * k + 4 * a));
-#pragma unroll
-                for (int k = 0; k < NOWN; ++k) {
-                  const int r = 16 * BL::at(k) + li;
-                  if (r < nrow)
-                    *reinterpret_cast<bf16x4 *>(go + (tok0 + r) * (size_t)dv + jt * DVT + 16 * ct + 4 * lg) = rows[k];
-                }
-              }
+              for (int ct = 0; ct < NCT; ++ct) store4(orow + 16 * ct, ao[ct][k]);
             }
-          } else {
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-              for (int k = 0; k < NOWN; ++k)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                  const int r = 16 * BL::at(k) + 4 * lg + j;
-                  if (r < nrow) go[(tok0 + r) * (size_t)dv + jt * DVT + 16 * ct + li] = Elem<E>::from_f32(ao[ct][k][j]);
-                }
           }
         }
         if (NOWN > 0 && i >= 0 && i < nch) {
@@ -1198,12 +1146,13 @@ __global__ __launch_bounds__(64 * kWaves) void kla_chunk_kernel(ChunkParams p) {
             for (int k = 0; k < NOWN; ++k) {
               ao[ct][k] = zero4();
 #pragma unroll
-              for (int q = 0; q < NQG; ++q) ao[ct][k] = O::mma_grp(qa[k][q], sbq[q], ao[ct][k]);
+              for (int q = 0; q < NQG; ++q) ao[ct][k] = O::mma_grp(sbq[q], qa[k][q], ao[ct][k]);
             }
           }
+          // Diag(Gam): lane li holds row 16 rt + li
 #pragma unroll
           for (int k = 0; k < NOWN; ++k) {
-            const f32x4 gm = *reinterpret_cast<const f32x4 *>(vec + C + 16 * BL::at(k) + 4 * lg);
+            const float gm = vec[C + 16 * BL::at(k) + li];
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) ao[ct][k] = gm * ao[ct][k];
           }
