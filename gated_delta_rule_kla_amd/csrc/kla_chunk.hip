@@ -306,17 +306,32 @@ struct LdsPad {
   static constexpr int V = 32 / (int)sizeof(E);
 };
 
-// Layout of the per-chunk data the prep kernel hands to the scan kernel: the
-// T'^T image (zero blocks and pads included), then the row vectors gamma,
-// Gam, d (fp32).
+// The per-chunk data the prep kernel hands to the scan kernel.  In LDS: the
+// T'^T image (C rows of LDC, grouped columns, zero blocks and pads included),
+// then the row vectors gamma, Gam, d (fp32).  In the workspace the image is
+// packed: rows s < RW keep all C columns, rows s >= RW only the last C - RW
+// (T' U-products never read rows >= 32 at columns < 32: those are zero
+// blocks of the upper block triangle of T'^T), then the three vectors.
 template <typename E, int C>
 struct TpLayout {
   static constexpr int PAD = LdsPad<E>::V;
   static constexpr int LDC = C + PAD;                      // T'^T rows (grouped columns)
-  static constexpr int TP_IMG = C * LDC * (int)sizeof(E);
+  static constexpr int TP_IMG = C * LDC * (int)sizeof(E);  // LDS image
   static constexpr int VEC3 = 3 * C * 4;
-  static constexpr int BYTES = TP_IMG + VEC3;              // workspace bytes per (chunk, head)
-  static_assert(TP_IMG % 16 == 0 && VEC3 % 16 == 0, "align");
+  static constexpr int LDS_BYTES = TP_IMG + VEC3;          // one LDS slot
+  static constexpr int RW = C > 32 ? 32 : C;
+  static constexpr int PACK = (RW * C + (C - RW) * (C - RW)) * (int)sizeof(E);
+  static constexpr int BYTES = PACK + VEC3;                // workspace bytes per (chunk, head)
+  static constexpr int EPP = 16 / (int)sizeof(E);          // elements per 16-byte piece
+  // LDS element offset (in the image) of packed 16-byte piece pc < PACK / 16
+  static __device__ __forceinline__ int piece_to_lds(int pc) {
+    int e = pc * EPP;
+    if (e < RW * C) return (e / C) * LDC + e % C;
+    e -= RW * C;
+    return (RW + e / (C - RW)) * LDC + RW + e % (C - RW);
+  }
+  static_assert(TP_IMG % 16 == 0 && VEC3 % 16 == 0 && PACK % 16 == 0, "align");
+  static_assert((C - RW) % EPP == 0 && C % EPP == 0, "pieces stay inside a row");
 };
 
 // Workspace slot of chunk c of sequence n: dense batches use n * ceil(T/C) + c;
@@ -394,20 +409,28 @@ struct RowLoad {
   }
 };
 
-// NP 16-byte pieces copied from global memory (consecutive lanes, consecutive
-// pieces) into LDS, one step ahead.
-template <int NP>
-struct PieceCopy {
+// A chunk's packed T'^T image and gamma, Gam, d from the workspace into the
+// LDS slot (image rows at their LDS positions, the vectors after the image).
+template <typename E, int C>
+struct ImgCopy {
+  using TL = TpLayout<E, C>;
+  static constexpr int NI = TL::PACK / 16, NP = TL::BYTES / 16;
   static constexpr int NPL = (NP + 63) / 64;
   u32x4 r[NPL];
   __device__ __forceinline__ void issue(const void *src, int lane) {
 #pragma unroll
     for (int j = 0; j < NPL; ++j) r[j] = reinterpret_cast<const u32x4 *>(src)[min(lane + 64 * j, NP - 1)];
   }
-  __device__ __forceinline__ void put(void *dst, int lane) const {
+  __device__ __forceinline__ void put(E *slot, int lane) const {
 #pragma unroll
-    for (int j = 0; j < NPL; ++j)
-      if (NP % 64 == 0 || lane + 64 * j < NP) reinterpret_cast<u32x4 *>(dst)[lane + 64 * j] = r[j];
+    for (int j = 0; j < NPL; ++j) {
+      const int i = lane + 64 * j;
+      if (NP % 64 == 0 || i < NP) {
+        char *d = i < NI ? reinterpret_cast<char *>(slot + TL::piece_to_lds(i))
+                         : reinterpret_cast<char *>(slot) + TL::TP_IMG + 16 * (i - NI);
+        *reinterpret_cast<u32x4 *>(d) = r[j];
+      }
+    }
   }
 };
 
@@ -755,17 +778,16 @@ __global__ __launch_bounds__(64 * kPrepWaves) void kla_chunk_prep_kernel(ChunkPa
             }
           }
         }
-        // the T'^T image and gamma, Gam, d to the workspace (16-byte pieces;
-        // all LDS reads first, then the stores)
-        constexpr int NI = TL::TP_IMG / 16, NP = NI + TL::VEC3 / 16, NPL = (NP + 63) / 64;
+        // the packed T'^T image and gamma, Gam, d to the workspace (16-byte
+        // pieces; all LDS reads first, then the stores)
+        constexpr int NI = TL::PACK / 16, NP = NI + TL::VEC3 / 16, NPL = (NP + 63) / 64;
         u32x4 *dst = reinterpret_cast<u32x4 *>(ws_of(sp));
-        const u32x4 *im = reinterpret_cast<const u32x4 *>(img);
         const u32x4 *vs = reinterpret_cast<const u32x4 *>(bv);
         u32x4 pc[NPL];
 #pragma unroll
         for (int j = 0; j < NPL; ++j) {
           const int i = min(lane + 64 * j, NP - 1);
-          pc[j] = i < NI ? im[i] : vs[i - NI];
+          pc[j] = i < NI ? *reinterpret_cast<const u32x4 *>(img + TL::piece_to_lds(i)) : vs[i - NI];
         }
 #pragma unroll
         for (int j = 0; j < NPL; ++j)
@@ -806,7 +828,7 @@ struct ChunkShape {
   // sizes in bytes
   static constexpr int K_SLOT = C * LDK * (int)sizeof(E);
   static constexpr int V_SLOT = C * LDV * (int)sizeof(E);
-  static constexpr int TP_SLOT = TpLayout<E, C>::BYTES;    // T'^T image, then gamma, Gam, d
+  static constexpr int TP_SLOT = TpLayout<E, C>::LDS_BYTES;  // T'^T image, then gamma, Gam, d
   static constexpr int SU_S = NCT * (DK / KG) * 64 * 16;   // chunk-start S groups, 16 B per lane
   static constexpr int SU_U = NCT * (C / KG) * 64 * 16;    // U~ groups
   static constexpr int SU_SLOT = SU_S + SU_U;
@@ -1202,7 +1224,7 @@ __global__ __launch_bounds__(64 * kWaves) void kla_chunk_kernel(ChunkParams p) {
   } else {
     // =================== T'^T, gamma/Gam/d and the V slice of chunk i+1 ========
     // (two sets, two steps ahead, as for K, when the registers allow)
-    using TC = PieceCopy<TL::BYTES / 16>;
+    using TC = ImgCopy<E, C>;
     constexpr int NSET = TC::NPL <= 20 ? 2 : 1;
     TC tin[NSET];
     VSliceLoad<E, C, DVT> vin[NSET];

@@ -124,7 +124,7 @@ kla_status_t kla_chunk_fwd(const void *q, const void *k, const void *v,
 
 /*
  * kla_chunk_workspace_bytes -- device workspace kla_chunk_fwd needs for these
- * arguments (the same meaning as there; host-only, no HIP call).  11,008
+ * arguments (the same meaning as there; host-only, no HIP call).  6,912
  * bytes per (64-token chunk, head) in bf16.  kla_gdn_chunk_fwd needs the same.  Returns 0 when no workspace is
  * needed (no tokens) and also for arguments kla_chunk_fwd would reject.
  */

@@ -190,18 +190,18 @@ def test_binding_refuses_cpu_tensors():
 
 
 def test_workspace_bytes():
-    # bf16, chunk 64, per (chunk, head): one 64 x 80 bf16 T'^T image (rows padded by 32 bytes)
-    # and gamma, Gam, d (3 x 64 fp32)
-    per = 64 * 80 * 2 + 3 * 64 * 4
+    # bf16, chunk 64, per (chunk, head): the T'^T image packed to the part the scan reads (rows
+    # 0..31 all 64 columns, rows 32..63 the last 32) and gamma, Gam, d (3 x 64 fp32)
+    per = (32 * 64 + 32 * 32) * 2 + 3 * 64 * 4
     assert _ws_bytes() == 2 * 4 * 2 * per                  # B=2 rows x ceil(100/64)=2 chunks x H=4
     assert _ws_bytes(T=128) == 2 * 4 * 2 * per
     assert _ws_bytes(T=129) == 2 * 4 * 3 * per
     assert _ws_bytes(T=0) == 0 and _ws_bytes(N=0, B=0) == 0
     assert _ws_bytes(dk=96) == 0                           # unsupported -> 0
-    # fp32 chunk 16: 16 x 24 fp32 image + 3 x 16 fp32
-    assert _ws_bytes(dtype=1, chunk=16, dk=32, dv=16) == 2 * 4 * 7 * (16 * 24 * 4 + 3 * 16 * 4)
-    # fp32 chunk 64: 64 x 72 fp32 image + 3 x 64 fp32
-    assert _ws_bytes(dtype=1, chunk=64, dk=32, dv=16) == 2 * 4 * 2 * (64 * 72 * 4 + 3 * 64 * 4)
+    # fp32 chunk 16: 16 x 16 fp32 image + 3 x 16 fp32
+    assert _ws_bytes(dtype=1, chunk=16, dk=32, dv=16) == 2 * 4 * 7 * (16 * 16 * 4 + 3 * 16 * 4)
+    # fp32 chunk 64: packed 64-column image (32 x 64 + 32 x 32 fp32) + 3 x 64 fp32
+    assert _ws_bytes(dtype=1, chunk=64, dk=32, dv=16) == 2 * 4 * 2 * ((32 * 64 + 32 * 32) * 4 + 3 * 64 * 4)
     # packed sequences: floor(T / C) + N + 1 slots per head (rounded up to 256 bytes), then the
     # longest-first sequence order (N int32, rounded up to 256 bytes)
     arr = (ctypes.c_int32 * 4)(0, 30, 60, 100)
