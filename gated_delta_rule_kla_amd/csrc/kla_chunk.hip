@@ -326,9 +326,13 @@ struct TpLayout {
   // LDS element offset (in the image) of packed 16-byte piece pc < PACK / 16
   static __device__ __forceinline__ int piece_to_lds(int pc) {
     int e = pc * EPP;
-    if (e < RW * C) return (e / C) * LDC + e % C;
-    e -= RW * C;
-    return (RW + e / (C - RW)) * LDC + RW + e % (C - RW);
+    if constexpr (C > RW) {
+      if (e >= RW * C) {
+        e -= RW * C;
+        return (RW + e / (C - RW)) * LDC + RW + e % (C - RW);
+      }
+    }
+    return (e / C) * LDC + e % C;
   }
   static_assert(TP_IMG % 16 == 0 && VEC3 % 16 == 0 && PACK % 16 == 0, "align");
   static_assert((C - RW) % EPP == 0 && C % EPP == 0, "pieces stay inside a row");
