@@ -128,6 +128,17 @@ def test_prefill_varlen_with_empty_and_tiny_sequences():
     check_prefill(x)
 
 
+@pytest.mark.parametrize("nseq", [2048, 2100])
+def test_prefill_varlen_many_short_sequences(nseq):
+    """Up to 2048 packed sequences are scheduled longest first (a ranking kernel
+    writes the order into the workspace); beyond that in index order."""
+    rng = np.random.default_rng(nseq)
+    lengths = [int(x) for x in rng.choice([0, 1, 2, 3, 17, 64, 65], size=nseq)]
+    x = inputs.make_prefill(H=1, dk=128, dv=32, chunk=64, s0_std=0.02, lengths=lengths, seed=nseq,
+                            name=f"varlen-{nseq}")
+    check_prefill(x)
+
+
 def test_prefill_no_initial_state_and_no_tokens():
     x = inputs.make_prefill(H=2, dk=128, dv=64, chunk=64, lengths=[0, 0], seed=13, name="empty")
     o, S = run_prefill(x)
