@@ -24,13 +24,13 @@
 namespace kla {
 
 constexpr int decode_threads(int dk, int dv) {
-  return dk * dv / 64 < 64 ? 64 : (dk * dv / 64 > 1024 ? 1024 : dk * dv / 64);
+  return dk * dv / 32 < 64 ? 64 : (dk * dv / 32 > 1024 ? 1024 : dk * dv / 32);
 }
 
 template <int DK, int DV>
 struct DecodeShape {
   static constexpr int TPR = DV / 4;                        // threads per row
-  static constexpr int NT = decode_threads(DK, DV);         // ~64 state floats per thread
+  static constexpr int NT = decode_threads(DK, DV);         // ~32 state floats per thread
   static constexpr int RG = NT / TPR;                       // row groups
   static constexpr int RPT = DK / RG;                       // rows per thread
   static constexpr int NW = NT / 64;                        // waves
