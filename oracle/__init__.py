@@ -8,6 +8,7 @@ with the HIP kernels or their binding.
 from .kla_oracle import (gdn_decode_step, gdn_forward, gdn_recurrence, kla_decode_step, kla_forward,
                          kla_recurrence)
 from .kla_chunk_oracle import kla_chunkwise
+from .kla_backward_oracle import gdn_backward, kla_backward
 
 __all__ = ["kla_recurrence", "kla_forward", "kla_decode_step", "kla_chunkwise", "gdn_recurrence",
-           "gdn_forward", "gdn_decode_step"]
+           "gdn_forward", "gdn_decode_step", "kla_backward", "gdn_backward"]
