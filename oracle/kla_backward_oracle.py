@@ -72,7 +72,9 @@ def _heads_backward(q, k, v, g, coef, eps, S0, dO, dST, beta_given):
     gq, gk, gv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
     gg, gcoef = np.zeros((H, L)), np.zeros((H, L))
     dS = dST.copy()
-    for c0 in range(((L - 1) // _CKPT) * _CKPT if L else 0, -1, -_CKPT):
+    if L == 0:  # an empty sequence passes its state (and the state's gradient) through
+        return gq, gk, gv, gg, gcoef, dS
+    for c0 in range(((L - 1) // _CKPT) * _CKPT, -1, -_CKPT):
         c1 = min(c0 + _CKPT, L)
         states = [ckpt[c0]]                      # S_{c0-1+1} .. S_{c1}: states[j] = state before token c0+j
         for t in range(c0, c1):

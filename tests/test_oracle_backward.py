@@ -90,10 +90,11 @@ def test_fd_kla_batch_no_states():
 
 
 def test_fd_kla_packed_sequences():
+    """Packed sequences, one of them empty (its state and gradient pass through)."""
     q, k, v, g, eta, do, rng = _case(13, 1, 1, 17, 3, 3)
-    cu = [0, 5, 6, 17]
-    S0 = rng.standard_normal((3, 1, 3, 3))
-    dS_T = rng.standard_normal((3, 1, 3, 3))
+    cu = [0, 5, 5, 6, 17]
+    S0 = rng.standard_normal((4, 1, 3, 3))
+    dS_T = rng.standard_normal((4, 1, 3, 3))
     _fd_check(kla_forward, kbo.kla_backward, q, k, v, g, eta, 1e-6, do, dS_T, S0, cu)
 
 
