@@ -94,6 +94,33 @@ kla_status_t chunk_fwd_impl(const void *q, const void *k, const void *v, const v
   return from_hip(kla::launch_chunk_fwd(a, reinterpret_cast<hipStream_t>(stream)));
 }
 
+kla_status_t chunk_bwd_impl(const void *q, const void *k, const void *v, const void *g, const void *eta,
+                            float eps, int beta_direct, const float *initial_state, const void *dout,
+                            const float *dfinal_state, void *dq, void *dk, void *dv, float *dg, float *deta,
+                            float *dinitial_state, const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
+                            int num_seqs, int B, int H, int T, int dkk, int dvv, int chunk, void *workspace,
+                            size_t workspace_bytes, kla_dtype_t dtype, void *stream) {
+  const kla_status_t st =
+      check_chunk_shapes(eps, cu_seqlens, cu_seqlens_host, num_seqs, B, H, T, dkk, dvv, chunk, dtype);
+  if (st != KLA_OK) return st;
+  if (!kla::chunk_bwd_supported(dtype, dkk, dvv, chunk)) return KLA_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return KLA_OK;
+  if ((long long)B * T > 0 &&
+      (!q || !k || !v || !g || !eta || !dout || !dq || !dk || !dv || !dg || !deta))
+    return KLA_ERR_NULL;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(g) || misaligned(eta) ||
+      misaligned(initial_state) || misaligned(dout) || misaligned(dfinal_state) || misaligned(dq) ||
+      misaligned(dk) || misaligned(dv) || misaligned(dg) || misaligned(deta) || misaligned(dinitial_state) ||
+      misaligned(workspace))
+    return KLA_ERR_ALIGN;
+  const kla::ChunkArgs a = chunk_args(q, k, v, g, eta, eps, initial_state, nullptr, nullptr, cu_seqlens,
+                                      num_seqs, B, H, T, dkk, dvv, chunk, dtype, workspace, beta_direct);
+  const size_t need = (long long)B * T > 0 ? kla::chunk_bwd_workspace_bytes(a) : 0;
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return KLA_ERR_WORKSPACE;
+  const kla::ChunkBwdArgs b{dout, dfinal_state, dq, dk, dv, dg, deta, dinitial_state};
+  return from_hip(kla::launch_chunk_bwd(a, b, reinterpret_cast<hipStream_t>(stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -143,6 +170,39 @@ kla_status_t kla_gdn_chunk_fwd(const void *q, const void *k, const void *v, cons
                                size_t workspace_bytes, kla_dtype_t dtype, void *stream) {
   return chunk_fwd_impl(q, k, v, g, beta, 0.f, 1, initial_state, o, final_state, cu_seqlens, cu_seqlens_host,
                         num_seqs, B, H, T, dk, dv, chunk, workspace, workspace_bytes, dtype, stream);
+}
+
+size_t kla_chunk_bwd_workspace_bytes(const int32_t *cu_seqlens, const int32_t *cu_seqlens_host, int num_seqs,
+                                     int B, int H, int T, int dk, int dv, int chunk, kla_dtype_t dtype) {
+  if (check_chunk_shapes(0.f, cu_seqlens, cu_seqlens_host, num_seqs, B, H, T, dk, dv, chunk, dtype) != KLA_OK)
+    return 0;
+  if (!kla::chunk_bwd_supported(dtype, dk, dv, chunk)) return 0;
+  if (num_seqs == 0 || (long long)B * T == 0) return 0;
+  return kla::chunk_bwd_workspace_bytes(chunk_args(nullptr, nullptr, nullptr, nullptr, nullptr, 0.f, nullptr,
+                                                   nullptr, nullptr, cu_seqlens, num_seqs, B, H, T, dk, dv,
+                                                   chunk, dtype, nullptr, 0));
+}
+
+kla_status_t kla_chunk_bwd(const void *q, const void *k, const void *v, const void *g, const void *eta,
+                           float eps, const float *initial_state, const void *dout, const float *dfinal_state,
+                           void *dq, void *dk_, void *dv_, float *dg, float *deta, float *dinitial_state,
+                           const int32_t *cu_seqlens, const int32_t *cu_seqlens_host, int num_seqs, int B,
+                           int H, int T, int dk, int dv, int chunk, void *workspace, size_t workspace_bytes,
+                           kla_dtype_t dtype, void *stream) {
+  return chunk_bwd_impl(q, k, v, g, eta, eps, 0, initial_state, dout, dfinal_state, dq, dk_, dv_, dg, deta,
+                        dinitial_state, cu_seqlens, cu_seqlens_host, num_seqs, B, H, T, dk, dv, chunk, workspace,
+                        workspace_bytes, dtype, stream);
+}
+
+kla_status_t kla_gdn_chunk_bwd(const void *q, const void *k, const void *v, const void *g, const void *beta,
+                               const float *initial_state, const void *dout, const float *dfinal_state, void *dq,
+                               void *dk_, void *dv_, float *dg, float *dbeta, float *dinitial_state,
+                               const int32_t *cu_seqlens, const int32_t *cu_seqlens_host, int num_seqs, int B,
+                               int H, int T, int dk, int dv, int chunk, void *workspace, size_t workspace_bytes,
+                               kla_dtype_t dtype, void *stream) {
+  return chunk_bwd_impl(q, k, v, g, beta, 0.f, 1, initial_state, dout, dfinal_state, dq, dk_, dv_, dg, dbeta,
+                        dinitial_state, cu_seqlens, cu_seqlens_host, num_seqs, B, H, T, dk, dv, chunk, workspace,
+                        workspace_bytes, dtype, stream);
 }
 
 kla_status_t kla_decode_step(const void *q, const void *k, const void *v, const void *g,

@@ -1,0 +1,863 @@
+// kla_bwd.hip -- gradients of the chunkwise KLA forward for gfx950.
+//
+// "Resumen Técnico: Atención Lineal Kaczmarz (KLA)" (gist.science/es/paper/2605.08587),
+// §"Implementación": KLA keeps Gated DeltaNet's parallel chunk training algorithm and
+// changes only the diagonal coefficient matrix Diag(beta) inside it.  This file is the
+// reverse mode of that chunk algorithm.  Per chunk of C tokens with start state S
+// (gamma = running sum of g in the chunk, Gam = exp(gamma), d_r = exp(gamma_C - gamma_r),
+// E_rs = exp(gamma_r - gamma_s)):
+//
+//   forward                                   reverse (dS' = dL/d(chunk-end state))
+//   A  = strictly-lower(Diag(b) K K^T . E)     dU  = P^T dO + Diag(d) K dS'
+//   T  = (I + A)^-1,  W = T Diag(b)            dX  = W^T dU  (= dV)
+//   P  = lower(Q K^T . E)                      dP  = dO U^T,   dW = dU X^T
+//   X  = V - Diag(Gam) K S,   U = W X          dS  = Gam_C dS' + (Diag(Gam) Q)^T dO - (Diag(Gam) K)^T dX
+//   O  = Diag(Gam) Q S + P U                   dA  = -T^T (dW Diag(b)) T^T   (strictly lower)
+//   S' = Gam_C S + K^T Diag(d) U               then dQ, dK, db, dgamma from A, P, X, O, S'
+//
+// Four kernels, through a caller-provided workspace:
+//   prep     (chunk, head) in parallel: b, gamma, ||k||^2, T and P into the workspace.
+//   states   (sequence, head, 16 state columns): the chunk-start states, in order.
+//   dstates  (sequence, head, 16 state columns): dS' of every chunk, in reverse order;
+//            the gradient of the initial state is what is left at the start.
+//   grads    (chunk, head) in parallel: everything else from S, dS' and the chunk's
+//            inputs, streaming the state columns 16 at a time.
+// All arithmetic is fp32 FMA through padded LDS rows (odd row strides keep the
+// transposed reads free of bank conflicts); there are no atomics, so results are
+// deterministic run to run.
+#include <algorithm>
+
+#include "kla_common.h"
+#include "kla_internal.h"
+
+namespace kla {
+
+namespace {
+
+constexpr int kBT = 256;  // threads per workgroup in every backward kernel
+constexpr int kNS = 16;   // state columns per slice
+constexpr int kLS = kNS + 1;
+
+struct BwdParams {
+  const void *q, *k, *v, *g, *eta, *dout;
+  float eps;
+  const float *s0, *dsfin;
+  void *dq, *dk, *dv;
+  float *dg, *deta, *ds0;
+  const int32_t *cu;
+  float *prep, *states, *dstates;
+  int B, H, T, DV, nseq, nslot, nsl;
+  int beta_direct;
+};
+
+// Per (head, slot) record of the prep kernel, in floats.
+template <int C> struct PrepRec {
+  static constexpr int TM = 0;            // T = (I + A)^-1, C x C row-major
+  static constexpr int PM = C * C;        // P = lower(Q K^T . E), C x C row-major
+  static constexpr int BETA = 2 * C * C;  // b_r
+  static constexpr int GAM = BETA + C;    // gamma_r (rows past the chunk's end hold the last value)
+  static constexpr int NRM = GAM + C;     // ||k_r||^2
+  static constexpr int FLOATS = NRM + 2 * C;
+};
+
+__device__ __forceinline__ int clampi(int x, int lo, int hi) { return min(max(x, lo), hi); }
+
+// Slot of chunk c of sequence n (as the forward workspace): dense batches use
+// n * ceil(T/C) + c, packed sequences n + floor(t0_n / C) + c.
+struct SeqLoc {
+  long long row0;  // token row of the sequence's first token in [B*H*T]
+  int len, slot0;
+};
+
+__device__ __forceinline__ SeqLoc seq_loc(const BwdParams &p, int n, int h, int C) {
+  if (p.cu) {
+    const int t0 = clampi(p.cu[n], 0, p.T);
+    const int t1 = clampi(p.cu[n + 1], t0, p.T);
+    return {(long long)h * p.T + t0, t1 - t0, n + t0 / C};
+  }
+  const int nchT = (p.T + C - 1) / C;
+  return {((long long)n * p.H + h) * p.T, p.T, n * nchT};
+}
+
+struct ChunkLoc {
+  long long row0;  // token row of the chunk's first token
+  int rows;        // tokens in the chunk, 0 if the slot holds no chunk
+};
+
+__device__ __forceinline__ ChunkLoc chunk_loc(const BwdParams &p, int slot, int h, int C) {
+  int b = 0, t0 = 0, len = p.T, c = slot;
+  if (p.cu) {
+    // the sequence n with n + floor(cu[n] / C) <= slot (strictly increasing in n)
+    int lo = 0, hi = p.nseq - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (mid + clampi(p.cu[mid], 0, p.T) / C <= slot) lo = mid; else hi = mid - 1;
+    }
+    t0 = clampi(p.cu[lo], 0, p.T);
+    len = clampi(p.cu[lo + 1], t0, p.T) - t0;
+    c = slot - (lo + t0 / C);
+  } else {
+    const int nchT = (p.T + C - 1) / C;
+    b = slot / nchT;
+    c = slot % nchT;
+  }
+  const bool ok = c >= 0 && c * C < len;
+  return {((long long)b * p.H + h) * p.T + t0 + (long long)c * C, ok ? min(C, len - c * C) : 0};
+}
+
+template <typename E>
+__device__ __forceinline__ float ld(const void *base, long long i) {
+  return Elem<E>::to_f32(static_cast<const E *>(base)[i]);
+}
+
+// Rows [0, rows) of a [*, D] token tensor from token row `row0` into LDS with row
+// stride LD, zeros past `rows`.
+template <typename E, int R, int D, int LD>
+__device__ __forceinline__ void load_rows(float *dst, const void *src, long long row0, int rows, int col0,
+                                          int ld_src) {
+  for (int e = threadIdx.x; e < R * D; e += kBT) {
+    const int r = e / D, i = e % D;
+    dst[r * LD + i] = r < rows ? ld<E>(src, (row0 + r) * ld_src + col0 + i) : 0.f;
+  }
+}
+
+// ============================================================================
+// prep: b, gamma, ||k||^2, T = (I + A)^-1 and P for one (chunk, head)
+// ============================================================================
+template <typename E, int C, int DK>
+struct PrepSmem {
+  static constexpr int LK = DK + 1, LC = C + 1;
+  static constexpr int K = 0, Q = K + C * LK, A = Q + C * LK, T = A + C * LC, G = T + C * LC;
+  static constexpr int BETA = G + C, GAM = BETA + C, NRM = GAM + C, FLOATS = NRM + C;
+};
+
+template <typename E, int C, int DK>
+__global__ __launch_bounds__(kBT) void kla_bwd_prep_kernel(BwdParams p) {
+  using L = PrepSmem<E, C, DK>;
+  using R = PrepRec<C>;
+  constexpr int LK = L::LK, LC = L::LC;
+  __shared__ float sm[L::FLOATS];
+  float *sK = sm + L::K, *sQ = sm + L::Q, *sA = sm + L::A, *sT = sm + L::T;
+  float *sg = sm + L::G, *sb = sm + L::BETA, *sgam = sm + L::GAM, *snrm = sm + L::NRM;
+  const int slot = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
+  const ChunkLoc cl = chunk_loc(p, slot, h, C);
+  if (cl.rows == 0) return;  // uniform: no chunk behind this slot
+  const int rows = cl.rows;
+
+  load_rows<E, C, DK, LK>(sK, p.k, cl.row0, rows, 0, DK);
+  load_rows<E, C, DK, LK>(sQ, p.q, cl.row0, rows, 0, DK);
+  for (int r = t; r < C; r += kBT) {
+    sg[r] = r < rows ? ld<E>(p.g, cl.row0 + r) : 0.f;
+    sb[r] = r < rows ? ld<E>(p.eta, cl.row0 + r) : 0.f;  // eta (or b) for now
+  }
+  __syncthreads();
+  for (int r = t; r < C; r += kBT) {
+    float n = 0.f;
+    for (int i = 0; i < DK; ++i) n = fmaf(sK[r * LK + i], sK[r * LK + i], n);
+    snrm[r] = n;
+    sb[r] = r >= rows ? 0.f : (p.beta_direct ? sb[r] : sb[r] / (n + p.eps));
+  }
+  if (t == 0) {
+    float a = 0.f;
+    for (int r = 0; r < C; ++r) {
+      a += sg[r];
+      sgam[r] = a;
+    }
+  }
+  __syncthreads();
+  float *rec = p.prep + ((size_t)h * p.nslot + slot) * R::FLOATS;
+  for (int e = t; e < C * C; e += kBT) {
+    const int r = e / C, s = e % C;
+    float a = 0.f, pv = 0.f;
+    if (s <= r) {
+      float gkk = 0.f, gqk = 0.f;
+      for (int i = 0; i < DK; ++i) {
+        gkk = fmaf(sK[r * LK + i], sK[s * LK + i], gkk);
+        gqk = fmaf(sQ[r * LK + i], sK[s * LK + i], gqk);
+      }
+      const float ex = __expf(sgam[r] - sgam[s]);
+      pv = gqk * ex;
+      if (s < r) a = sb[r] * gkk * ex;
+    }
+    sA[r * LC + s] = a;
+    sT[r * LC + s] = r == s ? 1.f : 0.f;
+    rec[R::PM + e] = pv;
+  }
+  __syncthreads();
+  // T[r][j] = -sum_{j <= s < r} A[r][s] T[s][j] below the unit diagonal: one column
+  // per thread, rows in order (forward substitution).
+  if (t < C) {
+    const int j = t;
+    for (int r = j + 1; r < C; ++r) {
+      float acc = 0.f;
+      for (int s = j; s < r; ++s) acc = fmaf(sA[r * LC + s], sT[s * LC + j], acc);
+      sT[r * LC + j] = -acc;
+    }
+  }
+  __syncthreads();
+  for (int e = t; e < C * C; e += kBT) rec[R::TM + e] = sT[(e / C) * LC + e % C];
+  for (int r = t; r < C; r += kBT) {
+    rec[R::BETA + r] = sb[r];
+    rec[R::GAM + r] = sgam[r];
+    rec[R::NRM + r] = snrm[r];
+  }
+}
+
+// ============================================================================
+// states: the chunk-start state of every chunk, 16 state columns per workgroup
+// ============================================================================
+template <int C, int DK>
+struct StatesSmem {
+  static constexpr int LK = DK + 1, LC = C + 1;
+  static constexpr int K = 0, T = K + C * LK, V = T + C * LC, X = V + C * kLS, S = X + C * kLS;
+  static constexpr int BETA = S + DK * kLS, GAM = BETA + C, FLOATS = GAM + C;
+};
+
+template <typename E, int C, int DK>
+__global__ __launch_bounds__(kBT) void kla_bwd_states_kernel(BwdParams p) {
+  using L = StatesSmem<C, DK>;
+  using R = PrepRec<C>;
+  constexpr int LK = L::LK, LC = L::LC;
+  __shared__ float sm[L::FLOATS];
+  float *sK = sm + L::K, *sT = sm + L::T, *sV = sm + L::V, *sX = sm + L::X, *sS = sm + L::S;
+  float *sb = sm + L::BETA, *sgam = sm + L::GAM;
+  const int t = threadIdx.x;
+  const int js = blockIdx.x % p.nsl, gidx = blockIdx.x / p.nsl;
+  const int h = gidx % p.H, n = gidx / p.H;
+  const int col0 = js * kNS;
+  const SeqLoc sq = seq_loc(p, n, h, C);
+  const size_t sbase = ((size_t)n * p.H + h) * DK * p.DV;
+  for (int e = t; e < DK * kNS; e += kBT) {
+    const int i = e / kNS, j = e % kNS;
+    sS[i * kLS + j] = p.s0 ? p.s0[sbase + (size_t)i * p.DV + col0 + j] : 0.f;
+  }
+  const int nch = (sq.len + C - 1) / C;
+  for (int c = 0; c < nch; ++c) {
+    const int rows = min(C, sq.len - c * C);
+    const long long row0 = sq.row0 + (long long)c * C;
+    const size_t slot = (size_t)h * p.nslot + sq.slot0 + c;
+    const float *rec = p.prep + slot * R::FLOATS;
+    __syncthreads();
+    float *st = p.states + slot * DK * p.DV;
+    for (int e = t; e < DK * kNS; e += kBT) {
+      const int i = e / kNS, j = e % kNS;
+      st[(size_t)i * p.DV + col0 + j] = sS[i * kLS + j];
+    }
+    load_rows<E, C, DK, LK>(sK, p.k, row0, rows, 0, DK);
+    load_rows<E, C, kNS, kLS>(sV, p.v, row0, rows, col0, p.DV);
+    for (int e = t; e < C * C; e += kBT) sT[(e / C) * LC + e % C] = rec[R::TM + e];
+    for (int r = t; r < C; r += kBT) {
+      sb[r] = rec[R::BETA + r];
+      sgam[r] = rec[R::GAM + r];
+    }
+    __syncthreads();
+    // X = V - Diag(Gam) K S, kept as Diag(b) X
+    for (int e = t; e < C * kNS; e += kBT) {
+      const int r = e / kNS, j = e % kNS;
+      float acc = 0.f;
+      for (int i = 0; i < DK; ++i) acc = fmaf(sK[r * LK + i], sS[i * kLS + j], acc);
+      sX[r * kLS + j] = sb[r] * (sV[r * kLS + j] - __expf(sgam[r]) * acc);
+    }
+    __syncthreads();
+    // Diag(d) U with U = T Diag(b) X  (into sV)
+    const float gC = sgam[C - 1];
+    for (int e = t; e < C * kNS; e += kBT) {
+      const int r = e / kNS, j = e % kNS;
+      float acc = 0.f;
+      for (int s = 0; s <= r; ++s) acc = fmaf(sT[r * LC + s], sX[s * kLS + j], acc);
+      sV[r * kLS + j] = __expf(gC - sgam[r]) * acc;
+    }
+    __syncthreads();
+    // S <- Gam_C S + K^T Diag(d) U
+    const float GC = __expf(gC);
+    for (int e = t; e < DK * kNS; e += kBT) {
+      const int i = e / kNS, j = e % kNS;
+      float acc = 0.f;
+      for (int r = 0; r < C; ++r) acc = fmaf(sK[r * LK + i], sV[r * kLS + j], acc);
+      sS[i * kLS + j] = fmaf(GC, sS[i * kLS + j], acc);
+    }
+  }
+}
+
+// ============================================================================
+// dstates: dS' of every chunk (reverse order) and the initial-state gradient
+// ============================================================================
+template <int C, int DK>
+struct DStatesSmem {
+  static constexpr int LK = DK + 1, LC = C + 1;
+  static constexpr int K = 0, Q = K + C * LK, T = Q + C * LK, P = T + C * LC, O = P + C * LC;
+  static constexpr int U = O + C * kLS, S = U + C * kLS, BETA = S + DK * kLS, GAM = BETA + C;
+  static constexpr int FLOATS = GAM + C;
+};
+
+template <typename E, int C, int DK>
+__global__ __launch_bounds__(kBT) void kla_bwd_dstates_kernel(BwdParams p) {
+  using L = DStatesSmem<C, DK>;
+  using R = PrepRec<C>;
+  constexpr int LK = L::LK, LC = L::LC;
+  constexpr int PER = C * kNS / kBT > 0 ? (C * kNS + kBT - 1) / kBT : 1;
+  __shared__ float sm[L::FLOATS];
+  float *sK = sm + L::K, *sQ = sm + L::Q, *sT = sm + L::T, *sP = sm + L::P, *sO = sm + L::O;
+  float *sU = sm + L::U, *sS = sm + L::S, *sb = sm + L::BETA, *sgam = sm + L::GAM;
+  const int t = threadIdx.x;
+  const int js = blockIdx.x % p.nsl, gidx = blockIdx.x / p.nsl;
+  const int h = gidx % p.H, n = gidx / p.H;
+  const int col0 = js * kNS;
+  const SeqLoc sq = seq_loc(p, n, h, C);
+  const size_t sbase = ((size_t)n * p.H + h) * DK * p.DV;
+  for (int e = t; e < DK * kNS; e += kBT) {
+    const int i = e / kNS, j = e % kNS;
+    sS[i * kLS + j] = p.dsfin ? p.dsfin[sbase + (size_t)i * p.DV + col0 + j] : 0.f;
+  }
+  const int nch = (sq.len + C - 1) / C;
+  for (int c = nch - 1; c >= 0; --c) {
+    const int rows = min(C, sq.len - c * C);
+    const long long row0 = sq.row0 + (long long)c * C;
+    const size_t slot = (size_t)h * p.nslot + sq.slot0 + c;
+    const float *rec = p.prep + slot * R::FLOATS;
+    __syncthreads();
+    float *dst = p.dstates + slot * DK * p.DV;
+    for (int e = t; e < DK * kNS; e += kBT) {
+      const int i = e / kNS, j = e % kNS;
+      dst[(size_t)i * p.DV + col0 + j] = sS[i * kLS + j];
+    }
+    load_rows<E, C, DK, LK>(sK, p.k, row0, rows, 0, DK);
+    load_rows<E, C, DK, LK>(sQ, p.q, row0, rows, 0, DK);
+    load_rows<E, C, kNS, kLS>(sO, p.dout, row0, rows, col0, p.DV);
+    for (int e = t; e < C * C; e += kBT) {
+      sT[(e / C) * LC + e % C] = rec[R::TM + e];
+      sP[(e / C) * LC + e % C] = rec[R::PM + e];
+    }
+    for (int r = t; r < C; r += kBT) {
+      sb[r] = rec[R::BETA + r];
+      sgam[r] = rec[R::GAM + r];
+    }
+    __syncthreads();
+    const float gC = sgam[C - 1];
+    // dU = P^T dO + Diag(d) K dS'
+    for (int e = t; e < C * kNS; e += kBT) {
+      const int r = e / kNS, j = e % kNS;
+      float a = 0.f, b = 0.f;
+      for (int s = r; s < C; ++s) a = fmaf(sP[s * LC + r], sO[s * kLS + j], a);
+      for (int i = 0; i < DK; ++i) b = fmaf(sK[r * LK + i], sS[i * kLS + j], b);
+      sU[r * kLS + j] = fmaf(__expf(gC - sgam[r]), b, a);
+    }
+    __syncthreads();
+    // dX = Diag(b) T^T dU; keep Diag(Gam) dX and Diag(Gam) dO for the state step
+    float gdx[PER], gdo[PER];
+#pragma unroll
+    for (int m = 0; m < PER; ++m) {
+      const int e = t + m * kBT;
+      gdx[m] = gdo[m] = 0.f;
+      if (e < C * kNS) {
+        const int r = e / kNS, j = e % kNS;
+        float a = 0.f;
+        for (int s = r; s < C; ++s) a = fmaf(sT[s * LC + r], sU[s * kLS + j], a);
+        const float G = __expf(sgam[r]);
+        gdx[m] = G * sb[r] * a;
+        gdo[m] = G * sO[r * kLS + j];
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < PER; ++m) {
+      const int e = t + m * kBT;
+      if (e < C * kNS) {
+        const int r = e / kNS, j = e % kNS;
+        sU[r * kLS + j] = gdx[m];
+        sO[r * kLS + j] = gdo[m];
+      }
+    }
+    __syncthreads();
+    // dS = Gam_C dS' + (Diag(Gam) Q)^T dO - (Diag(Gam) K)^T dX
+    const float GC = __expf(gC);
+    for (int e = t; e < DK * kNS; e += kBT) {
+      const int i = e / kNS, j = e % kNS;
+      float acc = 0.f;
+      for (int r = 0; r < C; ++r)
+        acc = fmaf(sQ[r * LK + i], sO[r * kLS + j], fmaf(-sK[r * LK + i], sU[r * kLS + j], acc));
+      sS[i * kLS + j] = fmaf(GC, sS[i * kLS + j], acc);
+    }
+  }
+  if (p.ds0) {
+    __syncthreads();
+    for (int e = t; e < DK * kNS; e += kBT) {
+      const int i = e / kNS, j = e % kNS;
+      p.ds0[sbase + (size_t)i * p.DV + col0 + j] = sS[i * kLS + j];
+    }
+  }
+}
+
+// ============================================================================
+// grads: dq, dk, dv, dg, deta of one (chunk, head)
+// ============================================================================
+template <int C, int DK>
+struct GradSmem {
+  static constexpr int LK = DK + 1, LC = C + 1;
+  static constexpr int K = 0, Q = K + C * LK, T = Q + C * LK, P = T + C * LC;  // P, later Y, dEE
+  static constexpr int SL = P + C * LC;                                      // slice region
+  static constexpr int S = SL, D = S + DK * kLS, V = D + DK * kLS, O = V + C * kLS, X = O + C * kLS;
+  static constexpr int U = X + C * kLS, DU = U + C * kLS, DX = DU + C * kLS, SL_END = DX + C * kLS;
+  static constexpr int B1 = SL, B2 = SL + C * LC;  // C x C stage, over the slice region
+  static constexpr int SL_SIZE = SL_END - SL > 2 * C * LC ? SL_END - SL : 2 * C * LC;
+  static constexpr int VEC = SL + SL_SIZE;
+  static constexpr int BETA = VEC, GAM = BETA + C, NRM = GAM + C, ETA = NRM + C, DGAM = ETA + C, DD = DGAM + C;
+  static constexpr int DB1 = DD + C, DB2 = DB1 + C, DGE = DB2 + C, CF = DGE + C, GM = CF + C, DEC = GM + C;
+  static constexpr int RED = DEC + C;
+  static constexpr int FLOATS = RED + kBT;
+};
+
+template <typename E, int C, int DK>
+__global__ __launch_bounds__(kBT) void kla_bwd_grads_kernel(BwdParams p) {
+  using L = GradSmem<C, DK>;
+  using R = PrepRec<C>;
+  constexpr int LK = L::LK, LC = L::LC;
+  constexpr int TC = C / 16, TK = DK / 16;  // per-thread rows (C) and columns (C or DK)
+  static_assert(C % 16 == 0 && DK % 16 == 0, "16 x 16 thread grid");
+  __shared__ float sm[L::FLOATS];
+  float *sK = sm + L::K, *sQ = sm + L::Q, *sT = sm + L::T, *sP = sm + L::P;
+  float *sS = sm + L::S, *sD = sm + L::D, *sV = sm + L::V, *sO = sm + L::O, *sX = sm + L::X;
+  float *sU = sm + L::U, *sdU = sm + L::DU, *sdX = sm + L::DX;
+  float *sb = sm + L::BETA, *sgam = sm + L::GAM, *snrm = sm + L::NRM, *seta = sm + L::ETA;
+  float *sdgam = sm + L::DGAM, *sdd = sm + L::DD, *sdb1 = sm + L::DB1, *sdb2 = sm + L::DB2;
+  float *sdge = sm + L::DGE, *scf = sm + L::CF, *sred = sm + L::RED, *sGm = sm + L::GM, *sdec = sm + L::DEC;
+  const int slot = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
+  const ChunkLoc cl = chunk_loc(p, slot, h, C);
+  if (cl.rows == 0) return;  // uniform
+  const int rows = cl.rows;
+  const int rb = t / 16, cb = t % 16;  // 16 x 16 thread grid
+  const size_t sidx = (size_t)h * p.nslot + slot;
+  const float *rec = p.prep + sidx * R::FLOATS;
+  const float *Sg = p.states + sidx * DK * p.DV;
+  const float *Dg = p.dstates + sidx * DK * p.DV;
+
+  load_rows<E, C, DK, LK>(sK, p.k, cl.row0, rows, 0, DK);
+  load_rows<E, C, DK, LK>(sQ, p.q, cl.row0, rows, 0, DK);
+  for (int e = t; e < C * C; e += kBT) {
+    sT[(e / C) * LC + e % C] = rec[R::TM + e];
+    sP[(e / C) * LC + e % C] = rec[R::PM + e];
+  }
+  for (int r = t; r < C; r += kBT) {
+    sb[r] = rec[R::BETA + r];
+    sgam[r] = rec[R::GAM + r];
+    snrm[r] = rec[R::NRM + r];
+    seta[r] = r < rows ? ld<E>(p.eta, cl.row0 + r) : 0.f;
+    sdgam[r] = 0.f;
+    sdd[r] = 0.f;
+  }
+  const float gC = rec[R::GAM + C - 1];
+  for (int r = t; r < C; r += kBT) {
+    const float gr = rec[R::GAM + r];
+    sGm[r] = __expf(gr);
+    sdec[r] = __expf(gC - gr);
+  }
+
+  float accW[TC][TC], accP[TC][TC], accQ[TC][TK], accK[TC][TK];
+#pragma unroll
+  for (int a = 0; a < TC; ++a) {
+#pragma unroll
+    for (int b = 0; b < TC; ++b) accW[a][b] = accP[a][b] = 0.f;
+#pragma unroll
+    for (int b = 0; b < TK; ++b) accQ[a][b] = accK[a][b] = 0.f;
+  }
+  float gcp = 0.f;  // partial <S, dS'>
+
+  for (int js = 0; js < p.nsl; ++js) {
+    const int col0 = js * kNS;
+    __syncthreads();
+    for (int e = t; e < DK * kNS; e += kBT) {
+      const int i = e / kNS, j = e % kNS;
+      const float s = Sg[(size_t)i * p.DV + col0 + j], d = Dg[(size_t)i * p.DV + col0 + j];
+      sS[i * kLS + j] = s;
+      sD[i * kLS + j] = d;
+      gcp = fmaf(s, d, gcp);
+    }
+    load_rows<E, C, kNS, kLS>(sV, p.v, cl.row0, rows, col0, p.DV);
+    load_rows<E, C, kNS, kLS>(sO, p.dout, cl.row0, rows, col0, p.DV);
+    __syncthreads();
+    // entries (r = rb*TC + a, j = cb) of the C x 16 slice products
+    float ks[TC], qs[TC], kd[TC], u[TC];
+#pragma unroll
+    for (int a = 0; a < TC; ++a) {
+      const int r = rb * TC + a;
+      float x0 = 0.f, x1 = 0.f, x2 = 0.f;
+      for (int i = 0; i < DK; ++i) {
+        const float kr = sK[r * LK + i];
+        x0 = fmaf(kr, sS[i * kLS + cb], x0);
+        x1 = fmaf(sQ[r * LK + i], sS[i * kLS + cb], x1);
+        x2 = fmaf(kr, sD[i * kLS + cb], x2);
+      }
+      ks[a] = x0;
+      qs[a] = x1;
+      kd[a] = x2;
+      sX[r * kLS + cb] = sV[r * kLS + cb] - sGm[r] * x0;
+    }
+    __syncthreads();
+    // U = T Diag(b) X;  dU = P^T dO + Diag(d) K dS'
+#pragma unroll
+    for (int a = 0; a < TC; ++a) {
+      const int r = rb * TC + a;
+      float x0 = 0.f, x1 = 0.f;
+      for (int s = 0; s <= r; ++s) x0 = fmaf(sT[r * LC + s] * sb[s], sX[s * kLS + cb], x0);
+      for (int s = r; s < C; ++s) x1 = fmaf(sP[s * LC + r], sO[s * kLS + cb], x1);
+      u[a] = x0;
+      sU[r * kLS + cb] = x0;
+      sdU[r * kLS + cb] = fmaf(sdec[r], kd[a], x1);
+    }
+    __syncthreads();
+    // dX = Diag(b) T^T dU (= dV); row sums for dGam and dd
+#pragma unroll
+    for (int a = 0; a < TC; ++a) {
+      const int r = rb * TC + a;
+      float x0 = 0.f;
+      for (int s = r; s < C; ++s) x0 = fmaf(sT[s * LC + r], sdU[s * kLS + cb], x0);
+      const float dx = sb[r] * x0;
+      sdX[r * kLS + cb] = dx;
+      if (r < rows)
+        static_cast<E *>(p.dv)[(cl.row0 + r) * p.DV + col0 + cb] = Elem<E>::from_f32(dx);
+      float pg = qs[a] * sO[r * kLS + cb] - ks[a] * dx;
+      float pd = kd[a] * u[a];
+#pragma unroll
+      for (int off = 8; off >= 1; off >>= 1) {
+        pg += __shfl_xor(pg, off);
+        pd += __shfl_xor(pd, off);
+      }
+      if (cb == 0) {
+        sdgam[r] += pg;
+        sdd[r] += pd;
+      }
+    }
+    __syncthreads();
+    // accumulate dW = dU X^T, dP = dO U^T, dQ += Diag(Gam) dO S^T and
+    // dK += -Diag(Gam) dX S^T + Diag(d) U dS'^T (row scales applied to the left factors)
+    for (int j = 0; j < kNS; ++j) {
+      float du[TC], x[TC], o[TC], oq[TC], uu[TC], dxr[TC], ur[TC];
+#pragma unroll
+      for (int a = 0; a < TC; ++a) {
+        const int r = rb * TC + a, s = cb * TC + a;
+        du[a] = sdU[r * kLS + j];
+        o[a] = sO[r * kLS + j];
+        oq[a] = sGm[r] * o[a];
+        dxr[a] = -sGm[r] * sdX[r * kLS + j];
+        ur[a] = sdec[r] * sU[r * kLS + j];
+        x[a] = sX[s * kLS + j];
+        uu[a] = sU[s * kLS + j];
+      }
+      float sv[TK], dsv[TK];
+#pragma unroll
+      for (int b = 0; b < TK; ++b) {
+        sv[b] = sS[(cb * TK + b) * kLS + j];
+        dsv[b] = sD[(cb * TK + b) * kLS + j];
+      }
+#pragma unroll
+      for (int a = 0; a < TC; ++a) {
+#pragma unroll
+        for (int b = 0; b < TC; ++b) {
+          accW[a][b] = fmaf(du[a], x[b], accW[a][b]);
+          accP[a][b] = fmaf(o[a], uu[b], accP[a][b]);
+        }
+#pragma unroll
+        for (int b = 0; b < TK; ++b) {
+          accQ[a][b] = fmaf(oq[a], sv[b], accQ[a][b]);
+          accK[a][b] = fmaf(dxr[a], sv[b], fmaf(ur[a], dsv[b], accK[a][b]));
+        }
+      }
+    }
+  }
+
+  // ---------------- C x C stage ---------------------------------------------
+  // (the slice region now holds B1 and B2; sP's space is reused for Y, then dEE)
+  float *B1 = sm + L::B1, *B2 = sm + L::B2;
+  sred[t] = gcp;
+  __syncthreads();
+#pragma unroll
+  for (int a = 0; a < TC; ++a)
+#pragma unroll
+    for (int b = 0; b < TC; ++b) {
+      const int r = rb * TC + a, s = cb * TC + b;
+      B1[r * LC + s] = accW[a][b];  // dW
+      B2[r * LC + s] = accP[a][b];  // dP (entries above the diagonal are masked below)
+    }
+  __syncthreads();
+  // db_s (first part) = sum_r T_rs dW_rs;  Y = (dW Diag(b)) T^T
+  for (int s = t; s < C; s += kBT) {
+    float a = 0.f;
+    for (int r = s; r < C; ++r) a = fmaf(sT[r * LC + s], B1[r * LC + s], a);
+    sdb1[s] = a;
+  }
+  float y[TC][TC];
+#pragma unroll
+  for (int a = 0; a < TC; ++a)
+#pragma unroll
+    for (int b = 0; b < TC; ++b) y[a][b] = 0.f;
+  for (int m = 0; m < C; ++m) {
+    float w[TC], tt[TC];
+#pragma unroll
+    for (int a = 0; a < TC; ++a) {
+      w[a] = B1[(rb * TC + a) * LC + m] * sb[m];
+      tt[a] = sT[(cb * TC + a) * LC + m];
+    }
+#pragma unroll
+    for (int a = 0; a < TC; ++a)
+#pragma unroll
+      for (int b = 0; b < TC; ++b) y[a][b] = fmaf(w[a], tt[b], y[a][b]);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int a = 0; a < TC; ++a)
+#pragma unroll
+    for (int b = 0; b < TC; ++b) sP[(rb * TC + a) * LC + cb * TC + b] = y[a][b];
+  __syncthreads();
+  // dA = -T^T Y, strictly lower
+#pragma unroll
+  for (int a = 0; a < TC; ++a)
+#pragma unroll
+    for (int b = 0; b < TC; ++b) y[a][b] = 0.f;
+  for (int m = 0; m < C; ++m) {
+    float tt[TC], yy[TC];
+#pragma unroll
+    for (int a = 0; a < TC; ++a) {
+      tt[a] = sT[m * LC + rb * TC + a];
+      yy[a] = sP[m * LC + cb * TC + a];
+    }
+#pragma unroll
+    for (int a = 0; a < TC; ++a)
+#pragma unroll
+      for (int b = 0; b < TC; ++b) y[a][b] = fmaf(tt[a], yy[b], y[a][b]);
+  }
+  // per entry: dG = dA b_r E, dQK = dP E, dEE = (dA b_r G + dP QK) E, db_r += dA G E
+  float dgm[TC][TC], dqk[TC][TC], dee[TC][TC], dbr[TC];
+#pragma unroll
+  for (int a = 0; a < TC; ++a) {
+    const int r = rb * TC + a;
+    dbr[a] = 0.f;
+#pragma unroll
+    for (int b = 0; b < TC; ++b) {
+      const int s = cb * TC + b;
+      dgm[a][b] = dqk[a][b] = dee[a][b] = 0.f;
+      if (s <= r) {
+        float gkk = 0.f, gqk = 0.f;
+        for (int i = 0; i < DK; ++i) {
+          gkk = fmaf(sK[r * LK + i], sK[s * LK + i], gkk);
+          gqk = fmaf(sQ[r * LK + i], sK[s * LK + i], gqk);
+        }
+        const float ex = __expf(sgam[r] - sgam[s]);
+        const float dA = s < r ? -y[a][b] : 0.f;
+        const float dP = B2[r * LC + s];
+        dgm[a][b] = dA * sb[r] * ex;
+        dqk[a][b] = dP * ex;
+        dee[a][b] = (dA * sb[r] * gkk + dP * gqk) * ex;
+        dbr[a] = fmaf(dA * gkk, ex, dbr[a]);
+      }
+    }
+  }
+#pragma unroll
+  for (int a = 0; a < TC; ++a) {
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) dbr[a] += __shfl_xor(dbr[a], off);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int a = 0; a < TC; ++a) {
+    const int r = rb * TC + a;
+    if (cb == 0) sdb2[r] = dbr[a];
+#pragma unroll
+    for (int b = 0; b < TC; ++b) {
+      const int s = cb * TC + b;
+      B1[r * LC + s] = dgm[a][b];
+      B2[r * LC + s] = dqk[a][b];
+      sP[r * LC + s] = dee[a][b];
+    }
+  }
+  __syncthreads();
+  // dQ += dQK K;  dK += dQK^T Q + (dG + dG^T) K
+  for (int s = 0; s < C; ++s) {
+    float kq[TC], kt[TC], gg[TC];
+#pragma unroll
+    for (int a = 0; a < TC; ++a) {
+      const int r = rb * TC + a;
+      kq[a] = B2[r * LC + s];
+      kt[a] = B2[s * LC + r];
+      gg[a] = B1[r * LC + s] + B1[s * LC + r];
+    }
+#pragma unroll
+    for (int b = 0; b < TK; ++b) {
+      const int i = cb * TK + b;
+      const float ks = sK[s * LK + i], qs = sQ[s * LK + i];
+#pragma unroll
+      for (int a = 0; a < TC; ++a) {
+        accQ[a][b] = fmaf(kq[a], ks, accQ[a][b]);
+        accK[a][b] = fmaf(kt[a], qs, fmaf(gg[a], ks, accK[a][b]));
+      }
+    }
+  }
+  // per-row scalars: dgamma, then dg = reverse running sum; db, deta, the norm term
+  for (int r = t; r < C; r += kBT) {
+    float rs = 0.f, cs = 0.f;
+    for (int s = 0; s < C; ++s) {
+      rs += sP[r * LC + s];
+      cs += sP[s * LC + r];
+    }
+    sdge[r] = sdgam[r] * sGm[r] - sdd[r] * sdec[r] + rs - cs;
+  }
+  __syncthreads();
+  if (t == 0) {
+    float gcs = 0.f, ddd = 0.f;
+    for (int i = 0; i < kBT; ++i) gcs += sred[i];
+    for (int r = 0; r < C; ++r) ddd = fmaf(sdd[r], sdec[r], ddd);
+    sdge[C - 1] += gcs * __expf(gC) + ddd;
+    float acc = 0.f;
+    for (int r = C - 1; r >= 0; --r) {
+      acc += sdge[r];
+      sdge[r] = acc;
+    }
+  }
+  for (int r = t; r < C; r += kBT) {
+    const float db = sdb1[r] + sdb2[r];
+    const float den = snrm[r] + p.eps;
+    scf[r] = (p.beta_direct || r >= rows) ? 0.f : -2.f * seta[r] * db / (den * den);
+    if (r < rows) {
+      p.deta[cl.row0 + r] = p.beta_direct ? db : db / den;
+    }
+  }
+  __syncthreads();
+  for (int r = t; r < rows; r += kBT) p.dg[cl.row0 + r] = sdge[r];
+#pragma unroll
+  for (int a = 0; a < TC; ++a) {
+    const int r = rb * TC + a;
+    if (r < rows) {
+#pragma unroll
+      for (int b = 0; b < TK; ++b) {
+        const int i = cb * TK + b;
+        static_cast<E *>(p.dq)[(cl.row0 + r) * DK + i] = Elem<E>::from_f32(accQ[a][b]);
+        static_cast<E *>(p.dk)[(cl.row0 + r) * DK + i] =
+            Elem<E>::from_f32(fmaf(scf[r], sK[r * LK + i], accK[a][b]));
+      }
+    }
+  }
+}
+
+// ============================================================================
+// host side
+// ============================================================================
+template <int C, int DK>
+struct BwdLayout {
+  // workspace: prep records, then chunk-start states, then chunk-end state gradients
+  static size_t prep_bytes(const ChunkArgs &a, int nslot) {
+    return ((size_t)a.H * nslot * PrepRec<C>::FLOATS * 4 + 255) / 256 * 256;
+  }
+  static size_t state_bytes(const ChunkArgs &a, int nslot) {
+    return ((size_t)a.H * nslot * DK * a.dv * 4 + 255) / 256 * 256;
+  }
+};
+
+template <int C>
+int bwd_slots(const ChunkArgs &a) {
+  return a.cu_seqlens ? a.T / C + a.num_seqs + 1 : a.B * ((a.T + C - 1) / C);
+}
+
+template <typename E, int C, int DK>
+size_t bwd_workspace_bytes_t(const ChunkArgs &a) {
+  const int ns = bwd_slots<C>(a);
+  return BwdLayout<C, DK>::prep_bytes(a, ns) + 2 * BwdLayout<C, DK>::state_bytes(a, ns);
+}
+
+template <typename E, int C, int DK>
+hipError_t launch_bwd_t(const ChunkArgs &a, const ChunkBwdArgs &b, hipStream_t st) {
+  static_assert(PrepSmem<E, C, DK>::FLOATS * 4 <= 160 * 1024, "prep LDS");
+  static_assert(StatesSmem<C, DK>::FLOATS * 4 <= 160 * 1024, "states LDS");
+  static_assert(DStatesSmem<C, DK>::FLOATS * 4 <= 160 * 1024, "dstates LDS");
+  static_assert(GradSmem<C, DK>::FLOATS * 4 <= 160 * 1024, "grads LDS");
+  BwdParams p;
+  p.q = a.q;
+  p.k = a.k;
+  p.v = a.v;
+  p.g = a.g;
+  p.eta = a.eta;
+  p.dout = b.dout;
+  p.eps = a.eps;
+  p.s0 = a.initial_state;
+  p.dsfin = b.dfinal_state;
+  p.dq = b.dq;
+  p.dk = b.dk;
+  p.dv = b.dv;
+  p.dg = b.dg;
+  p.deta = b.deta;
+  p.ds0 = b.dinitial_state;
+  p.cu = a.cu_seqlens;
+  p.B = a.B;
+  p.H = a.H;
+  p.T = a.T;
+  p.DV = a.dv;
+  p.nseq = a.num_seqs;
+  p.nslot = bwd_slots<C>(a);
+  p.nsl = a.dv / kNS;
+  p.beta_direct = a.beta_direct;
+  char *ws = static_cast<char *>(a.workspace);
+  p.prep = reinterpret_cast<float *>(ws);
+  const size_t pb = BwdLayout<C, DK>::prep_bytes(a, p.nslot), sb = BwdLayout<C, DK>::state_bytes(a, p.nslot);
+  p.states = reinterpret_cast<float *>(ws + pb);
+  p.dstates = reinterpret_cast<float *>(ws + pb + sb);
+  const unsigned seq_blocks = (unsigned)((long long)a.num_seqs * a.H * p.nsl);
+  const bool tokens = (long long)a.B * a.T > 0 && p.nslot > 0;
+  if (tokens) {
+    hipLaunchKernelGGL((kla_bwd_prep_kernel<E, C, DK>), dim3((unsigned)p.nslot, (unsigned)a.H), dim3(kBT), 0, st, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((kla_bwd_states_kernel<E, C, DK>), dim3(seq_blocks), dim3(kBT), 0, st, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (seq_blocks > 0 && (tokens || p.ds0)) {
+    // with no tokens this only copies dS_final (or zeros) to the initial-state gradient
+    hipLaunchKernelGGL((kla_bwd_dstates_kernel<E, C, DK>), dim3(seq_blocks), dim3(kBT), 0, st, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (tokens) {
+    hipLaunchKernelGGL((kla_bwd_grads_kernel<E, C, DK>), dim3((unsigned)p.nslot, (unsigned)a.H), dim3(kBT), 0, st, p);
+    return hipGetLastError();
+  }
+  return hipSuccess;
+}
+
+}  // namespace
+
+bool chunk_bwd_supported(int dtype, int dk, int dv, int chunk) { return chunk_supported(dtype, dk, dv, chunk); }
+
+size_t chunk_bwd_workspace_bytes(const ChunkArgs &a) {
+  if (a.dtype == 0) return a.dk == 128 ? bwd_workspace_bytes_t<bf16, 64, 128>(a) : bwd_workspace_bytes_t<bf16, 64, 64>(a);
+  if (a.chunk == 16) {
+    switch (a.dk) {
+      case 16: return bwd_workspace_bytes_t<float, 16, 16>(a);
+      case 32: return bwd_workspace_bytes_t<float, 16, 32>(a);
+      case 64: return bwd_workspace_bytes_t<float, 16, 64>(a);
+      default: return bwd_workspace_bytes_t<float, 16, 128>(a);
+    }
+  }
+  return a.dk == 16 ? bwd_workspace_bytes_t<float, 64, 16>(a) : bwd_workspace_bytes_t<float, 64, 32>(a);
+}
+
+hipError_t launch_chunk_bwd(const ChunkArgs &a, const ChunkBwdArgs &b, hipStream_t st) {
+  if (a.dtype == 0) {
+    if (a.dk == 128) return launch_bwd_t<bf16, 64, 128>(a, b, st);
+    if (a.dk == 64) return launch_bwd_t<bf16, 64, 64>(a, b, st);
+    return hipErrorInvalidValue;
+  }
+  if (a.chunk == 16) {
+    switch (a.dk) {
+      case 16: return launch_bwd_t<float, 16, 16>(a, b, st);
+      case 32: return launch_bwd_t<float, 16, 32>(a, b, st);
+      case 64: return launch_bwd_t<float, 16, 64>(a, b, st);
+      case 128: return launch_bwd_t<float, 16, 128>(a, b, st);
+    }
+  } else if (a.chunk == 64) {
+    switch (a.dk) {
+      case 16: return launch_bwd_t<float, 64, 16>(a, b, st);
+      case 32: return launch_bwd_t<float, 64, 32>(a, b, st);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace kla

@@ -29,6 +29,15 @@ struct ChunkArgs {
   int beta_direct;  // 1: `eta` holds beta itself (gated delta rule); eps unused
 };
 
+// Upstream gradients in and gradients out of the backward pass (device pointers).
+struct ChunkBwdArgs {
+  const void *dout;             // dL/do, [B,H,T,dv], dtype
+  const float *dfinal_state;    // dL/dS_final, [N,H,dk,dv] fp32, or nullptr (zero)
+  void *dq, *dk, *dv;           // dtype, shaped as q, k, v
+  float *dg, *deta;             // fp32 [B,H,T]
+  float *dinitial_state;        // fp32 [N,H,dk,dv], or nullptr (not written)
+};
+
 // True if a kernel is compiled for this combination.
 bool decode_supported(int dtype, int dk, int dv);
 bool chunk_supported(int dtype, int dk, int dv, int chunk);
@@ -38,8 +47,15 @@ bool chunk_supported(int dtype, int dk, int dv, int chunk);
 // kernel).  Arguments are already validated and supported.
 size_t chunk_workspace_bytes(const ChunkArgs &a);
 
+// The backward pass supports the forward's shapes; its workspace holds per
+// (chunk, head) T, P and vectors plus the chunk-start states and chunk-end
+// state gradients (fp32).
+bool chunk_bwd_supported(int dtype, int dk, int dv, int chunk);
+size_t chunk_bwd_workspace_bytes(const ChunkArgs &a);
+
 // Enqueue the kernel(s).  Arguments are already validated.
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_chunk_fwd(const ChunkArgs &a, hipStream_t stream);
+hipError_t launch_chunk_bwd(const ChunkArgs &a, const ChunkBwdArgs &b, hipStream_t stream);
 
 }  // namespace kla

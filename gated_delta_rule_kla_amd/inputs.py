@@ -40,6 +40,7 @@ __all__ = [
     "decode_config",
     "CONFIGS",
     "to_f64",
+    "make_upstream",
 ]
 
 
@@ -253,3 +254,17 @@ def prefill_config(i: int, *, H: Optional[int] = None, T: Optional[int] = None,
 def decode_config(steps: int = 512, N: int = 256, H: int = 16) -> DecodeInputs:
     """Decode workload 3 (N sequences x H heads, 128x128 fp32 state)."""
     return make_decode(N=N, H=H, dk=128, dv=128, steps=steps, seed=1003, name="cfg3")
+
+
+def make_upstream(x: PrefillInputs, seed: int, *, ds_std: Optional[float] = 1.0):
+    """Seeded upstream gradients for a prefill call: dL/do ~ N(0, 1) per element,
+    rounded to the inputs' dtype ([B, H, T, dv]), and dL/dS_final ~ N(0, ds_std)
+    fp32 [N, H, dk, dv] (None when ``ds_std`` is None)."""
+    B, H, T, dk, dv = x.dims
+    rng = np.random.default_rng(seed)
+    do = _round(rng.standard_normal((B, H, T, dv), dtype=np.float32), x.q.dtype)
+    ds = None
+    if ds_std is not None:
+        ds = torch.from_numpy(
+            (np.float32(ds_std) * rng.standard_normal((x.num_seqs, H, dk, dv), dtype=np.float32)).copy())
+    return do, ds

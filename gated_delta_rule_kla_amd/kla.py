@@ -13,8 +13,9 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["chunk_fwd", "chunk_workspace_bytes", "decode_step", "gdn_chunk_fwd", "gdn_decode_step", "lib",
-           "lib_path", "KlaError", "KLA_DT_BF16", "KLA_DT_F32"]
+__all__ = ["chunk_fwd", "chunk_workspace_bytes", "decode_step", "gdn_chunk_fwd", "gdn_decode_step", "chunk_bwd",
+           "gdn_chunk_bwd", "chunk_bwd_workspace_bytes", "lib", "lib_path", "KlaError", "KLA_DT_BF16",
+           "KLA_DT_F32"]
 
 KLA_DT_BF16 = 0
 KLA_DT_F32 = 1
@@ -60,6 +61,14 @@ def lib() -> ctypes.CDLL:
         L.kla_gdn_chunk_fwd.restype = i32
         L.kla_gdn_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
         L.kla_gdn_decode_step.restype = i32
+        L.kla_chunk_bwd.argtypes = [vp, vp, vp, vp, vp, f32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                    i32, i32, i32, i32, i32, i32, i32, vp, sz, i32, vp]
+        L.kla_chunk_bwd.restype = i32
+        L.kla_gdn_chunk_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                        i32, i32, i32, i32, i32, i32, i32, vp, sz, i32, vp]
+        L.kla_gdn_chunk_bwd.restype = i32
+        L.kla_chunk_bwd_workspace_bytes.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, i32, i32]
+        L.kla_chunk_bwd_workspace_bytes.restype = sz
         L.kla_status_str.argtypes = [i32]
         L.kla_status_str.restype = ctypes.c_char_p
         L.kla_abi_version.argtypes = []
@@ -210,6 +219,119 @@ def chunk_workspace_bytes(B: int, H: int, T: int, dk: int, dv: int, chunk: int =
         return lib().kla_chunk_workspace_bytes(ctypes.c_void_p(16), cu.data_ptr(), cu.numel() - 1, B, H, T,
                                                dk, dv, int(chunk), _DTYPES[dtype])
     return lib().kla_chunk_workspace_bytes(None, None, B, B, H, T, dk, dv, int(chunk), _DTYPES[dtype])
+
+
+def _bwd_call(fn, q, k, v, g, coef, eps, do, initial_state, dfinal_state, cu_seqlens, chunk, cu_seqlens_host,
+              need_dinitial, workspace):
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError(f"kla.{fn} needs GPU tensors")
+    dtype = q.dtype
+    if dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {dtype}")
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    _need(q, "q", dtype, (B, H, T, dk), dev)
+    _need(k, "k", dtype, (B, H, T, dk), dev)
+    _need(v, "v", dtype, (B, H, T, dv), dev)
+    _need(g, "g", dtype, (B, H, T), dev)
+    _need(coef, "eta" if eps is not None else "beta", dtype, (B, H, T), dev)
+    _need(do, "do", dtype, (B, H, T, dv), dev)
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, (cu_seqlens.numel(),), dev)
+        if cu_seqlens_host is None:
+            cu_seqlens_host = cu_seqlens.cpu()
+        cu_seqlens_host = cu_seqlens_host.to(torch.int32).contiguous()
+        if cu_seqlens_host.numel() != cu_seqlens.numel():
+            raise ValueError("cu_seqlens_host does not mirror cu_seqlens")
+        N = cu_seqlens.numel() - 1
+    else:
+        N = B
+    if initial_state is not None:
+        _need(initial_state, "initial_state", torch.float32, (N, H, dk, dv), dev)
+    if dfinal_state is not None:
+        _need(dfinal_state, "dfinal_state", torch.float32, (N, H, dk, dv), dev)
+    dq = torch.empty_like(q)
+    dkk = torch.empty_like(k)
+    dvv = torch.empty_like(v)
+    dg = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    dcoef = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    ds0 = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev) if need_dinitial else None
+    host_ptr = None if cu_seqlens_host is None else cu_seqlens_host.data_ptr()
+    ws_bytes = lib().kla_chunk_bwd_workspace_bytes(_ptr(cu_seqlens), host_ptr, N, B, H, T, dk, dv, int(chunk),
+                                                   _DTYPES[dtype])
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    elif workspace.device != dev or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor on the inputs' device")
+    mid = (_ptr(initial_state), _ptr(do), _ptr(dfinal_state), _ptr(dq), _ptr(dkk), _ptr(dvv), _ptr(dg),
+           _ptr(dcoef), _ptr(ds0), _ptr(cu_seqlens), host_ptr, N, B, H, T, dk, dv, int(chunk),
+           _ptr(workspace), workspace.numel(), _DTYPES[dtype], _stream(dev))
+    if eps is not None:
+        st = lib().kla_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(coef), float(eps), *mid)
+        _check("kla_chunk_bwd", st)
+    else:
+        st = lib().kla_gdn_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(coef), *mid)
+        _check("kla_gdn_chunk_bwd", st)
+    return dq, dkk, dvv, dg, dcoef, ds0
+
+
+def chunk_bwd(
+    q: torch.Tensor,
+    k: torch.Tensor,
+    v: torch.Tensor,
+    g: torch.Tensor,
+    eta: torch.Tensor,
+    do: torch.Tensor,
+    eps: float = 1e-6,
+    initial_state: Optional[torch.Tensor] = None,
+    dfinal_state: Optional[torch.Tensor] = None,
+    cu_seqlens: Optional[torch.Tensor] = None,
+    chunk: int = 64,
+    cu_seqlens_host: Optional[torch.Tensor] = None,
+    need_dinitial: bool = True,
+    workspace: Optional[torch.Tensor] = None,
+):
+    """Gradients of chunk_fwd (kla_chunk_bwd) for upstream gradients ``do``
+    [B, H, T, dv] (dtype of q) and ``dfinal_state`` [N, H, dk, dv] fp32 or None.
+
+    Returns (dq, dk, dv, dg, deta, dinitial_state): dq, dk, dv in the inputs'
+    dtype; dg, deta [B, H, T] fp32; dinitial_state [N, H, dk, dv] fp32 (None
+    unless ``need_dinitial``).  Other arguments as chunk_fwd.
+    """
+    return _bwd_call("chunk_bwd", q, k, v, g, eta, eps, do, initial_state, dfinal_state, cu_seqlens, chunk,
+                     cu_seqlens_host, need_dinitial, workspace)
+
+
+def gdn_chunk_bwd(
+    q: torch.Tensor,
+    k: torch.Tensor,
+    v: torch.Tensor,
+    g: torch.Tensor,
+    beta: torch.Tensor,
+    do: torch.Tensor,
+    initial_state: Optional[torch.Tensor] = None,
+    dfinal_state: Optional[torch.Tensor] = None,
+    cu_seqlens: Optional[torch.Tensor] = None,
+    chunk: int = 64,
+    cu_seqlens_host: Optional[torch.Tensor] = None,
+    need_dinitial: bool = True,
+    workspace: Optional[torch.Tensor] = None,
+):
+    """Gradients of gdn_chunk_fwd (kla_gdn_chunk_bwd); the fifth result is dbeta."""
+    return _bwd_call("gdn_chunk_bwd", q, k, v, g, beta, None, do, initial_state, dfinal_state, cu_seqlens,
+                     chunk, cu_seqlens_host, need_dinitial, workspace)
+
+
+def chunk_bwd_workspace_bytes(B: int, H: int, T: int, dk: int, dv: int, chunk: int = 64,
+                              dtype: torch.dtype = torch.bfloat16,
+                              cu_seqlens_host: Optional[torch.Tensor] = None) -> int:
+    """Workspace bytes kla_chunk_bwd needs (kla_chunk_bwd_workspace_bytes)."""
+    if cu_seqlens_host is not None:
+        cu = cu_seqlens_host.to(torch.int32).contiguous()
+        return lib().kla_chunk_bwd_workspace_bytes(ctypes.c_void_p(16), cu.data_ptr(), cu.numel() - 1, B, H, T,
+                                                   dk, dv, int(chunk), _DTYPES[dtype])
+    return lib().kla_chunk_bwd_workspace_bytes(None, None, B, B, H, T, dk, dv, int(chunk), _DTYPES[dtype])
 
 
 def _decode_call(fn, q, k, v, g, coef, eps, state, out):

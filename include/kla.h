@@ -185,13 +185,78 @@ kla_status_t kla_gdn_decode_step(const void *q, const void *k, const void *v,
                                  int N, int H, int dk, int dv,
                                  kla_dtype_t dtype, void *stream);
 
+/*
+ * kla_chunk_bwd -- gradients of kla_chunk_fwd.
+ *
+ * KLA is trained with Gated DeltaNet's block-parallel algorithm, only the
+ * diagonal coefficient matrix Diag(beta) of the block solver changing
+ * (§"Implementación"); this is the reverse mode of that block solver.  For a
+ * scalar loss L with upstream gradients dout = dL/do and dfinal_state =
+ * dL/dS_final, it returns dL/dq, dL/dk (including the path through ||k||^2 in
+ * beta), dL/dv, dL/dg, dL/deta and dL/dinitial_state.
+ *
+ *   q, k, v, g, eta, eps, initial_state, cu_seqlens, cu_seqlens_host,
+ *   num_seqs, B, H, T, dk, dv, chunk, dtype: the forward call's arguments
+ *   dout            [B, H, T, dv]   dtype
+ *   dfinal_state    [N, H, dk, dv]  fp32, or NULL (zero)
+ *   dq, dk_, dv_    shaped and typed as q, k, v (written)
+ *   dg, deta        [B, H, T]       fp32 (written)
+ *   dinitial_state  [N, H, dk, dv]  fp32 (written), or NULL (not computed)
+ *   workspace       kla_chunk_bwd_workspace_bytes(...) bytes of device memory
+ *                   (16-byte aligned), owned by the caller, no initialisation
+ *                   needed; holds per (chunk, head) T = (I + A)^-1, the causal
+ *                   scores, the coefficient and decay vectors, the chunk-start
+ *                   state and the chunk-end state gradient (fp32).
+ *
+ * Every pointer is 16-byte aligned device memory; gradient buffers must not
+ * alias the inputs.  Positions of the gradient tensors that belong to no
+ * sequence are not written.  Status codes and validation as kla_chunk_fwd
+ * (all checks on the host before any HIP call); the supported shapes are
+ * kla_chunk_fwd's.  Four kernels run on `stream`: a parallel per-(chunk, head)
+ * prep, a forward scan that stores the chunk-start states, a reverse scan of
+ * the state gradients, and a parallel per-(chunk, head) gradient kernel.
+ */
+kla_status_t kla_chunk_bwd(const void *q, const void *k, const void *v,
+                           const void *g, const void *eta, float eps,
+                           const float *initial_state, const void *dout, const float *dfinal_state,
+                           void *dq, void *dk_, void *dv_, float *dg, float *deta,
+                           float *dinitial_state,
+                           const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
+                           int num_seqs, int B, int H, int T, int dk, int dv, int chunk,
+                           void *workspace, size_t workspace_bytes,
+                           kla_dtype_t dtype, void *stream);
+
+/*
+ * kla_gdn_chunk_bwd -- gradients of kla_gdn_chunk_fwd: as kla_chunk_bwd with
+ * beta [B, H, T] given in place of eta and eps; dbeta [B, H, T] fp32 is dL/dbeta.
+ */
+kla_status_t kla_gdn_chunk_bwd(const void *q, const void *k, const void *v,
+                               const void *g, const void *beta,
+                               const float *initial_state, const void *dout, const float *dfinal_state,
+                               void *dq, void *dk_, void *dv_, float *dg, float *dbeta,
+                               float *dinitial_state,
+                               const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
+                               int num_seqs, int B, int H, int T, int dk, int dv, int chunk,
+                               void *workspace, size_t workspace_bytes,
+                               kla_dtype_t dtype, void *stream);
+
+/*
+ * kla_chunk_bwd_workspace_bytes -- device workspace kla_chunk_bwd and
+ * kla_gdn_chunk_bwd need (host-only): per (chunk, head) 4 (2 C^2 + 4 C) bytes
+ * plus 8 dk dv bytes (rounded up per region).  0 when no workspace is needed
+ * or for arguments kla_chunk_bwd would reject.
+ */
+size_t kla_chunk_bwd_workspace_bytes(const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
+                                     int num_seqs, int B, int H, int T, int dk, int dv, int chunk,
+                                     kla_dtype_t dtype);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *kla_status_str(kla_status_t s);
 
 /* ABI version of this header (incremented on any incompatible change). */
 int kla_abi_version(void);
 
-#define KLA_ABI_VERSION 3
+#define KLA_ABI_VERSION 4
 
 #ifdef __cplusplus
 }

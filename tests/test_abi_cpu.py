@@ -29,7 +29,8 @@ def test_exports_every_declared_symbol():
     L = kla.lib()
     names = _declared()
     assert set(names) >= {"kla_chunk_fwd", "kla_chunk_workspace_bytes", "kla_decode_step", "kla_status_str",
-                          "kla_abi_version", "kla_gdn_chunk_fwd", "kla_gdn_decode_step"}
+                          "kla_abi_version", "kla_gdn_chunk_fwd", "kla_gdn_decode_step", "kla_chunk_bwd",
+                          "kla_gdn_chunk_bwd", "kla_chunk_bwd_workspace_bytes"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -231,3 +232,74 @@ def test_workspace_slots_never_collide():
                 assert s not in seen and 0 <= s < T // C + N + 1
                 seen.add(s)
             t0 += L
+
+
+def _bwd(fn="kla_chunk_bwd", **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, eta=FAKE, eps=1e-6, s0=None, do=FAKE, dsf=None,
+             dq=FAKE, dk_=FAKE, dv_=FAKE, dg=FAKE, deta=FAKE, ds0=None, cu=None, cuh=None,
+             N=2, B=2, H=4, T=100, dk=128, dv=128, chunk=64, ws=FAKE, ws_bytes=1 << 40, dtype=0)
+    a.update(kw)
+    head = (a["q"], a["k"], a["v"], a["g"], a["eta"])
+    if fn == "kla_chunk_bwd":
+        head = head + (a["eps"],)
+    return getattr(kla.lib(), fn)(*head, a["s0"], a["do"], a["dsf"], a["dq"], a["dk_"], a["dv_"], a["dg"],
+                                  a["deta"], a["ds0"], a["cu"], a["cuh"], a["N"], a["B"], a["H"], a["T"],
+                                  a["dk"], a["dv"], a["chunk"], a["ws"], a["ws_bytes"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("fn", ["kla_chunk_bwd", "kla_gdn_chunk_bwd"])
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=7), E_DTYPE),
+    (dict(H=0), E_SHAPE),
+    (dict(N=3), E_SHAPE),
+    (dict(dk=96), E_UNSUP),
+    (dict(chunk=32), E_UNSUP),
+    (dict(do=None), E_NULL),
+    (dict(dq=None), E_NULL),
+    (dict(dg=None), E_NULL),
+    (dict(deta=None), E_NULL),
+    (dict(dk_=FAKE + 8), E_ALIGN),
+    (dict(ds0=FAKE + 4), E_ALIGN),
+    (dict(dsf=FAKE + 4), E_ALIGN),
+    (dict(cu=FAKE), E_NULL),
+    (dict(ws=None), E_WS),
+    (dict(ws_bytes=1000), E_WS),
+    (dict(N=0, B=0), OK),
+])
+def test_chunk_bwd_rejects(fn, kw, code):
+    assert _bwd(fn, **kw) == code
+
+
+def test_chunk_bwd_eps_checked():
+    assert _bwd(eps=-1.0) == E_EPS
+    assert _bwd(eps=float("nan")) == E_EPS
+
+
+def test_chunk_bwd_workspace_bytes():
+    L = kla.lib()
+
+    def ws(**kw):
+        a = dict(cu=None, cuh=None, N=2, B=2, H=4, T=100, dk=128, dv=128, chunk=64, dtype=0)
+        a.update(kw)
+        return L.kla_chunk_bwd_workspace_bytes(a["cu"], a["cuh"], a["N"], a["B"], a["H"], a["T"], a["dk"],
+                                               a["dv"], a["chunk"], a["dtype"])
+
+    r256 = lambda x: (x + 255) // 256 * 256
+    # per (chunk, head): T and P (C x C fp32) + 4 C fp32 vectors; chunk-start state and chunk-end
+    # state gradient (dk x dv fp32 each); B=2 x ceil(100/64)=2 chunks x H=4
+    slots = 2 * 2 * 4
+    assert ws() == r256(slots * (2 * 64 * 64 + 4 * 64) * 4) + 2 * r256(slots * 128 * 128 * 4)
+    assert ws(dtype=1, chunk=16, dk=32, dv=16) == (r256(2 * 7 * 4 * (2 * 16 * 16 + 4 * 16) * 4)
+                                                   + 2 * r256(2 * 7 * 4 * 32 * 16 * 4))
+    assert ws(T=0) == 0 and ws(N=0, B=0) == 0 and ws(dk=96) == 0
+    assert kla.chunk_bwd_workspace_bytes(2, 4, 100, 128, 128) == ws()
+    assert _bwd(ws_bytes=ws() - 1) == E_WS
+
+
+def test_binding_refuses_cpu_tensors_bwd():
+    import torch
+    x = torch.zeros(1, 1, 4, 16)
+    with pytest.raises(ValueError):
+        kla.chunk_bwd(x, x, x, x[..., 0], x[..., 0], x)
+    with pytest.raises(ValueError):
+        kla.gdn_chunk_bwd(x, x, x, x[..., 0], x[..., 0], x)
