@@ -11,10 +11,11 @@ seeded synthetic tensors resident in HBM before timing starts.
 Also measured in the same run and reported in the same JSON line:
   * decode: 512 consecutive kla_decode_step calls, N=256 sequences x H=16,
     128x128 fp32 state (HBM-bound; reported as GB/s);
+  * backward: kla_chunk_bwd on the prefill workload (steps/10 timed calls);
   * cpu_baseline: the fp64 CPU oracle on a bounded sample of the prefill
     workload, on this host's cores.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--mode all|prefill|decode]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--mode all|prefill|decode|backward]
 """
 
 from __future__ import annotations
@@ -44,6 +45,22 @@ def prefill_algorithmic(B, H, T, dk, dv, C, n_states_read, n_states_written, N):
     th = B * H * T
     flops = th * (2 * C * (3 * dk + 2 * dv) + 6 * dk * dv)
     byts = th * (2 * (2 * dk + dv) + 2 * 2 + 2 * dv) + 4 * dk * dv * N * H * (n_states_read + n_states_written)
+    return flops, byts
+
+
+def backward_algorithmic(B, H, T, dk, dv, C, n_states_read, n_states_written, N):
+    """Fixed-formula work of one backward call (independent of the implementation).
+
+    flops per token-head: 12 dk dv + 8 C dv + 6 C dk + 4 C^2, the dense products of the
+      chunk form's reverse mode counted once each (dU, dX, dS, dP, dW, dA, dQ, dK); the
+      forward quantities a backward recomputes are not counted.
+    bytes per token-head: q, k, v, do, g, eta read and dq, dk, dv written once (bf16),
+      dg, deta written (fp32), plus 4 dk dv per state read or written per (sequence, head).
+    """
+    th = B * H * T
+    flops = th * (12 * dk * dv + 8 * C * dv + 6 * C * dk + 4 * C * C)
+    byts = (th * (2 * (2 * dk + 2 * dv) + 2 * 2 + 2 * (2 * dk + dv) + 2 * 4)
+            + 4 * dk * dv * N * H * (n_states_read + n_states_written))
     return flops, byts
 
 
@@ -111,6 +128,33 @@ def bench_prefill(steps, warmup):
     flops, byts = prefill_algorithmic(B, H, T, dk, dv, x.chunk, 0, 1, B)
     return dict(ms=ms, wall_ms=wall * 1e3 / steps, tokens=B * T, flops=flops, bytes=byts,
                 dims=(B, H, T, dk, dv, x.chunk))
+
+
+def bench_backward(steps, warmup):
+    """kla_chunk_bwd on the prefill workload: upstream gradients dL/do (bf16) and
+    dL/dS_final (fp32) seeded, the initial-state gradient requested."""
+    import torch
+    from gated_delta_rule_kla_amd import inputs, kla
+
+    dev = torch.device("cuda:0")
+    x = inputs.prefill_config(1)
+    B, H, T, dk, dv = x.dims
+    q, k, v, g, eta = (t.to(dev) for t in (x.q, x.k, x.v, x.g, x.eta))
+    do_h, ds_h = inputs.make_upstream(x, 101)
+    do, ds = do_h.to(dev), ds_h.to(dev)
+    ws = torch.empty(kla.chunk_bwd_workspace_bytes(B, H, T, dk, dv, x.chunk, q.dtype), dtype=torch.uint8,
+                     device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(_i):
+        kla.chunk_bwd(q, k, v, g, eta, do, x.eps, None, ds, None, chunk=x.chunk, workspace=ws)
+
+    for i in range(warmup):
+        step(i)
+    ms, wall = time_launches(step, steps, stream)
+    flops, byts = backward_algorithmic(B, H, T, dk, dv, x.chunk, 1, 1, B)
+    return dict(ms=ms, wall_ms=wall * 1e3 / steps, tokens=B * T, flops=flops, bytes=byts,
+                ws_bytes=ws.numel(), dims=(B, H, T, dk, dv, x.chunk))
 
 
 def bench_gdn(steps, warmup, decode_steps=512):
@@ -202,7 +246,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--mode", choices=["all", "prefill", "decode"], default="all")
+    ap.add_argument("--mode", choices=["all", "prefill", "decode", "backward"], default="all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 256 MiB device copy (for HBM counter calibration)")
@@ -274,6 +318,25 @@ def main():
             out.update({"value": gbs, "unit": "GB/s", "ms_per_step": d["ms"],
                         "config": {"workload": dec["workload"]}, "roofline": dec["roofline"]})
         out["decode"] = dec
+    if args.mode in ("all", "backward"):
+        bw = bench_backward(max(1, args.steps // 10), max(1, args.warmup // 10))
+        B, H, T, dk, dv, C = bw["dims"]
+        sec = bw["ms"] * 1e-3
+        gbs = bw["bytes"] / sec / 1e9
+        bwd = {"workload": f"KLA chunkwise backward (kla_chunk_bwd), B={B} H={H} T={T} dk={dk} dv={dv} "
+                           f"chunk={C}, bf16, upstream dL/do and dL/dS_final, dL/dS0 written",
+               "ms_per_step": bw["ms"], "wall_ms_per_step": bw["wall_ms"], "tokens/s": bw["tokens"] / sec,
+               "tflops": bw["flops"] / sec / 1e12, "workspace_bytes": bw["ws_bytes"],
+               "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                            "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                            "kernel": "kla_chunk_bwd: prep, states, dstates and grads kernels timed "
+                                      "together per call",
+                            "algorithmic_bytes_per_launch": bw["bytes"],
+                            "algorithmic_flops_per_launch": bw["flops"]}}
+        if args.mode == "backward":
+            out.update({"value": bw["tokens"] / sec, "unit": "tokens/s", "ms_per_step": bw["ms"],
+                        "config": {"workload": bwd["workload"]}, "roofline": bwd["roofline"]})
+        out["backward"] = bwd
     if args.mode == "all":
         gd = bench_gdn(args.steps, args.warmup)
         gdn = {"workload": "the same prefill and decode workloads through kla_gdn_chunk_fwd / "

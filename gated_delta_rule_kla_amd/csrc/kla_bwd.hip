@@ -110,15 +110,51 @@ __device__ __forceinline__ float ld(const void *base, long long i) {
   return Elem<E>::to_f32(static_cast<const E *>(base)[i]);
 }
 
-// Rows [0, rows) of a [*, D] token tensor from token row `row0` into LDS with row
-// stride LD, zeros past `rows`.
+// An [R x D] tile of a row-major array (row stride `ld` elements) moved as
+// 16-byte vectors: issue() loads this thread's vectors into registers (all of
+// them before any is used, so their latencies overlap), put() widens them to
+// fp32 into LDS rows of stride LD.  Rows at or past `rows` read as zero.
+template <typename E, int R, int D, int LD>
+struct TileLoad {
+  static constexpr int EPV = 16 / (int)sizeof(E);  // elements per vector
+  static constexpr int VPR = D / EPV;              // vectors per row
+  static constexpr int NV = R * VPR;
+  static constexpr int PER = (NV + kBT - 1) / kBT;
+  static_assert(D % EPV == 0, "rows are whole 16-byte vectors");
+  uint4 v[PER];
+
+  __device__ __forceinline__ void issue(const void *src, long long row0, int rows, int col0, long long ld) {
+#pragma unroll
+    for (int m = 0; m < PER; ++m) {
+      const int idx = (int)threadIdx.x + m * kBT;
+      const int r = idx / VPR, c = (idx % VPR) * EPV;
+      v[m] = make_uint4(0u, 0u, 0u, 0u);
+      if (idx < NV && r < rows)
+        v[m] = *reinterpret_cast<const uint4 *>(static_cast<const E *>(src) + (row0 + r) * ld + col0 + c);
+    }
+  }
+  __device__ __forceinline__ void put(float *dst) const {
+#pragma unroll
+    for (int m = 0; m < PER; ++m) {
+      const int idx = (int)threadIdx.x + m * kBT;
+      if (idx < NV) {
+        const int r = idx / VPR, c = (idx % VPR) * EPV;
+        const E *e = reinterpret_cast<const E *>(&v[m]);
+#pragma unroll
+        for (int u = 0; u < EPV; ++u) dst[r * LD + c + u] = Elem<E>::to_f32(e[u]);
+      }
+    }
+  }
+};
+
+// Rows [0, rows) of a [*, D] array from row `row0` into LDS with row stride LD,
+// zeros past `rows` (one batch of vector loads).
 template <typename E, int R, int D, int LD>
 __device__ __forceinline__ void load_rows(float *dst, const void *src, long long row0, int rows, int col0,
-                                          int ld_src) {
-  for (int e = threadIdx.x; e < R * D; e += kBT) {
-    const int r = e / D, i = e % D;
-    dst[r * LD + i] = r < rows ? ld<E>(src, (row0 + r) * ld_src + col0 + i) : 0.f;
-  }
+                                          long long ld_src) {
+  TileLoad<E, R, D, LD> tl;
+  tl.issue(src, row0, rows, col0, ld_src);
+  tl.put(dst);
 }
 
 // ============================================================================
@@ -227,29 +263,40 @@ __global__ __launch_bounds__(kBT) void kla_bwd_states_kernel(BwdParams p) {
   const int col0 = js * kNS;
   const SeqLoc sq = seq_loc(p, n, h, C);
   const size_t sbase = ((size_t)n * p.H + h) * DK * p.DV;
-  for (int e = t; e < DK * kNS; e += kBT) {
-    const int i = e / kNS, j = e % kNS;
-    sS[i * kLS + j] = p.s0 ? p.s0[sbase + (size_t)i * p.DV + col0 + j] : 0.f;
+  if (p.s0) {
+    load_rows<float, DK, kNS, kLS>(sS, p.s0 + sbase, 0, DK, col0, p.DV);
+  } else {
+    for (int e = t; e < DK * kNS; e += kBT) sS[(e / kNS) * kLS + e % kNS] = 0.f;
   }
   const int nch = (sq.len + C - 1) / C;
-  for (int c = 0; c < nch; ++c) {
+  // the next chunk's K rows, V slice, T and (b, gamma) are loaded while this one is computed
+  TileLoad<E, C, DK, LK> lk;
+  TileLoad<E, C, kNS, kLS> lv;
+  TileLoad<float, C, C, LC> lt;
+  TileLoad<float, 2, C, C> lb;  // b then gamma (adjacent in the record)
+  auto issue = [&](int c) {
     const int rows = min(C, sq.len - c * C);
     const long long row0 = sq.row0 + (long long)c * C;
+    const float *rec = p.prep + ((size_t)h * p.nslot + sq.slot0 + c) * R::FLOATS;
+    lk.issue(p.k, row0, rows, 0, DK);
+    lv.issue(p.v, row0, rows, col0, p.DV);
+    lt.issue(rec + R::TM, 0, C, 0, C);
+    lb.issue(rec + R::BETA, 0, 2, 0, C);
+  };
+  if (nch > 0) issue(0);
+  for (int c = 0; c < nch; ++c) {
     const size_t slot = (size_t)h * p.nslot + sq.slot0 + c;
-    const float *rec = p.prep + slot * R::FLOATS;
     __syncthreads();
     float *st = p.states + slot * DK * p.DV;
     for (int e = t; e < DK * kNS; e += kBT) {
       const int i = e / kNS, j = e % kNS;
       st[(size_t)i * p.DV + col0 + j] = sS[i * kLS + j];
     }
-    load_rows<E, C, DK, LK>(sK, p.k, row0, rows, 0, DK);
-    load_rows<E, C, kNS, kLS>(sV, p.v, row0, rows, col0, p.DV);
-    for (int e = t; e < C * C; e += kBT) sT[(e / C) * LC + e % C] = rec[R::TM + e];
-    for (int r = t; r < C; r += kBT) {
-      sb[r] = rec[R::BETA + r];
-      sgam[r] = rec[R::GAM + r];
-    }
+    lk.put(sK);
+    lv.put(sV);
+    lt.put(sT);
+    lb.put(sb);  // sb and sgam are adjacent in LDS: rows of stride C
+    if (c + 1 < nch) issue(c + 1);
     __syncthreads();
     // X = V - Diag(Gam) K S, kept as Diag(b) X
     for (int e = t; e < C * kNS; e += kBT) {
@@ -305,33 +352,44 @@ __global__ __launch_bounds__(kBT) void kla_bwd_dstates_kernel(BwdParams p) {
   const int col0 = js * kNS;
   const SeqLoc sq = seq_loc(p, n, h, C);
   const size_t sbase = ((size_t)n * p.H + h) * DK * p.DV;
-  for (int e = t; e < DK * kNS; e += kBT) {
-    const int i = e / kNS, j = e % kNS;
-    sS[i * kLS + j] = p.dsfin ? p.dsfin[sbase + (size_t)i * p.DV + col0 + j] : 0.f;
+  if (p.dsfin) {
+    load_rows<float, DK, kNS, kLS>(sS, p.dsfin + sbase, 0, DK, col0, p.DV);
+  } else {
+    for (int e = t; e < DK * kNS; e += kBT) sS[(e / kNS) * kLS + e % kNS] = 0.f;
   }
   const int nch = (sq.len + C - 1) / C;
-  for (int c = nch - 1; c >= 0; --c) {
+  // the previous chunk's inputs are loaded while this one is computed
+  TileLoad<E, C, DK, LK> lk, lq;
+  TileLoad<E, C, kNS, kLS> lo;
+  TileLoad<float, C, C, LC> lt, lp;
+  TileLoad<float, 2, C, C> lb;  // b then gamma
+  auto issue = [&](int c) {
     const int rows = min(C, sq.len - c * C);
     const long long row0 = sq.row0 + (long long)c * C;
+    const float *rec = p.prep + ((size_t)h * p.nslot + sq.slot0 + c) * R::FLOATS;
+    lk.issue(p.k, row0, rows, 0, DK);
+    lq.issue(p.q, row0, rows, 0, DK);
+    lo.issue(p.dout, row0, rows, col0, p.DV);
+    lt.issue(rec + R::TM, 0, C, 0, C);
+    lp.issue(rec + R::PM, 0, C, 0, C);
+    lb.issue(rec + R::BETA, 0, 2, 0, C);
+  };
+  if (nch > 0) issue(nch - 1);
+  for (int c = nch - 1; c >= 0; --c) {
     const size_t slot = (size_t)h * p.nslot + sq.slot0 + c;
-    const float *rec = p.prep + slot * R::FLOATS;
     __syncthreads();
     float *dst = p.dstates + slot * DK * p.DV;
     for (int e = t; e < DK * kNS; e += kBT) {
       const int i = e / kNS, j = e % kNS;
       dst[(size_t)i * p.DV + col0 + j] = sS[i * kLS + j];
     }
-    load_rows<E, C, DK, LK>(sK, p.k, row0, rows, 0, DK);
-    load_rows<E, C, DK, LK>(sQ, p.q, row0, rows, 0, DK);
-    load_rows<E, C, kNS, kLS>(sO, p.dout, row0, rows, col0, p.DV);
-    for (int e = t; e < C * C; e += kBT) {
-      sT[(e / C) * LC + e % C] = rec[R::TM + e];
-      sP[(e / C) * LC + e % C] = rec[R::PM + e];
-    }
-    for (int r = t; r < C; r += kBT) {
-      sb[r] = rec[R::BETA + r];
-      sgam[r] = rec[R::GAM + r];
-    }
+    lk.put(sK);
+    lq.put(sQ);
+    lo.put(sO);
+    lt.put(sT);
+    lp.put(sP);
+    lb.put(sb);
+    if (c > 0) issue(c - 1);
     __syncthreads();
     const float gC = sgam[C - 1];
     // dU = P^T dO + Diag(d) K dS'
@@ -431,16 +489,22 @@ __global__ __launch_bounds__(kBT) void kla_bwd_grads_kernel(BwdParams p) {
   const float *Sg = p.states + sidx * DK * p.DV;
   const float *Dg = p.dstates + sidx * DK * p.DV;
 
-  load_rows<E, C, DK, LK>(sK, p.k, cl.row0, rows, 0, DK);
-  load_rows<E, C, DK, LK>(sQ, p.q, cl.row0, rows, 0, DK);
-  for (int e = t; e < C * C; e += kBT) {
-    sT[(e / C) * LC + e % C] = rec[R::TM + e];
-    sP[(e / C) * LC + e % C] = rec[R::PM + e];
+  {
+    TileLoad<E, C, DK, LK> lk, lq;
+    TileLoad<float, C, C, LC> lt, lp;
+    TileLoad<float, 3, C, C> lb;  // b, gamma, ||k||^2 (adjacent in the record and in LDS)
+    lk.issue(p.k, cl.row0, rows, 0, DK);
+    lq.issue(p.q, cl.row0, rows, 0, DK);
+    lt.issue(rec + R::TM, 0, C, 0, C);
+    lp.issue(rec + R::PM, 0, C, 0, C);
+    lb.issue(rec + R::BETA, 0, 3, 0, C);
+    lk.put(sK);
+    lq.put(sQ);
+    lt.put(sT);
+    lp.put(sP);
+    lb.put(sb);
   }
   for (int r = t; r < C; r += kBT) {
-    sb[r] = rec[R::BETA + r];
-    sgam[r] = rec[R::GAM + r];
-    snrm[r] = rec[R::NRM + r];
     seta[r] = r < rows ? ld<E>(p.eta, cl.row0 + r) : 0.f;
     sdgam[r] = 0.f;
     sdd[r] = 0.f;
@@ -462,19 +526,30 @@ __global__ __launch_bounds__(kBT) void kla_bwd_grads_kernel(BwdParams p) {
   }
   float gcp = 0.f;  // partial <S, dS'>
 
+  // slice js + 1 of S, dS', V and dO is loaded while slice js is computed
+  TileLoad<float, DK, kNS, kLS> ls, ld_;
+  TileLoad<E, C, kNS, kLS> lv, lo;
+  auto issue = [&](int js) {
+    const int col0 = js * kNS;
+    ls.issue(Sg, 0, DK, col0, p.DV);
+    ld_.issue(Dg, 0, DK, col0, p.DV);
+    lv.issue(p.v, cl.row0, rows, col0, p.DV);
+    lo.issue(p.dout, cl.row0, rows, col0, p.DV);
+  };
+  issue(0);
   for (int js = 0; js < p.nsl; ++js) {
     const int col0 = js * kNS;
     __syncthreads();
+    ls.put(sS);
+    ld_.put(sD);
+    lv.put(sV);
+    lo.put(sO);
+    if (js + 1 < p.nsl) issue(js + 1);
+    __syncthreads();
     for (int e = t; e < DK * kNS; e += kBT) {
       const int i = e / kNS, j = e % kNS;
-      const float s = Sg[(size_t)i * p.DV + col0 + j], d = Dg[(size_t)i * p.DV + col0 + j];
-      sS[i * kLS + j] = s;
-      sD[i * kLS + j] = d;
-      gcp = fmaf(s, d, gcp);
+      gcp = fmaf(sS[i * kLS + j], sD[i * kLS + j], gcp);
     }
-    load_rows<E, C, kNS, kLS>(sV, p.v, cl.row0, rows, col0, p.DV);
-    load_rows<E, C, kNS, kLS>(sO, p.dout, cl.row0, rows, col0, p.DV);
-    __syncthreads();
     // entries (r = rb*TC + a, j = cb) of the C x 16 slice products
     float ks[TC], qs[TC], kd[TC], u[TC];
 #pragma unroll
