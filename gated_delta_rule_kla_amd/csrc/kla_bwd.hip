@@ -16,7 +16,8 @@
 //   S' = Gam_C S + K^T Diag(d) U               then dQ, dK, db, dgamma from A, P, X, O, S'
 //
 // Four kernels, through a caller-provided workspace:
-//   prep     (chunk, head) in parallel: b, gamma, ||k||^2, T and P into the workspace.
+//   prep     (chunk, head) in parallel: b, gamma, ||k||^2, T, P and K K^T . E into the
+//            workspace.
 //   states   (sequence, head, 16 state columns): the chunk-start states, in order.
 //   dstates  (sequence, head, 16 state columns): dS' of every chunk, in reverse order;
 //            the gradient of the initial state is what is left at the start.
@@ -34,7 +35,8 @@ namespace kla {
 
 namespace {
 
-constexpr int kBT = 256;  // threads per workgroup in every backward kernel
+constexpr int kBT = 256;  // threads per workgroup of the gradient kernel
+constexpr int kNT = 512;  // threads per workgroup of the prep and the two scan kernels
 constexpr int kNS = 16;   // state columns per slice
 constexpr int kLS = kNS + 1;
 
@@ -54,7 +56,8 @@ struct BwdParams {
 template <int C> struct PrepRec {
   static constexpr int TM = 0;            // T = (I + A)^-1, C x C row-major
   static constexpr int PM = C * C;        // P = lower(Q K^T . E), C x C row-major
-  static constexpr int BETA = 2 * C * C;  // b_r
+  static constexpr int GE = 2 * C * C;    // lower(K K^T . E), C x C row-major
+  static constexpr int BETA = 3 * C * C;  // b_r
   static constexpr int GAM = BETA + C;    // gamma_r (rows past the chunk's end hold the last value)
   static constexpr int NRM = GAM + C;     // ||k_r||^2
   static constexpr int FLOATS = NRM + 2 * C;
@@ -114,19 +117,19 @@ __device__ __forceinline__ float ld(const void *base, long long i) {
 // 16-byte vectors: issue() loads this thread's vectors into registers (all of
 // them before any is used, so their latencies overlap), put() widens them to
 // fp32 into LDS rows of stride LD.  Rows at or past `rows` read as zero.
-template <typename E, int R, int D, int LD>
+template <typename E, int R, int D, int LD, int NT = kBT>
 struct TileLoad {
   static constexpr int EPV = 16 / (int)sizeof(E);  // elements per vector
   static constexpr int VPR = D / EPV;              // vectors per row
   static constexpr int NV = R * VPR;
-  static constexpr int PER = (NV + kBT - 1) / kBT;
+  static constexpr int PER = (NV + NT - 1) / NT;
   static_assert(D % EPV == 0, "rows are whole 16-byte vectors");
   uint4 v[PER];
 
   __device__ __forceinline__ void issue(const void *src, long long row0, int rows, int col0, long long ld) {
 #pragma unroll
     for (int m = 0; m < PER; ++m) {
-      const int idx = (int)threadIdx.x + m * kBT;
+      const int idx = (int)threadIdx.x + m * NT;
       const int r = idx / VPR, c = (idx % VPR) * EPV;
       v[m] = make_uint4(0u, 0u, 0u, 0u);
       if (idx < NV && r < rows)
@@ -136,7 +139,7 @@ struct TileLoad {
   __device__ __forceinline__ void put(float *dst) const {
 #pragma unroll
     for (int m = 0; m < PER; ++m) {
-      const int idx = (int)threadIdx.x + m * kBT;
+      const int idx = (int)threadIdx.x + m * NT;
       if (idx < NV) {
         const int r = idx / VPR, c = (idx % VPR) * EPV;
         const E *e = reinterpret_cast<const E *>(&v[m]);
@@ -149,10 +152,10 @@ struct TileLoad {
 
 // Rows [0, rows) of a [*, D] array from row `row0` into LDS with row stride LD,
 // zeros past `rows` (one batch of vector loads).
-template <typename E, int R, int D, int LD>
+template <typename E, int R, int D, int LD, int NT = kBT>
 __device__ __forceinline__ void load_rows(float *dst, const void *src, long long row0, int rows, int col0,
                                           long long ld_src) {
-  TileLoad<E, R, D, LD> tl;
+  TileLoad<E, R, D, LD, NT> tl;
   tl.issue(src, row0, rows, col0, ld_src);
   tl.put(dst);
 }
@@ -168,7 +171,7 @@ struct PrepSmem {
 };
 
 template <typename E, int C, int DK>
-__global__ __launch_bounds__(kBT) void kla_bwd_prep_kernel(BwdParams p) {
+__global__ __launch_bounds__(kNT) void kla_bwd_prep_kernel(BwdParams p) {
   using L = PrepSmem<E, C, DK>;
   using R = PrepRec<C>;
   constexpr int LK = L::LK, LC = L::LC;
@@ -180,14 +183,14 @@ __global__ __launch_bounds__(kBT) void kla_bwd_prep_kernel(BwdParams p) {
   if (cl.rows == 0) return;  // uniform: no chunk behind this slot
   const int rows = cl.rows;
 
-  load_rows<E, C, DK, LK>(sK, p.k, cl.row0, rows, 0, DK);
-  load_rows<E, C, DK, LK>(sQ, p.q, cl.row0, rows, 0, DK);
-  for (int r = t; r < C; r += kBT) {
+  load_rows<E, C, DK, LK, kNT>(sK, p.k, cl.row0, rows, 0, DK);
+  load_rows<E, C, DK, LK, kNT>(sQ, p.q, cl.row0, rows, 0, DK);
+  for (int r = t; r < C; r += kNT) {
     sg[r] = r < rows ? ld<E>(p.g, cl.row0 + r) : 0.f;
     sb[r] = r < rows ? ld<E>(p.eta, cl.row0 + r) : 0.f;  // eta (or b) for now
   }
   __syncthreads();
-  for (int r = t; r < C; r += kBT) {
+  for (int r = t; r < C; r += kNT) {
     float n = 0.f;
     for (int i = 0; i < DK; ++i) n = fmaf(sK[r * LK + i], sK[r * LK + i], n);
     snrm[r] = n;
@@ -202,9 +205,9 @@ __global__ __launch_bounds__(kBT) void kla_bwd_prep_kernel(BwdParams p) {
   }
   __syncthreads();
   float *rec = p.prep + ((size_t)h * p.nslot + slot) * R::FLOATS;
-  for (int e = t; e < C * C; e += kBT) {
+  for (int e = t; e < C * C; e += kNT) {
     const int r = e / C, s = e % C;
-    float a = 0.f, pv = 0.f;
+    float a = 0.f, pv = 0.f, ge = 0.f;
     if (s <= r) {
       float gkk = 0.f, gqk = 0.f;
       for (int i = 0; i < DK; ++i) {
@@ -213,11 +216,13 @@ __global__ __launch_bounds__(kBT) void kla_bwd_prep_kernel(BwdParams p) {
       }
       const float ex = __expf(sgam[r] - sgam[s]);
       pv = gqk * ex;
+      ge = gkk * ex;
       if (s < r) a = sb[r] * gkk * ex;
     }
     sA[r * LC + s] = a;
     sT[r * LC + s] = r == s ? 1.f : 0.f;
     rec[R::PM + e] = pv;
+    rec[R::GE + e] = ge;
   }
   __syncthreads();
   // T[r][j] = -sum_{j <= s < r} A[r][s] T[s][j] below the unit diagonal: one column
@@ -231,8 +236,8 @@ __global__ __launch_bounds__(kBT) void kla_bwd_prep_kernel(BwdParams p) {
     }
   }
   __syncthreads();
-  for (int e = t; e < C * C; e += kBT) rec[R::TM + e] = sT[(e / C) * LC + e % C];
-  for (int r = t; r < C; r += kBT) {
+  for (int e = t; e < C * C; e += kNT) rec[R::TM + e] = sT[(e / C) * LC + e % C];
+  for (int r = t; r < C; r += kNT) {
     rec[R::BETA + r] = sb[r];
     rec[R::GAM + r] = sgam[r];
     rec[R::NRM + r] = snrm[r];
@@ -250,7 +255,7 @@ struct StatesSmem {
 };
 
 template <typename E, int C, int DK>
-__global__ __launch_bounds__(kBT) void kla_bwd_states_kernel(BwdParams p) {
+__global__ __launch_bounds__(kNT) void kla_bwd_states_kernel(BwdParams p) {
   using L = StatesSmem<C, DK>;
   using R = PrepRec<C>;
   constexpr int LK = L::LK, LC = L::LC;
@@ -264,16 +269,16 @@ __global__ __launch_bounds__(kBT) void kla_bwd_states_kernel(BwdParams p) {
   const SeqLoc sq = seq_loc(p, n, h, C);
   const size_t sbase = ((size_t)n * p.H + h) * DK * p.DV;
   if (p.s0) {
-    load_rows<float, DK, kNS, kLS>(sS, p.s0 + sbase, 0, DK, col0, p.DV);
+    load_rows<float, DK, kNS, kLS, kNT>(sS, p.s0 + sbase, 0, DK, col0, p.DV);
   } else {
-    for (int e = t; e < DK * kNS; e += kBT) sS[(e / kNS) * kLS + e % kNS] = 0.f;
+    for (int e = t; e < DK * kNS; e += kNT) sS[(e / kNS) * kLS + e % kNS] = 0.f;
   }
   const int nch = (sq.len + C - 1) / C;
   // the next chunk's K rows, V slice, T and (b, gamma) are loaded while this one is computed
-  TileLoad<E, C, DK, LK> lk;
-  TileLoad<E, C, kNS, kLS> lv;
-  TileLoad<float, C, C, LC> lt;
-  TileLoad<float, 2, C, C> lb;  // b then gamma (adjacent in the record)
+  TileLoad<E, C, DK, LK, kNT> lk;
+  TileLoad<E, C, kNS, kLS, kNT> lv;
+  TileLoad<float, C, C, LC, kNT> lt;
+  TileLoad<float, 2, C, C, kNT> lb;  // b then gamma (adjacent in the record)
   auto issue = [&](int c) {
     const int rows = min(C, sq.len - c * C);
     const long long row0 = sq.row0 + (long long)c * C;
@@ -288,7 +293,7 @@ __global__ __launch_bounds__(kBT) void kla_bwd_states_kernel(BwdParams p) {
     const size_t slot = (size_t)h * p.nslot + sq.slot0 + c;
     __syncthreads();
     float *st = p.states + slot * DK * p.DV;
-    for (int e = t; e < DK * kNS; e += kBT) {
+    for (int e = t; e < DK * kNS; e += kNT) {
       const int i = e / kNS, j = e % kNS;
       st[(size_t)i * p.DV + col0 + j] = sS[i * kLS + j];
     }
@@ -299,7 +304,7 @@ __global__ __launch_bounds__(kBT) void kla_bwd_states_kernel(BwdParams p) {
     if (c + 1 < nch) issue(c + 1);
     __syncthreads();
     // X = V - Diag(Gam) K S, kept as Diag(b) X
-    for (int e = t; e < C * kNS; e += kBT) {
+    for (int e = t; e < C * kNS; e += kNT) {
       const int r = e / kNS, j = e % kNS;
       float acc = 0.f;
       for (int i = 0; i < DK; ++i) acc = fmaf(sK[r * LK + i], sS[i * kLS + j], acc);
@@ -308,7 +313,7 @@ __global__ __launch_bounds__(kBT) void kla_bwd_states_kernel(BwdParams p) {
     __syncthreads();
     // Diag(d) U with U = T Diag(b) X  (into sV)
     const float gC = sgam[C - 1];
-    for (int e = t; e < C * kNS; e += kBT) {
+    for (int e = t; e < C * kNS; e += kNT) {
       const int r = e / kNS, j = e % kNS;
       float acc = 0.f;
       for (int s = 0; s <= r; ++s) acc = fmaf(sT[r * LC + s], sX[s * kLS + j], acc);
@@ -317,7 +322,7 @@ __global__ __launch_bounds__(kBT) void kla_bwd_states_kernel(BwdParams p) {
     __syncthreads();
     // S <- Gam_C S + K^T Diag(d) U
     const float GC = __expf(gC);
-    for (int e = t; e < DK * kNS; e += kBT) {
+    for (int e = t; e < DK * kNS; e += kNT) {
       const int i = e / kNS, j = e % kNS;
       float acc = 0.f;
       for (int r = 0; r < C; ++r) acc = fmaf(sK[r * LK + i], sV[r * kLS + j], acc);
@@ -338,11 +343,11 @@ struct DStatesSmem {
 };
 
 template <typename E, int C, int DK>
-__global__ __launch_bounds__(kBT) void kla_bwd_dstates_kernel(BwdParams p) {
+__global__ __launch_bounds__(kNT) void kla_bwd_dstates_kernel(BwdParams p) {
   using L = DStatesSmem<C, DK>;
   using R = PrepRec<C>;
   constexpr int LK = L::LK, LC = L::LC;
-  constexpr int PER = C * kNS / kBT > 0 ? (C * kNS + kBT - 1) / kBT : 1;
+  constexpr int PER = C * kNS / kNT > 0 ? (C * kNS + kNT - 1) / kNT : 1;
   __shared__ float sm[L::FLOATS];
   float *sK = sm + L::K, *sQ = sm + L::Q, *sT = sm + L::T, *sP = sm + L::P, *sO = sm + L::O;
   float *sU = sm + L::U, *sS = sm + L::S, *sb = sm + L::BETA, *sgam = sm + L::GAM;
@@ -353,16 +358,16 @@ __global__ __launch_bounds__(kBT) void kla_bwd_dstates_kernel(BwdParams p) {
   const SeqLoc sq = seq_loc(p, n, h, C);
   const size_t sbase = ((size_t)n * p.H + h) * DK * p.DV;
   if (p.dsfin) {
-    load_rows<float, DK, kNS, kLS>(sS, p.dsfin + sbase, 0, DK, col0, p.DV);
+    load_rows<float, DK, kNS, kLS, kNT>(sS, p.dsfin + sbase, 0, DK, col0, p.DV);
   } else {
-    for (int e = t; e < DK * kNS; e += kBT) sS[(e / kNS) * kLS + e % kNS] = 0.f;
+    for (int e = t; e < DK * kNS; e += kNT) sS[(e / kNS) * kLS + e % kNS] = 0.f;
   }
   const int nch = (sq.len + C - 1) / C;
   // the previous chunk's inputs are loaded while this one is computed
-  TileLoad<E, C, DK, LK> lk, lq;
-  TileLoad<E, C, kNS, kLS> lo;
-  TileLoad<float, C, C, LC> lt, lp;
-  TileLoad<float, 2, C, C> lb;  // b then gamma
+  TileLoad<E, C, DK, LK, kNT> lk, lq;
+  TileLoad<E, C, kNS, kLS, kNT> lo;
+  TileLoad<float, C, C, LC, kNT> lt, lp;
+  TileLoad<float, 2, C, C, kNT> lb;  // b then gamma
   auto issue = [&](int c) {
     const int rows = min(C, sq.len - c * C);
     const long long row0 = sq.row0 + (long long)c * C;
@@ -379,7 +384,7 @@ __global__ __launch_bounds__(kBT) void kla_bwd_dstates_kernel(BwdParams p) {
     const size_t slot = (size_t)h * p.nslot + sq.slot0 + c;
     __syncthreads();
     float *dst = p.dstates + slot * DK * p.DV;
-    for (int e = t; e < DK * kNS; e += kBT) {
+    for (int e = t; e < DK * kNS; e += kNT) {
       const int i = e / kNS, j = e % kNS;
       dst[(size_t)i * p.DV + col0 + j] = sS[i * kLS + j];
     }
@@ -393,7 +398,7 @@ __global__ __launch_bounds__(kBT) void kla_bwd_dstates_kernel(BwdParams p) {
     __syncthreads();
     const float gC = sgam[C - 1];
     // dU = P^T dO + Diag(d) K dS'
-    for (int e = t; e < C * kNS; e += kBT) {
+    for (int e = t; e < C * kNS; e += kNT) {
       const int r = e / kNS, j = e % kNS;
       float a = 0.f, b = 0.f;
       for (int s = r; s < C; ++s) a = fmaf(sP[s * LC + r], sO[s * kLS + j], a);
@@ -405,7 +410,7 @@ __global__ __launch_bounds__(kBT) void kla_bwd_dstates_kernel(BwdParams p) {
     float gdx[PER], gdo[PER];
 #pragma unroll
     for (int m = 0; m < PER; ++m) {
-      const int e = t + m * kBT;
+      const int e = t + m * kNT;
       gdx[m] = gdo[m] = 0.f;
       if (e < C * kNS) {
         const int r = e / kNS, j = e % kNS;
@@ -419,7 +424,7 @@ __global__ __launch_bounds__(kBT) void kla_bwd_dstates_kernel(BwdParams p) {
     __syncthreads();
 #pragma unroll
     for (int m = 0; m < PER; ++m) {
-      const int e = t + m * kBT;
+      const int e = t + m * kNT;
       if (e < C * kNS) {
         const int r = e / kNS, j = e % kNS;
         sU[r * kLS + j] = gdx[m];
@@ -429,7 +434,7 @@ __global__ __launch_bounds__(kBT) void kla_bwd_dstates_kernel(BwdParams p) {
     __syncthreads();
     // dS = Gam_C dS' + (Diag(Gam) Q)^T dO - (Diag(Gam) K)^T dX
     const float GC = __expf(gC);
-    for (int e = t; e < DK * kNS; e += kBT) {
+    for (int e = t; e < DK * kNS; e += kNT) {
       const int i = e / kNS, j = e % kNS;
       float acc = 0.f;
       for (int r = 0; r < C; ++r)
@@ -439,7 +444,7 @@ __global__ __launch_bounds__(kBT) void kla_bwd_dstates_kernel(BwdParams p) {
   }
   if (p.ds0) {
     __syncthreads();
-    for (int e = t; e < DK * kNS; e += kBT) {
+    for (int e = t; e < DK * kNS; e += kNT) {
       const int i = e / kNS, j = e % kNS;
       p.ds0[sbase + (size_t)i * p.DV + col0 + j] = sS[i * kLS + j];
     }
@@ -451,7 +456,9 @@ __global__ __launch_bounds__(kBT) void kla_bwd_dstates_kernel(BwdParams p) {
 // ============================================================================
 template <int C, int DK>
 struct GradSmem {
-  static constexpr int LK = DK + 1, LC = C + 1;
+  // K and Q rows 16-byte aligned (read as float4 along a row); 4 rows of a wave
+  // land on distinct banks
+  static constexpr int LK = DK + 4, LC = C + 1;
   static constexpr int K = 0, Q = K + C * LK, T = Q + C * LK, P = T + C * LC;  // P, later Y, dEE
   static constexpr int SL = P + C * LC;                                      // slice region
   static constexpr int S = SL, D = S + DK * kLS, V = D + DK * kLS, O = V + C * kLS, X = O + C * kLS;
@@ -556,11 +563,17 @@ __global__ __launch_bounds__(kBT) void kla_bwd_grads_kernel(BwdParams p) {
     for (int a = 0; a < TC; ++a) {
       const int r = rb * TC + a;
       float x0 = 0.f, x1 = 0.f, x2 = 0.f;
-      for (int i = 0; i < DK; ++i) {
-        const float kr = sK[r * LK + i];
-        x0 = fmaf(kr, sS[i * kLS + cb], x0);
-        x1 = fmaf(sQ[r * LK + i], sS[i * kLS + cb], x1);
-        x2 = fmaf(kr, sD[i * kLS + cb], x2);
+#pragma unroll 2
+      for (int i = 0; i < DK; i += 4) {
+        const f32x4 kr = *reinterpret_cast<const f32x4 *>(sK + r * LK + i);
+        const f32x4 qr = *reinterpret_cast<const f32x4 *>(sQ + r * LK + i);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float sv = sS[(i + u) * kLS + cb], dv = sD[(i + u) * kLS + cb];
+          x0 = fmaf(kr[u], sv, x0);
+          x1 = fmaf(qr[u], sv, x1);
+          x2 = fmaf(kr[u], dv, x2);
+        }
       }
       ks[a] = x0;
       qs[a] = x1;
@@ -641,7 +654,7 @@ __global__ __launch_bounds__(kBT) void kla_bwd_grads_kernel(BwdParams p) {
   }
 
   // ---------------- C x C stage ---------------------------------------------
-  // (the slice region now holds B1 and B2; sP's space is reused for Y, then dEE)
+  // (the slice region now holds B1 and B2; P stays in sP until dEE replaces it)
   float *B1 = sm + L::B1, *B2 = sm + L::B2;
   sred[t] = gcp;
   __syncthreads();
@@ -681,7 +694,7 @@ __global__ __launch_bounds__(kBT) void kla_bwd_grads_kernel(BwdParams p) {
 #pragma unroll
   for (int a = 0; a < TC; ++a)
 #pragma unroll
-    for (int b = 0; b < TC; ++b) sP[(rb * TC + a) * LC + cb * TC + b] = y[a][b];
+    for (int b = 0; b < TC; ++b) B1[(rb * TC + a) * LC + cb * TC + b] = y[a][b];  // Y over dW
   __syncthreads();
   // dA = -T^T Y, strictly lower
 #pragma unroll
@@ -693,14 +706,14 @@ __global__ __launch_bounds__(kBT) void kla_bwd_grads_kernel(BwdParams p) {
 #pragma unroll
     for (int a = 0; a < TC; ++a) {
       tt[a] = sT[m * LC + rb * TC + a];
-      yy[a] = sP[m * LC + cb * TC + a];
+      yy[a] = B1[m * LC + cb * TC + a];
     }
 #pragma unroll
     for (int a = 0; a < TC; ++a)
 #pragma unroll
       for (int b = 0; b < TC; ++b) y[a][b] = fmaf(tt[a], yy[b], y[a][b]);
   }
-  // per entry: dG = dA b_r E, dQK = dP E, dEE = (dA b_r G + dP QK) E, db_r += dA G E
+  // per entry: dG = dA b_r E, dQK = dP E, dEE = dA b_r (G . E) + dP P, db_r += dA (G . E)
   float dgm[TC][TC], dqk[TC][TC], dee[TC][TC], dbr[TC];
 #pragma unroll
   for (int a = 0; a < TC; ++a) {
@@ -711,18 +724,14 @@ __global__ __launch_bounds__(kBT) void kla_bwd_grads_kernel(BwdParams p) {
       const int s = cb * TC + b;
       dgm[a][b] = dqk[a][b] = dee[a][b] = 0.f;
       if (s <= r) {
-        float gkk = 0.f, gqk = 0.f;
-        for (int i = 0; i < DK; ++i) {
-          gkk = fmaf(sK[r * LK + i], sK[s * LK + i], gkk);
-          gqk = fmaf(sQ[r * LK + i], sK[s * LK + i], gqk);
-        }
         const float ex = __expf(sgam[r] - sgam[s]);
         const float dA = s < r ? -y[a][b] : 0.f;
         const float dP = B2[r * LC + s];
         dgm[a][b] = dA * sb[r] * ex;
         dqk[a][b] = dP * ex;
-        dee[a][b] = (dA * sb[r] * gkk + dP * gqk) * ex;
-        dbr[a] = fmaf(dA * gkk, ex, dbr[a]);
+        const float gE = rec[R::GE + r * C + s];
+        dee[a][b] = fmaf(dA * sb[r], gE, dP * sP[r * LC + s]);
+        dbr[a] = fmaf(dA, gE, dbr[a]);
       }
     }
   }
@@ -876,16 +885,16 @@ hipError_t launch_bwd_t(const ChunkArgs &a, const ChunkBwdArgs &b, hipStream_t s
   const unsigned seq_blocks = (unsigned)((long long)a.num_seqs * a.H * p.nsl);
   const bool tokens = (long long)a.B * a.T > 0 && p.nslot > 0;
   if (tokens) {
-    hipLaunchKernelGGL((kla_bwd_prep_kernel<E, C, DK>), dim3((unsigned)p.nslot, (unsigned)a.H), dim3(kBT), 0, st, p);
+    hipLaunchKernelGGL((kla_bwd_prep_kernel<E, C, DK>), dim3((unsigned)p.nslot, (unsigned)a.H), dim3(kNT), 0, st, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((kla_bwd_states_kernel<E, C, DK>), dim3(seq_blocks), dim3(kBT), 0, st, p);
+    hipLaunchKernelGGL((kla_bwd_states_kernel<E, C, DK>), dim3(seq_blocks), dim3(kNT), 0, st, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (seq_blocks > 0 && (tokens || p.ds0)) {
     // with no tokens this only copies dS_final (or zeros) to the initial-state gradient
-    hipLaunchKernelGGL((kla_bwd_dstates_kernel<E, C, DK>), dim3(seq_blocks), dim3(kBT), 0, st, p);
+    hipLaunchKernelGGL((kla_bwd_dstates_kernel<E, C, DK>), dim3(seq_blocks), dim3(kNT), 0, st, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -205,7 +205,8 @@ kla_status_t kla_gdn_decode_step(const void *q, const void *k, const void *v,
  *   workspace       kla_chunk_bwd_workspace_bytes(...) bytes of device memory
  *                   (16-byte aligned), owned by the caller, no initialisation
  *                   needed; holds per (chunk, head) T = (I + A)^-1, the causal
- *                   scores, the coefficient and decay vectors, the chunk-start
+ *                   scores, the decayed Gram matrix, the coefficient and decay
+ *                   vectors, the chunk-start
  *                   state and the chunk-end state gradient (fp32).
  *
  * Every pointer is 16-byte aligned device memory; gradient buffers must not
@@ -242,7 +243,7 @@ kla_status_t kla_gdn_chunk_bwd(const void *q, const void *k, const void *v,
 
 /*
  * kla_chunk_bwd_workspace_bytes -- device workspace kla_chunk_bwd and
- * kla_gdn_chunk_bwd need (host-only): per (chunk, head) 4 (2 C^2 + 4 C) bytes
+ * kla_gdn_chunk_bwd need (host-only): per (chunk, head) 4 (3 C^2 + 4 C) bytes
  * plus 8 dk dv bytes (rounded up per region).  0 when no workspace is needed
  * or for arguments kla_chunk_bwd would reject.
  */
