@@ -22,10 +22,10 @@
 //   dstates  (sequence, head, 16 state columns): dS' of every chunk, in reverse order;
 //            the gradient of the initial state is what is left at the start.
 //   grads    (chunk, head) in parallel: everything else from S, dS' and the chunk's
-//            inputs, streaming the state columns 16 at a time.
-// All arithmetic is fp32 FMA through padded LDS rows (odd row strides keep the
-// transposed reads free of bank conflicts); there are no atomics, so results are
-// deterministic run to run.
+//            inputs, streaming the state columns 16 at a time, on fp32 MFMA tiles.
+// All arithmetic is fp32 (vector FMA in the prep and scan kernels, 16x16x4 fp32
+// MFMA in the gradient kernel) through padded LDS rows; there are no atomics, so
+// results are deterministic run to run.
 #include <algorithm>
 
 #include "kla_common.h"
@@ -454,12 +454,16 @@ __global__ __launch_bounds__(kNT) void kla_bwd_dstates_kernel(BwdParams p) {
 // ============================================================================
 // grads: dq, dk, dv, dg, deta of one (chunk, head)
 // ============================================================================
+// On 16x16x4 fp32 MFMA tiles: lane l supplies A[l%16][l/16] and B[l/16][l%16] of
+// a 16x4 by 4x16 product; accumulator element i of lane l is row 4(l/16)+i,
+// column l%16.  Wave w owns row tile w (16 chunk rows) of every product and every
+// accumulator, so the per-slice phases need only two barriers.
 template <int C, int DK>
 struct GradSmem {
-  // K and Q rows 16-byte aligned (read as float4 along a row); 4 rows of a wave
-  // land on distinct banks
+  // K and Q rows 16-byte aligned; a 16-row by 4-column operand read lands on 64
+  // distinct banks (row stride = 4 mod 64)
   static constexpr int LK = DK + 4, LC = C + 1;
-  static constexpr int K = 0, Q = K + C * LK, T = Q + C * LK, P = T + C * LC;  // P, later Y, dEE
+  static constexpr int K = 0, Q = K + C * LK, T = Q + C * LK, P = T + C * LC;  // P, later dEE
   static constexpr int SL = P + C * LC;                                      // slice region
   static constexpr int S = SL, D = S + DK * kLS, V = D + DK * kLS, O = V + C * kLS, X = O + C * kLS;
   static constexpr int U = X + C * kLS, DU = U + C * kLS, DX = DU + C * kLS, SL_END = DX + C * kLS;
@@ -472,13 +476,17 @@ struct GradSmem {
   static constexpr int FLOATS = RED + kBT;
 };
 
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
 template <typename E, int C, int DK>
 __global__ __launch_bounds__(kBT) void kla_bwd_grads_kernel(BwdParams p) {
   using L = GradSmem<C, DK>;
   using R = PrepRec<C>;
   constexpr int LK = L::LK, LC = L::LC;
-  constexpr int TC = C / 16, TK = DK / 16;  // per-thread rows (C) and columns (C or DK)
-  static_assert(C % 16 == 0 && DK % 16 == 0, "16 x 16 thread grid");
+  constexpr int NRT = C / 16, NKT = DK / 16, NW = kBT / 64;
+  static_assert(C % 16 == 0 && DK % 16 == 0 && NRT <= NW, "one 16-row tile per wave at most");
   __shared__ float sm[L::FLOATS];
   float *sK = sm + L::K, *sQ = sm + L::Q, *sT = sm + L::T, *sP = sm + L::P;
   float *sS = sm + L::S, *sD = sm + L::D, *sV = sm + L::V, *sO = sm + L::O, *sX = sm + L::X;
@@ -490,7 +498,10 @@ __global__ __launch_bounds__(kBT) void kla_bwd_grads_kernel(BwdParams p) {
   const ChunkLoc cl = chunk_loc(p, slot, h, C);
   if (cl.rows == 0) return;  // uniform
   const int rows = cl.rows;
-  const int rb = t / 16, cb = t % 16;  // 16 x 16 thread grid
+  const int w = t >> 6, lane = t & 63, lr = lane & 15, lg = lane >> 4;
+  const int a = w;                 // this wave's row tile
+  const bool own = a < NRT;        // (uniform per wave)
+  const int ra = 16 * a + lr;      // operand row of this lane
   const size_t sidx = (size_t)h * p.nslot + slot;
   const float *rec = p.prep + sidx * R::FLOATS;
   const float *Sg = p.states + sidx * DK * p.DV;
@@ -511,26 +522,22 @@ __global__ __launch_bounds__(kBT) void kla_bwd_grads_kernel(BwdParams p) {
     lp.put(sP);
     lb.put(sb);
   }
+  const float gC = rec[R::GAM + C - 1];
   for (int r = t; r < C; r += kBT) {
     seta[r] = r < rows ? ld<E>(p.eta, cl.row0 + r) : 0.f;
     sdgam[r] = 0.f;
     sdd[r] = 0.f;
-  }
-  const float gC = rec[R::GAM + C - 1];
-  for (int r = t; r < C; r += kBT) {
     const float gr = rec[R::GAM + r];
     sGm[r] = __expf(gr);
     sdec[r] = __expf(gC - gr);
   }
 
-  float accW[TC][TC], accP[TC][TC], accQ[TC][TK], accK[TC][TK];
+  const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+  f32x4 accW[NRT], accP[NRT], accQ[NKT], accK[NKT];
 #pragma unroll
-  for (int a = 0; a < TC; ++a) {
+  for (int b = 0; b < NRT; ++b) accW[b] = accP[b] = z4;
 #pragma unroll
-    for (int b = 0; b < TC; ++b) accW[a][b] = accP[a][b] = 0.f;
-#pragma unroll
-    for (int b = 0; b < TK; ++b) accQ[a][b] = accK[a][b] = 0.f;
-  }
+  for (int b = 0; b < NKT; ++b) accQ[b] = accK[b] = z4;
   float gcp = 0.f;  // partial <S, dS'>
 
   // slice js + 1 of S, dS', V and dO is loaded while slice js is computed
@@ -553,101 +560,96 @@ __global__ __launch_bounds__(kBT) void kla_bwd_grads_kernel(BwdParams p) {
     lo.put(sO);
     if (js + 1 < p.nsl) issue(js + 1);
     __syncthreads();
-    for (int e = t; e < DK * kNS; e += kBT) {
-      const int i = e / kNS, j = e % kNS;
-      gcp = fmaf(sS[i * kLS + j], sD[i * kLS + j], gcp);
-    }
-    // entries (r = rb*TC + a, j = cb) of the C x 16 slice products
-    float ks[TC], qs[TC], kd[TC], u[TC];
-#pragma unroll
-    for (int a = 0; a < TC; ++a) {
-      const int r = rb * TC + a;
-      float x0 = 0.f, x1 = 0.f, x2 = 0.f;
-#pragma unroll 2
-      for (int i = 0; i < DK; i += 4) {
-        const f32x4 kr = *reinterpret_cast<const f32x4 *>(sK + r * LK + i);
-        const f32x4 qr = *reinterpret_cast<const f32x4 *>(sQ + r * LK + i);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const float sv = sS[(i + u) * kLS + cb], dv = sD[(i + u) * kLS + cb];
-          x0 = fmaf(kr[u], sv, x0);
-          x1 = fmaf(qr[u], sv, x1);
-          x2 = fmaf(kr[u], dv, x2);
-        }
+    for (int e = t; e < DK * kNS; e += kBT) gcp = fmaf(sS[(e / kNS) * kLS + e % kNS], sD[(e / kNS) * kLS + e % kNS], gcp);
+    // (A) K S, Q S, K dS' for this wave's rows; X = V - Diag(Gam) K S
+    f32x4 ks = z4, qs = z4, kd = z4;
+    if (own) {
+#pragma unroll 4
+      for (int k0 = 0; k0 < DK; k0 += 4) {
+        const int kk = k0 + lg;
+        const float ka = sK[ra * LK + kk], qa = sQ[ra * LK + kk];
+        const float sv = sS[kk * kLS + lr], dv = sD[kk * kLS + lr];
+        ks = mfma4(ka, sv, ks);
+        qs = mfma4(qa, sv, qs);
+        kd = mfma4(ka, dv, kd);
       }
-      ks[a] = x0;
-      qs[a] = x1;
-      kd[a] = x2;
-      sX[r * kLS + cb] = sV[r * kLS + cb] - sGm[r] * x0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * a + 4 * lg + i;
+        sX[r * kLS + lr] = sV[r * kLS + lr] - sGm[r] * ks[i];
+      }
     }
     __syncthreads();
-    // U = T Diag(b) X;  dU = P^T dO + Diag(d) K dS'
+    // (B) U = T Diag(b) X;  dU = P^T dO + Diag(d) K dS'   (T, P lower triangular)
+    f32x4 u = z4, du = z4;
+    if (own) {
+      for (int k0 = 0; k0 < 16 * (a + 1); k0 += 4) {
+        const int s_ = k0 + lg;
+        u = mfma4(sT[ra * LC + s_] * sb[s_], sX[s_ * kLS + lr], u);
+      }
+      for (int k0 = 16 * a; k0 < C; k0 += 4) {
+        const int s_ = k0 + lg;
+        du = mfma4(sP[s_ * LC + ra], sO[s_ * kLS + lr], du);
+      }
 #pragma unroll
-    for (int a = 0; a < TC; ++a) {
-      const int r = rb * TC + a;
-      float x0 = 0.f, x1 = 0.f;
-      for (int s = 0; s <= r; ++s) x0 = fmaf(sT[r * LC + s] * sb[s], sX[s * kLS + cb], x0);
-      for (int s = r; s < C; ++s) x1 = fmaf(sP[s * LC + r], sO[s * kLS + cb], x1);
-      u[a] = x0;
-      sU[r * kLS + cb] = x0;
-      sdU[r * kLS + cb] = fmaf(sdec[r], kd[a], x1);
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * a + 4 * lg + i;
+        du[i] = fmaf(sdec[r], kd[i], du[i]);
+        sU[r * kLS + lr] = u[i];
+        sdU[r * kLS + lr] = du[i];
+      }
     }
     __syncthreads();
-    // dX = Diag(b) T^T dU (= dV); row sums for dGam and dd
+    if (own) {
+      // (C) dX = Diag(b) T^T dU (= dV); row sums for dGam and dd
+      f32x4 dx = z4;
+      for (int k0 = 16 * a; k0 < C; k0 += 4) {
+        const int s_ = k0 + lg;
+        dx = mfma4(sT[s_ * LC + ra], sdU[s_ * kLS + lr], dx);
+      }
+      float pg[4], pd[4];
 #pragma unroll
-    for (int a = 0; a < TC; ++a) {
-      const int r = rb * TC + a;
-      float x0 = 0.f;
-      for (int s = r; s < C; ++s) x0 = fmaf(sT[s * LC + r], sdU[s * kLS + cb], x0);
-      const float dx = sb[r] * x0;
-      sdX[r * kLS + cb] = dx;
-      if (r < rows)
-        static_cast<E *>(p.dv)[(cl.row0 + r) * p.DV + col0 + cb] = Elem<E>::from_f32(dx);
-      float pg = qs[a] * sO[r * kLS + cb] - ks[a] * dx;
-      float pd = kd[a] * u[a];
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * a + 4 * lg + i;
+        dx[i] *= sb[r];
+        sdX[r * kLS + lr] = dx[i];
+        if (r < rows) static_cast<E *>(p.dv)[(cl.row0 + r) * p.DV + col0 + lr] = Elem<E>::from_f32(dx[i]);
+        pg[i] = qs[i] * sO[r * kLS + lr] - ks[i] * dx[i];
+        pd[i] = kd[i] * u[i];
+      }
 #pragma unroll
       for (int off = 8; off >= 1; off >>= 1) {
-        pg += __shfl_xor(pg, off);
-        pd += __shfl_xor(pd, off);
-      }
-      if (cb == 0) {
-        sdgam[r] += pg;
-        sdd[r] += pd;
-      }
-    }
-    __syncthreads();
-    // accumulate dW = dU X^T, dP = dO U^T, dQ += Diag(Gam) dO S^T and
-    // dK += -Diag(Gam) dX S^T + Diag(d) U dS'^T (row scales applied to the left factors)
-    for (int j = 0; j < kNS; ++j) {
-      float du[TC], x[TC], o[TC], oq[TC], uu[TC], dxr[TC], ur[TC];
 #pragma unroll
-      for (int a = 0; a < TC; ++a) {
-        const int r = rb * TC + a, s = cb * TC + a;
-        du[a] = sdU[r * kLS + j];
-        o[a] = sO[r * kLS + j];
-        oq[a] = sGm[r] * o[a];
-        dxr[a] = -sGm[r] * sdX[r * kLS + j];
-        ur[a] = sdec[r] * sU[r * kLS + j];
-        x[a] = sX[s * kLS + j];
-        uu[a] = sU[s * kLS + j];
+        for (int i = 0; i < 4; ++i) {
+          pg[i] += __shfl_xor(pg[i], off);
+          pd[i] += __shfl_xor(pd[i], off);
+        }
       }
-      float sv[TK], dsv[TK];
+      if (lr == 0) {
 #pragma unroll
-      for (int b = 0; b < TK; ++b) {
-        sv[b] = sS[(cb * TK + b) * kLS + j];
-        dsv[b] = sD[(cb * TK + b) * kLS + j];
+        for (int i = 0; i < 4; ++i) {
+          sdgam[16 * a + 4 * lg + i] += pg[i];
+          sdd[16 * a + 4 * lg + i] += pd[i];
+        }
       }
+      // (D) dW += dU X^T, dP += dO U^T (tiles at or below the diagonal),
+      //     dQ += Diag(Gam) dO S^T, dK += -Diag(Gam) dX S^T + Diag(d) U dS'^T
+      // (this wave's own rows of dU, dO, dX, U were written by this wave)
 #pragma unroll
-      for (int a = 0; a < TC; ++a) {
+      for (int k0 = 0; k0 < kNS; k0 += 4) {
+        const int j = k0 + lg;
+        const float adu = sdU[ra * kLS + j], ado = sO[ra * kLS + j];
+        const float aq = sGm[ra] * ado, akx = -sGm[ra] * sdX[ra * kLS + j], aku = sdec[ra] * sU[ra * kLS + j];
 #pragma unroll
-        for (int b = 0; b < TC; ++b) {
-          accW[a][b] = fmaf(du[a], x[b], accW[a][b]);
-          accP[a][b] = fmaf(o[a], uu[b], accP[a][b]);
+        for (int b = 0; b < NRT; ++b) {
+          accW[b] = mfma4(adu, sX[(16 * b + lr) * kLS + j], accW[b]);
+          if (b <= a) accP[b] = mfma4(ado, sU[(16 * b + lr) * kLS + j], accP[b]);
         }
 #pragma unroll
-        for (int b = 0; b < TK; ++b) {
-          accQ[a][b] = fmaf(oq[a], sv[b], accQ[a][b]);
-          accK[a][b] = fmaf(dxr[a], sv[b], fmaf(ur[a], dsv[b], accK[a][b]));
+        for (int b = 0; b < NKT; ++b) {
+          const float sv = sS[(16 * b + lr) * kLS + j], dv = sD[(16 * b + lr) * kLS + j];
+          accQ[b] = mfma4(aq, sv, accQ[b]);
+          accK[b] = mfma4(aku, dv, mfma4(akx, sv, accK[b]));
         }
       }
     }
@@ -658,129 +660,116 @@ __global__ __launch_bounds__(kBT) void kla_bwd_grads_kernel(BwdParams p) {
   float *B1 = sm + L::B1, *B2 = sm + L::B2;
   sred[t] = gcp;
   __syncthreads();
+  if (own) {
 #pragma unroll
-  for (int a = 0; a < TC; ++a)
+    for (int b = 0; b < NRT; ++b)
 #pragma unroll
-    for (int b = 0; b < TC; ++b) {
-      const int r = rb * TC + a, s = cb * TC + b;
-      B1[r * LC + s] = accW[a][b];  // dW
-      B2[r * LC + s] = accP[a][b];  // dP (entries above the diagonal are masked below)
-    }
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * a + 4 * lg + i, s_ = 16 * b + lr;
+        B1[r * LC + s_] = accW[b][i];               // dW
+        B2[r * LC + s_] = b <= a ? accP[b][i] : 0.f;  // dP (entries above the diagonal masked below)
+      }
+  }
   __syncthreads();
   // db_s (first part) = sum_r T_rs dW_rs;  Y = (dW Diag(b)) T^T
-  for (int s = t; s < C; s += kBT) {
-    float a = 0.f;
-    for (int r = s; r < C; ++r) a = fmaf(sT[r * LC + s], B1[r * LC + s], a);
-    sdb1[s] = a;
+  for (int s_ = t; s_ < C; s_ += kBT) {
+    float acc = 0.f;
+    for (int r = s_; r < C; ++r) acc = fmaf(sT[r * LC + s_], B1[r * LC + s_], acc);
+    sdb1[s_] = acc;
   }
-  float y[TC][TC];
+  f32x4 y[NRT];
 #pragma unroll
-  for (int a = 0; a < TC; ++a)
+  for (int b = 0; b < NRT; ++b) y[b] = z4;
+  if (own) {
 #pragma unroll
-    for (int b = 0; b < TC; ++b) y[a][b] = 0.f;
-  for (int m = 0; m < C; ++m) {
-    float w[TC], tt[TC];
-#pragma unroll
-    for (int a = 0; a < TC; ++a) {
-      w[a] = B1[(rb * TC + a) * LC + m] * sb[m];
-      tt[a] = sT[(cb * TC + a) * LC + m];
-    }
-#pragma unroll
-    for (int a = 0; a < TC; ++a)
-#pragma unroll
-      for (int b = 0; b < TC; ++b) y[a][b] = fmaf(w[a], tt[b], y[a][b]);
-  }
-  __syncthreads();
-#pragma unroll
-  for (int a = 0; a < TC; ++a)
-#pragma unroll
-    for (int b = 0; b < TC; ++b) B1[(rb * TC + a) * LC + cb * TC + b] = y[a][b];  // Y over dW
-  __syncthreads();
-  // dA = -T^T Y, strictly lower
-#pragma unroll
-  for (int a = 0; a < TC; ++a)
-#pragma unroll
-    for (int b = 0; b < TC; ++b) y[a][b] = 0.f;
-  for (int m = 0; m < C; ++m) {
-    float tt[TC], yy[TC];
-#pragma unroll
-    for (int a = 0; a < TC; ++a) {
-      tt[a] = sT[m * LC + rb * TC + a];
-      yy[a] = B1[m * LC + cb * TC + a];
-    }
-#pragma unroll
-    for (int a = 0; a < TC; ++a)
-#pragma unroll
-      for (int b = 0; b < TC; ++b) y[a][b] = fmaf(tt[a], yy[b], y[a][b]);
-  }
-  // per entry: dG = dA b_r E, dQK = dP E, dEE = dA b_r (G . E) + dP P, db_r += dA (G . E)
-  float dgm[TC][TC], dqk[TC][TC], dee[TC][TC], dbr[TC];
-#pragma unroll
-  for (int a = 0; a < TC; ++a) {
-    const int r = rb * TC + a;
-    dbr[a] = 0.f;
-#pragma unroll
-    for (int b = 0; b < TC; ++b) {
-      const int s = cb * TC + b;
-      dgm[a][b] = dqk[a][b] = dee[a][b] = 0.f;
-      if (s <= r) {
-        const float ex = __expf(sgam[r] - sgam[s]);
-        const float dA = s < r ? -y[a][b] : 0.f;
-        const float dP = B2[r * LC + s];
-        dgm[a][b] = dA * sb[r] * ex;
-        dqk[a][b] = dP * ex;
-        const float gE = rec[R::GE + r * C + s];
-        dee[a][b] = fmaf(dA * sb[r], gE, dP * sP[r * LC + s]);
-        dbr[a] = fmaf(dA, gE, dbr[a]);
+    for (int b = 0; b < NRT; ++b) {
+      // Y[r][s] = sum_{m <= s} dW[r][m] b_m T[s][m]
+      for (int k0 = 0; k0 < 16 * (b + 1); k0 += 4) {
+        const int m = k0 + lg;
+        y[b] = mfma4(B1[ra * LC + m] * sb[m], sT[(16 * b + lr) * LC + m], y[b]);
       }
     }
   }
+  __syncthreads();
+  if (own) {
 #pragma unroll
-  for (int a = 0; a < TC; ++a) {
+    for (int b = 0; b < NRT; ++b)
 #pragma unroll
-    for (int off = 8; off >= 1; off >>= 1) dbr[a] += __shfl_xor(dbr[a], off);
+      for (int i = 0; i < 4; ++i) B1[(16 * a + 4 * lg + i) * LC + 16 * b + lr] = y[b][i];  // Y over dW
   }
   __syncthreads();
+  // dA = -T^T Y (strictly lower); per entry dG = dA b_r E, dQK = dP E,
+  // dEE = dA b_r (G . E) + dP P, db_r += dA (G . E)
+  f32x4 dgm[NRT], dqk[NRT], dee[NRT];
+  float dbr[4] = {0.f, 0.f, 0.f, 0.f};
+  if (own) {
 #pragma unroll
-  for (int a = 0; a < TC; ++a) {
-    const int r = rb * TC + a;
-    if (cb == 0) sdb2[r] = dbr[a];
+    for (int b = 0; b < NRT; ++b) {
+      f32x4 da = z4;
+      if (b <= a) {
+        // dA[r][s] = -sum_{m >= r} T[m][r] Y[m][s]
+        for (int k0 = 16 * a; k0 < C; k0 += 4) {
+          const int m = k0 + lg;
+          da = mfma4(sT[m * LC + ra], B1[m * LC + 16 * b + lr], da);
+        }
+      }
 #pragma unroll
-    for (int b = 0; b < TC; ++b) {
-      const int s = cb * TC + b;
-      B1[r * LC + s] = dgm[a][b];
-      B2[r * LC + s] = dqk[a][b];
-      sP[r * LC + s] = dee[a][b];
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * a + 4 * lg + i, s_ = 16 * b + lr;
+        dgm[b][i] = dqk[b][i] = dee[b][i] = 0.f;
+        if (s_ <= r) {
+          const float ex = __expf(sgam[r] - sgam[s_]);
+          const float dA = s_ < r ? -da[i] : 0.f;
+          const float dP = B2[r * LC + s_];
+          const float gE = rec[R::GE + r * C + s_];
+          dgm[b][i] = dA * sb[r] * ex;
+          dqk[b][i] = dP * ex;
+          dee[b][i] = fmaf(dA * sb[r], gE, dP * sP[r * LC + s_]);
+          dbr[i] = fmaf(dA, gE, dbr[i]);
+        }
+      }
     }
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dbr[i] += __shfl_xor(dbr[i], off);
   }
   __syncthreads();
-  // dQ += dQK K;  dK += dQK^T Q + (dG + dG^T) K
-  for (int s = 0; s < C; ++s) {
-    float kq[TC], kt[TC], gg[TC];
+  if (own) {
 #pragma unroll
-    for (int a = 0; a < TC; ++a) {
-      const int r = rb * TC + a;
-      kq[a] = B2[r * LC + s];
-      kt[a] = B2[s * LC + r];
-      gg[a] = B1[r * LC + s] + B1[s * LC + r];
-    }
+    for (int i = 0; i < 4; ++i)
+      if (lr == 0) sdb2[16 * a + 4 * lg + i] = dbr[i];
 #pragma unroll
-    for (int b = 0; b < TK; ++b) {
-      const int i = cb * TK + b;
-      const float ks = sK[s * LK + i], qs = sQ[s * LK + i];
+    for (int b = 0; b < NRT; ++b)
 #pragma unroll
-      for (int a = 0; a < TC; ++a) {
-        accQ[a][b] = fmaf(kq[a], ks, accQ[a][b]);
-        accK[a][b] = fmaf(kt[a], qs, fmaf(gg[a], ks, accK[a][b]));
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * a + 4 * lg + i, s_ = 16 * b + lr;
+        B1[r * LC + s_] = dgm[b][i];
+        B2[r * LC + s_] = dqk[b][i];
+        sP[r * LC + s_] = dee[b][i];
+      }
+  }
+  __syncthreads();
+  if (own) {
+    // dQ += dQK K;  dK += dQK^T Q + (dG + dG^T) K
+    for (int k0 = 0; k0 < C; k0 += 4) {
+      const int s_ = k0 + lg;
+      const float aq = B2[ra * LC + s_], at = B2[s_ * LC + ra];
+      const float ag = B1[ra * LC + s_] + B1[s_ * LC + ra];
+#pragma unroll
+      for (int b = 0; b < NKT; ++b) {
+        const float kv = sK[s_ * LK + 16 * b + lr], qv = sQ[s_ * LK + 16 * b + lr];
+        accQ[b] = mfma4(aq, kv, accQ[b]);
+        accK[b] = mfma4(ag, kv, mfma4(at, qv, accK[b]));
       }
     }
   }
   // per-row scalars: dgamma, then dg = reverse running sum; db, deta, the norm term
   for (int r = t; r < C; r += kBT) {
     float rs = 0.f, cs = 0.f;
-    for (int s = 0; s < C; ++s) {
-      rs += sP[r * LC + s];
-      cs += sP[s * LC + r];
+    for (int s_ = 0; s_ < C; ++s_) {
+      rs += sP[r * LC + s_];
+      cs += sP[s_ * LC + r];
     }
     sdge[r] = sdgam[r] * sGm[r] - sdd[r] * sdec[r] + rs - cs;
   }
@@ -800,22 +789,22 @@ __global__ __launch_bounds__(kBT) void kla_bwd_grads_kernel(BwdParams p) {
     const float db = sdb1[r] + sdb2[r];
     const float den = snrm[r] + p.eps;
     scf[r] = (p.beta_direct || r >= rows) ? 0.f : -2.f * seta[r] * db / (den * den);
-    if (r < rows) {
-      p.deta[cl.row0 + r] = p.beta_direct ? db : db / den;
-    }
+    if (r < rows) p.deta[cl.row0 + r] = p.beta_direct ? db : db / den;
   }
   __syncthreads();
   for (int r = t; r < rows; r += kBT) p.dg[cl.row0 + r] = sdge[r];
+  if (own) {
 #pragma unroll
-  for (int a = 0; a < TC; ++a) {
-    const int r = rb * TC + a;
-    if (r < rows) {
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * a + 4 * lg + i;
+      if (r < rows) {
 #pragma unroll
-      for (int b = 0; b < TK; ++b) {
-        const int i = cb * TK + b;
-        static_cast<E *>(p.dq)[(cl.row0 + r) * DK + i] = Elem<E>::from_f32(accQ[a][b]);
-        static_cast<E *>(p.dk)[(cl.row0 + r) * DK + i] =
-            Elem<E>::from_f32(fmaf(scf[r], sK[r * LK + i], accK[a][b]));
+        for (int b = 0; b < NKT; ++b) {
+          const int c = 16 * b + lr;
+          static_cast<E *>(p.dq)[(cl.row0 + r) * DK + c] = Elem<E>::from_f32(accQ[b][i]);
+          static_cast<E *>(p.dk)[(cl.row0 + r) * DK + c] =
+              Elem<E>::from_f32(fmaf(scf[r], sK[r * LK + c], accK[b][i]));
+        }
       }
     }
   }
