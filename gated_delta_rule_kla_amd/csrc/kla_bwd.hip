@@ -23,8 +23,8 @@
 //            the gradient of the initial state is what is left at the start.
 //   grads    (chunk, head) in parallel: everything else from S, dS' and the chunk's
 //            inputs, streaming the state columns 16 at a time, on fp32 MFMA tiles.
-// All arithmetic is fp32 (vector FMA in the prep and scan kernels, 16x16x4 fp32
-// MFMA in the gradient kernel) through padded LDS rows; there are no atomics, so
+// All arithmetic is fp32 (vector FMA in the prep kernel, 16x16x4 fp32 MFMA in the
+// scans and the gradient kernel) through padded LDS rows; there are no atomics, so
 // results are deterministic run to run.
 #include <algorithm>
 
@@ -244,12 +244,23 @@ __global__ __launch_bounds__(kNT) void kla_bwd_prep_kernel(BwdParams p) {
   }
 }
 
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// The two scans run their products on 16x16x4 fp32 MFMA tiles (lane l supplies
+// A[l%16][l/16] and B[l/16][l%16]; accumulator element i of lane l is row
+// 4(l/16)+i, column l%16).  The 16-column state slice lives in accumulators:
+// wave w holds state rows 16w .. 16w+15 and copies them to LDS once per chunk for
+// the next chunk's K S (or K dS) product; chunk-row products (16-row tiles of C)
+// go to waves 0 .. C/16-1.
+
 // ============================================================================
 // states: the chunk-start state of every chunk, 16 state columns per workgroup
 // ============================================================================
 template <int C, int DK>
 struct StatesSmem {
-  static constexpr int LK = DK + 1, LC = C + 1;
+  static constexpr int LK = DK + 4, LC = C + 1;
   static constexpr int K = 0, T = K + C * LK, V = T + C * LC, X = V + C * kLS, S = X + C * kLS;
   static constexpr int BETA = S + DK * kLS, GAM = BETA + C, FLOATS = GAM + C;
 };
@@ -259,10 +270,13 @@ __global__ __launch_bounds__(kNT) void kla_bwd_states_kernel(BwdParams p) {
   using L = StatesSmem<C, DK>;
   using R = PrepRec<C>;
   constexpr int LK = L::LK, LC = L::LC;
+  constexpr int NRT = C / 16, NKT = DK / 16;
+  static_assert(NRT <= kNT / 64 && NKT <= kNT / 64, "one 16-row tile per wave");
   __shared__ float sm[L::FLOATS];
   float *sK = sm + L::K, *sT = sm + L::T, *sV = sm + L::V, *sX = sm + L::X, *sS = sm + L::S;
   float *sb = sm + L::BETA, *sgam = sm + L::GAM;
   const int t = threadIdx.x;
+  const int w = t >> 6, lane = t & 63, lr = lane & 15, lg = lane >> 4;
   const int js = blockIdx.x % p.nsl, gidx = blockIdx.x / p.nsl;
   const int h = gidx % p.H, n = gidx / p.H;
   const int col0 = js * kNS;
@@ -272,6 +286,13 @@ __global__ __launch_bounds__(kNT) void kla_bwd_states_kernel(BwdParams p) {
     load_rows<float, DK, kNS, kLS, kNT>(sS, p.s0 + sbase, 0, DK, col0, p.DV);
   } else {
     for (int e = t; e < DK * kNS; e += kNT) sS[(e / kNS) * kLS + e % kNS] = 0.f;
+  }
+  __syncthreads();
+  const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+  f32x4 Sr = z4;  // state rows 16w + 4lg + i, column lr (waves w < NKT)
+  if (w < NKT) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Sr[i] = sS[(16 * w + 4 * lg + i) * kLS + lr];
   }
   const int nch = (sq.len + C - 1) / C;
   // the next chunk's K rows, V slice, T and (b, gamma) are loaded while this one is computed
@@ -291,42 +312,54 @@ __global__ __launch_bounds__(kNT) void kla_bwd_states_kernel(BwdParams p) {
   if (nch > 0) issue(0);
   for (int c = 0; c < nch; ++c) {
     const size_t slot = (size_t)h * p.nslot + sq.slot0 + c;
-    __syncthreads();
-    float *st = p.states + slot * DK * p.DV;
-    for (int e = t; e < DK * kNS; e += kNT) {
-      const int i = e / kNS, j = e % kNS;
-      st[(size_t)i * p.DV + col0 + j] = sS[i * kLS + j];
+    if (w < NKT) {
+      float *st = p.states + slot * DK * p.DV;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st[(size_t)(16 * w + 4 * lg + i) * p.DV + col0 + lr] = Sr[i];
     }
+    __syncthreads();  // the previous chunk's readers of sK, sV, sT are done
     lk.put(sK);
     lv.put(sV);
     lt.put(sT);
     lb.put(sb);  // sb and sgam are adjacent in LDS: rows of stride C
     if (c + 1 < nch) issue(c + 1);
     __syncthreads();
-    // X = V - Diag(Gam) K S, kept as Diag(b) X
-    for (int e = t; e < C * kNS; e += kNT) {
-      const int r = e / kNS, j = e % kNS;
-      float acc = 0.f;
-      for (int i = 0; i < DK; ++i) acc = fmaf(sK[r * LK + i], sS[i * kLS + j], acc);
-      sX[r * kLS + j] = sb[r] * (sV[r * kLS + j] - __expf(sgam[r]) * acc);
+    // Diag(b) X = Diag(b) (V - Diag(Gam) K S), row tile w
+    if (w < NRT) {
+      const int ra = 16 * w + lr;
+      f32x4 ks = z4;
+#pragma unroll 8
+      for (int k0 = 0; k0 < DK; k0 += 4) ks = mfma4(sK[ra * LK + k0 + lg], sS[(k0 + lg) * kLS + lr], ks);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * w + 4 * lg + i;
+        sX[r * kLS + lr] = sb[r] * (sV[r * kLS + lr] - __expf(sgam[r]) * ks[i]);
+      }
     }
     __syncthreads();
-    // Diag(d) U with U = T Diag(b) X  (into sV)
+    // Diag(d) U with U = T Diag(b) X (T lower triangular), into sV
     const float gC = sgam[C - 1];
-    for (int e = t; e < C * kNS; e += kNT) {
-      const int r = e / kNS, j = e % kNS;
-      float acc = 0.f;
-      for (int s = 0; s <= r; ++s) acc = fmaf(sT[r * LC + s], sX[s * kLS + j], acc);
-      sV[r * kLS + j] = __expf(gC - sgam[r]) * acc;
+    if (w < NRT) {
+      const int ra = 16 * w + lr;
+      f32x4 u = z4;
+      for (int k0 = 0; k0 < 16 * (w + 1); k0 += 4) u = mfma4(sT[ra * LC + k0 + lg], sX[(k0 + lg) * kLS + lr], u);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * w + 4 * lg + i;
+        sV[r * kLS + lr] = __expf(gC - sgam[r]) * u[i];
+      }
     }
     __syncthreads();
-    // S <- Gam_C S + K^T Diag(d) U
-    const float GC = __expf(gC);
-    for (int e = t; e < DK * kNS; e += kNT) {
-      const int i = e / kNS, j = e % kNS;
-      float acc = 0.f;
-      for (int r = 0; r < C; ++r) acc = fmaf(sK[r * LK + i], sV[r * kLS + j], acc);
-      sS[i * kLS + j] = fmaf(GC, sS[i * kLS + j], acc);
+    // S <- Gam_C S + K^T Diag(d) U, state rows of wave w; copy to LDS for the next K S
+    if (w < NKT) {
+      const int ia = 16 * w + lr;
+      const float GC = __expf(gC);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Sr[i] *= GC;
+#pragma unroll 4
+      for (int k0 = 0; k0 < C; k0 += 4) Sr = mfma4(sK[(k0 + lg) * LK + ia], sV[(k0 + lg) * kLS + lr], Sr);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sS[(16 * w + 4 * lg + i) * kLS + lr] = Sr[i];
     }
   }
 }
@@ -336,7 +369,7 @@ __global__ __launch_bounds__(kNT) void kla_bwd_states_kernel(BwdParams p) {
 // ============================================================================
 template <int C, int DK>
 struct DStatesSmem {
-  static constexpr int LK = DK + 1, LC = C + 1;
+  static constexpr int LK = DK + 4, LC = C + 1;
   static constexpr int K = 0, Q = K + C * LK, T = Q + C * LK, P = T + C * LC, O = P + C * LC;
   static constexpr int U = O + C * kLS, S = U + C * kLS, BETA = S + DK * kLS, GAM = BETA + C;
   static constexpr int FLOATS = GAM + C;
@@ -347,11 +380,13 @@ __global__ __launch_bounds__(kNT) void kla_bwd_dstates_kernel(BwdParams p) {
   using L = DStatesSmem<C, DK>;
   using R = PrepRec<C>;
   constexpr int LK = L::LK, LC = L::LC;
-  constexpr int PER = C * kNS / kNT > 0 ? (C * kNS + kNT - 1) / kNT : 1;
+  constexpr int NRT = C / 16, NKT = DK / 16;
+  static_assert(NRT <= kNT / 64 && NKT <= kNT / 64, "one 16-row tile per wave");
   __shared__ float sm[L::FLOATS];
   float *sK = sm + L::K, *sQ = sm + L::Q, *sT = sm + L::T, *sP = sm + L::P, *sO = sm + L::O;
   float *sU = sm + L::U, *sS = sm + L::S, *sb = sm + L::BETA, *sgam = sm + L::GAM;
   const int t = threadIdx.x;
+  const int w = t >> 6, lane = t & 63, lr = lane & 15, lg = lane >> 4;
   const int js = blockIdx.x % p.nsl, gidx = blockIdx.x / p.nsl;
   const int h = gidx % p.H, n = gidx / p.H;
   const int col0 = js * kNS;
@@ -361,6 +396,13 @@ __global__ __launch_bounds__(kNT) void kla_bwd_dstates_kernel(BwdParams p) {
     load_rows<float, DK, kNS, kLS, kNT>(sS, p.dsfin + sbase, 0, DK, col0, p.DV);
   } else {
     for (int e = t; e < DK * kNS; e += kNT) sS[(e / kNS) * kLS + e % kNS] = 0.f;
+  }
+  __syncthreads();
+  const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+  f32x4 dSr = z4;  // dS rows 16w + 4lg + i, column lr (waves w < NKT)
+  if (w < NKT) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dSr[i] = sS[(16 * w + 4 * lg + i) * kLS + lr];
   }
   const int nch = (sq.len + C - 1) / C;
   // the previous chunk's inputs are loaded while this one is computed
@@ -382,12 +424,12 @@ __global__ __launch_bounds__(kNT) void kla_bwd_dstates_kernel(BwdParams p) {
   if (nch > 0) issue(nch - 1);
   for (int c = nch - 1; c >= 0; --c) {
     const size_t slot = (size_t)h * p.nslot + sq.slot0 + c;
-    __syncthreads();
-    float *dst = p.dstates + slot * DK * p.DV;
-    for (int e = t; e < DK * kNS; e += kNT) {
-      const int i = e / kNS, j = e % kNS;
-      dst[(size_t)i * p.DV + col0 + j] = sS[i * kLS + j];
+    if (w < NKT) {
+      float *dst = p.dstates + slot * DK * p.DV;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[(size_t)(16 * w + 4 * lg + i) * p.DV + col0 + lr] = dSr[i];
     }
+    __syncthreads();
     lk.put(sK);
     lq.put(sQ);
     lo.put(sO);
@@ -397,57 +439,63 @@ __global__ __launch_bounds__(kNT) void kla_bwd_dstates_kernel(BwdParams p) {
     if (c > 0) issue(c - 1);
     __syncthreads();
     const float gC = sgam[C - 1];
-    // dU = P^T dO + Diag(d) K dS'
-    for (int e = t; e < C * kNS; e += kNT) {
-      const int r = e / kNS, j = e % kNS;
-      float a = 0.f, b = 0.f;
-      for (int s = r; s < C; ++s) a = fmaf(sP[s * LC + r], sO[s * kLS + j], a);
-      for (int i = 0; i < DK; ++i) b = fmaf(sK[r * LK + i], sS[i * kLS + j], b);
-      sU[r * kLS + j] = fmaf(__expf(gC - sgam[r]), b, a);
+    // dU = P^T dO + Diag(d) K dS'  (P lower triangular), row tile w
+    if (w < NRT) {
+      const int ra = 16 * w + lr;
+      f32x4 a = z4, b = z4;
+      for (int k0 = 16 * w; k0 < C; k0 += 4) a = mfma4(sP[(k0 + lg) * LC + ra], sO[(k0 + lg) * kLS + lr], a);
+#pragma unroll 8
+      for (int k0 = 0; k0 < DK; k0 += 4) b = mfma4(sK[ra * LK + k0 + lg], sS[(k0 + lg) * kLS + lr], b);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * w + 4 * lg + i;
+        sU[r * kLS + lr] = fmaf(__expf(gC - sgam[r]), b[i], a[i]);
+      }
     }
     __syncthreads();
     // dX = Diag(b) T^T dU; keep Diag(Gam) dX and Diag(Gam) dO for the state step
-    float gdx[PER], gdo[PER];
+    f32x4 gdx = z4, gdo = z4;
+    if (w < NRT) {
+      const int ra = 16 * w + lr;
+      f32x4 x = z4;
+      for (int k0 = 16 * w; k0 < C; k0 += 4) x = mfma4(sT[(k0 + lg) * LC + ra], sU[(k0 + lg) * kLS + lr], x);
 #pragma unroll
-    for (int m = 0; m < PER; ++m) {
-      const int e = t + m * kNT;
-      gdx[m] = gdo[m] = 0.f;
-      if (e < C * kNS) {
-        const int r = e / kNS, j = e % kNS;
-        float a = 0.f;
-        for (int s = r; s < C; ++s) a = fmaf(sT[s * LC + r], sU[s * kLS + j], a);
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * w + 4 * lg + i;
         const float G = __expf(sgam[r]);
-        gdx[m] = G * sb[r] * a;
-        gdo[m] = G * sO[r * kLS + j];
+        gdx[i] = G * sb[r] * x[i];
+        gdo[i] = G * sO[r * kLS + lr];
       }
     }
     __syncthreads();
+    if (w < NRT) {
 #pragma unroll
-    for (int m = 0; m < PER; ++m) {
-      const int e = t + m * kNT;
-      if (e < C * kNS) {
-        const int r = e / kNS, j = e % kNS;
-        sU[r * kLS + j] = gdx[m];
-        sO[r * kLS + j] = gdo[m];
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * w + 4 * lg + i;
+        sU[r * kLS + lr] = gdx[i];
+        sO[r * kLS + lr] = gdo[i];
       }
     }
     __syncthreads();
-    // dS = Gam_C dS' + (Diag(Gam) Q)^T dO - (Diag(Gam) K)^T dX
-    const float GC = __expf(gC);
-    for (int e = t; e < DK * kNS; e += kNT) {
-      const int i = e / kNS, j = e % kNS;
-      float acc = 0.f;
-      for (int r = 0; r < C; ++r)
-        acc = fmaf(sQ[r * LK + i], sO[r * kLS + j], fmaf(-sK[r * LK + i], sU[r * kLS + j], acc));
-      sS[i * kLS + j] = fmaf(GC, sS[i * kLS + j], acc);
+    // dS = Gam_C dS' + (Diag(Gam) Q)^T dO - (Diag(Gam) K)^T dX, state rows of wave w
+    if (w < NKT) {
+      const int ia = 16 * w + lr;
+      const float GC = __expf(gC);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dSr[i] *= GC;
+#pragma unroll 4
+      for (int k0 = 0; k0 < C; k0 += 4) {
+        const int r = k0 + lg;
+        dSr = mfma4(sQ[r * LK + ia], sO[r * kLS + lr], dSr);
+        dSr = mfma4(-sK[r * LK + ia], sU[r * kLS + lr], dSr);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sS[(16 * w + 4 * lg + i) * kLS + lr] = dSr[i];
     }
   }
-  if (p.ds0) {
-    __syncthreads();
-    for (int e = t; e < DK * kNS; e += kNT) {
-      const int i = e / kNS, j = e % kNS;
-      p.ds0[sbase + (size_t)i * p.DV + col0 + j] = sS[i * kLS + j];
-    }
+  if (p.ds0 && w < NKT) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p.ds0[sbase + (size_t)(16 * w + 4 * lg + i) * p.DV + col0 + lr] = dSr[i];
   }
 }
 
@@ -475,10 +523,6 @@ struct GradSmem {
   static constexpr int RED = DEC + C;
   static constexpr int FLOATS = RED + kBT;
 };
-
-__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
 
 template <typename E, int C, int DK>
 __global__ __launch_bounds__(kBT) void kla_bwd_grads_kernel(BwdParams p) {
