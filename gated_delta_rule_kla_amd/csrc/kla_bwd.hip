@@ -23,9 +23,10 @@
 //            the gradient of the initial state is what is left at the start.
 //   grads    (chunk, head) in parallel: everything else from S, dS' and the chunk's
 //            inputs, streaming the state columns 16 at a time, on fp32 MFMA tiles.
-// All arithmetic is fp32 (vector FMA in the prep kernel, 16x16x4 fp32 MFMA in the
-// scans and the gradient kernel) through padded LDS rows; there are no atomics, so
-// results are deterministic run to run.
+// All arithmetic is fp32 (the prep kernel's K K^T and Q K^T take the bf16 inputs as
+// MFMA operands, exact products with fp32 sums; everything else is 16x16x4 fp32 MFMA
+// or vector FMA) through padded LDS rows; there are no atomics, so results are
+// deterministic run to run.
 #include <algorithm>
 
 #include "kla_common.h"
@@ -160,92 +161,197 @@ __device__ __forceinline__ void load_rows(float *dst, const void *src, long long
   tl.put(dst);
 }
 
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
 // ============================================================================
 // prep: b, gamma, ||k||^2, T = (I + A)^-1 and P for one (chunk, head)
 // ============================================================================
-template <typename E, int C, int DK>
-struct PrepSmem {
-  static constexpr int LK = DK + 1, LC = C + 1;
-  static constexpr int K = 0, Q = K + C * LK, A = Q + C * LK, T = A + C * LC, G = T + C * LC;
-  static constexpr int BETA = G + C, GAM = BETA + C, NRM = GAM + C, FLOATS = NRM + C;
+// Four waves.  K K^T and Q K^T run on MFMA (bf16 operands are exact products
+// with fp32 sums; the fp32 build uses fp32 MFMA): the lower-triangular 16x16
+// tiles split by row blocks {p, NB-1-p} over two waves per product, so a Gram
+// wave computes the diagonal tile -- hence the norms and b -- of every row it
+// needs.  T = (I + A)^-1 by 16x16 blocks: the diagonal blocks by column-parallel
+// forward substitution (one lane per column, one block per 16 lanes), then the
+// blocks below the diagonal level by level, T_ij = -T_ii sum_{j<=m<i} A_im T_mj,
+// as 16x16x16 fp32 MFMA products.
+constexpr int kPT = 256;  // threads per workgroup of the prep kernel
+
+template <typename E, int DK, int LK> struct PrepTile;
+
+template <int DK, int LK> struct PrepTile<bf16, DK, LK> {
+  // 16x16 tile of A B^T: rows of A and B (stride LK) from the given pointers
+  static __device__ __forceinline__ f32x4 run(const bf16 *A, const bf16 *B, int lr, int lg) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k0 = 0; k0 < DK; k0 += 32) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8 *>(A + lr * LK + k0 + 8 * lg);
+      const bf16x8 b = *reinterpret_cast<const bf16x8 *>(B + lr * LK + k0 + 8 * lg);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+    }
+    return acc;
+  }
+};
+
+template <int DK, int LK> struct PrepTile<float, DK, LK> {
+  static __device__ __forceinline__ f32x4 run(const float *A, const float *B, int lr, int lg) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k0 = 0; k0 < DK; k0 += 16) {
+      const f32x4 a = *reinterpret_cast<const f32x4 *>(A + lr * LK + k0 + 4 * lg);
+      const f32x4 b = *reinterpret_cast<const f32x4 *>(B + lr * LK + k0 + 4 * lg);
+#pragma unroll
+      for (int x = 0; x < 4; ++x) acc = mfma4(a[x], b[x], acc);
+    }
+    return acc;
+  }
 };
 
 template <typename E, int C, int DK>
-__global__ __launch_bounds__(kNT) void kla_bwd_prep_kernel(BwdParams p) {
+struct PrepSmem {
+  static constexpr int EPV = 16 / (int)sizeof(E);     // elements per 16-byte vector
+  static constexpr int LK = DK + EPV;                  // K, Q rows (elements), 16-byte padded
+  static constexpr int LC = C + 4;                     // A, T rows (floats)
+  static constexpr int KB = C * LK * (int)sizeof(E);   // bytes of the K (or Q) image
+  static constexpr int AB = C * LC * 4;                // bytes of A (or T)
+  // K, then Q; T reuses Q's bytes once the scores are out, then A
+  static constexpr int K = 0, Q = KB, T = KB, A = KB + (KB > AB ? KB : AB);
+  static constexpr int BYTES = A + AB;
+};
+
+template <typename E, int C, int DK>
+__global__ __launch_bounds__(kPT) void kla_bwd_prep_kernel(BwdParams p) {
   using L = PrepSmem<E, C, DK>;
   using R = PrepRec<C>;
-  constexpr int LK = L::LK, LC = L::LC;
-  __shared__ float sm[L::FLOATS];
-  float *sK = sm + L::K, *sQ = sm + L::Q, *sA = sm + L::A, *sT = sm + L::T;
-  float *sg = sm + L::G, *sb = sm + L::BETA, *sgam = sm + L::GAM, *snrm = sm + L::NRM;
+  using MM = PrepTile<E, DK, L::LK>;
+  constexpr int LK = L::LK, LC = L::LC, NB = C / 16, EPV = L::EPV, VPR = DK / EPV;
+  static_assert(C <= 64 && C % 16 == 0 && DK % (4 * EPV) == 0, "tile shapes");
+  __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
+  E *sK = reinterpret_cast<E *>(smem + L::K), *sQ = reinterpret_cast<E *>(smem + L::Q);
+  float *sT = reinterpret_cast<float *>(smem + L::T), *sA = reinterpret_cast<float *>(smem + L::A);
   const int slot = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
+  const int w = t >> 6, lane = t & 63, lr = lane & 15, lg = lane >> 4;
   const ChunkLoc cl = chunk_loc(p, slot, h, C);
   if (cl.rows == 0) return;  // uniform: no chunk behind this slot
   const int rows = cl.rows;
-
-  load_rows<E, C, DK, LK, kNT>(sK, p.k, cl.row0, rows, 0, DK);
-  load_rows<E, C, DK, LK, kNT>(sQ, p.q, cl.row0, rows, 0, DK);
-  for (int r = t; r < C; r += kNT) {
-    sg[r] = r < rows ? ld<E>(p.g, cl.row0 + r) : 0.f;
-    sb[r] = r < rows ? ld<E>(p.eta, cl.row0 + r) : 0.f;  // eta (or b) for now
-  }
-  __syncthreads();
-  for (int r = t; r < C; r += kNT) {
-    float n = 0.f;
-    for (int i = 0; i < DK; ++i) n = fmaf(sK[r * LK + i], sK[r * LK + i], n);
-    snrm[r] = n;
-    sb[r] = r >= rows ? 0.f : (p.beta_direct ? sb[r] : sb[r] / (n + p.eps));
-  }
-  if (t == 0) {
-    float a = 0.f;
-    for (int r = 0; r < C; ++r) {
-      a += sg[r];
-      sgam[r] = a;
-    }
-  }
-  __syncthreads();
   float *rec = p.prep + ((size_t)h * p.nslot + slot) * R::FLOATS;
-  for (int e = t; e < C * C; e += kNT) {
-    const int r = e / C, s = e % C;
-    float a = 0.f, pv = 0.f, ge = 0.f;
-    if (s <= r) {
-      float gkk = 0.f, gqk = 0.f;
-      for (int i = 0; i < DK; ++i) {
-        gkk = fmaf(sK[r * LK + i], sK[s * LK + i], gkk);
-        gqk = fmaf(sQ[r * LK + i], sK[s * LK + i], gqk);
-      }
-      const float ex = __expf(sgam[r] - sgam[s]);
-      pv = gqk * ex;
-      ge = gkk * ex;
-      if (s < r) a = sb[r] * gkk * ex;
-    }
-    sA[r * LC + s] = a;
-    sT[r * LC + s] = r == s ? 1.f : 0.f;
-    rec[R::PM + e] = pv;
-    rec[R::GE + e] = ge;
-  }
-  __syncthreads();
-  // T[r][j] = -sum_{j <= s < r} A[r][s] T[s][j] below the unit diagonal: one column
-  // per thread, rows in order (forward substitution).
-  if (t < C) {
-    const int j = t;
-    for (int r = j + 1; r < C; ++r) {
-      float acc = 0.f;
-      for (int s = j; s < r; ++s) acc = fmaf(sA[r * LC + s], sT[s * LC + j], acc);
-      sT[r * LC + j] = -acc;
-    }
-  }
-  __syncthreads();
-  for (int e = t; e < C * C; e += kNT) rec[R::TM + e] = sT[(e / C) * LC + e % C];
-  for (int r = t; r < C; r += kNT) {
-    rec[R::BETA + r] = sb[r];
-    rec[R::GAM + r] = sgam[r];
-    rec[R::NRM + r] = snrm[r];
-  }
-}
 
-__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  // K and Q rows as stored (16-byte vectors; rows past the chunk read as zero)
+  for (int idx = t; idx < 2 * C * VPR; idx += kPT) {
+    const int m = idx / (C * VPR), e = idx % (C * VPR), r = e / VPR, c = (e % VPR) * EPV;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (r < rows) v = ldg16(static_cast<const E *>(m ? p.q : p.k) + (cl.row0 + r) * DK + c);
+    *reinterpret_cast<uint4 *>((m ? sQ : sK) + r * LK + c) = v;
+  }
+  // gate prefix gamma (lane r holds gamma_r; rows past the chunk add zero) and eta
+  float gam = lane < rows ? ld<E>(p.g, cl.row0 + lane) : 0.f;
+  const float eta = lane < rows ? ld<E>(p.eta, cl.row0 + lane) : 0.f;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const float u = __shfl_up(gam, off);
+    if (lane >= off) gam += u;
+  }
+  if (w == 0 && lane < C) rec[R::GAM + lane] = gam;
+  __syncthreads();
+
+  // K K^T (waves 0, 1) and Q K^T (waves 2, 3) by row blocks {p, NB-1-p}
+  const int pw = w & 1;
+  const bool gram = w < 2;
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int Rb = pass ? NB - 1 - pw : pw;
+    if (Rb < 0 || Rb >= NB || (pass && Rb == pw)) continue;  // uniform per wave
+    const float gr = __shfl(gam, 16 * Rb + 4 * lg), gr1 = __shfl(gam, 16 * Rb + 4 * lg + 1);
+    const float gr2 = __shfl(gam, 16 * Rb + 4 * lg + 2), gr3 = __shfl(gam, 16 * Rb + 4 * lg + 3);
+    const float grow[4] = {gr, gr1, gr2, gr3};
+    float brow[4] = {0.f, 0.f, 0.f, 0.f};
+    if (gram) {
+      // diagonal tile first: the norms and b of this block's rows
+      const f32x4 d = MM::run(sK + 16 * Rb * LK, sK + 16 * Rb * LK, lr, lg);
+      const float dg = d[lr & 3];  // the diagonal entry when lg == lr >> 2
+      const float nrm = __shfl(dg, lr + 16 * (lr >> 2));  // ||k||^2 of row 16 Rb + lr
+      const float et = __shfl(eta, 16 * Rb + lr);
+      const int r = 16 * Rb + lr;
+      const float b = r >= rows ? 0.f : (p.beta_direct ? et : et / (nrm + p.eps));
+      if (lg == 0) {
+        rec[R::NRM + r] = nrm;
+        rec[R::BETA + r] = b;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) brow[i] = __shfl(b, 4 * lg + i);
+    }
+    const E *rowsA = (gram ? sK : sQ) + 16 * Rb * LK;
+    float *out = rec + (gram ? R::GE : R::PM);
+    for (int Sb = 0; Sb < NB; ++Sb) {
+      const int s = 16 * Sb + lr;
+      f32x4 v = {0.f, 0.f, 0.f, 0.f};
+      if (Sb <= Rb) v = MM::run(rowsA, sK + 16 * Sb * LK, lr, lg);
+      const float gc = __shfl(gam, s);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * Rb + 4 * lg + i;
+        // mask before the exponential: only s <= r is ever evaluated
+        const float ex = s <= r ? __expf(grow[i] - gc) : 0.f;
+        const float ge = v[i] * ex;
+        out[r * C + s] = ge;
+        if (gram && Sb <= Rb) sA[r * LC + s] = s < r ? brow[i] * ge : 0.f;
+      }
+    }
+  }
+  __syncthreads();  // A complete; Q no longer needed (T takes its place)
+
+  // diagonal blocks: lane 16b + j solves column j of T_bb = (I + A_bb)^-1
+  if (w == 0 && lg < NB) {
+    const int b = lg, j = lr;
+    const float *Ab = sA + 16 * b * LC + 16 * b;
+    float tc[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) tc[r] = r == j ? 1.f : 0.f;
+#pragma unroll
+    for (int r = 1; r < 16; ++r) {
+      float acc = 0.f;
+#pragma unroll
+      for (int s4 = 0; s4 < r; s4 += 4) {
+        const f32x4 a = *reinterpret_cast<const f32x4 *>(Ab + r * LC + s4);
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+          if (s4 + x < r) acc = fmaf(a[x], tc[s4 + x], acc);
+      }
+      if (r > j) tc[r] = -acc;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sT[(16 * b + r) * LC + 16 * b + j] = tc[r];
+  }
+  __syncthreads();
+  // blocks below the diagonal, level by level: wave w takes block (L + w, w)
+  for (int Lv = 1; Lv < NB; ++Lv) {
+    const int bi = Lv + w, bj = w;
+    if (bi < NB) {
+      f32x4 y = {0.f, 0.f, 0.f, 0.f};
+      for (int m = bj; m < bi; ++m) {
+        // Y += A_im T_mj, contraction index 4 lg + x
+        const f32x4 a = *reinterpret_cast<const f32x4 *>(sA + (16 * bi + lr) * LC + 16 * m + 4 * lg);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) y = mfma4(a[x], sT[(16 * m + 4 * lg + x) * LC + 16 * bj + lr], y);
+      }
+      // Z = T_ii Y: lane (lr, lg) holds Y[4 lg + x][lr], the B operand of step x as it stands
+      const f32x4 a = *reinterpret_cast<const f32x4 *>(sT + (16 * bi + lr) * LC + 16 * bi + 4 * lg);
+      f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int x = 0; x < 4; ++x) z = mfma4(a[x], y[x], z);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sT[(16 * bi + 4 * lg + i) * LC + 16 * bj + lr] = -z[i];
+    }
+    __syncthreads();
+  }
+  // T to the record, zero above the diagonal blocks
+  for (int e = t; e < C * C / 4; e += kPT) {
+    const int r = (4 * e) / C, s = (4 * e) % C;
+    f32x4 v = {0.f, 0.f, 0.f, 0.f};
+    if ((s >> 4) <= (r >> 4)) v = *reinterpret_cast<const f32x4 *>(sT + r * LC + s);
+    *reinterpret_cast<f32x4 *>(rec + R::TM + 4 * e) = v;
+  }
 }
 
 // The two scans run their products on 16x16x4 fp32 MFMA tiles (lane l supplies
@@ -881,7 +987,7 @@ size_t bwd_workspace_bytes_t(const ChunkArgs &a) {
 
 template <typename E, int C, int DK>
 hipError_t launch_bwd_t(const ChunkArgs &a, const ChunkBwdArgs &b, hipStream_t st) {
-  static_assert(PrepSmem<E, C, DK>::FLOATS * 4 <= 160 * 1024, "prep LDS");
+  static_assert(PrepSmem<E, C, DK>::BYTES <= 64 * 1024, "prep LDS (kept small: several workgroups per CU)");
   static_assert(StatesSmem<C, DK>::FLOATS * 4 <= 160 * 1024, "states LDS");
   static_assert(DStatesSmem<C, DK>::FLOATS * 4 <= 160 * 1024, "dstates LDS");
   static_assert(GradSmem<C, DK>::FLOATS * 4 <= 160 * 1024, "grads LDS");
@@ -918,7 +1024,7 @@ hipError_t launch_bwd_t(const ChunkArgs &a, const ChunkBwdArgs &b, hipStream_t s
   const unsigned seq_blocks = (unsigned)((long long)a.num_seqs * a.H * p.nsl);
   const bool tokens = (long long)a.B * a.T > 0 && p.nslot > 0;
   if (tokens) {
-    hipLaunchKernelGGL((kla_bwd_prep_kernel<E, C, DK>), dim3((unsigned)p.nslot, (unsigned)a.H), dim3(kNT), 0, st, p);
+    hipLaunchKernelGGL((kla_bwd_prep_kernel<E, C, DK>), dim3((unsigned)p.nslot, (unsigned)a.H), dim3(kPT), 0, st, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((kla_bwd_states_kernel<E, C, DK>), dim3(seq_blocks), dim3(kNT), 0, st, p);
