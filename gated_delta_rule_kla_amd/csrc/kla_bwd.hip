@@ -165,6 +165,34 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// One 16x16x16 product step of the scans and the gradient kernel, operands as four
+// fp32 values per lane: a[x] = A[row][k0 + 4 lg + x], b[x] = B[k0 + 4 lg + x][col].
+// The bf16 build rounds them to bf16 for one 16x16x16 bf16 MFMA (fp32 sums, 16 times
+// the fp32 MFMA rate; the inputs q, k, v and dO are bf16 already, so only derived
+// operands -- states, T, P and intermediate products -- are rounded); the fp32 build
+// runs four 16x16x4 fp32 MFMAs with the same pairing of contraction indices.
+template <typename E> struct Mma16;
+
+template <> struct Mma16<bf16> {
+  static __device__ __forceinline__ f32x4 run(f32x4 a, f32x4 b, f32x4 c) {
+    const bf16x4 ab = {(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3]};
+    const bf16x4 bb = {(bf16)b[0], (bf16)b[1], (bf16)b[2], (bf16)b[3]};
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ab, bb, c, 0, 0, 0);
+  }
+};
+
+template <> struct Mma16<float> {
+  static __device__ __forceinline__ f32x4 run(f32x4 a, f32x4 b, f32x4 c) {
+#pragma unroll
+    for (int x = 0; x < 4; ++x) c = mfma4(a[x], b[x], c);
+    return c;
+  }
+};
+
+// four LDS floats p[0], p[st], p[2 st], p[3 st]; and four consecutive 16-byte aligned ones
+__device__ __forceinline__ f32x4 gat4(const float *p, int st) { return f32x4{p[0], p[st], p[2 * st], p[3 * st]}; }
+__device__ __forceinline__ f32x4 vec4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
+
 // ============================================================================
 // prep: b, gamma, ||k||^2, T = (I + A)^-1 and P for one (chunk, head)
 // ============================================================================
@@ -375,10 +403,11 @@ template <typename E, int C, int DK>
 __global__ __launch_bounds__(kNT) void kla_bwd_states_kernel(BwdParams p) {
   using L = StatesSmem<C, DK>;
   using R = PrepRec<C>;
+  using MM = Mma16<E>;
   constexpr int LK = L::LK, LC = L::LC;
   constexpr int NRT = C / 16, NKT = DK / 16;
   static_assert(NRT <= kNT / 64 && NKT <= kNT / 64, "one 16-row tile per wave");
-  __shared__ float sm[L::FLOATS];
+  __shared__ __attribute__((aligned(16))) float sm[L::FLOATS];
   float *sK = sm + L::K, *sT = sm + L::T, *sV = sm + L::V, *sX = sm + L::X, *sS = sm + L::S;
   float *sb = sm + L::BETA, *sgam = sm + L::GAM;
   const int t = threadIdx.x;
@@ -434,8 +463,9 @@ __global__ __launch_bounds__(kNT) void kla_bwd_states_kernel(BwdParams p) {
     if (w < NRT) {
       const int ra = 16 * w + lr;
       f32x4 ks = z4;
-#pragma unroll 8
-      for (int k0 = 0; k0 < DK; k0 += 4) ks = mfma4(sK[ra * LK + k0 + lg], sS[(k0 + lg) * kLS + lr], ks);
+#pragma unroll 4
+      for (int k0 = 0; k0 < DK; k0 += 16)
+        ks = MM::run(vec4(sK + ra * LK + k0 + 4 * lg), gat4(sS + (k0 + 4 * lg) * kLS + lr, kLS), ks);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * w + 4 * lg + i;
@@ -448,7 +478,8 @@ __global__ __launch_bounds__(kNT) void kla_bwd_states_kernel(BwdParams p) {
     if (w < NRT) {
       const int ra = 16 * w + lr;
       f32x4 u = z4;
-      for (int k0 = 0; k0 < 16 * (w + 1); k0 += 4) u = mfma4(sT[ra * LC + k0 + lg], sX[(k0 + lg) * kLS + lr], u);
+      for (int k0 = 0; k0 < 16 * (w + 1); k0 += 16)
+        u = MM::run(gat4(sT + ra * LC + k0 + 4 * lg, 1), gat4(sX + (k0 + 4 * lg) * kLS + lr, kLS), u);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * w + 4 * lg + i;
@@ -462,8 +493,9 @@ __global__ __launch_bounds__(kNT) void kla_bwd_states_kernel(BwdParams p) {
       const float GC = __expf(gC);
 #pragma unroll
       for (int i = 0; i < 4; ++i) Sr[i] *= GC;
-#pragma unroll 4
-      for (int k0 = 0; k0 < C; k0 += 4) Sr = mfma4(sK[(k0 + lg) * LK + ia], sV[(k0 + lg) * kLS + lr], Sr);
+#pragma unroll
+      for (int k0 = 0; k0 < C; k0 += 16)
+        Sr = MM::run(gat4(sK + (k0 + 4 * lg) * LK + ia, LK), gat4(sV + (k0 + 4 * lg) * kLS + lr, kLS), Sr);
 #pragma unroll
       for (int i = 0; i < 4; ++i) sS[(16 * w + 4 * lg + i) * kLS + lr] = Sr[i];
     }
@@ -485,10 +517,11 @@ template <typename E, int C, int DK>
 __global__ __launch_bounds__(kNT) void kla_bwd_dstates_kernel(BwdParams p) {
   using L = DStatesSmem<C, DK>;
   using R = PrepRec<C>;
+  using MM = Mma16<E>;
   constexpr int LK = L::LK, LC = L::LC;
   constexpr int NRT = C / 16, NKT = DK / 16;
   static_assert(NRT <= kNT / 64 && NKT <= kNT / 64, "one 16-row tile per wave");
-  __shared__ float sm[L::FLOATS];
+  __shared__ __attribute__((aligned(16))) float sm[L::FLOATS];
   float *sK = sm + L::K, *sQ = sm + L::Q, *sT = sm + L::T, *sP = sm + L::P, *sO = sm + L::O;
   float *sU = sm + L::U, *sS = sm + L::S, *sb = sm + L::BETA, *sgam = sm + L::GAM;
   const int t = threadIdx.x;
@@ -549,9 +582,11 @@ __global__ __launch_bounds__(kNT) void kla_bwd_dstates_kernel(BwdParams p) {
     if (w < NRT) {
       const int ra = 16 * w + lr;
       f32x4 a = z4, b = z4;
-      for (int k0 = 16 * w; k0 < C; k0 += 4) a = mfma4(sP[(k0 + lg) * LC + ra], sO[(k0 + lg) * kLS + lr], a);
-#pragma unroll 8
-      for (int k0 = 0; k0 < DK; k0 += 4) b = mfma4(sK[ra * LK + k0 + lg], sS[(k0 + lg) * kLS + lr], b);
+      for (int k0 = 16 * w; k0 < C; k0 += 16)
+        a = MM::run(gat4(sP + (k0 + 4 * lg) * LC + ra, LC), gat4(sO + (k0 + 4 * lg) * kLS + lr, kLS), a);
+#pragma unroll 4
+      for (int k0 = 0; k0 < DK; k0 += 16)
+        b = MM::run(vec4(sK + ra * LK + k0 + 4 * lg), gat4(sS + (k0 + 4 * lg) * kLS + lr, kLS), b);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * w + 4 * lg + i;
@@ -564,7 +599,8 @@ __global__ __launch_bounds__(kNT) void kla_bwd_dstates_kernel(BwdParams p) {
     if (w < NRT) {
       const int ra = 16 * w + lr;
       f32x4 x = z4;
-      for (int k0 = 16 * w; k0 < C; k0 += 4) x = mfma4(sT[(k0 + lg) * LC + ra], sU[(k0 + lg) * kLS + lr], x);
+      for (int k0 = 16 * w; k0 < C; k0 += 16)
+        x = MM::run(gat4(sT + (k0 + 4 * lg) * LC + ra, LC), gat4(sU + (k0 + 4 * lg) * kLS + lr, kLS), x);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * w + 4 * lg + i;
@@ -589,11 +625,11 @@ __global__ __launch_bounds__(kNT) void kla_bwd_dstates_kernel(BwdParams p) {
       const float GC = __expf(gC);
 #pragma unroll
       for (int i = 0; i < 4; ++i) dSr[i] *= GC;
-#pragma unroll 4
-      for (int k0 = 0; k0 < C; k0 += 4) {
-        const int r = k0 + lg;
-        dSr = mfma4(sQ[r * LK + ia], sO[r * kLS + lr], dSr);
-        dSr = mfma4(-sK[r * LK + ia], sU[r * kLS + lr], dSr);
+#pragma unroll
+      for (int k0 = 0; k0 < C; k0 += 16) {
+        const int r = k0 + 4 * lg;
+        dSr = MM::run(gat4(sQ + r * LK + ia, LK), gat4(sO + r * kLS + lr, kLS), dSr);
+        dSr = MM::run(-gat4(sK + r * LK + ia, LK), gat4(sU + r * kLS + lr, kLS), dSr);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) sS[(16 * w + 4 * lg + i) * kLS + lr] = dSr[i];
@@ -634,10 +670,11 @@ template <typename E, int C, int DK>
 __global__ __launch_bounds__(kBT) void kla_bwd_grads_kernel(BwdParams p) {
   using L = GradSmem<C, DK>;
   using R = PrepRec<C>;
+  using MM = Mma16<E>;
   constexpr int LK = L::LK, LC = L::LC;
   constexpr int NRT = C / 16, NKT = DK / 16, NW = kBT / 64;
   static_assert(C % 16 == 0 && DK % 16 == 0 && NRT <= NW, "one 16-row tile per wave at most");
-  __shared__ float sm[L::FLOATS];
+  __shared__ __attribute__((aligned(16))) float sm[L::FLOATS];
   float *sK = sm + L::K, *sQ = sm + L::Q, *sT = sm + L::T, *sP = sm + L::P;
   float *sS = sm + L::S, *sD = sm + L::D, *sV = sm + L::V, *sO = sm + L::O, *sX = sm + L::X;
   float *sU = sm + L::U, *sdU = sm + L::DU, *sdX = sm + L::DX;
@@ -715,13 +752,13 @@ __global__ __launch_bounds__(kBT) void kla_bwd_grads_kernel(BwdParams p) {
     f32x4 ks = z4, qs = z4, kd = z4;
     if (own) {
 #pragma unroll 4
-      for (int k0 = 0; k0 < DK; k0 += 4) {
-        const int kk = k0 + lg;
-        const float ka = sK[ra * LK + kk], qa = sQ[ra * LK + kk];
-        const float sv = sS[kk * kLS + lr], dv = sD[kk * kLS + lr];
-        ks = mfma4(ka, sv, ks);
-        qs = mfma4(qa, sv, qs);
-        kd = mfma4(ka, dv, kd);
+      for (int k0 = 0; k0 < DK; k0 += 16) {
+        const int kk = k0 + 4 * lg;
+        const f32x4 ka = vec4(sK + ra * LK + kk), qa = vec4(sQ + ra * LK + kk);
+        const f32x4 sv = gat4(sS + kk * kLS + lr, kLS), dv = gat4(sD + kk * kLS + lr, kLS);
+        ks = MM::run(ka, sv, ks);
+        qs = MM::run(qa, sv, qs);
+        kd = MM::run(ka, dv, kd);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -733,13 +770,13 @@ __global__ __launch_bounds__(kBT) void kla_bwd_grads_kernel(BwdParams p) {
     // (B) U = T Diag(b) X;  dU = P^T dO + Diag(d) K dS'   (T, P lower triangular)
     f32x4 u = z4, du = z4;
     if (own) {
-      for (int k0 = 0; k0 < 16 * (a + 1); k0 += 4) {
-        const int s_ = k0 + lg;
-        u = mfma4(sT[ra * LC + s_] * sb[s_], sX[s_ * kLS + lr], u);
+      for (int k0 = 0; k0 < 16 * (a + 1); k0 += 16) {
+        const int s_ = k0 + 4 * lg;
+        u = MM::run(gat4(sT + ra * LC + s_, 1) * vec4(sb + s_), gat4(sX + s_ * kLS + lr, kLS), u);
       }
-      for (int k0 = 16 * a; k0 < C; k0 += 4) {
-        const int s_ = k0 + lg;
-        du = mfma4(sP[s_ * LC + ra], sO[s_ * kLS + lr], du);
+      for (int k0 = 16 * a; k0 < C; k0 += 16) {
+        const int s_ = k0 + 4 * lg;
+        du = MM::run(gat4(sP + s_ * LC + ra, LC), gat4(sO + s_ * kLS + lr, kLS), du);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -753,9 +790,9 @@ __global__ __launch_bounds__(kBT) void kla_bwd_grads_kernel(BwdParams p) {
     if (own) {
       // (C) dX = Diag(b) T^T dU (= dV); row sums for dGam and dd
       f32x4 dx = z4;
-      for (int k0 = 16 * a; k0 < C; k0 += 4) {
-        const int s_ = k0 + lg;
-        dx = mfma4(sT[s_ * LC + ra], sdU[s_ * kLS + lr], dx);
+      for (int k0 = 16 * a; k0 < C; k0 += 16) {
+        const int s_ = k0 + 4 * lg;
+        dx = MM::run(gat4(sT + s_ * LC + ra, LC), gat4(sdU + s_ * kLS + lr, kLS), dx);
       }
       float pg[4], pd[4];
 #pragma unroll
@@ -785,21 +822,22 @@ __global__ __launch_bounds__(kBT) void kla_bwd_grads_kernel(BwdParams p) {
       // (D) dW += dU X^T, dP += dO U^T (tiles at or below the diagonal),
       //     dQ += Diag(Gam) dO S^T, dK += -Diag(Gam) dX S^T + Diag(d) U dS'^T
       // (this wave's own rows of dU, dO, dX, U were written by this wave)
-#pragma unroll
-      for (int k0 = 0; k0 < kNS; k0 += 4) {
-        const int j = k0 + lg;
-        const float adu = sdU[ra * kLS + j], ado = sO[ra * kLS + j];
-        const float aq = sGm[ra] * ado, akx = -sGm[ra] * sdX[ra * kLS + j], aku = sdec[ra] * sU[ra * kLS + j];
+      static_assert(kNS == 16, "one 16x16x16 step per slice");
+      {
+        const int j = 4 * lg;
+        const f32x4 adu = gat4(sdU + ra * kLS + j, 1), ado = gat4(sO + ra * kLS + j, 1);
+        const f32x4 aq = sGm[ra] * ado, akx = -sGm[ra] * gat4(sdX + ra * kLS + j, 1);
+        const f32x4 aku = sdec[ra] * gat4(sU + ra * kLS + j, 1);
 #pragma unroll
         for (int b = 0; b < NRT; ++b) {
-          accW[b] = mfma4(adu, sX[(16 * b + lr) * kLS + j], accW[b]);
-          if (b <= a) accP[b] = mfma4(ado, sU[(16 * b + lr) * kLS + j], accP[b]);
+          accW[b] = MM::run(adu, gat4(sX + (16 * b + lr) * kLS + j, 1), accW[b]);
+          if (b <= a) accP[b] = MM::run(ado, gat4(sU + (16 * b + lr) * kLS + j, 1), accP[b]);
         }
 #pragma unroll
         for (int b = 0; b < NKT; ++b) {
-          const float sv = sS[(16 * b + lr) * kLS + j], dv = sD[(16 * b + lr) * kLS + j];
-          accQ[b] = mfma4(aq, sv, accQ[b]);
-          accK[b] = mfma4(aku, dv, mfma4(akx, sv, accK[b]));
+          const f32x4 sv = gat4(sS + (16 * b + lr) * kLS + j, 1), dv = gat4(sD + (16 * b + lr) * kLS + j, 1);
+          accQ[b] = MM::run(aq, sv, accQ[b]);
+          accK[b] = MM::run(aku, dv, MM::run(akx, sv, accK[b]));
         }
       }
     }
@@ -834,9 +872,9 @@ __global__ __launch_bounds__(kBT) void kla_bwd_grads_kernel(BwdParams p) {
 #pragma unroll
     for (int b = 0; b < NRT; ++b) {
       // Y[r][s] = sum_{m <= s} dW[r][m] b_m T[s][m]
-      for (int k0 = 0; k0 < 16 * (b + 1); k0 += 4) {
-        const int m = k0 + lg;
-        y[b] = mfma4(B1[ra * LC + m] * sb[m], sT[(16 * b + lr) * LC + m], y[b]);
+      for (int k0 = 0; k0 < 16 * (b + 1); k0 += 16) {
+        const int m = k0 + 4 * lg;
+        y[b] = MM::run(gat4(B1 + ra * LC + m, 1) * vec4(sb + m), gat4(sT + (16 * b + lr) * LC + m, 1), y[b]);
       }
     }
   }
@@ -858,9 +896,9 @@ __global__ __launch_bounds__(kBT) void kla_bwd_grads_kernel(BwdParams p) {
       f32x4 da = z4;
       if (b <= a) {
         // dA[r][s] = -sum_{m >= r} T[m][r] Y[m][s]
-        for (int k0 = 16 * a; k0 < C; k0 += 4) {
-          const int m = k0 + lg;
-          da = mfma4(sT[m * LC + ra], B1[m * LC + 16 * b + lr], da);
+        for (int k0 = 16 * a; k0 < C; k0 += 16) {
+          const int m = k0 + 4 * lg;
+          da = MM::run(gat4(sT + m * LC + ra, LC), gat4(B1 + m * LC + 16 * b + lr, LC), da);
         }
       }
 #pragma unroll
@@ -902,15 +940,15 @@ __global__ __launch_bounds__(kBT) void kla_bwd_grads_kernel(BwdParams p) {
   __syncthreads();
   if (own) {
     // dQ += dQK K;  dK += dQK^T Q + (dG + dG^T) K
-    for (int k0 = 0; k0 < C; k0 += 4) {
-      const int s_ = k0 + lg;
-      const float aq = B2[ra * LC + s_], at = B2[s_ * LC + ra];
-      const float ag = B1[ra * LC + s_] + B1[s_ * LC + ra];
+    for (int k0 = 0; k0 < C; k0 += 16) {
+      const int s_ = k0 + 4 * lg;
+      const f32x4 aq = gat4(B2 + ra * LC + s_, 1), at = gat4(B2 + s_ * LC + ra, LC);
+      const f32x4 ag = gat4(B1 + ra * LC + s_, 1) + gat4(B1 + s_ * LC + ra, LC);
 #pragma unroll
       for (int b = 0; b < NKT; ++b) {
-        const float kv = sK[s_ * LK + 16 * b + lr], qv = sQ[s_ * LK + 16 * b + lr];
-        accQ[b] = mfma4(aq, kv, accQ[b]);
-        accK[b] = mfma4(ag, kv, mfma4(at, qv, accK[b]));
+        const f32x4 kv = gat4(sK + s_ * LK + 16 * b + lr, LK), qv = gat4(sQ + s_ * LK + 16 * b + lr, LK);
+        accQ[b] = MM::run(aq, kv, accQ[b]);
+        accK[b] = MM::run(ag, kv, MM::run(at, qv, accK[b]));
       }
     }
   }
