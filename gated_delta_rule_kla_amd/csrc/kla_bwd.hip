@@ -39,7 +39,10 @@ namespace {
 constexpr int kBT = 256;  // threads per workgroup of the gradient kernel
 constexpr int kNT = 512;  // threads per workgroup of the prep and the two scan kernels
 constexpr int kNS = 16;   // state columns per slice
-constexpr int kLS = kNS + 1;
+// LDS row strides are multiples of 4 floats so that four consecutive entries of a row are
+// one 16-byte read; 4 rows apart is then 16 (mod 64) banks, which keeps the column
+// gathers (16 lanes along a row, lane groups 4 rows apart) free of bank conflicts too
+constexpr int kLS = kNS + 4;
 
 struct BwdParams {
   const void *q, *k, *v, *g, *eta, *dout;
@@ -394,7 +397,7 @@ __global__ __launch_bounds__(kPT) void kla_bwd_prep_kernel(BwdParams p) {
 // ============================================================================
 template <int C, int DK>
 struct StatesSmem {
-  static constexpr int LK = DK + 4, LC = C + 1;
+  static constexpr int LK = DK + 4, LC = C + 4;
   static constexpr int K = 0, T = K + C * LK, V = T + C * LC, X = V + C * kLS, S = X + C * kLS;
   static constexpr int BETA = S + DK * kLS, GAM = BETA + C, FLOATS = GAM + C;
 };
@@ -479,7 +482,7 @@ __global__ __launch_bounds__(kNT) void kla_bwd_states_kernel(BwdParams p) {
       const int ra = 16 * w + lr;
       f32x4 u = z4;
       for (int k0 = 0; k0 < 16 * (w + 1); k0 += 16)
-        u = MM::run(gat4(sT + ra * LC + k0 + 4 * lg, 1), gat4(sX + (k0 + 4 * lg) * kLS + lr, kLS), u);
+        u = MM::run(vec4(sT + ra * LC + k0 + 4 * lg), gat4(sX + (k0 + 4 * lg) * kLS + lr, kLS), u);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * w + 4 * lg + i;
@@ -507,7 +510,7 @@ __global__ __launch_bounds__(kNT) void kla_bwd_states_kernel(BwdParams p) {
 // ============================================================================
 template <int C, int DK>
 struct DStatesSmem {
-  static constexpr int LK = DK + 4, LC = C + 1;
+  static constexpr int LK = DK + 4, LC = C + 4;
   static constexpr int K = 0, Q = K + C * LK, T = Q + C * LK, P = T + C * LC, O = P + C * LC;
   static constexpr int U = O + C * kLS, S = U + C * kLS, BETA = S + DK * kLS, GAM = BETA + C;
   static constexpr int FLOATS = GAM + C;
@@ -652,7 +655,7 @@ template <int C, int DK>
 struct GradSmem {
   // K and Q rows 16-byte aligned; a 16-row by 4-column operand read lands on 64
   // distinct banks (row stride = 4 mod 64)
-  static constexpr int LK = DK + 4, LC = C + 1;
+  static constexpr int LK = DK + 4, LC = C + 4;
   static constexpr int K = 0, Q = K + C * LK, T = Q + C * LK, P = T + C * LC;  // P, later dEE
   static constexpr int SL = P + C * LC;                                      // slice region
   static constexpr int S = SL, D = S + DK * kLS, V = D + DK * kLS, O = V + C * kLS, X = O + C * kLS;
@@ -772,7 +775,7 @@ __global__ __launch_bounds__(kBT) void kla_bwd_grads_kernel(BwdParams p) {
     if (own) {
       for (int k0 = 0; k0 < 16 * (a + 1); k0 += 16) {
         const int s_ = k0 + 4 * lg;
-        u = MM::run(gat4(sT + ra * LC + s_, 1) * vec4(sb + s_), gat4(sX + s_ * kLS + lr, kLS), u);
+        u = MM::run(vec4(sT + ra * LC + s_) * vec4(sb + s_), gat4(sX + s_ * kLS + lr, kLS), u);
       }
       for (int k0 = 16 * a; k0 < C; k0 += 16) {
         const int s_ = k0 + 4 * lg;
@@ -825,17 +828,17 @@ __global__ __launch_bounds__(kBT) void kla_bwd_grads_kernel(BwdParams p) {
       static_assert(kNS == 16, "one 16x16x16 step per slice");
       {
         const int j = 4 * lg;
-        const f32x4 adu = gat4(sdU + ra * kLS + j, 1), ado = gat4(sO + ra * kLS + j, 1);
-        const f32x4 aq = sGm[ra] * ado, akx = -sGm[ra] * gat4(sdX + ra * kLS + j, 1);
-        const f32x4 aku = sdec[ra] * gat4(sU + ra * kLS + j, 1);
+        const f32x4 adu = vec4(sdU + ra * kLS + j), ado = vec4(sO + ra * kLS + j);
+        const f32x4 aq = sGm[ra] * ado, akx = -sGm[ra] * vec4(sdX + ra * kLS + j);
+        const f32x4 aku = sdec[ra] * vec4(sU + ra * kLS + j);
 #pragma unroll
         for (int b = 0; b < NRT; ++b) {
-          accW[b] = MM::run(adu, gat4(sX + (16 * b + lr) * kLS + j, 1), accW[b]);
-          if (b <= a) accP[b] = MM::run(ado, gat4(sU + (16 * b + lr) * kLS + j, 1), accP[b]);
+          accW[b] = MM::run(adu, vec4(sX + (16 * b + lr) * kLS + j), accW[b]);
+          if (b <= a) accP[b] = MM::run(ado, vec4(sU + (16 * b + lr) * kLS + j), accP[b]);
         }
 #pragma unroll
         for (int b = 0; b < NKT; ++b) {
-          const f32x4 sv = gat4(sS + (16 * b + lr) * kLS + j, 1), dv = gat4(sD + (16 * b + lr) * kLS + j, 1);
+          const f32x4 sv = vec4(sS + (16 * b + lr) * kLS + j), dv = vec4(sD + (16 * b + lr) * kLS + j);
           accQ[b] = MM::run(aq, sv, accQ[b]);
           accK[b] = MM::run(aku, dv, MM::run(akx, sv, accK[b]));
         }
@@ -874,7 +877,7 @@ __global__ __launch_bounds__(kBT) void kla_bwd_grads_kernel(BwdParams p) {
       // Y[r][s] = sum_{m <= s} dW[r][m] b_m T[s][m]
       for (int k0 = 0; k0 < 16 * (b + 1); k0 += 16) {
         const int m = k0 + 4 * lg;
-        y[b] = MM::run(gat4(B1 + ra * LC + m, 1) * vec4(sb + m), gat4(sT + (16 * b + lr) * LC + m, 1), y[b]);
+        y[b] = MM::run(vec4(B1 + ra * LC + m) * vec4(sb + m), vec4(sT + (16 * b + lr) * LC + m), y[b]);
       }
     }
   }
@@ -942,8 +945,8 @@ __global__ __launch_bounds__(kBT) void kla_bwd_grads_kernel(BwdParams p) {
     // dQ += dQK K;  dK += dQK^T Q + (dG + dG^T) K
     for (int k0 = 0; k0 < C; k0 += 16) {
       const int s_ = k0 + 4 * lg;
-      const f32x4 aq = gat4(B2 + ra * LC + s_, 1), at = gat4(B2 + s_ * LC + ra, LC);
-      const f32x4 ag = gat4(B1 + ra * LC + s_, 1) + gat4(B1 + s_ * LC + ra, LC);
+      const f32x4 aq = vec4(B2 + ra * LC + s_), at = gat4(B2 + s_ * LC + ra, LC);
+      const f32x4 ag = vec4(B1 + ra * LC + s_) + gat4(B1 + s_ * LC + ra, LC);
 #pragma unroll
       for (int b = 0; b < NKT; ++b) {
         const f32x4 kv = gat4(sK + s_ * LK + 16 * b + lr, LK), qv = gat4(sQ + s_ * LK + 16 * b + lr, LK);
