@@ -36,7 +36,8 @@ namespace kla {
 
 namespace {
 
-constexpr int kBT = 256;  // threads per workgroup of the gradient kernel
+constexpr int kBT = 256;  // default thread count of the tile loaders
+constexpr int kGT = 512;  // threads per workgroup of the gradient kernel
 constexpr int kNT = 512;  // threads per workgroup of the prep and the two scan kernels
 constexpr int kNS = 16;   // state columns per slice
 // LDS row strides are multiples of 4 floats so that four consecutive entries of a row are
@@ -666,17 +667,18 @@ struct GradSmem {
   static constexpr int BETA = VEC, GAM = BETA + C, NRM = GAM + C, ETA = NRM + C, DGAM = ETA + C, DD = DGAM + C;
   static constexpr int DB1 = DD + C, DB2 = DB1 + C, DGE = DB2 + C, CF = DGE + C, GM = CF + C, DEC = GM + C;
   static constexpr int RED = DEC + C;
-  static constexpr int FLOATS = RED + kBT;
+  static constexpr int FLOATS = RED + kGT;
 };
 
 template <typename E, int C, int DK>
-__global__ __launch_bounds__(kBT) void kla_bwd_grads_kernel(BwdParams p) {
+__global__ __launch_bounds__(kGT) void kla_bwd_grads_kernel(BwdParams p) {
   using L = GradSmem<C, DK>;
   using R = PrepRec<C>;
   using MM = Mma16<E>;
   constexpr int LK = L::LK, LC = L::LC;
-  constexpr int NRT = C / 16, NKT = DK / 16, NW = kBT / 64;
-  static_assert(C % 16 == 0 && DK % 16 == 0 && NRT <= NW, "one 16-row tile per wave at most");
+  constexpr int NRT = C / 16, NKT = DK / 16;
+  constexpr int NKH = (NKT + 1) / 2;  // dQ, dK column tiles per wave: b = 2 i + half
+  static_assert(C % 16 == 0 && DK % 16 == 0 && NRT <= 4 && kGT == 512, "a wave pair per 16-row tile");
   __shared__ __attribute__((aligned(16))) float sm[L::FLOATS];
   float *sK = sm + L::K, *sQ = sm + L::Q, *sT = sm + L::T, *sP = sm + L::P;
   float *sS = sm + L::S, *sD = sm + L::D, *sV = sm + L::V, *sO = sm + L::O, *sX = sm + L::X;
@@ -689,8 +691,11 @@ __global__ __launch_bounds__(kBT) void kla_bwd_grads_kernel(BwdParams p) {
   if (cl.rows == 0) return;  // uniform
   const int rows = cl.rows;
   const int w = t >> 6, lane = t & 63, lr = lane & 15, lg = lane >> 4;
-  const int a = w;                 // this wave's row tile
+  // waves w and w + 4 share row tile a = w & 3; the first of the pair (the lead) runs
+  // the per-slice products and the C x C stage, and the pair splits the outer products
+  const int a = w & 3, half = w >> 2;
   const bool own = a < NRT;        // (uniform per wave)
+  const bool lead = own && half == 0;
   const int ra = 16 * a + lr;      // operand row of this lane
   const size_t sidx = (size_t)h * p.nslot + slot;
   const float *rec = p.prep + sidx * R::FLOATS;
@@ -698,9 +703,9 @@ __global__ __launch_bounds__(kBT) void kla_bwd_grads_kernel(BwdParams p) {
   const float *Dg = p.dstates + sidx * DK * p.DV;
 
   {
-    TileLoad<E, C, DK, LK> lk, lq;
-    TileLoad<float, C, C, LC> lt, lp;
-    TileLoad<float, 3, C, C> lb;  // b, gamma, ||k||^2 (adjacent in the record and in LDS)
+    TileLoad<E, C, DK, LK, kGT> lk, lq;
+    TileLoad<float, C, C, LC, kGT> lt, lp;
+    TileLoad<float, 3, C, C, kGT> lb;  // b, gamma, ||k||^2 (adjacent in the record and in LDS)
     lk.issue(p.k, cl.row0, rows, 0, DK);
     lq.issue(p.q, cl.row0, rows, 0, DK);
     lt.issue(rec + R::TM, 0, C, 0, C);
@@ -713,7 +718,7 @@ __global__ __launch_bounds__(kBT) void kla_bwd_grads_kernel(BwdParams p) {
     lb.put(sb);
   }
   const float gC = rec[R::GAM + C - 1];
-  for (int r = t; r < C; r += kBT) {
+  for (int r = t; r < C; r += kGT) {
     seta[r] = r < rows ? ld<E>(p.eta, cl.row0 + r) : 0.f;
     sdgam[r] = 0.f;
     sdd[r] = 0.f;
@@ -723,16 +728,16 @@ __global__ __launch_bounds__(kBT) void kla_bwd_grads_kernel(BwdParams p) {
   }
 
   const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
-  f32x4 accW[NRT], accP[NRT], accQ[NKT], accK[NKT];
+  f32x4 accWP[NRT], accQ[NKH], accK[NKH];  // accWP: dW (lead) or dP (its partner)
 #pragma unroll
-  for (int b = 0; b < NRT; ++b) accW[b] = accP[b] = z4;
+  for (int b = 0; b < NRT; ++b) accWP[b] = z4;
 #pragma unroll
-  for (int b = 0; b < NKT; ++b) accQ[b] = accK[b] = z4;
+  for (int i = 0; i < NKH; ++i) accQ[i] = accK[i] = z4;
   float gcp = 0.f;  // partial <S, dS'>
 
   // slice js + 1 of S, dS', V and dO is loaded while slice js is computed
-  TileLoad<float, DK, kNS, kLS> ls, ld_;
-  TileLoad<E, C, kNS, kLS> lv, lo;
+  TileLoad<float, DK, kNS, kLS, kGT> ls, ld_;
+  TileLoad<E, C, kNS, kLS, kGT> lv, lo;
   auto issue = [&](int js) {
     const int col0 = js * kNS;
     ls.issue(Sg, 0, DK, col0, p.DV);
@@ -750,10 +755,10 @@ __global__ __launch_bounds__(kBT) void kla_bwd_grads_kernel(BwdParams p) {
     lo.put(sO);
     if (js + 1 < p.nsl) issue(js + 1);
     __syncthreads();
-    for (int e = t; e < DK * kNS; e += kBT) gcp = fmaf(sS[(e / kNS) * kLS + e % kNS], sD[(e / kNS) * kLS + e % kNS], gcp);
+    for (int e = t; e < DK * kNS; e += kGT) gcp = fmaf(sS[(e / kNS) * kLS + e % kNS], sD[(e / kNS) * kLS + e % kNS], gcp);
     // (A) K S, Q S, K dS' for this wave's rows; X = V - Diag(Gam) K S
     f32x4 ks = z4, qs = z4, kd = z4;
-    if (own) {
+    if (lead) {
 #pragma unroll 4
       for (int k0 = 0; k0 < DK; k0 += 16) {
         const int kk = k0 + 4 * lg;
@@ -772,7 +777,7 @@ __global__ __launch_bounds__(kBT) void kla_bwd_grads_kernel(BwdParams p) {
     __syncthreads();
     // (B) U = T Diag(b) X;  dU = P^T dO + Diag(d) K dS'   (T, P lower triangular)
     f32x4 u = z4, du = z4;
-    if (own) {
+    if (lead) {
       for (int k0 = 0; k0 < 16 * (a + 1); k0 += 16) {
         const int s_ = k0 + 4 * lg;
         u = MM::run(vec4(sT + ra * LC + s_) * vec4(sb + s_), gat4(sX + s_ * kLS + lr, kLS), u);
@@ -790,7 +795,7 @@ __global__ __launch_bounds__(kBT) void kla_bwd_grads_kernel(BwdParams p) {
       }
     }
     __syncthreads();
-    if (own) {
+    if (lead) {
       // (C) dX = Diag(b) T^T dU (= dV); row sums for dGam and dd
       f32x4 dx = z4;
       for (int k0 = 16 * a; k0 < C; k0 += 16) {
@@ -822,25 +827,32 @@ __global__ __launch_bounds__(kBT) void kla_bwd_grads_kernel(BwdParams p) {
           sdd[16 * a + 4 * lg + i] += pd[i];
         }
       }
-      // (D) dW += dU X^T, dP += dO U^T (tiles at or below the diagonal),
-      //     dQ += Diag(Gam) dO S^T, dK += -Diag(Gam) dX S^T + Diag(d) U dS'^T
-      // (this wave's own rows of dU, dO, dX, U were written by this wave)
-      static_assert(kNS == 16, "one 16x16x16 step per slice");
-      {
-        const int j = 4 * lg;
-        const f32x4 adu = vec4(sdU + ra * kLS + j), ado = vec4(sO + ra * kLS + j);
-        const f32x4 aq = sGm[ra] * ado, akx = -sGm[ra] * vec4(sdX + ra * kLS + j);
-        const f32x4 aku = sdec[ra] * vec4(sU + ra * kLS + j);
+    }
+    __syncthreads();  // the rows of dU, dX and U the lead waves wrote
+    // (D) dW += dU X^T (lead), dP += dO U^T (partner; tiles at or below the diagonal),
+    //     dQ += Diag(Gam) dO S^T, dK += -Diag(Gam) dX S^T + Diag(d) U dS'^T (split by column tile)
+    static_assert(kNS == 16, "one 16x16x16 step per slice");
+    if (own) {
+      const int j = 4 * lg;
+      const f32x4 ado = vec4(sO + ra * kLS + j);
+      if (half == 0) {
+        const f32x4 adu = vec4(sdU + ra * kLS + j);
 #pragma unroll
-        for (int b = 0; b < NRT; ++b) {
-          accW[b] = MM::run(adu, vec4(sX + (16 * b + lr) * kLS + j), accW[b]);
-          if (b <= a) accP[b] = MM::run(ado, vec4(sU + (16 * b + lr) * kLS + j), accP[b]);
-        }
+        for (int b = 0; b < NRT; ++b) accWP[b] = MM::run(adu, vec4(sX + (16 * b + lr) * kLS + j), accWP[b]);
+      } else {
 #pragma unroll
-        for (int b = 0; b < NKT; ++b) {
+        for (int b = 0; b < NRT; ++b)
+          if (b <= a) accWP[b] = MM::run(ado, vec4(sU + (16 * b + lr) * kLS + j), accWP[b]);
+      }
+      const f32x4 aq = sGm[ra] * ado, akx = -sGm[ra] * vec4(sdX + ra * kLS + j);
+      const f32x4 aku = sdec[ra] * vec4(sU + ra * kLS + j);
+#pragma unroll
+      for (int i = 0; i < NKH; ++i) {
+        const int b = 2 * i + half;
+        if (b < NKT) {
           const f32x4 sv = vec4(sS + (16 * b + lr) * kLS + j), dv = vec4(sD + (16 * b + lr) * kLS + j);
-          accQ[b] = MM::run(aq, sv, accQ[b]);
-          accK[b] = MM::run(aku, dv, MM::run(akx, sv, accK[b]));
+          accQ[i] = MM::run(aq, sv, accQ[i]);
+          accK[i] = MM::run(aku, dv, MM::run(akx, sv, accK[i]));
         }
       }
     }
@@ -857,13 +869,15 @@ __global__ __launch_bounds__(kBT) void kla_bwd_grads_kernel(BwdParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * a + 4 * lg + i, s_ = 16 * b + lr;
-        B1[r * LC + s_] = accW[b][i];               // dW
-        B2[r * LC + s_] = b <= a ? accP[b][i] : 0.f;  // dP (entries above the diagonal masked below)
+        if (half == 0)
+          B1[r * LC + s_] = accWP[b][i];                // dW
+        else
+          B2[r * LC + s_] = b <= a ? accWP[b][i] : 0.f;  // dP (entries above the diagonal masked below)
       }
   }
   __syncthreads();
   // db_s (first part) = sum_r T_rs dW_rs;  Y = (dW Diag(b)) T^T
-  for (int s_ = t; s_ < C; s_ += kBT) {
+  for (int s_ = t; s_ < C; s_ += kGT) {
     float acc = 0.f;
     for (int r = s_; r < C; ++r) acc = fmaf(sT[r * LC + s_], B1[r * LC + s_], acc);
     sdb1[s_] = acc;
@@ -871,7 +885,7 @@ __global__ __launch_bounds__(kBT) void kla_bwd_grads_kernel(BwdParams p) {
   f32x4 y[NRT];
 #pragma unroll
   for (int b = 0; b < NRT; ++b) y[b] = z4;
-  if (own) {
+  if (lead) {
 #pragma unroll
     for (int b = 0; b < NRT; ++b) {
       // Y[r][s] = sum_{m <= s} dW[r][m] b_m T[s][m]
@@ -882,7 +896,7 @@ __global__ __launch_bounds__(kBT) void kla_bwd_grads_kernel(BwdParams p) {
     }
   }
   __syncthreads();
-  if (own) {
+  if (lead) {
 #pragma unroll
     for (int b = 0; b < NRT; ++b)
 #pragma unroll
@@ -893,7 +907,7 @@ __global__ __launch_bounds__(kBT) void kla_bwd_grads_kernel(BwdParams p) {
   // dEE = dA b_r (G . E) + dP P, db_r += dA (G . E)
   f32x4 dgm[NRT], dqk[NRT], dee[NRT];
   float dbr[4] = {0.f, 0.f, 0.f, 0.f};
-  if (own) {
+  if (lead) {
 #pragma unroll
     for (int b = 0; b < NRT; ++b) {
       f32x4 da = z4;
@@ -926,7 +940,7 @@ __global__ __launch_bounds__(kBT) void kla_bwd_grads_kernel(BwdParams p) {
       for (int i = 0; i < 4; ++i) dbr[i] += __shfl_xor(dbr[i], off);
   }
   __syncthreads();
-  if (own) {
+  if (lead) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       if (lr == 0) sdb2[16 * a + 4 * lg + i] = dbr[i];
@@ -948,15 +962,18 @@ __global__ __launch_bounds__(kBT) void kla_bwd_grads_kernel(BwdParams p) {
       const f32x4 aq = vec4(B2 + ra * LC + s_), at = gat4(B2 + s_ * LC + ra, LC);
       const f32x4 ag = vec4(B1 + ra * LC + s_) + gat4(B1 + s_ * LC + ra, LC);
 #pragma unroll
-      for (int b = 0; b < NKT; ++b) {
-        const f32x4 kv = gat4(sK + s_ * LK + 16 * b + lr, LK), qv = gat4(sQ + s_ * LK + 16 * b + lr, LK);
-        accQ[b] = MM::run(aq, kv, accQ[b]);
-        accK[b] = MM::run(ag, kv, MM::run(at, qv, accK[b]));
+      for (int i = 0; i < NKH; ++i) {
+        const int b = 2 * i + half;
+        if (b < NKT) {
+          const f32x4 kv = gat4(sK + s_ * LK + 16 * b + lr, LK), qv = gat4(sQ + s_ * LK + 16 * b + lr, LK);
+          accQ[i] = MM::run(aq, kv, accQ[i]);
+          accK[i] = MM::run(ag, kv, MM::run(at, qv, accK[i]));
+        }
       }
     }
   }
   // per-row scalars: dgamma, then dg = reverse running sum; db, deta, the norm term
-  for (int r = t; r < C; r += kBT) {
+  for (int r = t; r < C; r += kGT) {
     float rs = 0.f, cs = 0.f;
     for (int s_ = 0; s_ < C; ++s_) {
       rs += sP[r * LC + s_];
@@ -967,7 +984,7 @@ __global__ __launch_bounds__(kBT) void kla_bwd_grads_kernel(BwdParams p) {
   __syncthreads();
   if (t == 0) {
     float gcs = 0.f, ddd = 0.f;
-    for (int i = 0; i < kBT; ++i) gcs += sred[i];
+    for (int i = 0; i < kGT; ++i) gcs += sred[i];
     for (int r = 0; r < C; ++r) ddd = fmaf(sdd[r], sdec[r], ddd);
     sdge[C - 1] += gcs * __expf(gC) + ddd;
     float acc = 0.f;
@@ -976,25 +993,28 @@ __global__ __launch_bounds__(kBT) void kla_bwd_grads_kernel(BwdParams p) {
       sdge[r] = acc;
     }
   }
-  for (int r = t; r < C; r += kBT) {
+  for (int r = t; r < C; r += kGT) {
     const float db = sdb1[r] + sdb2[r];
     const float den = snrm[r] + p.eps;
     scf[r] = (p.beta_direct || r >= rows) ? 0.f : -2.f * seta[r] * db / (den * den);
     if (r < rows) p.deta[cl.row0 + r] = p.beta_direct ? db : db / den;
   }
   __syncthreads();
-  for (int r = t; r < rows; r += kBT) p.dg[cl.row0 + r] = sdge[r];
+  for (int r = t; r < rows; r += kGT) p.dg[cl.row0 + r] = sdge[r];
   if (own) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 16 * a + 4 * lg + i;
       if (r < rows) {
 #pragma unroll
-        for (int b = 0; b < NKT; ++b) {
-          const int c = 16 * b + lr;
-          static_cast<E *>(p.dq)[(cl.row0 + r) * DK + c] = Elem<E>::from_f32(accQ[b][i]);
-          static_cast<E *>(p.dk)[(cl.row0 + r) * DK + c] =
-              Elem<E>::from_f32(fmaf(scf[r], sK[r * LK + c], accK[b][i]));
+        for (int ii = 0; ii < NKH; ++ii) {
+          const int b = 2 * ii + half;
+          if (b < NKT) {
+            const int c = 16 * b + lr;
+            static_cast<E *>(p.dq)[(cl.row0 + r) * DK + c] = Elem<E>::from_f32(accQ[ii][i]);
+            static_cast<E *>(p.dk)[(cl.row0 + r) * DK + c] =
+                Elem<E>::from_f32(fmaf(scf[r], sK[r * LK + c], accK[ii][i]));
+          }
         }
       }
     }
@@ -1079,7 +1099,7 @@ hipError_t launch_bwd_t(const ChunkArgs &a, const ChunkBwdArgs &b, hipStream_t s
     if (e != hipSuccess) return e;
   }
   if (tokens) {
-    hipLaunchKernelGGL((kla_bwd_grads_kernel<E, C, DK>), dim3((unsigned)p.nslot, (unsigned)a.H), dim3(kBT), 0, st, p);
+    hipLaunchKernelGGL((kla_bwd_grads_kernel<E, C, DK>), dim3((unsigned)p.nslot, (unsigned)a.H), dim3(kGT), 0, st, p);
     return hipGetLastError();
   }
   return hipSuccess;
