@@ -509,48 +509,56 @@ __global__ __launch_bounds__(kNT) void kla_bwd_states_kernel(BwdParams p) {
 // ============================================================================
 // dstates: dS' of every chunk (reverse order) and the initial-state gradient
 // ============================================================================
-template <int C, int DK>
+template <int C, int DK, int NS>
 struct DStatesSmem {
+  static constexpr int LS = NS + 4;  // dO, dX and dS slice rows (a multiple of 4 floats, see kLS)
   static constexpr int LK = DK + 4, LC = C + 4;
   static constexpr int K = 0, Q = K + C * LK, T = Q + C * LK, P = T + C * LC, O = P + C * LC;
-  static constexpr int U = O + C * kLS, S = U + C * kLS, BETA = S + DK * kLS, GAM = BETA + C;
+  static constexpr int U = O + C * LS, S = U + C * LS, BETA = S + DK * LS, GAM = BETA + C;
   static constexpr int FLOATS = GAM + C;
 };
 
-template <typename E, int C, int DK>
+// NS state columns per workgroup (16 or 32): the chunk's K, Q, T and P go through LDS
+// once per workgroup, so wider slices spend less of each step on them.
+template <typename E, int C, int DK, int NS>
 __global__ __launch_bounds__(kNT) void kla_bwd_dstates_kernel(BwdParams p) {
-  using L = DStatesSmem<C, DK>;
+  using L = DStatesSmem<C, DK, NS>;
   using R = PrepRec<C>;
   using MM = Mma16<E>;
-  constexpr int LK = L::LK, LC = L::LC;
+  constexpr int LK = L::LK, LC = L::LC, LS = L::LS, CT = NS / 16;
   constexpr int NRT = C / 16, NKT = DK / 16;
-  static_assert(NRT <= kNT / 64 && NKT <= kNT / 64, "one 16-row tile per wave");
+  static_assert(NRT <= kNT / 64 && NKT <= kNT / 64 && NS % 16 == 0, "one 16-row tile per wave");
   __shared__ __attribute__((aligned(16))) float sm[L::FLOATS];
   float *sK = sm + L::K, *sQ = sm + L::Q, *sT = sm + L::T, *sP = sm + L::P, *sO = sm + L::O;
   float *sU = sm + L::U, *sS = sm + L::S, *sb = sm + L::BETA, *sgam = sm + L::GAM;
   const int t = threadIdx.x;
   const int w = t >> 6, lane = t & 63, lr = lane & 15, lg = lane >> 4;
-  const int js = blockIdx.x % p.nsl, gidx = blockIdx.x / p.nsl;
+  const int nsd = p.DV / NS;
+  const int js = blockIdx.x % nsd, gidx = blockIdx.x / nsd;
   const int h = gidx % p.H, n = gidx / p.H;
-  const int col0 = js * kNS;
+  const int col0 = js * NS;
   const SeqLoc sq = seq_loc(p, n, h, C);
   const size_t sbase = ((size_t)n * p.H + h) * DK * p.DV;
   if (p.dsfin) {
-    load_rows<float, DK, kNS, kLS, kNT>(sS, p.dsfin + sbase, 0, DK, col0, p.DV);
+    load_rows<float, DK, NS, LS, kNT>(sS, p.dsfin + sbase, 0, DK, col0, p.DV);
   } else {
-    for (int e = t; e < DK * kNS; e += kNT) sS[(e / kNS) * kLS + e % kNS] = 0.f;
+    for (int e = t; e < DK * NS; e += kNT) sS[(e / NS) * LS + e % NS] = 0.f;
   }
   __syncthreads();
   const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
-  f32x4 dSr = z4;  // dS rows 16w + 4lg + i, column lr (waves w < NKT)
-  if (w < NKT) {
+  f32x4 dSr[CT];  // dS rows 16w + 4lg + i, column 16 ct + lr (waves w < NKT)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dSr[i] = sS[(16 * w + 4 * lg + i) * kLS + lr];
+  for (int ct = 0; ct < CT; ++ct) {
+    dSr[ct] = z4;
+    if (w < NKT) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dSr[ct][i] = sS[(16 * w + 4 * lg + i) * LS + 16 * ct + lr];
+    }
   }
   const int nch = (sq.len + C - 1) / C;
   // the previous chunk's inputs are loaded while this one is computed
   TileLoad<E, C, DK, LK, kNT> lk, lq;
-  TileLoad<E, C, kNS, kLS, kNT> lo;
+  TileLoad<E, C, NS, LS, kNT> lo;
   TileLoad<float, C, C, LC, kNT> lt, lp;
   TileLoad<float, 2, C, C, kNT> lb;  // b then gamma
   auto issue = [&](int c) {
@@ -570,7 +578,9 @@ __global__ __launch_bounds__(kNT) void kla_bwd_dstates_kernel(BwdParams p) {
     if (w < NKT) {
       float *dst = p.dstates + slot * DK * p.DV;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dst[(size_t)(16 * w + 4 * lg + i) * p.DV + col0 + lr] = dSr[i];
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[(size_t)(16 * w + 4 * lg + i) * p.DV + col0 + 16 * ct + lr] = dSr[ct][i];
     }
     __syncthreads();
     lk.put(sK);
@@ -585,32 +595,53 @@ __global__ __launch_bounds__(kNT) void kla_bwd_dstates_kernel(BwdParams p) {
     // dU = P^T dO + Diag(d) K dS'  (P lower triangular), row tile w
     if (w < NRT) {
       const int ra = 16 * w + lr;
-      f32x4 a = z4, b = z4;
-      for (int k0 = 16 * w; k0 < C; k0 += 16)
-        a = MM::run(gat4(sP + (k0 + 4 * lg) * LC + ra, LC), gat4(sO + (k0 + 4 * lg) * kLS + lr, kLS), a);
+      f32x4 a[CT], b[CT];
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) a[ct] = b[ct] = z4;
+      for (int k0 = 16 * w; k0 < C; k0 += 16) {
+        const f32x4 pa = gat4(sP + (k0 + 4 * lg) * LC + ra, LC);
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+          a[ct] = MM::run(pa, gat4(sO + (k0 + 4 * lg) * LS + 16 * ct + lr, LS), a[ct]);
+      }
 #pragma unroll 4
-      for (int k0 = 0; k0 < DK; k0 += 16)
-        b = MM::run(vec4(sK + ra * LK + k0 + 4 * lg), gat4(sS + (k0 + 4 * lg) * kLS + lr, kLS), b);
+      for (int k0 = 0; k0 < DK; k0 += 16) {
+        const f32x4 ka = vec4(sK + ra * LK + k0 + 4 * lg);
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+          b[ct] = MM::run(ka, gat4(sS + (k0 + 4 * lg) * LS + 16 * ct + lr, LS), b[ct]);
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * w + 4 * lg + i;
-        sU[r * kLS + lr] = fmaf(__expf(gC - sgam[r]), b[i], a[i]);
+        const float dr = __expf(gC - sgam[r]);
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) sU[r * LS + 16 * ct + lr] = fmaf(dr, b[ct][i], a[ct][i]);
       }
     }
     __syncthreads();
     // dX = Diag(b) T^T dU; keep Diag(Gam) dX and Diag(Gam) dO for the state step
-    f32x4 gdx = z4, gdo = z4;
+    f32x4 gdx[CT], gdo[CT];
     if (w < NRT) {
       const int ra = 16 * w + lr;
-      f32x4 x = z4;
-      for (int k0 = 16 * w; k0 < C; k0 += 16)
-        x = MM::run(gat4(sT + (k0 + 4 * lg) * LC + ra, LC), gat4(sU + (k0 + 4 * lg) * kLS + lr, kLS), x);
+      f32x4 x[CT];
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) x[ct] = z4;
+      for (int k0 = 16 * w; k0 < C; k0 += 16) {
+        const f32x4 ta = gat4(sT + (k0 + 4 * lg) * LC + ra, LC);
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+          x[ct] = MM::run(ta, gat4(sU + (k0 + 4 * lg) * LS + 16 * ct + lr, LS), x[ct]);
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * w + 4 * lg + i;
         const float G = __expf(sgam[r]);
-        gdx[i] = G * sb[r] * x[i];
-        gdo[i] = G * sO[r * kLS + lr];
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          gdx[ct][i] = G * sb[r] * x[ct][i];
+          gdo[ct][i] = G * sO[r * LS + 16 * ct + lr];
+        }
       }
     }
     __syncthreads();
@@ -618,8 +649,11 @@ __global__ __launch_bounds__(kNT) void kla_bwd_dstates_kernel(BwdParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * w + 4 * lg + i;
-        sU[r * kLS + lr] = gdx[i];
-        sO[r * kLS + lr] = gdo[i];
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          sU[r * LS + 16 * ct + lr] = gdx[ct][i];
+          sO[r * LS + 16 * ct + lr] = gdo[ct][i];
+        }
       }
     }
     __syncthreads();
@@ -628,20 +662,29 @@ __global__ __launch_bounds__(kNT) void kla_bwd_dstates_kernel(BwdParams p) {
       const int ia = 16 * w + lr;
       const float GC = __expf(gC);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dSr[i] *= GC;
+      for (int ct = 0; ct < CT; ++ct) dSr[ct] = GC * dSr[ct];
 #pragma unroll
       for (int k0 = 0; k0 < C; k0 += 16) {
         const int r = k0 + 4 * lg;
-        dSr = MM::run(gat4(sQ + r * LK + ia, LK), gat4(sO + r * kLS + lr, kLS), dSr);
-        dSr = MM::run(-gat4(sK + r * LK + ia, LK), gat4(sU + r * kLS + lr, kLS), dSr);
+        const f32x4 qa = gat4(sQ + r * LK + ia, LK), ka = -gat4(sK + r * LK + ia, LK);
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          dSr[ct] = MM::run(qa, gat4(sO + r * LS + 16 * ct + lr, LS), dSr[ct]);
+          dSr[ct] = MM::run(ka, gat4(sU + r * LS + 16 * ct + lr, LS), dSr[ct]);
+        }
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sS[(16 * w + 4 * lg + i) * kLS + lr] = dSr[i];
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sS[(16 * w + 4 * lg + i) * LS + 16 * ct + lr] = dSr[ct][i];
     }
   }
   if (p.ds0 && w < NKT) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) p.ds0[sbase + (size_t)(16 * w + 4 * lg + i) * p.DV + col0 + lr] = dSr[i];
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        p.ds0[sbase + (size_t)(16 * w + 4 * lg + i) * p.DV + col0 + 16 * ct + lr] = dSr[ct][i];
   }
 }
 
@@ -1050,7 +1093,7 @@ template <typename E, int C, int DK>
 hipError_t launch_bwd_t(const ChunkArgs &a, const ChunkBwdArgs &b, hipStream_t st) {
   static_assert(PrepSmem<E, C, DK>::BYTES <= 64 * 1024, "prep LDS (kept small: several workgroups per CU)");
   static_assert(StatesSmem<C, DK>::FLOATS * 4 <= 160 * 1024, "states LDS");
-  static_assert(DStatesSmem<C, DK>::FLOATS * 4 <= 160 * 1024, "dstates LDS");
+  static_assert(DStatesSmem<C, DK, 32>::FLOATS * 4 <= 160 * 1024, "dstates LDS");
   static_assert(GradSmem<C, DK>::FLOATS * 4 <= 160 * 1024, "grads LDS");
   BwdParams p;
   p.q = a.q;
@@ -1093,8 +1136,12 @@ hipError_t launch_bwd_t(const ChunkArgs &a, const ChunkBwdArgs &b, hipStream_t s
     if (e != hipSuccess) return e;
   }
   if (seq_blocks > 0 && (tokens || p.ds0)) {
-    // with no tokens this only copies dS_final (or zeros) to the initial-state gradient
-    hipLaunchKernelGGL((kla_bwd_dstates_kernel<E, C, DK>), dim3(seq_blocks), dim3(kNT), 0, st, p);
+    // with no tokens this only copies dS_final (or zeros) to the initial-state gradient;
+    // 32 state columns per workgroup where dv allows
+    if (a.dv % 32 == 0)
+      hipLaunchKernelGGL((kla_bwd_dstates_kernel<E, C, DK, 32>), dim3(seq_blocks / 2), dim3(kNT), 0, st, p);
+    else
+      hipLaunchKernelGGL((kla_bwd_dstates_kernel<E, C, DK, 16>), dim3(seq_blocks), dim3(kNT), 0, st, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
