@@ -396,47 +396,54 @@ __global__ __launch_bounds__(kPT) void kla_bwd_prep_kernel(BwdParams p) {
 // ============================================================================
 // states: the chunk-start state of every chunk, 16 state columns per workgroup
 // ============================================================================
-template <int C, int DK>
+template <int C, int DK, int NS>
 struct StatesSmem {
+  static constexpr int LS = NS + 4;  // V, X and S slice rows (a multiple of 4 floats, see kLS)
   static constexpr int LK = DK + 4, LC = C + 4;
-  static constexpr int K = 0, T = K + C * LK, V = T + C * LC, X = V + C * kLS, S = X + C * kLS;
-  static constexpr int BETA = S + DK * kLS, GAM = BETA + C, FLOATS = GAM + C;
+  static constexpr int K = 0, T = K + C * LK, V = T + C * LC, X = V + C * LS, S = X + C * LS;
+  static constexpr int BETA = S + DK * LS, GAM = BETA + C, FLOATS = GAM + C;
 };
 
-template <typename E, int C, int DK>
+// NS state columns per workgroup (16 or 32), as for the state-gradient scan below.
+template <typename E, int C, int DK, int NS>
 __global__ __launch_bounds__(kNT) void kla_bwd_states_kernel(BwdParams p) {
-  using L = StatesSmem<C, DK>;
+  using L = StatesSmem<C, DK, NS>;
   using R = PrepRec<C>;
   using MM = Mma16<E>;
-  constexpr int LK = L::LK, LC = L::LC;
+  constexpr int LK = L::LK, LC = L::LC, LS = L::LS, CT = NS / 16;
   constexpr int NRT = C / 16, NKT = DK / 16;
-  static_assert(NRT <= kNT / 64 && NKT <= kNT / 64, "one 16-row tile per wave");
+  static_assert(NRT <= kNT / 64 && NKT <= kNT / 64 && NS % 16 == 0, "one 16-row tile per wave");
   __shared__ __attribute__((aligned(16))) float sm[L::FLOATS];
   float *sK = sm + L::K, *sT = sm + L::T, *sV = sm + L::V, *sX = sm + L::X, *sS = sm + L::S;
   float *sb = sm + L::BETA, *sgam = sm + L::GAM;
   const int t = threadIdx.x;
   const int w = t >> 6, lane = t & 63, lr = lane & 15, lg = lane >> 4;
-  const int js = blockIdx.x % p.nsl, gidx = blockIdx.x / p.nsl;
+  const int nsd = p.DV / NS;
+  const int js = blockIdx.x % nsd, gidx = blockIdx.x / nsd;
   const int h = gidx % p.H, n = gidx / p.H;
-  const int col0 = js * kNS;
+  const int col0 = js * NS;
   const SeqLoc sq = seq_loc(p, n, h, C);
   const size_t sbase = ((size_t)n * p.H + h) * DK * p.DV;
   if (p.s0) {
-    load_rows<float, DK, kNS, kLS, kNT>(sS, p.s0 + sbase, 0, DK, col0, p.DV);
+    load_rows<float, DK, NS, LS, kNT>(sS, p.s0 + sbase, 0, DK, col0, p.DV);
   } else {
-    for (int e = t; e < DK * kNS; e += kNT) sS[(e / kNS) * kLS + e % kNS] = 0.f;
+    for (int e = t; e < DK * NS; e += kNT) sS[(e / NS) * LS + e % NS] = 0.f;
   }
   __syncthreads();
   const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
-  f32x4 Sr = z4;  // state rows 16w + 4lg + i, column lr (waves w < NKT)
-  if (w < NKT) {
+  f32x4 Sr[CT];  // state rows 16w + 4lg + i, column 16 ct + lr (waves w < NKT)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) Sr[i] = sS[(16 * w + 4 * lg + i) * kLS + lr];
+  for (int ct = 0; ct < CT; ++ct) {
+    Sr[ct] = z4;
+    if (w < NKT) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Sr[ct][i] = sS[(16 * w + 4 * lg + i) * LS + 16 * ct + lr];
+    }
   }
   const int nch = (sq.len + C - 1) / C;
   // the next chunk's K rows, V slice, T and (b, gamma) are loaded while this one is computed
   TileLoad<E, C, DK, LK, kNT> lk;
-  TileLoad<E, C, kNS, kLS, kNT> lv;
+  TileLoad<E, C, NS, LS, kNT> lv;
   TileLoad<float, C, C, LC, kNT> lt;
   TileLoad<float, 2, C, C, kNT> lb;  // b then gamma (adjacent in the record)
   auto issue = [&](int c) {
@@ -454,7 +461,9 @@ __global__ __launch_bounds__(kNT) void kla_bwd_states_kernel(BwdParams p) {
     if (w < NKT) {
       float *st = p.states + slot * DK * p.DV;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) st[(size_t)(16 * w + 4 * lg + i) * p.DV + col0 + lr] = Sr[i];
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st[(size_t)(16 * w + 4 * lg + i) * p.DV + col0 + 16 * ct + lr] = Sr[ct][i];
     }
     __syncthreads();  // the previous chunk's readers of sK, sV, sT are done
     lk.put(sK);
@@ -466,14 +475,23 @@ __global__ __launch_bounds__(kNT) void kla_bwd_states_kernel(BwdParams p) {
     // Diag(b) X = Diag(b) (V - Diag(Gam) K S), row tile w
     if (w < NRT) {
       const int ra = 16 * w + lr;
-      f32x4 ks = z4;
+      f32x4 ks[CT];
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) ks[ct] = z4;
 #pragma unroll 4
-      for (int k0 = 0; k0 < DK; k0 += 16)
-        ks = MM::run(vec4(sK + ra * LK + k0 + 4 * lg), gat4(sS + (k0 + 4 * lg) * kLS + lr, kLS), ks);
+      for (int k0 = 0; k0 < DK; k0 += 16) {
+        const f32x4 ka = vec4(sK + ra * LK + k0 + 4 * lg);
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+          ks[ct] = MM::run(ka, gat4(sS + (k0 + 4 * lg) * LS + 16 * ct + lr, LS), ks[ct]);
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * w + 4 * lg + i;
-        sX[r * kLS + lr] = sb[r] * (sV[r * kLS + lr] - __expf(sgam[r]) * ks[i]);
+        const float G = __expf(sgam[r]);
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+          sX[r * LS + 16 * ct + lr] = sb[r] * (sV[r * LS + 16 * ct + lr] - G * ks[ct][i]);
       }
     }
     __syncthreads();
@@ -481,13 +499,21 @@ __global__ __launch_bounds__(kNT) void kla_bwd_states_kernel(BwdParams p) {
     const float gC = sgam[C - 1];
     if (w < NRT) {
       const int ra = 16 * w + lr;
-      f32x4 u = z4;
-      for (int k0 = 0; k0 < 16 * (w + 1); k0 += 16)
-        u = MM::run(vec4(sT + ra * LC + k0 + 4 * lg), gat4(sX + (k0 + 4 * lg) * kLS + lr, kLS), u);
+      f32x4 u[CT];
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) u[ct] = z4;
+      for (int k0 = 0; k0 < 16 * (w + 1); k0 += 16) {
+        const f32x4 ta = vec4(sT + ra * LC + k0 + 4 * lg);
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+          u[ct] = MM::run(ta, gat4(sX + (k0 + 4 * lg) * LS + 16 * ct + lr, LS), u[ct]);
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * w + 4 * lg + i;
-        sV[r * kLS + lr] = __expf(gC - sgam[r]) * u[i];
+        const float dr = __expf(gC - sgam[r]);
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) sV[r * LS + 16 * ct + lr] = dr * u[ct][i];
       }
     }
     __syncthreads();
@@ -496,12 +522,18 @@ __global__ __launch_bounds__(kNT) void kla_bwd_states_kernel(BwdParams p) {
       const int ia = 16 * w + lr;
       const float GC = __expf(gC);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) Sr[i] *= GC;
+      for (int ct = 0; ct < CT; ++ct) Sr[ct] = GC * Sr[ct];
 #pragma unroll
-      for (int k0 = 0; k0 < C; k0 += 16)
-        Sr = MM::run(gat4(sK + (k0 + 4 * lg) * LK + ia, LK), gat4(sV + (k0 + 4 * lg) * kLS + lr, kLS), Sr);
+      for (int k0 = 0; k0 < C; k0 += 16) {
+        const f32x4 ka = gat4(sK + (k0 + 4 * lg) * LK + ia, LK);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sS[(16 * w + 4 * lg + i) * kLS + lr] = Sr[i];
+        for (int ct = 0; ct < CT; ++ct)
+          Sr[ct] = MM::run(ka, gat4(sV + (k0 + 4 * lg) * LS + 16 * ct + lr, LS), Sr[ct]);
+      }
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sS[(16 * w + 4 * lg + i) * LS + 16 * ct + lr] = Sr[ct][i];
     }
   }
 }
@@ -1092,7 +1124,7 @@ size_t bwd_workspace_bytes_t(const ChunkArgs &a) {
 template <typename E, int C, int DK>
 hipError_t launch_bwd_t(const ChunkArgs &a, const ChunkBwdArgs &b, hipStream_t st) {
   static_assert(PrepSmem<E, C, DK>::BYTES <= 64 * 1024, "prep LDS (kept small: several workgroups per CU)");
-  static_assert(StatesSmem<C, DK>::FLOATS * 4 <= 160 * 1024, "states LDS");
+  static_assert(StatesSmem<C, DK, 32>::FLOATS * 4 <= 160 * 1024, "states LDS");
   static_assert(DStatesSmem<C, DK, 32>::FLOATS * 4 <= 160 * 1024, "dstates LDS");
   static_assert(GradSmem<C, DK>::FLOATS * 4 <= 160 * 1024, "grads LDS");
   BwdParams p;
@@ -1131,7 +1163,10 @@ hipError_t launch_bwd_t(const ChunkArgs &a, const ChunkBwdArgs &b, hipStream_t s
     hipLaunchKernelGGL((kla_bwd_prep_kernel<E, C, DK>), dim3((unsigned)p.nslot, (unsigned)a.H), dim3(kPT), 0, st, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((kla_bwd_states_kernel<E, C, DK>), dim3(seq_blocks), dim3(kNT), 0, st, p);
+    if (a.dv % 32 == 0)
+      hipLaunchKernelGGL((kla_bwd_states_kernel<E, C, DK, 32>), dim3(seq_blocks / 2), dim3(kNT), 0, st, p);
+    else
+      hipLaunchKernelGGL((kla_bwd_states_kernel<E, C, DK, 16>), dim3(seq_blocks), dim3(kNT), 0, st, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
