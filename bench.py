@@ -328,7 +328,9 @@ def main():
                "ms_per_step": bw["ms"], "wall_ms_per_step": bw["wall_ms"], "tokens/s": bw["tokens"] / sec,
                "tflops": bw["flops"] / sec / 1e12, "workspace_bytes": bw["ws_bytes"],
                "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                            "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                            "frac": gbs / HBM_PEAK_GBS,
+                            "traffic": recorded_traffic("kla_chunk_bwd_b4_h16_t4096_hbm.md",
+                                                        "gated_delta_rule_kla_amd/csrc/kla_bwd.hip"),
                             "kernel": "kla_chunk_bwd: prep, states, dstates and grads kernels timed "
                                       "together per call",
                             "algorithmic_bytes_per_launch": bw["bytes"],

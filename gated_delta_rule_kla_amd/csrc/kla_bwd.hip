@@ -419,7 +419,12 @@ __global__ __launch_bounds__(kNT) void kla_bwd_states_kernel(BwdParams p) {
   const int t = threadIdx.x;
   const int w = t >> 6, lane = t & 63, lr = lane & 15, lg = lane >> 4;
   const int nsd = p.DV / NS;
-  const int js = blockIdx.x % nsd, gidx = blockIdx.x / nsd;
+  // blockIdx % 8 picks the XCD: the column slices of one (sequence, head) go to one XCD so
+  // that they share the chunk's K, T (and Q, P) through its L2; the grid is padded to
+  // whole rounds of 8 groups
+  const int xcd = blockIdx.x & 7, i8 = blockIdx.x >> 3;
+  const int gidx = (i8 / nsd) * 8 + xcd, js = i8 % nsd;
+  if (gidx >= p.nseq * p.H) return;  // padding (uniform per workgroup)
   const int h = gidx % p.H, n = gidx / p.H;
   const int col0 = js * NS;
   const SeqLoc sq = seq_loc(p, n, h, C);
@@ -566,7 +571,12 @@ __global__ __launch_bounds__(kNT) void kla_bwd_dstates_kernel(BwdParams p) {
   const int t = threadIdx.x;
   const int w = t >> 6, lane = t & 63, lr = lane & 15, lg = lane >> 4;
   const int nsd = p.DV / NS;
-  const int js = blockIdx.x % nsd, gidx = blockIdx.x / nsd;
+  // blockIdx % 8 picks the XCD: the column slices of one (sequence, head) go to one XCD so
+  // that they share the chunk's K, T (and Q, P) through its L2; the grid is padded to
+  // whole rounds of 8 groups
+  const int xcd = blockIdx.x & 7, i8 = blockIdx.x >> 3;
+  const int gidx = (i8 / nsd) * 8 + xcd, js = i8 % nsd;
+  if (gidx >= p.nseq * p.H) return;  // padding (uniform per workgroup)
   const int h = gidx % p.H, n = gidx / p.H;
   const int col0 = js * NS;
   const SeqLoc sq = seq_loc(p, n, h, C);
@@ -1158,25 +1168,29 @@ hipError_t launch_bwd_t(const ChunkArgs &a, const ChunkBwdArgs &b, hipStream_t s
   p.states = reinterpret_cast<float *>(ws + pb);
   p.dstates = reinterpret_cast<float *>(ws + pb + sb);
   const unsigned seq_blocks = (unsigned)((long long)a.num_seqs * a.H * p.nsl);
+  // the two scans: (sequence, head) groups padded to whole rounds of 8, times the slices
+  const unsigned groups8 = (unsigned)(((long long)a.num_seqs * a.H + 7) / 8 * 8);
+  const unsigned ns32 = a.dv % 32 == 0 ? 1u : 0u;
+  const unsigned scan_blocks = groups8 * (unsigned)(a.dv / (ns32 ? 32 : 16));
   const bool tokens = (long long)a.B * a.T > 0 && p.nslot > 0;
   if (tokens) {
     hipLaunchKernelGGL((kla_bwd_prep_kernel<E, C, DK>), dim3((unsigned)p.nslot, (unsigned)a.H), dim3(kPT), 0, st, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (a.dv % 32 == 0)
-      hipLaunchKernelGGL((kla_bwd_states_kernel<E, C, DK, 32>), dim3(seq_blocks / 2), dim3(kNT), 0, st, p);
-    else
-      hipLaunchKernelGGL((kla_bwd_states_kernel<E, C, DK, 16>), dim3(seq_blocks), dim3(kNT), 0, st, p);
+    if (scan_blocks > 0 && ns32)
+      hipLaunchKernelGGL((kla_bwd_states_kernel<E, C, DK, 32>), dim3(scan_blocks), dim3(kNT), 0, st, p);
+    else if (scan_blocks > 0)
+      hipLaunchKernelGGL((kla_bwd_states_kernel<E, C, DK, 16>), dim3(scan_blocks), dim3(kNT), 0, st, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (seq_blocks > 0 && (tokens || p.ds0)) {
     // with no tokens this only copies dS_final (or zeros) to the initial-state gradient;
     // 32 state columns per workgroup where dv allows
-    if (a.dv % 32 == 0)
-      hipLaunchKernelGGL((kla_bwd_dstates_kernel<E, C, DK, 32>), dim3(seq_blocks / 2), dim3(kNT), 0, st, p);
+    if (ns32)
+      hipLaunchKernelGGL((kla_bwd_dstates_kernel<E, C, DK, 32>), dim3(scan_blocks), dim3(kNT), 0, st, p);
     else
-      hipLaunchKernelGGL((kla_bwd_dstates_kernel<E, C, DK, 16>), dim3(seq_blocks), dim3(kNT), 0, st, p);
+      hipLaunchKernelGGL((kla_bwd_dstates_kernel<E, C, DK, 16>), dim3(scan_blocks), dim3(kNT), 0, st, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
