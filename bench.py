@@ -130,6 +130,48 @@ def bench_prefill(steps, warmup):
                 dims=(B, H, T, dk, dv, x.chunk))
 
 
+def bench_prefill_other(steps, warmup):
+    """The other two prefill workloads, each timed as one kla_chunk_fwd call per
+    step: the long-context one (B=1 H=16 T=65536 dk=128 dv=256, no initial state)
+    and the 32 packed sequences of log-uniform lengths (H=32, cu_seqlens, nonzero
+    initial states).  Reported beside the main line, not as the metric."""
+    import torch
+    from gated_delta_rule_kla_amd import inputs, kla
+
+    dev = torch.device("cuda:0")
+    res = {}
+    for i in (2, 4):
+        x = inputs.prefill_config(i)
+        B, H, T, dk, dv = x.dims
+        q, k, v, g, eta = (t.to(dev) for t in (x.q, x.k, x.v, x.g, x.eta))
+        s0 = x.initial_state.to(dev) if x.initial_state is not None else None
+        cu = x.cu_seqlens.to(dev) if x.cu_seqlens is not None else None
+        cu_h = x.cu_seqlens if x.cu_seqlens is not None else None
+        N = (x.cu_seqlens.numel() - 1) if x.cu_seqlens is not None else B
+        o = torch.empty((B, H, T, dv), dtype=q.dtype, device=dev)
+        S = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+        ws = torch.empty(kla.chunk_workspace_bytes(B, H, T, dk, dv, x.chunk, q.dtype, cu_seqlens_host=cu_h),
+                         dtype=torch.uint8, device=dev)
+        stream = torch.cuda.current_stream(dev)
+
+        def step(_i):
+            kla.chunk_fwd(q, k, v, g, eta, x.eps, s0, cu, chunk=x.chunk, cu_seqlens_host=cu_h,
+                          out=o, final_state=S, workspace=ws)
+
+        for j in range(warmup):
+            step(j)
+        ms, _ = time_launches(step, steps, stream)
+        flops, byts = prefill_algorithmic(B, H, T, dk, dv, x.chunk, 1 if s0 is not None else 0, 1, N)
+        sec = ms * 1e-3
+        res[inputs.CONFIGS[i]] = {
+            "ms_per_call": ms, "tokens/s": B * T / sec, "tflops": flops / sec / 1e12,
+            "GB/s": byts / sec / 1e9, "hbm_frac": byts / sec / 1e9 / HBM_PEAK_GBS,
+            "algorithmic_bytes_per_launch": byts, "algorithmic_flops_per_launch": flops}
+        del q, k, v, g, eta, o, S, ws, s0, cu
+        torch.cuda.empty_cache()
+    return res
+
+
 def bench_backward(steps, warmup):
     """kla_chunk_bwd on the prefill workload: upstream gradients dL/do (bf16) and
     dL/dS_final (fp32) seeded, the initial-state gradient requested."""
@@ -340,6 +382,7 @@ def main():
                         "config": {"workload": bwd["workload"]}, "roofline": bwd["roofline"]})
         out["backward"] = bwd
     if args.mode == "all":
+        out["prefill_other_workloads"] = bench_prefill_other(max(2, args.steps // 20), max(1, args.warmup // 10))
         gd = bench_gdn(args.steps, args.warmup)
         gdn = {"workload": "the same prefill and decode workloads through kla_gdn_chunk_fwd / "
                            "kla_gdn_decode_step (update coefficient given; unit-length keys)",
