@@ -57,15 +57,21 @@ struct BwdParams {
   int beta_direct;
 };
 
-// Per (head, slot) record of the prep kernel, in floats.
-template <int C> struct PrepRec {
-  static constexpr int TM = 0;            // T = (I + A)^-1, C x C row-major
-  static constexpr int PM = C * C;        // P = lower(Q K^T . E), C x C row-major
-  static constexpr int GE = 2 * C * C;    // lower(K K^T . E), C x C row-major
-  static constexpr int BETA = 3 * C * C;  // b_r
-  static constexpr int GAM = BETA + C;    // gamma_r (rows past the chunk's end hold the last value)
-  static constexpr int NRM = GAM + C;     // ||k_r||^2
-  static constexpr int FLOATS = NRM + 2 * C;
+// Per (head, slot) record of the prep kernel: T = (I + A)^-1, P = lower(Q K^T . E) and
+// lower(K K^T . E), C x C row-major in the input element type (the bf16 path feeds them to
+// bf16 MFMA steps, so a wider copy would only be rounded again on the way in), then b,
+// gamma (rows past the chunk's end hold the last value) and ||k||^2 as fp32, and a spare row.
+template <typename E, int C> struct PrepRec {
+  static constexpr int TM = 0, PM = C * C, GE = 2 * C * C;            // E elements
+  static constexpr size_t MAT = 3 * (size_t)C * C * sizeof(E);        // bytes of the matrices
+  static constexpr int BETA = 0, GAM = C, NRM = 2 * C, VEC = 4 * C;   // floats after them
+  static constexpr size_t BYTES = MAT + VEC * 4;
+  static_assert(MAT % 16 == 0 && BYTES % 16 == 0, "16-byte aligned records");
+  static __device__ __forceinline__ char *at(float *base, size_t idx) {
+    return reinterpret_cast<char *>(base) + idx * BYTES;
+  }
+  static __device__ __forceinline__ E *mat(char *r) { return reinterpret_cast<E *>(r); }
+  static __device__ __forceinline__ float *vec(char *r) { return reinterpret_cast<float *>(r + MAT); }
 };
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return min(max(x, lo), hi); }
@@ -255,7 +261,7 @@ struct PrepSmem {
 template <typename E, int C, int DK>
 __global__ __launch_bounds__(kPT) void kla_bwd_prep_kernel(BwdParams p) {
   using L = PrepSmem<E, C, DK>;
-  using R = PrepRec<C>;
+  using R = PrepRec<E, C>;
   using MM = PrepTile<E, DK, L::LK>;
   constexpr int LK = L::LK, LC = L::LC, NB = C / 16, EPV = L::EPV, VPR = DK / EPV;
   static_assert(C <= 64 && C % 16 == 0 && DK % (4 * EPV) == 0, "tile shapes");
@@ -267,7 +273,9 @@ __global__ __launch_bounds__(kPT) void kla_bwd_prep_kernel(BwdParams p) {
   const ChunkLoc cl = chunk_loc(p, slot, h, C);
   if (cl.rows == 0) return;  // uniform: no chunk behind this slot
   const int rows = cl.rows;
-  float *rec = p.prep + ((size_t)h * p.nslot + slot) * R::FLOATS;
+  char *recb = R::at(p.prep, (size_t)h * p.nslot + slot);
+  E *rm = R::mat(recb);
+  float *rv = R::vec(recb);
 
   // K and Q rows as stored (16-byte vectors; rows past the chunk read as zero)
   for (int idx = t; idx < 2 * C * VPR; idx += kPT) {
@@ -284,7 +292,7 @@ __global__ __launch_bounds__(kPT) void kla_bwd_prep_kernel(BwdParams p) {
     const float u = __shfl_up(gam, off);
     if (lane >= off) gam += u;
   }
-  if (w == 0 && lane < C) rec[R::GAM + lane] = gam;
+  if (w == 0 && lane < C) rv[R::GAM + lane] = gam;
   __syncthreads();
 
   // K K^T (waves 0, 1) and Q K^T (waves 2, 3) by row blocks {p, NB-1-p}
@@ -307,14 +315,14 @@ __global__ __launch_bounds__(kPT) void kla_bwd_prep_kernel(BwdParams p) {
       const int r = 16 * Rb + lr;
       const float b = r >= rows ? 0.f : (p.beta_direct ? et : et / (nrm + p.eps));
       if (lg == 0) {
-        rec[R::NRM + r] = nrm;
-        rec[R::BETA + r] = b;
+        rv[R::NRM + r] = nrm;
+        rv[R::BETA + r] = b;
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) brow[i] = __shfl(b, 4 * lg + i);
     }
     const E *rowsA = (gram ? sK : sQ) + 16 * Rb * LK;
-    float *out = rec + (gram ? R::GE : R::PM);
+    E *out = rm + (gram ? R::GE : R::PM);
     for (int Sb = 0; Sb < NB; ++Sb) {
       const int s = 16 * Sb + lr;
       f32x4 v = {0.f, 0.f, 0.f, 0.f};
@@ -326,7 +334,7 @@ __global__ __launch_bounds__(kPT) void kla_bwd_prep_kernel(BwdParams p) {
         // mask before the exponential: only s <= r is ever evaluated
         const float ex = s <= r ? __expf(grow[i] - gc) : 0.f;
         const float ge = v[i] * ex;
-        out[r * C + s] = ge;
+        out[r * C + s] = Elem<E>::from_f32(ge);
         if (gram && Sb <= Rb) sA[r * LC + s] = s < r ? brow[i] * ge : 0.f;
       }
     }
@@ -382,7 +390,9 @@ __global__ __launch_bounds__(kPT) void kla_bwd_prep_kernel(BwdParams p) {
     const int r = (4 * e) / C, s = (4 * e) % C;
     f32x4 v = {0.f, 0.f, 0.f, 0.f};
     if ((s >> 4) <= (r >> 4)) v = *reinterpret_cast<const f32x4 *>(sT + r * LC + s);
-    *reinterpret_cast<f32x4 *>(rec + R::TM + 4 * e) = v;
+    E *dt = rm + R::TM + 4 * e;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) dt[x] = Elem<E>::from_f32(v[x]);
   }
 }
 
@@ -408,7 +418,7 @@ struct StatesSmem {
 template <typename E, int C, int DK, int NS>
 __global__ __launch_bounds__(kNT) void kla_bwd_states_kernel(BwdParams p) {
   using L = StatesSmem<C, DK, NS>;
-  using R = PrepRec<C>;
+  using R = PrepRec<E, C>;
   using MM = Mma16<E>;
   constexpr int LK = L::LK, LC = L::LC, LS = L::LS, CT = NS / 16;
   constexpr int NRT = C / 16, NKT = DK / 16;
@@ -449,16 +459,16 @@ __global__ __launch_bounds__(kNT) void kla_bwd_states_kernel(BwdParams p) {
   // the next chunk's K rows, V slice, T and (b, gamma) are loaded while this one is computed
   TileLoad<E, C, DK, LK, kNT> lk;
   TileLoad<E, C, NS, LS, kNT> lv;
-  TileLoad<float, C, C, LC, kNT> lt;
+  TileLoad<E, C, C, LC, kNT> lt;
   TileLoad<float, 2, C, C, kNT> lb;  // b then gamma (adjacent in the record)
   auto issue = [&](int c) {
     const int rows = min(C, sq.len - c * C);
     const long long row0 = sq.row0 + (long long)c * C;
-    const float *rec = p.prep + ((size_t)h * p.nslot + sq.slot0 + c) * R::FLOATS;
+    char *recb = R::at(p.prep, (size_t)h * p.nslot + sq.slot0 + c);
     lk.issue(p.k, row0, rows, 0, DK);
     lv.issue(p.v, row0, rows, col0, p.DV);
-    lt.issue(rec + R::TM, 0, C, 0, C);
-    lb.issue(rec + R::BETA, 0, 2, 0, C);
+    lt.issue(R::mat(recb) + R::TM, 0, C, 0, C);
+    lb.issue(R::vec(recb) + R::BETA, 0, 2, 0, C);
   };
   if (nch > 0) issue(0);
   for (int c = 0; c < nch; ++c) {
@@ -560,7 +570,7 @@ struct DStatesSmem {
 template <typename E, int C, int DK, int NS>
 __global__ __launch_bounds__(kNT) void kla_bwd_dstates_kernel(BwdParams p) {
   using L = DStatesSmem<C, DK, NS>;
-  using R = PrepRec<C>;
+  using R = PrepRec<E, C>;
   using MM = Mma16<E>;
   constexpr int LK = L::LK, LC = L::LC, LS = L::LS, CT = NS / 16;
   constexpr int NRT = C / 16, NKT = DK / 16;
@@ -601,18 +611,18 @@ __global__ __launch_bounds__(kNT) void kla_bwd_dstates_kernel(BwdParams p) {
   // the previous chunk's inputs are loaded while this one is computed
   TileLoad<E, C, DK, LK, kNT> lk, lq;
   TileLoad<E, C, NS, LS, kNT> lo;
-  TileLoad<float, C, C, LC, kNT> lt, lp;
+  TileLoad<E, C, C, LC, kNT> lt, lp;
   TileLoad<float, 2, C, C, kNT> lb;  // b then gamma
   auto issue = [&](int c) {
     const int rows = min(C, sq.len - c * C);
     const long long row0 = sq.row0 + (long long)c * C;
-    const float *rec = p.prep + ((size_t)h * p.nslot + sq.slot0 + c) * R::FLOATS;
+    char *recb = R::at(p.prep, (size_t)h * p.nslot + sq.slot0 + c);
     lk.issue(p.k, row0, rows, 0, DK);
     lq.issue(p.q, row0, rows, 0, DK);
     lo.issue(p.dout, row0, rows, col0, p.DV);
-    lt.issue(rec + R::TM, 0, C, 0, C);
-    lp.issue(rec + R::PM, 0, C, 0, C);
-    lb.issue(rec + R::BETA, 0, 2, 0, C);
+    lt.issue(R::mat(recb) + R::TM, 0, C, 0, C);
+    lp.issue(R::mat(recb) + R::PM, 0, C, 0, C);
+    lb.issue(R::vec(recb) + R::BETA, 0, 2, 0, C);
   };
   if (nch > 0) issue(nch - 1);
   for (int c = nch - 1; c >= 0; --c) {
@@ -758,7 +768,7 @@ struct GradSmem {
 template <typename E, int C, int DK>
 __global__ __launch_bounds__(kGT) void kla_bwd_grads_kernel(BwdParams p) {
   using L = GradSmem<C, DK>;
-  using R = PrepRec<C>;
+  using R = PrepRec<E, C>;
   using MM = Mma16<E>;
   constexpr int LK = L::LK, LC = L::LC;
   constexpr int NRT = C / 16, NKT = DK / 16;
@@ -783,31 +793,33 @@ __global__ __launch_bounds__(kGT) void kla_bwd_grads_kernel(BwdParams p) {
   const bool lead = own && half == 0;
   const int ra = 16 * a + lr;      // operand row of this lane
   const size_t sidx = (size_t)h * p.nslot + slot;
-  const float *rec = p.prep + sidx * R::FLOATS;
+  char *recb = R::at(p.prep, sidx);
+  const E *rm = R::mat(recb);
+  const float *rv = R::vec(recb);
   const float *Sg = p.states + sidx * DK * p.DV;
   const float *Dg = p.dstates + sidx * DK * p.DV;
 
   {
     TileLoad<E, C, DK, LK, kGT> lk, lq;
-    TileLoad<float, C, C, LC, kGT> lt, lp;
+    TileLoad<E, C, C, LC, kGT> lt, lp;
     TileLoad<float, 3, C, C, kGT> lb;  // b, gamma, ||k||^2 (adjacent in the record and in LDS)
     lk.issue(p.k, cl.row0, rows, 0, DK);
     lq.issue(p.q, cl.row0, rows, 0, DK);
-    lt.issue(rec + R::TM, 0, C, 0, C);
-    lp.issue(rec + R::PM, 0, C, 0, C);
-    lb.issue(rec + R::BETA, 0, 3, 0, C);
+    lt.issue(rm + R::TM, 0, C, 0, C);
+    lp.issue(rm + R::PM, 0, C, 0, C);
+    lb.issue(rv + R::BETA, 0, 3, 0, C);
     lk.put(sK);
     lq.put(sQ);
     lt.put(sT);
     lp.put(sP);
     lb.put(sb);
   }
-  const float gC = rec[R::GAM + C - 1];
+  const float gC = rv[R::GAM + C - 1];
   for (int r = t; r < C; r += kGT) {
     seta[r] = r < rows ? ld<E>(p.eta, cl.row0 + r) : 0.f;
     sdgam[r] = 0.f;
     sdd[r] = 0.f;
-    const float gr = rec[R::GAM + r];
+    const float gr = rv[R::GAM + r];
     sGm[r] = __expf(gr);
     sdec[r] = __expf(gC - gr);
   }
@@ -1011,7 +1023,7 @@ __global__ __launch_bounds__(kGT) void kla_bwd_grads_kernel(BwdParams p) {
           const float ex = __expf(sgam[r] - sgam[s_]);
           const float dA = s_ < r ? -da[i] : 0.f;
           const float dP = B2[r * LC + s_];
-          const float gE = rec[R::GE + r * C + s_];
+          const float gE = Elem<E>::to_f32(rm[R::GE + r * C + s_]);
           dgm[b][i] = dA * sb[r] * ex;
           dqk[b][i] = dP * ex;
           dee[b][i] = fmaf(dA * sb[r], gE, dP * sP[r * LC + s_]);
@@ -1109,11 +1121,11 @@ __global__ __launch_bounds__(kGT) void kla_bwd_grads_kernel(BwdParams p) {
 // ============================================================================
 // host side
 // ============================================================================
-template <int C, int DK>
+template <typename E, int C, int DK>
 struct BwdLayout {
   // workspace: prep records, then chunk-start states, then chunk-end state gradients
   static size_t prep_bytes(const ChunkArgs &a, int nslot) {
-    return ((size_t)a.H * nslot * PrepRec<C>::FLOATS * 4 + 255) / 256 * 256;
+    return ((size_t)a.H * nslot * PrepRec<E, C>::BYTES + 255) / 256 * 256;
   }
   static size_t state_bytes(const ChunkArgs &a, int nslot) {
     return ((size_t)a.H * nslot * DK * a.dv * 4 + 255) / 256 * 256;
@@ -1128,7 +1140,7 @@ int bwd_slots(const ChunkArgs &a) {
 template <typename E, int C, int DK>
 size_t bwd_workspace_bytes_t(const ChunkArgs &a) {
   const int ns = bwd_slots<C>(a);
-  return BwdLayout<C, DK>::prep_bytes(a, ns) + 2 * BwdLayout<C, DK>::state_bytes(a, ns);
+  return BwdLayout<E, C, DK>::prep_bytes(a, ns) + 2 * BwdLayout<E, C, DK>::state_bytes(a, ns);
 }
 
 template <typename E, int C, int DK>
@@ -1164,7 +1176,7 @@ hipError_t launch_bwd_t(const ChunkArgs &a, const ChunkBwdArgs &b, hipStream_t s
   p.beta_direct = a.beta_direct;
   char *ws = static_cast<char *>(a.workspace);
   p.prep = reinterpret_cast<float *>(ws);
-  const size_t pb = BwdLayout<C, DK>::prep_bytes(a, p.nslot), sb = BwdLayout<C, DK>::state_bytes(a, p.nslot);
+  const size_t pb = BwdLayout<E, C, DK>::prep_bytes(a, p.nslot), sb = BwdLayout<E, C, DK>::state_bytes(a, p.nslot);
   p.states = reinterpret_cast<float *>(ws + pb);
   p.dstates = reinterpret_cast<float *>(ws + pb + sb);
   const unsigned seq_blocks = (unsigned)((long long)a.num_seqs * a.H * p.nsl);
