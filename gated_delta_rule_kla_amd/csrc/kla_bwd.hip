@@ -52,7 +52,8 @@ struct BwdParams {
   void *dq, *dk, *dv;
   float *dg, *deta, *ds0;
   const int32_t *cu;
-  float *prep, *states, *dstates;
+  float *prep;
+  void *states, *dstates;  // chunk-start states and chunk-end state gradients, input element type
   int B, H, T, DV, nseq, nslot, nsl;
   int beta_direct;
 };
@@ -474,11 +475,12 @@ __global__ __launch_bounds__(kNT) void kla_bwd_states_kernel(BwdParams p) {
   for (int c = 0; c < nch; ++c) {
     const size_t slot = (size_t)h * p.nslot + sq.slot0 + c;
     if (w < NKT) {
-      float *st = p.states + slot * DK * p.DV;
+      E *st = static_cast<E *>(p.states) + slot * DK * p.DV;
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) st[(size_t)(16 * w + 4 * lg + i) * p.DV + col0 + 16 * ct + lr] = Sr[ct][i];
+        for (int i = 0; i < 4; ++i)
+          st[(size_t)(16 * w + 4 * lg + i) * p.DV + col0 + 16 * ct + lr] = Elem<E>::from_f32(Sr[ct][i]);
     }
     __syncthreads();  // the previous chunk's readers of sK, sV, sT are done
     lk.put(sK);
@@ -628,11 +630,12 @@ __global__ __launch_bounds__(kNT) void kla_bwd_dstates_kernel(BwdParams p) {
   for (int c = nch - 1; c >= 0; --c) {
     const size_t slot = (size_t)h * p.nslot + sq.slot0 + c;
     if (w < NKT) {
-      float *dst = p.dstates + slot * DK * p.DV;
+      E *dst = static_cast<E *>(p.dstates) + slot * DK * p.DV;
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dst[(size_t)(16 * w + 4 * lg + i) * p.DV + col0 + 16 * ct + lr] = dSr[ct][i];
+        for (int i = 0; i < 4; ++i)
+          dst[(size_t)(16 * w + 4 * lg + i) * p.DV + col0 + 16 * ct + lr] = Elem<E>::from_f32(dSr[ct][i]);
     }
     __syncthreads();
     lk.put(sK);
@@ -796,8 +799,8 @@ __global__ __launch_bounds__(kGT) void kla_bwd_grads_kernel(BwdParams p) {
   char *recb = R::at(p.prep, sidx);
   const E *rm = R::mat(recb);
   const float *rv = R::vec(recb);
-  const float *Sg = p.states + sidx * DK * p.DV;
-  const float *Dg = p.dstates + sidx * DK * p.DV;
+  const E *Sg = static_cast<const E *>(p.states) + sidx * DK * p.DV;
+  const E *Dg = static_cast<const E *>(p.dstates) + sidx * DK * p.DV;
 
   {
     TileLoad<E, C, DK, LK, kGT> lk, lq;
@@ -833,7 +836,7 @@ __global__ __launch_bounds__(kGT) void kla_bwd_grads_kernel(BwdParams p) {
   float gcp = 0.f;  // partial <S, dS'>
 
   // slice js + 1 of S, dS', V and dO is loaded while slice js is computed
-  TileLoad<float, DK, kNS, kLS, kGT> ls, ld_;
+  TileLoad<E, DK, kNS, kLS, kGT> ls, ld_;
   TileLoad<E, C, kNS, kLS, kGT> lv, lo;
   auto issue = [&](int js) {
     const int col0 = js * kNS;
@@ -1128,7 +1131,7 @@ struct BwdLayout {
     return ((size_t)a.H * nslot * PrepRec<E, C>::BYTES + 255) / 256 * 256;
   }
   static size_t state_bytes(const ChunkArgs &a, int nslot) {
-    return ((size_t)a.H * nslot * DK * a.dv * 4 + 255) / 256 * 256;
+    return ((size_t)a.H * nslot * DK * a.dv * sizeof(E) + 255) / 256 * 256;
   }
 };
 
@@ -1177,8 +1180,8 @@ hipError_t launch_bwd_t(const ChunkArgs &a, const ChunkBwdArgs &b, hipStream_t s
   char *ws = static_cast<char *>(a.workspace);
   p.prep = reinterpret_cast<float *>(ws);
   const size_t pb = BwdLayout<E, C, DK>::prep_bytes(a, p.nslot), sb = BwdLayout<E, C, DK>::state_bytes(a, p.nslot);
-  p.states = reinterpret_cast<float *>(ws + pb);
-  p.dstates = reinterpret_cast<float *>(ws + pb + sb);
+  p.states = ws + pb;
+  p.dstates = ws + pb + sb;
   const unsigned seq_blocks = (unsigned)((long long)a.num_seqs * a.H * p.nsl);
   // the two scans: (sequence, head) groups padded to whole rounds of 8, times the slices
   const unsigned groups8 = (unsigned)(((long long)a.num_seqs * a.H + 7) / 8 * 8);

@@ -205,9 +205,9 @@ kla_status_t kla_gdn_decode_step(const void *q, const void *k, const void *v,
  *   workspace       kla_chunk_bwd_workspace_bytes(...) bytes of device memory
  *                   (16-byte aligned), owned by the caller, no initialisation
  *                   needed; holds per (chunk, head) T = (I + A)^-1, the causal
- *                   scores and the decayed Gram matrix (in `dtype`), the
- *                   coefficient and decay vectors, the chunk-start state and the
- *                   chunk-end state gradient (fp32).
+ *                   scores and the decayed Gram matrix, the coefficient and
+ *                   decay vectors (fp32), the chunk-start state and the
+ *                   chunk-end state gradient (matrices and states in `dtype`).
  *
  * Every pointer is 16-byte aligned device memory; gradient buffers must not
  * alias the inputs.  Positions of the gradient tensors that belong to no
@@ -243,8 +243,8 @@ kla_status_t kla_gdn_chunk_bwd(const void *q, const void *k, const void *v,
 
 /*
  * kla_chunk_bwd_workspace_bytes -- device workspace kla_chunk_bwd and
- * kla_gdn_chunk_bwd need (host-only): per (chunk, head) 3 C^2 e + 16 C bytes,
- * e = 2 for bf16 and 4 for fp32, plus 8 dk dv bytes (rounded up per region).  0 when no workspace is needed
+ * kla_gdn_chunk_bwd need (host-only): per (chunk, head) 3 C^2 e + 16 C bytes
+ * plus 2 dk dv e bytes, e = 2 for bf16 and 4 for fp32 (rounded up per region).  0 when no workspace is needed
  * or for arguments kla_chunk_bwd would reject.
  */
 size_t kla_chunk_bwd_workspace_bytes(const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,

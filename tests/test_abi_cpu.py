@@ -286,10 +286,10 @@ def test_chunk_bwd_workspace_bytes():
 
     r256 = lambda x: (x + 255) // 256 * 256
     # per (chunk, head): T, P and K K^T . E (C x C in the input element type) + 4 C fp32 vectors;
-    # chunk-start state and chunk-end state gradient (dk x dv fp32 each); B=2 x ceil(100/64)=2
-    # chunks x H=4
+    # chunk-start state and chunk-end state gradient (dk x dv each, in the input element type);
+    # B=2 x ceil(100/64)=2 chunks x H=4
     slots = 2 * 2 * 4
-    assert ws() == r256(slots * (3 * 64 * 64 * 2 + 4 * 64 * 4)) + 2 * r256(slots * 128 * 128 * 4)
+    assert ws() == r256(slots * (3 * 64 * 64 * 2 + 4 * 64 * 4)) + 2 * r256(slots * 128 * 128 * 2)
     assert ws(dtype=1, chunk=16, dk=32, dv=16) == (r256(2 * 7 * 4 * (3 * 16 * 16 + 4 * 16) * 4)
                                                    + 2 * r256(2 * 7 * 4 * 32 * 16 * 4))
     assert ws(T=0) == 0 and ws(N=0, B=0) == 0 and ws(dk=96) == 0
