@@ -765,7 +765,7 @@ struct GradSmem {
   static constexpr int BETA = VEC, GAM = BETA + C, NRM = GAM + C, ETA = NRM + C, DGAM = ETA + C, DD = DGAM + C;
   static constexpr int DB1 = DD + C, DB2 = DB1 + C, DGE = DB2 + C, CF = DGE + C, GM = CF + C, DEC = GM + C;
   static constexpr int RED = DEC + C;
-  static constexpr int FLOATS = RED + kGT;
+  static constexpr int FLOATS = RED + kGT / 64;
 };
 
 template <typename E, int C, int DK>
@@ -961,7 +961,12 @@ __global__ __launch_bounds__(kGT) void kla_bwd_grads_kernel(BwdParams p) {
   // ---------------- C x C stage ---------------------------------------------
   // (the slice region now holds B1 and B2; P stays in sP until dEE replaces it)
   float *B1 = sm + L::B1, *B2 = sm + L::B2;
-  sred[t] = gcp;
+  {
+    float gs = gcp;  // <S, dS'>: one partial sum per wave
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) gs += __shfl_xor(gs, off);
+    if (lane == 0) sred[w] = gs;
+  }
   __syncthreads();
   if (own) {
 #pragma unroll
@@ -1073,25 +1078,39 @@ __global__ __launch_bounds__(kGT) void kla_bwd_grads_kernel(BwdParams p) {
     }
   }
   // per-row scalars: dgamma, then dg = reverse running sum; db, deta, the norm term
-  for (int r = t; r < C; r += kGT) {
+  // (eight lanes per row, whole rows per wave: C is a multiple of 8)
+  for (int r = t >> 3; r < C; r += kGT / 8) {
+    const int j = t & 7;
     float rs = 0.f, cs = 0.f;
-    for (int s_ = 0; s_ < C; ++s_) {
+    for (int s_ = j; s_ < C; s_ += 8) {
       rs += sP[r * LC + s_];
       cs += sP[s_ * LC + r];
     }
-    sdge[r] = sdgam[r] * sGm[r] - sdd[r] * sdec[r] + rs - cs;
+#pragma unroll
+    for (int off = 4; off >= 1; off >>= 1) {
+      rs += __shfl_xor(rs, off);
+      cs += __shfl_xor(cs, off);
+    }
+    if (j == 0) sdge[r] = sdgam[r] * sGm[r] - sdd[r] * sdec[r] + rs - cs;
   }
   __syncthreads();
-  if (t == 0) {
-    float gcs = 0.f, ddd = 0.f;
-    for (int i = 0; i < kGT; ++i) gcs += sred[i];
-    for (int r = 0; r < C; ++r) ddd = fmaf(sdd[r], sdec[r], ddd);
-    sdge[C - 1] += gcs * __expf(gC) + ddd;
-    float acc = 0.f;
-    for (int r = C - 1; r >= 0; --r) {
-      acc += sdge[r];
-      sdge[r] = acc;
+  if (w == 0) {
+    // the chunk-end terms go to the last row, then dg_r = sum_{r' >= r} dgamma_r' (lane r)
+    float gcs = lane < kGT / 64 ? sred[lane] : 0.f;
+    float ddd = lane < C ? sdd[lane] * sdec[lane] : 0.f;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      gcs += __shfl_xor(gcs, off);
+      ddd += __shfl_xor(ddd, off);
     }
+    float v = lane < C ? sdge[lane] : 0.f;
+    if (lane == C - 1) v += gcs * __expf(gC) + ddd;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float u = __shfl_down(v, off);
+      if (lane + off < 64) v += u;
+    }
+    if (lane < C) sdge[lane] = v;
   }
   for (int r = t; r < C; r += kGT) {
     const float db = sdb1[r] + sdb2[r];
