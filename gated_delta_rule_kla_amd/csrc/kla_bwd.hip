@@ -982,10 +982,13 @@ __global__ __launch_bounds__(kGT) void kla_bwd_grads_kernel(BwdParams p) {
   }
   __syncthreads();
   // db_s (first part) = sum_r T_rs dW_rs;  Y = (dW Diag(b)) T^T
-  for (int s_ = t; s_ < C; s_ += kGT) {
+  // (eight lanes per column, whole columns per wave: C is a multiple of 8)
+  for (int s_ = t >> 3; s_ < C; s_ += kGT / 8) {
     float acc = 0.f;
-    for (int r = s_; r < C; ++r) acc = fmaf(sT[r * LC + s_], B1[r * LC + s_], acc);
-    sdb1[s_] = acc;
+    for (int r = s_ + (t & 7); r < C; r += 8) acc = fmaf(sT[r * LC + s_], B1[r * LC + s_], acc);
+#pragma unroll
+    for (int off = 4; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+    if ((t & 7) == 0) sdb1[s_] = acc;
   }
   f32x4 y[NRT];
 #pragma unroll
