@@ -856,32 +856,42 @@ __global__ __launch_bounds__(kGT) void kla_bwd_grads_kernel(BwdParams p) {
     if (js + 1 < p.nsl) issue(js + 1);
     __syncthreads();
     for (int e = t; e < DK * kNS; e += kGT) gcp = fmaf(sS[(e / kNS) * kLS + e % kNS], sD[(e / kNS) * kLS + e % kNS], gcp);
-    // (A) K S, Q S, K dS' for this wave's rows; X = V - Diag(Gam) K S
+    // Phases A-C for row tile a, split over the wave pair: the lead forms K S, Q S, X, U
+    // and dX (= dV) and the dGam row sums; its partner K dS', dU and the dd row sums.
+    // (A) lead: K S, Q S and X = V - Diag(Gam) K S; partner: K dS'
     f32x4 ks = z4, qs = z4, kd = z4;
     if (lead) {
 #pragma unroll 4
       for (int k0 = 0; k0 < DK; k0 += 16) {
         const int kk = k0 + 4 * lg;
-        const f32x4 ka = vec4(sK + ra * LK + kk), qa = vec4(sQ + ra * LK + kk);
-        const f32x4 sv = gat4(sS + kk * kLS + lr, kLS), dv = gat4(sD + kk * kLS + lr, kLS);
-        ks = MM::run(ka, sv, ks);
-        qs = MM::run(qa, sv, qs);
-        kd = MM::run(ka, dv, kd);
+        const f32x4 sv = gat4(sS + kk * kLS + lr, kLS);
+        ks = MM::run(vec4(sK + ra * LK + kk), sv, ks);
+        qs = MM::run(vec4(sQ + ra * LK + kk), sv, qs);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * a + 4 * lg + i;
         sX[r * kLS + lr] = sV[r * kLS + lr] - sGm[r] * ks[i];
       }
+    } else if (own) {
+#pragma unroll 4
+      for (int k0 = 0; k0 < DK; k0 += 16) {
+        const int kk = k0 + 4 * lg;
+        kd = MM::run(vec4(sK + ra * LK + kk), gat4(sD + kk * kLS + lr, kLS), kd);
+      }
     }
     __syncthreads();
-    // (B) U = T Diag(b) X;  dU = P^T dO + Diag(d) K dS'   (T, P lower triangular)
-    f32x4 u = z4, du = z4;
+    // (B) lead: U = T Diag(b) X; partner: dU = P^T dO + Diag(d) K dS'  (T, P lower triangular)
     if (lead) {
+      f32x4 u = z4;
       for (int k0 = 0; k0 < 16 * (a + 1); k0 += 16) {
         const int s_ = k0 + 4 * lg;
         u = MM::run(vec4(sT + ra * LC + s_) * vec4(sb + s_), gat4(sX + s_ * kLS + lr, kLS), u);
       }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sU[(16 * a + 4 * lg + i) * kLS + lr] = u[i];
+    } else if (own) {
+      f32x4 du = z4;
       for (int k0 = 16 * a; k0 < C; k0 += 16) {
         const int s_ = k0 + 4 * lg;
         du = MM::run(gat4(sP + s_ * LC + ra, LC), gat4(sO + s_ * kLS + lr, kLS), du);
@@ -889,20 +899,19 @@ __global__ __launch_bounds__(kGT) void kla_bwd_grads_kernel(BwdParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * a + 4 * lg + i;
-        du[i] = fmaf(sdec[r], kd[i], du[i]);
-        sU[r * kLS + lr] = u[i];
-        sdU[r * kLS + lr] = du[i];
+        sdU[r * kLS + lr] = fmaf(sdec[r], kd[i], du[i]);
       }
     }
     __syncthreads();
+    // (C) lead: dX = Diag(b) T^T dU (= dV) and sum_c (Q S . dO - K S . dX);
+    //     partner: sum_c (K dS' . U)
     if (lead) {
-      // (C) dX = Diag(b) T^T dU (= dV); row sums for dGam and dd
       f32x4 dx = z4;
       for (int k0 = 16 * a; k0 < C; k0 += 16) {
         const int s_ = k0 + 4 * lg;
         dx = MM::run(gat4(sT + s_ * LC + ra, LC), gat4(sdU + s_ * kLS + lr, kLS), dx);
       }
-      float pg[4], pd[4];
+      float pg[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * a + 4 * lg + i;
@@ -910,22 +919,26 @@ __global__ __launch_bounds__(kGT) void kla_bwd_grads_kernel(BwdParams p) {
         sdX[r * kLS + lr] = dx[i];
         if (r < rows) static_cast<E *>(p.dv)[(cl.row0 + r) * p.DV + col0 + lr] = Elem<E>::from_f32(dx[i]);
         pg[i] = qs[i] * sO[r * kLS + lr] - ks[i] * dx[i];
-        pd[i] = kd[i] * u[i];
       }
 #pragma unroll
-      for (int off = 8; off >= 1; off >>= 1) {
+      for (int off = 8; off >= 1; off >>= 1)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pg[i] += __shfl_xor(pg[i], off);
-          pd[i] += __shfl_xor(pd[i], off);
-        }
-      }
+        for (int i = 0; i < 4; ++i) pg[i] += __shfl_xor(pg[i], off);
       if (lr == 0) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          sdgam[16 * a + 4 * lg + i] += pg[i];
-          sdd[16 * a + 4 * lg + i] += pd[i];
-        }
+        for (int i = 0; i < 4; ++i) sdgam[16 * a + 4 * lg + i] += pg[i];
+      }
+    } else if (own) {
+      float pd[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pd[i] = kd[i] * sU[(16 * a + 4 * lg + i) * kLS + lr];
+#pragma unroll
+      for (int off = 8; off >= 1; off >>= 1)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pd[i] += __shfl_xor(pd[i], off);
+      if (lr == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sdd[16 * a + 4 * lg + i] += pd[i];
       }
     }
     __syncthreads();  // the rows of dU, dX and U the lead waves wrote
