@@ -764,7 +764,8 @@ struct GradSmem {
   static constexpr int VEC = SL + SL_SIZE;
   static constexpr int BETA = VEC, GAM = BETA + C, NRM = GAM + C, ETA = NRM + C, DGAM = ETA + C, DD = DGAM + C;
   static constexpr int DB1 = DD + C, DB2 = DB1 + C, DGE = DB2 + C, CF = DGE + C, GM = CF + C, DEC = GM + C;
-  static constexpr int RED = DEC + C;
+  static constexpr int DB3 = DEC + C;  // the partner waves' part of the db row sums
+  static constexpr int RED = DB3 + C;
   static constexpr int FLOATS = RED + kGT / 64;
 };
 
@@ -783,6 +784,7 @@ __global__ __launch_bounds__(kGT) void kla_bwd_grads_kernel(BwdParams p) {
   float *sU = sm + L::U, *sdU = sm + L::DU, *sdX = sm + L::DX;
   float *sb = sm + L::BETA, *sgam = sm + L::GAM, *snrm = sm + L::NRM, *seta = sm + L::ETA;
   float *sdgam = sm + L::DGAM, *sdd = sm + L::DD, *sdb1 = sm + L::DB1, *sdb2 = sm + L::DB2;
+  float *sdb3 = sm + L::DB3;
   float *sdge = sm + L::DGE, *scf = sm + L::CF, *sred = sm + L::RED, *sGm = sm + L::GM, *sdec = sm + L::DEC;
   const int slot = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
   const ChunkLoc cl = chunk_loc(p, slot, h, C);
@@ -1003,12 +1005,15 @@ __global__ __launch_bounds__(kGT) void kla_bwd_grads_kernel(BwdParams p) {
     for (int off = 4; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
     if ((t & 7) == 0) sdb1[s_] = acc;
   }
+  // the wave pair of row tile a splits the C x C tiles: column block b goes to the wave
+  // whose half equals b mod 2
   f32x4 y[NRT];
 #pragma unroll
   for (int b = 0; b < NRT; ++b) y[b] = z4;
-  if (lead) {
+  if (own) {
 #pragma unroll
     for (int b = 0; b < NRT; ++b) {
+      if ((b & 1) != half) continue;
       // Y[r][s] = sum_{m <= s} dW[r][m] b_m T[s][m]
       for (int k0 = 0; k0 < 16 * (b + 1); k0 += 16) {
         const int m = k0 + 4 * lg;
@@ -1017,20 +1022,23 @@ __global__ __launch_bounds__(kGT) void kla_bwd_grads_kernel(BwdParams p) {
     }
   }
   __syncthreads();
-  if (lead) {
+  if (own) {
 #pragma unroll
     for (int b = 0; b < NRT; ++b)
+      if ((b & 1) == half) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) B1[(16 * a + 4 * lg + i) * LC + 16 * b + lr] = y[b][i];  // Y over dW
+        for (int i = 0; i < 4; ++i) B1[(16 * a + 4 * lg + i) * LC + 16 * b + lr] = y[b][i];  // Y over dW
+      }
   }
   __syncthreads();
   // dA = -T^T Y (strictly lower); per entry dG = dA b_r E, dQK = dP E,
   // dEE = dA b_r (G . E) + dP P, db_r += dA (G . E)
   f32x4 dgm[NRT], dqk[NRT], dee[NRT];
   float dbr[4] = {0.f, 0.f, 0.f, 0.f};
-  if (lead) {
+  if (own) {
 #pragma unroll
     for (int b = 0; b < NRT; ++b) {
+      if ((b & 1) != half) continue;
       f32x4 da = z4;
       if (b <= a) {
         // dA[r][s] = -sum_{m >= r} T[m][r] Y[m][s]
@@ -1061,18 +1069,20 @@ __global__ __launch_bounds__(kGT) void kla_bwd_grads_kernel(BwdParams p) {
       for (int i = 0; i < 4; ++i) dbr[i] += __shfl_xor(dbr[i], off);
   }
   __syncthreads();
-  if (lead) {
+  if (own) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      if (lr == 0) sdb2[16 * a + 4 * lg + i] = dbr[i];
+      if (lr == 0) (half ? sdb3 : sdb2)[16 * a + 4 * lg + i] = dbr[i];
 #pragma unroll
     for (int b = 0; b < NRT; ++b)
+      if ((b & 1) == half) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * a + 4 * lg + i, s_ = 16 * b + lr;
-        B1[r * LC + s_] = dgm[b][i];
-        B2[r * LC + s_] = dqk[b][i];
-        sP[r * LC + s_] = dee[b][i];
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * a + 4 * lg + i, s_ = 16 * b + lr;
+          B1[r * LC + s_] = dgm[b][i];
+          B2[r * LC + s_] = dqk[b][i];
+          sP[r * LC + s_] = dee[b][i];
+        }
       }
   }
   __syncthreads();
@@ -1129,7 +1139,7 @@ __global__ __launch_bounds__(kGT) void kla_bwd_grads_kernel(BwdParams p) {
     if (lane < C) sdge[lane] = v;
   }
   for (int r = t; r < C; r += kGT) {
-    const float db = sdb1[r] + sdb2[r];
+    const float db = sdb1[r] + sdb2[r] + sdb3[r];
     const float den = snrm[r] + p.eps;
     scf[r] = (p.beta_direct || r >= rows) ? 0.f : -2.f * seta[r] * db / (den * den);
     if (r < rows) p.deta[cl.row0 + r] = p.beta_direct ? db : db / den;
