@@ -647,68 +647,47 @@ __global__ __launch_bounds__(kNT) void kla_bwd_dstates_kernel(BwdParams p) {
     if (c > 0) issue(c - 1);
     __syncthreads();
     const float gC = sgam[C - 1];
-    // dU = P^T dO + Diag(d) K dS'  (P lower triangular), row tile w
-    if (w < NRT) {
-      const int ra = 16 * w + lr;
-      f32x4 a[CT], b[CT];
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct) a[ct] = b[ct] = z4;
-      for (int k0 = 16 * w; k0 < C; k0 += 16) {
-        const f32x4 pa = gat4(sP + (k0 + 4 * lg) * LC + ra, LC);
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct)
-          a[ct] = MM::run(pa, gat4(sO + (k0 + 4 * lg) * LS + 16 * ct + lr, LS), a[ct]);
-      }
+    // The row-tile phases: wave w takes row tile w & 3 and column tile w >> 2 (with 16
+    // state columns waves 4-7 have none and wait).
+    const int rtw = w & 3, ctw = w >> 2;
+    const bool tile = rtw < NRT && ctw < CT;  // (uniform per wave)
+    const int ra = 16 * rtw + lr, cc = 16 * ctw + lr;
+    // dU = P^T dO + Diag(d) K dS'  (P lower triangular)
+    if (tile) {
+      f32x4 a = z4, b = z4;
+      for (int k0 = 16 * rtw; k0 < C; k0 += 16)
+        a = MM::run(gat4(sP + (k0 + 4 * lg) * LC + ra, LC), gat4(sO + (k0 + 4 * lg) * LS + cc, LS), a);
 #pragma unroll 4
-      for (int k0 = 0; k0 < DK; k0 += 16) {
-        const f32x4 ka = vec4(sK + ra * LK + k0 + 4 * lg);
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct)
-          b[ct] = MM::run(ka, gat4(sS + (k0 + 4 * lg) * LS + 16 * ct + lr, LS), b[ct]);
-      }
+      for (int k0 = 0; k0 < DK; k0 += 16)
+        b = MM::run(vec4(sK + ra * LK + k0 + 4 * lg), gat4(sS + (k0 + 4 * lg) * LS + cc, LS), b);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = 16 * w + 4 * lg + i;
-        const float dr = __expf(gC - sgam[r]);
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct) sU[r * LS + 16 * ct + lr] = fmaf(dr, b[ct][i], a[ct][i]);
+        const int r = 16 * rtw + 4 * lg + i;
+        sU[r * LS + cc] = fmaf(__expf(gC - sgam[r]), b[i], a[i]);
       }
     }
     __syncthreads();
     // dX = Diag(b) T^T dU; keep Diag(Gam) dX and Diag(Gam) dO for the state step
-    f32x4 gdx[CT], gdo[CT];
-    if (w < NRT) {
-      const int ra = 16 * w + lr;
-      f32x4 x[CT];
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct) x[ct] = z4;
-      for (int k0 = 16 * w; k0 < C; k0 += 16) {
-        const f32x4 ta = gat4(sT + (k0 + 4 * lg) * LC + ra, LC);
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct)
-          x[ct] = MM::run(ta, gat4(sU + (k0 + 4 * lg) * LS + 16 * ct + lr, LS), x[ct]);
-      }
+    f32x4 gdx = z4, gdo = z4;
+    if (tile) {
+      f32x4 x = z4;
+      for (int k0 = 16 * rtw; k0 < C; k0 += 16)
+        x = MM::run(gat4(sT + (k0 + 4 * lg) * LC + ra, LC), gat4(sU + (k0 + 4 * lg) * LS + cc, LS), x);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = 16 * w + 4 * lg + i;
+        const int r = 16 * rtw + 4 * lg + i;
         const float G = __expf(sgam[r]);
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
-          gdx[ct][i] = G * sb[r] * x[ct][i];
-          gdo[ct][i] = G * sO[r * LS + 16 * ct + lr];
-        }
+        gdx[i] = G * sb[r] * x[i];
+        gdo[i] = G * sO[r * LS + cc];
       }
     }
     __syncthreads();
-    if (w < NRT) {
+    if (tile) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = 16 * w + 4 * lg + i;
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
-          sU[r * LS + 16 * ct + lr] = gdx[ct][i];
-          sO[r * LS + 16 * ct + lr] = gdo[ct][i];
-        }
+        const int r = 16 * rtw + 4 * lg + i;
+        sU[r * LS + cc] = gdx[i];
+        sO[r * LS + cc] = gdo[i];
       }
     }
     __syncthreads();
