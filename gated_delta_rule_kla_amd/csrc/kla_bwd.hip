@@ -489,48 +489,34 @@ __global__ __launch_bounds__(kNT) void kla_bwd_states_kernel(BwdParams p) {
     lb.put(sb);  // sb and sgam are adjacent in LDS: rows of stride C
     if (c + 1 < nch) issue(c + 1);
     __syncthreads();
-    // Diag(b) X = Diag(b) (V - Diag(Gam) K S), row tile w
-    if (w < NRT) {
-      const int ra = 16 * w + lr;
-      f32x4 ks[CT];
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct) ks[ct] = z4;
+    // The row-tile phases: wave w takes row tile w & 3 and column tile w >> 2 (with 16
+    // state columns waves 4-7 have none and wait).
+    const int rtw = w & 3, ctw = w >> 2;
+    const bool tile = rtw < NRT && ctw < CT;  // (uniform per wave)
+    const int ra = 16 * rtw + lr, cc = 16 * ctw + lr;
+    // Diag(b) X = Diag(b) (V - Diag(Gam) K S)
+    if (tile) {
+      f32x4 ks = z4;
 #pragma unroll 4
-      for (int k0 = 0; k0 < DK; k0 += 16) {
-        const f32x4 ka = vec4(sK + ra * LK + k0 + 4 * lg);
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct)
-          ks[ct] = MM::run(ka, gat4(sS + (k0 + 4 * lg) * LS + 16 * ct + lr, LS), ks[ct]);
-      }
+      for (int k0 = 0; k0 < DK; k0 += 16)
+        ks = MM::run(vec4(sK + ra * LK + k0 + 4 * lg), gat4(sS + (k0 + 4 * lg) * LS + cc, LS), ks);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = 16 * w + 4 * lg + i;
-        const float G = __expf(sgam[r]);
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct)
-          sX[r * LS + 16 * ct + lr] = sb[r] * (sV[r * LS + 16 * ct + lr] - G * ks[ct][i]);
+        const int r = 16 * rtw + 4 * lg + i;
+        sX[r * LS + cc] = sb[r] * (sV[r * LS + cc] - __expf(sgam[r]) * ks[i]);
       }
     }
     __syncthreads();
     // Diag(d) U with U = T Diag(b) X (T lower triangular), into sV
     const float gC = sgam[C - 1];
-    if (w < NRT) {
-      const int ra = 16 * w + lr;
-      f32x4 u[CT];
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct) u[ct] = z4;
-      for (int k0 = 0; k0 < 16 * (w + 1); k0 += 16) {
-        const f32x4 ta = vec4(sT + ra * LC + k0 + 4 * lg);
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct)
-          u[ct] = MM::run(ta, gat4(sX + (k0 + 4 * lg) * LS + 16 * ct + lr, LS), u[ct]);
-      }
+    if (tile) {
+      f32x4 u = z4;
+      for (int k0 = 0; k0 < 16 * (rtw + 1); k0 += 16)
+        u = MM::run(vec4(sT + ra * LC + k0 + 4 * lg), gat4(sX + (k0 + 4 * lg) * LS + cc, LS), u);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = 16 * w + 4 * lg + i;
-        const float dr = __expf(gC - sgam[r]);
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct) sV[r * LS + 16 * ct + lr] = dr * u[ct][i];
+        const int r = 16 * rtw + 4 * lg + i;
+        sV[r * LS + cc] = __expf(gC - sgam[r]) * u[i];
       }
     }
     __syncthreads();
