@@ -95,6 +95,8 @@ def test_bwd_fp32_chunk16(dk):
     (2, 2, 129, 64, 64),       # dk 64
     (1, 1, 64, 128, 32),       # exactly one chunk
     (1, 1, 7, 128, 128),       # shorter than one chunk
+    (1, 3, 200, 128, 48),      # dv not a multiple of 32: 16-column scan slices
+    (2, 1, 90, 64, 16),        # a single 16-column slice, dk 64
 ])
 def test_bwd_bf16(B, H, T, dk, dv):
     x = inputs.make_prefill(B=B, H=H, T=T, dk=dk, dv=dv, chunk=64, s0_std=0.02, seed=B * H + T + 1,
