@@ -12,8 +12,8 @@ Also measured in the same run and reported in the same JSON line:
   * decode: 512 consecutive kla_decode_step calls, N=256 sequences x H=16,
     128x128 fp32 state (HBM-bound; reported as GB/s);
   * backward: kla_chunk_bwd on the prefill workload (steps/10 timed calls);
-  * cpu_baseline: the fp64 CPU oracle on a bounded sample of the prefill
-    workload, on this host's cores.
+  * cpu_baseline: the fp64 CPU oracle on this host's cores (a process pool),
+    on the whole prefill workload and bounded samples of the others.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--mode all|prefill|decode|backward]
 """
@@ -111,7 +111,7 @@ def bench_prefill(steps, warmup):
     from gated_delta_rule_kla_amd import inputs, kla
 
     dev = torch.device("cuda:0")
-    x = inputs.prefill_config(1)
+    x = _workload(1)
     B, H, T, dk, dv = x.dims
     q, k, v, g, eta = (t.to(dev) for t in (x.q, x.k, x.v, x.g, x.eta))
     o = torch.empty((B, H, T, dv), dtype=q.dtype, device=dev)
@@ -141,7 +141,7 @@ def bench_prefill_other(steps, warmup):
     dev = torch.device("cuda:0")
     res = {}
     for i in (2, 4):
-        x = inputs.prefill_config(i)
+        x = _workload(i)
         B, H, T, dk, dv = x.dims
         q, k, v, g, eta = (t.to(dev) for t in (x.q, x.k, x.v, x.g, x.eta))
         s0 = x.initial_state.to(dev) if x.initial_state is not None else None
@@ -179,7 +179,7 @@ def bench_backward(steps, warmup):
     from gated_delta_rule_kla_amd import inputs, kla
 
     dev = torch.device("cuda:0")
-    x = inputs.prefill_config(1)
+    x = _workload(1)
     B, H, T, dk, dv = x.dims
     q, k, v, g, eta = (t.to(dev) for t in (x.q, x.k, x.v, x.g, x.eta))
     do_h, ds_h = inputs.make_upstream(x, 101)
@@ -208,7 +208,7 @@ def bench_gdn(steps, warmup, decode_steps=512):
     from gated_delta_rule_kla_amd import inputs, kla
 
     dev = torch.device("cuda:0")
-    x = inputs.unit_keys(inputs.prefill_config(1))
+    x = inputs.unit_keys(_workload(1))
     B, H, T, dk, dv = x.dims
     q, k, v, g, beta = (t.to(dev) for t in (x.q, x.k, x.v, x.g, x.eta))
     o = torch.empty((B, H, T, dv), dtype=q.dtype, device=dev)
@@ -223,7 +223,7 @@ def bench_gdn(steps, warmup, decode_steps=512):
         pstep(i)
     p_ms, _ = time_launches(pstep, steps, stream)
     del q, k, v, g, beta, o, S, ws
-    d = inputs.unit_keys(inputs.decode_config(steps=decode_steps))
+    d = inputs.unit_keys(_workload(3) if decode_steps == 512 else inputs.decode_config(steps=decode_steps))
     dq, dk_, dv_, dg, db = (t.to(dev) for t in (d.q, d.k, d.v, d.g, d.eta))
     st = d.state.to(dev)
     do = torch.empty((d.q.shape[1], d.q.shape[2], d.v.shape[-1]), dtype=dq.dtype, device=dev)
@@ -237,12 +237,43 @@ def bench_gdn(steps, warmup, decode_steps=512):
     return dict(prefill_ms=p_ms, decode_ms=d_ms, tokens=B * T)
 
 
+def bench_decode_large(steps_total=64, warmup=16, N=1024):
+    """The decode step with a state four times the 256 MB Infinity Cache (N=1024
+    sequences x 16 heads x 128 x 128 fp32 = 1 GiB), so that no step can find
+    the previous step's writes in that cache: the figure checks that the decode
+    rate is HBM's, not the cache's."""
+    import torch
+    from gated_delta_rule_kla_amd import inputs, kla
+
+    dev = torch.device("cuda:0")
+    d = inputs.decode_config(steps=steps_total, N=N)
+    H, dk = d.q.shape[2:]
+    dv = d.v.shape[-1]
+    q, k, v, g, eta = (t.to(dev) for t in (d.q, d.k, d.v, d.g, d.eta))
+    st = d.state.to(dev)
+    o = torch.empty((N, H, dv), dtype=q.dtype, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        kla.decode_step(q[i], k[i], v[i], g[i], eta[i], d.eps, st, out=o)
+
+    for i in range(warmup):
+        step(i % steps_total)
+    ms, _ = time_launches(step, steps_total, stream)
+    byts, _ = decode_algorithmic(N, H, dk, dv)
+    del q, k, v, g, eta, st, o
+    torch.cuda.empty_cache()
+    return {"workload": f"KLA decode step, N={N} H={H} dk={dk} dv={dv}, fp32 state of {N * H * dk * dv * 4 >> 20} "
+                        f"MiB, {steps_total} consecutive steps",
+            "ms_per_step": ms, "GB/s": byts / ms / 1e6, "hbm_frac": byts / ms / 1e6 / HBM_PEAK_GBS}
+
+
 def bench_decode(steps_total=512, warmup=64):
     import torch
     from gated_delta_rule_kla_amd import inputs, kla
 
     dev = torch.device("cuda:0")
-    d = inputs.decode_config(steps=steps_total)
+    d = _workload(3) if steps_total == 512 else inputs.decode_config(steps=steps_total)
     N, H, dk = d.q.shape[1:]
     dv = d.v.shape[-1]
     q, k, v, g, eta = (t.to(dev) for t in (d.q, d.k, d.v, d.g, d.eta))
@@ -261,26 +292,111 @@ def bench_decode(steps_total=512, warmup=64):
                 steps=steps_total)
 
 
-def cpu_baseline(rows=4):
-    """The fp64 oracle, as it stands, on batch rows [0, rows) of the prefill
-    workload (all 16 heads, all 4096 tokens), single-threaded BLAS.  With the
-    default rows=4 the sample is the whole workload (a few seconds of CPU)."""
+# Generated workloads, kept for the whole run: the CPU baseline and the GPU legs
+# use the same seeded tensors (generating the largest takes tens of seconds).
+# The CPU-baseline pool's workers are forked after it is filled, so they inherit
+# it without copying (they only read it).
+_CPU_WORK = {}
+
+
+def _workload(i):
+    from gated_delta_rule_kla_amd import inputs
+    if i not in _CPU_WORK:
+        _CPU_WORK[i] = inputs.decode_config() if i == 3 else inputs.prefill_config(i)
+    return _CPU_WORK[i]
+
+
+def _cpu_task(task):
+    """One (workload, sequence, head) unit of the oracle, timed in a worker."""
+    import numpy as np
+    from gated_delta_rule_kla_amd import inputs
+    from oracle import kla_decode_step, kla_recurrence
+
+    f = inputs.to_f64
+    kind, i, a, b, h = task
+    t0 = time.perf_counter()
+    if kind == "prefill":
+        x = _CPU_WORK[i]
+        if x.cu_seqlens is None:
+            row, lo, hi, n = a, 0, x.q.shape[2], a
+        else:
+            row, lo, hi, n = 0, int(x.cu_seqlens[a]), int(x.cu_seqlens[a + 1]), a
+        s0 = None if x.initial_state is None else f(x.initial_state[n, h])
+        kla_recurrence(f(x.q[row, h, lo:hi]), f(x.k[row, h, lo:hi]), f(x.v[row, h, lo:hi]),
+                       f(x.g[row, h, lo:hi]), f(x.eta[row, h, lo:hi]), x.eps, s0)
+        units = hi - lo
+    else:  # decode: every step of one (sequence, head)
+        d = _CPU_WORK[i]
+        S = f(d.state[a:a + 1, h:h + 1])
+        for s in range(d.q.shape[0]):
+            _, S = kla_decode_step(f(d.q[s, a:a + 1, h:h + 1]), f(d.k[s, a:a + 1, h:h + 1]),
+                                   f(d.v[s, a:a + 1, h:h + 1]), f(d.g[s, a:a + 1, h:h + 1]),
+                                   f(d.eta[s, a:a + 1, h:h + 1]), d.eps, S)
+        units = d.q.shape[0]
+    return units, time.perf_counter() - t0
+
+
+def _cpu_worker_init():
     from threadpoolctl import threadpool_limits
+    import torch
+    torch.set_num_threads(1)
+    threadpool_limits(1)
+
+
+def cpu_baseline():
+    """The fp64 oracle, as it stands, on this host's cores: a process pool over
+    (sequence, head) pairs, one BLAS thread per worker.  Runs before anything
+    touches the GPU (the workers are forked from this process).
+
+    Samples (each pair runs in full, every token or step):
+      0  the tiny fp32 workload, whole;
+      1  the B=4 H=16 T=4096 prefill workload, whole (64 pairs) -- `value`;
+      2  the T=65536 dv=256 workload, heads 0, 5, 10, 15 (4 of 16 pairs);
+      3  the decode workload, 64 of 4096 (sequence, head) pairs over all 512 steps;
+      4  the 32 packed sequences, heads 0, 4, ..., 28 (256 of 1024 pairs).
+    Tokens/s for a sample = tokens of the pairs it ran (one head each) / wall
+    seconds x heads of the workload, i.e. the workload's own token rate if the
+    oracle kept that speed on every head."""
+    import multiprocessing as mp
 
     from gated_delta_rule_kla_amd import inputs
-    from oracle import kla_forward
 
-    x = inputs.prefill_config(1)
-    f = inputs.to_f64
-    q, k, v, g, eta = (f(t[:rows]) for t in (x.q, x.k, x.v, x.g, x.eta))
-    with threadpool_limits(1):
-        t0 = time.perf_counter()
-        kla_forward(q, k, v, g, eta, x.eps)
-        dt = time.perf_counter() - t0
-    tokens = rows * x.q.shape[2]
-    return dict(value=tokens / dt, unit="tokens/s", cores=1, kind="oracle",
-                sample=f"fp64 numpy recurrence on batch rows 0..{rows - 1} of the B=4 H=16 T=4096 "
-                       f"dk=dv=128 workload ({tokens} tokens x 16 heads), {dt:.1f} s, 1 thread")
+    cores = max(1, min(len(os.sched_getaffinity(0)), 16))
+    for i in range(5):
+        _workload(i)
+    plans = {
+        0: [("prefill", 0, 0, 0, 0)],
+        1: [("prefill", 1, b, 0, h) for b in range(4) for h in range(16)],
+        2: [("prefill", 2, 0, 0, h) for h in (0, 5, 10, 15)],
+        3: [("decode", 3, n, 0, h) for n, h in zip(range(0, 256, 4), [i % 16 for i in range(64)])],
+        4: [("prefill", 4, n, 0, h) for n in range(32) for h in range(0, 32, 4)],
+    }
+    heads = {0: 1, 1: 16, 2: 16, 3: 16, 4: 32}
+    per = {}
+    ctx = mp.get_context("fork")
+    with ctx.Pool(cores, initializer=_cpu_worker_init) as pool:
+        for i, tasks in plans.items():
+            t0 = time.perf_counter()
+            res = pool.map(_cpu_task, tasks, chunksize=1)
+            wall = time.perf_counter() - t0
+            units = sum(u for u, _ in res)
+            busy = sum(t for _, t in res)
+            if i == 3:
+                per[inputs.CONFIGS[i]] = {
+                    "seconds": wall, "pairs": len(tasks), "steps": units // len(tasks),
+                    "head_steps/s": units / wall, "tokens/s": units / wall / heads[i],
+                    "worker_seconds": busy}
+            else:
+                per[inputs.CONFIGS[i]] = {
+                    "seconds": wall, "pairs": len(tasks), "token_heads": units,
+                    "tokens/s": units / wall / heads[i], "worker_seconds": busy}
+    head = per[inputs.CONFIGS[1]]
+    return dict(value=head["tokens/s"], unit="tokens/s", cores=cores, kind="oracle",
+                sample=(f"fp64 numpy token recurrence over all 64 (sequence, head) pairs of the B=4 H=16 "
+                        f"T=4096 dk=dv=128 workload, a process pool of {cores} workers with one BLAS "
+                        f"thread each, {head['seconds']:.1f} s wall; the other workloads on the "
+                        f"samples listed in per_workload"),
+                per_workload=per)
 
 
 def main():
@@ -298,6 +414,11 @@ def main():
         print("bench.py: this operator build measures one GPU only (no multi-GPU path); "
               "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+
+    # the CPU baseline forks its worker pool, so it runs before anything touches the GPU
+    cpu = None
+    if args.mode == "all" and not args.no_cpu_baseline:
+        cpu = cpu_baseline()
 
     import torch
     if not torch.cuda.is_available():
@@ -359,6 +480,8 @@ def main():
         if args.mode == "decode":
             out.update({"value": gbs, "unit": "GB/s", "ms_per_step": d["ms"],
                         "config": {"workload": dec["workload"]}, "roofline": dec["roofline"]})
+        if args.mode == "all":
+            dec["beyond_infinity_cache"] = bench_decode_large()
         out["decode"] = dec
     if args.mode in ("all", "backward"):
         bw = bench_backward(max(1, args.steps // 10), max(1, args.warmup // 10))
@@ -393,8 +516,8 @@ def main():
         if "decode" in out:
             gdn["kla_over_gdn_decode_time"] = out["decode"]["ms_per_step"] / gd["decode_ms"]
         out["gdn"] = gdn
-    if args.mode == "all" and not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline()
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
     print(json.dumps(out))
 
 

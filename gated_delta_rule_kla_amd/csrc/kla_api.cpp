@@ -4,7 +4,9 @@
 // error paths run (and are tested) on machines without a GPU.  After
 // validation the call only enqueues kernels on the caller's stream.
 #include <cmath>
+#include <algorithm>
 #include <cstdint>
+#include <vector>
 
 #include "../../include/kla.h"
 #include "kla_internal.h"
@@ -157,8 +159,8 @@ kla_status_t kla_chunk_fwd(const void *q, const void *k, const void *v, const vo
                            const void *eta, float eps, const float *initial_state, void *o,
                            float *final_state, const int32_t *cu_seqlens,
                            const int32_t *cu_seqlens_host, int num_seqs, int B, int H, int T,
-                           int dk, int dv, int chunk, void *workspace, size_t workspace_bytes,
-                           kla_dtype_t dtype, void *stream) {
+                           int dk, int dv, int chunk, kla_dtype_t dtype, void *workspace,
+                           size_t workspace_bytes, void *stream) {
   return chunk_fwd_impl(q, k, v, g, eta, eps, 0, initial_state, o, final_state, cu_seqlens, cu_seqlens_host,
                         num_seqs, B, H, T, dk, dv, chunk, workspace, workspace_bytes, dtype, stream);
 }
@@ -166,10 +168,30 @@ kla_status_t kla_chunk_fwd(const void *q, const void *k, const void *v, const vo
 kla_status_t kla_gdn_chunk_fwd(const void *q, const void *k, const void *v, const void *g,
                                const void *beta, const float *initial_state, void *o, float *final_state,
                                const int32_t *cu_seqlens, const int32_t *cu_seqlens_host, int num_seqs,
-                               int B, int H, int T, int dk, int dv, int chunk, void *workspace,
-                               size_t workspace_bytes, kla_dtype_t dtype, void *stream) {
+                               int B, int H, int T, int dk, int dv, int chunk, kla_dtype_t dtype,
+                               void *workspace, size_t workspace_bytes, void *stream) {
   return chunk_fwd_impl(q, k, v, g, beta, 0.f, 1, initial_state, o, final_state, cu_seqlens, cu_seqlens_host,
                         num_seqs, B, H, T, dk, dv, chunk, workspace, workspace_bytes, dtype, stream);
+}
+
+size_t kla_chunk_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk, int num_seqs) {
+  // neither the element type nor the layout is an argument: the largest need
+  // over both element types and over the dense (num_seqs == B) and packed
+  // layouts.  A packed layout needs B == 1; its size only depends on
+  // cu_seqlens through num_seqs, so a valid mirror (all tokens in the last
+  // sequence) stands in for the caller's.
+  if (B < 0 || T < 0 || num_seqs < 0 || T >= 0x7fffffff) return 0;
+  size_t best = 0;
+  for (const kla_dtype_t dt : {KLA_DT_BF16, KLA_DT_F32}) {
+    if (num_seqs == B) best = std::max(best, kla_chunk_workspace_bytes(nullptr, nullptr, B, B, H, T, dk, dv, chunk, dt));
+    if (B == 1 && num_seqs >= 1) {
+      std::vector<int32_t> cu((size_t)num_seqs + 1, 0);
+      cu[num_seqs] = T;
+      const int32_t *dev_stub = cu.data();  // only tested for NULL here
+      best = std::max(best, kla_chunk_workspace_bytes(dev_stub, cu.data(), num_seqs, 1, H, T, dk, dv, chunk, dt));
+    }
+  }
+  return best;
 }
 
 size_t kla_chunk_bwd_workspace_bytes(const int32_t *cu_seqlens, const int32_t *cu_seqlens_host, int num_seqs,
@@ -187,8 +209,8 @@ kla_status_t kla_chunk_bwd(const void *q, const void *k, const void *v, const vo
                            float eps, const float *initial_state, const void *dout, const float *dfinal_state,
                            void *dq, void *dk_, void *dv_, float *dg, float *deta, float *dinitial_state,
                            const int32_t *cu_seqlens, const int32_t *cu_seqlens_host, int num_seqs, int B,
-                           int H, int T, int dk, int dv, int chunk, void *workspace, size_t workspace_bytes,
-                           kla_dtype_t dtype, void *stream) {
+                           int H, int T, int dk, int dv, int chunk, kla_dtype_t dtype, void *workspace,
+                           size_t workspace_bytes, void *stream) {
   return chunk_bwd_impl(q, k, v, g, eta, eps, 0, initial_state, dout, dfinal_state, dq, dk_, dv_, dg, deta,
                         dinitial_state, cu_seqlens, cu_seqlens_host, num_seqs, B, H, T, dk, dv, chunk, workspace,
                         workspace_bytes, dtype, stream);
@@ -198,8 +220,8 @@ kla_status_t kla_gdn_chunk_bwd(const void *q, const void *k, const void *v, cons
                                const float *initial_state, const void *dout, const float *dfinal_state, void *dq,
                                void *dk_, void *dv_, float *dg, float *dbeta, float *dinitial_state,
                                const int32_t *cu_seqlens, const int32_t *cu_seqlens_host, int num_seqs, int B,
-                               int H, int T, int dk, int dv, int chunk, void *workspace, size_t workspace_bytes,
-                               kla_dtype_t dtype, void *stream) {
+                               int H, int T, int dk, int dv, int chunk, kla_dtype_t dtype, void *workspace,
+                               size_t workspace_bytes, void *stream) {
   return chunk_bwd_impl(q, k, v, g, beta, 0.f, 1, initial_state, dout, dfinal_state, dq, dk_, dv_, dg, dbeta,
                         dinitial_state, cu_seqlens, cu_seqlens_host, num_seqs, B, H, T, dk, dv, chunk, workspace,
                         workspace_bytes, dtype, stream);

@@ -18,15 +18,17 @@
 // Four kernels, through a caller-provided workspace:
 //   prep     (chunk, head) in parallel: b, gamma, ||k||^2, T, P and K K^T . E into the
 //            workspace.
-//   states   (sequence, head, 16 state columns): the chunk-start states, in order.
-//   dstates  (sequence, head, 16 state columns): dS' of every chunk, in reverse order;
-//            the gradient of the initial state is what is left at the start.
+//   states   (sequence, head, 32 state columns, or 16 when dv is not a multiple of 32):
+//            the chunk-start states, in order.
+//   dstates  (sequence, head, 32 or 16 state columns): dS' of every chunk, in reverse
+//            order; the gradient of the initial state is what is left at the start.
 //   grads    (chunk, head) in parallel: everything else from S, dS' and the chunk's
-//            inputs, streaming the state columns 16 at a time, on fp32 MFMA tiles.
-// All arithmetic is fp32 (the prep kernel's K K^T and Q K^T take the bf16 inputs as
-// MFMA operands, exact products with fp32 sums; everything else is 16x16x4 fp32 MFMA
-// or vector FMA) through padded LDS rows; there are no atomics, so results are
-// deterministic run to run.
+//            inputs, streaming the state columns 16 at a time.
+// Sums are fp32 throughout.  The prep kernel's K K^T and Q K^T take the inputs as MFMA
+// operands (bf16: exact products, 16x16x32 bf16 MFMA).  The other products are 16x16x16
+// steps (Mma16 below): on the bf16 build one 16x16x16 bf16 MFMA whose operands are
+// rounded to bf16 from fp32 LDS values, on the fp32 build four 16x16x4 fp32 MFMAs.  There
+// are no atomics, so results are deterministic run to run.
 #include <algorithm>
 
 #include "kla_common.h"
@@ -397,12 +399,12 @@ __global__ __launch_bounds__(kPT) void kla_bwd_prep_kernel(BwdParams p) {
   }
 }
 
-// The two scans run their products on 16x16x4 fp32 MFMA tiles (lane l supplies
-// A[l%16][l/16] and B[l/16][l%16]; accumulator element i of lane l is row
-// 4(l/16)+i, column l%16).  The 16-column state slice lives in accumulators:
-// wave w holds state rows 16w .. 16w+15 and copies them to LDS once per chunk for
-// the next chunk's K S (or K dS) product; chunk-row products (16-row tiles of C)
-// go to waves 0 .. C/16-1.
+// The two scans run their products as 16x16x16 steps (Mma16: lane l supplies
+// A[l%16][4(l/16) .. +3] and B[4(l/16) .. +3][l%16]; accumulator element i of lane l
+// is row 4(l/16)+i, column l%16).  The state slice (NS = 32 or 16 columns) lives in
+// accumulators: wave w holds state rows 16w .. 16w+15 of its column tile and copies
+// them to LDS once per chunk for the next chunk's K S (or K dS) product; chunk-row
+// products (16-row tiles of C) are spread over the waves by (row tile, column tile).
 
 // ============================================================================
 // states: the chunk-start state of every chunk, 16 state columns per workgroup

@@ -13,7 +13,7 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["chunk_fwd", "chunk_workspace_bytes", "decode_step", "gdn_chunk_fwd", "gdn_decode_step", "chunk_bwd",
+__all__ = ["chunk_fwd", "chunk_workspace_bytes", "chunk_fwd_workspace_bytes", "decode_step", "gdn_chunk_fwd", "gdn_decode_step", "chunk_bwd",
            "gdn_chunk_bwd", "chunk_bwd_workspace_bytes", "lib", "lib_path", "KlaError", "KLA_DT_BF16",
            "KLA_DT_F32"]
 
@@ -49,7 +49,7 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(path)
         vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
         L.kla_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, f32, vp, vp, vp, vp, vp,
-                                    i32, i32, i32, i32, i32, i32, i32, vp, sz, i32, vp]
+                                    i32, i32, i32, i32, i32, i32, i32, i32, vp, sz, vp]
         L.kla_chunk_fwd.restype = i32
         L.kla_chunk_workspace_bytes.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, i32, i32]
         L.kla_chunk_workspace_bytes.restype = sz
@@ -57,18 +57,20 @@ def lib() -> ctypes.CDLL:
                                       i32, i32, i32, i32, i32, vp]
         L.kla_decode_step.restype = i32
         L.kla_gdn_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
-                                        i32, i32, i32, i32, i32, i32, i32, vp, sz, i32, vp]
+                                        i32, i32, i32, i32, i32, i32, i32, i32, vp, sz, vp]
         L.kla_gdn_chunk_fwd.restype = i32
         L.kla_gdn_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
         L.kla_gdn_decode_step.restype = i32
         L.kla_chunk_bwd.argtypes = [vp, vp, vp, vp, vp, f32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
-                                    i32, i32, i32, i32, i32, i32, i32, vp, sz, i32, vp]
+                                    i32, i32, i32, i32, i32, i32, i32, i32, vp, sz, vp]
         L.kla_chunk_bwd.restype = i32
         L.kla_gdn_chunk_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
-                                        i32, i32, i32, i32, i32, i32, i32, vp, sz, i32, vp]
+                                        i32, i32, i32, i32, i32, i32, i32, i32, vp, sz, vp]
         L.kla_gdn_chunk_bwd.restype = i32
         L.kla_chunk_bwd_workspace_bytes.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, i32, i32]
         L.kla_chunk_bwd_workspace_bytes.restype = sz
+        L.kla_chunk_fwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+        L.kla_chunk_fwd_workspace_bytes.restype = sz
         L.kla_status_str.argtypes = [i32]
         L.kla_status_str.restype = ctypes.c_char_p
         L.kla_abi_version.argtypes = []
@@ -146,7 +148,7 @@ def _chunk_call(fn: str, q, k, v, g, coef, eps, initial_state, cu_seqlens, chunk
     elif workspace.device != dev or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous uint8 tensor on the inputs' device")
     tail = (_ptr(initial_state), _ptr(out), _ptr(final_state), _ptr(cu_seqlens), host_ptr, N, B, H, T, dk, dv,
-            int(chunk), _ptr(workspace), workspace.numel(), _DTYPES[dtype], _stream(dev))
+            int(chunk), _DTYPES[dtype], _ptr(workspace), workspace.numel(), _stream(dev))
     if eps is not None:
         st = lib().kla_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(coef), float(eps), *tail)
         _check("kla_chunk_fwd", st)
@@ -221,6 +223,13 @@ def chunk_workspace_bytes(B: int, H: int, T: int, dk: int, dv: int, chunk: int =
     return lib().kla_chunk_workspace_bytes(None, None, B, B, H, T, dk, dv, int(chunk), _DTYPES[dtype])
 
 
+def chunk_fwd_workspace_bytes(B: int, H: int, T: int, dk: int, dv: int, chunk: int = 64,
+                              num_seqs: Optional[int] = None) -> int:
+    """Upper bound on the workspace bytes kla_chunk_fwd needs for these sizes,
+    for either dtype and either layout (kla_chunk_fwd_workspace_bytes)."""
+    return lib().kla_chunk_fwd_workspace_bytes(B, H, T, dk, dv, int(chunk), B if num_seqs is None else num_seqs)
+
+
 def _bwd_call(fn, q, k, v, g, coef, eps, do, initial_state, dfinal_state, cu_seqlens, chunk, cu_seqlens_host,
               need_dinitial, workspace):
     dev = q.device
@@ -266,7 +275,7 @@ def _bwd_call(fn, q, k, v, g, coef, eps, do, initial_state, dfinal_state, cu_seq
         raise ValueError("workspace must be a contiguous uint8 tensor on the inputs' device")
     mid = (_ptr(initial_state), _ptr(do), _ptr(dfinal_state), _ptr(dq), _ptr(dkk), _ptr(dvv), _ptr(dg),
            _ptr(dcoef), _ptr(ds0), _ptr(cu_seqlens), host_ptr, N, B, H, T, dk, dv, int(chunk),
-           _ptr(workspace), workspace.numel(), _DTYPES[dtype], _stream(dev))
+           _DTYPES[dtype], _ptr(workspace), workspace.numel(), _stream(dev))
     if eps is not None:
         st = lib().kla_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(coef), float(eps), *mid)
         _check("kla_chunk_bwd", st)

@@ -119,8 +119,19 @@ kla_status_t kla_chunk_fwd(const void *q, const void *k, const void *v,
                            const float *initial_state, void *o, float *final_state,
                            const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
                            int num_seqs, int B, int H, int T, int dk, int dv, int chunk,
-                           void *workspace, size_t workspace_bytes,
-                           kla_dtype_t dtype, void *stream);
+                           kla_dtype_t dtype, void *workspace, size_t workspace_bytes,
+                           void *stream);
+
+/*
+ * kla_chunk_fwd_workspace_bytes -- an upper bound on the device workspace
+ * kla_chunk_fwd (and kla_gdn_chunk_fwd) needs for these sizes, valid for
+ * either element type and for both the dense (num_seqs == B) and the packed
+ * (cu_seqlens) layout, since neither is an argument here.  Host-only, no HIP
+ * call.  Returns 0 for sizes kla_chunk_fwd would reject for both element
+ * types, and when no workspace is needed (no tokens).  Callers that know the
+ * dtype and cu_seqlens may use the exact kla_chunk_workspace_bytes below.
+ */
+size_t kla_chunk_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk, int num_seqs);
 
 /*
  * kla_chunk_workspace_bytes -- device workspace kla_chunk_fwd needs for these
@@ -176,8 +187,8 @@ kla_status_t kla_gdn_chunk_fwd(const void *q, const void *k, const void *v,
                                const float *initial_state, void *o, float *final_state,
                                const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
                                int num_seqs, int B, int H, int T, int dk, int dv, int chunk,
-                               void *workspace, size_t workspace_bytes,
-                               kla_dtype_t dtype, void *stream);
+                               kla_dtype_t dtype, void *workspace, size_t workspace_bytes,
+                               void *stream);
 
 kla_status_t kla_gdn_decode_step(const void *q, const void *k, const void *v,
                                  const void *g, const void *beta,
@@ -224,8 +235,8 @@ kla_status_t kla_chunk_bwd(const void *q, const void *k, const void *v,
                            float *dinitial_state,
                            const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
                            int num_seqs, int B, int H, int T, int dk, int dv, int chunk,
-                           void *workspace, size_t workspace_bytes,
-                           kla_dtype_t dtype, void *stream);
+                           kla_dtype_t dtype, void *workspace, size_t workspace_bytes,
+                           void *stream);
 
 /*
  * kla_gdn_chunk_bwd -- gradients of kla_gdn_chunk_fwd: as kla_chunk_bwd with
@@ -238,8 +249,8 @@ kla_status_t kla_gdn_chunk_bwd(const void *q, const void *k, const void *v,
                                float *dinitial_state,
                                const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
                                int num_seqs, int B, int H, int T, int dk, int dv, int chunk,
-                               void *workspace, size_t workspace_bytes,
-                               kla_dtype_t dtype, void *stream);
+                               kla_dtype_t dtype, void *workspace, size_t workspace_bytes,
+                               void *stream);
 
 /*
  * kla_chunk_bwd_workspace_bytes -- device workspace kla_chunk_bwd and
@@ -257,7 +268,7 @@ const char *kla_status_str(kla_status_t s);
 /* ABI version of this header (incremented on any incompatible change). */
 int kla_abi_version(void);
 
-#define KLA_ABI_VERSION 4
+#define KLA_ABI_VERSION 5
 
 #ifdef __cplusplus
 }

@@ -28,7 +28,8 @@ def _declared():
 def test_exports_every_declared_symbol():
     L = kla.lib()
     names = _declared()
-    assert set(names) >= {"kla_chunk_fwd", "kla_chunk_workspace_bytes", "kla_decode_step", "kla_status_str",
+    assert set(names) >= {"kla_chunk_fwd", "kla_chunk_fwd_workspace_bytes", "kla_chunk_workspace_bytes",
+                          "kla_decode_step", "kla_status_str",
                           "kla_abi_version", "kla_gdn_chunk_fwd", "kla_gdn_decode_step", "kla_chunk_bwd",
                           "kla_gdn_chunk_bwd", "kla_chunk_bwd_workspace_bytes"}
     for n in names:
@@ -61,8 +62,8 @@ def _chunk(**kw):
     a.update(kw)
     return kla.lib().kla_chunk_fwd(a["q"], a["k"], a["v"], a["g"], a["eta"], a["eps"], a["s0"],
                                    a["o"], a["sf"], a["cu"], a["cuh"], a["N"], a["B"], a["H"],
-                                   a["T"], a["dk"], a["dv"], a["chunk"], a["ws"], a["ws_bytes"],
-                                   a["dtype"], None)
+                                   a["T"], a["dk"], a["dv"], a["chunk"], a["dtype"], a["ws"],
+                                   a["ws_bytes"], None)
 
 
 def _decode(**kw):
@@ -143,7 +144,7 @@ def _gdn_chunk(**kw):
     a.update(kw)
     return kla.lib().kla_gdn_chunk_fwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["s0"], a["o"], a["sf"],
                                        a["cu"], a["cuh"], a["N"], a["B"], a["H"], a["T"], a["dk"], a["dv"],
-                                       a["chunk"], a["ws"], a["ws_bytes"], a["dtype"], None)
+                                       a["chunk"], a["dtype"], a["ws"], a["ws_bytes"], None)
 
 
 def _gdn_decode(**kw):
@@ -215,6 +216,36 @@ def test_workspace_bytes():
     assert _chunk(ws_bytes=_ws_bytes() - 1) == E_WS
 
 
+def test_fwd_workspace_bound_query():
+    """kla_chunk_fwd_workspace_bytes(B, H, T, dk, dv, chunk, num_seqs) takes neither the dtype nor
+    cu_seqlens, so it bounds the exact need over both element types and both layouts."""
+    L = kla.lib()
+    q = lambda B, H, T, dk, dv, C, N: L.kla_chunk_fwd_workspace_bytes(B, H, T, dk, dv, C, N)
+    for (B, H, T, dk, dv, C) in [(2, 4, 100, 128, 128, 64), (4, 16, 4096, 128, 128, 64), (1, 3, 777, 32, 16, 16),
+                                 (1, 2, 300, 16, 32, 64)]:
+        bound = q(B, H, T, dk, dv, C, B)
+        exact = [_ws_bytes(B=B, N=B, H=H, T=T, dk=dk, dv=dv, chunk=C, dtype=dt) for dt in (0, 1)]
+        if B == 1:  # one sequence may also come packed with cu_seqlens = [0, T]
+            arr = (ctypes.c_int32 * 2)(0, T)
+            exact += [_ws_bytes(cu=FAKE, cuh=ctypes.addressof(arr), N=1, B=1, H=H, T=T, dk=dk, dv=dv, chunk=C,
+                                dtype=dt) for dt in (0, 1)]
+        assert bound == max(exact) and bound > 0
+        if B == 1:
+            for N in (1, 3, 17):
+                arr = (ctypes.c_int32 * (N + 1))(*([0] * N + [T]))
+                ex = [_ws_bytes(cu=FAKE, cuh=ctypes.addressof(arr), N=N, B=1, H=H, T=T, dk=dk, dv=dv, chunk=C,
+                                dtype=dt) for dt in (0, 1)]
+                assert q(1, H, T, dk, dv, C, N) >= max(ex) > 0
+                # any other split of the same tokens into N sequences needs the same bytes
+                arr2 = (ctypes.c_int32 * (N + 1))(*[T * i // N for i in range(N + 1)])
+                ex2 = [_ws_bytes(cu=FAKE, cuh=ctypes.addressof(arr2), N=N, B=1, H=H, T=T, dk=dk, dv=dv,
+                                 chunk=C, dtype=dt) for dt in (0, 1)]
+                assert ex2 == ex
+    assert q(2, 4, 0, 128, 128, 64, 2) == 0
+    assert q(2, 4, 100, 96, 128, 64, 2) == 0             # unsupported for both dtypes
+    assert kla.chunk_fwd_workspace_bytes(2, 4, 100, 128, 128) == q(2, 4, 100, 128, 128, 64, 2)
+
+
 def test_workspace_slots_never_collide():
     """The packed-sequence slot of chunk c of sequence n is n + floor(t0_n / C) + c: distinct for all
     (n, c) and below floor(T / C) + N + 1, for any lengths (brute force over random length mixes)."""
@@ -244,7 +275,7 @@ def _bwd(fn="kla_chunk_bwd", **kw):
         head = head + (a["eps"],)
     return getattr(kla.lib(), fn)(*head, a["s0"], a["do"], a["dsf"], a["dq"], a["dk_"], a["dv_"], a["dg"],
                                   a["deta"], a["ds0"], a["cu"], a["cuh"], a["N"], a["B"], a["H"], a["T"],
-                                  a["dk"], a["dv"], a["chunk"], a["ws"], a["ws_bytes"], a["dtype"], None)
+                                  a["dk"], a["dv"], a["chunk"], a["dtype"], a["ws"], a["ws_bytes"], None)
 
 
 @pytest.mark.parametrize("fn", ["kla_chunk_bwd", "kla_gdn_chunk_bwd"])
