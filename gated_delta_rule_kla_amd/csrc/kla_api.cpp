@@ -75,11 +75,14 @@ kla_status_t decode_impl(const void *q, const void *k, const void *v, const void
   return from_hip(kla::launch_decode(a, reinterpret_cast<hipStream_t>(stream)));
 }
 
+// static_scratch: take the workspace from the library's fixed per-GPU buffer
+// (kla_chunk_fwd_noalloc) instead of the caller's.
 kla_status_t chunk_fwd_impl(const void *q, const void *k, const void *v, const void *g, const void *eta,
                             float eps, int beta_direct, const float *initial_state, void *o,
                             float *final_state, const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
                             int num_seqs, int B, int H, int T, int dk, int dv, int chunk, void *workspace,
-                            size_t workspace_bytes, kla_dtype_t dtype, void *stream) {
+                            size_t workspace_bytes, kla_dtype_t dtype, void *stream,
+                            bool static_scratch = false) {
   const kla_status_t st =
       check_chunk_shapes(eps, cu_seqlens, cu_seqlens_host, num_seqs, B, H, T, dk, dv, chunk, dtype);
   if (st != KLA_OK) return st;
@@ -89,10 +92,20 @@ kla_status_t chunk_fwd_impl(const void *q, const void *k, const void *v, const v
   if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(g) || misaligned(eta) ||
       misaligned(o) || misaligned(initial_state) || misaligned(final_state) || misaligned(workspace))
     return KLA_ERR_ALIGN;
-  const kla::ChunkArgs a = chunk_args(q, k, v, g, eta, eps, initial_state, o, final_state, cu_seqlens, num_seqs,
-                                      B, H, T, dk, dv, chunk, dtype, workspace, beta_direct);
+  kla::ChunkArgs a = chunk_args(q, k, v, g, eta, eps, initial_state, o, final_state, cu_seqlens, num_seqs,
+                                B, H, T, dk, dv, chunk, dtype, workspace, beta_direct);
   const size_t need = (long long)B * T > 0 ? kla::chunk_workspace_bytes(a) : 0;
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return KLA_ERR_WORKSPACE;
+  if (static_scratch) {
+    // every check above and this one run before the first HIP call
+    if (need > kla::static_scratch_bytes()) return KLA_ERR_SCRATCH;
+    if (need > 0) {
+      void *p = nullptr;
+      if (kla::static_scratch(&p) != hipSuccess) return KLA_ERR_HIP;
+      a.workspace = p;
+    }
+  } else if (need > 0 && (workspace == nullptr || workspace_bytes < need)) {
+    return KLA_ERR_WORKSPACE;
+  }
   return from_hip(kla::launch_chunk_fwd(a, reinterpret_cast<hipStream_t>(stream)));
 }
 
@@ -141,6 +154,7 @@ const char *kla_status_str(kla_status_t s) {
     case KLA_ERR_ALIGN: return "data pointers must be 16-byte aligned";
     case KLA_ERR_WORKSPACE: return "workspace missing or smaller than kla_chunk_workspace_bytes()";
     case KLA_ERR_HIP: return "HIP runtime error";
+    case KLA_ERR_SCRATCH: return "the call needs more scratch than kla_chunk_fwd_noalloc's fixed buffer holds";
   }
   return "unknown status";
 }
@@ -172,6 +186,15 @@ kla_status_t kla_gdn_chunk_fwd(const void *q, const void *k, const void *v, cons
                                void *workspace, size_t workspace_bytes, void *stream) {
   return chunk_fwd_impl(q, k, v, g, beta, 0.f, 1, initial_state, o, final_state, cu_seqlens, cu_seqlens_host,
                         num_seqs, B, H, T, dk, dv, chunk, workspace, workspace_bytes, dtype, stream);
+}
+
+kla_status_t kla_chunk_fwd_noalloc(const void *q, const void *k, const void *v, const void *g, const void *eta,
+                                   float eps, const float *initial_state, void *o, float *final_state,
+                                   const int32_t *cu_seqlens, const int32_t *cu_seqlens_host, int num_seqs,
+                                   int B, int H, int T, int dk, int dv, int chunk, kla_dtype_t dtype,
+                                   void *stream) {
+  return chunk_fwd_impl(q, k, v, g, eta, eps, 0, initial_state, o, final_state, cu_seqlens, cu_seqlens_host,
+                        num_seqs, B, H, T, dk, dv, chunk, nullptr, 0, dtype, stream, true);
 }
 
 size_t kla_chunk_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk, int num_seqs) {

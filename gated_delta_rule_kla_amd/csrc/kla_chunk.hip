@@ -42,9 +42,12 @@
 // and Q rows) are stored with their columns permuted into that order, and K^T,
 // T' (stored transposed) and the V slice are read with gfx950's transposing
 // LDS read.
+#include "kla.h"
 #include "kla_common.h"
 #include "kla_internal.h"
 
+#include <atomic>
+#include <mutex>
 #include <type_traits>
 
 namespace kla {
@@ -1385,6 +1388,50 @@ hipError_t launch_chunk_fwd(const ChunkArgs &a, hipStream_t st) {
     }
   }
   return hipErrorInvalidValue;
+}
+
+// ---------------------------------------------------------------------------
+// Fixed scratch for the allocation-free entry point (kla_chunk_fwd_noalloc)
+// ---------------------------------------------------------------------------
+// The prep -> scan hand-over above needs a device workspace.  Callers that
+// cannot allocate get it from this file-scope buffer instead: one copy per GPU,
+// created when the code object is loaded on that GPU and held until the
+// process ends.  Its contents need no initialisation: every slot the scan
+// reads is written by the prep kernel of the same call, and the sequence
+// order by the ranking kernel.  Calls that overlap in time on one GPU share
+// it and therefore race.
+constexpr size_t kStaticScratchBytes = KLA_NOALLOC_SCRATCH_BYTES;
+static __device__ __attribute__((aligned(256))) char scratch[kStaticScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+}  // namespace
+
+size_t static_scratch_bytes() { return kStaticScratchBytes; }
+
+hipError_t static_scratch(void **ptr) {
+  // In host code `scratch` names a host-side stand-in, not the device copy:
+  // the device address comes from hipGetSymbolAddress, looked up once per
+  // device with that device current, and only that address is used.
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (p == nullptr) return hipErrorInvalidSymbol;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  return hipSuccess;
 }
 
 }  // namespace kla

@@ -53,6 +53,12 @@ size_t chunk_workspace_bytes(const ChunkArgs &a);
 bool chunk_bwd_supported(int dtype, int dk, int dv, int chunk);
 size_t chunk_bwd_workspace_bytes(const ChunkArgs &a);
 
+// The fixed per-GPU scratch behind kla_chunk_fwd_noalloc: its size, and its
+// device address on the current device (looked up on the first call per
+// device; no allocation).
+size_t static_scratch_bytes();
+hipError_t static_scratch(void **ptr);
+
 // Enqueue the kernel(s).  Arguments are already validated.
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_chunk_fwd(const ChunkArgs &a, hipStream_t stream);

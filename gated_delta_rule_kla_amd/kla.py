@@ -69,6 +69,9 @@ def lib() -> ctypes.CDLL:
         L.kla_gdn_chunk_bwd.restype = i32
         L.kla_chunk_bwd_workspace_bytes.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, i32, i32]
         L.kla_chunk_bwd_workspace_bytes.restype = sz
+        L.kla_chunk_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, f32, vp, vp, vp, vp, vp,
+                                            i32, i32, i32, i32, i32, i32, i32, i32, vp]
+        L.kla_chunk_fwd_noalloc.restype = i32
         L.kla_chunk_fwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
         L.kla_chunk_fwd_workspace_bytes.restype = sz
         L.kla_status_str.argtypes = [i32]
@@ -141,6 +144,15 @@ def _chunk_call(fn: str, q, k, v, g, coef, eps, initial_state, cu_seqlens, chunk
     if final_state is not None:
         _need(final_state, "final_state", torch.float32, (N, H, dk, dv), dev)
     host_ptr = None if cu_seqlens_host is None else cu_seqlens_host.data_ptr()
+    if isinstance(workspace, str) and workspace == "static" and eps is not None:
+        # kla_chunk_fwd_noalloc: the library's fixed per-GPU scratch, no workspace argument
+        st = lib().kla_chunk_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(coef), float(eps),
+                                         _ptr(initial_state), _ptr(out), _ptr(final_state), _ptr(cu_seqlens),
+                                         host_ptr, N, B, H, T, dk, dv, int(chunk), _DTYPES[dtype], _stream(dev))
+        _check("kla_chunk_fwd_noalloc", st)
+        return out, final_state
+    if isinstance(workspace, str):
+        raise ValueError(f"kla.{fn}: workspace must be a tensor or None ('static' is for chunk_fwd only)")
     ws_bytes = lib().kla_chunk_workspace_bytes(_ptr(cu_seqlens), host_ptr, N, B, H, T, dk, dv, int(chunk),
                                                _DTYPES[dtype])
     if workspace is None:
@@ -182,10 +194,16 @@ def chunk_fwd(
     ``final_state`` may be passed as the same tensor as ``initial_state`` to
     update it in place.  ``workspace`` (uint8, on the GPU, at least
     chunk_workspace_bytes(...) bytes) is taken from torch's caching allocator
-    on the current stream when not given.
+    on the current stream when not given.  ``workspace="static"`` calls
+    kla_chunk_fwd_noalloc instead, which uses the library's fixed per-GPU
+    scratch buffer (KLA_NOALLOC_SCRATCH_BYTES, 64 MiB) and allocates nothing
+    (pass ``out`` and ``final_state`` to keep the call allocation-free here too).
     """
     return _chunk_call("chunk_fwd", q, k, v, g, eta, eps, initial_state, cu_seqlens, chunk,
                        output_final_state, cu_seqlens_host, out, final_state, workspace)
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # KLA_NOALLOC_SCRATCH_BYTES in include/kla.h
 
 
 def gdn_chunk_fwd(

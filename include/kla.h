@@ -63,7 +63,8 @@ typedef enum {
     KLA_ERR_EPS = -6,         /* eps < 0, NaN or infinite                        */
     KLA_ERR_WORKSPACE = -7,   /* workspace NULL or below kla_chunk_workspace_bytes */
     KLA_ERR_ALIGN = -8,       /* a data pointer is not 16-byte aligned           */
-    KLA_ERR_HIP = -9          /* the HIP runtime rejected a launch               */
+    KLA_ERR_HIP = -9,         /* the HIP runtime rejected a launch               */
+    KLA_ERR_SCRATCH = -10     /* kla_chunk_fwd_noalloc: more scratch than its fixed buffer */
 } kla_status_t;
 
 /*
@@ -121,6 +122,29 @@ kla_status_t kla_chunk_fwd(const void *q, const void *k, const void *v,
                            int num_seqs, int B, int H, int T, int dk, int dv, int chunk,
                            kla_dtype_t dtype, void *workspace, size_t workspace_bytes,
                            void *stream);
+
+/*
+ * kla_chunk_fwd_noalloc -- kla_chunk_fwd for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same arguments without the workspace, the same
+ * kernels and results.  The workspace comes from a fixed buffer inside the
+ * library, one per GPU, of KLA_NOALLOC_SCRATCH_BYTES (64 MiB), held from the
+ * library's first use on that GPU until the process ends.  The call allocates nothing (no hipMalloc, no allocating library
+ * routine); its first call on a device looks the buffer's address up once.
+ *
+ *   Returns KLA_ERR_SCRATCH, before any HIP call, when the call needs more
+ *   than that buffer: kla_chunk_workspace_bytes(...) for the same arguments
+ *   must not exceed it (B=4 H=16 T=4096 dk=dv=128 bf16 needs 28.3 MB).
+ *   Every call on one GPU shares the buffer: calls that overlap in time on
+ *   the same GPU (different streams, different host threads) race and give
+ *   wrong results.  Other status codes as kla_chunk_fwd.
+ */
+kla_status_t kla_chunk_fwd_noalloc(const void *q, const void *k, const void *v,
+                                   const void *g, const void *eta, float eps,
+                                   const float *initial_state, void *o, float *final_state,
+                                   const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
+                                   int num_seqs, int B, int H, int T, int dk, int dv, int chunk,
+                                   kla_dtype_t dtype, void *stream);
 
 /*
  * kla_chunk_fwd_workspace_bytes -- an upper bound on the device workspace
@@ -268,7 +292,10 @@ const char *kla_status_str(kla_status_t s);
 /* ABI version of this header (incremented on any incompatible change). */
 int kla_abi_version(void);
 
-#define KLA_ABI_VERSION 5
+#define KLA_ABI_VERSION 6
+
+/* Size of kla_chunk_fwd_noalloc's fixed per-GPU scratch buffer, in bytes. */
+#define KLA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 
 #ifdef __cplusplus
 }

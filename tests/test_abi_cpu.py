@@ -17,6 +17,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(kla.lib_path()),
                                 reason="libkla.so not built (run __graft_entry__.build())")
 
 OK, E_NULL, E_SHAPE, E_DTYPE, E_UNSUP, E_SEQ, E_EPS, E_WS, E_ALIGN, E_HIP = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9
+E_SCRATCH = -10
 FAKE = 0x7F0000000000  # never dereferenced: every case below fails validation first
 
 
@@ -31,7 +32,7 @@ def test_exports_every_declared_symbol():
     assert set(names) >= {"kla_chunk_fwd", "kla_chunk_fwd_workspace_bytes", "kla_chunk_workspace_bytes",
                           "kla_decode_step", "kla_status_str",
                           "kla_abi_version", "kla_gdn_chunk_fwd", "kla_gdn_decode_step", "kla_chunk_bwd",
-                          "kla_gdn_chunk_bwd", "kla_chunk_bwd_workspace_bytes"}
+                          "kla_gdn_chunk_bwd", "kla_chunk_bwd_workspace_bytes", "kla_chunk_fwd_noalloc"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -43,7 +44,7 @@ def test_abi_version_matches_header():
 
 def test_status_strings():
     L = kla.lib()
-    for s in (OK, E_NULL, E_SHAPE, E_DTYPE, E_UNSUP, E_SEQ, E_EPS, E_WS, E_ALIGN, E_HIP, -77):
+    for s in (OK, E_NULL, E_SHAPE, E_DTYPE, E_UNSUP, E_SEQ, E_EPS, E_WS, E_ALIGN, E_HIP, E_SCRATCH, -77):
         txt = L.kla_status_str(s)
         assert isinstance(txt, bytes) and len(txt) > 0
 
@@ -335,3 +336,29 @@ def test_binding_refuses_cpu_tensors_bwd():
         kla.chunk_bwd(x, x, x, x[..., 0], x[..., 0], x)
     with pytest.raises(ValueError):
         kla.gdn_chunk_bwd(x, x, x, x[..., 0], x[..., 0], x)
+
+
+def _noalloc(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, eta=FAKE, eps=1e-6, s0=None, o=FAKE, sf=FAKE,
+             cu=None, cuh=None, N=2, B=2, H=4, T=100, dk=128, dv=128, chunk=64, dtype=0)
+    a.update(kw)
+    return kla.lib().kla_chunk_fwd_noalloc(a["q"], a["k"], a["v"], a["g"], a["eta"], a["eps"], a["s0"],
+                                           a["o"], a["sf"], a["cu"], a["cuh"], a["N"], a["B"], a["H"],
+                                           a["T"], a["dk"], a["dv"], a["chunk"], a["dtype"], None)
+
+
+def test_noalloc_scratch_limit_and_validation():
+    """kla_chunk_fwd_noalloc validates like kla_chunk_fwd and refuses, before any HIP call, a call
+    whose workspace would not fit its fixed 64 MiB buffer."""
+    limit = int(re.search(r"#define KLA_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)",
+                          open(HEADER).read()).group(1)) << 20
+    assert limit == kla.NOALLOC_SCRATCH_BYTES == 64 << 20
+    # B=4 H=64 T=8192 bf16: 4 x 64 x 128 chunk-heads x 6,912 B = 226 MB
+    assert _ws_bytes(N=4, B=4, H=64, T=8192) > limit
+    assert _noalloc(N=4, B=4, H=64, T=8192) == E_SCRATCH
+    # the B=4 H=16 T=4096 workload fits (28.3 MB)
+    assert _ws_bytes(N=4, B=4, H=16, T=4096) <= limit
+    for kw, code in [(dict(dtype=7), E_DTYPE), (dict(eps=-1.0), E_EPS), (dict(dk=96), E_UNSUP),
+                     (dict(q=None), E_NULL), (dict(k=FAKE + 8), E_ALIGN), (dict(N=3), E_SHAPE),
+                     (dict(N=0, B=0), OK)]:
+        assert _noalloc(**kw) == code, kw
