@@ -136,9 +136,60 @@ kla_status_t chunk_bwd_impl(const void *q, const void *k, const void *v, const v
   return from_hip(kla::launch_chunk_bwd(a, b, reinterpret_cast<hipStream_t>(stream)));
 }
 
+kla_status_t check_pgdn(kla_gain_t gain, float band, float eps) {
+  if (gain != KLA_GAIN_GIVEN && gain != KLA_GAIN_KACZMARZ) return KLA_ERR_PARAM;
+  if (!std::isfinite(band) || band < 1.f) return KLA_ERR_PARAM;
+  if (gain == KLA_GAIN_KACZMARZ && bad_eps(eps)) return KLA_ERR_EPS;
+  return KLA_OK;
+}
+
+float band_log(float band) { return band == 1.f ? 0.f : std::log(band); }
+
 }  // namespace
 
 extern "C" {
+
+kla_status_t kla_pgdn_chunk_fwd(const void *q, const void *k, const void *v, const void *g, const void *coef,
+                                float eps, kla_gain_t gain, float band, const float *initial_state,
+                                const float *initial_acc, void *o, float *final_state, float *final_acc,
+                                const int32_t *cu_seqlens, const int32_t *cu_seqlens_host, int num_seqs, int B,
+                                int H, int T, int dk, int dv, int chunk, kla_dtype_t dtype, void *stream) {
+  if (dtype != KLA_DT_BF16 && dtype != KLA_DT_F32) return KLA_ERR_DTYPE;
+  kla_status_t st = check_pgdn(gain, band, eps);
+  if (st != KLA_OK) return st;
+  const float e = gain == KLA_GAIN_KACZMARZ ? eps : 0.f;
+  st = check_chunk_shapes(e, cu_seqlens, cu_seqlens_host, num_seqs, B, H, T, dk, dv, chunk, dtype);
+  if (st != KLA_OK) return st;
+  if (!kla::general_supported(dtype, dk, dv, chunk)) return KLA_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return KLA_OK;
+  if ((long long)B * T > 0 && (!q || !k || !v || !g || !coef || !o)) return KLA_ERR_NULL;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(g) || misaligned(coef) || misaligned(o) ||
+      misaligned(initial_state) || misaligned(final_state) || misaligned(initial_acc) || misaligned(final_acc))
+    return KLA_ERR_ALIGN;
+  const kla::ChunkArgs a = chunk_args(q, k, v, g, coef, e, initial_state, o, final_state, cu_seqlens, num_seqs, B,
+                                      H, T, dk, dv, chunk, dtype, nullptr, gain == KLA_GAIN_GIVEN ? 1 : 0);
+  const kla::GenExtra x{1, band_log(band), initial_acc, final_acc};
+  return from_hip(kla::launch_chunk_general(a, x, reinterpret_cast<hipStream_t>(stream)));
+}
+
+kla_status_t kla_pgdn_decode_step(const void *q, const void *k, const void *v, const void *g, const void *coef,
+                                  float eps, kla_gain_t gain, float band, float *state, float *acc, void *o,
+                                  int N, int H, int dk, int dv, kla_dtype_t dtype, void *stream) {
+  if (dtype != KLA_DT_BF16 && dtype != KLA_DT_F32) return KLA_ERR_DTYPE;
+  if (N < 0 || H <= 0 || dk <= 0 || dv <= 0) return KLA_ERR_SHAPE;
+  const kla_status_t st = check_pgdn(gain, band, eps);
+  if (st != KLA_OK) return st;
+  if (!kla::pgdn_decode_supported(dtype, dk, dv)) return KLA_ERR_UNSUPPORTED;
+  if (N == 0) return KLA_OK;
+  if (!q || !k || !v || !g || !coef || !state || !acc || !o) return KLA_ERR_NULL;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(g) || misaligned(coef) || misaligned(state) ||
+      misaligned(acc) || misaligned(o))
+    return KLA_ERR_ALIGN;
+  if ((long long)N * H > 0x7fffffffLL) return KLA_ERR_SHAPE;
+  const float e = gain == KLA_GAIN_KACZMARZ ? eps : 0.f;
+  kla::DecodeArgs a{q, k, v, g, coef, e, state, o, N, H, dk, dv, (int)dtype, gain == KLA_GAIN_GIVEN ? 1 : 0};
+  return from_hip(kla::launch_pgdn_decode(a, band_log(band), acc, reinterpret_cast<hipStream_t>(stream)));
+}
 
 int kla_abi_version(void) { return KLA_ABI_VERSION; }
 
@@ -154,6 +205,7 @@ const char *kla_status_str(kla_status_t s) {
     case KLA_ERR_ALIGN: return "data pointers must be 16-byte aligned";
     case KLA_ERR_WORKSPACE: return "workspace missing or smaller than kla_chunk_workspace_bytes()";
     case KLA_ERR_HIP: return "HIP runtime error";
+    case KLA_ERR_PARAM: return "gain must be a kla_gain_t and band finite and >= 1";
     case KLA_ERR_SCRATCH: return "the call needs more scratch than kla_chunk_fwd_noalloc's fixed buffer holds";
   }
   return "unknown status";

@@ -1230,7 +1230,7 @@ hipError_t launch_bwd_t(const ChunkArgs &a, const ChunkBwdArgs &b, hipStream_t s
 
 }  // namespace
 
-bool chunk_bwd_supported(int dtype, int dk, int dv, int chunk) { return chunk_supported(dtype, dk, dv, chunk); }
+bool chunk_bwd_supported(int dtype, int dk, int dv, int chunk) { return fast_chunk_supported(dtype, dk, dv, chunk); }
 
 size_t chunk_bwd_workspace_bytes(const ChunkArgs &a) {
   if (a.dtype == 0) return a.dk == 128 ? bwd_workspace_bytes_t<bf16, 64, 128>(a) : bwd_workspace_bytes_t<bf16, 64, 64>(a);

@@ -1295,6 +1295,8 @@ static size_t workspace_bytes_t(const ChunkArgs &a) {
 }
 
 size_t chunk_workspace_bytes(const ChunkArgs &a) {
+  // the general kernel (shapes outside the pipelined ones) needs no workspace
+  if (!fast_chunk_supported(a.dtype, a.dk, a.dv, a.chunk)) return 0;
   if (a.dtype == 0) return workspace_bytes_t<bf16, 64>(a);
   return a.chunk == 16 ? workspace_bytes_t<float, 16>(a) : workspace_bytes_t<float, 64>(a);
 }
@@ -1349,6 +1351,11 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t st) {
 }
 
 bool chunk_supported(int dtype, int dk, int dv, int chunk) {
+  return fast_chunk_supported(dtype, dk, dv, chunk) || general_supported(dtype, dk, dv, chunk);
+}
+
+// The shapes the pipelined prep + scan kernels are compiled for.
+bool fast_chunk_supported(int dtype, int dk, int dv, int chunk) {
   if (dtype == 0) {
     return chunk == 64 && (dk == 64 || dk == 128) && dv % 16 == 0 && dv >= 16 && dv <= 256;
   }
@@ -1368,6 +1375,10 @@ static bool use_two_column_tiles(const ChunkArgs &a) {
 }
 
 hipError_t launch_chunk_fwd(const ChunkArgs &a, hipStream_t st) {
+  if (!fast_chunk_supported(a.dtype, a.dk, a.dv, a.chunk)) {
+    const GenExtra none{0, 0.f, nullptr, nullptr};
+    return launch_chunk_general(a, none, st);
+  }
   if (a.dtype == 0) {
     const bool two = use_two_column_tiles(a);
     if (a.dk == 128) return two ? launch_chunk_t<bf16, 64, 128, 2>(a, st) : launch_chunk_t<bf16, 64, 128, 1>(a, st);

@@ -38,9 +38,21 @@ struct ChunkBwdArgs {
   float *dinitial_state;        // fp32 [N,H,dk,dv], or nullptr (not written)
 };
 
-// True if a kernel is compiled for this combination.
+// PGDN (the preconditioned variant) and its parameters, for the general chunk kernel.
+struct GenExtra {
+  int pgdn;                  // 1: write keys w_t = p_t (.) k_t (PGDN); 0: w = k
+  float band_c;              // ln(band) of the preconditioner's squash (0: p = 1)
+  const float *initial_acc;  // [N, H, dk] fp32 accumulator at the start, or nullptr (zeros)
+  float *final_acc;          // [N, H, dk] fp32, or nullptr
+};
+
+// True if a kernel is compiled for this combination.  chunk_supported covers
+// both the pipelined kernels (fast_chunk_supported) and the general kernel.
 bool decode_supported(int dtype, int dk, int dv);
 bool chunk_supported(int dtype, int dk, int dv, int chunk);
+bool fast_chunk_supported(int dtype, int dk, int dv, int chunk);
+bool general_supported(int dtype, int dk, int dv, int chunk);
+bool pgdn_decode_supported(int dtype, int dk, int dv);
 
 // Bytes of device workspace kla_chunk_fwd needs for these arguments (the
 // per-chunk T' and decay vectors handed from the prep kernel to the scan
@@ -63,5 +75,8 @@ hipError_t static_scratch(void **ptr);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_chunk_fwd(const ChunkArgs &a, hipStream_t stream);
 hipError_t launch_chunk_bwd(const ChunkArgs &a, const ChunkBwdArgs &b, hipStream_t stream);
+hipError_t launch_chunk_general(const ChunkArgs &a, const GenExtra &x, hipStream_t stream);
+// a.eta holds the coefficient (beta when a.beta_direct, else eta); acc [N, H, dk] in place
+hipError_t launch_pgdn_decode(const DecodeArgs &a, float band_c, float *acc, hipStream_t stream);
 
 }  // namespace kla

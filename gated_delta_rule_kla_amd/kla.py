@@ -13,12 +13,14 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["chunk_fwd", "chunk_workspace_bytes", "chunk_fwd_workspace_bytes", "decode_step", "gdn_chunk_fwd", "gdn_decode_step", "chunk_bwd",
+__all__ = ["chunk_fwd", "chunk_workspace_bytes", "chunk_fwd_workspace_bytes", "pgdn_chunk_fwd", "pgdn_decode_step",
+           "GAINS", "decode_step", "gdn_chunk_fwd", "gdn_decode_step", "chunk_bwd",
            "gdn_chunk_bwd", "chunk_bwd_workspace_bytes", "lib", "lib_path", "KlaError", "KLA_DT_BF16",
            "KLA_DT_F32"]
 
 KLA_DT_BF16 = 0
 KLA_DT_F32 = 1
+GAINS = {"given": 0, "kaczmarz": 1}  # kla_gain_t
 _DTYPES = {torch.bfloat16: KLA_DT_BF16, torch.float32: KLA_DT_F32}
 
 _LIB: Optional[ctypes.CDLL] = None
@@ -74,6 +76,12 @@ def lib() -> ctypes.CDLL:
         L.kla_chunk_fwd_noalloc.restype = i32
         L.kla_chunk_fwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
         L.kla_chunk_fwd_workspace_bytes.restype = sz
+        L.kla_pgdn_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, f32, i32, f32, vp, vp, vp, vp, vp, vp, vp,
+                                         i32, i32, i32, i32, i32, i32, i32, i32, vp]
+        L.kla_pgdn_chunk_fwd.restype = i32
+        L.kla_pgdn_decode_step.argtypes = [vp, vp, vp, vp, vp, f32, i32, f32, vp, vp, vp,
+                                           i32, i32, i32, i32, i32, vp]
+        L.kla_pgdn_decode_step.restype = i32
         L.kla_status_str.argtypes = [i32]
         L.kla_status_str.restype = ctypes.c_char_p
         L.kla_abi_version.argtypes = []
@@ -420,3 +428,114 @@ def gdn_decode_step(
     """One gated-delta-rule step (kla_gdn_decode_step): as decode_step with the
     update coefficient ``beta`` [N, H] given; ``state`` is updated in place."""
     return _decode_call("gdn_decode_step", q, k, v, g, beta, None, state, out)
+
+
+def pgdn_chunk_fwd(
+    q: torch.Tensor,
+    k: torch.Tensor,
+    v: torch.Tensor,
+    g: torch.Tensor,
+    coef: torch.Tensor,
+    eps: float = 1e-6,
+    gain: str = "given",
+    band: float = 1.5,
+    initial_state: Optional[torch.Tensor] = None,
+    initial_acc: Optional[torch.Tensor] = None,
+    cu_seqlens: Optional[torch.Tensor] = None,
+    chunk: int = 64,
+    output_final_state: bool = True,
+    cu_seqlens_host: Optional[torch.Tensor] = None,
+    out: Optional[torch.Tensor] = None,
+    final_state: Optional[torch.Tensor] = None,
+    final_acc: Optional[torch.Tensor] = None,
+):
+    """Preconditioned gated delta rule prefill (kla_pgdn_chunk_fwd).
+
+    As chunk_fwd, with ``coef`` [B, H, T] the update coefficient beta
+    (gain="given") or eta (gain="kaczmarz": beta = eta / (k . w + eps)), the
+    preconditioner's band x >= 1, and the key accumulator [N, H, dk] fp32 in
+    (``initial_acc``, zeros when None) and out.  Returns (o, final_state,
+    final_acc) (the last two None unless ``output_final_state`` or given)."""
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("kla.pgdn_chunk_fwd needs GPU tensors")
+    dtype = q.dtype
+    if dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {dtype}")
+    if gain not in GAINS:
+        raise ValueError(f"gain must be one of {sorted(GAINS)}")
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    for t, name, shp in ((q, "q", (B, H, T, dk)), (k, "k", (B, H, T, dk)), (v, "v", (B, H, T, dv)),
+                         (g, "g", (B, H, T)), (coef, "coef", (B, H, T))):
+        _need(t, name, dtype, shp, dev)
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, (cu_seqlens.numel(),), dev)
+        if cu_seqlens_host is None:
+            cu_seqlens_host = cu_seqlens.cpu()
+        cu_seqlens_host = cu_seqlens_host.to(torch.int32).contiguous()
+        N = cu_seqlens.numel() - 1
+    else:
+        N = B
+    if initial_state is not None:
+        _need(initial_state, "initial_state", torch.float32, (N, H, dk, dv), dev)
+    if initial_acc is not None:
+        _need(initial_acc, "initial_acc", torch.float32, (N, H, dk), dev)
+    if out is None:
+        out = torch.empty((B, H, T, dv), dtype=dtype, device=dev)
+    _need(out, "out", dtype, (B, H, T, dv), dev)
+    if output_final_state and final_state is None:
+        final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    if output_final_state and final_acc is None:
+        final_acc = torch.empty((N, H, dk), dtype=torch.float32, device=dev)
+    if final_state is not None:
+        _need(final_state, "final_state", torch.float32, (N, H, dk, dv), dev)
+    if final_acc is not None:
+        _need(final_acc, "final_acc", torch.float32, (N, H, dk), dev)
+    host_ptr = None if cu_seqlens_host is None else cu_seqlens_host.data_ptr()
+    st = lib().kla_pgdn_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(coef), float(eps), GAINS[gain],
+                                  float(band), _ptr(initial_state), _ptr(initial_acc), _ptr(out), _ptr(final_state),
+                                  _ptr(final_acc), _ptr(cu_seqlens), host_ptr, N, B, H, T, dk, dv, int(chunk),
+                                  _DTYPES[dtype], _stream(dev))
+    _check("kla_pgdn_chunk_fwd", st)
+    return out, final_state, final_acc
+
+
+def pgdn_decode_step(
+    q: torch.Tensor,
+    k: torch.Tensor,
+    v: torch.Tensor,
+    g: torch.Tensor,
+    coef: torch.Tensor,
+    eps: float,
+    state: torch.Tensor,
+    acc: torch.Tensor,
+    gain: str = "given",
+    band: float = 1.5,
+    out: Optional[torch.Tensor] = None,
+) -> torch.Tensor:
+    """One preconditioned gated-delta-rule step (kla_pgdn_decode_step);
+    ``state`` [N, H, dk, dv] and ``acc`` [N, H, dk] (fp32) are updated in place."""
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("kla.pgdn_decode_step needs GPU tensors")
+    dtype = q.dtype
+    if dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {dtype}")
+    if gain not in GAINS:
+        raise ValueError(f"gain must be one of {sorted(GAINS)}")
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    for t, name, shp in ((q, "q", (N, H, dk)), (k, "k", (N, H, dk)), (v, "v", (N, H, dv)), (g, "g", (N, H)),
+                         (coef, "coef", (N, H))):
+        _need(t, name, dtype, shp, dev)
+    _need(state, "state", torch.float32, (N, H, dk, dv), dev)
+    _need(acc, "acc", torch.float32, (N, H, dk), dev)
+    if out is None:
+        out = torch.empty((N, H, dv), dtype=dtype, device=dev)
+    _need(out, "out", dtype, (N, H, dv), dev)
+    st = lib().kla_pgdn_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(coef), float(eps), GAINS[gain],
+                                    float(band), _ptr(state), _ptr(acc), _ptr(out), N, H, dk, dv, _DTYPES[dtype],
+                                    _stream(dev))
+    _check("kla_pgdn_decode_step", st)
+    return out

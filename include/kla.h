@@ -64,8 +64,15 @@ typedef enum {
     KLA_ERR_WORKSPACE = -7,   /* workspace NULL or below kla_chunk_workspace_bytes */
     KLA_ERR_ALIGN = -8,       /* a data pointer is not 16-byte aligned           */
     KLA_ERR_HIP = -9,         /* the HIP runtime rejected a launch               */
-    KLA_ERR_SCRATCH = -10     /* kla_chunk_fwd_noalloc: more scratch than its fixed buffer */
+    KLA_ERR_SCRATCH = -10,    /* kla_chunk_fwd_noalloc: more scratch than its fixed buffer */
+    KLA_ERR_PARAM = -11       /* PGDN: gain not a kla_gain_t, or band not finite and >= 1 */
 } kla_status_t;
+
+/* The update coefficient ("gain") of the preconditioned variant (kla_pgdn_*). */
+typedef enum {
+    KLA_GAIN_GIVEN = 0,    /* coef is beta_t itself (Gated DeltaNet's learned coefficient)  */
+    KLA_GAIN_KACZMARZ = 1  /* coef is eta_t; beta_t = eta_t / (k_t . w_t + eps)             */
+} kla_gain_t;
 
 /*
  * kla_chunk_fwd -- chunkwise-parallel prefill (the block solver).
@@ -110,10 +117,13 @@ typedef enum {
  * scan kernel then walks each sequence's chunks with the state in registers,
  * and forms the decayed causal scores of Q K^T and the output.
  *
- * Supported: dtype BF16 with chunk 64 and dk in {64, 128}; dtype F32 with
- * chunk 16 and dk in {16, 32, 64, 128}, or chunk 64 and dk in {16, 32}; for
- * both, dv a multiple of 16 in [16, 256].  Anything else returns
- * KLA_ERR_UNSUPPORTED.
+ * Supported: either dtype, chunk in {16, 64}, dk in {16, 32, 64, 128}, dv a
+ * multiple of 16 in [16, 256].  Anything else returns KLA_ERR_UNSUPPORTED.
+ * The pipelined prep + scan kernels run BF16 with chunk 64 and dk in {64, 128},
+ * and F32 with chunk 16 (any dk) or chunk 64 with dk in {16, 32}; the other
+ * combinations run a general kernel (one workgroup per sequence, head and 16
+ * state columns, fp32 end to end, no workspace: kla_chunk_workspace_bytes
+ * returns 0 for them), which is correct for every shape but not tuned.
  */
 kla_status_t kla_chunk_fwd(const void *q, const void *k, const void *v,
                            const void *g, const void *eta, float eps,
@@ -248,7 +258,9 @@ kla_status_t kla_gdn_decode_step(const void *q, const void *k, const void *v,
  * alias the inputs.  Positions of the gradient tensors that belong to no
  * sequence are not written.  Status codes and validation as kla_chunk_fwd
  * (all checks on the host before any HIP call); the supported shapes are
- * kla_chunk_fwd's.  Four kernels run on `stream`: a parallel per-(chunk, head)
+ * those of kla_chunk_fwd's pipelined kernels (BF16: chunk 64, dk in {64, 128};
+ * F32: chunk 16 with dk in {16, 32, 64, 128}, chunk 64 with dk in {16, 32};
+ * dv a multiple of 16 in [16, 256]); others return KLA_ERR_UNSUPPORTED.  Four kernels run on `stream`: a parallel per-(chunk, head)
  * prep, a forward scan that stores the chunk-start states, a reverse scan of
  * the state gradients, and a parallel per-(chunk, head) gradient kernel.
  */
@@ -286,13 +298,67 @@ size_t kla_chunk_bwd_workspace_bytes(const int32_t *cu_seqlens, const int32_t *c
                                      int num_seqs, int B, int H, int T, int dk, int dv, int chunk,
                                      kla_dtype_t dtype);
 
+/*
+ * kla_pgdn_chunk_fwd -- chunkwise prefill of the preconditioned gated delta
+ * rule (PGDN), "Preconditioned DeltaNet" (gist.science/es/paper/2604.21100):
+ * §2.C accumulates the keys' diagonal second moments A_t = A_{t-1} + k_t (.) k_t
+ * and preconditions with P_t = Diag(A_t)^-1 squashed into [1/band, band];
+ * §2.A applies it to the write key (w_t = p_t (.) k_t); §2.D gives the gated
+ * variant and its block-parallel form.  Per token:
+ *
+ *     A_t  = A_{t-1} + k_t (.) k_t                     (no decay; includes token t)
+ *     p_t  = exp(c tanh(r / c)),  r_i = ln((mean_j A_t,j + 1e-30) / (A_t,i + 1e-30)),
+ *            c = ln(band)  (band = 1: p_t = 1, the gated delta rule / KLA)
+ *     w_t  = p_t (.) k_t
+ *     beta = coef_t (KLA_GAIN_GIVEN)  or  coef_t / (k_t . w_t + eps) (KLA_GAIN_KACZMARZ)
+ *     e_t  = v_t - (alpha_t S_{t-1})^T k_t,  S_t = alpha_t S_{t-1} + beta w_t e_t^T,
+ *     o_t  = S_t^T q_t,  alpha_t = exp(g_t)
+ *
+ * The page fixes the accumulator, the inverse, the band and the log-space
+ * squash; the normalisation by the mean over coordinates, the tanh form and
+ * the Kaczmarz gain are this library's reading of it.
+ *
+ *   q, k, v, g, cu_seqlens, cu_seqlens_host, num_seqs, B, H, T, dk, dv,
+ *   chunk, dtype, initial_state, o, final_state: as kla_chunk_fwd
+ *   coef          [B, H, T] dtype: beta_t (KLA_GAIN_GIVEN) or eta_t (KLA_GAIN_KACZMARZ)
+ *   eps           >= 0, finite (used by KLA_GAIN_KACZMARZ only)
+ *   band          the squash's bound x: finite, >= 1
+ *   initial_acc   [N, H, dk] fp32 accumulator before the first token, or NULL (zeros)
+ *   final_acc     [N, H, dk] fp32, or NULL (not written); may alias initial_acc
+ *
+ * Supported: either dtype, chunk in {16, 64}, dk in {16, 32, 64, 128}, dv a
+ * multiple of 16 in [16, 256]; runs the general kernel (no workspace).
+ * KLA_ERR_PARAM for a bad gain or band; other status codes as kla_chunk_fwd.
+ */
+kla_status_t kla_pgdn_chunk_fwd(const void *q, const void *k, const void *v,
+                                const void *g, const void *coef, float eps,
+                                kla_gain_t gain, float band,
+                                const float *initial_state, const float *initial_acc,
+                                void *o, float *final_state, float *final_acc,
+                                const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
+                                int num_seqs, int B, int H, int T, int dk, int dv, int chunk,
+                                kla_dtype_t dtype, void *stream);
+
+/*
+ * kla_pgdn_decode_step -- one PGDN token for N sequences x H heads (the
+ * per-token rule above): q, k [N, H, dk], v [N, H, dv], g, coef [N, H] (dtype);
+ * state [N, H, dk, dv] fp32 and acc [N, H, dk] fp32 updated IN PLACE;
+ * o [N, H, dv] dtype.  Supported: dk in {16, 32, 64, 128}, dv in [1, 256],
+ * either dtype.  Status codes as kla_pgdn_chunk_fwd.
+ */
+kla_status_t kla_pgdn_decode_step(const void *q, const void *k, const void *v,
+                                  const void *g, const void *coef, float eps,
+                                  kla_gain_t gain, float band, float *state, float *acc,
+                                  void *o, int N, int H, int dk, int dv,
+                                  kla_dtype_t dtype, void *stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *kla_status_str(kla_status_t s);
 
 /* ABI version of this header (incremented on any incompatible change). */
 int kla_abi_version(void);
 
-#define KLA_ABI_VERSION 6
+#define KLA_ABI_VERSION 7
 
 /* Size of kla_chunk_fwd_noalloc's fixed per-GPU scratch buffer, in bytes. */
 #define KLA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)

@@ -18,7 +18,9 @@ pytestmark = pytest.mark.skipif(not os.path.exists(kla.lib_path()),
 
 OK, E_NULL, E_SHAPE, E_DTYPE, E_UNSUP, E_SEQ, E_EPS, E_WS, E_ALIGN, E_HIP = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9
 E_SCRATCH = -10
+E_PARAM = -11
 FAKE = 0x7F0000000000  # never dereferenced: every case below fails validation first
+OK_IF_NO_TOKENS = "ok-if-no-tokens"
 
 
 def _declared():
@@ -32,7 +34,8 @@ def test_exports_every_declared_symbol():
     assert set(names) >= {"kla_chunk_fwd", "kla_chunk_fwd_workspace_bytes", "kla_chunk_workspace_bytes",
                           "kla_decode_step", "kla_status_str",
                           "kla_abi_version", "kla_gdn_chunk_fwd", "kla_gdn_decode_step", "kla_chunk_bwd",
-                          "kla_gdn_chunk_bwd", "kla_chunk_bwd_workspace_bytes", "kla_chunk_fwd_noalloc"}
+                          "kla_gdn_chunk_bwd", "kla_chunk_bwd_workspace_bytes", "kla_chunk_fwd_noalloc",
+                          "kla_pgdn_chunk_fwd", "kla_pgdn_decode_step"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -44,7 +47,7 @@ def test_abi_version_matches_header():
 
 def test_status_strings():
     L = kla.lib()
-    for s in (OK, E_NULL, E_SHAPE, E_DTYPE, E_UNSUP, E_SEQ, E_EPS, E_WS, E_ALIGN, E_HIP, E_SCRATCH, -77):
+    for s in (OK, E_NULL, E_SHAPE, E_DTYPE, E_UNSUP, E_SEQ, E_EPS, E_WS, E_ALIGN, E_HIP, E_SCRATCH, E_PARAM, -77):
         txt = L.kla_status_str(s)
         assert isinstance(txt, bytes) and len(txt) > 0
 
@@ -86,7 +89,7 @@ def _decode(**kw):
     (dict(dk=96), E_UNSUP),
     (dict(dv=24), E_UNSUP),
     (dict(chunk=32), E_UNSUP),
-    (dict(dtype=1, chunk=64, dk=128), E_UNSUP),  # fp32 debug build: chunk 64 needs dk <= 32
+    (dict(dk=256), E_UNSUP),                     # the general kernel stops at dk = 128
     (dict(q=None), E_NULL),
     (dict(o=None), E_NULL),
     (dict(k=FAKE + 8), E_ALIGN),
@@ -281,6 +284,9 @@ def _bwd(fn="kla_chunk_bwd", **kw):
 
 @pytest.mark.parametrize("fn", ["kla_chunk_bwd", "kla_gdn_chunk_bwd"])
 @pytest.mark.parametrize("kw,code", [
+    (dict(dtype=0, chunk=16), E_UNSUP),           # forward-only shapes (general kernel)
+    (dict(dtype=0, dk=16), E_UNSUP),
+    (dict(dtype=1, chunk=64, dk=128), E_UNSUP),
     (dict(dtype=7), E_DTYPE),
     (dict(H=0), E_SHAPE),
     (dict(N=3), E_SHAPE),
@@ -362,3 +368,59 @@ def test_noalloc_scratch_limit_and_validation():
                      (dict(q=None), E_NULL), (dict(k=FAKE + 8), E_ALIGN), (dict(N=3), E_SHAPE),
                      (dict(N=0, B=0), OK)]:
         assert _noalloc(**kw) == code, kw
+
+
+def test_chunk_fwd_supported_shape_set():
+    """The shape set of the contract: either dtype, chunk 16 or 64, dk 16 .. 128 (powers of two),
+    dv a multiple of 16 up to 256; the pipelined kernels take some of it (and need a workspace),
+    the general kernel the rest (no workspace)."""
+    for dt in (0, 1):
+        for C in (16, 64):
+            for dk in (16, 32, 64, 128):
+                for dv in (16, 128, 256):
+                    fast = (dt == 0 and C == 64 and dk in (64, 128)) or (dt == 1 and (C == 16 or dk <= 32))
+                    ws = _ws_bytes(dtype=dt, chunk=C, dk=dk, dv=dv)
+                    assert (ws > 0) == fast, (dt, C, dk, dv, ws)
+                    # supported: validation gets past the shape checks to the (failing) pointer check,
+                    # which comes before any launch
+                    assert _chunk(dtype=dt, chunk=C, dk=dk, dv=dv, q=None) == E_NULL, (dt, C, dk, dv)
+    for bad in (dict(chunk=32), dict(dk=96), dict(dk=256), dict(dv=272), dict(dv=24)):
+        assert _chunk(**bad) == E_UNSUP
+
+
+def _pgdn(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, c=FAKE, eps=1e-6, gain=0, band=1.5, s0=None, a0=None, o=FAKE,
+             sf=None, af=None, cu=None, cuh=None, N=2, B=2, H=4, T=100, dk=128, dv=128, chunk=64, dtype=0)
+    a.update(kw)
+    return kla.lib().kla_pgdn_chunk_fwd(a["q"], a["k"], a["v"], a["g"], a["c"], a["eps"], a["gain"], a["band"],
+                                        a["s0"], a["a0"], a["o"], a["sf"], a["af"], a["cu"], a["cuh"], a["N"],
+                                        a["B"], a["H"], a["T"], a["dk"], a["dv"], a["chunk"], a["dtype"], None)
+
+
+def _pgdn_dec(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, c=FAKE, eps=1e-6, gain=1, band=1.5, S=FAKE, A=FAKE, o=FAKE,
+             N=3, H=2, dk=128, dv=128, dtype=0)
+    a.update(kw)
+    return kla.lib().kla_pgdn_decode_step(a["q"], a["k"], a["v"], a["g"], a["c"], a["eps"], a["gain"], a["band"],
+                                          a["S"], a["A"], a["o"], a["N"], a["H"], a["dk"], a["dv"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(gain=2), E_PARAM), (dict(gain=-1), E_PARAM), (dict(band=0.9), E_PARAM), (dict(band=float("nan")), E_PARAM),
+    (dict(band=float("inf")), E_PARAM), (dict(gain=1, eps=-1.0), E_EPS), (dict(gain=0, eps=-1.0), OK_IF_NO_TOKENS),
+    (dict(dtype=3), E_DTYPE), (dict(dk=96), E_UNSUP), (dict(chunk=32), E_UNSUP), (dict(c=None), E_NULL),
+    (dict(a0=FAKE + 4), E_ALIGN), (dict(af=FAKE + 8), E_ALIGN), (dict(N=3), E_SHAPE), (dict(N=0, B=0), OK),
+])
+def test_pgdn_chunk_fwd_rejects(kw, code):
+    if code == OK_IF_NO_TOKENS:   # eps is unused with the given gain: only the other checks apply
+        assert _pgdn(N=0, B=0, **kw) == OK
+        return
+    assert _pgdn(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(gain=5), E_PARAM), (dict(band=0.5), E_PARAM), (dict(eps=float("nan")), E_EPS), (dict(dk=48), E_UNSUP),
+    (dict(dv=300), E_UNSUP), (dict(A=None), E_NULL), (dict(A=FAKE + 4), E_ALIGN), (dict(N=0), OK),
+])
+def test_pgdn_decode_rejects(kw, code):
+    assert _pgdn_dec(**kw) == code
