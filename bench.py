@@ -15,7 +15,8 @@ Also measured in the same run and reported in the same JSON line:
   * cpu_baseline: the fp64 CPU oracle on this host's cores (a process pool),
     on the whole prefill workload and bounded samples of the others.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--mode all|prefill|decode|backward]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+                       [--mode all|prefill|decode|backward|prefill-other]
 """
 
 from __future__ import annotations
@@ -404,7 +405,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--mode", choices=["all", "prefill", "decode", "backward"], default="all")
+    ap.add_argument("--mode", choices=["all", "prefill", "decode", "backward", "prefill-other"], default="all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 256 MiB device copy (for HBM counter calibration)")
@@ -504,6 +505,8 @@ def main():
             out.update({"value": bw["tokens"] / sec, "unit": "tokens/s", "ms_per_step": bw["ms"],
                         "config": {"workload": bwd["workload"]}, "roofline": bwd["roofline"]})
         out["backward"] = bwd
+    if args.mode == "prefill-other":
+        out["prefill_other_workloads"] = bench_prefill_other(max(2, args.steps // 20), max(1, args.warmup // 10))
     if args.mode == "all":
         out["prefill_other_workloads"] = bench_prefill_other(max(2, args.steps // 20), max(1, args.warmup // 10))
         gd = bench_gdn(args.steps, args.warmup)

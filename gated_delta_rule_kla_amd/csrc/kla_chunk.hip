@@ -806,6 +806,280 @@ __global__ __launch_bounds__(64 * kPrepWaves) void kla_chunk_prep_kernel(ChunkPa
 }
 
 // ---------------------------------------------------------------------------
+// prep kernel, one wave per (chunk, head): the bf16 build
+// ---------------------------------------------------------------------------
+// The same S-independent work and the same workspace image as the pipelined
+// prep kernel above, organised for latency hiding instead of a pipeline: each
+// workgroup is one wave that owns one (chunk, head) from start to end, and a CU
+// holds seven of them, whose load, MFMA and solve phases overlap.  Global
+// memory is only touched with coalesced 16-byte accesses (consecutive lanes,
+// consecutive bytes): K rows come in four rows per instruction into a padded
+// LDS tile and go from there into the Gram MFMA operands (the same registers
+// serve as both operands of K K^T); the packed T'^T image is assembled in the
+// same LDS area once K is in registers, and leaves in 16-byte pieces.  (Loads
+// or stores that give each lane its own row cost the texture-address unit
+// several times more per instruction; with one wave per chunk that unit, not
+// the arithmetic, set the kernel's time.)
+template <int DK>
+struct PrepWaveShape {
+  static constexpr int C = 64, NB = 4;
+  static constexpr int RB = DK * 2 + 16;   // padded K row in LDS: 16 rows hit distinct banks
+  static constexpr int LDA = 24;           // bf16 rows of one transposed 16x16 off-diagonal A block
+  static constexpr int LDD = 20;           // fp32 rows of the diagonal blocks (A, then T), transposed
+  static constexpr int TD_BYTES = NB * 16 * LDD * 4;
+  static constexpr int IMG_BYTES = TpLayout<bf16, 64>::PACK;  // the packed T'^T image
+  static constexpr int R_BYTES = C * RB > IMG_BYTES + TD_BYTES ? C * RB : IMG_BYTES + TD_BYTES;
+  static constexpr int OFF_TD = IMG_BYTES;                    // inside R, after the image
+  static constexpr int OFF_A = R_BYTES;
+  static constexpr int A_BYTES = 6 * 16 * LDA * 2;
+  static constexpr int OFF_VEC = OFF_A + A_BYTES;             // ||k||^2, gamma, beta
+  static constexpr int BYTES = OFF_VEC + 3 * C * 4;
+  static_assert(IMG_BYTES % 16 == 0 && OFF_TD % 16 == 0 && OFF_A % 16 == 0 && OFF_VEC % 16 == 0, "lds align");
+  static_assert(BYTES * 7 <= 160 * 1024, "seven workgroups per CU");
+};
+
+template <int DK>
+__global__ __launch_bounds__(64) void kla_chunk_prep_wave_kernel(ChunkParams p) {
+  using Sh = PrepWaveShape<DK>;
+  using TL = TpLayout<bf16, 64>;
+  using M = Mm16<bf16>;
+  constexpr int C = 64, NB = 4, LDA = Sh::LDA, LDD = Sh::LDD, NQ = DK / 32, PPR = DK * 2 / 16;
+  constexpr int NLD = C * PPR / 64;
+  __shared__ __attribute__((aligned(16))) char smem[Sh::BYTES];
+  const int lane = threadIdx.x;
+  const int li = lane & 15, lg = lane >> 4;
+  const int h = blockIdx.y;
+  // this wave's run of p.pslots consecutive slots of head h
+  const int s0 = blockIdx.x * p.pslots, s1 = min(s0 + p.pslots, p.nslot);
+
+  // the chunk behind a slot (as in the pipelined prep kernel): its first token
+  // and row count (0 = no chunk)
+  auto describe = [&](int slot, size_t &tok, int &nrow) {
+    int b = 0, t0 = 0, len = p.T, c = slot;
+    if (p.cu) {
+      int lo = 0, hi = p.nseq - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (mid + min(max(p.cu[mid], 0), p.T) / C <= slot) lo = mid; else hi = mid - 1;
+      }
+      t0 = min(max(p.cu[lo], 0), p.T);
+      len = min(max(p.cu[lo + 1], t0), p.T) - t0;
+      c = slot - (lo + t0 / C);
+    } else {
+      const int nchT = (p.T + C - 1) / C;
+      b = slot / nchT;
+      c = slot % nchT;
+      if (b >= p.nseq) len = 0;
+    }
+    nrow = __builtin_amdgcn_readfirstlane((slot < s1 && c >= 0 && c * C < len) ? min(C, len - c * C) : 0);
+    const size_t t = ((size_t)b * p.H + h) * (size_t)p.T + (size_t)t0 + (size_t)max(c, 0) * C;
+    const unsigned lo32 = __builtin_amdgcn_readfirstlane((unsigned)t), hi32 = __builtin_amdgcn_readfirstlane((unsigned)(t >> 32));
+    tok = ((size_t)hi32 << 32) | lo32;
+  };
+  // K rows (coalesced; rows past the end read as zero), g and eta of row `lane`
+  uint4 kr[NLD];
+  unsigned short lgraw = 0, leraw = 0;
+  auto issue = [&](size_t tok, int nrow) {
+    const bf16 *gk = static_cast<const bf16 *>(p.k) + tok * DK;
+    const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(gk, nrow * DK * 2);
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) kr[j] = buffer_ld16(rk, (64 * j + lane) * 16);
+    const bf16 *gp = static_cast<const bf16 *>(p.g) + tok, *ep = static_cast<const bf16 *>(p.eta) + tok;
+    lgraw = buffer_ld_elem(buffer_rsrc(gp, nrow * 2), lane, gp);
+    leraw = buffer_ld_elem(buffer_rsrc(ep, nrow * 2), lane, ep);
+  };
+
+  char *R = smem;  // K rows, then the packed image and the diagonal blocks
+  bf16 *img = reinterpret_cast<bf16 *>(R);
+  float *Td = reinterpret_cast<float *>(R + Sh::OFF_TD);
+  bf16 *Ablk = reinterpret_cast<bf16 *>(smem + Sh::OFF_A);
+  float *sNrm = reinterpret_cast<float *>(smem + Sh::OFF_VEC);
+  float *sGam = sNrm + C, *sBet = sNrm + 2 * C;
+
+  // the loaded K rows into the LDS tile (waits for those loads)
+  auto stage = [&]() {
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) {
+      const int pc = 64 * j + lane;
+      *reinterpret_cast<uint4 *>(R + (pc / PPR) * Sh::RB + (pc % PPR) * 16) = kr[j];
+    }
+  };
+  // everything else for one slot, from the staged K rows and its g, eta
+  auto process = [&](int slot, int nrow, unsigned short graw, unsigned short eraw) {
+    char *ws = p.ws + ((size_t)h * p.nslot + slot) * TL::BYTES;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    // operand layout: lane supplies row 16 rb + li, columns 32 q + 8 lg .. + 7
+    bf16x8 kf[NB][NQ];
+#pragma unroll
+    for (int rb = 0; rb < NB; ++rb)
+#pragma unroll
+      for (int q = 0; q < NQ; ++q)
+        kf[rb][q] = *reinterpret_cast<const bf16x8 *>(R + (16 * rb + li) * Sh::RB + (32 * q + 8 * lg) * 2);
+
+    // ---- Gram tiles G[rt][st] = K_rt K_st^T (st <= rt) and the norms -----------
+    f32x4 G[NB][NB];
+#pragma unroll
+    for (int rt = 0; rt < NB; ++rt)
+#pragma unroll
+      for (int st = 0; st <= rt; ++st) {
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[rt][q], kf[st][q], acc, 0, 0, 0);
+        G[rt][st] = acc;
+      }
+#pragma unroll
+    for (int rt = 0; rt < NB; ++rt) {
+      // ||k_r||^2 of row 16 rt + li: diagonal tile, lane group li >> 2, element li & 3
+      const f32x4 d = G[rt][rt];
+      const int j = li & 3;
+      const float nr = j == 0 ? d[0] : j == 1 ? d[1] : j == 2 ? d[2] : d[3];
+      if (lg == (li >> 2)) sNrm[16 * rt + li] = nr;
+    }
+    // gate scan, Gam, d, beta (lane = chunk row); beta past the sequence end is 0
+    const float gam = wave_inclusive_scan(elem_bits_to_f32(graw));
+    const float gamC = lane_value(gam, C - 1);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the norms, written by other lanes
+    const float el = elem_bits_to_f32(eraw);
+    const float beta = lane < nrow ? (p.beta_direct ? el : el / (sNrm[lane] + p.eps)) : 0.f;
+    sGam[lane] = gam;
+    sBet[lane] = beta;
+    {
+      float *vec = reinterpret_cast<float *>(ws + TL::PACK);
+      vec[lane] = gam;
+      vec[C + lane] = __expf(gam);
+      vec[2 * C + lane] = __expf(gamC - gam);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+
+    // ---- A = beta_r (K K^T)_rs exp(gamma_r - gamma_s), r > s ---------------------
+    // (the K rows in R are dead: every lane's operand reads completed before the Gram)
+#pragma unroll
+    for (int rt = 0; rt < NB; ++rt) {
+      const f32x4 gr4 = *reinterpret_cast<const f32x4 *>(sGam + 16 * rt + 4 * lg);
+      const f32x4 br4 = *reinterpret_cast<const f32x4 *>(sBet + 16 * rt + 4 * lg);
+#pragma unroll
+      for (int st = 0; st <= rt; ++st) {
+        const float gs = sGam[16 * st + li];
+        const f32x4 acc = G[rt][st];
+        f32x4 av;
+        if (st < rt) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) av[j] = br4[j] * acc[j] * __expf(gr4[j] - gs);
+          store4(Ablk + (rt * (rt - 1) / 2 + st) * 16 * LDA + li * LDA + 4 * lg, av);  // A^T[s'][r']
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const bool below = 4 * lg + j > li;
+            av[j] = below ? br4[j] * acc[j] * __expf(gr4[j] - gs) : 0.f;
+          }
+          *reinterpret_cast<f32x4 *>(Td + (rt * 16 + li) * LDD + 4 * lg) = av;  // A_bb^T, fp32
+        }
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+
+    // packed image position of T'^T[s][col], col in grouped order (perm)
+    auto pk = [&](int s, int pc) {
+      return s < TL::RW ? s * C + pc : TL::RW * C + (s - TL::RW) * (C - TL::RW) + (pc - TL::RW);
+    };
+    auto put4 = [&](int s, int col, f32x4 v) {  // four consecutive columns col..col+3 (col % 4 == 0)
+      store4(img + pk(s, Ops<bf16>::perm(col)), v);
+    };
+
+    // ---- diagonal blocks T_bb = (I + A_bb)^-1: lane = (block lg, column li) -----
+    {
+      float *At = Td + lg * 16 * LDD;
+      float x[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) x[r] = (r == li) ? 1.f : 0.f;
+      f32x4 cur[4], nxt[4];
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) cur[qd] = *reinterpret_cast<const f32x4 *>(At + 4 * qd);
+#pragma unroll
+      for (int s2 = 0; s2 < 15; ++s2) {
+        if (s2 + 1 < 15) {
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd)
+            if (4 * qd + 3 > s2 + 1) nxt[qd] = *reinterpret_cast<const f32x4 *>(At + (s2 + 1) * LDD + 4 * qd);
+        }
+#pragma unroll
+        for (int r = s2 + 1; r < 16; ++r) x[r] = fmaf(-cur[r >> 2][r & 3], x[s2], x[r]);
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) cur[qd] = nxt[qd];
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // every lane has read its A_bb rows
+      const float bs = sBet[16 * lg + li];
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {
+        const f32x4 t4 = {x[4 * qd], x[4 * qd + 1], x[4 * qd + 2], x[4 * qd + 3]};
+        *reinterpret_cast<f32x4 *>(At + li * LDD + 4 * qd) = t4;  // T_bb, transposed
+        put4(16 * lg + li, 16 * lg + 4 * qd, bs * t4);           // diagonal block of T'^T
+      }
+    }
+    // the zero blocks inside the packed part: rows 16..31 x columns 0..15 and rows 48..63 x 32..47
+    put4(16 + li, 4 * lg, zero4());
+    put4(48 + li, 32 + 4 * lg, zero4());
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+
+    // ---- off-diagonal blocks level by level: T_ij = -T_ii sum_m A_im T_mj ---------
+    {
+      f32x4 Toff[NB][NB];
+#pragma unroll
+      for (int dist = 1; dist < NB; ++dist) {
+#pragma unroll
+        for (int i = dist; i < NB; ++i) {
+          const int j = i - dist;
+          f32x4 y = zero4();
+#pragma unroll
+          for (int m = j; m < i; ++m) {
+            const M::Op a = M::ld_t(Ablk + (i * (i - 1) / 2 + m) * 16 * LDA, LDA, lane);
+            const f32x4 bt = (m == j) ? *reinterpret_cast<const f32x4 *>(Td + (j * 16 + li) * LDD + 4 * lg) : Toff[m][j];
+            y = M::mma(a, M::cvt(bt), y);
+          }
+          f32x4 ti;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ti[e] = Td[(i * 16 + 4 * lg + e) * LDD + li];
+          const f32x4 t = -M::mma(M::cvt(ti), M::cvt(y), zero4());
+          Toff[i][j] = t;
+          put4(16 * j + li, 16 * i + 4 * lg, sBet[16 * j + li] * t);  // T'^T[16j + li][16i + 4lg + e]
+        }
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+
+    // ---- the packed image to the workspace, 16-byte pieces ----------------------
+    static_assert(TL::PACK % 1024 == 0, "whole instructions of 16-byte pieces");
+#pragma unroll
+    for (int j = 0; j < TL::PACK / 1024; ++j) {
+      const int pc = 64 * j + lane;
+      reinterpret_cast<uint4 *>(ws)[pc] = *reinterpret_cast<const uint4 *>(R + 16 * pc);
+    }
+    // the LDS of this slot is reused by the next: its reads have all completed
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  };
+
+  // ---- the run: the next slot's loads are in flight while this one computes ----
+  // (one register set: the current slot's rows are in LDS before the next
+  // slot's loads reuse the registers)
+  if (s0 >= s1) return;
+  size_t cur_tok;
+  int cur_rows;
+  describe(s0, cur_tok, cur_rows);
+  if (cur_rows > 0) issue(cur_tok, cur_rows);
+  for (int slot = s0; slot < s1; ++slot) {
+    size_t nxt_tok;
+    int nxt_rows;
+    describe(slot + 1, nxt_tok, nxt_rows);
+    const unsigned short graw = lgraw, eraw = leraw;
+    if (cur_rows > 0) stage();
+    if (nxt_rows > 0) issue(nxt_tok, nxt_rows);
+    if (cur_rows > 0) process(slot, cur_rows, graw, eraw);
+    cur_tok = nxt_tok;
+    cur_rows = nxt_rows;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // scan kernel: roles and LDS plan
 // ---------------------------------------------------------------------------
 // Waves of a workgroup.  Step i (one barrier each, i = -1 .. nch) has
@@ -1336,13 +1610,25 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t st) {
     p.order = order;
   }
   if ((long long)a.B * a.T > 0 && p.nslot > 0) {
-    // slots per workgroup: the longest run that still gives two workgroups
-    // per CU (the pipeline is latency-bound; two resident workgroups overlap)
-    const long long work = (long long)p.nslot * a.H;
-    p.pslots = (int)std::min<long long>(kPrepSlots, std::max<long long>(2, work / 512));
-    const unsigned runs = (unsigned)((p.nslot + p.pslots - 1) / p.pslots);
-    hipLaunchKernelGGL((kla_chunk_prep_kernel<E, C, DK>), dim3(runs, (unsigned)a.H),
-                       dim3(PrepShape<E, C, DK>::NT), 0, st, p);
+    if constexpr (std::is_same<E, bf16>::value && C == 64) {
+      // bf16: one wave per run of consecutive slots of one head, each run
+      // prefetching its next slot while it computes the current one.  Runs of
+      // one slot while the grid is at most about two rounds of the seven
+      // one-wave workgroups a CU holds (more concurrent waves hide more);
+      // longer runs beyond that, where the prefetch overlaps every round.
+      const long long total = (long long)p.nslot * a.H;
+      p.pslots = (int)std::min<long long>(8, std::max<long long>(1, total / (2 * 7 * 256)));
+      const unsigned runs = (unsigned)((p.nslot + p.pslots - 1) / p.pslots);
+      hipLaunchKernelGGL((kla_chunk_prep_wave_kernel<DK>), dim3(runs, (unsigned)a.H), dim3(64), 0, st, p);
+    } else {
+      // slots per workgroup: the longest run that still gives two workgroups
+      // per CU (the pipeline is latency-bound; two resident workgroups overlap)
+      const long long work = (long long)p.nslot * a.H;
+      p.pslots = (int)std::min<long long>(kPrepSlots, std::max<long long>(2, work / 512));
+      const unsigned runs = (unsigned)((p.nslot + p.pslots - 1) / p.pslots);
+      hipLaunchKernelGGL((kla_chunk_prep_kernel<E, C, DK>), dim3(runs, (unsigned)a.H),
+                         dim3(PrepShape<E, C, DK>::NT), 0, st, p);
+    }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
