@@ -18,8 +18,9 @@
 // Four kernels, through a caller-provided workspace:
 //   prep     (chunk, head) in parallel: b, gamma, ||k||^2, T, P and K K^T . E into the
 //            workspace.
-//   states   (sequence, head, 32 state columns, or 16 when dv is not a multiple of 32):
-//            the chunk-start states, in order.
+//   states   the chunk-start states, in order: the forward's own pipelined prep and
+//            scan kernels (kla_chunk.hip) in states mode, which write the state at
+//            the start of every chunk instead of the outputs.
 //   dstates  (sequence, head, 32 or 16 state columns): dS' of every chunk, in reverse
 //            order; the gradient of the initial state is what is left at the start.
 //   grads    (chunk, head) in parallel: everything else from S, dS' and the chunk's
@@ -407,143 +408,6 @@ __global__ __launch_bounds__(kPT) void kla_bwd_prep_kernel(BwdParams p) {
 // products (16-row tiles of C) are spread over the waves by (row tile, column tile).
 
 // ============================================================================
-// states: the chunk-start state of every chunk, 16 state columns per workgroup
-// ============================================================================
-template <int C, int DK, int NS>
-struct StatesSmem {
-  static constexpr int LS = NS + 4;  // V, X and S slice rows (a multiple of 4 floats, see kLS)
-  static constexpr int LK = DK + 4, LC = C + 4;
-  static constexpr int K = 0, T = K + C * LK, V = T + C * LC, X = V + C * LS, S = X + C * LS;
-  static constexpr int BETA = S + DK * LS, GAM = BETA + C, FLOATS = GAM + C;
-};
-
-// NS state columns per workgroup (16 or 32), as for the state-gradient scan below.
-template <typename E, int C, int DK, int NS>
-__global__ __launch_bounds__(kNT) void kla_bwd_states_kernel(BwdParams p) {
-  using L = StatesSmem<C, DK, NS>;
-  using R = PrepRec<E, C>;
-  using MM = Mma16<E>;
-  constexpr int LK = L::LK, LC = L::LC, LS = L::LS, CT = NS / 16;
-  constexpr int NRT = C / 16, NKT = DK / 16;
-  static_assert(NRT <= kNT / 64 && NKT <= kNT / 64 && NS % 16 == 0, "one 16-row tile per wave");
-  __shared__ __attribute__((aligned(16))) float sm[L::FLOATS];
-  float *sK = sm + L::K, *sT = sm + L::T, *sV = sm + L::V, *sX = sm + L::X, *sS = sm + L::S;
-  float *sb = sm + L::BETA, *sgam = sm + L::GAM;
-  const int t = threadIdx.x;
-  const int w = t >> 6, lane = t & 63, lr = lane & 15, lg = lane >> 4;
-  const int nsd = p.DV / NS;
-  // blockIdx % 8 picks the XCD: the column slices of one (sequence, head) go to one XCD so
-  // that they share the chunk's K, T (and Q, P) through its L2; the grid is padded to
-  // whole rounds of 8 groups
-  const int xcd = blockIdx.x & 7, i8 = blockIdx.x >> 3;
-  const int gidx = (i8 / nsd) * 8 + xcd, js = i8 % nsd;
-  if (gidx >= p.nseq * p.H) return;  // padding (uniform per workgroup)
-  const int h = gidx % p.H, n = gidx / p.H;
-  const int col0 = js * NS;
-  const SeqLoc sq = seq_loc(p, n, h, C);
-  const size_t sbase = ((size_t)n * p.H + h) * DK * p.DV;
-  if (p.s0) {
-    load_rows<float, DK, NS, LS, kNT>(sS, p.s0 + sbase, 0, DK, col0, p.DV);
-  } else {
-    for (int e = t; e < DK * NS; e += kNT) sS[(e / NS) * LS + e % NS] = 0.f;
-  }
-  __syncthreads();
-  const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
-  f32x4 Sr[CT];  // state rows 16w + 4lg + i, column 16 ct + lr (waves w < NKT)
-#pragma unroll
-  for (int ct = 0; ct < CT; ++ct) {
-    Sr[ct] = z4;
-    if (w < NKT) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) Sr[ct][i] = sS[(16 * w + 4 * lg + i) * LS + 16 * ct + lr];
-    }
-  }
-  const int nch = (sq.len + C - 1) / C;
-  // the next chunk's K rows, V slice, T and (b, gamma) are loaded while this one is computed
-  TileLoad<E, C, DK, LK, kNT> lk;
-  TileLoad<E, C, NS, LS, kNT> lv;
-  TileLoad<E, C, C, LC, kNT> lt;
-  TileLoad<float, 2, C, C, kNT> lb;  // b then gamma (adjacent in the record)
-  auto issue = [&](int c) {
-    const int rows = min(C, sq.len - c * C);
-    const long long row0 = sq.row0 + (long long)c * C;
-    char *recb = R::at(p.prep, (size_t)h * p.nslot + sq.slot0 + c);
-    lk.issue(p.k, row0, rows, 0, DK);
-    lv.issue(p.v, row0, rows, col0, p.DV);
-    lt.issue(R::mat(recb) + R::TM, 0, C, 0, C);
-    lb.issue(R::vec(recb) + R::BETA, 0, 2, 0, C);
-  };
-  if (nch > 0) issue(0);
-  for (int c = 0; c < nch; ++c) {
-    const size_t slot = (size_t)h * p.nslot + sq.slot0 + c;
-    if (w < NKT) {
-      E *st = static_cast<E *>(p.states) + slot * DK * p.DV;
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          st[(size_t)(16 * w + 4 * lg + i) * p.DV + col0 + 16 * ct + lr] = Elem<E>::from_f32(Sr[ct][i]);
-    }
-    __syncthreads();  // the previous chunk's readers of sK, sV, sT are done
-    lk.put(sK);
-    lv.put(sV);
-    lt.put(sT);
-    lb.put(sb);  // sb and sgam are adjacent in LDS: rows of stride C
-    if (c + 1 < nch) issue(c + 1);
-    __syncthreads();
-    // The row-tile phases: wave w takes row tile w & 3 and column tile w >> 2 (with 16
-    // state columns waves 4-7 have none and wait).
-    const int rtw = w & 3, ctw = w >> 2;
-    const bool tile = rtw < NRT && ctw < CT;  // (uniform per wave)
-    const int ra = 16 * rtw + lr, cc = 16 * ctw + lr;
-    // Diag(b) X = Diag(b) (V - Diag(Gam) K S)
-    if (tile) {
-      f32x4 ks = z4;
-#pragma unroll 4
-      for (int k0 = 0; k0 < DK; k0 += 16)
-        ks = MM::run(vec4(sK + ra * LK + k0 + 4 * lg), gat4(sS + (k0 + 4 * lg) * LS + cc, LS), ks);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * rtw + 4 * lg + i;
-        sX[r * LS + cc] = sb[r] * (sV[r * LS + cc] - __expf(sgam[r]) * ks[i]);
-      }
-    }
-    __syncthreads();
-    // Diag(d) U with U = T Diag(b) X (T lower triangular), into sV
-    const float gC = sgam[C - 1];
-    if (tile) {
-      f32x4 u = z4;
-      for (int k0 = 0; k0 < 16 * (rtw + 1); k0 += 16)
-        u = MM::run(vec4(sT + ra * LC + k0 + 4 * lg), gat4(sX + (k0 + 4 * lg) * LS + cc, LS), u);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * rtw + 4 * lg + i;
-        sV[r * LS + cc] = __expf(gC - sgam[r]) * u[i];
-      }
-    }
-    __syncthreads();
-    // S <- Gam_C S + K^T Diag(d) U, state rows of wave w; copy to LDS for the next K S
-    if (w < NKT) {
-      const int ia = 16 * w + lr;
-      const float GC = __expf(gC);
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct) Sr[ct] = GC * Sr[ct];
-#pragma unroll
-      for (int k0 = 0; k0 < C; k0 += 16) {
-        const f32x4 ka = gat4(sK + (k0 + 4 * lg) * LK + ia, LK);
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct)
-          Sr[ct] = MM::run(ka, gat4(sV + (k0 + 4 * lg) * LS + 16 * ct + lr, LS), Sr[ct]);
-      }
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sS[(16 * w + 4 * lg + i) * LS + 16 * ct + lr] = Sr[ct][i];
-    }
-  }
-}
-
-// ============================================================================
 // dstates: dS' of every chunk (reverse order) and the initial-state gradient
 // ============================================================================
 template <int C, int DK, int NS>
@@ -710,6 +574,44 @@ __global__ __launch_bounds__(kNT) void kla_bwd_dstates_kernel(BwdParams p) {
   }
 }
 
+// One 16-column slice of a chunk-start state stored in the forward scan's
+// operand groups (kla_chunk.hip, ChunkParams::states): for each group q of KG
+// state rows, 64 lanes x 16 bytes, lane l holding column l & 15 of the slice and
+// rows (bf16, KG = 32) 32 q + 16 (x >> 2) + 4 (l >> 4) + (x & 3) or (fp32, KG = 16)
+// 16 q + 4 (l >> 4) + x.  One contiguous block per slice, moved as 16-byte pieces
+// and scattered into fp32 LDS rows of stride kLS.
+template <typename E, int DK> struct GroupLoad {
+  static constexpr int EPV = 16 / (int)sizeof(E);  // elements per piece (8 or 4)
+  static constexpr int KG = sizeof(E) == 2 ? 32 : 16;
+  static constexpr int NP = DK * kNS / EPV;        // pieces per slice
+  static constexpr int PER = (NP + kGT - 1) / kGT;
+  uint4 v[PER];
+  // base: the chunk's states (DK x DV elements); slice js = columns 16 js ..
+  __device__ __forceinline__ void issue(const E *base, int js) {
+    const uint4 *src = reinterpret_cast<const uint4 *>(base + (size_t)js * DK * kNS);
+#pragma unroll
+    for (int m = 0; m < PER; ++m) {
+      const int pc = (int)threadIdx.x + m * kGT;
+      if (pc < NP) v[m] = src[pc];
+    }
+  }
+  __device__ __forceinline__ void put(float *dst) const {
+#pragma unroll
+    for (int m = 0; m < PER; ++m) {
+      const int pc = (int)threadIdx.x + m * kGT;
+      if (pc < NP) {
+        const int q = pc >> 6, l = pc & 63;
+        const E *e = reinterpret_cast<const E *>(&v[m]);
+#pragma unroll
+        for (int x = 0; x < EPV; ++x) {
+          const int row = KG == 32 ? 32 * q + 16 * (x >> 2) + 4 * (l >> 4) + (x & 3) : 16 * q + 4 * (l >> 4) + x;
+          dst[row * kLS + (l & 15)] = Elem<E>::to_f32(e[x]);
+        }
+      }
+    }
+  }
+};
+
 // ============================================================================
 // grads: dq, dk, dv, dg, deta of one (chunk, head)
 // ============================================================================
@@ -805,11 +707,12 @@ __global__ __launch_bounds__(kGT) void kla_bwd_grads_kernel(BwdParams p) {
   float gcp = 0.f;  // partial <S, dS'>
 
   // slice js + 1 of S, dS', V and dO is loaded while slice js is computed
-  TileLoad<E, DK, kNS, kLS, kGT> ls, ld_;
+  GroupLoad<E, DK> ls;
+  TileLoad<E, DK, kNS, kLS, kGT> ld_;
   TileLoad<E, C, kNS, kLS, kGT> lv, lo;
   auto issue = [&](int js) {
     const int col0 = js * kNS;
-    ls.issue(Sg, 0, DK, col0, p.DV);
+    ls.issue(Sg, js);
     ld_.issue(Dg, 0, DK, col0, p.DV);
     lv.issue(p.v, cl.row0, rows, col0, p.DV);
     lo.issue(p.dout, cl.row0, rows, col0, p.DV);
@@ -1152,16 +1055,18 @@ int bwd_slots(const ChunkArgs &a) {
   return a.cu_seqlens ? a.T / C + a.num_seqs + 1 : a.B * ((a.T + C - 1) / C);
 }
 
+// After the two state regions: the forward's own workspace, used by the forward
+// kernels that produce the chunk-start states (launch_chunk_states).
 template <typename E, int C, int DK>
 size_t bwd_workspace_bytes_t(const ChunkArgs &a) {
   const int ns = bwd_slots<C>(a);
-  return BwdLayout<E, C, DK>::prep_bytes(a, ns) + 2 * BwdLayout<E, C, DK>::state_bytes(a, ns);
+  return BwdLayout<E, C, DK>::prep_bytes(a, ns) + 2 * BwdLayout<E, C, DK>::state_bytes(a, ns) +
+         chunk_workspace_bytes(a);
 }
 
 template <typename E, int C, int DK>
 hipError_t launch_bwd_t(const ChunkArgs &a, const ChunkBwdArgs &b, hipStream_t st) {
   static_assert(PrepSmem<E, C, DK>::BYTES <= 64 * 1024, "prep LDS (kept small: several workgroups per CU)");
-  static_assert(StatesSmem<C, DK, 32>::FLOATS * 4 <= 160 * 1024, "states LDS");
   static_assert(DStatesSmem<C, DK, 32>::FLOATS * 4 <= 160 * 1024, "dstates LDS");
   static_assert(GradSmem<C, DK>::FLOATS * 4 <= 160 * 1024, "grads LDS");
   BwdParams p;
@@ -1204,11 +1109,13 @@ hipError_t launch_bwd_t(const ChunkArgs &a, const ChunkBwdArgs &b, hipStream_t s
     hipLaunchKernelGGL((kla_bwd_prep_kernel<E, C, DK>), dim3((unsigned)p.nslot, (unsigned)a.H), dim3(kPT), 0, st, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (scan_blocks > 0 && ns32)
-      hipLaunchKernelGGL((kla_bwd_states_kernel<E, C, DK, 32>), dim3(scan_blocks), dim3(kNT), 0, st, p);
-    else if (scan_blocks > 0)
-      hipLaunchKernelGGL((kla_bwd_states_kernel<E, C, DK, 16>), dim3(scan_blocks), dim3(kNT), 0, st, p);
-    e = hipGetLastError();
+    // the chunk-start states: the forward's pipelined prep and scan kernels in states
+    // mode (no outputs), into p.states as operand groups
+    ChunkArgs fa = a;
+    fa.o = nullptr;
+    fa.final_state = nullptr;
+    fa.workspace = ws + pb + 2 * sb;
+    e = launch_chunk_states(fa, p.states, st);
     if (e != hipSuccess) return e;
   }
   if (seq_blocks > 0 && (tokens || p.ds0)) {

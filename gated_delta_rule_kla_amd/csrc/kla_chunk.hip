@@ -361,6 +361,13 @@ struct ChunkParams {
   int H, T, dv, n_tiles, ngroups, nseq, nslot;
   int pslots;  // prep kernel: workspace slots per workgroup (1 .. kPrepSlots)
   int beta_direct;  // 1: `eta` holds beta itself (gated delta rule); eps unused
+  // States mode (the backward pass's chunk-start states): when set, the scan
+  // writes the state at the start of every chunk here instead of the outputs,
+  // as the chain's operand groups: slot (h * nslot + slot of the chunk), then
+  // 16-column tile, then group q of KG state rows, 64 lanes x 16 bytes (lane l,
+  // element x: column l & 15 of the tile; bf16 rows 16 (x >> 2) + 4 (l >> 4) +
+  // (x & 3), fp32 rows 4 (l >> 4) + x, of the group).  o and sfin are unused.
+  char *states;
 };
 
 // Raw buffer resource over bytes [0, n) of p: loads at offsets >= n return 0
@@ -1247,6 +1254,17 @@ __global__ __launch_bounds__(64 * kWaves) void kla_chunk_kernel(ChunkParams p) {
           sb[ct][q] = O::b_from_d(&accS[ct][q * TPG]);
           suS[((CT0 + ct) * NQG + q) * 64 + lane] = sb[ct][q];
         }
+      if (p.states) {
+        // the chunk-start state of chunk c, in operand groups (coalesced 16-byte stores)
+        const size_t slot = (size_t)h * p.nslot + slot0 + c;
+#pragma unroll
+        for (int ct = 0; ct < NCW; ++ct)
+#pragma unroll
+          for (int q = 0; q < NQG; ++q) {
+            const size_t grp = (slot * (size_t)(dv / 16) + (size_t)(jt * NCT + CT0 + ct)) * NQG + q;
+            reinterpret_cast<Grp *>(p.states + grp * 64 * 16)[lane] = sb[ct][q];
+          }
+      }
     };
     __syncthreads();
     for (int i = -1; i <= iend; ++i) {
@@ -1358,9 +1376,10 @@ __global__ __launch_bounds__(64 * kWaves) void kla_chunk_kernel(ChunkParams p) {
       constexpr int NOW1 = NOWN > 0 ? NOWN : 1;
       f32x4 ao[NCT][NOW1];  // output of the pending chunk, as O^T tiles
       Grp pa[NOW1][NCG];    // its P rows as left operands
+      const bool outputs = p.states == nullptr;  // states mode writes no outputs
       __syncthreads();
       for (int i = -1; i <= iend; ++i) {
-        if (NOWN > 0 && i >= 1 && i <= nch) {
+        if (NOWN > 0 && outputs && i >= 1 && i <= nch) {
           // ---- output of chunk i-1: O = Diag(Gam) Q S + P U~ ----
           const int c = i - 1;
           const int nrow = nrow_of(c);
@@ -1390,7 +1409,7 @@ __global__ __launch_bounds__(64 * kWaves) void kla_chunk_kernel(ChunkParams p) {
             }
           }
         }
-        if (NOWN > 0 && i >= 0 && i < nch) {
+        if (NOWN > 0 && outputs && i >= 0 && i < nch) {
           // ---- chunk i: P rows and Diag(Gam) Q S ----
           const int c = i;
           const E *Q = sQ(c);
@@ -1576,9 +1595,10 @@ size_t chunk_workspace_bytes(const ChunkArgs &a) {
 }
 
 template <typename E, int C, int DK, int NCT>
-static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t st) {
+static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t st, char *states = nullptr) {
   using Sh = ChunkShape<E, C, DK, NCT>;
   ChunkParams p;
+  p.states = states;
   p.q = a.q;
   p.k = a.k;
   p.v = a.v;
@@ -1660,31 +1680,42 @@ static bool use_two_column_tiles(const ChunkArgs &a) {
   return a.dv % 32 == 0 && (long long)a.num_seqs * a.H * (a.dv / 32) >= 256;
 }
 
+static hipError_t launch_fast(const ChunkArgs &a, hipStream_t st, char *states) {
+  if (a.dtype == 0) {
+    const bool two = use_two_column_tiles(a);
+    if (a.dk == 128)
+      return two ? launch_chunk_t<bf16, 64, 128, 2>(a, st, states) : launch_chunk_t<bf16, 64, 128, 1>(a, st, states);
+    if (a.dk == 64)
+      return two ? launch_chunk_t<bf16, 64, 64, 2>(a, st, states) : launch_chunk_t<bf16, 64, 64, 1>(a, st, states);
+    return hipErrorInvalidValue;
+  }
+  if (a.chunk == 16) {
+    switch (a.dk) {
+      case 16: return launch_chunk_t<float, 16, 16, 1>(a, st, states);
+      case 32: return launch_chunk_t<float, 16, 32, 1>(a, st, states);
+      case 64: return launch_chunk_t<float, 16, 64, 1>(a, st, states);
+      case 128: return launch_chunk_t<float, 16, 128, 1>(a, st, states);
+    }
+  } else if (a.chunk == 64) {
+    switch (a.dk) {
+      case 16: return launch_chunk_t<float, 64, 16, 1>(a, st, states);
+      case 32: return launch_chunk_t<float, 64, 32, 1>(a, st, states);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_chunk_fwd(const ChunkArgs &a, hipStream_t st) {
   if (!fast_chunk_supported(a.dtype, a.dk, a.dv, a.chunk)) {
     const GenExtra none{0, 0.f, nullptr, nullptr};
     return launch_chunk_general(a, none, st);
   }
-  if (a.dtype == 0) {
-    const bool two = use_two_column_tiles(a);
-    if (a.dk == 128) return two ? launch_chunk_t<bf16, 64, 128, 2>(a, st) : launch_chunk_t<bf16, 64, 128, 1>(a, st);
-    if (a.dk == 64) return two ? launch_chunk_t<bf16, 64, 64, 2>(a, st) : launch_chunk_t<bf16, 64, 64, 1>(a, st);
-    return hipErrorInvalidValue;
-  }
-  if (a.chunk == 16) {
-    switch (a.dk) {
-      case 16: return launch_chunk_t<float, 16, 16, 1>(a, st);
-      case 32: return launch_chunk_t<float, 16, 32, 1>(a, st);
-      case 64: return launch_chunk_t<float, 16, 64, 1>(a, st);
-      case 128: return launch_chunk_t<float, 16, 128, 1>(a, st);
-    }
-  } else if (a.chunk == 64) {
-    switch (a.dk) {
-      case 16: return launch_chunk_t<float, 64, 16, 1>(a, st);
-      case 32: return launch_chunk_t<float, 64, 32, 1>(a, st);
-    }
-  }
-  return hipErrorInvalidValue;
+  return launch_fast(a, st, nullptr);
+}
+
+hipError_t launch_chunk_states(const ChunkArgs &a, void *states, hipStream_t st) {
+  if (!fast_chunk_supported(a.dtype, a.dk, a.dv, a.chunk)) return hipErrorInvalidValue;
+  return launch_fast(a, st, static_cast<char *>(states));
 }
 
 // ---------------------------------------------------------------------------

@@ -76,6 +76,11 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_chunk_fwd(const ChunkArgs &a, hipStream_t stream);
 hipError_t launch_chunk_bwd(const ChunkArgs &a, const ChunkBwdArgs &b, hipStream_t stream);
 hipError_t launch_chunk_general(const ChunkArgs &a, const GenExtra &x, hipStream_t stream);
+// The forward's prep and scan kernels in states mode: the state at the start of
+// every chunk into `states` (the layout of ChunkParams::states in
+// kla_chunk.hip; dk * dv elements of the element type per (head, slot)), no
+// outputs.  a.workspace is the forward workspace (chunk_workspace_bytes(a)).
+hipError_t launch_chunk_states(const ChunkArgs &a, void *states, hipStream_t stream);
 // a.eta holds the coefficient (beta when a.beta_direct, else eta); acc [N, H, dk] in place
 hipError_t launch_pgdn_decode(const DecodeArgs &a, float band_c, float *acc, hipStream_t stream);
 
