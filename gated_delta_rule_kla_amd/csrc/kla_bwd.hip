@@ -21,8 +21,9 @@
 //   states   the chunk-start states, in order: the forward's own pipelined prep and
 //            scan kernels (kla_chunk.hip) in states mode, which write the state at
 //            the start of every chunk instead of the outputs.
-//   dstates  (sequence, head, 32 or 16 state columns): dS' of every chunk, in reverse
-//            order; the gradient of the initial state is what is left at the start.
+//   dstates  dS' of every chunk, in reverse order, by the forward's machinery run as
+//            the adjoint scan (kla_chunk.hip, kla_chunk_rev_kernel); the gradient of
+//            the initial state is what is left at the start.
 //   grads    (chunk, head) in parallel: everything else from S, dS' and the chunk's
 //            inputs, streaming the state columns 16 at a time.
 // Sums are fp32 throughout.  The prep kernel's K K^T and Q K^T take the inputs as MFMA
@@ -407,173 +408,6 @@ __global__ __launch_bounds__(kPT) void kla_bwd_prep_kernel(BwdParams p) {
 // them to LDS once per chunk for the next chunk's K S (or K dS) product; chunk-row
 // products (16-row tiles of C) are spread over the waves by (row tile, column tile).
 
-// ============================================================================
-// dstates: dS' of every chunk (reverse order) and the initial-state gradient
-// ============================================================================
-template <int C, int DK, int NS>
-struct DStatesSmem {
-  static constexpr int LS = NS + 4;  // dO, dX and dS slice rows (a multiple of 4 floats, see kLS)
-  static constexpr int LK = DK + 4, LC = C + 4;
-  static constexpr int K = 0, Q = K + C * LK, T = Q + C * LK, P = T + C * LC, O = P + C * LC;
-  static constexpr int U = O + C * LS, S = U + C * LS, BETA = S + DK * LS, GAM = BETA + C;
-  static constexpr int FLOATS = GAM + C;
-};
-
-// NS state columns per workgroup (16 or 32): the chunk's K, Q, T and P go through LDS
-// once per workgroup, so wider slices spend less of each step on them.
-template <typename E, int C, int DK, int NS>
-__global__ __launch_bounds__(kNT) void kla_bwd_dstates_kernel(BwdParams p) {
-  using L = DStatesSmem<C, DK, NS>;
-  using R = PrepRec<E, C>;
-  using MM = Mma16<E>;
-  constexpr int LK = L::LK, LC = L::LC, LS = L::LS, CT = NS / 16;
-  constexpr int NRT = C / 16, NKT = DK / 16;
-  static_assert(NRT <= kNT / 64 && NKT <= kNT / 64 && NS % 16 == 0, "one 16-row tile per wave");
-  __shared__ __attribute__((aligned(16))) float sm[L::FLOATS];
-  float *sK = sm + L::K, *sQ = sm + L::Q, *sT = sm + L::T, *sP = sm + L::P, *sO = sm + L::O;
-  float *sU = sm + L::U, *sS = sm + L::S, *sb = sm + L::BETA, *sgam = sm + L::GAM;
-  const int t = threadIdx.x;
-  const int w = t >> 6, lane = t & 63, lr = lane & 15, lg = lane >> 4;
-  const int nsd = p.DV / NS;
-  // blockIdx % 8 picks the XCD: the column slices of one (sequence, head) go to one XCD so
-  // that they share the chunk's K, T (and Q, P) through its L2; the grid is padded to
-  // whole rounds of 8 groups
-  const int xcd = blockIdx.x & 7, i8 = blockIdx.x >> 3;
-  const int gidx = (i8 / nsd) * 8 + xcd, js = i8 % nsd;
-  if (gidx >= p.nseq * p.H) return;  // padding (uniform per workgroup)
-  const int h = gidx % p.H, n = gidx / p.H;
-  const int col0 = js * NS;
-  const SeqLoc sq = seq_loc(p, n, h, C);
-  const size_t sbase = ((size_t)n * p.H + h) * DK * p.DV;
-  if (p.dsfin) {
-    load_rows<float, DK, NS, LS, kNT>(sS, p.dsfin + sbase, 0, DK, col0, p.DV);
-  } else {
-    for (int e = t; e < DK * NS; e += kNT) sS[(e / NS) * LS + e % NS] = 0.f;
-  }
-  __syncthreads();
-  const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
-  f32x4 dSr[CT];  // dS rows 16w + 4lg + i, column 16 ct + lr (waves w < NKT)
-#pragma unroll
-  for (int ct = 0; ct < CT; ++ct) {
-    dSr[ct] = z4;
-    if (w < NKT) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) dSr[ct][i] = sS[(16 * w + 4 * lg + i) * LS + 16 * ct + lr];
-    }
-  }
-  const int nch = (sq.len + C - 1) / C;
-  // the previous chunk's inputs are loaded while this one is computed
-  TileLoad<E, C, DK, LK, kNT> lk, lq;
-  TileLoad<E, C, NS, LS, kNT> lo;
-  TileLoad<E, C, C, LC, kNT> lt, lp;
-  TileLoad<float, 2, C, C, kNT> lb;  // b then gamma
-  auto issue = [&](int c) {
-    const int rows = min(C, sq.len - c * C);
-    const long long row0 = sq.row0 + (long long)c * C;
-    char *recb = R::at(p.prep, (size_t)h * p.nslot + sq.slot0 + c);
-    lk.issue(p.k, row0, rows, 0, DK);
-    lq.issue(p.q, row0, rows, 0, DK);
-    lo.issue(p.dout, row0, rows, col0, p.DV);
-    lt.issue(R::mat(recb) + R::TM, 0, C, 0, C);
-    lp.issue(R::mat(recb) + R::PM, 0, C, 0, C);
-    lb.issue(R::vec(recb) + R::BETA, 0, 2, 0, C);
-  };
-  if (nch > 0) issue(nch - 1);
-  for (int c = nch - 1; c >= 0; --c) {
-    const size_t slot = (size_t)h * p.nslot + sq.slot0 + c;
-    if (w < NKT) {
-      E *dst = static_cast<E *>(p.dstates) + slot * DK * p.DV;
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          dst[(size_t)(16 * w + 4 * lg + i) * p.DV + col0 + 16 * ct + lr] = Elem<E>::from_f32(dSr[ct][i]);
-    }
-    __syncthreads();
-    lk.put(sK);
-    lq.put(sQ);
-    lo.put(sO);
-    lt.put(sT);
-    lp.put(sP);
-    lb.put(sb);
-    if (c > 0) issue(c - 1);
-    __syncthreads();
-    const float gC = sgam[C - 1];
-    // The row-tile phases: wave w takes row tile w & 3 and column tile w >> 2 (with 16
-    // state columns waves 4-7 have none and wait).
-    const int rtw = w & 3, ctw = w >> 2;
-    const bool tile = rtw < NRT && ctw < CT;  // (uniform per wave)
-    const int ra = 16 * rtw + lr, cc = 16 * ctw + lr;
-    // dU = P^T dO + Diag(d) K dS'  (P lower triangular)
-    if (tile) {
-      f32x4 a = z4, b = z4;
-      for (int k0 = 16 * rtw; k0 < C; k0 += 16)
-        a = MM::run(gat4(sP + (k0 + 4 * lg) * LC + ra, LC), gat4(sO + (k0 + 4 * lg) * LS + cc, LS), a);
-#pragma unroll 4
-      for (int k0 = 0; k0 < DK; k0 += 16)
-        b = MM::run(vec4(sK + ra * LK + k0 + 4 * lg), gat4(sS + (k0 + 4 * lg) * LS + cc, LS), b);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * rtw + 4 * lg + i;
-        sU[r * LS + cc] = fmaf(__expf(gC - sgam[r]), b[i], a[i]);
-      }
-    }
-    __syncthreads();
-    // dX = Diag(b) T^T dU; keep Diag(Gam) dX and Diag(Gam) dO for the state step
-    f32x4 gdx = z4, gdo = z4;
-    if (tile) {
-      f32x4 x = z4;
-      for (int k0 = 16 * rtw; k0 < C; k0 += 16)
-        x = MM::run(gat4(sT + (k0 + 4 * lg) * LC + ra, LC), gat4(sU + (k0 + 4 * lg) * LS + cc, LS), x);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * rtw + 4 * lg + i;
-        const float G = __expf(sgam[r]);
-        gdx[i] = G * sb[r] * x[i];
-        gdo[i] = G * sO[r * LS + cc];
-      }
-    }
-    __syncthreads();
-    if (tile) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * rtw + 4 * lg + i;
-        sU[r * LS + cc] = gdx[i];
-        sO[r * LS + cc] = gdo[i];
-      }
-    }
-    __syncthreads();
-    // dS = Gam_C dS' + (Diag(Gam) Q)^T dO - (Diag(Gam) K)^T dX, state rows of wave w
-    if (w < NKT) {
-      const int ia = 16 * w + lr;
-      const float GC = __expf(gC);
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct) dSr[ct] = GC * dSr[ct];
-#pragma unroll
-      for (int k0 = 0; k0 < C; k0 += 16) {
-        const int r = k0 + 4 * lg;
-        const f32x4 qa = gat4(sQ + r * LK + ia, LK), ka = -gat4(sK + r * LK + ia, LK);
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
-          dSr[ct] = MM::run(qa, gat4(sO + r * LS + 16 * ct + lr, LS), dSr[ct]);
-          dSr[ct] = MM::run(ka, gat4(sU + r * LS + 16 * ct + lr, LS), dSr[ct]);
-        }
-      }
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sS[(16 * w + 4 * lg + i) * LS + 16 * ct + lr] = dSr[ct][i];
-    }
-  }
-  if (p.ds0 && w < NKT) {
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        p.ds0[sbase + (size_t)(16 * w + 4 * lg + i) * p.DV + col0 + 16 * ct + lr] = dSr[ct][i];
-  }
-}
-
 // One 16-column slice of a chunk-start state stored in the forward scan's
 // operand groups (kla_chunk.hip, ChunkParams::states): for each group q of KG
 // state rows, 64 lanes x 16 bytes, lane l holding column l & 15 of the slice and
@@ -707,13 +541,12 @@ __global__ __launch_bounds__(kGT) void kla_bwd_grads_kernel(BwdParams p) {
   float gcp = 0.f;  // partial <S, dS'>
 
   // slice js + 1 of S, dS', V and dO is loaded while slice js is computed
-  GroupLoad<E, DK> ls;
-  TileLoad<E, DK, kNS, kLS, kGT> ld_;
+  GroupLoad<E, DK> ls, ld_;
   TileLoad<E, C, kNS, kLS, kGT> lv, lo;
   auto issue = [&](int js) {
     const int col0 = js * kNS;
     ls.issue(Sg, js);
-    ld_.issue(Dg, 0, DK, col0, p.DV);
+    ld_.issue(Dg, js);
     lv.issue(p.v, cl.row0, rows, col0, p.DV);
     lo.issue(p.dout, cl.row0, rows, col0, p.DV);
   };
@@ -1067,7 +900,6 @@ size_t bwd_workspace_bytes_t(const ChunkArgs &a) {
 template <typename E, int C, int DK>
 hipError_t launch_bwd_t(const ChunkArgs &a, const ChunkBwdArgs &b, hipStream_t st) {
   static_assert(PrepSmem<E, C, DK>::BYTES <= 64 * 1024, "prep LDS (kept small: several workgroups per CU)");
-  static_assert(DStatesSmem<C, DK, 32>::FLOATS * 4 <= 160 * 1024, "dstates LDS");
   static_assert(GradSmem<C, DK>::FLOATS * 4 <= 160 * 1024, "grads LDS");
   BwdParams p;
   p.q = a.q;
@@ -1119,13 +951,13 @@ hipError_t launch_bwd_t(const ChunkArgs &a, const ChunkBwdArgs &b, hipStream_t s
     if (e != hipSuccess) return e;
   }
   if (seq_blocks > 0 && (tokens || p.ds0)) {
-    // with no tokens this only copies dS_final (or zeros) to the initial-state gradient;
-    // 32 state columns per workgroup where dv allows
-    if (ns32)
-      hipLaunchKernelGGL((kla_bwd_dstates_kernel<E, C, DK, 32>), dim3(scan_blocks), dim3(kNT), 0, st, p);
-    else
-      hipLaunchKernelGGL((kla_bwd_dstates_kernel<E, C, DK, 16>), dim3(scan_blocks), dim3(kNT), 0, st, p);
-    const hipError_t e = hipGetLastError();
+    // the chunk-end state gradients, in reverse, on the forward's machinery (with no
+    // tokens this only copies dS_final, or zeros, to the initial-state gradient)
+    ChunkArgs fa = a;
+    fa.o = nullptr;
+    fa.final_state = nullptr;
+    fa.workspace = ws + pb + 2 * sb;
+    const hipError_t e = launch_chunk_rev(fa, p.dsfin, p.dout, p.ds0, p.dstates, st);
     if (e != hipSuccess) return e;
   }
   if (tokens) {

@@ -1551,6 +1551,395 @@ __global__ __launch_bounds__(64 * kWaves) void kla_chunk_kernel(ChunkParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// reverse scan kernel: the backward pass's state gradients
+// ---------------------------------------------------------------------------
+// The gradient of a scalar loss with respect to the chunk-end state, dS', runs
+// backwards through the chunks by the adjoint of the chunk step above (T' =
+// T Diag(beta), Gam, d and Gam_C of the chunk; P the decayed causal scores):
+//
+//   Y   = P^T dO + Diag(d) K dS'              (the gradient of U~)
+//   dX  = T'^T Y                              (the gradient of X)
+//   dS  = Gam_C dS' + Q^T Diag(Gam) dO - K^T Diag(Gam) dX
+//
+// and dS becomes the dS' of the previous chunk.  It runs on the forward's own
+// machinery: the same T'^T images and gamma/Gam/d vectors (the forward prep
+// kernel's workspace), the same loaders (dO in place of V, chunks in reverse
+// order), and a chain wave per 16 state columns holding dS' in MFMA
+// accumulators -- K dS' is the forward's K S, K^T and Q^T products its state
+// update, T'^T Y reads the T'^T image by rows where the forward reads it by
+// columns.  The P waves form P (as Q K^T) for the column blocks they own and
+// P^T dO for the matching rows of Y, which only the chunk's inputs determine;
+// they hand it to the chain through LDS in the middle of the step, so a step
+// has two LDS-only barriers: (1) chain: K dS' and Gam_C dS' + Q^T Diag(Gam) dO,
+// P waves: P^T dO; (2) chain: Y, dX and the K^T term.  In ChunkParams:
+// s0 = dL/dS_final (or nullptr), sfin = the initial-state gradient (or
+// nullptr), v = dO, states = where dS' of every chunk goes (the operand-group
+// layout of states mode), ws = the forward workspace.
+template <typename E, int C, int DK, int NCT>
+struct RevShape {
+  using F = ChunkShape<E, C, DK, NCT>;
+  static constexpr int NB = F::NB, DVT = F::DVT, NCW = F::NCW, NT = F::NT;
+  static constexpr int LDK = F::LDK, LDC = F::LDC, LDV = F::LDV;
+  static constexpr int K_SLOT = F::K_SLOT, V_SLOT = F::V_SLOT, TP_SLOT = F::TP_SLOT;
+  static constexpr int YP = NCT * NB * 64 * 16;  // P^T dO tiles, fp32 accumulator layout
+  static constexpr int OFF_K = 0;
+  static constexpr int OFF_V = OFF_K + 2 * K_SLOT;
+  static constexpr int OFF_TP = OFF_V + 2 * V_SLOT;
+  static constexpr int OFF_YP = OFF_TP + 2 * TP_SLOT;
+  static constexpr int OFF_Q = OFF_YP + YP;
+  static constexpr int BYTES = OFF_Q + 2 * K_SLOT;
+  static_assert(BYTES <= 160 * 1024, "LDS budget");
+};
+
+template <typename E, int C, int DK, int NCT>
+__global__ __launch_bounds__(64 * kWaves) void kla_chunk_rev_kernel(ChunkParams p) {
+  using Sh = RevShape<E, C, DK, NCT>;
+  using TL = TpLayout<E, C>;
+  using O = Ops<E>;
+  using Grp = typename O::Grp;
+  constexpr int NB = Sh::NB, DVT = Sh::DVT, LDK = Sh::LDK, LDC = Sh::LDC, LDV = Sh::LDV;
+  constexpr int KG = O::KG, TPG = KG / 16;
+  constexpr int NQG = DK / KG;  // contraction groups over dk
+  constexpr int NCG = C / KG;   // contraction groups over the chunk
+
+  __shared__ __attribute__((aligned(16))) char smem[Sh::BYTES];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int li = lane & 15;
+  const int lg = lane >> 4;
+
+  // ---- which (sequence, head, column slice): as the forward scan -------------
+  const int xcd = blockIdx.x & 7, i8 = blockIdx.x >> 3;
+  const int gidx = (i8 / p.n_tiles) * 8 + xcd;
+  if (gidx >= p.ngroups) return;  // padding (uniform per workgroup)
+  const int jt = i8 % p.n_tiles;
+  const int h = gidx % p.H;
+  const int n = p.order ? p.order[gidx / p.H] : gidx / p.H;
+  const int nh = n * p.H + h;
+  int b = n, t0 = 0, t1 = p.T, slot0;
+  if (p.cu) {
+    b = 0;
+    t0 = min(max(p.cu[n], 0), p.T);
+    t1 = min(max(p.cu[n + 1], t0), p.T);
+    slot0 = n + t0 / C;
+  } else {
+    slot0 = n * ((p.T + C - 1) / C);
+  }
+  const int len = t1 - t0;
+  const int nch = (len + C - 1) / C;
+  const size_t row0 = ((size_t)b * p.H + h) * (size_t)p.T + (size_t)t0;
+  const E *gq = static_cast<const E *>(p.q);
+  const E *gk = static_cast<const E *>(p.k);
+  const E *gdo = static_cast<const E *>(p.v);
+  const char *ws = p.ws + (size_t)h * p.nslot * TL::BYTES;
+  const int dv = p.dv;
+  // step i handles chunk nch - 1 - i
+  auto chunk_of = [&](int i) { return min(max(nch - 1 - i, 0), nch - 1); };
+  auto nrow_of = [&](int c) { return min(C, len - c * C); };
+  auto tok0_of = [&](int c) { return row0 + (size_t)c * C; };
+  const int iend = nch + (nch & 1);
+
+  if (nch == 0) {
+    // no tokens: the initial-state gradient is dL/dS_final
+    if (p.sfin) {
+      const size_t sbase = (size_t)nh * DK * (size_t)dv;
+      for (int e = threadIdx.x; e < DK * DVT; e += Sh::NT) {
+        const size_t off = sbase + (size_t)(e / DVT) * dv + (size_t)jt * DVT + (e % DVT);
+        p.sfin[off] = p.s0 ? p.s0[off] : 0.f;
+      }
+    }
+    return;
+  }
+
+  auto sK = [&](int i) { return reinterpret_cast<E *>(smem + Sh::OFF_K + (i & 1) * Sh::K_SLOT); };
+  auto sQ = [&](int i) { return reinterpret_cast<E *>(smem + Sh::OFF_Q + (i & 1) * Sh::K_SLOT); };
+  auto sV = [&](int i) { return reinterpret_cast<E *>(smem + Sh::OFF_V + (i & 1) * Sh::V_SLOT); };
+  auto sTp = [&](int i) { return reinterpret_cast<E *>(smem + Sh::OFF_TP + (i & 1) * Sh::TP_SLOT); };
+  auto sVec = [&](int i) {
+    return reinterpret_cast<float *>(smem + Sh::OFF_TP + (i & 1) * Sh::TP_SLOT + TL::TP_IMG);
+  };
+  f32x4 *sYp = reinterpret_cast<f32x4 *>(smem + Sh::OFF_YP);
+
+  if (wave == CHAIN0 || wave == CHAIN1) {
+    auto chain = [&](auto ct0_c) {
+      constexpr int CT0 = decltype(ct0_c)::value;
+      constexpr int NCW = CT0 < NCT ? (NCT - CT0 < Sh::NCW ? NCT - CT0 : Sh::NCW) : 0;
+      constexpr int NCW1 = NCW > 0 ? NCW : 1;
+      f32x4 accS[NCW1][DK / 16];  // dS'
+      const size_t sbase = (size_t)nh * DK * (size_t)dv;
+#pragma unroll
+      for (int ct = 0; ct < NCW; ++ct) {
+        const int col = jt * DVT + 16 * (CT0 + ct) + li;
+#pragma unroll
+        for (int it = 0; it < DK / 16; ++it)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            accS[ct][it][j] = p.s0 ? p.s0[sbase + (size_t)(16 * it + 4 * lg + j) * dv + col] : 0.f;
+      }
+      Grp sb[NCW1][NQG];
+      // dS' of chunk c as operand groups, also to the output
+      auto publish = [&](int c) {
+        const size_t slot = (size_t)h * p.nslot + slot0 + c;
+#pragma unroll
+        for (int ct = 0; ct < NCW; ++ct)
+#pragma unroll
+          for (int q = 0; q < NQG; ++q) {
+            sb[ct][q] = O::b_from_d(&accS[ct][q * TPG]);
+            const size_t grp = (slot * (size_t)(dv / 16) + (size_t)(jt * NCT + CT0 + ct)) * NQG + q;
+            reinterpret_cast<Grp *>(p.states + grp * 64 * 16)[lane] = sb[ct][q];
+          }
+      };
+      f32x4 x[NCW1][NB];
+      __syncthreads();
+      for (int i = -1; i <= iend; ++i) {
+        const bool live = NCW > 0 && i >= 0 && i < nch;
+        const int c = chunk_of(i);
+        if (NCW > 0 && i == -1) publish(nch - 1);
+        // ---- phase 1: K dS' and Gam_C dS' + Q^T Diag(Gam) dO ----
+        if (live) {
+          const E *K = sK(i);
+          const E *Q = sQ(i);
+          const E *V = sV(i);
+          const float *vec = sVec(i);
+#pragma unroll
+          for (int rt = 0; rt < NB; ++rt) {
+#pragma unroll
+            for (int ct = 0; ct < NCW; ++ct) x[ct][rt] = zero4();
+#pragma unroll
+            for (int q = 0; q < NQG; ++q) {
+              const Grp a = O::a_row(K + (16 * rt + li) * LDK, q * KG, lg);
+#pragma unroll
+              for (int ct = 0; ct < NCW; ++ct) x[ct][rt] = O::mma_grp(a, sb[ct][q], x[ct][rt]);
+            }
+          }
+          // Diag(Gam) dO as B groups
+          Grp gob[NCW1][NCG];
+#pragma unroll
+          for (int ct = 0; ct < NCW; ++ct)
+#pragma unroll
+            for (int q = 0; q < NCG; ++q) {
+              f32x4 t[TPG];
+#pragma unroll
+              for (int tt = 0; tt < TPG; ++tt) {
+                const int r16 = 16 * (q * TPG + tt);
+                t[tt] = *reinterpret_cast<const f32x4 *>(vec + C + r16 + 4 * lg) * O::col4(V, LDV, r16, 16 * (CT0 + ct), lane);
+              }
+              gob[ct][q] = O::b_from_d(t);
+            }
+          const float gC = vec[C + C - 1];
+#pragma unroll
+          for (int it = 0; it < DK / 16; ++it) {
+#pragma unroll
+            for (int ct = 0; ct < NCW; ++ct) accS[ct][it] = gC * accS[ct][it];
+#pragma unroll
+            for (int q = 0; q < NCG; ++q) {
+              const Grp a = O::a_trans(Q, LDK, q * KG, 16 * it, lane);
+#pragma unroll
+              for (int ct = 0; ct < NCW; ++ct) accS[ct][it] = O::mma_grp(a, gob[ct][q], accS[ct][it]);
+            }
+          }
+        }
+        lds_barrier();
+        // ---- phase 2: Y, dX = T'^T Y, and - K^T Diag(Gam) dX ----
+        if (live) {
+          const E *K = sK(i);
+          const E *TpT = sTp(i);
+          const float *vec = sVec(i);
+          Grp yb[NCW1][NCG];
+#pragma unroll
+          for (int ct = 0; ct < NCW; ++ct) {
+            f32x4 y[NB];
+#pragma unroll
+            for (int rt = 0; rt < NB; ++rt) {
+              const f32x4 d4 = *reinterpret_cast<const f32x4 *>(vec + 2 * C + 16 * rt + 4 * lg);
+              y[rt] = sYp[((CT0 + ct) * NB + rt) * 64 + lane] + d4 * x[ct][rt];
+            }
+#pragma unroll
+            for (int q = 0; q < NCG; ++q) yb[ct][q] = O::b_from_d(&y[q * TPG]);
+          }
+          // dX: row block rt of T'^T is zero left of column block rt (T' lower triangular)
+          Grp gxb[NCW1][NCG];
+          f32x4 u[NCW1][NB];
+#pragma unroll
+          for (int rt = 0; rt < NB; ++rt) {
+#pragma unroll
+            for (int ct = 0; ct < NCW; ++ct) u[ct][rt] = zero4();
+#pragma unroll
+            for (int q = rt / TPG; q < NCG; ++q) {
+              const Grp a = O::a_row(TpT + (16 * rt + li) * LDC, q * KG, lg);
+#pragma unroll
+              for (int ct = 0; ct < NCW; ++ct) u[ct][rt] = O::mma_grp(a, yb[ct][q], u[ct][rt]);
+            }
+          }
+#pragma unroll
+          for (int ct = 0; ct < NCW; ++ct)
+#pragma unroll
+            for (int q = 0; q < NCG; ++q) {
+              f32x4 t[TPG];
+#pragma unroll
+              for (int tt = 0; tt < TPG; ++tt) {
+                const int r16 = 16 * (q * TPG + tt);
+                t[tt] = -(*reinterpret_cast<const f32x4 *>(vec + C + r16 + 4 * lg)) * u[ct][q * TPG + tt];
+              }
+              gxb[ct][q] = O::b_from_d(t);
+            }
+#pragma unroll
+          for (int it = 0; it < DK / 16; ++it)
+#pragma unroll
+            for (int q = 0; q < NCG; ++q) {
+              const Grp a = O::a_trans(K, LDK, q * KG, 16 * it, lane);
+#pragma unroll
+              for (int ct = 0; ct < NCW; ++ct) accS[ct][it] = O::mma_grp(a, gxb[ct][q], accS[ct][it]);
+            }
+          if (c > 0) publish(c - 1);
+        }
+        lds_barrier();
+      }
+      if (p.sfin) {
+#pragma unroll
+        for (int ct = 0; ct < NCW; ++ct) {
+          const int col = jt * DVT + 16 * (CT0 + ct) + li;
+#pragma unroll
+          for (int it = 0; it < DK / 16; ++it)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) p.sfin[sbase + (size_t)(16 * it + 4 * lg + j) * dv + col] = accS[ct][it][j];
+        }
+      }
+    };
+    if (wave == CHAIN0)
+      chain(std::integral_constant<int, 0>{});
+    else
+      chain(std::integral_constant<int, Sh::NCW>{});
+  } else if (wave == PW0 || wave == PW1) {
+    // ---- P waves: P^T dO for the rows of Y whose column block they own ----
+    auto pwave = [&](auto part_c) {
+      constexpr int part = decltype(part_c)::value;
+      using BL = OwnBlocks<NB, part>;
+      constexpr int NOWN = BL::N;
+      __syncthreads();
+      for (int i = -1; i <= iend; ++i) {
+        if (NOWN > 0 && i >= 0 && i < nch) {
+          const E *Q = sQ(i);
+          const E *K = sK(i);
+          const E *V = sV(i);
+          const float *vec = sVec(i);
+          // dO of the slice as B groups (contraction over the chunk rows)
+          Grp ob[NCT][NCG];
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+            for (int q = 0; q < NCG; ++q) {
+              f32x4 t[TPG];
+#pragma unroll
+              for (int tt = 0; tt < TPG; ++tt) t[tt] = O::col4(V, LDV, 16 * (q * TPG + tt), 16 * ct, lane);
+              ob[ct][q] = O::b_from_d(t);
+            }
+#pragma unroll
+          for (int k = 0; k < NOWN; ++k) {
+            const int st = BL::at(k);
+            Grp kb[NQG];
+#pragma unroll
+            for (int q = 0; q < NQG; ++q) kb[q] = O::a_row(K + (16 * st + li) * LDK, q * KG, lg);
+            const float gs = vec[16 * st + li];
+            // P tiles (rt, st), rt >= st: D[r][s] = q_r . k_s exp(gamma_r - gamma_s), r >= s
+            f32x4 pt[NB];
+#pragma unroll
+            for (int rt = 0; rt < NB; ++rt) {
+              pt[rt] = zero4();
+              if (rt < st) continue;
+#pragma unroll
+              for (int q = 0; q < NQG; ++q) pt[rt] = O::mma_grp(O::a_row(Q + (16 * rt + li) * LDK, q * KG, lg), kb[q], pt[rt]);
+              const f32x4 gr = *reinterpret_cast<const f32x4 *>(vec + 16 * rt + 4 * lg);
+#pragma unroll
+              for (int j = 0; j < 4; ++j)
+                pt[rt][j] = (rt > st || 4 * lg + j >= li) ? pt[rt][j] * __expf(gr[j] - gs) : 0.f;
+            }
+            // the D layout of P is the left-operand layout of P^T: rows s of Y
+            Grp pa[NCG];
+#pragma unroll
+            for (int q = 0; q < NCG; ++q) pa[q] = O::b_from_d(&pt[q * TPG]);
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+              f32x4 y = zero4();
+#pragma unroll
+              for (int q = st / TPG; q < NCG; ++q) y = O::mma_grp(pa[q], ob[ct][q], y);
+              sYp[(ct * NB + st) * 64 + lane] = y;
+            }
+          }
+        }
+        lds_barrier();
+        lds_barrier();
+      }
+    };
+    if (wave == PW0)
+      pwave(std::integral_constant<int, 0>{});
+    else
+      pwave(std::integral_constant<int, 1>{});
+  } else if (wave == LOADK) {
+    // ---- K rows of the next step's chunk (two register sets, two steps ahead) ----
+    RowLoad<E, DK, AllBlocks<NB>> kin[2];
+    kin[0].issue(gk + tok0_of(chunk_of(0)) * DK, nrow_of(chunk_of(0)), lane);
+    kin[1].issue(gk + tok0_of(chunk_of(1)) * DK, nrow_of(chunk_of(1)), lane);
+    __syncthreads();
+    auto step = [&](int i, auto set_c) {
+      constexpr int S = decltype(set_c)::value;
+      kin[S].put(sK(i + 1), LDK, lane, [](int, int row) { return row; });
+      kin[S].issue(gk + tok0_of(chunk_of(i + 3)) * DK, nrow_of(chunk_of(i + 3)), lane);
+      lds_barrier();
+      lds_barrier();
+    };
+    for (int i = -1; i <= iend; i += 2) {
+      step(i, std::integral_constant<int, 0>{});
+      step(i + 1, std::integral_constant<int, 1>{});
+    }
+  } else if (wave == LOADQ) {
+    RowLoad<E, DK, AllBlocks<NB>> qin[2];
+    qin[0].issue(gq + tok0_of(chunk_of(0)) * DK, nrow_of(chunk_of(0)), lane);
+    qin[1].issue(gq + tok0_of(chunk_of(1)) * DK, nrow_of(chunk_of(1)), lane);
+    __syncthreads();
+    auto step = [&](int i, auto set_c) {
+      constexpr int S = decltype(set_c)::value;
+      qin[S].put(sQ(i + 1), LDK, lane, [](int, int row) { return row; });
+      qin[S].issue(gq + tok0_of(chunk_of(i + 3)) * DK, nrow_of(chunk_of(i + 3)), lane);
+      lds_barrier();
+      lds_barrier();
+    };
+    for (int i = -1; i <= iend; i += 2) {
+      step(i, std::integral_constant<int, 0>{});
+      step(i + 1, std::integral_constant<int, 1>{});
+    }
+  } else {
+    // ---- T'^T, gamma/Gam/d and the dO slice of the next step's chunk ----
+    using TC = ImgCopy<E, C>;
+    constexpr int NSET = TC::NPL <= 20 ? 2 : 1;
+    TC tin[NSET];
+    VSliceLoad<E, C, DVT> vin[NSET];
+    auto fetch = [&](int i, auto set_c) {
+      constexpr int S = decltype(set_c)::value;
+      const int c = chunk_of(i);
+      tin[S].issue(ws + (size_t)(slot0 + c) * TL::BYTES, lane);
+      vin[S].issue(gdo + tok0_of(c) * dv, nrow_of(c), dv, jt * DVT, lane);
+    };
+    fetch(0, std::integral_constant<int, 0>{});
+    if constexpr (NSET == 2) fetch(1, std::integral_constant<int, NSET - 1>{});
+    __syncthreads();
+    auto step = [&](int i, auto set_c) {
+      constexpr int S = decltype(set_c)::value;
+      tin[S].put(sTp(i + 1), lane);
+      vin[S].put(sV(i + 1), LDV, lane);
+      fetch(i + 1 + NSET, set_c);
+      lds_barrier();
+      lds_barrier();
+    };
+    for (int i = -1; i <= iend; i += 2) {
+      step(i, std::integral_constant<int, 0>{});
+      step(i + 1, std::integral_constant<int, NSET - 1>{});
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // host-side dispatch
 // ---------------------------------------------------------------------------
 // Packed sequences, longest first: order[rank] = n, rank = the number of
@@ -1711,6 +2100,70 @@ hipError_t launch_chunk_fwd(const ChunkArgs &a, hipStream_t st) {
     return launch_chunk_general(a, none, st);
   }
   return launch_fast(a, st, nullptr);
+}
+
+template <typename E, int C, int DK, int NCT>
+static hipError_t launch_rev_t(const ChunkArgs &a, const float *dsfin, const void *dout, float *ds0, void *dstates,
+                               hipStream_t st) {
+  using Sh = RevShape<E, C, DK, NCT>;
+  ChunkParams p{};
+  p.q = a.q;
+  p.k = a.k;
+  p.v = dout;
+  p.g = a.g;
+  p.eta = a.eta;
+  p.eps = a.eps;
+  p.s0 = dsfin;
+  p.o = nullptr;
+  p.sfin = ds0;
+  p.cu = a.cu_seqlens;
+  p.ws = static_cast<char *>(a.workspace);
+  p.H = a.H;
+  p.T = a.T;
+  p.dv = a.dv;
+  p.n_tiles = a.dv / Sh::DVT;
+  p.nseq = a.num_seqs;
+  p.beta_direct = a.beta_direct;
+  p.nslot = slots_per_head(a.cu_seqlens != nullptr, a.B, a.T, a.num_seqs, C);
+  p.ngroups = a.num_seqs * a.H;
+  p.states = static_cast<char *>(dstates);
+  p.order = nullptr;
+  if (p.ngroups == 0) return hipSuccess;
+  // the packed-sequence order the states pass wrote into the same workspace
+  if (a.cu_seqlens && a.num_seqs > 1 && a.num_seqs <= kMaxOrdered && (long long)a.B * a.T > 0)
+    p.order = reinterpret_cast<const int *>(static_cast<char *>(a.workspace) + order_offset_t<E, C>(a));
+  const long long nblk = ((long long)p.ngroups + 7) / 8 * 8 * p.n_tiles;
+  hipLaunchKernelGGL((kla_chunk_rev_kernel<E, C, DK, NCT>), dim3((unsigned)nblk), dim3(Sh::NT), 0, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_chunk_rev(const ChunkArgs &a, const float *dsfin, const void *dout, float *ds0, void *dstates,
+                            hipStream_t st) {
+  if (!fast_chunk_supported(a.dtype, a.dk, a.dv, a.chunk)) return hipErrorInvalidValue;
+  if (a.dtype == 0) {
+    const bool two = use_two_column_tiles(a);
+    if (a.dk == 128)
+      return two ? launch_rev_t<bf16, 64, 128, 2>(a, dsfin, dout, ds0, dstates, st)
+                 : launch_rev_t<bf16, 64, 128, 1>(a, dsfin, dout, ds0, dstates, st);
+    if (a.dk == 64)
+      return two ? launch_rev_t<bf16, 64, 64, 2>(a, dsfin, dout, ds0, dstates, st)
+                 : launch_rev_t<bf16, 64, 64, 1>(a, dsfin, dout, ds0, dstates, st);
+    return hipErrorInvalidValue;
+  }
+  if (a.chunk == 16) {
+    switch (a.dk) {
+      case 16: return launch_rev_t<float, 16, 16, 1>(a, dsfin, dout, ds0, dstates, st);
+      case 32: return launch_rev_t<float, 16, 32, 1>(a, dsfin, dout, ds0, dstates, st);
+      case 64: return launch_rev_t<float, 16, 64, 1>(a, dsfin, dout, ds0, dstates, st);
+      case 128: return launch_rev_t<float, 16, 128, 1>(a, dsfin, dout, ds0, dstates, st);
+    }
+  } else if (a.chunk == 64) {
+    switch (a.dk) {
+      case 16: return launch_rev_t<float, 64, 16, 1>(a, dsfin, dout, ds0, dstates, st);
+      case 32: return launch_rev_t<float, 64, 32, 1>(a, dsfin, dout, ds0, dstates, st);
+    }
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_chunk_states(const ChunkArgs &a, void *states, hipStream_t st) {

@@ -81,6 +81,12 @@ hipError_t launch_chunk_general(const ChunkArgs &a, const GenExtra &x, hipStream
 // kla_chunk.hip; dk * dv elements of the element type per (head, slot)), no
 // outputs.  a.workspace is the forward workspace (chunk_workspace_bytes(a)).
 hipError_t launch_chunk_states(const ChunkArgs &a, void *states, hipStream_t stream);
+// The reverse scan of the state gradients on the same machinery, after
+// launch_chunk_states on the same workspace: dS' of every chunk into dstates
+// (the same layout as states), dL/dS_final from dsfin (or zeros), the
+// initial-state gradient into ds0 (or not written).
+hipError_t launch_chunk_rev(const ChunkArgs &a, const float *dsfin, const void *dout, float *ds0, void *dstates,
+                            hipStream_t stream);
 // a.eta holds the coefficient (beta when a.beta_direct, else eta); acc [N, H, dk] in place
 hipError_t launch_pgdn_decode(const DecodeArgs &a, float band_c, float *acc, hipStream_t stream);
 
