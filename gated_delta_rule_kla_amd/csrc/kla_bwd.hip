@@ -35,6 +35,7 @@
 
 #include "kla_common.h"
 #include "kla_internal.h"
+#include "kla_ops.h"
 
 namespace kla {
 
@@ -58,6 +59,7 @@ struct BwdParams {
   const int32_t *cu;
   float *prep;
   void *states, *dstates;  // chunk-start states and chunk-end state gradients, input element type
+  const char *fws;         // the forward workspace: T'^T images and gamma, Gam, d per (head, slot)
   int B, H, T, DV, nseq, nslot, nsl;
   int beta_direct;
 };
@@ -870,6 +872,548 @@ __global__ __launch_bounds__(kGT) void kla_bwd_grads_kernel(BwdParams p) {
 }
 
 // ============================================================================
+// grads, bf16: the same gradients on the chunk kernels' operand machinery
+// ============================================================================
+// One workgroup of eight waves per (chunk, head), as the kernel above, but the
+// per-column work runs over blocks of 64 state columns (two for dv = 128, not
+// eight slices of 16), every product is a 16x16x32 bf16 MFMA whose operands
+// come straight from bf16 LDS rows in the grouped column order of kla_ops.h
+// (row reads for contractions along a row, transposing reads for contractions
+// down a column), and T'^T with gamma, Gam, d is the forward prep kernel's
+// image of the chunk (the forward workspace), so T' X and T'^T dU read it as
+// the forward and the adjoint scans do.  Waves w and w + 4 share row tile
+// w & 3 (16 chunk rows); in the per-block phases each takes two of the block's
+// four 16-column tiles, in the outer products the same dW / dP and dQ, dK
+// tiles as above, so the C x C stage and the output are the code above.
+//
+// The state blocks are kept transposed (S^T, dS'^T: a row per state column,
+// grouped over dk), where a 16-byte piece of the operand-group layout the
+// states kernels write is one group of a row, so it is stored whole.
+// Per block of columns J (S, dS' the chunk-start state and chunk-end state
+// gradient restricted to J; V, dO likewise):
+//   (A) K S, Q S, K dS'; X = V - Diag(Gam) K S; dU = P^T dO + Diag(d) K dS'
+//   (B) U = T' X; dX = T'^T dU (= dV); row sums for dgamma and dd
+//   (D) dW += dU X^T, dP += dO U^T, dQ += dO S^T, dK += -Diag(Gam) dX S^T + Diag(d) U dS'^T
+template <int DK>
+struct Grad2Smem {
+  static constexpr int C = 64, JB = 64;
+  using TL = TpLayout<bf16, 64>;
+  static constexpr int PAD = LdsPad<bf16>::V;
+  static constexpr int LDK = DK + PAD;   // K, Q rows
+  static constexpr int LDC = TL::LDC;    // T'^T image and P rows
+  static constexpr int LDJ = JB + PAD;   // rows of the block arrays
+  static constexpr int K = 0;
+  static constexpr int Q = K + C * LDK * 2;
+  static constexpr int TP = Q + C * LDK * 2;         // T'^T image, then gamma, Gam, d (fp32)
+  static constexpr int P = TP + TL::LDS_BYTES;
+  static constexpr int S = P + C * LDC * 2;         // S^T of the block: JB rows of DK
+  static constexpr int DS = S + JB * LDK * 2;        // dS'^T likewise
+  static constexpr int VX = DS + JB * LDK * 2;       // V, then X
+  static constexpr int DO = VX + C * LDJ * 2;
+  static constexpr int U = DO + C * LDJ * 2;
+  static constexpr int UD = U + C * LDJ * 2;         // Diag(d) U
+  static constexpr int DU = UD + C * LDJ * 2;
+  static constexpr int GX = DU + C * LDJ * 2;        // -Diag(Gam) dX
+  static constexpr int BLK_END = GX + C * LDJ * 2;
+  // the C x C stage reuses the bytes from 0: K, Q (fp32, natural), T, P (fp32), dW, dP
+  static constexpr int LK = DK + 4, LC = C + 4;
+  static constexpr int FK = 0, FQ = FK + C * LK * 4, FT = FQ + C * LK * 4, FP = FT + C * LC * 4;
+  static constexpr int FB1 = FP + C * LC * 4, FB2 = FB1 + C * LC * 4, F_END = FB2 + C * LC * 4;
+  static constexpr int VEC = (BLK_END > F_END ? BLK_END : F_END);   // fp32 vectors, kept throughout
+  static constexpr int BETA = 0, GAM = BETA + C, NRM = GAM + C, ETA = NRM + C, DGAM = ETA + C, DD = DGAM + 2 * C;
+  static constexpr int DB1 = DD + 2 * C, DB2 = DB1 + C, DB3 = DB2 + C, DGE = DB3 + C, CF = DGE + C, GM = CF + C;
+  static constexpr int DEC = GM + C, RED = DEC + C, NVEC = RED + kGT / 64;
+  static constexpr int BYTES = VEC + NVEC * 4;
+  static_assert(BYTES <= 160 * 1024, "LDS budget");
+  static_assert(TP % 16 == 0 && P % 16 == 0 && S % 16 == 0 && VX % 16 == 0 && GX % 16 == 0 && VEC % 16 == 0, "align");
+};
+
+template <int DK>
+__global__ __launch_bounds__(kGT) void kla_bwd_grads2_kernel(BwdParams p) {
+  using L = Grad2Smem<DK>;
+  using R = PrepRec<bf16, 64>;
+  using O = Ops<bf16>;
+  using Grp = O::Grp;
+  using TLy = TpLayout<bf16, 64>;
+  using MM = Mma16<bf16>;
+  constexpr int C = 64, NRT = 4, NKT = DK / 16, NKH = (NKT + 1) / 2, NQG = DK / 32, JB = L::JB;
+  constexpr int LDK = L::LDK, LDC = L::LDC, LDJ = L::LDJ, LK = L::LK, LC = L::LC;
+  __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
+  bf16 *bK = reinterpret_cast<bf16 *>(smem + L::K), *bQ = reinterpret_cast<bf16 *>(smem + L::Q);
+  bf16 *bTp = reinterpret_cast<bf16 *>(smem + L::TP), *bP = reinterpret_cast<bf16 *>(smem + L::P);
+  const float *fvec = reinterpret_cast<const float *>(smem + L::TP + TLy::TP_IMG);  // gamma, Gam, d
+  bf16 *bS = reinterpret_cast<bf16 *>(smem + L::S), *bD = reinterpret_cast<bf16 *>(smem + L::DS);
+  bf16 *bVX = reinterpret_cast<bf16 *>(smem + L::VX), *bO = reinterpret_cast<bf16 *>(smem + L::DO);
+  bf16 *bU = reinterpret_cast<bf16 *>(smem + L::U), *bUD = reinterpret_cast<bf16 *>(smem + L::UD);
+  bf16 *bDU = reinterpret_cast<bf16 *>(smem + L::DU), *bGX = reinterpret_cast<bf16 *>(smem + L::GX);
+  float *vec = reinterpret_cast<float *>(smem + L::VEC);
+  float *sb = vec + L::BETA, *sgam = vec + L::GAM, *snrm = vec + L::NRM, *seta = vec + L::ETA;
+  float *sdgam2 = vec + L::DGAM, *sdd2 = vec + L::DD;  // per half of the column tiles
+  float *sdb1 = vec + L::DB1, *sdb2 = vec + L::DB2, *sdb3 = vec + L::DB3, *sdge = vec + L::DGE, *scf = vec + L::CF;
+  float *sGm = vec + L::GM, *sdec = vec + L::DEC, *sred = vec + L::RED;
+
+  const int slot = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
+  const ChunkLoc cl = chunk_loc(p, slot, h, C);
+  if (cl.rows == 0) return;  // uniform
+  const int rows = cl.rows;
+  const int w = t >> 6, lane = t & 63, lr = lane & 15, lg = lane >> 4;
+  const int a = w & 3, half = w >> 2;
+  const bool own = true, lead = half == 0;
+  const int ra = 16 * a + lr;
+  const size_t sidx = (size_t)h * p.nslot + slot;
+  char *recb = R::at(p.prep, sidx);
+  const bf16 *rm = R::mat(recb);
+  const float *rv = R::vec(recb);
+  const bf16 *Sg = static_cast<const bf16 *>(p.states) + sidx * DK * p.DV;
+  const bf16 *Dg = static_cast<const bf16 *>(p.dstates) + sidx * DK * p.DV;
+  const int ntile = p.DV / 16;                 // 16-column tiles of the state
+  const int nblk = (ntile + 3) / 4;
+
+  // ---- the chunk's K, Q rows, P and T'^T image (grouped columns), vectors -----
+  if (w < 2) {
+    RowLoad<bf16, DK, AllBlocks<4>> rl;
+    rl.issue(static_cast<const bf16 *>(w == 0 ? p.k : p.q) + cl.row0 * DK, rows, lane);
+    rl.put(w == 0 ? bK : bQ, LDK, lane, [](int, int row) { return row; });
+  } else if (w == 2) {
+    ImgCopy<bf16, 64> ic;
+    ic.issue(p.fws + sidx * TLy::BYTES, lane);
+    ic.put(bTp, lane);
+  } else {
+    // P: C rows of C natural columns, 16-byte pieces into grouped rows (waves 3..7)
+    for (int pc = t - 192; pc < C * C / 8; pc += kGT - 192) {
+      const uint4 v = *reinterpret_cast<const uint4 *>(rm + R::PM + 8 * pc);
+      O::st_piece(bP + (pc / 8) * LDC, pc % 8, v);
+    }
+  }
+  for (int r = t; r < C; r += kGT) {
+    sb[r] = rv[R::BETA + r];
+    sgam[r] = rv[R::GAM + r];
+    snrm[r] = rv[R::NRM + r];
+    seta[r] = r < rows ? ld<bf16>(p.eta, cl.row0 + r) : 0.f;
+    sdgam2[r] = sdgam2[C + r] = 0.f;
+    sdd2[r] = sdd2[C + r] = 0.f;
+  }
+  const float gC = rv[R::GAM + C - 1];
+  for (int r = t; r < C; r += kGT) {
+    const float gr = rv[R::GAM + r];
+    sGm[r] = __expf(gr);
+    sdec[r] = __expf(gC - gr);
+  }
+
+  const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+  f32x4 accWP[NRT], accQ[NKH], accK[NKH];  // accWP: dW (half 0) or dP (half 1)
+#pragma unroll
+  for (int b = 0; b < NRT; ++b) accWP[b] = z4;
+#pragma unroll
+  for (int i = 0; i < NKH; ++i) accQ[i] = accK[i] = z4;
+  float gcp = 0.f;  // partial <S, dS'>
+
+  // ---- block loads: S, dS' pieces (operand groups), V and dO rows ----------
+  // S, dS' of a block: tiles 4 blk .. (up to 4), groups q of 32 rows, 64 lanes of 16 bytes
+  constexpr int SPIECES = 4 * NQG * 64;           // pieces of a full block
+  constexpr int SPER = (SPIECES + kGT - 1) / kGT;
+  uint4 sv[SPER], dv[SPER], vv, ov;
+  auto issue = [&](int blk) {
+    const int nt = min(4, ntile - 4 * blk);
+#pragma unroll
+    for (int m = 0; m < SPER; ++m) {
+      const int pc = t + m * kGT;
+      const int ct = pc / (NQG * 64);
+      if (ct < nt) {
+        const size_t off = ((size_t)(4 * blk + ct) * NQG) * 64 + (pc % (NQG * 64));  // 16-byte pieces
+        sv[m] = reinterpret_cast<const uint4 *>(Sg)[off];
+        dv[m] = reinterpret_cast<const uint4 *>(Dg)[off];
+      }
+    }
+    // V and dO rows: 8 columns per piece
+    const int r = t >> 3, m8 = t & 7;
+    vv = ov = make_uint4(0u, 0u, 0u, 0u);
+    if (r < rows && m8 < 2 * nt) {
+      const size_t e = (size_t)(cl.row0 + r) * p.DV + JB * blk + 8 * m8;
+      vv = *reinterpret_cast<const uint4 *>(static_cast<const bf16 *>(p.v) + e);
+      ov = *reinterpret_cast<const uint4 *>(static_cast<const bf16 *>(p.dout) + e);
+    }
+  };
+  auto put = [&](int blk) {
+    const int nt = min(4, ntile - 4 * blk);
+    if (nt < 4) {
+      // a partial block: the missing columns of every block array read as zero
+      for (int e = t; e < (JB - 16 * nt) * LDK; e += kGT) {
+        bS[16 * nt * LDK + e] = bD[16 * nt * LDK + e] = (bf16)0.f;
+      }
+      for (int e = t; e < C * (JB - 16 * nt); e += kGT) {
+        const int row = e / (JB - 16 * nt), col = O::perm(16 * nt + e % (JB - 16 * nt));
+        bU[row * LDJ + col] = bUD[row * LDJ + col] = bDU[row * LDJ + col] = bGX[row * LDJ + col] = (bf16)0.f;
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < SPER; ++m) {
+      const int pc = t + m * kGT;
+      const int ct = pc / (NQG * 64);
+      if (ct < nt) {
+        // state rows 32 q + 16 (x >> 2) + 4 (l >> 4) + (x & 3), column 16 ct + (l & 15):
+        // group 32 q + 8 (l >> 4) of row 16 ct + (l & 15) of S^T
+        const int q = (pc / 64) % NQG, l = pc & 63;
+        const int off = (16 * ct + (l & 15)) * LDK + 32 * q + 8 * (l >> 4);
+        *reinterpret_cast<uint4 *>(bS + off) = sv[m];
+        *reinterpret_cast<uint4 *>(bD + off) = dv[m];
+        const Grp es = __builtin_bit_cast(Grp, sv[m]), ed = __builtin_bit_cast(Grp, dv[m]);
+#pragma unroll
+        for (int x = 0; x < 8; ++x) gcp = fmaf((float)es[x], (float)ed[x], gcp);
+      }
+    }
+    const int r = t >> 3, m8 = t & 7;
+    O::st_piece(bVX + r * LDJ, m8, vv);
+    O::st_piece(bO + r * LDJ, m8, ov);
+  };
+  // D-layout tile of a grouped block array: M[r16 + 4 lg + j][c0 + lr], j < 4
+  auto col4g = [&](const bf16 *M, int r16, int c0) {
+    const int x = (lane >> 2) & 3, a4 = lane & 3;
+    const bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (lds_bf16x4 *)(M + (r16 + 4 * lg + x) * LDJ + O::perm(c0 + 4 * a4)));
+    return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+  };
+  // four bf16 of a D tile into a grouped block array (rows r16 + 4 lg + j, column c0 + lr)
+  auto put_d = [&](bf16 *M, int r16, int c0, f32x4 v) {
+    const int col = O::perm(c0 + lr);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) M[(r16 + 4 * lg + j) * LDJ + col] = (bf16)v[j];
+  };
+
+  issue(0);
+  for (int blk = 0; blk < nblk; ++blk) {
+    __syncthreads();  // the previous block's readers are done (and the chunk's loads are in LDS)
+    put(blk);
+    if (blk + 1 < nblk) issue(blk + 1);
+    __syncthreads();
+    const int nt = min(4, ntile - 4 * blk);
+    // ---- (A) K S, Q S, K dS', X, dU for row tile a and column tiles 2 half, 2 half + 1 ----
+    f32x4 ks[2], qs[2], kd[2];
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+      const int ct = 2 * half + cc;
+      ks[cc] = qs[cc] = kd[cc] = z4;
+      if (ct >= nt) continue;
+#pragma unroll
+      for (int q = 0; q < NQG; ++q) {
+        const Grp bs = O::a_row(bS + (16 * ct + lr) * LDK, 32 * q, lg), bd = O::a_row(bD + (16 * ct + lr) * LDK, 32 * q, lg);
+        const Grp ak = O::a_row(bK + ra * LDK, 32 * q, lg), aq = O::a_row(bQ + ra * LDK, 32 * q, lg);
+        ks[cc] = O::mma_grp(ak, bs, ks[cc]);
+        qs[cc] = O::mma_grp(aq, bs, qs[cc]);
+        kd[cc] = O::mma_grp(ak, bd, kd[cc]);
+      }
+    }
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+      const int ct = 2 * half + cc;
+      if (ct >= nt) continue;
+      // P^T dO (P lower triangular: row block a of P^T needs rows >= 16 a of P)
+      f32x4 pd = z4;
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+        if (q >= a / 2)
+          pd = O::mma_grp(O::a_trans(bP, LDC, 32 * q, 16 * a, lane), O::a_trans(bO, LDJ, 32 * q, 16 * ct, lane), pd);
+      const f32x4 v4 = col4g(bVX, 16 * a, 16 * ct);
+      const f32x4 gm = *reinterpret_cast<const f32x4 *>(fvec + C + 16 * a + 4 * lg);
+      const f32x4 d4 = *reinterpret_cast<const f32x4 *>(fvec + 2 * C + 16 * a + 4 * lg);
+      // (a V tile is read and overwritten by X only by the wave that owns it)
+      put_d(bVX, 16 * a, 16 * ct, v4 - gm * ks[cc]);
+      put_d(bDU, 16 * a, 16 * ct, pd + d4 * kd[cc]);
+    }
+    __syncthreads();
+    // ---- (B) U = T' X, dX = T'^T dU (= dV), row sums ----
+    float pg[4] = {0.f, 0.f, 0.f, 0.f}, pdd[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+      const int ct = 2 * half + cc;
+      if (ct >= nt) continue;
+      f32x4 u = z4, dx = z4;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        if (32 * q < 16 * (a + 1))
+          u = O::mma_grp(O::a_trans(bTp, LDC, 32 * q, 16 * a, lane), O::a_trans(bVX, LDJ, 32 * q, 16 * ct, lane), u);
+        if (q >= a / 2)
+          dx = O::mma_grp(O::a_row(bTp + ra * LDC, 32 * q, lg), O::a_trans(bDU, LDJ, 32 * q, 16 * ct, lane), dx);
+      }
+      const f32x4 gm = *reinterpret_cast<const f32x4 *>(fvec + C + 16 * a + 4 * lg);
+      const f32x4 d4 = *reinterpret_cast<const f32x4 *>(fvec + 2 * C + 16 * a + 4 * lg);
+      put_d(bU, 16 * a, 16 * ct, u);
+      put_d(bUD, 16 * a, 16 * ct, d4 * u);
+      put_d(bGX, 16 * a, 16 * ct, -(gm * dx));
+      const f32x4 o4 = col4g(bO, 16 * a, 16 * ct);
+      const int col = JB * blk + 16 * ct + lr;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = 16 * a + 4 * lg + j;
+        if (r < rows) static_cast<bf16 *>(p.dv)[(cl.row0 + r) * p.DV + col] = (bf16)dx[j];
+        pg[j] += qs[cc][j] * o4[j] - ks[cc][j] * dx[j];
+        pdd[j] += kd[cc][j] * u[j];
+      }
+    }
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        pg[j] += __shfl_xor(pg[j], off);
+        pdd[j] += __shfl_xor(pdd[j], off);
+      }
+    if (lr == 0) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        sdgam2[half * C + 16 * a + 4 * lg + j] += pg[j];
+        sdd2[half * C + 16 * a + 4 * lg + j] += pdd[j];
+      }
+    }
+    __syncthreads();
+    // ---- (D) dW += dU X^T (half 0), dP += dO U^T (half 1, tiles at or below the diagonal),
+    //      dQ += dO S^T, dK += GX S^T + UD dS'^T (column tiles b = 2 i + half) ----
+#pragma unroll
+    for (int q = 0; q < JB / 32; ++q) {
+      if (32 * q >= 16 * nt) continue;
+      const Grp adu = O::a_row(bDU + ra * LDJ, 32 * q, lg), ado = O::a_row(bO + ra * LDJ, 32 * q, lg);
+      const Grp agx = O::a_row(bGX + ra * LDJ, 32 * q, lg), aud = O::a_row(bUD + ra * LDJ, 32 * q, lg);
+      if (half == 0) {
+#pragma unroll
+        for (int b = 0; b < NRT; ++b) accWP[b] = O::mma_grp(adu, O::a_row(bVX + (16 * b + lr) * LDJ, 32 * q, lg), accWP[b]);
+      } else {
+#pragma unroll
+        for (int b = 0; b < NRT; ++b)
+          if (b <= a) accWP[b] = O::mma_grp(ado, O::a_row(bU + (16 * b + lr) * LDJ, 32 * q, lg), accWP[b]);
+      }
+#pragma unroll
+      for (int i = 0; i < NKH; ++i) {
+        const int b = 2 * i + half;
+        if (b < NKT) {
+          const Grp srow = O::a_trans(bS, LDK, 32 * q, 16 * b, lane);
+          accQ[i] = O::mma_grp(ado, srow, accQ[i]);
+          accK[i] = O::mma_grp(aud, O::a_trans(bD, LDK, 32 * q, 16 * b, lane), O::mma_grp(agx, srow, accK[i]));
+        }
+      }
+    }
+  }
+  // dQ so far is dO S^T: rows scaled by Gam
+  {
+    const f32x4 gm = *reinterpret_cast<const f32x4 *>(fvec + C + 16 * a + 4 * lg);
+#pragma unroll
+    for (int i = 0; i < NKH; ++i) accQ[i] = gm * accQ[i];
+  }
+  // dgamma, dd row sums of the two halves
+  __syncthreads();
+  for (int r = t; r < C; r += kGT) {
+    sdgam2[r] += sdgam2[C + r];
+    sdd2[r] += sdd2[C + r];
+  }
+  float *sdgam = sdgam2, *sdd = sdd2;
+
+  // ---------------- C x C stage (as in kla_bwd_grads_kernel) ----------------
+  // fp32 K, Q (natural columns), T and P over the block arrays
+  float *sK = reinterpret_cast<float *>(smem + L::FK), *sQ = reinterpret_cast<float *>(smem + L::FQ);
+  float *sT = reinterpret_cast<float *>(smem + L::FT), *sP = reinterpret_cast<float *>(smem + L::FP);
+  float *B1 = reinterpret_cast<float *>(smem + L::FB1), *B2 = reinterpret_cast<float *>(smem + L::FB2);
+  __syncthreads();  // the block arrays are dead
+  {
+    TileLoad<bf16, C, DK, LK, kGT> lk, lq;
+    TileLoad<bf16, C, C, LC, kGT> lt, lp;
+    lk.issue(p.k, cl.row0, rows, 0, DK);
+    lq.issue(p.q, cl.row0, rows, 0, DK);
+    lt.issue(rm + R::TM, 0, C, 0, C);
+    lp.issue(rm + R::PM, 0, C, 0, C);
+    lk.put(sK);
+    lq.put(sQ);
+    lt.put(sT);
+    lp.put(sP);
+  }
+  {
+    float gs = gcp;  // <S, dS'>: one partial sum per wave
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) gs += __shfl_xor(gs, off);
+    if (lane == 0) sred[w] = gs;
+  }
+  __syncthreads();
+  if (own) {
+#pragma unroll
+    for (int b = 0; b < NRT; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * a + 4 * lg + i, s_ = 16 * b + lr;
+        if (half == 0)
+          B1[r * LC + s_] = accWP[b][i];                // dW
+        else
+          B2[r * LC + s_] = b <= a ? accWP[b][i] : 0.f;  // dP (entries above the diagonal masked below)
+      }
+  }
+  __syncthreads();
+  // db_s (first part) = sum_r T_rs dW_rs;  Y = (dW Diag(b)) T^T
+  // (eight lanes per column, whole columns per wave: C is a multiple of 8)
+  for (int s_ = t >> 3; s_ < C; s_ += kGT / 8) {
+    float acc = 0.f;
+    for (int r = s_ + (t & 7); r < C; r += 8) acc = fmaf(sT[r * LC + s_], B1[r * LC + s_], acc);
+#pragma unroll
+    for (int off = 4; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+    if ((t & 7) == 0) sdb1[s_] = acc;
+  }
+  // the wave pair of row tile a splits the C x C tiles: column block b goes to the wave
+  // whose half equals b mod 2
+  f32x4 y[NRT];
+#pragma unroll
+  for (int b = 0; b < NRT; ++b) y[b] = z4;
+  if (own) {
+#pragma unroll
+    for (int b = 0; b < NRT; ++b) {
+      if ((b & 1) != half) continue;
+      // Y[r][s] = sum_{m <= s} dW[r][m] b_m T[s][m]
+      for (int k0 = 0; k0 < 16 * (b + 1); k0 += 16) {
+        const int m = k0 + 4 * lg;
+        y[b] = MM::run(vec4(B1 + ra * LC + m) * vec4(sb + m), vec4(sT + (16 * b + lr) * LC + m), y[b]);
+      }
+    }
+  }
+  __syncthreads();
+  if (own) {
+#pragma unroll
+    for (int b = 0; b < NRT; ++b)
+      if ((b & 1) == half) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) B1[(16 * a + 4 * lg + i) * LC + 16 * b + lr] = y[b][i];  // Y over dW
+      }
+  }
+  __syncthreads();
+  // dA = -T^T Y (strictly lower); per entry dG = dA b_r E, dQK = dP E,
+  // dEE = dA b_r (G . E) + dP P, db_r += dA (G . E)
+  f32x4 dgm[NRT], dqk[NRT], dee[NRT];
+  float dbr[4] = {0.f, 0.f, 0.f, 0.f};
+  if (own) {
+#pragma unroll
+    for (int b = 0; b < NRT; ++b) {
+      if ((b & 1) != half) continue;
+      f32x4 da = z4;
+      if (b <= a) {
+        // dA[r][s] = -sum_{m >= r} T[m][r] Y[m][s]
+        for (int k0 = 16 * a; k0 < C; k0 += 16) {
+          const int m = k0 + 4 * lg;
+          da = MM::run(gat4(sT + m * LC + ra, LC), gat4(B1 + m * LC + 16 * b + lr, LC), da);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * a + 4 * lg + i, s_ = 16 * b + lr;
+        dgm[b][i] = dqk[b][i] = dee[b][i] = 0.f;
+        if (s_ <= r) {
+          const float ex = __expf(sgam[r] - sgam[s_]);
+          const float dA = s_ < r ? -da[i] : 0.f;
+          const float dP = B2[r * LC + s_];
+          const float gE = (float)rm[R::GE + r * C + s_];
+          dgm[b][i] = dA * sb[r] * ex;
+          dqk[b][i] = dP * ex;
+          dee[b][i] = fmaf(dA * sb[r], gE, dP * sP[r * LC + s_]);
+          dbr[i] = fmaf(dA, gE, dbr[i]);
+        }
+      }
+    }
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dbr[i] += __shfl_xor(dbr[i], off);
+  }
+  __syncthreads();
+  if (own) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (lr == 0) (half ? sdb3 : sdb2)[16 * a + 4 * lg + i] = dbr[i];
+#pragma unroll
+    for (int b = 0; b < NRT; ++b)
+      if ((b & 1) == half) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * a + 4 * lg + i, s_ = 16 * b + lr;
+          B1[r * LC + s_] = dgm[b][i];
+          B2[r * LC + s_] = dqk[b][i];
+          sP[r * LC + s_] = dee[b][i];
+        }
+      }
+  }
+  __syncthreads();
+  if (own) {
+    // dQ += dQK K;  dK += dQK^T Q + (dG + dG^T) K
+    for (int k0 = 0; k0 < C; k0 += 16) {
+      const int s_ = k0 + 4 * lg;
+      const f32x4 aq = vec4(B2 + ra * LC + s_), at = gat4(B2 + s_ * LC + ra, LC);
+      const f32x4 ag = vec4(B1 + ra * LC + s_) + gat4(B1 + s_ * LC + ra, LC);
+#pragma unroll
+      for (int i = 0; i < NKH; ++i) {
+        const int b = 2 * i + half;
+        if (b < NKT) {
+          const f32x4 kv = gat4(sK + s_ * LK + 16 * b + lr, LK), qv = gat4(sQ + s_ * LK + 16 * b + lr, LK);
+          accQ[i] = MM::run(aq, kv, accQ[i]);
+          accK[i] = MM::run(ag, kv, MM::run(at, qv, accK[i]));
+        }
+      }
+    }
+  }
+  // per-row scalars: dgamma, then dg = reverse running sum; db, deta, the norm term
+  // (eight lanes per row, whole rows per wave: C is a multiple of 8)
+  for (int r = t >> 3; r < C; r += kGT / 8) {
+    const int j = t & 7;
+    float rs = 0.f, cs = 0.f;
+    for (int s_ = j; s_ < C; s_ += 8) {
+      rs += sP[r * LC + s_];
+      cs += sP[s_ * LC + r];
+    }
+#pragma unroll
+    for (int off = 4; off >= 1; off >>= 1) {
+      rs += __shfl_xor(rs, off);
+      cs += __shfl_xor(cs, off);
+    }
+    if (j == 0) sdge[r] = sdgam[r] * sGm[r] - sdd[r] * sdec[r] + rs - cs;
+  }
+  __syncthreads();
+  if (w == 0) {
+    // the chunk-end terms go to the last row, then dg_r = sum_{r' >= r} dgamma_r' (lane r)
+    float gcs = lane < kGT / 64 ? sred[lane] : 0.f;
+    float ddd = lane < C ? sdd[lane] * sdec[lane] : 0.f;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      gcs += __shfl_xor(gcs, off);
+      ddd += __shfl_xor(ddd, off);
+    }
+    float v = lane < C ? sdge[lane] : 0.f;
+    if (lane == C - 1) v += gcs * __expf(gC) + ddd;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float u = __shfl_down(v, off);
+      if (lane + off < 64) v += u;
+    }
+    if (lane < C) sdge[lane] = v;
+  }
+  for (int r = t; r < C; r += kGT) {
+    const float db = sdb1[r] + sdb2[r] + sdb3[r];
+    const float den = snrm[r] + p.eps;
+    scf[r] = (p.beta_direct || r >= rows) ? 0.f : -2.f * seta[r] * db / (den * den);
+    if (r < rows) p.deta[cl.row0 + r] = p.beta_direct ? db : db / den;
+  }
+  __syncthreads();
+  for (int r = t; r < rows; r += kGT) p.dg[cl.row0 + r] = sdge[r];
+  if (own) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * a + 4 * lg + i;
+      if (r < rows) {
+#pragma unroll
+        for (int ii = 0; ii < NKH; ++ii) {
+          const int b = 2 * ii + half;
+          if (b < NKT) {
+            const int c = 16 * b + lr;
+            static_cast<bf16 *>(p.dq)[(cl.row0 + r) * DK + c] = (bf16)(accQ[ii][i]);
+            static_cast<bf16 *>(p.dk)[(cl.row0 + r) * DK + c] =
+                (bf16)(fmaf(scf[r], sK[r * LK + c], accK[ii][i]));
+          }
+        }
+      }
+    }
+  }
+}
+
+// ============================================================================
 // host side
 // ============================================================================
 template <typename E, int C, int DK>
@@ -931,6 +1475,7 @@ hipError_t launch_bwd_t(const ChunkArgs &a, const ChunkBwdArgs &b, hipStream_t s
   const size_t pb = BwdLayout<E, C, DK>::prep_bytes(a, p.nslot), sb = BwdLayout<E, C, DK>::state_bytes(a, p.nslot);
   p.states = ws + pb;
   p.dstates = ws + pb + sb;
+  p.fws = ws + pb + 2 * sb;
   const unsigned seq_blocks = (unsigned)((long long)a.num_seqs * a.H * p.nsl);
   // the two scans: (sequence, head) groups padded to whole rounds of 8, times the slices
   const unsigned groups8 = (unsigned)(((long long)a.num_seqs * a.H + 7) / 8 * 8);
@@ -961,7 +1506,10 @@ hipError_t launch_bwd_t(const ChunkArgs &a, const ChunkBwdArgs &b, hipStream_t s
     if (e != hipSuccess) return e;
   }
   if (tokens) {
-    hipLaunchKernelGGL((kla_bwd_grads_kernel<E, C, DK>), dim3((unsigned)p.nslot, (unsigned)a.H), dim3(kGT), 0, st, p);
+    if constexpr (std::is_same<E, bf16>::value && C == 64)
+      hipLaunchKernelGGL((kla_bwd_grads2_kernel<DK>), dim3((unsigned)p.nslot, (unsigned)a.H), dim3(kGT), 0, st, p);
+    else
+      hipLaunchKernelGGL((kla_bwd_grads_kernel<E, C, DK>), dim3((unsigned)p.nslot, (unsigned)a.H), dim3(kGT), 0, st, p);
     return hipGetLastError();
   }
   return hipSuccess;
