@@ -60,6 +60,7 @@ struct BwdParams {
   float *prep;
   void *states, *dstates;  // chunk-start states and chunk-end state gradients, input element type
   const char *fws;         // the forward workspace: T'^T images and gamma, Gam, d per (head, slot)
+  const char *timg;        // bf16, chunk 64: the packed T^T images per (head, slot), else nullptr
   int B, H, T, DV, nseq, nslot, nsl;
   int beta_direct;
 };
@@ -879,12 +880,14 @@ __global__ __launch_bounds__(kGT) void kla_bwd_grads_kernel(BwdParams p) {
 // eight slices of 16), every product is a 16x16x32 bf16 MFMA whose operands
 // come straight from bf16 LDS rows in the grouped column order of kla_ops.h
 // (row reads for contractions along a row, transposing reads for contractions
-// down a column), and T'^T with gamma, Gam, d is the forward prep kernel's
-// image of the chunk (the forward workspace), so T' X and T'^T dU read it as
-// the forward and the adjoint scans do.  Waves w and w + 4 share row tile
-// w & 3 (16 chunk rows); in the per-block phases each takes two of the block's
-// four 16-column tiles, in the outer products the same dW / dP and dQ, dK
-// tiles as above, so the C x C stage and the output are the code above.
+// down a column).  No prep record: T'^T with gamma, Gam, d is the forward prep
+// kernel's image of the chunk (the forward workspace), so T' X and T'^T dU read
+// it as the forward and the adjoint scans do; T^T (without beta) is the second
+// image the same kernel writes in states mode; P = lower(Q K^T . E), ||k||^2
+// and b are formed here from the K and Q rows in LDS.  Waves w and w + 4 share
+// row tile w & 3 (16 chunk rows); in the per-block phases each takes two of the
+// block's four 16-column tiles; tile (a, b) of a C x C product belongs to the
+// wave of row tile a with half = b & 1; dQ, dK column tile b to half b & 1.
 //
 // The state blocks are kept transposed (S^T, dS'^T: a row per state column,
 // grouped over dk), where a 16-byte piece of the operand-group layout the
@@ -915,13 +918,20 @@ struct Grad2Smem {
   static constexpr int DU = UD + C * LDJ * 2;
   static constexpr int GX = DU + C * LDJ * 2;        // -Diag(Gam) dX
   static constexpr int BLK_END = GX + C * LDJ * 2;
-  // the C x C stage reuses the bytes from 0: K, Q (fp32, natural), T, P (fp32), dW, dP
-  static constexpr int LK = DK + 4, LC = C + 4;
-  static constexpr int FK = 0, FQ = FK + C * LK * 4, FT = FQ + C * LK * 4, FP = FT + C * LC * 4;
-  static constexpr int FB1 = FP + C * LC * 4, FB2 = FB1 + C * LC * 4, F_END = FB2 + C * LC * 4;
-  static constexpr int VEC = (BLK_END > F_END ? BLK_END : F_END);   // fp32 vectors, kept throughout
+  // the C x C stage reuses the block arrays: the T^T image, dW, Y, dQK, dG (bf16, grouped
+  // columns), dP (fp32), then the per-tile partial sums; dQ, dK are staged (bf16, natural
+  // rows) over T .. dQK once those are read
+  static constexpr int LCF = C + 4, LDO = DK + 8;
+  static constexpr int CT = S, CW = CT + C * LDC * 2, CY = CW + C * LDC * 2, CQK = CY + C * LDC * 2;
+  static constexpr int CG = CQK + C * LDC * 2, CDP = CG + C * LDC * 2, CPART = CDP + C * LCF * 4;
+  static constexpr int PROW = 0, PCOL = 2 * C, PDB = 6 * C, PCT = 8 * C, NPART = 12 * C;  // floats
+  static constexpr int C_END = CPART + NPART * 4;
+  static constexpr int SDQ = CT, SDK = SDQ + C * LDO * 2;
+  static_assert(SDK + C * LDO * 2 <= CG, "the staged dQ, dK stay clear of dG, dP and the partial sums");
+  static_assert(CDP % 16 == 0 && CPART % 16 == 0, "align");
+  static constexpr int VEC = (BLK_END > C_END ? BLK_END : C_END);   // fp32 vectors, kept throughout
   static constexpr int BETA = 0, GAM = BETA + C, NRM = GAM + C, ETA = NRM + C, DGAM = ETA + C, DD = DGAM + 2 * C;
-  static constexpr int DB1 = DD + 2 * C, DB2 = DB1 + C, DB3 = DB2 + C, DGE = DB3 + C, CF = DGE + C, GM = CF + C;
+  static constexpr int CF = DD + 2 * C, GM = CF + C;
   static constexpr int DEC = GM + C, RED = DEC + C, NVEC = RED + kGT / 64;
   static constexpr int BYTES = VEC + NVEC * 4;
   static_assert(BYTES <= 160 * 1024, "LDS budget");
@@ -931,13 +941,11 @@ struct Grad2Smem {
 template <int DK>
 __global__ __launch_bounds__(kGT) void kla_bwd_grads2_kernel(BwdParams p) {
   using L = Grad2Smem<DK>;
-  using R = PrepRec<bf16, 64>;
   using O = Ops<bf16>;
   using Grp = O::Grp;
   using TLy = TpLayout<bf16, 64>;
-  using MM = Mma16<bf16>;
   constexpr int C = 64, NRT = 4, NKT = DK / 16, NKH = (NKT + 1) / 2, NQG = DK / 32, JB = L::JB;
-  constexpr int LDK = L::LDK, LDC = L::LDC, LDJ = L::LDJ, LK = L::LK, LC = L::LC;
+  constexpr int LDK = L::LDK, LDC = L::LDC, LDJ = L::LDJ, LCF = L::LCF, LDO = L::LDO;
   __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
   bf16 *bK = reinterpret_cast<bf16 *>(smem + L::K), *bQ = reinterpret_cast<bf16 *>(smem + L::Q);
   bf16 *bTp = reinterpret_cast<bf16 *>(smem + L::TP), *bP = reinterpret_cast<bf16 *>(smem + L::P);
@@ -949,7 +957,7 @@ __global__ __launch_bounds__(kGT) void kla_bwd_grads2_kernel(BwdParams p) {
   float *vec = reinterpret_cast<float *>(smem + L::VEC);
   float *sb = vec + L::BETA, *sgam = vec + L::GAM, *snrm = vec + L::NRM, *seta = vec + L::ETA;
   float *sdgam2 = vec + L::DGAM, *sdd2 = vec + L::DD;  // per half of the column tiles
-  float *sdb1 = vec + L::DB1, *sdb2 = vec + L::DB2, *sdb3 = vec + L::DB3, *sdge = vec + L::DGE, *scf = vec + L::CF;
+  float *scf = vec + L::CF;
   float *sGm = vec + L::GM, *sdec = vec + L::DEC, *sred = vec + L::RED;
 
   const int slot = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
@@ -961,44 +969,11 @@ __global__ __launch_bounds__(kGT) void kla_bwd_grads2_kernel(BwdParams p) {
   const bool own = true, lead = half == 0;
   const int ra = 16 * a + lr;
   const size_t sidx = (size_t)h * p.nslot + slot;
-  char *recb = R::at(p.prep, sidx);
-  const bf16 *rm = R::mat(recb);
-  const float *rv = R::vec(recb);
+  const float *gv = reinterpret_cast<const float *>(p.fws + sidx * TLy::BYTES + TLy::PACK);  // gamma, Gam, d
   const bf16 *Sg = static_cast<const bf16 *>(p.states) + sidx * DK * p.DV;
   const bf16 *Dg = static_cast<const bf16 *>(p.dstates) + sidx * DK * p.DV;
   const int ntile = p.DV / 16;                 // 16-column tiles of the state
   const int nblk = (ntile + 3) / 4;
-
-  // ---- the chunk's K, Q rows, P and T'^T image (grouped columns), vectors -----
-  if (w < 2) {
-    RowLoad<bf16, DK, AllBlocks<4>> rl;
-    rl.issue(static_cast<const bf16 *>(w == 0 ? p.k : p.q) + cl.row0 * DK, rows, lane);
-    rl.put(w == 0 ? bK : bQ, LDK, lane, [](int, int row) { return row; });
-  } else if (w == 2) {
-    ImgCopy<bf16, 64> ic;
-    ic.issue(p.fws + sidx * TLy::BYTES, lane);
-    ic.put(bTp, lane);
-  } else {
-    // P: C rows of C natural columns, 16-byte pieces into grouped rows (waves 3..7)
-    for (int pc = t - 192; pc < C * C / 8; pc += kGT - 192) {
-      const uint4 v = *reinterpret_cast<const uint4 *>(rm + R::PM + 8 * pc);
-      O::st_piece(bP + (pc / 8) * LDC, pc % 8, v);
-    }
-  }
-  for (int r = t; r < C; r += kGT) {
-    sb[r] = rv[R::BETA + r];
-    sgam[r] = rv[R::GAM + r];
-    snrm[r] = rv[R::NRM + r];
-    seta[r] = r < rows ? ld<bf16>(p.eta, cl.row0 + r) : 0.f;
-    sdgam2[r] = sdgam2[C + r] = 0.f;
-    sdd2[r] = sdd2[C + r] = 0.f;
-  }
-  const float gC = rv[R::GAM + C - 1];
-  for (int r = t; r < C; r += kGT) {
-    const float gr = rv[R::GAM + r];
-    sGm[r] = __expf(gr);
-    sdec[r] = __expf(gC - gr);
-  }
 
   const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
   f32x4 accWP[NRT], accQ[NKH], accK[NKH];  // accWP: dW (half 0) or dP (half 1)
@@ -1012,7 +987,7 @@ __global__ __launch_bounds__(kGT) void kla_bwd_grads2_kernel(BwdParams p) {
   // S, dS' of a block: tiles 4 blk .. (up to 4), groups q of 32 rows, 64 lanes of 16 bytes
   constexpr int SPIECES = 4 * NQG * 64;           // pieces of a full block
   constexpr int SPER = (SPIECES + kGT - 1) / kGT;
-  uint4 sv[SPER], dv[SPER], vv, ov;
+  uint4 sv[SPER], dv[SPER], vv, ov, tv;  // tv: a 16-byte piece of T (for the C x C stage)
   auto issue = [&](int blk) {
     const int nt = min(4, ntile - 4 * blk);
 #pragma unroll
@@ -1074,18 +1049,73 @@ __global__ __launch_bounds__(kGT) void kla_bwd_grads2_kernel(BwdParams p) {
     return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
   };
   // four bf16 of a D tile into a grouped block array (rows r16 + 4 lg + j, column c0 + lr)
-  auto put_d = [&](bf16 *M, int r16, int c0, f32x4 v) {
+  auto put_d = [&](bf16 *M, int r16, int c0, f32x4 v, int ld = L::LDJ) {
     const int col = O::perm(c0 + lr);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) M[(r16 + 4 * lg + j) * LDJ + col] = (bf16)v[j];
+    for (int j = 0; j < 4; ++j) M[(r16 + 4 * lg + j) * ld + col] = (bf16)v[j];
   };
 
-  issue(0);
+  issue(0);  // the first block's loads fly with the chunk's
+  // ---- the chunk's K, Q rows, P and T'^T image (grouped columns), vectors -----
+  if (w < 2) {
+    RowLoad<bf16, DK, AllBlocks<4>> rl;
+    rl.issue(static_cast<const bf16 *>(w == 0 ? p.k : p.q) + cl.row0 * DK, rows, lane);
+    rl.put(w == 0 ? bK : bQ, LDK, lane, [](int, int row) { return row; });
+  } else if (w == 2) {
+    ImgCopy<bf16, 64> ic;
+    ic.issue(p.fws + sidx * TLy::BYTES, lane);
+    ic.put(bTp, lane);
+  }
+  for (int r = t; r < C; r += kGT) {
+    sgam[r] = gv[r];
+    sGm[r] = gv[C + r];
+    sdec[r] = gv[2 * C + r];
+    seta[r] = r < rows ? ld<bf16>(p.eta, cl.row0 + r) : 0.f;
+    sdgam2[r] = sdgam2[C + r] = 0.f;
+    sdd2[r] = sdd2[C + r] = 0.f;
+  }
+  const float gC = gv[C - 1];
+
   for (int blk = 0; blk < nblk; ++blk) {
-    __syncthreads();  // the previous block's readers are done (and the chunk's loads are in LDS)
+    lds_barrier();  // the previous block's readers are done (and the chunk's loads are in LDS)
     put(blk);
-    if (blk + 1 < nblk) issue(blk + 1);
-    __syncthreads();
+    if (blk + 1 < nblk)
+      issue(blk + 1);
+    else if (t < TLy::PACK / 16)
+      tv = reinterpret_cast<const uint4 *>(p.timg + sidx * TLy::PACK)[t];  // the T^T image
+    if (blk == 0) {
+      // ||k_r||^2 and b_r (eight lanes per row); P = lower(Q K^T . E), tiles b <= a
+      {
+        const int r = t >> 3;
+        float nr = 0.f;
+#pragma unroll
+        for (int m = 0; m < DK / 64; ++m) nr += O::sumsq(*reinterpret_cast<const Grp *>(bK + r * LDK + 8 * (t & 7) + 64 * m));
+#pragma unroll
+        for (int off = 4; off >= 1; off >>= 1) nr += __shfl_xor(nr, off);
+        if ((t & 7) == 0) {
+          snrm[r] = nr;
+          sb[r] = r < rows ? (p.beta_direct ? seta[r] : seta[r] / (nr + p.eps)) : 0.f;
+        }
+      }
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        const int b = 2 * cc + half;
+        f32x4 pv = z4;
+        if (b <= a) {
+#pragma unroll
+          for (int q = 0; q < NQG; ++q)
+            pv = O::mma_grp(O::a_row(bQ + ra * LDK, 32 * q, lg), O::a_row(bK + (16 * b + lr) * LDK, 32 * q, lg), pv);
+          const int s_ = 16 * b + lr;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int r = 16 * a + 4 * lg + j;
+            pv[j] = s_ <= r ? pv[j] * __expf(sgam[r] - sgam[s_]) : 0.f;
+          }
+        }
+        put_d(bP, 16 * a, 16 * b, pv, LDC);
+      }
+    }
+    lds_barrier();
     const int nt = min(4, ntile - 4 * blk);
     // ---- (A) K S, Q S, K dS', X, dU for row tile a and column tiles 2 half, 2 half + 1 ----
     f32x4 ks[2], qs[2], kd[2];
@@ -1120,7 +1150,7 @@ __global__ __launch_bounds__(kGT) void kla_bwd_grads2_kernel(BwdParams p) {
       put_d(bVX, 16 * a, 16 * ct, v4 - gm * ks[cc]);
       put_d(bDU, 16 * a, 16 * ct, pd + d4 * kd[cc]);
     }
-    __syncthreads();
+    lds_barrier();
     // ---- (B) U = T' X, dX = T'^T dU (= dV), row sums ----
     float pg[4] = {0.f, 0.f, 0.f, 0.f}, pdd[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1164,7 +1194,7 @@ __global__ __launch_bounds__(kGT) void kla_bwd_grads2_kernel(BwdParams p) {
         sdd2[half * C + 16 * a + 4 * lg + j] += pdd[j];
       }
     }
-    __syncthreads();
+    lds_barrier();
     // ---- (D) dW += dU X^T (half 0), dP += dO U^T (half 1, tiles at or below the diagonal),
     //      dQ += dO S^T, dK += GX S^T + UD dS'^T (column tiles b = 2 i + half) ----
 #pragma unroll
@@ -1197,218 +1227,204 @@ __global__ __launch_bounds__(kGT) void kla_bwd_grads2_kernel(BwdParams p) {
 #pragma unroll
     for (int i = 0; i < NKH; ++i) accQ[i] = gm * accQ[i];
   }
-  // dgamma, dd row sums of the two halves
-  __syncthreads();
-  for (int r = t; r < C; r += kGT) {
-    sdgam2[r] += sdgam2[C + r];
-    sdd2[r] += sdd2[C + r];
-  }
-  float *sdgam = sdgam2, *sdd = sdd2;
-
-  // ---------------- C x C stage (as in kla_bwd_grads_kernel) ----------------
-  // fp32 K, Q (natural columns), T and P over the block arrays
-  float *sK = reinterpret_cast<float *>(smem + L::FK), *sQ = reinterpret_cast<float *>(smem + L::FQ);
-  float *sT = reinterpret_cast<float *>(smem + L::FT), *sP = reinterpret_cast<float *>(smem + L::FP);
-  float *B1 = reinterpret_cast<float *>(smem + L::FB1), *B2 = reinterpret_cast<float *>(smem + L::FB2);
-  __syncthreads();  // the block arrays are dead
-  {
-    TileLoad<bf16, C, DK, LK, kGT> lk, lq;
-    TileLoad<bf16, C, C, LC, kGT> lt, lp;
-    lk.issue(p.k, cl.row0, rows, 0, DK);
-    lq.issue(p.q, cl.row0, rows, 0, DK);
-    lt.issue(rm + R::TM, 0, C, 0, C);
-    lp.issue(rm + R::PM, 0, C, 0, C);
-    lk.put(sK);
-    lq.put(sQ);
-    lt.put(sT);
-    lp.put(sP);
-  }
   {
     float gs = gcp;  // <S, dS'>: one partial sum per wave
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) gs += __shfl_xor(gs, off);
     if (lane == 0) sred[w] = gs;
   }
-  __syncthreads();
-  if (own) {
+  lds_barrier();  // the block arrays are dead
+
+  // ---------------- C x C stage ----------------------------------------------
+  // With T = (I + A)^-1 (so T' = T Diag(b)), dW = dU X^T and dP = dO U^T:
+  //   db_s  = sum_r T_rs dW_rs + sum_s' dA_ss' (G . E)_ss'
+  //   Y     = dW T'^T,   dA = -T^T Y (strictly lower)
+  //   dG    = Diag(b) dA . E,   dQK = dP . E,   dEE = Diag(b) dA . G . E + dP . P
+  //   dQ   += dQK K,   dK += dQK^T Q + (dG + dG^T) K
+  //   dgamma_r += sum_s dEE_rs - sum_s dEE_sr
+  // Tile (a, b) of a C x C product belongs to the wave of row tile a with half = b & 1.
+  for (int r = t; r < C; r += kGT) {
+    sdgam2[r] += sdgam2[C + r];
+    sdd2[r] += sdd2[C + r];
+  }
+  const float *sdgam = sdgam2, *sdd = sdd2;
+  bf16 *cT = reinterpret_cast<bf16 *>(smem + L::CT), *cW = reinterpret_cast<bf16 *>(smem + L::CW);
+  bf16 *cY = reinterpret_cast<bf16 *>(smem + L::CY), *cQK = reinterpret_cast<bf16 *>(smem + L::CQK);
+  bf16 *cG = reinterpret_cast<bf16 *>(smem + L::CG);
+  float *cdP = reinterpret_cast<float *>(smem + L::CDP), *part = reinterpret_cast<float *>(smem + L::CPART);
+  float *prow = part + L::PROW, *pcol = part + L::PCOL, *pdb = part + L::PDB, *pct = part + L::PCT;
+  if (t < TLy::PACK / 16) *reinterpret_cast<uint4 *>(cT + TLy::piece_to_lds(t)) = tv;  // T^T
+  for (int e = t; e < L::NPART; e += kGT) part[e] = 0.f;
+  if (half == 0) {
+#pragma unroll
+    for (int b = 0; b < NRT; ++b) put_d(cW, 16 * a, 16 * b, accWP[b], LDC);
+  } else {
 #pragma unroll
     for (int b = 0; b < NRT; ++b)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * a + 4 * lg + i, s_ = 16 * b + lr;
-        if (half == 0)
-          B1[r * LC + s_] = accWP[b][i];                // dW
-        else
-          B2[r * LC + s_] = b <= a ? accWP[b][i] : 0.f;  // dP (entries above the diagonal masked below)
-      }
+      for (int j = 0; j < 4; ++j) cdP[(16 * a + 4 * lg + j) * LCF + 16 * b + lr] = b <= a ? accWP[b][j] : 0.f;
   }
-  __syncthreads();
-  // db_s (first part) = sum_r T_rs dW_rs;  Y = (dW Diag(b)) T^T
-  // (eight lanes per column, whole columns per wave: C is a multiple of 8)
-  for (int s_ = t >> 3; s_ < C; s_ += kGT / 8) {
-    float acc = 0.f;
-    for (int r = s_ + (t & 7); r < C; r += 8) acc = fmaf(sT[r * LC + s_], B1[r * LC + s_], acc);
+  lds_barrier();
+  // Y tiles; the column sums of T . dW (the dW tiles are still in the half-0 registers)
 #pragma unroll
-    for (int off = 4; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-    if ((t & 7) == 0) sdb1[s_] = acc;
+  for (int cc = 0; cc < 2; ++cc) {
+    const int b = 2 * cc + half;
+    f32x4 y = z4;
+#pragma unroll
+    for (int q = 0; q < 2; ++q)  // T'^T rows m <= s: contraction block q reaches column tile b
+      if (32 * q < 16 * (b + 1))
+        y = O::mma_grp(O::a_row(cW + ra * LDC, 32 * q, lg), O::a_trans(bTp, LDC, 32 * q, 16 * b, lane), y);
+    put_d(cY, 16 * a, 16 * b, y, LDC);
   }
-  // the wave pair of row tile a splits the C x C tiles: column block b goes to the wave
-  // whose half equals b mod 2
-  f32x4 y[NRT];
-#pragma unroll
-  for (int b = 0; b < NRT; ++b) y[b] = z4;
-  if (own) {
+  if (half == 0) {
 #pragma unroll
     for (int b = 0; b < NRT; ++b) {
-      if ((b & 1) != half) continue;
-      // Y[r][s] = sum_{m <= s} dW[r][m] b_m T[s][m]
-      for (int k0 = 0; k0 < 16 * (b + 1); k0 += 16) {
-        const int m = k0 + 4 * lg;
-        y[b] = MM::run(vec4(B1 + ra * LC + m) * vec4(sb + m), vec4(sT + (16 * b + lr) * LC + m), y[b]);
+      if (b > a) continue;
+      const int s_ = 16 * b + lr;
+      float cs = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = 16 * a + 4 * lg + j;
+        if (s_ <= r) cs = fmaf((float)cT[s_ * LDC + O::perm(r)], accWP[b][j], cs);  // T^T[s][r]
       }
+      cs += __shfl_xor(cs, 16);
+      cs += __shfl_xor(cs, 32);
+      if (lg == 0) pct[a * C + s_] = cs;
     }
   }
-  __syncthreads();
-  if (own) {
+  lds_barrier();
+  // dA, G . E and the entrywise terms for the tiles at or below the diagonal
+  {
+    float re[4] = {0.f, 0.f, 0.f, 0.f}, rb[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int b = 0; b < NRT; ++b)
-      if ((b & 1) == half) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) B1[(16 * a + 4 * lg + i) * LC + 16 * b + lr] = y[b][i];  // Y over dW
-      }
-  }
-  __syncthreads();
-  // dA = -T^T Y (strictly lower); per entry dG = dA b_r E, dQK = dP E,
-  // dEE = dA b_r (G . E) + dP P, db_r += dA (G . E)
-  f32x4 dgm[NRT], dqk[NRT], dee[NRT];
-  float dbr[4] = {0.f, 0.f, 0.f, 0.f};
-  if (own) {
-#pragma unroll
-    for (int b = 0; b < NRT; ++b) {
-      if ((b & 1) != half) continue;
-      f32x4 da = z4;
+    for (int cc = 0; cc < 2; ++cc) {
+      const int b = 2 * cc + half;
+      f32x4 dg4 = z4, dq4 = z4;
       if (b <= a) {
-        // dA[r][s] = -sum_{m >= r} T[m][r] Y[m][s]
-        for (int k0 = 16 * a; k0 < C; k0 += 16) {
-          const int m = k0 + 4 * lg;
-          da = MM::run(gat4(sT + m * LC + ra, LC), gat4(B1 + m * LC + 16 * b + lr, LC), da);
-        }
-      }
+        f32x4 da = z4, gk = z4;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * a + 4 * lg + i, s_ = 16 * b + lr;
-        dgm[b][i] = dqk[b][i] = dee[b][i] = 0.f;
-        if (s_ <= r) {
-          const float ex = __expf(sgam[r] - sgam[s_]);
-          const float dA = s_ < r ? -da[i] : 0.f;
-          const float dP = B2[r * LC + s_];
-          const float gE = (float)rm[R::GE + r * C + s_];
-          dgm[b][i] = dA * sb[r] * ex;
-          dqk[b][i] = dP * ex;
-          dee[b][i] = fmaf(dA * sb[r], gE, dP * sP[r * LC + s_]);
-          dbr[i] = fmaf(dA, gE, dbr[i]);
+        for (int q = 0; q < 2; ++q)  // T^T row r: rows m >= r of T
+          if (q >= a / 2)
+            da = O::mma_grp(O::a_row(cT + ra * LDC, 32 * q, lg), O::a_trans(cY, LDC, 32 * q, 16 * b, lane), da);
+#pragma unroll
+        for (int q = 0; q < NQG; ++q)
+          gk = O::mma_grp(O::a_row(bK + ra * LDK, 32 * q, lg), O::a_row(bK + (16 * b + lr) * LDK, 32 * q, lg), gk);
+        const int s_ = 16 * b + lr;
+        float ce = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = 16 * a + 4 * lg + j;
+          if (s_ <= r) {
+            const float ex = __expf(sgam[r] - sgam[s_]);
+            const float dA = s_ < r ? -da[j] : 0.f;
+            const float ge = gk[j] * ex, dP = cdP[r * LCF + s_];
+            dg4[j] = dA * sb[r] * ex;
+            dq4[j] = dP * ex;
+            const float dee = fmaf(dA * sb[r], ge, dP * (float)bP[r * LDC + O::perm(s_)]);
+            re[j] += dee;
+            ce += dee;
+            rb[j] = fmaf(dA, ge, rb[j]);
+          }
         }
+        ce += __shfl_xor(ce, 16);
+        ce += __shfl_xor(ce, 32);
+        if (lg == 0) pcol[a * C + s_] = ce;
       }
+      put_d(cG, 16 * a, 16 * b, dg4, LDC);  // zero above the diagonal
+      put_d(cQK, 16 * a, 16 * b, dq4, LDC);
     }
 #pragma unroll
     for (int off = 8; off >= 1; off >>= 1)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dbr[i] += __shfl_xor(dbr[i], off);
-  }
-  __syncthreads();
-  if (own) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (lr == 0) (half ? sdb3 : sdb2)[16 * a + 4 * lg + i] = dbr[i];
-#pragma unroll
-    for (int b = 0; b < NRT; ++b)
-      if ((b & 1) == half) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 16 * a + 4 * lg + i, s_ = 16 * b + lr;
-          B1[r * LC + s_] = dgm[b][i];
-          B2[r * LC + s_] = dqk[b][i];
-          sP[r * LC + s_] = dee[b][i];
-        }
+      for (int j = 0; j < 4; ++j) {
+        re[j] += __shfl_xor(re[j], off);
+        rb[j] += __shfl_xor(rb[j], off);
       }
-  }
-  __syncthreads();
-  if (own) {
-    // dQ += dQK K;  dK += dQK^T Q + (dG + dG^T) K
-    for (int k0 = 0; k0 < C; k0 += 16) {
-      const int s_ = k0 + 4 * lg;
-      const f32x4 aq = vec4(B2 + ra * LC + s_), at = gat4(B2 + s_ * LC + ra, LC);
-      const f32x4 ag = vec4(B1 + ra * LC + s_) + gat4(B1 + s_ * LC + ra, LC);
+    if (lr == 0) {
 #pragma unroll
-      for (int i = 0; i < NKH; ++i) {
-        const int b = 2 * i + half;
-        if (b < NKT) {
-          const f32x4 kv = gat4(sK + s_ * LK + 16 * b + lr, LK), qv = gat4(sQ + s_ * LK + 16 * b + lr, LK);
-          accQ[i] = MM::run(aq, kv, accQ[i]);
-          accK[i] = MM::run(ag, kv, MM::run(at, qv, accK[i]));
-        }
+      for (int j = 0; j < 4; ++j) {
+        prow[half * C + 16 * a + 4 * lg + j] = re[j];
+        pdb[half * C + 16 * a + 4 * lg + j] = rb[j];
       }
     }
   }
-  // per-row scalars: dgamma, then dg = reverse running sum; db, deta, the norm term
-  // (eight lanes per row, whole rows per wave: C is a multiple of 8)
-  for (int r = t >> 3; r < C; r += kGT / 8) {
-    const int j = t & 7;
-    float rs = 0.f, cs = 0.f;
-    for (int s_ = j; s_ < C; s_ += 8) {
-      rs += sP[r * LC + s_];
-      cs += sP[s_ * LC + r];
+  lds_barrier();
+  // dQ += dQK K;  dK += dQK^T Q + dG K + dG^T K  (contraction over the chunk rows s)
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const bool lo = 32 * q < 16 * (a + 1), up = q >= a / 2;  // row r: s <= r; column r: s >= r
+    Grp aqk = O::zero_grp(), ag = O::zero_grp(), aqt = O::zero_grp(), agt = O::zero_grp();
+    if (lo) {
+      aqk = O::a_row(cQK + ra * LDC, 32 * q, lg);
+      ag = O::a_row(cG + ra * LDC, 32 * q, lg);
+    }
+    if (up) {
+      aqt = O::a_trans(cQK, LDC, 32 * q, 16 * a, lane);
+      agt = O::a_trans(cG, LDC, 32 * q, 16 * a, lane);
     }
 #pragma unroll
-    for (int off = 4; off >= 1; off >>= 1) {
-      rs += __shfl_xor(rs, off);
-      cs += __shfl_xor(cs, off);
+    for (int i = 0; i < NKH; ++i) {
+      const int b = 2 * i + half;
+      if (b < NKT) {
+        const Grp kb = O::a_trans(bK, LDK, 32 * q, 16 * b, lane);
+        if (lo) {
+          accQ[i] = O::mma_grp(aqk, kb, accQ[i]);
+          accK[i] = O::mma_grp(ag, kb, accK[i]);
+        }
+        if (up) accK[i] = O::mma_grp(agt, kb, O::mma_grp(aqt, O::a_trans(bQ, LDK, 32 * q, 16 * b, lane), accK[i]));
+      }
     }
-    if (j == 0) sdge[r] = sdgam[r] * sGm[r] - sdd[r] * sdec[r] + rs - cs;
   }
-  __syncthreads();
+  // per-row scalars (wave 0, lane = chunk row): dgamma, the chunk-end terms on the last
+  // row, dg = reverse running sum; db, deta and the norm term of dk
   if (w == 0) {
-    // the chunk-end terms go to the last row, then dg_r = sum_{r' >= r} dgamma_r' (lane r)
-    float gcs = lane < kGT / 64 ? sred[lane] : 0.f;
-    float ddd = lane < C ? sdd[lane] * sdec[lane] : 0.f;
+    const int r = lane;
+    float v = sdgam[r] * sGm[r] - sdd[r] * sdec[r] + prow[r] + prow[C + r] -
+              (pcol[r] + pcol[C + r] + pcol[2 * C + r] + pcol[3 * C + r]);
+    float gcs = lane < kGT / 64 ? sred[lane] : 0.f, ddd = sdd[r] * sdec[r];
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
       gcs += __shfl_xor(gcs, off);
       ddd += __shfl_xor(ddd, off);
     }
-    float v = lane < C ? sdge[lane] : 0.f;
-    if (lane == C - 1) v += gcs * __expf(gC) + ddd;
+    if (r == C - 1) v += gcs * __expf(gC) + ddd;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const float u = __shfl_down(v, off);
       if (lane + off < 64) v += u;
     }
-    if (lane < C) sdge[lane] = v;
-  }
-  for (int r = t; r < C; r += kGT) {
-    const float db = sdb1[r] + sdb2[r] + sdb3[r];
+    const float db = pct[r] + pct[C + r] + pct[2 * C + r] + pct[3 * C + r] + pdb[r] + pdb[C + r];
     const float den = snrm[r] + p.eps;
     scf[r] = (p.beta_direct || r >= rows) ? 0.f : -2.f * seta[r] * db / (den * den);
-    if (r < rows) p.deta[cl.row0 + r] = p.beta_direct ? db : db / den;
+    if (r < rows) {
+      p.dg[cl.row0 + r] = v;
+      p.deta[cl.row0 + r] = p.beta_direct ? db : db / den;
+    }
   }
-  __syncthreads();
-  for (int r = t; r < rows; r += kGT) p.dg[cl.row0 + r] = sdge[r];
-  if (own) {
+  lds_barrier();  // T .. dQK are read; scf is set
+  // dQ, dK (with the norm term) staged as natural rows, then stored in 16-byte pieces
+  bf16 *sdq = reinterpret_cast<bf16 *>(smem + L::SDQ), *sdk = reinterpret_cast<bf16 *>(smem + L::SDK);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * a + 4 * lg + i;
-      if (r < rows) {
+  for (int i = 0; i < NKH; ++i) {
+    const int b = 2 * i + half;
+    if (b < NKT) {
+      const int c = 16 * b + lr;
 #pragma unroll
-        for (int ii = 0; ii < NKH; ++ii) {
-          const int b = 2 * ii + half;
-          if (b < NKT) {
-            const int c = 16 * b + lr;
-            static_cast<bf16 *>(p.dq)[(cl.row0 + r) * DK + c] = (bf16)(accQ[ii][i]);
-            static_cast<bf16 *>(p.dk)[(cl.row0 + r) * DK + c] =
-                (bf16)(fmaf(scf[r], sK[r * LK + c], accK[ii][i]));
-          }
-        }
+      for (int j = 0; j < 4; ++j) {
+        const int r = 16 * a + 4 * lg + j;
+        sdq[r * LDO + c] = (bf16)accQ[i][j];
+        sdk[r * LDO + c] = (bf16)fmaf(scf[r], (float)bK[r * LDK + O::perm(c)], accK[i][j]);
       }
+    }
+  }
+  lds_barrier();
+  constexpr int PPR = DK / 8;  // 16-byte pieces per row
+  for (int pc = t; pc < C * PPR; pc += kGT) {
+    const int r = pc / PPR, m = pc % PPR;
+    if (r < rows) {
+      const size_t e = (size_t)(cl.row0 + r) * DK + 8 * m;
+      *reinterpret_cast<uint4 *>(static_cast<bf16 *>(p.dq) + e) = *reinterpret_cast<const uint4 *>(sdq + r * LDO + 8 * m);
+      *reinterpret_cast<uint4 *>(static_cast<bf16 *>(p.dk) + e) = *reinterpret_cast<const uint4 *>(sdk + r * LDO + 8 * m);
     }
   }
 }
@@ -1419,8 +1435,11 @@ __global__ __launch_bounds__(kGT) void kla_bwd_grads2_kernel(BwdParams p) {
 template <typename E, int C, int DK>
 struct BwdLayout {
   // workspace: prep records, then chunk-start states, then chunk-end state gradients
+  // (bf16, chunk 64: no prep records; the T^T images of the forward prep kernel instead)
+  static constexpr bool kImg = std::is_same<E, bf16>::value && C == 64;
   static size_t prep_bytes(const ChunkArgs &a, int nslot) {
-    return ((size_t)a.H * nslot * PrepRec<E, C>::BYTES + 255) / 256 * 256;
+    const size_t per = kImg ? (size_t)TpLayout<bf16, 64>::PACK : PrepRec<E, C>::BYTES;
+    return ((size_t)a.H * nslot * per + 255) / 256 * 256;
   }
   static size_t state_bytes(const ChunkArgs &a, int nslot) {
     return ((size_t)a.H * nslot * DK * a.dv * sizeof(E) + 255) / 256 * 256;
@@ -1471,7 +1490,9 @@ hipError_t launch_bwd_t(const ChunkArgs &a, const ChunkBwdArgs &b, hipStream_t s
   p.nsl = a.dv / kNS;
   p.beta_direct = a.beta_direct;
   char *ws = static_cast<char *>(a.workspace);
-  p.prep = reinterpret_cast<float *>(ws);
+  constexpr bool img = BwdLayout<E, C, DK>::kImg;
+  p.prep = img ? nullptr : reinterpret_cast<float *>(ws);
+  p.timg = img ? ws : nullptr;
   const size_t pb = BwdLayout<E, C, DK>::prep_bytes(a, p.nslot), sb = BwdLayout<E, C, DK>::state_bytes(a, p.nslot);
   p.states = ws + pb;
   p.dstates = ws + pb + sb;
@@ -1483,16 +1504,18 @@ hipError_t launch_bwd_t(const ChunkArgs &a, const ChunkBwdArgs &b, hipStream_t s
   const unsigned scan_blocks = groups8 * (unsigned)(a.dv / (ns32 ? 32 : 16));
   const bool tokens = (long long)a.B * a.T > 0 && p.nslot > 0;
   if (tokens) {
-    hipLaunchKernelGGL((kla_bwd_prep_kernel<E, C, DK>), dim3((unsigned)p.nslot, (unsigned)a.H), dim3(kPT), 0, st, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if constexpr (!img) {
+      hipLaunchKernelGGL((kla_bwd_prep_kernel<E, C, DK>), dim3((unsigned)p.nslot, (unsigned)a.H), dim3(kPT), 0, st, p);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
     // the chunk-start states: the forward's pipelined prep and scan kernels in states
-    // mode (no outputs), into p.states as operand groups
+    // mode (no outputs), into p.states as operand groups (and, for bf16, the T^T images)
     ChunkArgs fa = a;
     fa.o = nullptr;
     fa.final_state = nullptr;
     fa.workspace = ws + pb + 2 * sb;
-    e = launch_chunk_states(fa, p.states, st);
+    const hipError_t e = launch_chunk_states(fa, p.states, st, img ? ws : nullptr);
     if (e != hipSuccess) return e;
   }
   if (seq_blocks > 0 && (tokens || p.ds0)) {

@@ -87,6 +87,10 @@ struct ChunkParams {
   // element x: column l & 15 of the tile; bf16 rows 16 (x >> 2) + 4 (l >> 4) +
   // (x & 3), fp32 rows 4 (l >> 4) + x, of the group).  o and sfin are unused.
   char *states;
+  // With states (bf16 prep kernel only): also the packed image of T^T, T = (I + A)^-1
+  // without the Diag(beta) of T', per (head, slot) at timg + (h * nslot + slot) *
+  // TpLayout<bf16, 64>::PACK (the gradient kernel's T), or nullptr.
+  char *timg;
 };
 
 
@@ -462,7 +466,7 @@ struct PrepWaveShape {
   static_assert(BYTES * 7 <= 160 * 1024, "seven workgroups per CU");
 };
 
-template <int DK>
+template <int DK, bool TIMG>  // TIMG: also write the T^T image (p.timg)
 __global__ __launch_bounds__(64) void kla_chunk_prep_wave_kernel(ChunkParams p) {
   using Sh = PrepWaveShape<DK>;
   using TL = TpLayout<bf16, 64>;
@@ -646,8 +650,8 @@ __global__ __launch_bounds__(64) void kla_chunk_prep_wave_kernel(ChunkParams p) 
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 
     // ---- off-diagonal blocks level by level: T_ij = -T_ii sum_m A_im T_mj ---------
+    f32x4 Toff[NB][NB];  // (live past this block only with TIMG)
     {
-      f32x4 Toff[NB][NB];
 #pragma unroll
       for (int dist = 1; dist < NB; ++dist) {
 #pragma unroll
@@ -677,6 +681,27 @@ __global__ __launch_bounds__(64) void kla_chunk_prep_wave_kernel(ChunkParams p) 
     for (int j = 0; j < TL::PACK / 1024; ++j) {
       const int pc = 64 * j + lane;
       reinterpret_cast<uint4 *>(ws)[pc] = *reinterpret_cast<const uint4 *>(R + 16 * pc);
+    }
+    if constexpr (TIMG) {
+      // the same image of T^T (no beta): the diagonal blocks from their transposed
+      // copies in Td, the off-diagonal ones from registers, the zero blocks again
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the image above is read
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd)
+        put4(16 * lg + li, 16 * lg + 4 * qd, *reinterpret_cast<const f32x4 *>(Td + (lg * 16 + li) * LDD + 4 * qd));
+      put4(16 + li, 4 * lg, zero4());
+      put4(48 + li, 32 + 4 * lg, zero4());
+#pragma unroll
+      for (int dist = 1; dist < NB; ++dist)
+#pragma unroll
+        for (int i = dist; i < NB; ++i) put4(16 * (i - dist) + li, 16 * i + 4 * lg, Toff[i][i - dist]);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      char *wt = p.timg + ((size_t)h * p.nslot + slot) * TL::PACK;
+#pragma unroll
+      for (int j = 0; j < TL::PACK / 1024; ++j) {
+        const int pc = 64 * j + lane;
+        reinterpret_cast<uint4 *>(wt)[pc] = *reinterpret_cast<const uint4 *>(R + 16 * pc);
+      }
     }
     // the LDS of this slot is reused by the next: its reads have all completed
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -1601,10 +1626,12 @@ size_t chunk_workspace_bytes(const ChunkArgs &a) {
 }
 
 template <typename E, int C, int DK, int NCT>
-static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t st, char *states = nullptr) {
+static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t st, char *states = nullptr,
+                                  char *timg = nullptr) {
   using Sh = ChunkShape<E, C, DK, NCT>;
   ChunkParams p;
   p.states = states;
+  p.timg = timg;
   p.q = a.q;
   p.k = a.k;
   p.v = a.v;
@@ -1645,7 +1672,10 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t st, char *state
       const long long total = (long long)p.nslot * a.H;
       p.pslots = (int)std::min<long long>(8, std::max<long long>(1, total / (2 * 7 * 256)));
       const unsigned runs = (unsigned)((p.nslot + p.pslots - 1) / p.pslots);
-      hipLaunchKernelGGL((kla_chunk_prep_wave_kernel<DK>), dim3(runs, (unsigned)a.H), dim3(64), 0, st, p);
+      if (timg)
+        hipLaunchKernelGGL((kla_chunk_prep_wave_kernel<DK, true>), dim3(runs, (unsigned)a.H), dim3(64), 0, st, p);
+      else
+        hipLaunchKernelGGL((kla_chunk_prep_wave_kernel<DK, false>), dim3(runs, (unsigned)a.H), dim3(64), 0, st, p);
     } else {
       // slots per workgroup: the longest run that still gives two workgroups
       // per CU (the pipeline is latency-bound; two resident workgroups overlap)
@@ -1686,15 +1716,18 @@ static bool use_two_column_tiles(const ChunkArgs &a) {
   return a.dv % 32 == 0 && (long long)a.num_seqs * a.H * (a.dv / 32) >= 256;
 }
 
-static hipError_t launch_fast(const ChunkArgs &a, hipStream_t st, char *states) {
+static hipError_t launch_fast(const ChunkArgs &a, hipStream_t st, char *states, char *timg = nullptr) {
   if (a.dtype == 0) {
     const bool two = use_two_column_tiles(a);
     if (a.dk == 128)
-      return two ? launch_chunk_t<bf16, 64, 128, 2>(a, st, states) : launch_chunk_t<bf16, 64, 128, 1>(a, st, states);
+      return two ? launch_chunk_t<bf16, 64, 128, 2>(a, st, states, timg)
+                 : launch_chunk_t<bf16, 64, 128, 1>(a, st, states, timg);
     if (a.dk == 64)
-      return two ? launch_chunk_t<bf16, 64, 64, 2>(a, st, states) : launch_chunk_t<bf16, 64, 64, 1>(a, st, states);
+      return two ? launch_chunk_t<bf16, 64, 64, 2>(a, st, states, timg)
+                 : launch_chunk_t<bf16, 64, 64, 1>(a, st, states, timg);
     return hipErrorInvalidValue;
   }
+  if (timg) return hipErrorInvalidValue;  // the T^T image comes from the bf16 prep kernel only
   if (a.chunk == 16) {
     switch (a.dk) {
       case 16: return launch_chunk_t<float, 16, 16, 1>(a, st, states);
@@ -1783,9 +1816,9 @@ hipError_t launch_chunk_rev(const ChunkArgs &a, const float *dsfin, const void *
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_chunk_states(const ChunkArgs &a, void *states, hipStream_t st) {
+hipError_t launch_chunk_states(const ChunkArgs &a, void *states, hipStream_t st, void *timg) {
   if (!fast_chunk_supported(a.dtype, a.dk, a.dv, a.chunk)) return hipErrorInvalidValue;
-  return launch_fast(a, st, static_cast<char *>(states));
+  return launch_fast(a, st, static_cast<char *>(states), static_cast<char *>(timg));
 }
 
 // ---------------------------------------------------------------------------

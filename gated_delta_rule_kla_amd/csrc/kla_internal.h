@@ -80,7 +80,9 @@ hipError_t launch_chunk_general(const ChunkArgs &a, const GenExtra &x, hipStream
 // every chunk into `states` (the layout of ChunkParams::states in
 // kla_chunk.hip; dk * dv elements of the element type per (head, slot)), no
 // outputs.  a.workspace is the forward workspace (chunk_workspace_bytes(a)).
-hipError_t launch_chunk_states(const ChunkArgs &a, void *states, hipStream_t stream);
+// timg (bf16 only, or nullptr): also the packed image of T^T per (head, slot),
+// TpLayout<bf16, 64>::PACK bytes each (ChunkParams::timg).
+hipError_t launch_chunk_states(const ChunkArgs &a, void *states, hipStream_t stream, void *timg = nullptr);
 // The reverse scan of the state gradients on the same machinery, after
 // launch_chunk_states on the same workspace: dS' of every chunk into dstates
 // (the same layout as states), dL/dS_final from dsfin (or zeros), the

@@ -323,12 +323,13 @@ def test_chunk_bwd_workspace_bytes():
                                                a["dv"], a["chunk"], a["dtype"])
 
     r256 = lambda x: (x + 255) // 256 * 256
-    # per (chunk, head): T, P and K K^T . E (C x C in the input element type) + 4 C fp32 vectors;
-    # chunk-start state and chunk-end state gradient (dk x dv each, in the input element type);
-    # B=2 x ceil(100/64)=2 chunks x H=4; then the forward's workspace (its kernels produce the
-    # chunk-start states)
+    # per (chunk, head): bf16 chunk 64 -- the packed T^T image (rows < 32 all 64 columns, rows
+    # >= 32 the last 32, bf16); otherwise T, P and K K^T . E (C x C in the input element type)
+    # + 4 C fp32 vectors; then the chunk-start state and chunk-end state gradient (dk x dv each,
+    # in the input element type); B=2 x ceil(100/64)=2 chunks x H=4; then the forward's
+    # workspace (its kernels produce the chunk-start states)
     slots = 2 * 2 * 4
-    assert ws() == r256(slots * (3 * 64 * 64 * 2 + 4 * 64 * 4)) + 2 * r256(slots * 128 * 128 * 2) + _ws_bytes()
+    assert ws() == r256(slots * (32 * 64 + 32 * 32) * 2) + 2 * r256(slots * 128 * 128 * 2) + _ws_bytes()
     assert ws(dtype=1, chunk=16, dk=32, dv=16) == (r256(2 * 7 * 4 * (3 * 16 * 16 + 4 * 16) * 4)
                                                    + 2 * r256(2 * 7 * 4 * 32 * 16 * 4)
                                                    + _ws_bytes(dtype=1, chunk=16, dk=32, dv=16))
