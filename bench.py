@@ -12,11 +12,14 @@ Also measured in the same run and reported in the same JSON line:
   * decode: 512 consecutive kla_decode_step calls, N=256 sequences x H=16,
     128x128 fp32 state (HBM-bound; reported as GB/s);
   * backward: kla_chunk_bwd on the prefill workload (steps/10 timed calls);
+  * the other prefill workloads (T=65536 dv=256; 32 packed sequences, H=32);
+  * gdn: the same kernels with the update coefficient given;
+  * pgdn: the preconditioned variant, prefill (general kernel) and decode;
   * cpu_baseline: the fp64 CPU oracle on this host's cores (a process pool),
     on the whole prefill workload and bounded samples of the others.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
-                       [--mode all|prefill|decode|backward|prefill-other]
+                       [--mode all|prefill|decode|backward|prefill-other|pgdn]
 """
 
 from __future__ import annotations
@@ -71,13 +74,15 @@ def decode_algorithmic(N, H, dk, dv):
     return N * H * per_head, N * H * 6 * dk * dv
 
 
-def recorded_traffic(profile_md, kernel_src):
+def recorded_traffic(profile_md, *kernel_srcs):
     """HBM bytes per launch from a committed rocprofv3 counter summary, or None
-    when the kernel source has changed since those counters were taken."""
+    when a kernel source has changed since those counters were taken (the
+    summary records the sha256 of the listed sources' bytes, concatenated in
+    order)."""
     import hashlib
     try:
         txt = open(os.path.join(ROOT, "profiles", profile_md)).read()
-        src = open(os.path.join(ROOT, kernel_src), "rb").read()
+        src = b"".join(open(os.path.join(ROOT, f), "rb").read() for f in kernel_srcs)
     except OSError:
         return None
     fields = dict(line.split(": ", 1) for line in txt.splitlines() if ": " in line and line[:1].isalpha())
@@ -236,6 +241,61 @@ def bench_gdn(steps, warmup, decode_steps=512):
         dstep(i % decode_steps)
     d_ms, _ = time_launches(dstep, decode_steps, stream)
     return dict(prefill_ms=p_ms, decode_ms=d_ms, tokens=B * T)
+
+
+def bench_pgdn(steps, warmup, decode_steps=64):
+    """PGDN (kla_pgdn_chunk_fwd / kla_pgdn_decode_step: the preconditioned gated
+    delta rule, coefficient given, band 1.5) on the prefill workload and the first
+    steps of the decode workload, both with unit-length keys.  The prefill runs on
+    the general chunk kernel (one workgroup per (sequence, head, 16 state
+    columns), the S-independent work redone per column slice)."""
+    import torch
+    from gated_delta_rule_kla_amd import inputs, kla
+
+    dev = torch.device("cuda:0")
+    x = inputs.unit_keys(_workload(1))
+    B, H, T, dk, dv = x.dims
+    q, k, v, g, beta = (t.to(dev) for t in (x.q, x.k, x.v, x.g, x.eta))
+    o = torch.empty((B, H, T, dv), dtype=q.dtype, device=dev)
+    S = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    A = torch.empty((B, H, dk), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def pstep(_i):
+        kla.pgdn_chunk_fwd(q, k, v, g, beta, x.eps, "given", 1.5, None, None, chunk=x.chunk, out=o,
+                           final_state=S, final_acc=A)
+
+    for i in range(warmup):
+        pstep(i)
+    p_ms, _ = time_launches(pstep, steps, stream)
+    _, p_bytes = prefill_algorithmic(B, H, T, dk, dv, x.chunk, 0, 1, B)
+    p_bytes += 4 * dk * B * H  # the final accumulator
+    del q, k, v, g, beta, o, S, A
+    d = inputs.unit_keys(_workload(3))
+    N, Hd, dkd = d.q.shape[1:]
+    dvd = d.v.shape[-1]
+    dq, dk_, dv_, dg, db = (t[:decode_steps].to(dev) for t in (d.q, d.k, d.v, d.g, d.eta))
+    st = d.state.to(dev)
+    acc = torch.zeros((N, Hd, dkd), dtype=torch.float32, device=dev)
+    do = torch.empty((N, Hd, dvd), dtype=dq.dtype, device=dev)
+
+    def dstep(i):
+        kla.pgdn_decode_step(dq[i], dk_[i], dv_[i], dg[i], db[i], d.eps, st, acc, "given", 1.5, out=do)
+
+    for i in range(16):
+        dstep(i % decode_steps)
+    d_ms, _ = time_launches(dstep, decode_steps, stream)
+    d_bytes, _ = decode_algorithmic(N, Hd, dkd, dvd)
+    d_bytes += 8 * dkd * N * Hd  # the accumulator read and written
+    del st, acc
+    torch.cuda.empty_cache()
+    return {"workload": f"PGDN (given coefficient, band 1.5, unit-length keys): prefill B={B} H={H} T={T} "
+                        f"dk={dk} dv={dv} chunk={x.chunk} bf16 through the general chunk kernel; decode "
+                        f"N={N} H={Hd} dk={dkd} dv={dvd}, {decode_steps} consecutive steps",
+            "prefill_ms_per_call": p_ms, "prefill_tokens/s": B * T / (p_ms * 1e-3),
+            "prefill_GB/s": p_bytes / p_ms / 1e6, "prefill_hbm_frac": p_bytes / p_ms / 1e6 / HBM_PEAK_GBS,
+            "decode_ms_per_step": d_ms, "decode_GB/s": d_bytes / d_ms / 1e6,
+            "decode_hbm_frac": d_bytes / d_ms / 1e6 / HBM_PEAK_GBS}
 
 
 def bench_decode_large(steps_total=64, warmup=16, N=1024):
@@ -405,7 +465,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--mode", choices=["all", "prefill", "decode", "backward", "prefill-other"], default="all")
+    ap.add_argument("--mode", choices=["all", "prefill", "decode", "backward", "prefill-other", "pgdn"],
+                    default="all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 256 MiB device copy (for HBM counter calibration)")
@@ -456,7 +517,7 @@ def main():
                          "frac": gbs / HBM_PEAK_GBS,
                          "traffic": recorded_traffic("kla_chunk_fwd_prefill_b4_h16_t4096_hbm.md",
                                                      "gated_delta_rule_kla_amd/csrc/kla_chunk.hip"),
-                         "kernel": "kla_chunk_fwd: kla_chunk_prep_kernel<bf16,64,128> then "
+                         "kernel": "kla_chunk_fwd: kla_chunk_prep_wave_kernel<128> then "
                                    "kla_chunk_kernel<bf16,64,128,2>, timed together per call",
                          "algorithmic_bytes_per_launch": p["bytes"],
                          "algorithmic_flops_per_launch": p["flops"],
@@ -496,9 +557,11 @@ def main():
                "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                             "frac": gbs / HBM_PEAK_GBS,
                             "traffic": recorded_traffic("kla_chunk_bwd_b4_h16_t4096_hbm.md",
+                                                        "gated_delta_rule_kla_amd/csrc/kla_chunk.hip",
                                                         "gated_delta_rule_kla_amd/csrc/kla_bwd.hip"),
-                            "kernel": "kla_chunk_bwd: prep, states, dstates and grads kernels timed "
-                                      "together per call",
+                            "kernel": "kla_chunk_bwd: the forward prep (with the T image) and scan "
+                                      "(states mode), the adjoint scan and the gradient kernel, "
+                                      "timed together per call",
                             "algorithmic_bytes_per_launch": bw["bytes"],
                             "algorithmic_flops_per_launch": bw["flops"]}}
         if args.mode == "backward":
@@ -507,6 +570,8 @@ def main():
         out["backward"] = bwd
     if args.mode == "prefill-other":
         out["prefill_other_workloads"] = bench_prefill_other(max(2, args.steps // 20), max(1, args.warmup // 10))
+    if args.mode in ("all", "pgdn"):
+        out["pgdn"] = bench_pgdn(max(2, args.steps // 40), 1)
     if args.mode == "all":
         out["prefill_other_workloads"] = bench_prefill_other(max(2, args.steps // 20), max(1, args.warmup // 10))
         gd = bench_gdn(args.steps, args.warmup)

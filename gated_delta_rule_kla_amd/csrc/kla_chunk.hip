@@ -758,7 +758,11 @@ struct ChunkShape {
   // sizes in bytes
   static constexpr int K_SLOT = C * LDK * (int)sizeof(E);
   static constexpr int V_SLOT = C * LDV * (int)sizeof(E);
-  static constexpr int TP_SLOT = TpLayout<E, C>::LDS_BYTES;  // T'^T image, then gamma, Gam, d
+  // T'^T image, then gamma, Gam, d; compact (rows >= 32 hold their last 32 columns only,
+  // all the T' X products read there) where four column tiles need the room
+  static constexpr bool COMPACT = NCT > 2;
+  static constexpr int TP_SLOT = COMPACT ? TpLayout<E, C>::LDS_BYTES_C : TpLayout<E, C>::LDS_BYTES;
+  static constexpr int TP_VEC = COMPACT ? TpLayout<E, C>::TP_IMG_C : TpLayout<E, C>::TP_IMG;
   static constexpr int SU_S = NCT * (DK / KG) * 64 * 16;   // chunk-start S groups, 16 B per lane
   static constexpr int SU_U = NCT * (C / KG) * 64 * 16;    // U~ groups
   static constexpr int SU_SLOT = SU_S + SU_U;
@@ -855,7 +859,7 @@ __global__ __launch_bounds__(64 * kWaves) void kla_chunk_kernel(ChunkParams p) {
   auto sTp = [&](int c) { return reinterpret_cast<E *>(smem + Sh::OFF_TP + (c & 1) * Sh::TP_SLOT); };
   // per-chunk row vectors: gamma, Gam = exp(gamma), d = exp(gamma_C - gamma)
   auto sVec = [&](int c) {
-    return reinterpret_cast<float *>(smem + Sh::OFF_TP + (c & 1) * Sh::TP_SLOT + TL::TP_IMG);
+    return reinterpret_cast<float *>(smem + Sh::OFF_TP + (c & 1) * Sh::TP_SLOT + Sh::TP_VEC);
   };
   auto sSuS = [&](int c) { return reinterpret_cast<Grp *>(smem + Sh::OFF_SU + (c & 1) * Sh::SU_SLOT); };
   auto sSuU = [&](int c) {
@@ -952,7 +956,11 @@ __global__ __launch_bounds__(64 * kWaves) void kla_chunk_kernel(ChunkParams p) {
           for (int ct = 0; ct < NCW; ++ct) u[ct][rt] = zero4();
 #pragma unroll
           for (int q = 0; q * KG < 16 * (rt + 1); ++q) {
-            const Grp a = O::a_trans(TpT, LDC, q * KG, 16 * rt, lane);
+            Grp a;
+            if (Sh::COMPACT && q * KG >= TL::RW)
+              a = O::a_trans(TpT + TL::RW * LDC, TL::LD2, q * KG - TL::RW, 16 * rt - TL::RW, lane);
+            else
+              a = O::a_trans(TpT, LDC, q * KG, 16 * rt, lane);
 #pragma unroll
             for (int ct = 0; ct < NCW; ++ct) u[ct][rt] = O::mma_grp(a, xb[ct][q], u[ct][rt]);
           }
@@ -1166,7 +1174,7 @@ __global__ __launch_bounds__(64 * kWaves) void kla_chunk_kernel(ChunkParams p) {
   } else {
     // =================== T'^T, gamma/Gam/d and the V slice of chunk i+1 ========
     // (two sets, two steps ahead, as for K, when the registers allow)
-    using TC = ImgCopy<E, C>;
+    using TC = ImgCopy<E, C, Sh::COMPACT>;
     constexpr int NSET = TC::NPL <= 20 ? 2 : 1;
     TC tin[NSET];
     VSliceLoad<E, C, DVT> vin[NSET];
@@ -1222,7 +1230,7 @@ struct RevShape {
   using F = ChunkShape<E, C, DK, NCT>;
   static constexpr int NB = F::NB, DVT = F::DVT, NCW = F::NCW, NT = F::NT;
   static constexpr int LDK = F::LDK, LDC = F::LDC, LDV = F::LDV;
-  static constexpr int K_SLOT = F::K_SLOT, V_SLOT = F::V_SLOT, TP_SLOT = F::TP_SLOT;
+  static constexpr int K_SLOT = F::K_SLOT, V_SLOT = F::V_SLOT, TP_SLOT = TpLayout<E, C>::LDS_BYTES;
   static constexpr int YP = NCT * NB * 64 * 16;  // P^T dO tiles, fp32 accumulator layout
   static constexpr int OFF_K = 0;
   static constexpr int OFF_V = OFF_K + 2 * K_SLOT;
@@ -1715,9 +1723,19 @@ bool fast_chunk_supported(int dtype, int dk, int dv, int chunk) {
 static bool use_two_column_tiles(const ChunkArgs &a) {
   return a.dv % 32 == 0 && (long long)a.num_seqs * a.H * (a.dv / 32) >= 256;
 }
+// 64 columns (four tiles) when that still leaves at least eight workgroups per CU
+// (throughput-bound grids: a step costs about 1.5x the two-tile step for twice
+// the columns, 1.94 -> 1.50 ms on 32 packed sequences x 32 heads)
+static bool use_four_column_tiles(const ChunkArgs &a) {
+  return a.dv % 64 == 0 && (long long)a.num_seqs * a.H * (a.dv / 64) >= 8 * 256;
+}
 
 static hipError_t launch_fast(const ChunkArgs &a, hipStream_t st, char *states, char *timg = nullptr) {
   if (a.dtype == 0) {
+    if (!states && use_four_column_tiles(a)) {
+      if (a.dk == 128) return launch_chunk_t<bf16, 64, 128, 4>(a, st, states, timg);
+      if (a.dk == 64) return launch_chunk_t<bf16, 64, 64, 4>(a, st, states, timg);
+    }
     const bool two = use_two_column_tiles(a);
     if (a.dk == 128)
       return two ? launch_chunk_t<bf16, 64, 128, 2>(a, st, states, timg)

@@ -281,8 +281,24 @@ struct TpLayout {
     }
     return (e / C) * LDC + e % C;
   }
-  static_assert(TP_IMG % 16 == 0 && VEC3 % 16 == 0 && PACK % 16 == 0, "align");
+  // Compact LDS image: rows >= RW keep only their last C - RW columns (rows of LD2),
+  // as in the workspace; the vectors follow it.
+  static constexpr int LD2 = C > RW ? (C - RW) + PAD : LDC;
+  static constexpr int TP_IMG_C = (RW * LDC + (C - RW) * LD2) * (int)sizeof(E);
+  static constexpr int LDS_BYTES_C = TP_IMG_C + VEC3;
+  static __device__ __forceinline__ int piece_to_lds_c(int pc) {
+    int e = pc * EPP;
+    if constexpr (C > RW) {
+      if (e >= RW * C) {
+        e -= RW * C;
+        return RW * LDC + (e / (C - RW)) * LD2 + e % (C - RW);
+      }
+    }
+    return (e / C) * LDC + e % C;
+  }
+  static_assert(TP_IMG % 16 == 0 && VEC3 % 16 == 0 && PACK % 16 == 0 && TP_IMG_C % 16 == 0, "align");
   static_assert((C - RW) % EPP == 0 && C % EPP == 0, "pieces stay inside a row");
+  static_assert((LD2 * (int)sizeof(E)) % 16 == 0, "row align");
 };
 
 // Workspace slot of chunk c of sequence n: dense batches use n * ceil(T/C) + c;
@@ -348,7 +364,7 @@ struct RowLoad {
 
 // A chunk's packed T'^T image and gamma, Gam, d from the workspace into the
 // LDS slot (image rows at their LDS positions, the vectors after the image).
-template <typename E, int C>
+template <typename E, int C, bool COMPACT = false>
 struct ImgCopy {
   using TL = TpLayout<E, C>;
   static constexpr int NI = TL::PACK / 16, NP = TL::BYTES / 16;
@@ -363,8 +379,8 @@ struct ImgCopy {
     for (int j = 0; j < NPL; ++j) {
       const int i = lane + 64 * j;
       if (NP % 64 == 0 || i < NP) {
-        char *d = i < NI ? reinterpret_cast<char *>(slot + TL::piece_to_lds(i))
-                         : reinterpret_cast<char *>(slot) + TL::TP_IMG + 16 * (i - NI);
+        char *d = i < NI ? reinterpret_cast<char *>(slot + (COMPACT ? TL::piece_to_lds_c(i) : TL::piece_to_lds(i)))
+                         : reinterpret_cast<char *>(slot) + (COMPACT ? TL::TP_IMG_C : TL::TP_IMG) + 16 * (i - NI);
         *reinterpret_cast<u32x4 *>(d) = r[j];
       }
     }

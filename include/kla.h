@@ -249,10 +249,11 @@ kla_status_t kla_gdn_decode_step(const void *q, const void *k, const void *v,
  *   dinitial_state  [N, H, dk, dv]  fp32 (written), or NULL (not computed)
  *   workspace       kla_chunk_bwd_workspace_bytes(...) bytes of device memory
  *                   (16-byte aligned), owned by the caller, no initialisation
- *                   needed; holds per (chunk, head) T = (I + A)^-1, the causal
- *                   scores and the decayed Gram matrix, the coefficient and
- *                   decay vectors (fp32), the chunk-start state and the
- *                   chunk-end state gradient (matrices and states in `dtype`).
+ *                   needed; holds per (chunk, head) T = (I + A)^-1 (BF16: as
+ *                   its packed transposed image; F32: with the causal scores,
+ *                   the decayed Gram matrix and the coefficient and decay
+ *                   vectors), the chunk-start state and the chunk-end state
+ *                   gradient (in `dtype`), then the forward's own workspace.
  *
  * Every pointer is 16-byte aligned device memory; gradient buffers must not
  * alias the inputs.  Positions of the gradient tensors that belong to no
@@ -260,10 +261,11 @@ kla_status_t kla_gdn_decode_step(const void *q, const void *k, const void *v,
  * (all checks on the host before any HIP call); the supported shapes are
  * those of kla_chunk_fwd's pipelined kernels (BF16: chunk 64, dk in {64, 128};
  * F32: chunk 16 with dk in {16, 32, 64, 128}, chunk 64 with dk in {16, 32};
- * dv a multiple of 16 in [16, 256]); others return KLA_ERR_UNSUPPORTED.  Kernels run on `stream`: a parallel per-(chunk, head) prep,
- * the forward's prep and scan kernels storing the chunk-start states, a
- * reverse scan of the state gradients, and a parallel per-(chunk, head)
- * gradient kernel.
+ * dv a multiple of 16 in [16, 256]); others return KLA_ERR_UNSUPPORTED.
+ * Kernels run on `stream`: the forward's prep and scan kernels storing the
+ * chunk-start states (BF16: the prep also writes the T image), a reverse scan
+ * of the state gradients, and a parallel per-(chunk, head) gradient kernel
+ * (F32: after a per-(chunk, head) prep of its own).
  */
 kla_status_t kla_chunk_bwd(const void *q, const void *k, const void *v,
                            const void *g, const void *eta, float eps,
@@ -291,10 +293,11 @@ kla_status_t kla_gdn_chunk_bwd(const void *q, const void *k, const void *v,
 
 /*
  * kla_chunk_bwd_workspace_bytes -- device workspace kla_chunk_bwd and
- * kla_gdn_chunk_bwd need (host-only): per (chunk, head) 3 C^2 e + 16 C bytes
- * plus 2 dk dv e bytes, e = 2 for bf16 and 4 for fp32 (rounded up per region),
- * plus kla_chunk_workspace_bytes(...) for the forward kernels that recompute
- * the chunk-start states.  0 when no workspace is needed or for arguments
+ * kla_gdn_chunk_bwd need (host-only): per (chunk, head) 6,144 bytes (BF16, the
+ * packed T image) or 3 C^2 e + 16 C bytes (F32), plus 2 dk dv e bytes, e = 2
+ * for bf16 and 4 for fp32 (rounded up per region), plus
+ * kla_chunk_workspace_bytes(...) for the forward kernels that recompute the
+ * chunk-start states.  0 when no workspace is needed or for arguments
  * kla_chunk_bwd would reject.
  */
 size_t kla_chunk_bwd_workspace_bytes(const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,

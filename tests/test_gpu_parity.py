@@ -139,6 +139,23 @@ def test_prefill_varlen_many_short_sequences(nseq):
     check_prefill(x)
 
 
+@pytest.mark.parametrize("dk", [128, 64])
+def test_prefill_four_column_tiles_packed(dk):
+    """Grids with at least eight workgroups per CU at 64 state columns each run the
+    four-tile scan (compact T'^T image in LDS): 64 packed ragged sequences x 32
+    heads x dv=128, with initial states; (sequence, head) pairs sampled across the
+    batch, every column compared."""
+    rng = np.random.default_rng(640 + dk)
+    lengths = [int(x) for x in rng.integers(1, 300, size=64)]
+    lengths[3], lengths[7] = 64, 128  # whole chunks only
+    x = inputs.make_prefill(H=32, dk=dk, dv=128, chunk=64, s0_std=0.02, lengths=lengths, seed=641 + dk,
+                            name=f"four-tiles-dk{dk}")
+    o, S = run_prefill(x)
+    pairs = [(0, 0), (3, 31), (7, 16), (63, 5)] + [(int(n), int(h)) for n, h in
+                                                   zip(rng.integers(0, 64, 8), rng.integers(0, 32, 8))]
+    _sampled(x, o, S, pairs)
+
+
 def test_prefill_no_initial_state_and_no_tokens():
     x = inputs.make_prefill(H=2, dk=128, dv=64, chunk=64, lengths=[0, 0], seed=13, name="empty")
     o, S = run_prefill(x)
