@@ -33,6 +33,7 @@
 #include "kla.h"
 #include "kla_common.h"
 #include "kla_internal.h"
+#include "kla_ops.h"
 
 namespace kla {
 
@@ -133,16 +134,53 @@ __global__ __launch_bounds__(kGenThreads) void kla_chunk_general_kernel(GenParam
   const int nch = (len + C - 1) / C;
   for (int ch = 0; ch < nch; ++ch) {
     const int r0 = ch * C, nrow = min(C, len - r0);
-    // ---- load the chunk (rows >= nrow as zeros) --------------------------------
-    for (int e = tid; e < C * DK; e += kGenThreads) {
-      const int r = e / DK, i = e % DK;
-      const bool ok = r < nrow;
-      sK[r * L::LK + i] = ok ? Elem<E>::to_f32(gk[(size_t)(r0 + r) * DK + i]) : 0.f;
-      sQ[r * L::LK + i] = ok ? Elem<E>::to_f32(gq[(size_t)(r0 + r) * DK + i]) : 0.f;
-    }
-    for (int e = tid; e < C * kGenCols; e += kGenThreads) {
-      const int r = e / kGenCols, c = e % kGenCols;
-      sV[r * L::LV + c] = r < nrow ? Elem<E>::to_f32(gv[(size_t)(r0 + r) * dv + col0 + c]) : 0.f;
+    // ---- load the chunk: 16-byte pieces, all in flight before any is stored; rows
+    // past the chunk's end read as zero through the buffer bounds ------------------
+    {
+      constexpr int EP = 16 / (int)sizeof(E);                 // elements per piece
+      constexpr int PK = C * DK / EP;                         // pieces of K (and of Q)
+      constexpr int NPK = (PK + kGenThreads - 1) / kGenThreads;
+      constexpr int PPV = kGenCols / EP;                      // pieces per V row slice
+      constexpr int PV = C * PPV;
+      constexpr int NPV = (PV + kGenThreads - 1) / kGenThreads;
+      const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(gk + (size_t)r0 * DK, nrow * DK * (int)sizeof(E));
+      const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(gq + (size_t)r0 * DK, nrow * DK * (int)sizeof(E));
+      const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(gv + (size_t)r0 * dv, nrow * dv * (int)sizeof(E));
+      uint4 kv[NPK], qv[NPK], vv[NPV];
+#pragma unroll
+      for (int m = 0; m < NPK; ++m) {
+        const int pc = min(tid + kGenThreads * m, PK - 1);
+        kv[m] = buffer_ld16(rk, pc * 16);
+        qv[m] = buffer_ld16(rq, pc * 16);
+      }
+#pragma unroll
+      for (int m = 0; m < NPV; ++m) {
+        const int pc = min(tid + kGenThreads * m, PV - 1);
+        vv[m] = buffer_ld16(rv, ((pc / PPV) * dv + col0 + (pc % PPV) * EP) * (int)sizeof(E));
+      }
+#pragma unroll
+      for (int m = 0; m < NPK; ++m) {
+        const int pc = tid + kGenThreads * m;
+        if (PK % kGenThreads == 0 || pc < PK) {
+          const int r = pc / (DK / EP), i0 = (pc % (DK / EP)) * EP;
+          const E *ke = reinterpret_cast<const E *>(&kv[m]), *qe = reinterpret_cast<const E *>(&qv[m]);
+#pragma unroll
+          for (int x = 0; x < EP; ++x) {
+            sK[r * L::LK + i0 + x] = Elem<E>::to_f32(ke[x]);
+            sQ[r * L::LK + i0 + x] = Elem<E>::to_f32(qe[x]);
+          }
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < NPV; ++m) {
+        const int pc = tid + kGenThreads * m;
+        if (PV % kGenThreads == 0 || pc < PV) {
+          const int r = pc / PPV, c0 = (pc % PPV) * EP;
+          const E *ve = reinterpret_cast<const E *>(&vv[m]);
+#pragma unroll
+          for (int x = 0; x < EP; ++x) sV[r * L::LV + c0 + x] = Elem<E>::to_f32(ve[x]);
+        }
+      }
     }
     if (tid < C) {
       sG[tid] = tid < nrow ? Elem<E>::to_f32(gg[r0 + tid]) : 0.f;
@@ -224,17 +262,24 @@ __global__ __launch_bounds__(kGenThreads) void kla_chunk_general_kernel(GenParam
     __syncthreads();
 
     // ---- T = (I + A)^-1 by forward substitution, one column per thread; T' = T Diag(beta)
+    // Thread j keeps column j of T in registers (both loops unrolled, so it is never
+    // indexed at run time) and reads the rows of A as broadcasts; four partial sums
+    // shorten the dependent chain of each row.  Entries above the diagonal come out
+    // as zero because the column's entries above row j are zero.
     if (tid < C) {
       const int j = tid;
-      for (int r = 0; r < j; ++r) sT[r * L::LC + j] = 0.f;
-      sT[j * L::LC + j] = 1.f;
-      for (int r = j + 1; r < C; ++r) {
-        float s = 0.f;
-        for (int m = j; m < r; ++m) s = fmaf(sAP[r * L::LC + m], sT[m * L::LC + j], s);
-        sT[r * L::LC + j] = -s;
+      float tc[C];
+#pragma unroll
+      for (int r = 0; r < C; ++r) {
+        float s4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < r; ++m) s4[m & 3] = fmaf(sAP[r * L::LC + m], tc[m], s4[m & 3]);
+        const float sum = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+        tc[r] = r < j ? 0.f : (r == j ? 1.f : -sum);
       }
       const float bj = sBeta[j];
-      for (int r = j; r < C; ++r) sT[r * L::LC + j] *= bj;
+#pragma unroll
+      for (int r = 0; r < C; ++r) sT[r * L::LC + j] = tc[r] * bj;
     }
     __syncthreads();
 
