@@ -455,7 +455,11 @@ struct PrepWaveShape {
   static constexpr int LDA = 24;           // bf16 rows of one transposed 16x16 off-diagonal A block
   static constexpr int LDD = 20;           // fp32 rows of the diagonal blocks (A, then T), transposed
   static constexpr int TD_BYTES = NB * 16 * LDD * 4;
-  static constexpr int IMG_BYTES = TpLayout<bf16, 64>::PACK;  // the packed T'^T image
+  // the T'^T image in LDS: the workspace's packed rows, padded by 16 bytes (rows < 32:
+  // 72 elements, rows >= 32: 40) so that a column written by 16 lanes (one row each)
+  // hits distinct banks; the copy to the workspace drops the padding
+  static constexpr int IL0 = 64 + 8, IL1 = 32 + 8;
+  static constexpr int IMG_BYTES = (32 * IL0 + 32 * IL1) * 2;
   static constexpr int R_BYTES = C * RB > IMG_BYTES + TD_BYTES ? C * RB : IMG_BYTES + TD_BYTES;
   static constexpr int OFF_TD = IMG_BYTES;                    // inside R, after the image
   static constexpr int OFF_A = R_BYTES;
@@ -608,7 +612,14 @@ __global__ __launch_bounds__(64) void kla_chunk_prep_wave_kernel(ChunkParams p) 
 
     // packed image position of T'^T[s][col], col in grouped order (perm)
     auto pk = [&](int s, int pc) {
-      return s < TL::RW ? s * C + pc : TL::RW * C + (s - TL::RW) * (C - TL::RW) + (pc - TL::RW);
+      return s < TL::RW ? s * Sh::IL0 + pc : TL::RW * Sh::IL0 + (s - TL::RW) * Sh::IL1 + (pc - TL::RW);
+    };
+    // LDS byte offset of 16-byte piece q of the packed workspace image
+    auto piece_src = [&](int q) {
+      const int e = 8 * q;
+      return 2 * (e < TL::RW * C ? (e / C) * Sh::IL0 + e % C
+                                 : TL::RW * Sh::IL0 + ((e - TL::RW * C) / (C - TL::RW)) * Sh::IL1 +
+                                       (e - TL::RW * C) % (C - TL::RW));
     };
     auto put4 = [&](int s, int col, f32x4 v) {  // four consecutive columns col..col+3 (col % 4 == 0)
       store4(img + pk(s, Ops<bf16>::perm(col)), v);
@@ -680,7 +691,7 @@ __global__ __launch_bounds__(64) void kla_chunk_prep_wave_kernel(ChunkParams p) 
 #pragma unroll
     for (int j = 0; j < TL::PACK / 1024; ++j) {
       const int pc = 64 * j + lane;
-      reinterpret_cast<uint4 *>(ws)[pc] = *reinterpret_cast<const uint4 *>(R + 16 * pc);
+      reinterpret_cast<uint4 *>(ws)[pc] = *reinterpret_cast<const uint4 *>(R + piece_src(pc));
     }
     if constexpr (TIMG) {
       // the same image of T^T (no beta): the diagonal blocks from their transposed
@@ -700,7 +711,7 @@ __global__ __launch_bounds__(64) void kla_chunk_prep_wave_kernel(ChunkParams p) 
 #pragma unroll
       for (int j = 0; j < TL::PACK / 1024; ++j) {
         const int pc = 64 * j + lane;
-        reinterpret_cast<uint4 *>(wt)[pc] = *reinterpret_cast<const uint4 *>(R + 16 * pc);
+        reinterpret_cast<uint4 *>(wt)[pc] = *reinterpret_cast<const uint4 *>(R + piece_src(pc));
       }
     }
     // the LDS of this slot is reused by the next: its reads have all completed
