@@ -149,11 +149,22 @@ float band_log(float band) { return band == 1.f ? 0.f : std::log(band); }
 
 extern "C" {
 
+size_t kla_pgdn_chunk_workspace_bytes(const int32_t *cu_seqlens, const int32_t *cu_seqlens_host, int num_seqs,
+                                      int B, int H, int T, int dk, int dv, int chunk, kla_dtype_t dtype) {
+  if (check_chunk_shapes(0.f, cu_seqlens, cu_seqlens_host, num_seqs, B, H, T, dk, dv, chunk, dtype) != KLA_OK)
+    return 0;
+  if (num_seqs == 0 || (long long)B * T == 0) return 0;
+  return kla::pgdn_workspace_bytes(chunk_args(nullptr, nullptr, nullptr, nullptr, nullptr, 0.f, nullptr, nullptr,
+                                              nullptr, cu_seqlens, num_seqs, B, H, T, dk, dv, chunk, dtype,
+                                              nullptr, 0));
+}
+
 kla_status_t kla_pgdn_chunk_fwd(const void *q, const void *k, const void *v, const void *g, const void *coef,
                                 float eps, kla_gain_t gain, float band, const float *initial_state,
                                 const float *initial_acc, void *o, float *final_state, float *final_acc,
                                 const int32_t *cu_seqlens, const int32_t *cu_seqlens_host, int num_seqs, int B,
-                                int H, int T, int dk, int dv, int chunk, kla_dtype_t dtype, void *stream) {
+                                int H, int T, int dk, int dv, int chunk, kla_dtype_t dtype, void *workspace,
+                                size_t workspace_bytes, void *stream) {
   if (dtype != KLA_DT_BF16 && dtype != KLA_DT_F32) return KLA_ERR_DTYPE;
   kla_status_t st = check_pgdn(gain, band, eps);
   if (st != KLA_OK) return st;
@@ -164,11 +175,17 @@ kla_status_t kla_pgdn_chunk_fwd(const void *q, const void *k, const void *v, con
   if (num_seqs == 0) return KLA_OK;
   if ((long long)B * T > 0 && (!q || !k || !v || !g || !coef || !o)) return KLA_ERR_NULL;
   if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(g) || misaligned(coef) || misaligned(o) ||
-      misaligned(initial_state) || misaligned(final_state) || misaligned(initial_acc) || misaligned(final_acc))
+      misaligned(initial_state) || misaligned(final_state) || misaligned(initial_acc) || misaligned(final_acc) ||
+      misaligned(workspace))
     return KLA_ERR_ALIGN;
   const kla::ChunkArgs a = chunk_args(q, k, v, g, coef, e, initial_state, o, final_state, cu_seqlens, num_seqs, B,
-                                      H, T, dk, dv, chunk, dtype, nullptr, gain == KLA_GAIN_GIVEN ? 1 : 0);
+                                      H, T, dk, dv, chunk, dtype, workspace, gain == KLA_GAIN_GIVEN ? 1 : 0);
   const kla::GenExtra x{1, band_log(band), initial_acc, final_acc};
+  if (kla::pgdn_fast_supported(dtype, dk, dv, chunk)) {
+    const size_t need = (long long)B * T > 0 ? kla::pgdn_workspace_bytes(a) : 0;
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return KLA_ERR_WORKSPACE;
+    return from_hip(kla::launch_pgdn_fast(a, x, reinterpret_cast<hipStream_t>(stream)));
+  }
   return from_hip(kla::launch_chunk_general(a, x, reinterpret_cast<hipStream_t>(stream)));
 }
 

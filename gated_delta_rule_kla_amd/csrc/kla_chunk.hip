@@ -91,7 +91,26 @@ struct ChunkParams {
   // without the Diag(beta) of T', per (head, slot) at timg + (h * nslot + slot) *
   // TpLayout<bf16, 64>::PACK (the gradient kernel's T), or nullptr.
   char *timg;
+  // PGDN (bf16, chunk 64): the write keys W = P (.) K per (head, slot), C x dk bf16 rows,
+  // written by the prep kernel and read by the scan in place of K where the state is
+  // written (the update and the causal scores); the key accumulator at each chunk's
+  // start per (head, slot), dk fp32; ln(band) of the preconditioner's squash.
+  char *pg_w;
+  float *pg_acc;
+  float band_c;
+  const float *pg_acc0;  // [N, H, dk] accumulator at each sequence's start, or nullptr (zeros)
+  float *pg_accfin;      // [N, H, dk] at each sequence's end, or nullptr
 };
+
+// PGDN's preconditioner weight of one key coordinate: accumulator a, the row's mean
+// accumulator m, c = ln(band): p = exp(c tanh(r / c)), r = ln((m + delta) / (a + delta))
+// (tanh from one exponential: 1 - 2 / (exp(2x) + 1), exact at both saturations).
+__device__ __forceinline__ float pgdn_precond(float a, float m, float c) {
+  if (c == 0.f) return 1.f;
+  const float r = __logf((m + 1e-30f) / (a + 1e-30f));
+  const float th = 1.f - 2.f / (__expf(2.f * r / c) + 1.f);
+  return __expf(c * th);
+}
 
 
 // ---------------------------------------------------------------------------
@@ -448,7 +467,7 @@ __global__ __launch_bounds__(64 * kPrepWaves) void kla_chunk_prep_kernel(ChunkPa
 // or stores that give each lane its own row cost the texture-address unit
 // several times more per instruction; with one wave per chunk that unit, not
 // the arithmetic, set the kernel's time.)
-template <int DK>
+template <int DK, bool PG = false>
 struct PrepWaveShape {
   static constexpr int C = 64, NB = 4;
   static constexpr int RB = DK * 2 + 16;   // padded K row in LDS: 16 rows hit distinct banks
@@ -464,15 +483,19 @@ struct PrepWaveShape {
   static constexpr int OFF_TD = IMG_BYTES;                    // inside R, after the image
   static constexpr int OFF_A = R_BYTES;
   static constexpr int A_BYTES = 6 * 16 * LDA * 2;
-  static constexpr int OFF_VEC = OFF_A + A_BYTES;             // ||k||^2, gamma, beta
-  static constexpr int BYTES = OFF_VEC + 3 * C * 4;
-  static_assert(IMG_BYTES % 16 == 0 && OFF_TD % 16 == 0 && OFF_A % 16 == 0 && OFF_VEC % 16 == 0, "lds align");
-  static_assert(BYTES * 7 <= 160 * 1024, "seven workgroups per CU");
+  static constexpr int OFF_VEC = OFF_A + A_BYTES;             // ||k||^2 (PGDN: k . w), gamma, beta, PGDN mean
+  static constexpr int OFF_W = OFF_VEC + 4 * C * 4;           // PGDN: the write keys, rows as K's
+  static constexpr int BYTES = OFF_W + (PG ? C * RB : 0);
+  static_assert(IMG_BYTES % 16 == 0 && OFF_TD % 16 == 0 && OFF_A % 16 == 0 && OFF_VEC % 16 == 0 &&
+                OFF_W % 16 == 0, "lds align");
+  static_assert(BYTES * (PG ? 4 : 7) <= 160 * 1024, "seven (PGDN: four) workgroups per CU");
 };
 
-template <int DK, bool TIMG>  // TIMG: also write the T^T image (p.timg)
+// TIMG: also write the T^T image (p.timg).  PG: PGDN -- the write keys W from the key
+// accumulator (p.pg_acc holds it at each chunk's start), A and beta from K W^T, W to p.pg_w.
+template <int DK, bool TIMG, bool PG>
 __global__ __launch_bounds__(64) void kla_chunk_prep_wave_kernel(ChunkParams p) {
-  using Sh = PrepWaveShape<DK>;
+  using Sh = PrepWaveShape<DK, PG>;
   using TL = TpLayout<bf16, 64>;
   using M = Mm16<bf16>;
   constexpr int C = 64, NB = 4, LDA = Sh::LDA, LDD = Sh::LDD, NQ = DK / 32, PPR = DK * 2 / 16;
@@ -526,7 +549,8 @@ __global__ __launch_bounds__(64) void kla_chunk_prep_wave_kernel(ChunkParams p) 
   float *Td = reinterpret_cast<float *>(R + Sh::OFF_TD);
   bf16 *Ablk = reinterpret_cast<bf16 *>(smem + Sh::OFF_A);
   float *sNrm = reinterpret_cast<float *>(smem + Sh::OFF_VEC);
-  float *sGam = sNrm + C, *sBet = sNrm + 2 * C;
+  float *sGam = sNrm + C, *sBet = sNrm + 2 * C, *sMean = sNrm + 3 * C;
+  char *Wt = smem + Sh::OFF_W;
 
   // the loaded K rows into the LDS tile (waits for those loads)
   auto stage = [&]() {
@@ -548,7 +572,54 @@ __global__ __launch_bounds__(64) void kla_chunk_prep_wave_kernel(ChunkParams p) 
       for (int q = 0; q < NQ; ++q)
         kf[rb][q] = *reinterpret_cast<const bf16x8 *>(R + (16 * rb + li) * Sh::RB + (32 * q + 8 * lg) * 2);
 
-    // ---- Gram tiles G[rt][st] = K_rt K_st^T (st <= rt) and the norms -----------
+    // ---- PGDN: the write keys w_r = p_r (.) k_r --------------------------------------
+    // A_r = A_start + sum_{t <= r} k_t (.) k_t per coordinate; the row's mean of A_r is
+    // (sum_i A_start,i + sum_{t <= r} ||k_t||^2) / dk, a prefix over the rows (lanes)
+    bf16x8 wf[NB][NQ];
+    if constexpr (PG) {
+      const float *a0 = p.pg_acc + ((size_t)h * p.nslot + slot) * DK;
+      float st0 = 0.f, nk = 0.f;
+#pragma unroll
+      for (int cc = 0; cc < DK / 64; ++cc) st0 += a0[lane + 64 * cc];
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) st0 += __shfl_xor(st0, off);
+#pragma unroll
+      for (int m = 0; m < DK / 8; ++m) nk += Ops<bf16>::sumsq(*reinterpret_cast<const bf16x8 *>(R + lane * Sh::RB + 16 * m));
+      sMean[lane] = (st0 + wave_inclusive_scan(nk)) * (1.f / DK);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int cc = 0; cc < DK / 64; ++cc) {
+        const int i = lane + 64 * cc;
+        float a = a0[i];
+        for (int r = 0; r < C; ++r) {
+          const float kv = (float)*reinterpret_cast<const bf16 *>(R + r * Sh::RB + 2 * i);
+          a = fmaf(kv, kv, a);
+          *reinterpret_cast<bf16 *>(Wt + r * Sh::RB + 2 * i) = (bf16)(pgdn_precond(a, sMean[r], p.band_c) * kv);
+        }
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int rb = 0; rb < NB; ++rb)
+#pragma unroll
+        for (int q = 0; q < NQ; ++q)
+          wf[rb][q] = *reinterpret_cast<const bf16x8 *>(Wt + (16 * rb + li) * Sh::RB + (32 * q + 8 * lg) * 2);
+      // W to the workspace: C rows of dk, 16-byte pieces
+      char *wg = p.pg_w + ((size_t)h * p.nslot + slot) * (C * DK * 2);
+#pragma unroll
+      for (int j = 0; j < C * DK / 8 / 64; ++j) {
+        const int pc = 64 * j + lane;
+        reinterpret_cast<uint4 *>(wg)[pc] =
+            *reinterpret_cast<const uint4 *>(Wt + (pc / (DK / 8)) * Sh::RB + (pc % (DK / 8)) * 16);
+      }
+    } else {
+#pragma unroll
+      for (int rb = 0; rb < NB; ++rb)
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) wf[rb][q] = kf[rb][q];
+    }
+
+    // ---- Gram tiles G[rt][st] = K_rt W_st^T (st <= rt; W = K outside PGDN) and the
+    // diagonal k_r . w_r (||k_r||^2) ---------------------------------------------------
     f32x4 G[NB][NB];
 #pragma unroll
     for (int rt = 0; rt < NB; ++rt)
@@ -556,7 +627,7 @@ __global__ __launch_bounds__(64) void kla_chunk_prep_wave_kernel(ChunkParams p) 
       for (int st = 0; st <= rt; ++st) {
         f32x4 acc = zero4();
 #pragma unroll
-        for (int q = 0; q < NQ; ++q) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[rt][q], kf[st][q], acc, 0, 0, 0);
+        for (int q = 0; q < NQ; ++q) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[rt][q], wf[st][q], acc, 0, 0, 0);
         G[rt][st] = acc;
       }
 #pragma unroll
@@ -740,6 +811,70 @@ __global__ __launch_bounds__(64) void kla_chunk_prep_wave_kernel(ChunkParams p) 
 }
 
 // ---------------------------------------------------------------------------
+// PGDN: the key accumulator at every chunk's start
+// ---------------------------------------------------------------------------
+// Token t's preconditioner needs A_t = A_0 + sum_{t' <= t} k_t' (.) k_t' over the whole
+// sequence ("Preconditioned DeltaNet", section 2.C).  Two small passes before the prep
+// kernel: the sum of k (.) k over each chunk's rows (all chunks at once, one thread per
+// key coordinate, coalesced row reads), then a running sum over each sequence's chunks
+// that leaves in every slot the accumulator at its chunk's start and writes the
+// sequence's final accumulator.  Slots hold chunks as in the workspace.
+template <int DK>
+__global__ __launch_bounds__(DK) void kla_pgdn_chunk_sum_kernel(ChunkParams p) {
+  constexpr int C = 64;
+  const int slot = blockIdx.x, h = blockIdx.y, i = threadIdx.x;
+  int b = 0, t0 = 0, len = p.T, c = slot;
+  if (p.cu) {
+    int lo = 0, hi = p.nseq - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (mid + min(max(p.cu[mid], 0), p.T) / C <= slot) lo = mid; else hi = mid - 1;
+    }
+    t0 = min(max(p.cu[lo], 0), p.T);
+    len = min(max(p.cu[lo + 1], t0), p.T) - t0;
+    c = slot - (lo + t0 / C);
+  } else {
+    const int nchT = (p.T + C - 1) / C;
+    b = slot / nchT;
+    c = slot % nchT;
+    if (b >= p.nseq) len = 0;
+  }
+  const int nrow = (c >= 0 && c * C < len) ? min(C, len - c * C) : 0;
+  const bf16 *gk = static_cast<const bf16 *>(p.k) +
+                   (((size_t)b * p.H + h) * (size_t)p.T + (size_t)t0 + (size_t)max(c, 0) * C) * DK;
+  float s = 0.f;
+  for (int r = 0; r < nrow; ++r) {
+    const float kv = (float)gk[(size_t)r * DK + i];
+    s = fmaf(kv, kv, s);
+  }
+  p.pg_acc[((size_t)h * p.nslot + slot) * DK + i] = s;
+}
+
+template <int DK>
+__global__ __launch_bounds__(DK) void kla_pgdn_acc_scan_kernel(ChunkParams p) {
+  constexpr int C = 64;
+  const int nh = blockIdx.x, i = threadIdx.x;
+  const int n = nh / p.H, h = nh % p.H;
+  int t0 = 0, t1 = p.T, slot0;
+  if (p.cu) {
+    t0 = min(max(p.cu[n], 0), p.T);
+    t1 = min(max(p.cu[n + 1], t0), p.T);
+    slot0 = n + t0 / C;
+  } else {
+    slot0 = n * ((p.T + C - 1) / C);
+  }
+  const int nch = (t1 - t0 + C - 1) / C;
+  float a = p.pg_acc0 ? p.pg_acc0[(size_t)nh * DK + i] : 0.f;
+  float *acc = p.pg_acc + ((size_t)h * p.nslot + slot0) * DK + i;
+  for (int c = 0; c < nch; ++c) {
+    const float s = acc[(size_t)c * DK];
+    acc[(size_t)c * DK] = a;
+    a += s;
+  }
+  if (p.pg_accfin) p.pg_accfin[(size_t)nh * DK + i] = a;
+}
+
+// ---------------------------------------------------------------------------
 // scan kernel: roles and LDS plan
 // ---------------------------------------------------------------------------
 // Waves of a workgroup.  Step i (one barrier each, i = -1 .. nch) has
@@ -750,15 +885,15 @@ __global__ __launch_bounds__(64) void kla_chunk_prep_wave_kernel(ChunkParams p) 
 //   LOADQ    Q rows of chunk i+1 into LDS
 // The P waves issue no global loads: their output stores would otherwise sit
 // in the same wait counter as the loads.  Waves w and w+4 share a SIMD.
-enum Role { CHAIN0 = 0, CHAIN1 = 1, PW0 = 2, PW1 = 3, LOADK = 4, LOADT = 5, LOADQ = 6 };
-constexpr int kWaves = 7;
+enum Role { CHAIN0 = 0, CHAIN1 = 1, PW0 = 2, PW1 = 3, LOADK = 4, LOADT = 5, LOADQ = 6, LOADW = 7 };
+constexpr int kWaves = 7;  // (PGDN: an eighth, LOADW, brings the write keys of chunk i+1)
 
-template <typename E, int C, int DK, int NCT>
+template <typename E, int C, int DK, int NCT, bool PG = false>
 struct ChunkShape {
   static constexpr int NB = C / 16;            // 16-row blocks per chunk
   static constexpr int DVT = 16 * NCT;         // state columns per workgroup
   static constexpr int NCW = (NCT + 1) / 2;    // 16-column tiles per chain wave
-  static constexpr int NT = 64 * kWaves;
+  static constexpr int NT = 64 * (kWaves + (PG ? 1 : 0));
   static constexpr int PAD = LdsPad<E>::V;
   static constexpr int LDK = DK + PAD;         // K and Q rows (grouped columns)
   static constexpr int LDC = TpLayout<E, C>::LDC;
@@ -770,8 +905,8 @@ struct ChunkShape {
   static constexpr int K_SLOT = C * LDK * (int)sizeof(E);
   static constexpr int V_SLOT = C * LDV * (int)sizeof(E);
   // T'^T image, then gamma, Gam, d; compact (rows >= 32 hold their last 32 columns only,
-  // all the T' X products read there) where four column tiles need the room
-  static constexpr bool COMPACT = NCT > 2;
+  // all the T' X products read there) where four column tiles or PGDN's write keys need the room
+  static constexpr bool COMPACT = NCT > 2 || PG;
   static constexpr int TP_SLOT = COMPACT ? TpLayout<E, C>::LDS_BYTES_C : TpLayout<E, C>::LDS_BYTES;
   static constexpr int TP_VEC = COMPACT ? TpLayout<E, C>::TP_IMG_C : TpLayout<E, C>::TP_IMG;
   static constexpr int SU_S = NCT * (DK / KG) * 64 * 16;   // chunk-start S groups, 16 B per lane
@@ -783,7 +918,11 @@ struct ChunkShape {
   static constexpr int OFF_TP = OFF_V + 2 * V_SLOT;
   static constexpr int OFF_SU = OFF_TP + 2 * TP_SLOT;
   static constexpr int OFF_Q = OFF_SU + 2 * SU_SLOT;
-  static constexpr int BYTES = OFF_Q + 2 * K_SLOT;
+  // PGDN: write-key rows, 16-byte padding (the LDS budget allows no more)
+  static constexpr int LDW = DK + 16 / (int)sizeof(E);
+  static constexpr int W_SLOT = PG ? C * LDW * (int)sizeof(E) : 0;
+  static constexpr int OFF_W = OFF_Q + 2 * K_SLOT;
+  static constexpr int BYTES = OFF_W + 2 * W_SLOT;
 
   static_assert(C == 16 || C == 64, "chunk");
   static_assert(C % KG == 0 && DK % KG == 0 && DK % Ops<E>::KSTEP == 0, "dk");
@@ -794,9 +933,9 @@ struct ChunkShape {
   static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
-template <typename E, int C, int DK, int NCT>
-__global__ __launch_bounds__(64 * kWaves) void kla_chunk_kernel(ChunkParams p) {
-  using Sh = ChunkShape<E, C, DK, NCT>;
+template <typename E, int C, int DK, int NCT, bool PG = false>
+__global__ __launch_bounds__(64 * (kWaves + (PG ? 1 : 0))) void kla_chunk_kernel(ChunkParams p) {
+  using Sh = ChunkShape<E, C, DK, NCT, PG>;
   using TL = TpLayout<E, C>;
   using O = Ops<E>;
   using Grp = typename O::Grp;
@@ -873,6 +1012,11 @@ __global__ __launch_bounds__(64 * kWaves) void kla_chunk_kernel(ChunkParams p) {
     return reinterpret_cast<float *>(smem + Sh::OFF_TP + (c & 1) * Sh::TP_SLOT + Sh::TP_VEC);
   };
   auto sSuS = [&](int c) { return reinterpret_cast<Grp *>(smem + Sh::OFF_SU + (c & 1) * Sh::SU_SLOT); };
+  // the rows the state is written with: K, or PGDN's write keys
+  auto sWk = [&](int c) {
+    return PG ? reinterpret_cast<E *>(smem + Sh::OFF_W + (c & 1) * Sh::W_SLOT) : sK(c);
+  };
+  constexpr int LDWK = PG ? Sh::LDW : LDK;
   auto sSuU = [&](int c) {
     return reinterpret_cast<Grp *>(smem + Sh::OFF_SU + (c & 1) * Sh::SU_SLOT + Sh::SU_S);
   };
@@ -991,15 +1135,16 @@ __global__ __launch_bounds__(64 * kWaves) void kla_chunk_kernel(ChunkParams p) {
             }
             dub[ct][q] = O::b_from_d(du);
           }
-        // S <- Gam_C S + K^T Diag(d) U~
+        // S <- Gam_C S + K^T Diag(d) U~  (PGDN: W^T)
         const float gC = vec[C + C - 1];
+        const E *Wk = sWk(c);
 #pragma unroll
         for (int it = 0; it < DK / 16; ++it) {
 #pragma unroll
           for (int ct = 0; ct < NCW; ++ct) accS[ct][it] = gC * accS[ct][it];
 #pragma unroll
           for (int q = 0; q < NCG; ++q) {
-            const Grp a = O::a_trans(K, LDK, q * KG, 16 * it, lane);
+            const Grp a = O::a_trans(Wk, LDWK, q * KG, 16 * it, lane);
 #pragma unroll
             for (int ct = 0; ct < NCW; ++ct) accS[ct][it] = O::mma_grp(a, dub[ct][q], accS[ct][it]);
           }
@@ -1074,7 +1219,7 @@ __global__ __launch_bounds__(64 * kWaves) void kla_chunk_kernel(ChunkParams p) {
           // ---- chunk i: P rows and Diag(Gam) Q S ----
           const int c = i;
           const E *Q = sQ(c);
-          const E *K = sK(c);
+          const E *K = sWk(c);  // the causal scores use the write keys (PGDN: W)
           const float *vec = sVec(c);
           const Grp *suS = sSuS(c);
           Grp qa[NOW1][NQG];
@@ -1089,7 +1234,7 @@ __global__ __launch_bounds__(64 * kWaves) void kla_chunk_kernel(ChunkParams p) {
             if (st > BL::at(NOWN - 1)) continue;
             Grp kb[NQG];
 #pragma unroll
-            for (int q = 0; q < NQG; ++q) kb[q] = O::a_row(K + (16 * st + li) * LDK, q * KG, lg);
+            for (int q = 0; q < NQG; ++q) kb[q] = O::a_row(K + (16 * st + li) * LDWK, q * KG, lg);
 #pragma unroll
             for (int k = 0; k < NOWN; ++k) {
               if (st > BL::at(k)) continue;
@@ -1160,6 +1305,23 @@ __global__ __launch_bounds__(64 * kWaves) void kla_chunk_kernel(ChunkParams p) {
       constexpr int S = decltype(set_c)::value;
       kin[S].put(sK(i + 1), LDK, lane, [](int, int row) { return row; });
       kin[S].issue(gk + tok0_of(clampc(i + 3)) * DK, nrow_of(clampc(i + 3)), lane);
+      lds_barrier();
+    };
+    for (int i = -1; i <= iend; i += 2) {
+      step(i, std::integral_constant<int, 0>{});
+      step(i + 1, std::integral_constant<int, 1>{});
+    }
+  } else if (PG && wave == LOADW) {
+    // =================== PGDN write keys of chunk i+1 (two sets, two steps ahead) ====
+    const E *gw = reinterpret_cast<const E *>(p.pg_w) + ((size_t)h * p.nslot + slot0) * (C * DK);
+    RowLoad<E, DK, AllBlocks<NB>> win[2];
+    win[0].issue(gw, C, lane);
+    win[1].issue(gw + (size_t)clampc(1) * (C * DK), C, lane);
+    __syncthreads();
+    auto step = [&](int i, auto set_c) {
+      constexpr int S = decltype(set_c)::value;
+      win[S].put(sWk(i + 1), Sh::LDW, lane, [](int, int row) { return row; });
+      win[S].issue(gw + (size_t)clampc(i + 3) * (C * DK), C, lane);
       lds_barrier();
     };
     for (int i = -1; i <= iend; i += 2) {
@@ -1644,13 +1806,26 @@ size_t chunk_workspace_bytes(const ChunkArgs &a) {
   return a.chunk == 16 ? workspace_bytes_t<float, 16>(a) : workspace_bytes_t<float, 64>(a);
 }
 
-template <typename E, int C, int DK, int NCT>
+struct PgArgs {
+  char *w;
+  float *acc;
+  float band_c;
+  const float *acc0;
+  float *accfin;
+};
+
+template <typename E, int C, int DK, int NCT, bool PG = false>
 static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t st, char *states = nullptr,
-                                  char *timg = nullptr) {
-  using Sh = ChunkShape<E, C, DK, NCT>;
+                                  char *timg = nullptr, const PgArgs *pg = nullptr) {
+  using Sh = ChunkShape<E, C, DK, NCT, PG>;
   ChunkParams p;
   p.states = states;
   p.timg = timg;
+  p.pg_w = pg ? pg->w : nullptr;
+  p.pg_acc = pg ? pg->acc : nullptr;
+  p.band_c = pg ? pg->band_c : 0.f;
+  p.pg_acc0 = pg ? pg->acc0 : nullptr;
+  p.pg_accfin = pg ? pg->accfin : nullptr;
   p.q = a.q;
   p.k = a.k;
   p.v = a.v;
@@ -1681,6 +1856,17 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t st, char *state
     if (e != hipSuccess) return e;
     p.order = order;
   }
+  if constexpr (PG) {
+    // the key accumulator at every chunk's start (also with no tokens: final = initial)
+    if ((long long)a.B * a.T > 0 && p.nslot > 0) {
+      hipLaunchKernelGGL((kla_pgdn_chunk_sum_kernel<DK>), dim3((unsigned)p.nslot, (unsigned)a.H), dim3(DK), 0, st, p);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((kla_pgdn_acc_scan_kernel<DK>), dim3((unsigned)p.ngroups), dim3(DK), 0, st, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if ((long long)a.B * a.T > 0 && p.nslot > 0) {
     if constexpr (std::is_same<E, bf16>::value && C == 64) {
       // bf16: one wave per run of consecutive slots of one head, each run
@@ -1691,10 +1877,12 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t st, char *state
       const long long total = (long long)p.nslot * a.H;
       p.pslots = (int)std::min<long long>(8, std::max<long long>(1, total / (2 * 7 * 256)));
       const unsigned runs = (unsigned)((p.nslot + p.pslots - 1) / p.pslots);
-      if (timg)
-        hipLaunchKernelGGL((kla_chunk_prep_wave_kernel<DK, true>), dim3(runs, (unsigned)a.H), dim3(64), 0, st, p);
+      if (p.pg_w)
+        hipLaunchKernelGGL((kla_chunk_prep_wave_kernel<DK, false, true>), dim3(runs, (unsigned)a.H), dim3(64), 0, st, p);
+      else if (timg)
+        hipLaunchKernelGGL((kla_chunk_prep_wave_kernel<DK, true, false>), dim3(runs, (unsigned)a.H), dim3(64), 0, st, p);
       else
-        hipLaunchKernelGGL((kla_chunk_prep_wave_kernel<DK, false>), dim3(runs, (unsigned)a.H), dim3(64), 0, st, p);
+        hipLaunchKernelGGL((kla_chunk_prep_wave_kernel<DK, false, false>), dim3(runs, (unsigned)a.H), dim3(64), 0, st, p);
     } else {
       // slots per workgroup: the longest run that still gives two workgroups
       // per CU (the pipeline is latency-bound; two resident workgroups overlap)
@@ -1707,7 +1895,7 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t st, char *state
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((kla_chunk_kernel<E, C, DK, NCT>), dim3((unsigned)nblk), dim3(Sh::NT), 0, st, p);
+  hipLaunchKernelGGL((kla_chunk_kernel<E, C, DK, NCT, PG>), dim3((unsigned)nblk), dim3(Sh::NT), 0, st, p);
   return hipGetLastError();
 }
 
@@ -1771,6 +1959,37 @@ static hipError_t launch_fast(const ChunkArgs &a, hipStream_t st, char *states, 
     }
   }
   return hipErrorInvalidValue;
+}
+
+// PGDN on the pipelined kernels: bf16, chunk 64, dk 64 or 128.
+bool pgdn_fast_supported(int dtype, int dk, int dv, int chunk) {
+  return dtype == 0 && chunk == 64 && (dk == 64 || dk == 128) && dv % 16 == 0 && dv >= 16 && dv <= 256;
+}
+
+// The forward workspace, then the chunk-start key accumulators (dk fp32 per (head,
+// slot)), then the write keys (C x dk bf16 per (head, slot)).
+static size_t pgdn_acc_offset(const ChunkArgs &a) { return (chunk_workspace_bytes(a) + 255) / 256 * 256; }
+static size_t pgdn_w_offset(const ChunkArgs &a) {
+  const int ns = slots_per_head(a.cu_seqlens != nullptr, a.B, a.T, a.num_seqs, 64);
+  return pgdn_acc_offset(a) + ((size_t)a.H * ns * a.dk * 4 + 255) / 256 * 256;
+}
+size_t pgdn_workspace_bytes(const ChunkArgs &a) {
+  if (!pgdn_fast_supported(a.dtype, a.dk, a.dv, a.chunk)) return 0;
+  const int ns = slots_per_head(a.cu_seqlens != nullptr, a.B, a.T, a.num_seqs, 64);
+  return pgdn_w_offset(a) + (size_t)a.H * ns * 64 * a.dk * 2;
+}
+
+hipError_t launch_pgdn_fast(const ChunkArgs &a, const GenExtra &x, hipStream_t st) {
+  if (!pgdn_fast_supported(a.dtype, a.dk, a.dv, a.chunk)) return hipErrorInvalidValue;
+  char *ws = static_cast<char *>(a.workspace);
+  const PgArgs pg{ws + pgdn_w_offset(a), reinterpret_cast<float *>(ws + pgdn_acc_offset(a)), x.band_c,
+                  x.initial_acc, x.final_acc};
+  const bool two = use_two_column_tiles(a);
+  if (a.dk == 128)
+    return two ? launch_chunk_t<bf16, 64, 128, 2, true>(a, st, nullptr, nullptr, &pg)
+               : launch_chunk_t<bf16, 64, 128, 1, true>(a, st, nullptr, nullptr, &pg);
+  return two ? launch_chunk_t<bf16, 64, 64, 2, true>(a, st, nullptr, nullptr, &pg)
+             : launch_chunk_t<bf16, 64, 64, 1, true>(a, st, nullptr, nullptr, &pg);
 }
 
 hipError_t launch_chunk_fwd(const ChunkArgs &a, hipStream_t st) {

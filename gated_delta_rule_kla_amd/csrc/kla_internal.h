@@ -75,6 +75,12 @@ hipError_t static_scratch(void **ptr);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_chunk_fwd(const ChunkArgs &a, hipStream_t stream);
 hipError_t launch_chunk_bwd(const ChunkArgs &a, const ChunkBwdArgs &b, hipStream_t stream);
+// PGDN on the pipelined prep + scan kernels (bf16, chunk 64, dk 64 or 128): its
+// device workspace (0 outside those shapes) and launch.  The workspace holds the
+// forward's (T'^T images, order), the chunk-start key accumulators and the write keys.
+bool pgdn_fast_supported(int dtype, int dk, int dv, int chunk);
+size_t pgdn_workspace_bytes(const ChunkArgs &a);
+hipError_t launch_pgdn_fast(const ChunkArgs &a, const GenExtra &x, hipStream_t stream);
 hipError_t launch_chunk_general(const ChunkArgs &a, const GenExtra &x, hipStream_t stream);
 // The forward's prep and scan kernels in states mode: the state at the start of
 // every chunk into `states` (the layout of ChunkParams::states in

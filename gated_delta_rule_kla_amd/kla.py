@@ -14,6 +14,7 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = ["chunk_fwd", "chunk_workspace_bytes", "chunk_fwd_workspace_bytes", "pgdn_chunk_fwd", "pgdn_decode_step",
+           "pgdn_chunk_workspace_bytes",
            "GAINS", "decode_step", "gdn_chunk_fwd", "gdn_decode_step", "chunk_bwd",
            "gdn_chunk_bwd", "chunk_bwd_workspace_bytes", "lib", "lib_path", "KlaError", "KLA_DT_BF16",
            "KLA_DT_F32"]
@@ -77,8 +78,10 @@ def lib() -> ctypes.CDLL:
         L.kla_chunk_fwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
         L.kla_chunk_fwd_workspace_bytes.restype = sz
         L.kla_pgdn_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, f32, i32, f32, vp, vp, vp, vp, vp, vp, vp,
-                                         i32, i32, i32, i32, i32, i32, i32, i32, vp]
+                                         i32, i32, i32, i32, i32, i32, i32, i32, vp, sz, vp]
         L.kla_pgdn_chunk_fwd.restype = i32
+        L.kla_pgdn_chunk_workspace_bytes.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, i32, i32]
+        L.kla_pgdn_chunk_workspace_bytes.restype = sz
         L.kla_pgdn_decode_step.argtypes = [vp, vp, vp, vp, vp, f32, i32, f32, vp, vp, vp,
                                            i32, i32, i32, i32, i32, vp]
         L.kla_pgdn_decode_step.restype = i32
@@ -247,6 +250,13 @@ def chunk_workspace_bytes(B: int, H: int, T: int, dk: int, dv: int, chunk: int =
         return lib().kla_chunk_workspace_bytes(ctypes.c_void_p(16), cu.data_ptr(), cu.numel() - 1, B, H, T,
                                                dk, dv, int(chunk), _DTYPES[dtype])
     return lib().kla_chunk_workspace_bytes(None, None, B, B, H, T, dk, dv, int(chunk), _DTYPES[dtype])
+
+
+def pgdn_chunk_workspace_bytes(B: int, H: int, T: int, dk: int, dv: int, chunk: int = 64,
+                               dtype: torch.dtype = torch.bfloat16) -> int:
+    """Workspace bytes kla_pgdn_chunk_fwd needs for a dense batch
+    (kla_pgdn_chunk_workspace_bytes); 0 where it runs the general kernel."""
+    return lib().kla_pgdn_chunk_workspace_bytes(None, None, B, B, H, T, dk, dv, int(chunk), _DTYPES[dtype])
 
 
 def chunk_fwd_workspace_bytes(B: int, H: int, T: int, dk: int, dv: int, chunk: int = 64,
@@ -448,14 +458,17 @@ def pgdn_chunk_fwd(
     out: Optional[torch.Tensor] = None,
     final_state: Optional[torch.Tensor] = None,
     final_acc: Optional[torch.Tensor] = None,
+    workspace: Optional[torch.Tensor] = None,
 ):
     """Preconditioned gated delta rule prefill (kla_pgdn_chunk_fwd).
 
     As chunk_fwd, with ``coef`` [B, H, T] the update coefficient beta
     (gain="given") or eta (gain="kaczmarz": beta = eta / (k . w + eps)), the
     preconditioner's band x >= 1, and the key accumulator [N, H, dk] fp32 in
-    (``initial_acc``, zeros when None) and out.  Returns (o, final_state,
-    final_acc) (the last two None unless ``output_final_state`` or given)."""
+    (``initial_acc``, zeros when None) and out.  ``workspace`` (uint8, at least
+    kla_pgdn_chunk_workspace_bytes(...) bytes) is taken from torch's caching
+    allocator when not given.  Returns (o, final_state, final_acc) (the last two
+    None unless ``output_final_state`` or given)."""
     dev = q.device
     if dev.type != "cuda":
         raise ValueError("kla.pgdn_chunk_fwd needs GPU tensors")
@@ -493,10 +506,16 @@ def pgdn_chunk_fwd(
     if final_acc is not None:
         _need(final_acc, "final_acc", torch.float32, (N, H, dk), dev)
     host_ptr = None if cu_seqlens_host is None else cu_seqlens_host.data_ptr()
+    ws_bytes = lib().kla_pgdn_chunk_workspace_bytes(_ptr(cu_seqlens), host_ptr, N, B, H, T, dk, dv, int(chunk),
+                                                    _DTYPES[dtype])
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    elif workspace.device != dev or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor on the inputs' device")
     st = lib().kla_pgdn_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(coef), float(eps), GAINS[gain],
                                   float(band), _ptr(initial_state), _ptr(initial_acc), _ptr(out), _ptr(final_state),
                                   _ptr(final_acc), _ptr(cu_seqlens), host_ptr, N, B, H, T, dk, dv, int(chunk),
-                                  _DTYPES[dtype], _stream(dev))
+                                  _DTYPES[dtype], _ptr(workspace), workspace.numel(), _stream(dev))
     _check("kla_pgdn_chunk_fwd", st)
     return out, final_state, final_acc
 

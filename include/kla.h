@@ -332,9 +332,16 @@ size_t kla_chunk_bwd_workspace_bytes(const int32_t *cu_seqlens, const int32_t *c
  *   initial_acc   [N, H, dk] fp32 accumulator before the first token, or NULL (zeros)
  *   final_acc     [N, H, dk] fp32, or NULL (not written); may alias initial_acc
  *
+ *   workspace     kla_pgdn_chunk_workspace_bytes(...) bytes of device memory
+ *                 (16-byte aligned, no initialisation needed; NULL when that is 0)
+ *
  * Supported: either dtype, chunk in {16, 64}, dk in {16, 32, 64, 128}, dv a
- * multiple of 16 in [16, 256]; runs the general kernel (no workspace).
- * KLA_ERR_PARAM for a bad gain or band; other status codes as kla_chunk_fwd.
+ * multiple of 16 in [16, 256].  BF16 with chunk 64 and dk in {64, 128} runs the
+ * pipelined prep and scan kernels (after two small passes that form the key
+ * accumulator at every chunk's start); the prep also forms the write keys into
+ * the workspace.  Every other supported shape runs the general kernel and needs
+ * no workspace.  KLA_ERR_PARAM for a bad gain or band; KLA_ERR_WORKSPACE for a
+ * missing or short workspace; other status codes as kla_chunk_fwd.
  */
 kla_status_t kla_pgdn_chunk_fwd(const void *q, const void *k, const void *v,
                                 const void *g, const void *coef, float eps,
@@ -343,7 +350,20 @@ kla_status_t kla_pgdn_chunk_fwd(const void *q, const void *k, const void *v,
                                 void *o, float *final_state, float *final_acc,
                                 const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
                                 int num_seqs, int B, int H, int T, int dk, int dv, int chunk,
-                                kla_dtype_t dtype, void *stream);
+                                kla_dtype_t dtype, void *workspace, size_t workspace_bytes,
+                                void *stream);
+
+/*
+ * kla_pgdn_chunk_workspace_bytes -- device workspace kla_pgdn_chunk_fwd needs
+ * (host-only): kla_chunk_workspace_bytes(...) plus, per (chunk, head), dk fp32
+ * (the key accumulator at the chunk's start) and chunk x dk bf16 (the write
+ * keys), each region rounded up to 256 bytes.  0 for shapes that run the
+ * general kernel, with no tokens, or for arguments kla_pgdn_chunk_fwd would
+ * reject.
+ */
+size_t kla_pgdn_chunk_workspace_bytes(const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
+                                      int num_seqs, int B, int H, int T, int dk, int dv, int chunk,
+                                      kla_dtype_t dtype);
 
 /*
  * kla_pgdn_decode_step -- one PGDN token for N sequences x H heads (the
@@ -364,7 +384,7 @@ const char *kla_status_str(kla_status_t s);
 /* ABI version of this header (incremented on any incompatible change). */
 int kla_abi_version(void);
 
-#define KLA_ABI_VERSION 7
+#define KLA_ABI_VERSION 8
 
 /* Size of kla_chunk_fwd_noalloc's fixed per-GPU scratch buffer, in bytes. */
 #define KLA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)

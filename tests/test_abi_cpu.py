@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol():
                           "kla_decode_step", "kla_status_str",
                           "kla_abi_version", "kla_gdn_chunk_fwd", "kla_gdn_decode_step", "kla_chunk_bwd",
                           "kla_gdn_chunk_bwd", "kla_chunk_bwd_workspace_bytes", "kla_chunk_fwd_noalloc",
-                          "kla_pgdn_chunk_fwd", "kla_pgdn_decode_step"}
+                          "kla_pgdn_chunk_fwd", "kla_pgdn_decode_step", "kla_pgdn_chunk_workspace_bytes"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -393,11 +393,13 @@ def test_chunk_fwd_supported_shape_set():
 
 def _pgdn(**kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, c=FAKE, eps=1e-6, gain=0, band=1.5, s0=None, a0=None, o=FAKE,
-             sf=None, af=None, cu=None, cuh=None, N=2, B=2, H=4, T=100, dk=128, dv=128, chunk=64, dtype=0)
+             sf=None, af=None, cu=None, cuh=None, N=2, B=2, H=4, T=100, dk=128, dv=128, chunk=64, dtype=0,
+             ws=None, wsb=0)
     a.update(kw)
     return kla.lib().kla_pgdn_chunk_fwd(a["q"], a["k"], a["v"], a["g"], a["c"], a["eps"], a["gain"], a["band"],
                                         a["s0"], a["a0"], a["o"], a["sf"], a["af"], a["cu"], a["cuh"], a["N"],
-                                        a["B"], a["H"], a["T"], a["dk"], a["dv"], a["chunk"], a["dtype"], None)
+                                        a["B"], a["H"], a["T"], a["dk"], a["dv"], a["chunk"], a["dtype"], a["ws"],
+                                        a["wsb"], None)
 
 
 def _pgdn_dec(**kw):
@@ -419,6 +421,24 @@ def test_pgdn_chunk_fwd_rejects(kw, code):
         assert _pgdn(N=0, B=0, **kw) == OK
         return
     assert _pgdn(**kw) == code
+
+
+def test_pgdn_workspace():
+    """bf16, chunk 64, dk 64 or 128 run the pipelined kernels: their workspace is the
+    forward's plus, per (chunk, head), dk fp32 (chunk-start key accumulator) and
+    64 x dk bf16 (write keys), each region rounded up to 256 bytes; other shapes run
+    the general kernel and need none.  A call without it fails before any launch."""
+    L = kla.lib()
+    q = lambda dk=128, dtype=0, chunk=64, T=100: L.kla_pgdn_chunk_workspace_bytes(None, None, 2, 2, 4, T, dk, 128,
+                                                                                 chunk, dtype)
+    r256 = lambda x: (x + 255) // 256 * 256
+    slots = 2 * 2 * 4
+    for dk in (128, 64):
+        assert q(dk) == r256(_ws_bytes(dk=dk)) + r256(slots * dk * 4) + slots * 64 * dk * 2
+    assert q(dtype=1) == 0 and q(chunk=16) == 0 and q(dk=32) == 0 and q(T=0) == 0
+    assert kla.pgdn_chunk_workspace_bytes(2, 4, 100, 128, 128) == q()
+    assert _pgdn() == E_WS
+    assert _pgdn(ws=FAKE, wsb=q() - 1) == E_WS
 
 
 @pytest.mark.parametrize("kw,code", [

@@ -156,6 +156,14 @@ def test_pgdn_prefill(gain, dtype, chunk, dk):
     check_pgdn(x, acc0, gain, 1.5, chunk)
 
 
+@pytest.mark.parametrize("gain", ["given", "kaczmarz"])
+def test_pgdn_prefill_two_column_tiles(gain):
+    """Enough (sequence, head) pairs for 32-column workgroups in the pipelined PGDN scan:
+    B=8 x H=16 x dv=64, bf16, chunk 64, dk 128, ragged tail."""
+    x, acc0 = _pgdn_inputs(230, B=8, H=16, T=130, dk=128, dv=64, unit=gain == "given")
+    check_pgdn(x, acc0, gain, 1.5, 64)
+
+
 def test_pgdn_prefill_varlen_no_initial_accumulator():
     x, _ = _pgdn_inputs(210, H=3, dk=128, dv=64, lengths=[0, 1, 63, 64, 65, 130, 0])
     check_pgdn(x, None, "kaczmarz", 2.0, 64)
