@@ -105,10 +105,11 @@ struct ChunkParams {
 // PGDN's preconditioner weight of one key coordinate: accumulator a, the row's mean
 // accumulator m, c = ln(band): p = exp(c tanh(r / c)), r = ln((m + delta) / (a + delta))
 // (tanh from one exponential: 1 - 2 / (exp(2x) + 1), exact at both saturations).
-__device__ __forceinline__ float pgdn_precond(float a, float m, float c) {
+__device__ __forceinline__ float pgdn_precond_l(float a, float log_m, float c) {
+  // log_m = ln(m + delta) of the row, precomputed
   if (c == 0.f) return 1.f;
-  const float r = __logf((m + 1e-30f) / (a + 1e-30f));
-  const float th = 1.f - 2.f / (__expf(2.f * r / c) + 1.f);
+  const float r = log_m - __logf(a + 1e-30f);
+  const float th = 1.f - 2.f * __builtin_amdgcn_rcpf(__expf(2.f * r / c) + 1.f);
   return __expf(c * th);
 }
 
@@ -491,8 +492,8 @@ struct PrepWaveShape {
   static_assert(BYTES * (PG ? 4 : 7) <= 160 * 1024, "seven (PGDN: four) workgroups per CU");
 };
 
-// TIMG: also write the T^T image (p.timg).  PG: PGDN -- the write keys W from the key
-// accumulator (p.pg_acc holds it at each chunk's start), A and beta from K W^T, W to p.pg_w.
+// TIMG: also write the T^T image (p.timg).  PG: PGDN -- A and beta from K W^T with the
+// write keys W of p.pg_w.
 template <int DK, bool TIMG, bool PG>
 __global__ __launch_bounds__(64) void kla_chunk_prep_wave_kernel(ChunkParams p) {
   using Sh = PrepWaveShape<DK, PG>;
@@ -549,7 +550,7 @@ __global__ __launch_bounds__(64) void kla_chunk_prep_wave_kernel(ChunkParams p) 
   float *Td = reinterpret_cast<float *>(R + Sh::OFF_TD);
   bf16 *Ablk = reinterpret_cast<bf16 *>(smem + Sh::OFF_A);
   float *sNrm = reinterpret_cast<float *>(smem + Sh::OFF_VEC);
-  float *sGam = sNrm + C, *sBet = sNrm + 2 * C, *sMean = sNrm + 3 * C;
+  float *sGam = sNrm + C, *sBet = sNrm + 2 * C;
   char *Wt = smem + Sh::OFF_W;
 
   // the loaded K rows into the LDS tile (waits for those loads)
@@ -563,6 +564,22 @@ __global__ __launch_bounds__(64) void kla_chunk_prep_wave_kernel(ChunkParams p) 
   // everything else for one slot, from the staged K rows and its g, eta
   auto process = [&](int slot, int nrow, unsigned short graw, unsigned short eraw) {
     char *ws = p.ws + ((size_t)h * p.nslot + slot) * TL::BYTES;
+    if constexpr (PG) {
+      // PGDN: the chunk's write keys (kla_pgdn_wkeys_kernel wrote them) into their LDS tile
+      // (four 16-byte pieces in flight at a time: a whole-tile register array spills)
+      const uint4 *wg = reinterpret_cast<const uint4 *>(p.pg_w + ((size_t)h * p.nslot + slot) * (C * DK * 2));
+      auto wput = [&](int pc, uint4 v) {
+        *reinterpret_cast<uint4 *>(Wt + (pc / (DK / 8)) * Sh::RB + (pc % (DK / 8)) * 16) = v;
+      };
+      for (int j = 0; j < C * DK / 8 / 64; j += 4) {
+        const uint4 w0 = wg[64 * j + lane], w1 = wg[64 * (j + 1) + lane];
+        const uint4 w2 = wg[64 * (j + 2) + lane], w3 = wg[64 * (j + 3) + lane];
+        wput(64 * j + lane, w0);
+        wput(64 * (j + 1) + lane, w1);
+        wput(64 * (j + 2) + lane, w2);
+        wput(64 * (j + 3) + lane, w3);
+      }
+    }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     // operand layout: lane supplies row 16 rb + li, columns 32 q + 8 lg .. + 7
     bf16x8 kf[NB][NQ];
@@ -572,45 +589,14 @@ __global__ __launch_bounds__(64) void kla_chunk_prep_wave_kernel(ChunkParams p) 
       for (int q = 0; q < NQ; ++q)
         kf[rb][q] = *reinterpret_cast<const bf16x8 *>(R + (16 * rb + li) * Sh::RB + (32 * q + 8 * lg) * 2);
 
-    // ---- PGDN: the write keys w_r = p_r (.) k_r --------------------------------------
-    // A_r = A_start + sum_{t <= r} k_t (.) k_t per coordinate; the row's mean of A_r is
-    // (sum_i A_start,i + sum_{t <= r} ||k_t||^2) / dk, a prefix over the rows (lanes)
+    // ---- PGDN: the write keys of the chunk (staged above) as operands ----------------
     bf16x8 wf[NB][NQ];
     if constexpr (PG) {
-      const float *a0 = p.pg_acc + ((size_t)h * p.nslot + slot) * DK;
-      float st0 = 0.f, nk = 0.f;
-#pragma unroll
-      for (int cc = 0; cc < DK / 64; ++cc) st0 += a0[lane + 64 * cc];
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) st0 += __shfl_xor(st0, off);
-#pragma unroll
-      for (int m = 0; m < DK / 8; ++m) nk += Ops<bf16>::sumsq(*reinterpret_cast<const bf16x8 *>(R + lane * Sh::RB + 16 * m));
-      sMean[lane] = (st0 + wave_inclusive_scan(nk)) * (1.f / DK);
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-      for (int cc = 0; cc < DK / 64; ++cc) {
-        const int i = lane + 64 * cc;
-        float a = a0[i];
-        for (int r = 0; r < C; ++r) {
-          const float kv = (float)*reinterpret_cast<const bf16 *>(R + r * Sh::RB + 2 * i);
-          a = fmaf(kv, kv, a);
-          *reinterpret_cast<bf16 *>(Wt + r * Sh::RB + 2 * i) = (bf16)(pgdn_precond(a, sMean[r], p.band_c) * kv);
-        }
-      }
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
       for (int rb = 0; rb < NB; ++rb)
 #pragma unroll
         for (int q = 0; q < NQ; ++q)
           wf[rb][q] = *reinterpret_cast<const bf16x8 *>(Wt + (16 * rb + li) * Sh::RB + (32 * q + 8 * lg) * 2);
-      // W to the workspace: C rows of dk, 16-byte pieces
-      char *wg = p.pg_w + ((size_t)h * p.nslot + slot) * (C * DK * 2);
-#pragma unroll
-      for (int j = 0; j < C * DK / 8 / 64; ++j) {
-        const int pc = 64 * j + lane;
-        reinterpret_cast<uint4 *>(wg)[pc] =
-            *reinterpret_cast<const uint4 *>(Wt + (pc / (DK / 8)) * Sh::RB + (pc % (DK / 8)) * 16);
-      }
     } else {
 #pragma unroll
       for (int rb = 0; rb < NB; ++rb)
@@ -820,9 +806,10 @@ __global__ __launch_bounds__(64) void kla_chunk_prep_wave_kernel(ChunkParams p) 
 // that leaves in every slot the accumulator at its chunk's start and writes the
 // sequence's final accumulator.  Slots hold chunks as in the workspace.
 template <int DK>
-__global__ __launch_bounds__(DK) void kla_pgdn_chunk_sum_kernel(ChunkParams p) {
-  constexpr int C = 64;
-  const int slot = blockIdx.x, h = blockIdx.y, i = threadIdx.x;
+__global__ __launch_bounds__(128) void kla_pgdn_chunk_sum_kernel(ChunkParams p) {
+  constexpr int C = 64, NT = 128, PPR = DK / 8, RPI = NT / PPR;  // pieces per row, rows per instruction
+  __shared__ float red[RPI][DK];
+  const int slot = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
   int b = 0, t0 = 0, len = p.T, c = slot;
   if (p.cu) {
     int lo = 0, hi = p.nseq - 1;
@@ -842,12 +829,28 @@ __global__ __launch_bounds__(DK) void kla_pgdn_chunk_sum_kernel(ChunkParams p) {
   const int nrow = (c >= 0 && c * C < len) ? min(C, len - c * C) : 0;
   const bf16 *gk = static_cast<const bf16 *>(p.k) +
                    (((size_t)b * p.H + h) * (size_t)p.T + (size_t)t0 + (size_t)max(c, 0) * C) * DK;
-  float s = 0.f;
-  for (int r = 0; r < nrow; ++r) {
-    const float kv = (float)gk[(size_t)r * DK + i];
-    s = fmaf(kv, kv, s);
+  // thread t: coordinates 8 (t % PPR) .. +7 of rows t / PPR + RPI m (16-byte pieces, rows
+  // past the chunk's end read as zero)
+  const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(gk, nrow * DK * 2);
+  uint4 kv[C / RPI];
+#pragma unroll
+  for (int m = 0; m < C / RPI; ++m) kv[m] = buffer_ld16(rk, (t + NT * m) * 16);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int m = 0; m < C / RPI; ++m) {
+    const bf16x8 e = __builtin_bit_cast(bf16x8, kv[m]);
+#pragma unroll
+    for (int x = 0; x < 8; ++x) acc[x] = fmaf((float)e[x], (float)e[x], acc[x]);
   }
-  p.pg_acc[((size_t)h * p.nslot + slot) * DK + i] = s;
+#pragma unroll
+  for (int x = 0; x < 8; ++x) red[t / PPR][8 * (t % PPR) + x] = acc[x];
+  __syncthreads();
+  if (t < DK) {
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < RPI; ++j) s += red[j][t];
+    p.pg_acc[((size_t)h * p.nslot + slot) * DK + t] = s;
+  }
 }
 
 template <int DK>
@@ -866,12 +869,126 @@ __global__ __launch_bounds__(DK) void kla_pgdn_acc_scan_kernel(ChunkParams p) {
   const int nch = (t1 - t0 + C - 1) / C;
   float a = p.pg_acc0 ? p.pg_acc0[(size_t)nh * DK + i] : 0.f;
   float *acc = p.pg_acc + ((size_t)h * p.nslot + slot0) * DK + i;
-  for (int c = 0; c < nch; ++c) {
-    const float s = acc[(size_t)c * DK];
-    acc[(size_t)c * DK] = a;
-    a += s;
+  for (int c0 = 0; c0 < nch; c0 += 16) {  // 16 chunk sums in flight at a time
+    float sv[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) sv[j] = c0 + j < nch ? acc[(size_t)(c0 + j) * DK] : 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (c0 + j < nch) acc[(size_t)(c0 + j) * DK] = a;
+      a += sv[j];
+    }
   }
   if (p.pg_accfin) p.pg_accfin[(size_t)nh * DK + i] = a;
+}
+
+// The write keys of one chunk (one workgroup of four waves per (chunk, head)): with
+// A_start the accumulator at the chunk's start, A_r = A_start + sum_{t <= r} k_t (.) k_t
+// per coordinate (each thread walks 32 rows of one coordinate) and the row's mean of A_r
+// from the prefix of ||k_t||^2; w_r,i = p(A_r,i, mean_r) k_r,i, written as C rows of dk
+// bf16 (rows past the chunk's end are zero).
+template <int DK>
+struct WkeysShape {
+  static constexpr int C = 64, NT = 256;
+  static constexpr int OFF_K = 0;                      // K rows, bf16 (then W)
+  static constexpr int OFF_V = C * DK * 2;             // norms, then ln of the row means; start sum
+  static constexpr int OFF_T = OFF_V + (C + 4) * 4;    // per coordinate: sum of squares of rows 0..31
+  static constexpr int BYTES = OFF_T + DK * 4;
+};
+
+template <int DK>
+__global__ __launch_bounds__(256) void kla_pgdn_wkeys_kernel(ChunkParams p) {
+  using Sh = WkeysShape<DK>;
+  constexpr int C = 64, NT = Sh::NT;
+  __shared__ __attribute__((aligned(16))) char smem[Sh::BYTES];
+  bf16 *sk = reinterpret_cast<bf16 *>(smem + Sh::OFF_K);
+  float *sv = reinterpret_cast<float *>(smem + Sh::OFF_V);
+  float *stot = reinterpret_cast<float *>(smem + Sh::OFF_T);
+  const int slot = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
+  int b = 0, t0 = 0, len = p.T, c = slot;
+  if (p.cu) {
+    int lo = 0, hi = p.nseq - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (mid + min(max(p.cu[mid], 0), p.T) / C <= slot) lo = mid; else hi = mid - 1;
+    }
+    t0 = min(max(p.cu[lo], 0), p.T);
+    len = min(max(p.cu[lo + 1], t0), p.T) - t0;
+    c = slot - (lo + t0 / C);
+  } else {
+    const int nchT = (p.T + C - 1) / C;
+    b = slot / nchT;
+    c = slot % nchT;
+    if (b >= p.nseq) len = 0;
+  }
+  const int nrow = (c >= 0 && c * C < len) ? min(C, len - c * C) : 0;
+  if (nrow == 0) return;  // uniform: no chunk in this slot
+  const bf16 *gk = static_cast<const bf16 *>(p.k) +
+                   (((size_t)b * p.H + h) * (size_t)p.T + (size_t)t0 + (size_t)c * C) * DK;
+  const float *a0 = p.pg_acc + ((size_t)h * p.nslot + slot) * DK;
+  // K rows (16-byte pieces; rows past the end as zero)
+  {
+    const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(gk, nrow * DK * 2);
+    constexpr int NP = C * DK / 8 / NT;
+    uint4 kv[NP];
+#pragma unroll
+    for (int j = 0; j < NP; ++j) kv[j] = buffer_ld16(rk, (t + NT * j) * 16);
+#pragma unroll
+    for (int j = 0; j < NP; ++j) reinterpret_cast<uint4 *>(sk)[t + NT * j] = kv[j];
+  }
+  __syncthreads();
+  // row norms (four threads per row) and the start accumulator's sum
+  {
+    const int r = t >> 2, part = t & 3;
+    float nk = 0.f;
+#pragma unroll
+    for (int m = 0; m < DK / 32; ++m)
+      nk += Ops<bf16>::sumsq(*reinterpret_cast<const bf16x8 *>(sk + r * DK + 8 * (part + 4 * m)));
+    nk += __shfl_xor(nk, 1);
+    nk += __shfl_xor(nk, 2);
+    if (part == 0) sv[r] = nk;
+    if (t < 64) {
+      float s0 = 0.f;
+#pragma unroll
+      for (int m = 0; m < DK / 64; ++m) s0 += a0[t + 64 * m];
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) s0 += __shfl_xor(s0, off);
+      if (t == 0) sv[C] = s0;
+    }
+    for (int i = t; i < DK; i += NT) {  // the first half's rows per coordinate (K still intact)
+      float a = 0.f;
+#pragma unroll 8
+      for (int r = 0; r < 32; ++r) {
+        const float kv = (float)sk[r * DK + i];
+        a = fmaf(kv, kv, a);
+      }
+      stot[i] = a;
+    }
+  }
+  __syncthreads();
+  if (t < 64) {  // ln of the row means: (start sum + prefix of the norms) / dk, lane = row
+    const float m = (sv[C] + wave_inclusive_scan(sv[t])) * (1.f / DK);
+    sv[t] = __logf(m + 1e-30f);
+  }
+  __syncthreads();
+  // thread (coordinate i, half hf) walks its 32 rows with the accumulator in a register
+  // (the second half starts from the first half's total) and replaces k by w in place
+  for (int e = t; e < 2 * DK; e += NT) {
+    const int i = e % DK, hf = e / DK;
+    const float a00 = a0[i];
+    float a = hf ? a00 + stot[i] : a00;
+#pragma unroll 4
+    for (int r = 32 * hf; r < 32 * hf + 32; ++r) {
+      const float kv = (float)sk[r * DK + i];
+      a = fmaf(kv, kv, a);
+      sk[r * DK + i] = (bf16)(pgdn_precond_l(a, sv[r], p.band_c) * kv);
+    }
+  }
+  __syncthreads();
+  char *wg = p.pg_w + ((size_t)h * p.nslot + slot) * (C * DK * 2);
+#pragma unroll
+  for (int j = 0; j < C * DK / 8 / NT; ++j)
+    reinterpret_cast<uint4 *>(wg)[t + NT * j] = reinterpret_cast<const uint4 *>(sk)[t + NT * j];
 }
 
 // ---------------------------------------------------------------------------
@@ -1859,13 +1976,18 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t st, char *state
   if constexpr (PG) {
     // the key accumulator at every chunk's start (also with no tokens: final = initial)
     if ((long long)a.B * a.T > 0 && p.nslot > 0) {
-      hipLaunchKernelGGL((kla_pgdn_chunk_sum_kernel<DK>), dim3((unsigned)p.nslot, (unsigned)a.H), dim3(DK), 0, st, p);
+      hipLaunchKernelGGL((kla_pgdn_chunk_sum_kernel<DK>), dim3((unsigned)p.nslot, (unsigned)a.H), dim3(128), 0, st, p);
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL((kla_pgdn_acc_scan_kernel<DK>), dim3((unsigned)p.ngroups), dim3(DK), 0, st, p);
-    const hipError_t e = hipGetLastError();
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if ((long long)a.B * a.T > 0 && p.nslot > 0) {
+      hipLaunchKernelGGL((kla_pgdn_wkeys_kernel<DK>), dim3((unsigned)p.nslot, (unsigned)a.H), dim3(256), 0, st, p);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
   }
   if ((long long)a.B * a.T > 0 && p.nslot > 0) {
     if constexpr (std::is_same<E, bf16>::value && C == 64) {

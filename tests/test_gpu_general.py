@@ -149,7 +149,7 @@ def check_pgdn(x, acc0, gain, band, chunk):
 
 
 @pytest.mark.parametrize("gain", ["given", "kaczmarz"])
-@pytest.mark.parametrize("dtype,chunk,dk", [(torch.bfloat16, 64, 128), (torch.bfloat16, 16, 64),
+@pytest.mark.parametrize("dtype,chunk,dk", [(torch.bfloat16, 64, 128), (torch.bfloat16, 64, 64), (torch.bfloat16, 16, 64),
                                              (torch.float32, 64, 32), (torch.float32, 16, 128)])
 def test_pgdn_prefill(gain, dtype, chunk, dk):
     x, acc0 = _pgdn_inputs(200 + dk + chunk, dk=dk, dtype=dtype, unit=gain == "given")
