@@ -102,16 +102,6 @@ struct ChunkParams {
   float *pg_accfin;      // [N, H, dk] at each sequence's end, or nullptr
 };
 
-// PGDN's preconditioner weight of one key coordinate: accumulator a, the row's mean
-// accumulator m, c = ln(band): p = exp(c tanh(r / c)), r = ln((m + delta) / (a + delta))
-// (tanh from one exponential: 1 - 2 / (exp(2x) + 1), exact at both saturations).
-__device__ __forceinline__ float pgdn_precond_l(float a, float log_m, float c) {
-  // log_m = ln(m + delta) of the row, precomputed
-  if (c == 0.f) return 1.f;
-  const float r = log_m - __logf(a + 1e-30f);
-  const float th = 1.f - 2.f * __builtin_amdgcn_rcpf(__expf(2.f * r / c) + 1.f);
-  return __expf(c * th);
-}
 
 
 // ---------------------------------------------------------------------------

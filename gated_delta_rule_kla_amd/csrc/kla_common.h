@@ -33,4 +33,18 @@ template <> struct Elem<float> {
 __device__ __forceinline__ uint4 ldg16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
 __device__ __forceinline__ void stg16(void *p, uint4 v) { *reinterpret_cast<uint4 *>(p) = v; }
 
+// PGDN's preconditioner weight of one key coordinate ("Preconditioned DeltaNet",
+// §2.C: the inverse of the accumulated diagonal key moments, squashed in log space
+// into [1/band, band]): with the coordinate's accumulator a, log_m = ln(m + delta) of
+// the mean accumulator over the coordinates and c = ln(band),
+//   p = exp(c tanh(r / c)),  r = ln((m + delta) / (a + delta)),  delta = 1e-30,
+// tanh from one exponential, 1 - 2 / (exp(2x) + 1), exact at both saturations;
+// c = 0 (band 1) gives p = 1.
+__device__ __forceinline__ float pgdn_precond_l(float a, float log_m, float c) {
+  if (c == 0.f) return 1.f;
+  const float r = log_m - __logf(a + 1e-30f);
+  const float th = 1.f - 2.f * __builtin_amdgcn_rcpf(__expf(2.f * r / c) + 1.f);
+  return __expf(c * th);
+}
+
 }  // namespace kla

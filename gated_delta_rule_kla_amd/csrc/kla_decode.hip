@@ -18,6 +18,12 @@
 // full row, so each load/store instruction of a wave touches whole contiguous
 // rows.  Partial dot products are reduced across row groups with lane
 // shuffles inside a wave and through LDS across waves.
+//
+// With PG the same step is PGDN's ("Preconditioned DeltaNet", §2.C-2.D): the key
+// accumulator A += k (.) k (fp32, [N, H, dk], updated in place), the write key
+// w = p(A) (.) k, beta = eta (given) or eta / (k.w + eps), and
+//   o = alpha y_q + beta (w.q) e,   S = alpha S + beta w e^T
+// (the residual is still read with k).
 #include "kla_common.h"
 #include "kla_internal.h"
 
@@ -37,17 +43,19 @@ struct DecodeShape {
   static_assert(TPR <= 64 && RG * TPR == NT && RPT * RG == DK, "decode tiling");
 };
 
-template <typename E, int DK, int DV>
+template <typename E, int DK, int DV, bool PG = false>
 __global__ __launch_bounds__(decode_threads(DK, DV)) void kla_decode_kernel(
     const E *__restrict__ q, const E *__restrict__ k, const E *__restrict__ v,
     const E *__restrict__ g, const E *__restrict__ eta, float eps, int beta_direct, float *__restrict__ state,
-    E *__restrict__ o) {
+    E *__restrict__ o, float *__restrict__ acc = nullptr, float band_c = 0.f) {
   using Sh = DecodeShape<DK, DV>;
   constexpr int TPR = Sh::TPR, RG = Sh::RG, RPT = Sh::RPT, NW = Sh::NW;
-  constexpr int NRED = 10;  // y_k[4], y_q[4], k.k, k.q
+  constexpr int NRED = 10;  // y_k[4], y_q[4], k.w, w.q  (w = k outside PGDN)
 
   __shared__ float s_k[DK];
   __shared__ float s_q[DK];
+  __shared__ float s_w[PG ? DK : 1];
+  __shared__ float s_m[NW];
   __shared__ float s_red[NW > 1 ? NW : 1][TPR][NRED];
 
   const size_t nh = blockIdx.x;
@@ -72,6 +80,38 @@ __global__ __launch_bounds__(decode_threads(DK, DV)) void kla_decode_kernel(
   const float alpha = __expf(Elem<E>::to_f32(g[nh]));
   const float et = Elem<E>::to_f32(eta[nh]);
 
+  if constexpr (PG) {
+    // the accumulator, its mean over the coordinates, and the write key
+    constexpr int NA = (DK + Sh::NT - 1) / Sh::NT;
+    float av[NA], kk[NA], part = 0.f;
+#pragma unroll
+    for (int j = 0; j < NA; ++j) {
+      const int i = t + Sh::NT * j;
+      av[j] = 0.f;
+      kk[j] = 0.f;
+      if (i < DK) {
+        kk[j] = Elem<E>::to_f32(k[nh * DK + i]);
+        av[j] = fmaf(kk[j], kk[j], acc[nh * DK + i]);
+        part += av[j];
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off);
+    if ((t & 63) == 0) s_m[t >> 6] = part;
+    __syncthreads();
+    float tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) tot += s_m[w];
+    const float log_m = __logf(tot * (1.f / DK) + 1e-30f);
+#pragma unroll
+    for (int j = 0; j < NA; ++j) {
+      const int i = t + Sh::NT * j;
+      if (i < DK) {
+        s_w[i] = pgdn_precond_l(av[j], log_m, band_c) * kk[j];
+        acc[nh * DK + i] = av[j];
+      }
+    }
+  }
   __syncthreads();
 
   float red[NRED];
@@ -80,13 +120,14 @@ __global__ __launch_bounds__(decode_threads(DK, DV)) void kla_decode_kernel(
 #pragma unroll
   for (int p = 0; p < RPT; ++p) {
     const float kr = s_k[rg + RG * p], qr = s_q[rg + RG * p];
+    const float wr = PG ? s_w[rg + RG * p] : kr;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       red[c] = fmaf(s[p][c], kr, red[c]);
       red[4 + c] = fmaf(s[p][c], qr, red[4 + c]);
     }
-    red[8] = fmaf(kr, kr, red[8]);
-    red[9] = fmaf(kr, qr, red[9]);
+    red[8] = fmaf(kr, wr, red[8]);
+    red[9] = fmaf(wr, qr, red[9]);
   }
   // reduce over the row groups inside the wave (lanes TPR apart)
 #pragma unroll
@@ -120,7 +161,7 @@ __global__ __launch_bounds__(decode_threads(DK, DV)) void kla_decode_kernel(
   }
 #pragma unroll
   for (int p = 0; p < RPT; ++p) {
-    const float bk = beta * s_k[rg + RG * p];
+    const float bk = beta * (PG ? s_w[rg + RG * p] : s_k[rg + RG * p]);
     f32x4 n;
 #pragma unroll
     for (int c = 0; c < 4; ++c) n[c] = fmaf(alpha, s[p][c], bk * e[c]);
@@ -133,11 +174,17 @@ __global__ __launch_bounds__(decode_threads(DK, DV)) void kla_decode_kernel(
 }
 
 template <typename E, int DK, int DV>
-static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t st) {
+static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t st, float *acc = nullptr,
+                                  float band_c = 0.f) {
   const unsigned nblk = (unsigned)((size_t)a.N * a.H);
-  hipLaunchKernelGGL((kla_decode_kernel<E, DK, DV>), dim3(nblk), dim3(DecodeShape<DK, DV>::NT), 0,
-                     st, (const E *)a.q, (const E *)a.k, (const E *)a.v, (const E *)a.g,
-                     (const E *)a.eta, a.eps, a.beta_direct, a.state, (E *)a.o);
+  if (acc)
+    hipLaunchKernelGGL((kla_decode_kernel<E, DK, DV, true>), dim3(nblk), dim3(DecodeShape<DK, DV>::NT), 0,
+                       st, (const E *)a.q, (const E *)a.k, (const E *)a.v, (const E *)a.g,
+                       (const E *)a.eta, a.eps, a.beta_direct, a.state, (E *)a.o, acc, band_c);
+  else
+    hipLaunchKernelGGL((kla_decode_kernel<E, DK, DV, false>), dim3(nblk), dim3(DecodeShape<DK, DV>::NT), 0,
+                       st, (const E *)a.q, (const E *)a.k, (const E *)a.v, (const E *)a.g,
+                       (const E *)a.eta, a.eps, a.beta_direct, a.state, (E *)a.o, nullptr, 0.f);
   return hipGetLastError();
 }
 
@@ -157,32 +204,39 @@ bool decode_supported(int dtype, int dk, int dv) {
 }
 
 template <typename E, int DK>
-static hipError_t dispatch_dv(const DecodeArgs &a, hipStream_t st) {
+static hipError_t dispatch_dv(const DecodeArgs &a, hipStream_t st, float *acc, float band_c) {
   switch (a.dv) {
-    case 16: return launch_decode_t<E, DK, 16>(a, st);
-    case 32: return launch_decode_t<E, DK, 32>(a, st);
-    case 64: return launch_decode_t<E, DK, 64>(a, st);
-    case 128: return launch_decode_t<E, DK, 128>(a, st);
-    case 256: return launch_decode_t<E, DK, 256>(a, st);
+    case 16: return launch_decode_t<E, DK, 16>(a, st, acc, band_c);
+    case 32: return launch_decode_t<E, DK, 32>(a, st, acc, band_c);
+    case 64: return launch_decode_t<E, DK, 64>(a, st, acc, band_c);
+    case 128: return launch_decode_t<E, DK, 128>(a, st, acc, band_c);
+    case 256: return launch_decode_t<E, DK, 256>(a, st, acc, band_c);
   }
   return hipErrorInvalidValue;
 }
 
 template <typename E>
-static hipError_t dispatch_dk(const DecodeArgs &a, hipStream_t st) {
+static hipError_t dispatch_dk(const DecodeArgs &a, hipStream_t st, float *acc, float band_c) {
   switch (a.dk) {
-    case 16: return dispatch_dv<E, 16>(a, st);
-    case 32: return dispatch_dv<E, 32>(a, st);
-    case 64: return dispatch_dv<E, 64>(a, st);
-    case 128: return dispatch_dv<E, 128>(a, st);
-    case 256: return dispatch_dv<E, 256>(a, st);
+    case 16: return dispatch_dv<E, 16>(a, st, acc, band_c);
+    case 32: return dispatch_dv<E, 32>(a, st, acc, band_c);
+    case 64: return dispatch_dv<E, 64>(a, st, acc, band_c);
+    case 128: return dispatch_dv<E, 128>(a, st, acc, band_c);
+    case 256: return dispatch_dv<E, 256>(a, st, acc, band_c);
   }
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t st) {
-  if (a.dtype == 0) return dispatch_dk<bf16>(a, st);
-  return dispatch_dk<float>(a, st);
+  if (a.dtype == 0) return dispatch_dk<bf16>(a, st, nullptr, 0.f);
+  return dispatch_dk<float>(a, st, nullptr, 0.f);
+}
+
+// PGDN's step on the same kernel (the shapes decode_supported lists)
+hipError_t launch_decode_pgdn(const DecodeArgs &a, float band_c, float *acc, hipStream_t st) {
+  if (!acc) return hipErrorInvalidValue;
+  if (a.dtype == 0) return dispatch_dk<bf16>(a, st, acc, band_c);
+  return dispatch_dk<float>(a, st, acc, band_c);
 }
 
 }  // namespace kla

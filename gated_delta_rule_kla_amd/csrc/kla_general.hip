@@ -508,6 +508,8 @@ bool pgdn_decode_supported(int dtype, int dk, int dv) {
 }
 
 hipError_t launch_pgdn_decode(const DecodeArgs &a, float band_c, float *acc, hipStream_t st) {
+  // the HBM-tuned decode kernel where it has the shape; this one for the other dv
+  if (decode_supported(a.dtype, a.dk, a.dv)) return launch_decode_pgdn(a, band_c, acc, st);
   PgdnDecodeParams p;
   p.q = a.q;
   p.k = a.k;

@@ -96,6 +96,8 @@ hipError_t launch_chunk_states(const ChunkArgs &a, void *states, hipStream_t str
 hipError_t launch_chunk_rev(const ChunkArgs &a, const float *dsfin, const void *dout, float *ds0, void *dstates,
                             hipStream_t stream);
 // a.eta holds the coefficient (beta when a.beta_direct, else eta); acc [N, H, dk] in place
+// PGDN's decode step on kla_decode_kernel (the shapes decode_supported lists)
+hipError_t launch_decode_pgdn(const DecodeArgs &a, float band_c, float *acc, hipStream_t stream);
 hipError_t launch_pgdn_decode(const DecodeArgs &a, float band_c, float *acc, hipStream_t stream);
 
 }  // namespace kla
