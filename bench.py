@@ -246,9 +246,9 @@ def bench_gdn(steps, warmup, decode_steps=512):
 def bench_pgdn(steps, warmup, decode_steps=64):
     """PGDN (kla_pgdn_chunk_fwd / kla_pgdn_decode_step: the preconditioned gated
     delta rule, coefficient given, band 1.5) on the prefill workload and the first
-    steps of the decode workload, both with unit-length keys.  The prefill runs on
-    the general chunk kernel (one workgroup per (sequence, head, 16 state
-    columns), the S-independent work redone per column slice)."""
+    steps of the decode workload, both with unit-length keys: the pipelined prep
+    and scan kernels after the key-accumulator and write-key passes, and the
+    HBM-tuned decode kernel."""
     import torch
     from gated_delta_rule_kla_amd import inputs, kla
 
@@ -259,18 +259,20 @@ def bench_pgdn(steps, warmup, decode_steps=64):
     o = torch.empty((B, H, T, dv), dtype=q.dtype, device=dev)
     S = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
     A = torch.empty((B, H, dk), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(1, kla.pgdn_chunk_workspace_bytes(B, H, T, dk, dv, x.chunk, q.dtype)),
+                     dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
     def pstep(_i):
         kla.pgdn_chunk_fwd(q, k, v, g, beta, x.eps, "given", 1.5, None, None, chunk=x.chunk, out=o,
-                           final_state=S, final_acc=A)
+                           final_state=S, final_acc=A, workspace=ws)
 
     for i in range(warmup):
         pstep(i)
     p_ms, _ = time_launches(pstep, steps, stream)
     _, p_bytes = prefill_algorithmic(B, H, T, dk, dv, x.chunk, 0, 1, B)
     p_bytes += 4 * dk * B * H  # the final accumulator
-    del q, k, v, g, beta, o, S, A
+    del q, k, v, g, beta, o, S, A, ws
     d = inputs.unit_keys(_workload(3))
     N, Hd, dkd = d.q.shape[1:]
     dvd = d.v.shape[-1]
@@ -290,7 +292,7 @@ def bench_pgdn(steps, warmup, decode_steps=64):
     del st, acc
     torch.cuda.empty_cache()
     return {"workload": f"PGDN (given coefficient, band 1.5, unit-length keys): prefill B={B} H={H} T={T} "
-                        f"dk={dk} dv={dv} chunk={x.chunk} bf16 through the general chunk kernel; decode "
+                        f"dk={dk} dv={dv} chunk={x.chunk} bf16; decode "
                         f"N={N} H={Hd} dk={dkd} dv={dvd}, {decode_steps} consecutive steps",
             "prefill_ms_per_call": p_ms, "prefill_tokens/s": B * T / (p_ms * 1e-3),
             "prefill_GB/s": p_bytes / p_ms / 1e6, "prefill_hbm_frac": p_bytes / p_ms / 1e6 / HBM_PEAK_GBS,
