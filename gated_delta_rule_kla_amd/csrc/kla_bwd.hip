@@ -1153,6 +1153,8 @@ __global__ __launch_bounds__(kGT) void kla_bwd_grads2_kernel(BwdParams p) {
     lds_barrier();
     // ---- (B) U = T' X, dX = T'^T dU (= dV), row sums ----
     float pg[4] = {0.f, 0.f, 0.f, 0.f}, pdd[4] = {0.f, 0.f, 0.f, 0.f};
+    // dX^T tiles for the dV stores: lane (lr, lg) holds dV[16 a + lr][16 ct + 4 lg + j]
+    f32x4 dxt[2] = {z4, z4};
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc) {
       const int ct = 2 * half + cc;
@@ -1162,8 +1164,11 @@ __global__ __launch_bounds__(kGT) void kla_bwd_grads2_kernel(BwdParams p) {
       for (int q = 0; q < 2; ++q) {
         if (32 * q < 16 * (a + 1))
           u = O::mma_grp(O::a_trans(bTp, LDC, 32 * q, 16 * a, lane), O::a_trans(bVX, LDJ, 32 * q, 16 * ct, lane), u);
-        if (q >= a / 2)
-          dx = O::mma_grp(O::a_row(bTp + ra * LDC, 32 * q, lg), O::a_trans(bDU, LDJ, 32 * q, 16 * ct, lane), dx);
+        if (q >= a / 2) {
+          const Grp tr = O::a_row(bTp + ra * LDC, 32 * q, lg), du = O::a_trans(bDU, LDJ, 32 * q, 16 * ct, lane);
+          dx = O::mma_grp(tr, du, dx);
+          dxt[cc] = O::mma_grp(du, tr, dxt[cc]);  // the operands swapped: the transposed tile
+        }
       }
       const f32x4 gm = *reinterpret_cast<const f32x4 *>(fvec + C + 16 * a + 4 * lg);
       const f32x4 d4 = *reinterpret_cast<const f32x4 *>(fvec + 2 * C + 16 * a + 4 * lg);
@@ -1171,14 +1176,28 @@ __global__ __launch_bounds__(kGT) void kla_bwd_grads2_kernel(BwdParams p) {
       put_d(bUD, 16 * a, 16 * ct, d4 * u);
       put_d(bGX, 16 * a, 16 * ct, -(gm * dx));
       const f32x4 o4 = col4g(bO, 16 * a, 16 * ct);
-      const int col = JB * blk + 16 * ct + lr;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int r = 16 * a + 4 * lg + j;
-        if (r < rows) static_cast<bf16 *>(p.dv)[(cl.row0 + r) * p.DV + col] = (bf16)dx[j];
         pg[j] += qs[cc][j] * o4[j] - ks[cc][j] * dx[j];
         pdd[j] += kd[cc][j] * u[j];
       }
+    }
+    {
+      // dV: the lanes lg = 2 m and 2 m + 1 of a row swap 8-byte halves so that the even
+      // one holds columns 8 m .. 8 m + 7 of tile 2 half and the odd one those of tile
+      // 2 half + 1; a row's 64 bytes then leave as four 16-byte stores
+      const bf16x4 h0 = {(bf16)dxt[0][0], (bf16)dxt[0][1], (bf16)dxt[0][2], (bf16)dxt[0][3]};
+      const bf16x4 h1 = {(bf16)dxt[1][0], (bf16)dxt[1][1], (bf16)dxt[1][2], (bf16)dxt[1][3]};
+      const uint2 m0 = __builtin_bit_cast(uint2, h0), m1 = __builtin_bit_cast(uint2, h1);
+      const bool odd = (lg & 1) != 0;
+      const uint2 snd = odd ? m0 : m1;
+      const uint2 rcv = make_uint2((unsigned)__shfl_xor((int)snd.x, 16), (unsigned)__shfl_xor((int)snd.y, 16));
+      const uint4 piece = odd ? make_uint4(rcv.x, rcv.y, m1.x, m1.y) : make_uint4(m0.x, m0.y, rcv.x, rcv.y);
+      const int ctp = 2 * half + (odd ? 1 : 0);
+      const int r = 16 * a + lr;
+      if (r < rows && ctp < nt)
+        *reinterpret_cast<uint4 *>(static_cast<bf16 *>(p.dv) + (cl.row0 + r) * p.DV + JB * blk + 16 * ctp +
+                                   8 * (lg >> 1)) = piece;
     }
 #pragma unroll
     for (int off = 8; off >= 1; off >>= 1)

@@ -1437,6 +1437,12 @@ __global__ __launch_bounds__(64 * (kWaves + (PG ? 1 : 0))) void kla_chunk_kernel
     }
   } else if (wave == LOADQ) {
     // =================== Q rows of chunk i+1 (two sets, two steps ahead) ========
+    if (p.states) {
+      // states mode has no outputs, so nothing reads Q: keep the barrier count only
+      __syncthreads();
+      for (int i = -1; i <= iend; ++i) lds_barrier();
+      return;
+    }
     RowLoad<E, DK, AllBlocks<NB>> qin[2];
     qin[0].issue(gq + tok0_of(0) * DK, nrow_of(0), lane);
     qin[1].issue(gq + tok0_of(clampc(1)) * DK, nrow_of(clampc(1)), lane);
