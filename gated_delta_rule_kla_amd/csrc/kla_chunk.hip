@@ -987,9 +987,9 @@ __global__ __launch_bounds__(256) void kla_pgdn_wkeys_kernel(ChunkParams p) {
 // Waves of a workgroup.  Step i (one barrier each, i = -1 .. nch) has
 //   CHAIN[2] the state scan of chunk i (half of the state columns each)
 //   PW[2]    Diag(Gam) Q S and the causal scores of chunk i; output of chunk i-1
-//   LOADK    K rows of chunk i+1 into LDS (coalesced loads issued two steps ahead)
+//   LOADK    K rows of chunk i+1 into LDS (coalesced loads issued three steps ahead)
 //   LOADT    T'^T, gamma/Gam/d and the V slice of chunk i+1 into LDS
-//   LOADQ    Q rows of chunk i+1 into LDS
+//   LOADQ    Q rows of chunk i+1 into LDS (likewise)
 // The P waves issue no global loads: their output stores would otherwise sit
 // in the same wait counter as the loads.  Waves w and w+4 share a SIMD.
 enum Role { CHAIN0 = 0, CHAIN1 = 1, PW0 = 2, PW1 = 3, LOADK = 4, LOADT = 5, LOADQ = 6, LOADW = 7 };
@@ -1401,23 +1401,29 @@ __global__ __launch_bounds__(64 * (kWaves + (PG ? 1 : 0))) void kla_chunk_kernel
       pwave(std::integral_constant<int, 1>{});
   } else if (wave == LOADK) {
     // =================== K rows of chunk i+1 ==================================
-    // Two register sets, loads issued two steps ahead (the step alternates
-    // between them, so the set is a compile-time choice).  Stores past the
+    // Three register sets, loads issued three steps ahead (the steps rotate
+    // through them, so the set is a compile-time choice).  Stores past the
     // last chunk rewrite a slot nobody reads any more.
-    RowLoad<E, DK, AllBlocks<NB>> kin[2];
+    RowLoad<E, DK, AllBlocks<NB>> kin[3];
     kin[0].issue(gk + tok0_of(0) * DK, nrow_of(0), lane);
     kin[1].issue(gk + tok0_of(clampc(1)) * DK, nrow_of(clampc(1)), lane);
+    kin[2].issue(gk + tok0_of(clampc(2)) * DK, nrow_of(clampc(2)), lane);
     __syncthreads();
     auto step = [&](int i, auto set_c) {
       constexpr int S = decltype(set_c)::value;
       kin[S].put(sK(i + 1), LDK, lane, [](int, int row) { return row; });
-      kin[S].issue(gk + tok0_of(clampc(i + 3)) * DK, nrow_of(clampc(i + 3)), lane);
+      kin[S].issue(gk + tok0_of(clampc(i + 4)) * DK, nrow_of(clampc(i + 4)), lane);
       lds_barrier();
     };
-    for (int i = -1; i <= iend; i += 2) {
+    // set (i + 1) mod 3 holds chunk i + 1 at step i; the steps run from -1 to iend
+    int i = -1;
+    for (; i + 2 <= iend; i += 3) {
       step(i, std::integral_constant<int, 0>{});
       step(i + 1, std::integral_constant<int, 1>{});
+      step(i + 2, std::integral_constant<int, 2>{});
     }
+    if (i <= iend) step(i++, std::integral_constant<int, 0>{});
+    if (i <= iend) step(i++, std::integral_constant<int, 1>{});
   } else if (PG && wave == LOADW) {
     // =================== PGDN write keys of chunk i+1 (two sets, two steps ahead) ====
     const E *gw = reinterpret_cast<const E *>(p.pg_w) + ((size_t)h * p.nslot + slot0) * (C * DK);
@@ -1436,27 +1442,32 @@ __global__ __launch_bounds__(64 * (kWaves + (PG ? 1 : 0))) void kla_chunk_kernel
       step(i + 1, std::integral_constant<int, 1>{});
     }
   } else if (wave == LOADQ) {
-    // =================== Q rows of chunk i+1 (two sets, two steps ahead) ========
+    // =================== Q rows of chunk i+1 (three sets, three steps ahead) ====
     if (p.states) {
       // states mode has no outputs, so nothing reads Q: keep the barrier count only
       __syncthreads();
       for (int i = -1; i <= iend; ++i) lds_barrier();
       return;
     }
-    RowLoad<E, DK, AllBlocks<NB>> qin[2];
+    RowLoad<E, DK, AllBlocks<NB>> qin[3];
     qin[0].issue(gq + tok0_of(0) * DK, nrow_of(0), lane);
     qin[1].issue(gq + tok0_of(clampc(1)) * DK, nrow_of(clampc(1)), lane);
+    qin[2].issue(gq + tok0_of(clampc(2)) * DK, nrow_of(clampc(2)), lane);
     __syncthreads();
     auto step = [&](int i, auto set_c) {
       constexpr int S = decltype(set_c)::value;
       qin[S].put(sQ(i + 1), LDK, lane, [](int, int row) { return row; });
-      qin[S].issue(gq + tok0_of(clampc(i + 3)) * DK, nrow_of(clampc(i + 3)), lane);
+      qin[S].issue(gq + tok0_of(clampc(i + 4)) * DK, nrow_of(clampc(i + 4)), lane);
       lds_barrier();
     };
-    for (int i = -1; i <= iend; i += 2) {
+    int i = -1;
+    for (; i + 2 <= iend; i += 3) {
       step(i, std::integral_constant<int, 0>{});
       step(i + 1, std::integral_constant<int, 1>{});
+      step(i + 2, std::integral_constant<int, 2>{});
     }
+    if (i <= iend) step(i++, std::integral_constant<int, 0>{});
+    if (i <= iend) step(i++, std::integral_constant<int, 1>{});
   } else {
     // =================== T'^T, gamma/Gam/d and the V slice of chunk i+1 ========
     // (two sets, two steps ahead, as for K, when the registers allow)
