@@ -449,7 +449,7 @@ __global__ __launch_bounds__(64 * kPrepWaves) void kla_chunk_prep_kernel(ChunkPa
 // The same S-independent work and the same workspace image as the pipelined
 // prep kernel above, organised for latency hiding instead of a pipeline: each
 // workgroup is one wave that owns one (chunk, head) from start to end, and a CU
-// holds seven of them, whose load, MFMA and solve phases overlap.  Global
+// holds eight of them, whose load, MFMA and solve phases overlap.  Global
 // memory is only touched with coalesced 16-byte accesses (consecutive lanes,
 // consecutive bytes): K rows come in four rows per instruction into a padded
 // LDS tile and go from there into the Gram MFMA operands (the same registers
@@ -470,16 +470,18 @@ struct PrepWaveShape {
   // hits distinct banks; the copy to the workspace drops the padding
   static constexpr int IL0 = 64 + 8, IL1 = 32 + 8;
   static constexpr int IMG_BYTES = (32 * IL0 + 32 * IL1) * 2;
-  static constexpr int R_BYTES = C * RB > IMG_BYTES + TD_BYTES ? C * RB : IMG_BYTES + TD_BYTES;
-  static constexpr int OFF_TD = IMG_BYTES;                    // inside R, after the image
-  static constexpr int OFF_A = R_BYTES;
+  // R holds the K rows until the Gram tiles are formed, then the image, the diagonal
+  // blocks and the off-diagonal A blocks (all written after the K rows are dead)
   static constexpr int A_BYTES = 6 * 16 * LDA * 2;
-  static constexpr int OFF_VEC = OFF_A + A_BYTES;             // ||k||^2 (PGDN: k . w), gamma, beta, PGDN mean
+  static constexpr int OFF_TD = IMG_BYTES;                    // inside R, after the image
+  static constexpr int OFF_A = IMG_BYTES + TD_BYTES;          // inside R, after the diagonal blocks
+  static constexpr int R_BYTES = C * RB > OFF_A + A_BYTES ? C * RB : OFF_A + A_BYTES;
+  static constexpr int OFF_VEC = R_BYTES;                     // ||k||^2 (PGDN: k . w), gamma, beta, PGDN mean
   static constexpr int OFF_W = OFF_VEC + 4 * C * 4;           // PGDN: the write keys, rows as K's
   static constexpr int BYTES = OFF_W + (PG ? C * RB : 0);
   static_assert(IMG_BYTES % 16 == 0 && OFF_TD % 16 == 0 && OFF_A % 16 == 0 && OFF_VEC % 16 == 0 &&
                 OFF_W % 16 == 0, "lds align");
-  static_assert(BYTES * (PG ? 4 : 7) <= 160 * 1024, "seven (PGDN: four) workgroups per CU");
+  static_assert(BYTES * (PG ? 4 : 8) <= 160 * 1024, "eight (PGDN: four) workgroups per CU");
 };
 
 // TIMG: also write the T^T image (p.timg).  PG: PGDN -- A and beta from K W^T with the
@@ -2000,11 +2002,11 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t st, char *state
     if constexpr (std::is_same<E, bf16>::value && C == 64) {
       // bf16: one wave per run of consecutive slots of one head, each run
       // prefetching its next slot while it computes the current one.  Runs of
-      // one slot while the grid is at most about two rounds of the seven
+      // one slot while the grid is at most about two rounds of the eight
       // one-wave workgroups a CU holds (more concurrent waves hide more);
       // longer runs beyond that, where the prefetch overlaps every round.
       const long long total = (long long)p.nslot * a.H;
-      p.pslots = (int)std::min<long long>(8, std::max<long long>(1, total / (2 * 7 * 256)));
+      p.pslots = (int)std::min<long long>(8, std::max<long long>(1, total / (2 * 8 * 256)));
       const unsigned runs = (unsigned)((p.nslot + p.pslots - 1) / p.pslots);
       if (p.pg_w)
         hipLaunchKernelGGL((kla_chunk_prep_wave_kernel<DK, false, true>), dim3(runs, (unsigned)a.H), dim3(64), 0, st, p);
