@@ -6,6 +6,7 @@
 #include <cmath>
 #include <algorithm>
 #include <cstdint>
+#include <cstring>
 #include <vector>
 
 #include "../../include/kla.h"
@@ -15,6 +16,17 @@ namespace {
 
 bool misaligned(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
 
+// Enum-typed arguments come from C callers as plain ints and may hold any value; their
+// bytes are read as an int (a read as the C++ enum type is undefined outside the range
+// of its enumerators), and everything below works on that int.
+template <typename E>
+int raw(const E &e) {
+  static_assert(sizeof(E) == sizeof(int), "the enums of the C ABI are int-sized");
+  int v;
+  std::memcpy(&v, &e, sizeof v);
+  return v;
+}
+
 bool bad_eps(float eps) { return !std::isfinite(eps) || eps < 0.f; }
 
 kla_status_t from_hip(hipError_t e) { return e == hipSuccess ? KLA_OK : KLA_ERR_HIP; }
@@ -23,7 +35,7 @@ kla_status_t from_hip(hipError_t e) { return e == hipSuccess ? KLA_OK : KLA_ERR_
 // kla_chunk_workspace_bytes.
 kla_status_t check_chunk_shapes(float eps, const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
                                 int num_seqs, int B, int H, int T, int dk, int dv, int chunk,
-                                kla_dtype_t dtype) {
+                                int dtype) {
   if (dtype != KLA_DT_BF16 && dtype != KLA_DT_F32) return KLA_ERR_DTYPE;
   if (B < 0 || H <= 0 || T < 0 || dk <= 0 || dv <= 0 || chunk <= 0 || num_seqs < 0)
     return KLA_ERR_SHAPE;
@@ -52,15 +64,15 @@ kla_status_t check_chunk_shapes(float eps, const int32_t *cu_seqlens, const int3
 kla::ChunkArgs chunk_args(const void *q, const void *k, const void *v, const void *g, const void *eta,
                           float eps, const float *initial_state, void *o, float *final_state,
                           const int32_t *cu_seqlens, int num_seqs, int B, int H, int T, int dk, int dv,
-                          int chunk, kla_dtype_t dtype, void *workspace, int beta_direct) {
+                          int chunk, int dtype, void *workspace, int beta_direct) {
   return kla::ChunkArgs{q,          k,        v, g, eta, eps, initial_state, o,     final_state,
-                        cu_seqlens, num_seqs, B, H, T,   dk,  dv,            chunk, (int)dtype,
+                        cu_seqlens, num_seqs, B, H, T,   dk,  dv,            chunk, dtype,
                         workspace,  beta_direct};
 }
 
 kla_status_t decode_impl(const void *q, const void *k, const void *v, const void *g, const void *eta,
                          float eps, int beta_direct, float *state, void *o, int N, int H, int dk, int dv,
-                         kla_dtype_t dtype, void *stream) {
+                         int dtype, void *stream) {
   if (dtype != KLA_DT_BF16 && dtype != KLA_DT_F32) return KLA_ERR_DTYPE;
   if (N < 0 || H <= 0 || dk <= 0 || dv <= 0) return KLA_ERR_SHAPE;
   if (bad_eps(eps)) return KLA_ERR_EPS;
@@ -71,7 +83,7 @@ kla_status_t decode_impl(const void *q, const void *k, const void *v, const void
       misaligned(state) || misaligned(o))
     return KLA_ERR_ALIGN;
   if ((long long)N * H > 0x7fffffffLL) return KLA_ERR_SHAPE;
-  kla::DecodeArgs a{q, k, v, g, eta, eps, state, o, N, H, dk, dv, (int)dtype, beta_direct};
+  kla::DecodeArgs a{q, k, v, g, eta, eps, state, o, N, H, dk, dv, dtype, beta_direct};
   return from_hip(kla::launch_decode(a, reinterpret_cast<hipStream_t>(stream)));
 }
 
@@ -81,7 +93,7 @@ kla_status_t chunk_fwd_impl(const void *q, const void *k, const void *v, const v
                             float eps, int beta_direct, const float *initial_state, void *o,
                             float *final_state, const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
                             int num_seqs, int B, int H, int T, int dk, int dv, int chunk, void *workspace,
-                            size_t workspace_bytes, kla_dtype_t dtype, void *stream,
+                            size_t workspace_bytes, int dtype, void *stream,
                             bool static_scratch = false) {
   const kla_status_t st =
       check_chunk_shapes(eps, cu_seqlens, cu_seqlens_host, num_seqs, B, H, T, dk, dv, chunk, dtype);
@@ -114,7 +126,7 @@ kla_status_t chunk_bwd_impl(const void *q, const void *k, const void *v, const v
                             const float *dfinal_state, void *dq, void *dk, void *dv, float *dg, float *deta,
                             float *dinitial_state, const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
                             int num_seqs, int B, int H, int T, int dkk, int dvv, int chunk, void *workspace,
-                            size_t workspace_bytes, kla_dtype_t dtype, void *stream) {
+                            size_t workspace_bytes, int dtype, void *stream) {
   const kla_status_t st =
       check_chunk_shapes(eps, cu_seqlens, cu_seqlens_host, num_seqs, B, H, T, dkk, dvv, chunk, dtype);
   if (st != KLA_OK) return st;
@@ -136,7 +148,7 @@ kla_status_t chunk_bwd_impl(const void *q, const void *k, const void *v, const v
   return from_hip(kla::launch_chunk_bwd(a, b, reinterpret_cast<hipStream_t>(stream)));
 }
 
-kla_status_t check_pgdn(kla_gain_t gain, float band, float eps) {
+kla_status_t check_pgdn(int gain, float band, float eps) {
   if (gain != KLA_GAIN_GIVEN && gain != KLA_GAIN_KACZMARZ) return KLA_ERR_PARAM;
   if (!std::isfinite(band) || band < 1.f) return KLA_ERR_PARAM;
   if (gain == KLA_GAIN_KACZMARZ && bad_eps(eps)) return KLA_ERR_EPS;
@@ -150,7 +162,8 @@ float band_log(float band) { return band == 1.f ? 0.f : std::log(band); }
 extern "C" {
 
 size_t kla_pgdn_chunk_workspace_bytes(const int32_t *cu_seqlens, const int32_t *cu_seqlens_host, int num_seqs,
-                                      int B, int H, int T, int dk, int dv, int chunk, kla_dtype_t dtype) {
+                                      int B, int H, int T, int dk, int dv, int chunk, kla_dtype_t dtype_) {
+  const int dtype = raw(dtype_);
   if (check_chunk_shapes(0.f, cu_seqlens, cu_seqlens_host, num_seqs, B, H, T, dk, dv, chunk, dtype) != KLA_OK)
     return 0;
   if (num_seqs == 0 || (long long)B * T == 0) return 0;
@@ -160,11 +173,12 @@ size_t kla_pgdn_chunk_workspace_bytes(const int32_t *cu_seqlens, const int32_t *
 }
 
 kla_status_t kla_pgdn_chunk_fwd(const void *q, const void *k, const void *v, const void *g, const void *coef,
-                                float eps, kla_gain_t gain, float band, const float *initial_state,
+                                float eps, kla_gain_t gain_, float band, const float *initial_state,
                                 const float *initial_acc, void *o, float *final_state, float *final_acc,
                                 const int32_t *cu_seqlens, const int32_t *cu_seqlens_host, int num_seqs, int B,
-                                int H, int T, int dk, int dv, int chunk, kla_dtype_t dtype, void *workspace,
+                                int H, int T, int dk, int dv, int chunk, kla_dtype_t dtype_, void *workspace,
                                 size_t workspace_bytes, void *stream) {
+  const int dtype = raw(dtype_), gain = raw(gain_);
   if (dtype != KLA_DT_BF16 && dtype != KLA_DT_F32) return KLA_ERR_DTYPE;
   kla_status_t st = check_pgdn(gain, band, eps);
   if (st != KLA_OK) return st;
@@ -190,8 +204,9 @@ kla_status_t kla_pgdn_chunk_fwd(const void *q, const void *k, const void *v, con
 }
 
 kla_status_t kla_pgdn_decode_step(const void *q, const void *k, const void *v, const void *g, const void *coef,
-                                  float eps, kla_gain_t gain, float band, float *state, float *acc, void *o,
-                                  int N, int H, int dk, int dv, kla_dtype_t dtype, void *stream) {
+                                  float eps, kla_gain_t gain_, float band, float *state, float *acc, void *o,
+                                  int N, int H, int dk, int dv, kla_dtype_t dtype_, void *stream) {
+  const int dtype = raw(dtype_), gain = raw(gain_);
   if (dtype != KLA_DT_BF16 && dtype != KLA_DT_F32) return KLA_ERR_DTYPE;
   if (N < 0 || H <= 0 || dk <= 0 || dv <= 0) return KLA_ERR_SHAPE;
   const kla_status_t st = check_pgdn(gain, band, eps);
@@ -204,14 +219,14 @@ kla_status_t kla_pgdn_decode_step(const void *q, const void *k, const void *v, c
     return KLA_ERR_ALIGN;
   if ((long long)N * H > 0x7fffffffLL) return KLA_ERR_SHAPE;
   const float e = gain == KLA_GAIN_KACZMARZ ? eps : 0.f;
-  kla::DecodeArgs a{q, k, v, g, coef, e, state, o, N, H, dk, dv, (int)dtype, gain == KLA_GAIN_GIVEN ? 1 : 0};
+  kla::DecodeArgs a{q, k, v, g, coef, e, state, o, N, H, dk, dv, dtype, gain == KLA_GAIN_GIVEN ? 1 : 0};
   return from_hip(kla::launch_pgdn_decode(a, band_log(band), acc, reinterpret_cast<hipStream_t>(stream)));
 }
 
 int kla_abi_version(void) { return KLA_ABI_VERSION; }
 
 const char *kla_status_str(kla_status_t s) {
-  switch (s) {
+  switch (raw(s)) {
     case KLA_OK: return "ok";
     case KLA_ERR_NULL: return "a required pointer is NULL";
     case KLA_ERR_SHAPE: return "invalid or inconsistent sizes";
@@ -229,7 +244,8 @@ const char *kla_status_str(kla_status_t s) {
 }
 
 size_t kla_chunk_workspace_bytes(const int32_t *cu_seqlens, const int32_t *cu_seqlens_host, int num_seqs,
-                                 int B, int H, int T, int dk, int dv, int chunk, kla_dtype_t dtype) {
+                                 int B, int H, int T, int dk, int dv, int chunk, kla_dtype_t dtype_) {
+  const int dtype = raw(dtype_);
   if (check_chunk_shapes(0.f, cu_seqlens, cu_seqlens_host, num_seqs, B, H, T, dk, dv, chunk, dtype) != KLA_OK)
     return 0;
   if (num_seqs == 0 || (long long)B * T == 0) return 0;
@@ -242,8 +258,9 @@ kla_status_t kla_chunk_fwd(const void *q, const void *k, const void *v, const vo
                            const void *eta, float eps, const float *initial_state, void *o,
                            float *final_state, const int32_t *cu_seqlens,
                            const int32_t *cu_seqlens_host, int num_seqs, int B, int H, int T,
-                           int dk, int dv, int chunk, kla_dtype_t dtype, void *workspace,
+                           int dk, int dv, int chunk, kla_dtype_t dtype_, void *workspace,
                            size_t workspace_bytes, void *stream) {
+  const int dtype = raw(dtype_);
   return chunk_fwd_impl(q, k, v, g, eta, eps, 0, initial_state, o, final_state, cu_seqlens, cu_seqlens_host,
                         num_seqs, B, H, T, dk, dv, chunk, workspace, workspace_bytes, dtype, stream);
 }
@@ -251,8 +268,9 @@ kla_status_t kla_chunk_fwd(const void *q, const void *k, const void *v, const vo
 kla_status_t kla_gdn_chunk_fwd(const void *q, const void *k, const void *v, const void *g,
                                const void *beta, const float *initial_state, void *o, float *final_state,
                                const int32_t *cu_seqlens, const int32_t *cu_seqlens_host, int num_seqs,
-                               int B, int H, int T, int dk, int dv, int chunk, kla_dtype_t dtype,
+                               int B, int H, int T, int dk, int dv, int chunk, kla_dtype_t dtype_,
                                void *workspace, size_t workspace_bytes, void *stream) {
+  const int dtype = raw(dtype_);
   return chunk_fwd_impl(q, k, v, g, beta, 0.f, 1, initial_state, o, final_state, cu_seqlens, cu_seqlens_host,
                         num_seqs, B, H, T, dk, dv, chunk, workspace, workspace_bytes, dtype, stream);
 }
@@ -260,8 +278,9 @@ kla_status_t kla_gdn_chunk_fwd(const void *q, const void *k, const void *v, cons
 kla_status_t kla_chunk_fwd_noalloc(const void *q, const void *k, const void *v, const void *g, const void *eta,
                                    float eps, const float *initial_state, void *o, float *final_state,
                                    const int32_t *cu_seqlens, const int32_t *cu_seqlens_host, int num_seqs,
-                                   int B, int H, int T, int dk, int dv, int chunk, kla_dtype_t dtype,
+                                   int B, int H, int T, int dk, int dv, int chunk, kla_dtype_t dtype_,
                                    void *stream) {
+  const int dtype = raw(dtype_);
   return chunk_fwd_impl(q, k, v, g, eta, eps, 0, initial_state, o, final_state, cu_seqlens, cu_seqlens_host,
                         num_seqs, B, H, T, dk, dv, chunk, nullptr, 0, dtype, stream, true);
 }
@@ -287,7 +306,8 @@ size_t kla_chunk_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int ch
 }
 
 size_t kla_chunk_bwd_workspace_bytes(const int32_t *cu_seqlens, const int32_t *cu_seqlens_host, int num_seqs,
-                                     int B, int H, int T, int dk, int dv, int chunk, kla_dtype_t dtype) {
+                                     int B, int H, int T, int dk, int dv, int chunk, kla_dtype_t dtype_) {
+  const int dtype = raw(dtype_);
   if (check_chunk_shapes(0.f, cu_seqlens, cu_seqlens_host, num_seqs, B, H, T, dk, dv, chunk, dtype) != KLA_OK)
     return 0;
   if (!kla::chunk_bwd_supported(dtype, dk, dv, chunk)) return 0;
@@ -301,8 +321,9 @@ kla_status_t kla_chunk_bwd(const void *q, const void *k, const void *v, const vo
                            float eps, const float *initial_state, const void *dout, const float *dfinal_state,
                            void *dq, void *dk_, void *dv_, float *dg, float *deta, float *dinitial_state,
                            const int32_t *cu_seqlens, const int32_t *cu_seqlens_host, int num_seqs, int B,
-                           int H, int T, int dk, int dv, int chunk, kla_dtype_t dtype, void *workspace,
+                           int H, int T, int dk, int dv, int chunk, kla_dtype_t dtype_, void *workspace,
                            size_t workspace_bytes, void *stream) {
+  const int dtype = raw(dtype_);
   return chunk_bwd_impl(q, k, v, g, eta, eps, 0, initial_state, dout, dfinal_state, dq, dk_, dv_, dg, deta,
                         dinitial_state, cu_seqlens, cu_seqlens_host, num_seqs, B, H, T, dk, dv, chunk, workspace,
                         workspace_bytes, dtype, stream);
@@ -312,8 +333,9 @@ kla_status_t kla_gdn_chunk_bwd(const void *q, const void *k, const void *v, cons
                                const float *initial_state, const void *dout, const float *dfinal_state, void *dq,
                                void *dk_, void *dv_, float *dg, float *dbeta, float *dinitial_state,
                                const int32_t *cu_seqlens, const int32_t *cu_seqlens_host, int num_seqs, int B,
-                               int H, int T, int dk, int dv, int chunk, kla_dtype_t dtype, void *workspace,
+                               int H, int T, int dk, int dv, int chunk, kla_dtype_t dtype_, void *workspace,
                                size_t workspace_bytes, void *stream) {
+  const int dtype = raw(dtype_);
   return chunk_bwd_impl(q, k, v, g, beta, 0.f, 1, initial_state, dout, dfinal_state, dq, dk_, dv_, dg, dbeta,
                         dinitial_state, cu_seqlens, cu_seqlens_host, num_seqs, B, H, T, dk, dv, chunk, workspace,
                         workspace_bytes, dtype, stream);
@@ -321,13 +343,15 @@ kla_status_t kla_gdn_chunk_bwd(const void *q, const void *k, const void *v, cons
 
 kla_status_t kla_decode_step(const void *q, const void *k, const void *v, const void *g,
                              const void *eta, float eps, float *state, void *o, int N, int H,
-                             int dk, int dv, kla_dtype_t dtype, void *stream) {
+                             int dk, int dv, kla_dtype_t dtype_, void *stream) {
+  const int dtype = raw(dtype_);
   return decode_impl(q, k, v, g, eta, eps, 0, state, o, N, H, dk, dv, dtype, stream);
 }
 
 kla_status_t kla_gdn_decode_step(const void *q, const void *k, const void *v, const void *g,
                                  const void *beta, float *state, void *o, int N, int H, int dk, int dv,
-                                 kla_dtype_t dtype, void *stream) {
+                                 kla_dtype_t dtype_, void *stream) {
+  const int dtype = raw(dtype_);
   return decode_impl(q, k, v, g, beta, 0.f, 1, state, o, N, H, dk, dv, dtype, stream);
 }
 
