@@ -1078,12 +1078,8 @@ __global__ __launch_bounds__(kGT) void kla_bwd_grads2_kernel(BwdParams p) {
 
   for (int blk = 0; blk < nblk; ++blk) {
     lds_barrier();  // the previous block's readers are done (and the chunk's loads are in LDS)
-    put(blk);
-    if (blk + 1 < nblk)
-      issue(blk + 1);
-    else if (t < TLy::PACK / 16)
-      tv = reinterpret_cast<const uint4 *>(p.timg + sidx * TLy::PACK)[t];  // the T^T image
     if (blk == 0) {
+      // (before the first block is stored: its loads are still in flight)
       // ||k_r||^2 and b_r (eight lanes per row); P = lower(Q K^T . E), tiles b <= a
       {
         const int r = t >> 3;
@@ -1115,6 +1111,11 @@ __global__ __launch_bounds__(kGT) void kla_bwd_grads2_kernel(BwdParams p) {
         put_d(bP, 16 * a, 16 * b, pv, LDC);
       }
     }
+    put(blk);
+    if (blk + 1 < nblk)
+      issue(blk + 1);
+    else if (t < TLy::PACK / 16)
+      tv = reinterpret_cast<const uint4 *>(p.timg + sidx * TLy::PACK)[t];  // the T^T image
     lds_barrier();
     const int nt = min(4, ntile - 4 * blk);
     // ---- (A) K S, Q S, K dS', X, dU for row tile a and column tiles 2 half, 2 half + 1 ----
