@@ -883,7 +883,7 @@ template <int DK>
 struct WkeysShape {
   static constexpr int C = 64, NT = 256;
   static constexpr int OFF_K = 0;                      // K rows, bf16 (then W)
-  static constexpr int OFF_V = C * DK * 2;             // norms, then ln of the row means; start sum
+  static constexpr int OFF_V = C * DK * 2;             // norms, then log2 of the row means; start sum
   static constexpr int OFF_T = OFF_V + (C + 4) * 4;    // per coordinate: sum of squares of rows 0..31
   static constexpr int BYTES = OFF_T + DK * 4;
 };
@@ -958,13 +958,14 @@ __global__ __launch_bounds__(256) void kla_pgdn_wkeys_kernel(ChunkParams p) {
     }
   }
   __syncthreads();
-  if (t < 64) {  // ln of the row means: (start sum + prefix of the norms) / dk, lane = row
+  if (t < 64) {  // log2 of the row means: (start sum + prefix of the norms) / dk, lane = row
     const float m = (sv[C] + wave_inclusive_scan(sv[t])) * (1.f / DK);
-    sv[t] = __logf(m + 1e-30f);
+    sv[t] = pgdn_log2_mean(m);
   }
   __syncthreads();
   // thread (coordinate i, half hf) walks its 32 rows with the accumulator in a register
   // (the second half starts from the first half's total) and replaces k by w in place
+  const PgdnK pk = pgdn_k(p.band_c);
   for (int e = t; e < 2 * DK; e += NT) {
     const int i = e % DK, hf = e / DK;
     const float a00 = a0[i];
@@ -973,7 +974,7 @@ __global__ __launch_bounds__(256) void kla_pgdn_wkeys_kernel(ChunkParams p) {
     for (int r = 32 * hf; r < 32 * hf + 32; ++r) {
       const float kv = (float)sk[r * DK + i];
       a = fmaf(kv, kv, a);
-      sk[r * DK + i] = (bf16)(pgdn_precond_l(a, sv[r], p.band_c) * kv);
+      sk[r * DK + i] = (bf16)(pgdn_precond(a, sv[r], pk) * kv);
     }
   }
   __syncthreads();

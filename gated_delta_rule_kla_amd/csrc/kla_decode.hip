@@ -102,12 +102,13 @@ __global__ __launch_bounds__(decode_threads(DK, DV)) void kla_decode_kernel(
     float tot = 0.f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) tot += s_m[w];
-    const float log_m = __logf(tot * (1.f / DK) + 1e-30f);
+    const float log_m = pgdn_log2_mean(tot * (1.f / DK));
+    const PgdnK pk = pgdn_k(band_c);
 #pragma unroll
     for (int j = 0; j < NA; ++j) {
       const int i = t + Sh::NT * j;
       if (i < DK) {
-        s_w[i] = pgdn_precond_l(av[j], log_m, band_c) * kk[j];
+        s_w[i] = pgdn_precond(av[j], log_m, pk) * kk[j];
         acc[nh * DK + i] = av[j];
       }
     }
