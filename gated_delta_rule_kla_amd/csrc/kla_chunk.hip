@@ -485,9 +485,11 @@ struct PrepWaveShape {
 };
 
 // TIMG: also write the T^T image (p.timg).  PG: PGDN -- A and beta from K W^T with the
-// write keys W of p.pg_w.
+// write keys W of p.pg_w.  Two waves per SIMD (eight per CU, the LDS allows as many) caps
+// the registers at 256; without the cap the T^T image's live blocks took a few more and
+// halved the waves per CU (PGDN's LDS tile allows four per CU anyway).
 template <int DK, bool TIMG, bool PG>
-__global__ __launch_bounds__(64) void kla_chunk_prep_wave_kernel(ChunkParams p) {
+__global__ __launch_bounds__(64, PG ? 1 : 2) void kla_chunk_prep_wave_kernel(ChunkParams p) {
   using Sh = PrepWaveShape<DK, PG>;
   using TL = TpLayout<bf16, 64>;
   using M = Mm16<bf16>;
@@ -581,33 +583,31 @@ __global__ __launch_bounds__(64) void kla_chunk_prep_wave_kernel(ChunkParams p) 
       for (int q = 0; q < NQ; ++q)
         kf[rb][q] = *reinterpret_cast<const bf16x8 *>(R + (16 * rb + li) * Sh::RB + (32 * q + 8 * lg) * 2);
 
-    // ---- PGDN: the write keys of the chunk (staged above) as operands ----------------
-    bf16x8 wf[NB][NQ];
-    if constexpr (PG) {
-#pragma unroll
-      for (int rb = 0; rb < NB; ++rb)
-#pragma unroll
-        for (int q = 0; q < NQ; ++q)
-          wf[rb][q] = *reinterpret_cast<const bf16x8 *>(Wt + (16 * rb + li) * Sh::RB + (32 * q + 8 * lg) * 2);
-    } else {
-#pragma unroll
-      for (int rb = 0; rb < NB; ++rb)
-#pragma unroll
-        for (int q = 0; q < NQ; ++q) wf[rb][q] = kf[rb][q];
-    }
-
     // ---- Gram tiles G[rt][st] = K_rt W_st^T (st <= rt; W = K outside PGDN) and the
-    // diagonal k_r . w_r (||k_r||^2) ---------------------------------------------------
+    // diagonal k_r . w_r (||k_r||^2); PGDN's write-key operands are read from their LDS
+    // tile as the products need them (a register copy of the tile would leave the
+    // wave too many registers for two waves per SIMD) --------------------------------
+    auto wop = [&](int st, int q) -> bf16x8 {
+      if constexpr (PG)
+        return *reinterpret_cast<const bf16x8 *>(Wt + (16 * st + li) * Sh::RB + (32 * q + 8 * lg) * 2);
+      else
+        return kf[st][q];
+    };
     f32x4 G[NB][NB];
 #pragma unroll
-    for (int rt = 0; rt < NB; ++rt)
+    for (int st = 0; st < NB; ++st) {
+      bf16x8 w[NQ];  // block st of the write keys (of K outside PGDN), as right operands
 #pragma unroll
-      for (int st = 0; st <= rt; ++st) {
+      for (int q = 0; q < NQ; ++q) w[q] = wop(st, q);
+#pragma unroll
+      for (int rt = st; rt < NB; ++rt) {
         f32x4 acc = zero4();
 #pragma unroll
-        for (int q = 0; q < NQ; ++q) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[rt][q], wf[st][q], acc, 0, 0, 0);
+        for (int q = 0; q < NQ; ++q) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[rt][q], w[q], acc, 0, 0, 0);
         G[rt][st] = acc;
       }
+      if constexpr (PG) __builtin_amdgcn_sched_barrier(0);  // keep the next block's reads after these
+    }
 #pragma unroll
     for (int rt = 0; rt < NB; ++rt) {
       // ||k_r||^2 of row 16 rt + li: diagonal tile, lane group li >> 2, element li & 3
