@@ -31,6 +31,7 @@
 // steps (Mma16 below): on the bf16 build one 16x16x16 bf16 MFMA whose operands are
 // rounded to bf16 from fp32 LDS values, on the fp32 build four 16x16x4 fp32 MFMAs.  There
 // are no atomics, so results are deterministic run to run.
+#include <mutex>
 #include <algorithm>
 
 #include "kla_common.h"
@@ -1452,6 +1453,36 @@ __global__ __launch_bounds__(kGT) void kla_bwd_grads2_kernel(BwdParams p) {
 // ============================================================================
 // host side
 // ============================================================================
+// Per device: its CU count, and a second stream with two events on which the backward
+// runs its adjoint scan beside the states pass (created on first use, default priority,
+// kept until the process ends).  `lock` serialises the fork and join of concurrent calls
+// so that each waits on its own events.
+struct SideStream {
+  std::mutex lock;
+  bool ready = false;
+  int cus = 0;
+  hipStream_t stream = nullptr;
+  hipEvent_t prep_done = nullptr, rev_done = nullptr;
+};
+static SideStream *side_stream() {
+  static SideStream side[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  SideStream &s = side[dev];
+  std::lock_guard<std::mutex> g(s.lock);
+  if (!s.ready) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return nullptr;
+    if (hipStreamCreateWithFlags(&s.stream, hipStreamNonBlocking) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&s.prep_done, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&s.rev_done, hipEventDisableTiming) != hipSuccess)
+      return nullptr;
+    s.cus = n;
+    s.ready = true;
+  }
+  return &s;
+}
+
 template <typename E, int C, int DK>
 struct BwdLayout {
   // workspace: prep records, then chunk-start states, then chunk-end state gradients
@@ -1535,6 +1566,22 @@ hipError_t launch_bwd_t(const ChunkArgs &a, const ChunkBwdArgs &b, hipStream_t s
     fa.o = nullptr;
     fa.final_state = nullptr;
     fa.workspace = ws + pb + 2 * sb;
+    if constexpr (img) {
+      SideStream *side = side_stream();
+      if (side && bwd_scans_concurrent(fa, side->cus)) {
+        // the states pass on `st`, the adjoint scan on the side stream once the prep's
+        // workspace is complete; `st` waits for both before the gradient kernel
+        std::lock_guard<std::mutex> g(side->lock);
+        hipError_t e = launch_chunk_states(fa, p.states, st, ws, true, side->prep_done);
+        if (e == hipSuccess) e = hipStreamWaitEvent(side->stream, side->prep_done, 0);
+        if (e == hipSuccess) e = launch_chunk_rev(fa, p.dsfin, p.dout, p.ds0, p.dstates, side->stream, true);
+        if (e == hipSuccess) e = hipEventRecord(side->rev_done, side->stream);
+        if (e == hipSuccess) e = hipStreamWaitEvent(st, side->rev_done, 0);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((kla_bwd_grads2_kernel<DK>), dim3((unsigned)p.nslot, (unsigned)a.H), dim3(kGT), 0, st, p);
+        return hipGetLastError();
+      }
+    }
     const hipError_t e = launch_chunk_states(fa, p.states, st, img ? ws : nullptr);
     if (e != hipSuccess) return e;
   }

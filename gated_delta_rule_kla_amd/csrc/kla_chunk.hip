@@ -1943,7 +1943,8 @@ struct PgArgs {
 
 template <typename E, int C, int DK, int NCT, bool PG = false>
 static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t st, char *states = nullptr,
-                                  char *timg = nullptr, const PgArgs *pg = nullptr) {
+                                  char *timg = nullptr, const PgArgs *pg = nullptr,
+                                  hipEvent_t after_prep = nullptr) {
   using Sh = ChunkShape<E, C, DK, NCT, PG>;
   ChunkParams p;
   p.states = states;
@@ -2027,6 +2028,10 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t st, char *state
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  if (after_prep) {  // the workspace (images, order) is complete once this event has fired
+    const hipError_t e = hipEventRecord(after_prep, st);
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL((kla_chunk_kernel<E, C, DK, NCT, PG>), dim3((unsigned)nblk), dim3(Sh::NT), 0, st, p);
   return hipGetLastError();
 }
@@ -2061,22 +2066,23 @@ static bool use_four_column_tiles(const ChunkArgs &a) {
   return a.dv % 64 == 0 && (long long)a.num_seqs * a.H * (a.dv / 64) >= 8 * 256;
 }
 
-static hipError_t launch_fast(const ChunkArgs &a, hipStream_t st, char *states, char *timg = nullptr) {
+static hipError_t launch_fast(const ChunkArgs &a, hipStream_t st, char *states, char *timg = nullptr,
+                              bool four = false, hipEvent_t after_prep = nullptr) {
   if (a.dtype == 0) {
-    if (!states && use_four_column_tiles(a)) {
-      if (a.dk == 128) return launch_chunk_t<bf16, 64, 128, 4>(a, st, states, timg);
-      if (a.dk == 64) return launch_chunk_t<bf16, 64, 64, 4>(a, st, states, timg);
+    if ((four || !states) && a.dv % 64 == 0 && (four || use_four_column_tiles(a))) {
+      if (a.dk == 128) return launch_chunk_t<bf16, 64, 128, 4>(a, st, states, timg, nullptr, after_prep);
+      if (a.dk == 64) return launch_chunk_t<bf16, 64, 64, 4>(a, st, states, timg, nullptr, after_prep);
     }
     const bool two = use_two_column_tiles(a);
     if (a.dk == 128)
-      return two ? launch_chunk_t<bf16, 64, 128, 2>(a, st, states, timg)
-                 : launch_chunk_t<bf16, 64, 128, 1>(a, st, states, timg);
+      return two ? launch_chunk_t<bf16, 64, 128, 2>(a, st, states, timg, nullptr, after_prep)
+                 : launch_chunk_t<bf16, 64, 128, 1>(a, st, states, timg, nullptr, after_prep);
     if (a.dk == 64)
-      return two ? launch_chunk_t<bf16, 64, 64, 2>(a, st, states, timg)
-                 : launch_chunk_t<bf16, 64, 64, 1>(a, st, states, timg);
+      return two ? launch_chunk_t<bf16, 64, 64, 2>(a, st, states, timg, nullptr, after_prep)
+                 : launch_chunk_t<bf16, 64, 64, 1>(a, st, states, timg, nullptr, after_prep);
     return hipErrorInvalidValue;
   }
-  if (timg) return hipErrorInvalidValue;  // the T^T image comes from the bf16 prep kernel only
+  if (timg || four || after_prep) return hipErrorInvalidValue;  // bf16 paths only
   if (a.chunk == 16) {
     switch (a.dk) {
       case 16: return launch_chunk_t<float, 16, 16, 1>(a, st, states);
@@ -2168,9 +2174,13 @@ static hipError_t launch_rev_t(const ChunkArgs &a, const float *dsfin, const voi
 }
 
 hipError_t launch_chunk_rev(const ChunkArgs &a, const float *dsfin, const void *dout, float *ds0, void *dstates,
-                            hipStream_t st) {
+                            hipStream_t st, bool four) {
   if (!fast_chunk_supported(a.dtype, a.dk, a.dv, a.chunk)) return hipErrorInvalidValue;
   if (a.dtype == 0) {
+    if (four && a.dv % 64 == 0) {
+      if (a.dk == 128) return launch_rev_t<bf16, 64, 128, 4>(a, dsfin, dout, ds0, dstates, st);
+      if (a.dk == 64) return launch_rev_t<bf16, 64, 64, 4>(a, dsfin, dout, ds0, dstates, st);
+    }
     const bool two = use_two_column_tiles(a);
     if (a.dk == 128)
       return two ? launch_rev_t<bf16, 64, 128, 2>(a, dsfin, dout, ds0, dstates, st)
@@ -2196,9 +2206,19 @@ hipError_t launch_chunk_rev(const ChunkArgs &a, const float *dsfin, const void *
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_chunk_states(const ChunkArgs &a, void *states, hipStream_t st, void *timg) {
+hipError_t launch_chunk_states(const ChunkArgs &a, void *states, hipStream_t st, void *timg, bool four,
+                               hipEvent_t after_prep) {
   if (!fast_chunk_supported(a.dtype, a.dk, a.dv, a.chunk)) return hipErrorInvalidValue;
-  return launch_fast(a, st, static_cast<char *>(states), static_cast<char *>(timg));
+  return launch_fast(a, st, static_cast<char *>(states), static_cast<char *>(timg), four, after_prep);
+}
+
+// The backward's two state passes (the chunk-start states and the adjoint scan) depend
+// only on the prep's workspace, not on each other.  With 64-column slices both fit one
+// round of workgroups side by side (one per CU each), which runs them concurrently at the
+// higher per-CU throughput of the wider slices.
+bool bwd_scans_concurrent(const ChunkArgs &a, int cus) {
+  return a.dtype == 0 && a.chunk == 64 && (a.dk == 64 || a.dk == 128) && a.dv % 64 == 0 &&
+         2LL * a.num_seqs * a.H * (a.dv / 64) <= cus;
 }
 
 // ---------------------------------------------------------------------------

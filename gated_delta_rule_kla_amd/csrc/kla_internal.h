@@ -87,14 +87,20 @@ hipError_t launch_chunk_general(const ChunkArgs &a, const GenExtra &x, hipStream
 // kla_chunk.hip; dk * dv elements of the element type per (head, slot)), no
 // outputs.  a.workspace is the forward workspace (chunk_workspace_bytes(a)).
 // timg (bf16 only, or nullptr): also the packed image of T^T per (head, slot),
-// TpLayout<bf16, 64>::PACK bytes each (ChunkParams::timg).
-hipError_t launch_chunk_states(const ChunkArgs &a, void *states, hipStream_t stream, void *timg = nullptr);
+// TpLayout<bf16, 64>::PACK bytes each (ChunkParams::timg).  four (bf16, dv % 64 == 0):
+// 64-column scan slices; after_prep (bf16, or nullptr): recorded on the stream once the
+// prep kernel (and the packed-sequence order) is enqueued, before the scan.
+hipError_t launch_chunk_states(const ChunkArgs &a, void *states, hipStream_t stream, void *timg = nullptr,
+                               bool four = false, hipEvent_t after_prep = nullptr);
 // The reverse scan of the state gradients on the same machinery, after
 // launch_chunk_states on the same workspace: dS' of every chunk into dstates
 // (the same layout as states), dL/dS_final from dsfin (or zeros), the
 // initial-state gradient into ds0 (or not written).
 hipError_t launch_chunk_rev(const ChunkArgs &a, const float *dsfin, const void *dout, float *ds0, void *dstates,
-                            hipStream_t stream);
+                            hipStream_t stream, bool four = false);
+// True when the backward's two state passes run side by side (64-column slices, both
+// within one round of workgroups on `cus` CUs): see kla_chunk.hip.
+bool bwd_scans_concurrent(const ChunkArgs &a, int cus);
 // a.eta holds the coefficient (beta when a.beta_direct, else eta); acc [N, H, dk] in place
 // PGDN's decode step on kla_decode_kernel (the shapes decode_supported lists)
 hipError_t launch_decode_pgdn(const DecodeArgs &a, float band_c, float *acc, hipStream_t stream);

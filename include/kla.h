@@ -265,7 +265,15 @@ kla_status_t kla_gdn_decode_step(const void *q, const void *k, const void *v,
  * Kernels run on `stream`: the forward's prep and scan kernels storing the
  * chunk-start states (BF16: the prep also writes the T image), a reverse scan
  * of the state gradients, and a parallel per-(chunk, head) gradient kernel
- * (F32: after a per-(chunk, head) prep of its own).
+ * (F32: after a per-(chunk, head) prep of its own).  BF16 calls whose two
+ * scans fit side by side on the GPU (2 * num_seqs * H * dv / 64 workgroups at
+ * most one per CU, dv a multiple of 64) run the reverse scan on a stream of
+ * the library's own (one per device, created on first use, default priority,
+ * kept until the process ends), ordered after the prep on `stream` and before
+ * the gradient kernel by two events: all work still completes in `stream`'s
+ * order, and the caller's stream semantics (and graph capture of `stream`)
+ * are unchanged.  Enqueues from several host threads are serialised around
+ * that fork and join.
  */
 kla_status_t kla_chunk_bwd(const void *q, const void *k, const void *v,
                            const void *g, const void *eta, float eps,
