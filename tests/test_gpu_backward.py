@@ -158,6 +158,21 @@ def test_bwd_gdn_with_the_kaczmarz_step_matches_kla():
     assert rel_err(f(b[4]) / f(den), f(a[4])) <= 1e-4
 
 
+def test_bwd_large_grid_sequential_scans():
+    """A grid too large for the two state passes to run side by side (2 x 8 sequences x 17 heads x
+    2 slices of 64 columns > one workgroup per CU): they run one after the other on the caller's
+    stream with 32-column slices.  Compared on three sampled heads of every sequence."""
+    x = inputs.make_prefill(B=8, H=17, T=150, dk=128, dv=128, chunk=64, s0_std=0.02, seed=2917,
+                            name="bwd-large-grid")
+    do, ds = inputs.make_upstream(x, 2917)
+    got = run_bwd(x, do, ds)
+    heads = [0, 9, 16]
+    ref = oracle_bwd(x, do, ds, heads=heads)
+    for name, a, b in zip(NAMES, got, ref):
+        e = rel_err(f(a)[:, heads], b[:, heads])
+        assert e <= TOL[torch.bfloat16], (name, e)
+
+
 def test_bwd_deterministic():
     x = inputs.make_prefill(B=1, H=2, T=200, dk=128, dv=128, chunk=64, s0_std=0.02, seed=27, name="det")
     do, ds = inputs.make_upstream(x, 27)
