@@ -561,9 +561,9 @@ def main():
                             "traffic": recorded_traffic("kla_chunk_bwd_b4_h16_t4096_hbm.md",
                                                         "gated_delta_rule_kla_amd/csrc/kla_chunk.hip",
                                                         "gated_delta_rule_kla_amd/csrc/kla_bwd.hip"),
-                            "kernel": "kla_chunk_bwd: the forward prep (with the T image) and scan "
-                                      "(states mode), the adjoint scan and the gradient kernel, "
-                                      "timed together per call",
+                            "kernel": "kla_chunk_bwd: the forward prep (with the T image), the forward "
+                                      "scan in states mode beside the adjoint scan, and the gradient "
+                                      "kernel, timed together per call",
                             "algorithmic_bytes_per_launch": bw["bytes"],
                             "algorithmic_flops_per_launch": bw["flops"]}}
         if args.mode == "backward":
