@@ -68,6 +68,20 @@ __global__ __launch_bounds__(decode_threads(DK, DV)) void kla_decode_kernel(
     s_q[i] = Elem<E>::to_f32(q[nh * DK + i]);
   }
 
+  // PGDN: the accumulator and key loads go out before the state's, so that the
+  // accumulator update, its mean and the write key are formed while the state is in
+  // flight (a wait for a load also waits for every load issued before it)
+  constexpr int NA = PG ? (DK + Sh::NT - 1) / Sh::NT : 1;
+  float av[NA], kk[NA];
+  if constexpr (PG) {
+#pragma unroll
+    for (int j = 0; j < NA; ++j) {
+      const int i = t + Sh::NT * j;
+      kk[j] = i < DK ? Elem<E>::to_f32(k[nh * DK + i]) : 0.f;
+      av[j] = i < DK ? acc[nh * DK + i] : 0.f;
+    }
+  }
+
   float *S = state + nh * (size_t)(DK * DV);
   f32x4 s[RPT];
 #pragma unroll
@@ -82,18 +96,11 @@ __global__ __launch_bounds__(decode_threads(DK, DV)) void kla_decode_kernel(
 
   if constexpr (PG) {
     // the accumulator, its mean over the coordinates, and the write key
-    constexpr int NA = (DK + Sh::NT - 1) / Sh::NT;
-    float av[NA], kk[NA], part = 0.f;
+    float part = 0.f;
 #pragma unroll
     for (int j = 0; j < NA; ++j) {
-      const int i = t + Sh::NT * j;
-      av[j] = 0.f;
-      kk[j] = 0.f;
-      if (i < DK) {
-        kk[j] = Elem<E>::to_f32(k[nh * DK + i]);
-        av[j] = fmaf(kk[j], kk[j], acc[nh * DK + i]);
-        part += av[j];
-      }
+      av[j] = fmaf(kk[j], kk[j], av[j]);  // zero past DK
+      part += av[j];
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off);
