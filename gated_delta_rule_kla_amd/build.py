@@ -19,7 +19,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libkla.so")
-SOURCES = ["kla_api.cpp", "kla_decode.hip", "kla_chunk.hip", "kla_bwd.hip", "kla_general.hip"]
+SOURCES = ["kla_api.cpp", "kla_decode.hip", "kla_chunk.hip", "kla_bwd.hip", "kla_general.hip", "kla_seg.hip"]
 ARCH = os.environ.get("KLA_OFFLOAD_ARCH", "gfx950")
 
 

@@ -87,17 +87,37 @@ kla_status_t decode_impl(const void *q, const void *k, const void *v, const void
   return from_hip(kla::launch_decode(a, reinterpret_cast<hipStream_t>(stream)));
 }
 
+// Segments of a forward call: seg_req < 0 the library's choice (0 where it keeps one
+// segment per sequence), 0 none, > 0 that many chunks each.  KLA_ERR_UNSUPPORTED for a
+// requested length on shapes the segmented scan does not run; KLA_ERR_SHAPE when the
+// segment grid would not fit its int indices.  *L = 0: one segment per sequence.
+kla_status_t seg_length(const kla::ChunkArgs &a, const int32_t *cu_seqlens_host, int seg_req, int *L) {
+  *L = 0;
+  if (seg_req == 0) return KLA_OK;
+  const bool chosen = seg_req < 0;
+  if (!kla::chunk_seg_supported(a.dtype, a.dk, a.dv, a.chunk)) return chosen ? KLA_OK : KLA_ERR_UNSUPPORTED;
+  const int len = chosen ? kla::chunk_auto_seg_chunks(a, cu_seqlens_host) : seg_req;
+  if (len <= 0) return KLA_OK;
+  const long long nseg = kla::chunk_seg_count(a, cu_seqlens_host, len);
+  if (nseg * a.H * (a.dv / 16 + a.dk / 16) > 0x7fffffffLL) return chosen ? KLA_OK : KLA_ERR_SHAPE;
+  *L = len;
+  return KLA_OK;
+}
+
 // static_scratch: take the workspace from the library's fixed per-GPU buffer
-// (kla_chunk_fwd_noalloc) instead of the caller's.
+// (kla_chunk_fwd_noalloc) instead of the caller's.  seg_req: as seg_length; with the
+// library's choice, a workspace (or scratch) too small for the segments' buffers
+// runs the call unsegmented.
 kla_status_t chunk_fwd_impl(const void *q, const void *k, const void *v, const void *g, const void *eta,
                             float eps, int beta_direct, const float *initial_state, void *o,
                             float *final_state, const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
                             int num_seqs, int B, int H, int T, int dk, int dv, int chunk, void *workspace,
                             size_t workspace_bytes, int dtype, void *stream,
-                            bool static_scratch = false) {
+                            bool static_scratch = false, int seg_req = -1) {
   const kla_status_t st =
       check_chunk_shapes(eps, cu_seqlens, cu_seqlens_host, num_seqs, B, H, T, dk, dv, chunk, dtype);
   if (st != KLA_OK) return st;
+  if (seg_req > 0 && !kla::chunk_seg_supported(dtype, dk, dv, chunk)) return KLA_ERR_UNSUPPORTED;
   if (num_seqs == 0) return KLA_OK;
   // token tensors are only dereferenced when there are tokens
   if ((long long)B * T > 0 && (!q || !k || !v || !g || !eta || !o)) return KLA_ERR_NULL;
@@ -106,7 +126,18 @@ kla_status_t chunk_fwd_impl(const void *q, const void *k, const void *v, const v
     return KLA_ERR_ALIGN;
   kla::ChunkArgs a = chunk_args(q, k, v, g, eta, eps, initial_state, o, final_state, cu_seqlens, num_seqs,
                                 B, H, T, dk, dv, chunk, dtype, workspace, beta_direct);
-  const size_t need = (long long)B * T > 0 ? kla::chunk_workspace_bytes(a) : 0;
+  int L = 0;
+  const kla_status_t sst = seg_length(a, cu_seqlens_host, seg_req, &L);
+  if (sst != KLA_OK) return sst;
+  size_t need = (long long)B * T > 0 ? kla::chunk_workspace_bytes(a) : 0;
+  if (L > 0) {
+    const size_t seg_need = kla::chunk_seg_workspace_bytes(a, cu_seqlens_host, L);
+    const size_t have = static_scratch ? kla::static_scratch_bytes() : (workspace ? workspace_bytes : 0);
+    if (seg_req < 0 && have < seg_need)
+      L = 0;  // the library's choice falls back to one segment per sequence
+    else
+      need = seg_need;
+  }
   if (static_scratch) {
     // every check above and this one run before the first HIP call
     if (need > kla::static_scratch_bytes()) return KLA_ERR_SCRATCH;
@@ -118,7 +149,22 @@ kla_status_t chunk_fwd_impl(const void *q, const void *k, const void *v, const v
   } else if (need > 0 && (workspace == nullptr || workspace_bytes < need)) {
     return KLA_ERR_WORKSPACE;
   }
+  if (L > 0) return from_hip(kla::launch_chunk_fwd_seg(a, cu_seqlens_host, L, reinterpret_cast<hipStream_t>(stream)));
   return from_hip(kla::launch_chunk_fwd(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
+size_t chunk_ws_impl(const int32_t *cu_seqlens, const int32_t *cu_seqlens_host, int num_seqs, int B, int H, int T,
+                     int dk, int dv, int chunk, int dtype, int seg_req) {
+  if (check_chunk_shapes(0.f, cu_seqlens, cu_seqlens_host, num_seqs, B, H, T, dk, dv, chunk, dtype) != KLA_OK)
+    return 0;
+  if (seg_req > 0 && !kla::chunk_seg_supported(dtype, dk, dv, chunk)) return 0;
+  if (num_seqs == 0) return 0;
+  const kla::ChunkArgs a = chunk_args(nullptr, nullptr, nullptr, nullptr, nullptr, 0.f, nullptr, nullptr, nullptr,
+                                      cu_seqlens, num_seqs, B, H, T, dk, dv, chunk, dtype, nullptr, 0);
+  int L = 0;
+  if (seg_length(a, cu_seqlens_host, seg_req, &L) != KLA_OK) return 0;
+  if (L > 0) return kla::chunk_seg_workspace_bytes(a, cu_seqlens_host, L);
+  return (long long)B * T == 0 ? 0 : kla::chunk_workspace_bytes(a);
 }
 
 kla_status_t chunk_bwd_impl(const void *q, const void *k, const void *v, const void *g, const void *eta,
@@ -245,13 +291,25 @@ const char *kla_status_str(kla_status_t s) {
 
 size_t kla_chunk_workspace_bytes(const int32_t *cu_seqlens, const int32_t *cu_seqlens_host, int num_seqs,
                                  int B, int H, int T, int dk, int dv, int chunk, kla_dtype_t dtype_) {
-  const int dtype = raw(dtype_);
-  if (check_chunk_shapes(0.f, cu_seqlens, cu_seqlens_host, num_seqs, B, H, T, dk, dv, chunk, dtype) != KLA_OK)
-    return 0;
-  if (num_seqs == 0 || (long long)B * T == 0) return 0;
-  return kla::chunk_workspace_bytes(chunk_args(nullptr, nullptr, nullptr, nullptr, nullptr, 0.f, nullptr,
-                                               nullptr, nullptr, cu_seqlens, num_seqs, B, H, T, dk, dv, chunk,
-                                               dtype, nullptr, 0));
+  return chunk_ws_impl(cu_seqlens, cu_seqlens_host, num_seqs, B, H, T, dk, dv, chunk, raw(dtype_), -1);
+}
+
+size_t kla_chunk_seg_workspace_bytes(const int32_t *cu_seqlens, const int32_t *cu_seqlens_host, int num_seqs,
+                                     int B, int H, int T, int dk, int dv, int chunk, kla_dtype_t dtype_,
+                                     int seg_chunks) {
+  if (seg_chunks < 0) return 0;
+  return chunk_ws_impl(cu_seqlens, cu_seqlens_host, num_seqs, B, H, T, dk, dv, chunk, raw(dtype_), seg_chunks);
+}
+
+kla_status_t kla_chunk_fwd_seg(const void *q, const void *k, const void *v, const void *g, const void *eta,
+                               float eps, const float *initial_state, void *o, float *final_state,
+                               const int32_t *cu_seqlens, const int32_t *cu_seqlens_host, int num_seqs, int B,
+                               int H, int T, int dk, int dv, int chunk, kla_dtype_t dtype_, int seg_chunks,
+                               void *workspace, size_t workspace_bytes, void *stream) {
+  if (seg_chunks < 0) return KLA_ERR_SHAPE;
+  return chunk_fwd_impl(q, k, v, g, eta, eps, 0, initial_state, o, final_state, cu_seqlens, cu_seqlens_host,
+                        num_seqs, B, H, T, dk, dv, chunk, workspace, workspace_bytes, raw(dtype_), stream, false,
+                        seg_chunks);
 }
 
 kla_status_t kla_chunk_fwd(const void *q, const void *k, const void *v, const void *g,

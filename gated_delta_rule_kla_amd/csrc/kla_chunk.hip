@@ -47,6 +47,7 @@
 #include "kla_internal.h"
 #include "kla_ops.h"
 
+#include <algorithm>
 #include <atomic>
 #include <mutex>
 #include <type_traits>
@@ -100,7 +101,31 @@ struct ChunkParams {
   float band_c;
   const float *pg_acc0;  // [N, H, dk] accumulator at each sequence's start, or nullptr (zeros)
   float *pg_accfin;      // [N, H, dk] at each sequence's end, or nullptr
+  // Segments (forward scan only; seg_first == nullptr: one segment per sequence).
+  // Sequence n is cut into segments of seg_chunks chunks (the last may be shorter,
+  // an empty sequence is one empty segment); its segments are seg_first[n] ..
+  // seg_first[n + 1] - 1 (N + 1 prefix sums), and group g of the scan grid is
+  // (segment g / H, head g % H).  A group's first n_vtiles column tiles carry v's
+  // columns: a sequence's first segment starts from s0, a later one from zero, and
+  // each writes its end state to seg_d.  The other n_tiles - n_vtiles tiles (later
+  // segments only) carry the identity: zero v, start state I (dk x dk), outputs to
+  // eout in o's place, end state (the segment's transfer map) to seg_m.
+  const int *seg_first;
+  int seg_chunks, n_vtiles;
+  void *eout;    // [B, H, T, dk] element type: the identity tiles' outputs
+  float *seg_d;  // [nseg, H, dk, dv]
+  float *seg_m;  // [nseg, H, dk, dk]
 };
+
+// The sequence of segment s: the largest n with seg_first[n] <= s (n < nseq).
+__device__ __forceinline__ int seg_sequence(const int *seg_first, int nseq, int s) {
+  int lo = 0, hi = nseq - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (seg_first[mid] <= s) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
 
 
 
@@ -1072,7 +1097,18 @@ __global__ __launch_bounds__(64 * (kWaves + (PG ? 1 : 0))) void kla_chunk_kernel
   if (gidx >= p.ngroups) return;  // padding (uniform per workgroup)
   const int jt = i8 % p.n_tiles;
   const int h = gidx % p.H;
-  const int n = p.order ? p.order[gidx / p.H] : gidx / p.H;
+  // segment (ChunkParams::seg_first): segment g of sequence n, its chunks from c_lo on
+  int n, seg = 0, g = 0;
+  if (p.seg_first) {
+    seg = gidx / p.H;
+    if (seg >= p.seg_first[p.nseq]) return;  // (only with a cu_seqlens that disagrees with its mirror)
+    n = seg_sequence(p.seg_first, p.nseq, seg);
+    g = seg - p.seg_first[n];
+  } else {
+    n = p.order ? p.order[gidx / p.H] : gidx / p.H;
+  }
+  const bool idt = jt >= p.n_vtiles;  // an identity tile
+  if (idt && g == 0) return;          // a first segment needs no transfer map
   const int nh = n * p.H + h;  // (sequence, head) index of the state arrays
   int b = n, t0 = 0, t1 = p.T, slot0;
   if (p.cu) {
@@ -1083,15 +1119,38 @@ __global__ __launch_bounds__(64 * (kWaves + (PG ? 1 : 0))) void kla_chunk_kernel
   } else {
     slot0 = n * ((p.T + C - 1) / C);
   }
+  if (p.seg_first) {
+    // (a segment past the sequence's end, possible only with a cu_seqlens that
+    // disagrees with its mirror, is empty)
+    const int c_lo = (int)min((long long)g * p.seg_chunks, (long long)(t1 - t0 + C - 1) / C);
+    slot0 += c_lo;
+    t0 = (int)min((long long)t0 + (long long)c_lo * C, (long long)t1);
+    t1 = (int)min((long long)t1, (long long)t0 + (long long)p.seg_chunks * C);
+  }
   const int len = t1 - t0;
   const int nch = (len + C - 1) / C;
   const size_t row0 = ((size_t)b * p.H + h) * (size_t)p.T + (size_t)t0;
   const E *gq = static_cast<const E *>(p.q);
   const E *gk = static_cast<const E *>(p.k);
   const E *gv = static_cast<const E *>(p.v);
-  E *go = static_cast<E *>(p.o);
   const char *ws = p.ws + (size_t)h * p.nslot * TL::BYTES;
   const int dv = p.dv;
+  // this tile's state arrays (row stride ld_s, first column col_s): start (nullptr:
+  // zero, or I for an identity tile) and end; its output rows (row stride ld_s)
+  const int ld_s = idt ? DK : dv;
+  const int col_s = (idt ? jt - p.n_vtiles : jt) * DVT;
+  const float *s_init = idt || g > 0 || !p.s0 ? nullptr : p.s0 + (size_t)nh * DK * dv;
+  float *s_fin;
+  if (!p.seg_first)
+    s_fin = p.sfin ? p.sfin + (size_t)nh * DK * dv : nullptr;
+  else if (idt)
+    s_fin = p.seg_m + ((size_t)seg * p.H + h) * DK * DK;
+  else
+    s_fin = p.seg_d + ((size_t)seg * p.H + h) * DK * dv;
+  E *go = static_cast<E *>(idt ? p.eout : p.o);
+  auto s_start = [&](int row, int col) {
+    return idt ? (row == col ? 1.f : 0.f) : (s_init ? s_init[(size_t)row * ld_s + col] : 0.f);
+  };
   auto nrow_of = [&](int c) { return min(C, len - c * C); };
   auto tok0_of = [&](int c) { return row0 + (size_t)c * C; };
   // a prefetch past the last chunk re-reads the last chunk
@@ -1101,12 +1160,11 @@ __global__ __launch_bounds__(64 * (kWaves + (PG ? 1 : 0))) void kla_chunk_kernel
   const int iend = nch + (nch & 1);
 
   if (nch == 0) {
-    // empty sequence: the final state is the initial state
-    if (p.sfin) {
-      const size_t sbase = (size_t)nh * DK * (size_t)dv;
+    // empty sequence (or segment): the final state is the initial state
+    if (s_fin) {
       for (int e = threadIdx.x; e < DK * DVT; e += Sh::NT) {
-        const size_t off = sbase + (size_t)(e / DVT) * dv + (size_t)jt * DVT + (e % DVT);
-        p.sfin[off] = p.s0 ? p.s0[off] : 0.f;
+        const int row = e / DVT, col = col_s + e % DVT;
+        s_fin[(size_t)row * ld_s + col] = s_start(row, col);
       }
     }
     return;
@@ -1143,15 +1201,13 @@ __global__ __launch_bounds__(64 * (kWaves + (PG ? 1 : 0))) void kla_chunk_kernel
     constexpr int NCW = CT0 < NCT ? (NCT - CT0 < Sh::NCW ? NCT - CT0 : Sh::NCW) : 0;
     constexpr int NCW1 = NCW > 0 ? NCW : 1;
     f32x4 accS[NCW1][DK / 16];
-    const size_t sbase = (size_t)nh * DK * (size_t)dv;
 #pragma unroll
     for (int ct = 0; ct < NCW; ++ct) {
-      const int col = jt * DVT + 16 * (CT0 + ct) + li;
+      const int col = col_s + 16 * (CT0 + ct) + li;
 #pragma unroll
       for (int it = 0; it < DK / 16; ++it)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          accS[ct][it][j] = p.s0 ? p.s0[sbase + (size_t)(16 * it + 4 * lg + j) * dv + col] : 0.f;
+        for (int j = 0; j < 4; ++j) accS[ct][it][j] = s_start(16 * it + 4 * lg + j, col);
     }
     // chunk-start S as right operands, straight from the accumulators; also
     // published for the P waves (their Q S of that chunk)
@@ -1263,14 +1319,14 @@ __global__ __launch_bounds__(64 * (kWaves + (PG ? 1 : 0))) void kla_chunk_kernel
       }
       lds_barrier();
     }
-    if (p.sfin) {
+    if (s_fin) {
 #pragma unroll
       for (int ct = 0; ct < NCW; ++ct) {
-        const int col = jt * DVT + 16 * (CT0 + ct) + li;
+        const int col = col_s + 16 * (CT0 + ct) + li;
 #pragma unroll
         for (int it = 0; it < DK / 16; ++it)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) p.sfin[sbase + (size_t)(16 * it + 4 * lg + j) * dv + col] = accS[ct][it][j];
+          for (int j = 0; j < 4; ++j) s_fin[(size_t)(16 * it + 4 * lg + j) * ld_s + col] = accS[ct][it][j];
       }
     }
     };
@@ -1319,7 +1375,7 @@ __global__ __launch_bounds__(64 * (kWaves + (PG ? 1 : 0))) void kla_chunk_kernel
           for (int k = 0; k < NOWN; ++k) {
             const int r = 16 * BL::at(k) + li;
             if (r < nrow) {
-              E *orow = go + (tok0 + r) * (size_t)dv + jt * DVT + 4 * lg;
+              E *orow = go + (tok0 + r) * (size_t)ld_s + col_s + 4 * lg;
 #pragma unroll
               for (int ct = 0; ct < NCT; ++ct) store4(orow + 16 * ct, ao[ct][k]);
             }
@@ -1481,7 +1537,8 @@ __global__ __launch_bounds__(64 * (kWaves + (PG ? 1 : 0))) void kla_chunk_kernel
     auto fetch = [&](int c, auto set_c) {
       constexpr int S = decltype(set_c)::value;
       tin[S].issue(ws + (size_t)(slot0 + c) * TL::BYTES, lane);
-      vin[S].issue(gv + tok0_of(c) * dv, nrow_of(c), dv, jt * DVT, lane);
+      // an identity tile's v is zero: a load range of no rows reads zeros
+      vin[S].issue(gv + tok0_of(c) * dv, idt ? 0 : nrow_of(c), dv, idt ? 0 : jt * DVT, lane);
     };
     fetch(0, std::integral_constant<int, 0>{});
     if constexpr (NSET == 2) fetch(clampc(1), std::integral_constant<int, NSET - 1>{});
@@ -1941,12 +1998,26 @@ struct PgArgs {
   float *accfin;
 };
 
+// The segment-parallel scan's buffers (ChunkParams::seg_first and after).
+struct SegArgs {
+  const int *seg_first;
+  int seg_chunks;
+  long long nseg;
+  void *eout;
+  float *seg_d, *seg_m;
+};
+
 template <typename E, int C, int DK, int NCT, bool PG = false>
 static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t st, char *states = nullptr,
                                   char *timg = nullptr, const PgArgs *pg = nullptr,
-                                  hipEvent_t after_prep = nullptr) {
+                                  hipEvent_t after_prep = nullptr, const SegArgs *seg = nullptr) {
   using Sh = ChunkShape<E, C, DK, NCT, PG>;
+  static_assert(DK % Sh::DVT == 0, "identity tiles cover dk");
   ChunkParams p;
+  p.seg_first = nullptr;
+  p.seg_chunks = 0;
+  p.eout = nullptr;
+  p.seg_d = p.seg_m = nullptr;
   p.states = states;
   p.timg = timg;
   p.pg_w = pg ? pg->w : nullptr;
@@ -1969,14 +2040,14 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t st, char *state
   p.T = a.T;
   p.dv = a.dv;
   p.n_tiles = a.dv / Sh::DVT;
+  p.n_vtiles = p.n_tiles;
   p.nseq = a.num_seqs;
   p.beta_direct = a.beta_direct;
   p.nslot = slots_per_head(a.cu_seqlens != nullptr, a.B, a.T, a.num_seqs, C);
   p.ngroups = a.num_seqs * a.H;
   p.order = nullptr;
-  const long long nblk = ((long long)p.ngroups + 7) / 8 * 8 * p.n_tiles;
   if (p.ngroups == 0) return hipSuccess;
-  if (a.cu_seqlens && a.num_seqs > 1 && a.num_seqs <= kMaxOrdered && (long long)a.B * a.T > 0) {
+  if (!seg && a.cu_seqlens && a.num_seqs > 1 && a.num_seqs <= kMaxOrdered && (long long)a.B * a.T > 0) {
     int *order = reinterpret_cast<int *>(static_cast<char *>(a.workspace) + order_offset_t<E, C>(a));
     hipLaunchKernelGGL(kla_seq_order_kernel, dim3((unsigned)((a.num_seqs + 255) / 256)), dim3(256), 0, st,
                        a.cu_seqlens, a.num_seqs, a.T, order);
@@ -2032,6 +2103,17 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t st, char *state
     const hipError_t e = hipEventRecord(after_prep, st);
     if (e != hipSuccess) return e;
   }
+  if (seg) {
+    // groups are (segment, head); later segments add the identity tiles
+    p.seg_first = seg->seg_first;
+    p.seg_chunks = seg->seg_chunks;
+    p.eout = seg->eout;
+    p.seg_d = seg->seg_d;
+    p.seg_m = seg->seg_m;
+    p.n_tiles = p.n_vtiles + DK / Sh::DVT;
+    p.ngroups = (int)(seg->nseg * a.H);
+  }
+  const long long nblk = ((long long)p.ngroups + 7) / 8 * 8 * p.n_tiles;
   hipLaunchKernelGGL((kla_chunk_kernel<E, C, DK, NCT, PG>), dim3((unsigned)nblk), dim3(Sh::NT), 0, st, p);
   return hipGetLastError();
 }
@@ -2055,9 +2137,13 @@ bool fast_chunk_supported(int dtype, int dk, int dv, int chunk) {
 
 // Column slice width: 32 columns (two column tiles per workgroup) when that
 // still gives at least one workgroup per CU, else 16 (more workgroups, more
-// redundant S-independent work per column).
-static bool use_two_column_tiles(const ChunkArgs &a) {
-  return a.dv % 32 == 0 && (long long)a.num_seqs * a.H * (a.dv / 32) >= 256;
+// redundant S-independent work per column).  The forward scan takes 32 columns
+// down to half a workgroup per CU: with 16-column slices every step reloads K, Q
+// and T' per 16 columns, and for few long sequences that L2 traffic costs more than
+// the idle CUs (T=65536 H=16 dv=256: 1.20 ms with 128 two-tile workgroups against
+// 1.34 ms with 256 one-tile ones).
+static bool use_two_column_tiles(const ChunkArgs &a, bool fwd = false) {
+  return a.dv % 32 == 0 && (long long)a.num_seqs * a.H * (a.dv / 32) >= (fwd ? 128 : 256);
 }
 // 64 columns (four tiles) when that still leaves at least eight workgroups per CU
 // (throughput-bound grids: a step costs about 1.5x the two-tile step for twice
@@ -2073,7 +2159,7 @@ static hipError_t launch_fast(const ChunkArgs &a, hipStream_t st, char *states, 
       if (a.dk == 128) return launch_chunk_t<bf16, 64, 128, 4>(a, st, states, timg, nullptr, after_prep);
       if (a.dk == 64) return launch_chunk_t<bf16, 64, 64, 4>(a, st, states, timg, nullptr, after_prep);
     }
-    const bool two = use_two_column_tiles(a);
+    const bool two = use_two_column_tiles(a, states == nullptr);
     if (a.dk == 128)
       return two ? launch_chunk_t<bf16, 64, 128, 2>(a, st, states, timg, nullptr, after_prep)
                  : launch_chunk_t<bf16, 64, 128, 1>(a, st, states, timg, nullptr, after_prep);
@@ -2122,7 +2208,7 @@ hipError_t launch_pgdn_fast(const ChunkArgs &a, const GenExtra &x, hipStream_t s
   char *ws = static_cast<char *>(a.workspace);
   const PgArgs pg{ws + pgdn_w_offset(a), reinterpret_cast<float *>(ws + pgdn_acc_offset(a)), x.band_c,
                   x.initial_acc, x.final_acc};
-  const bool two = use_two_column_tiles(a);
+  const bool two = use_two_column_tiles(a, true);
   if (a.dk == 128)
     return two ? launch_chunk_t<bf16, 64, 128, 2, true>(a, st, nullptr, nullptr, &pg)
                : launch_chunk_t<bf16, 64, 128, 1, true>(a, st, nullptr, nullptr, &pg);
@@ -2136,6 +2222,133 @@ hipError_t launch_chunk_fwd(const ChunkArgs &a, hipStream_t st) {
     return launch_chunk_general(a, none, st);
   }
   return launch_fast(a, st, nullptr);
+}
+
+// ---------------------------------------------------------------------------
+// the segment-parallel forward (kla_seg.hip has the bookkeeping kernels)
+// ---------------------------------------------------------------------------
+// Workgroups the library's own choice of segments aims at: one per CU of an MI355X.
+constexpr int kSegTargetGroups = 256;
+
+static int seq_chunks_host(const ChunkArgs &a, const int32_t *cu_host, int n) {
+  const long long len = a.cu_seqlens ? (long long)cu_host[n + 1] - cu_host[n] : a.T;
+  return (int)((len + a.chunk - 1) / a.chunk);
+}
+
+long long chunk_seg_count(const ChunkArgs &a, const int32_t *cu_host, int L) {
+  auto segs = [&](long long nch) { return std::max(1LL, (nch + L - 1) / L); };
+  if (!a.cu_seqlens) return (long long)a.num_seqs * segs(((long long)a.T + a.chunk - 1) / a.chunk);
+  long long total = 0;
+  for (int n = 0; n < a.num_seqs; ++n) total += segs(seq_chunks_host(a, cu_host, n));
+  return total;
+}
+
+bool chunk_seg_supported(int dtype, int dk, int dv, int chunk) { return fast_chunk_supported(dtype, dk, dv, chunk); }
+
+namespace {
+struct SegLayout {
+  long long nseg;
+  size_t first, e, d, m, fix, end;
+};
+size_t up256(size_t x) { return (x + 255) / 256 * 256; }
+SegLayout seg_layout(const ChunkArgs &a, const int32_t *cu_host, int L) {
+  SegLayout l;
+  const size_t esz = a.dtype == 0 ? 2 : 4;
+  l.nseg = chunk_seg_count(a, cu_host, L);
+  const size_t nsh = (size_t)l.nseg * a.H;
+  l.first = up256(chunk_workspace_bytes(a));
+  l.e = l.first + up256(((size_t)a.num_seqs + 1) * 4);
+  l.d = l.e + up256((size_t)a.B * a.H * a.T * a.dk * esz);
+  l.m = l.d + up256(nsh * a.dk * a.dv * 4);
+  l.fix = l.m + up256(nsh * a.dk * a.dk * 4);
+  l.end = l.fix + up256(nsh * a.dk * a.dv * 4);
+  return l;
+}
+}  // namespace
+
+size_t chunk_seg_workspace_bytes(const ChunkArgs &a, const int32_t *cu_host, int L) {
+  return L > 0 ? seg_layout(a, cu_host, L).end : chunk_workspace_bytes(a);
+}
+
+// The library's choice: segments only where the plain scan leaves CUs idle (fewer
+// than one two-tile workgroup per CU) on long sequences, bf16 with 64-column tiles.
+// The smallest segment length whose grid (v's tiles for every segment, the identity
+// tiles for the later ones) still fits one round of workgroups, if that cuts the
+// longest sequence into at least three segments (a 64-column step costs about 1.75
+// two-column-tile steps, and the correction pass costs about a tenth of the scan).
+int chunk_auto_seg_chunks(const ChunkArgs &a, const int32_t *cu_host) {
+  if (a.dtype != 0 || a.chunk != 64 || (a.dk != 64 && a.dk != 128) || a.dv % 64 != 0) return 0;
+  if (a.num_seqs <= 0 || (a.cu_seqlens && !cu_host)) return 0;
+  if ((long long)a.num_seqs * a.H * (a.dv / 32) >= kSegTargetGroups) return 0;
+  int nch_max = 0;
+  for (int n = 0; n < (a.cu_seqlens ? a.num_seqs : 1); ++n) nch_max = std::max(nch_max, seq_chunks_host(a, cu_host, n));
+  if (nch_max < 96) return 0;
+  for (int G = 8; G >= 3; --G) {
+    const int L = (nch_max + G - 1) / G;
+    long long groups = 0;
+    for (int n = 0; n < a.num_seqs; ++n) {
+      const long long nch = a.cu_seqlens ? seq_chunks_host(a, cu_host, n) : nch_max;
+      const long long S = std::max(1LL, (nch + L - 1) / L);
+      groups += (long long)a.H * (S * (a.dv / 64) + (S - 1) * (a.dk / 64));
+    }
+    if (groups <= kSegTargetGroups) return L;
+  }
+  return 0;
+}
+
+template <typename E, int C, int DK>
+static hipError_t seg_scan_t(const ChunkArgs &a, const SegArgs &sa, hipStream_t st) {
+  if constexpr (std::is_same<E, bf16>::value) {
+    if (a.dv % 64 == 0) return launch_chunk_t<E, C, DK, 4>(a, st, nullptr, nullptr, nullptr, nullptr, &sa);
+    if (a.dv % 32 == 0) return launch_chunk_t<E, C, DK, 2>(a, st, nullptr, nullptr, nullptr, nullptr, &sa);
+  }
+  return launch_chunk_t<E, C, DK, 1>(a, st, nullptr, nullptr, nullptr, nullptr, &sa);
+}
+
+hipError_t launch_chunk_fwd_seg(const ChunkArgs &a, const int32_t *cu_host, int L, hipStream_t st) {
+  if (!chunk_seg_supported(a.dtype, a.dk, a.dv, a.chunk) || L <= 0) return hipErrorInvalidValue;
+  const SegLayout lay = seg_layout(a, cu_host, L);
+  char *ws = static_cast<char *>(a.workspace);
+  int *seg_first = reinterpret_cast<int *>(ws + lay.first);
+  SegFixParams f;
+  f.cu = a.cu_seqlens;
+  f.seg_first = seg_first;
+  f.nseq = a.num_seqs;
+  f.H = a.H;
+  f.T = a.T;
+  f.C = a.chunk;
+  f.dk = a.dk;
+  f.dv = a.dv;
+  f.dtype = a.dtype;
+  f.seg_chunks = L;
+  f.nseg = lay.nseg;
+  f.seg_d = reinterpret_cast<float *>(ws + lay.d);
+  f.seg_m = reinterpret_cast<float *>(ws + lay.m);
+  f.sfin = a.final_state;
+  f.sfix = ws + lay.fix;
+  f.eout = ws + lay.e;
+  f.o = a.o;
+  if (a.num_seqs == 0) return hipSuccess;
+  hipError_t e = launch_seg_table(f, seg_first, st);
+  if (e != hipSuccess) return e;
+  const SegArgs sa{seg_first, L, lay.nseg, ws + lay.e, reinterpret_cast<float *>(ws + lay.d),
+                   reinterpret_cast<float *>(ws + lay.m)};
+  ChunkArgs b = a;
+  b.final_state = nullptr;  // the end states go to seg_d; the combine writes the final state
+  if (a.dtype == 0) {
+    e = a.dk == 128 ? seg_scan_t<bf16, 64, 128>(b, sa, st) : seg_scan_t<bf16, 64, 64>(b, sa, st);
+  } else if (a.chunk == 16) {
+    switch (a.dk) {
+      case 16: e = seg_scan_t<float, 16, 16>(b, sa, st); break;
+      case 32: e = seg_scan_t<float, 16, 32>(b, sa, st); break;
+      case 64: e = seg_scan_t<float, 16, 64>(b, sa, st); break;
+      default: e = seg_scan_t<float, 16, 128>(b, sa, st); break;
+    }
+  } else {
+    e = a.dk == 16 ? seg_scan_t<float, 64, 16>(b, sa, st) : seg_scan_t<float, 64, 32>(b, sa, st);
+  }
+  if (e != hipSuccess) return e;
+  return launch_seg_finish(f, st);
 }
 
 template <typename E, int C, int DK, int NCT>

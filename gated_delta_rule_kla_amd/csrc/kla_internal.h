@@ -98,6 +98,37 @@ hipError_t launch_chunk_states(const ChunkArgs &a, void *states, hipStream_t str
 // initial-state gradient into ds0 (or not written).
 hipError_t launch_chunk_rev(const ChunkArgs &a, const float *dsfin, const void *dout, float *ds0, void *dstates,
                             hipStream_t stream, bool four = false);
+// The segment-parallel forward (kla_chunk.hip, kla_seg.hip): each sequence cut into
+// segments of L chunks, scanned side by side, then combined and corrected.
+// chunk_seg_supported: the shapes it runs (the pipelined kernels').  chunk_seg_count:
+// segments for L (cu_host: the host mirror, for packed sequences).  The workspace
+// holds kla_chunk_fwd's, then the segment table, the identity tiles' outputs E
+// ([B, H, T, dk], element type), the segments' end states and transfer maps and the
+// corrections' start states.  chunk_auto_seg_chunks: the library's choice of L for
+// kla_chunk_fwd (0: no segments), host-only.
+bool chunk_seg_supported(int dtype, int dk, int dv, int chunk);
+long long chunk_seg_count(const ChunkArgs &a, const int32_t *cu_host, int L);
+size_t chunk_seg_workspace_bytes(const ChunkArgs &a, const int32_t *cu_host, int L);
+int chunk_auto_seg_chunks(const ChunkArgs &a, const int32_t *cu_host);
+hipError_t launch_chunk_fwd_seg(const ChunkArgs &a, const int32_t *cu_host, int L, hipStream_t stream);
+
+// What the combine and correction kernels of the segmented forward read and write.
+struct SegFixParams {
+  const int32_t *cu;     // device cu_seqlens or nullptr (dense)
+  const int *seg_first;  // [nseq + 1] first segment of each sequence
+  int nseq, H, T, C, dk, dv, dtype, seg_chunks;
+  long long nseg;
+  const float *seg_d;  // [nseg, H, dk, dv] end states (first segments: from the initial state)
+  const float *seg_m;  // [nseg, H, dk, dk] transfer maps (later segments)
+  float *sfin;         // [nseq, H, dk, dv] final states, or nullptr
+  void *sfix;          // the later segments' start states (bf16 MFMA groups or fp32 rows)
+  const void *eout;    // [B, H, T, dk] the identity tiles' outputs
+  void *o;             // [B, H, T, dv] outputs, corrected in place
+};
+hipError_t launch_seg_table(const SegFixParams &f, int *seg_first, hipStream_t stream);
+hipError_t launch_seg_finish(const SegFixParams &f, hipStream_t stream);
+bool seg_correct_mfma(int dtype, int dk, int dv);
+
 // True when the backward's two state passes run side by side (64-column slices, both
 // within one round of workgroups on `cus` CUs): see kla_chunk.hip.
 bool bwd_scans_concurrent(const ChunkArgs &a, int cus);

@@ -56,6 +56,11 @@ def lib() -> ctypes.CDLL:
         L.kla_chunk_fwd.restype = i32
         L.kla_chunk_workspace_bytes.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, i32, i32]
         L.kla_chunk_workspace_bytes.restype = sz
+        L.kla_chunk_fwd_seg.argtypes = [vp, vp, vp, vp, vp, f32, vp, vp, vp, vp, vp,
+                                        i32, i32, i32, i32, i32, i32, i32, i32, i32, vp, sz, vp]
+        L.kla_chunk_fwd_seg.restype = i32
+        L.kla_chunk_seg_workspace_bytes.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, i32]
+        L.kla_chunk_seg_workspace_bytes.restype = sz
         L.kla_decode_step.argtypes = [vp, vp, vp, vp, vp, f32, vp, vp,
                                       i32, i32, i32, i32, i32, vp]
         L.kla_decode_step.restype = i32
@@ -120,7 +125,7 @@ def _need(t: torch.Tensor, name: str, dtype: torch.dtype, shape, device) -> None
 
 
 def _chunk_call(fn: str, q, k, v, g, coef, eps, initial_state, cu_seqlens, chunk, output_final_state,
-                cu_seqlens_host, out, final_state, workspace):
+                cu_seqlens_host, out, final_state, workspace, seg_chunks=None):
     dev = q.device
     if dev.type != "cuda":
         raise ValueError(f"kla.{fn} needs GPU tensors")
@@ -164,15 +169,25 @@ def _chunk_call(fn: str, q, k, v, g, coef, eps, initial_state, cu_seqlens, chunk
         return out, final_state
     if isinstance(workspace, str):
         raise ValueError(f"kla.{fn}: workspace must be a tensor or None ('static' is for chunk_fwd only)")
-    ws_bytes = lib().kla_chunk_workspace_bytes(_ptr(cu_seqlens), host_ptr, N, B, H, T, dk, dv, int(chunk),
-                                               _DTYPES[dtype])
+    if seg_chunks is not None:
+        if eps is None:
+            raise ValueError(f"kla.{fn}: seg_chunks is for chunk_fwd only")
+        ws_bytes = lib().kla_chunk_seg_workspace_bytes(_ptr(cu_seqlens), host_ptr, N, B, H, T, dk, dv, int(chunk),
+                                                       _DTYPES[dtype], int(seg_chunks))
+    else:
+        ws_bytes = lib().kla_chunk_workspace_bytes(_ptr(cu_seqlens), host_ptr, N, B, H, T, dk, dv, int(chunk),
+                                                   _DTYPES[dtype])
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     elif workspace.device != dev or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous uint8 tensor on the inputs' device")
     tail = (_ptr(initial_state), _ptr(out), _ptr(final_state), _ptr(cu_seqlens), host_ptr, N, B, H, T, dk, dv,
             int(chunk), _DTYPES[dtype], _ptr(workspace), workspace.numel(), _stream(dev))
-    if eps is not None:
+    if seg_chunks is not None:
+        st = lib().kla_chunk_fwd_seg(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(coef), float(eps), *tail[:13],
+                                     int(seg_chunks), *tail[13:])
+        _check("kla_chunk_fwd_seg", st)
+    elif eps is not None:
         st = lib().kla_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(coef), float(eps), *tail)
         _check("kla_chunk_fwd", st)
     else:
@@ -196,6 +211,7 @@ def chunk_fwd(
     out: Optional[torch.Tensor] = None,
     final_state: Optional[torch.Tensor] = None,
     workspace: Optional[torch.Tensor] = None,
+    seg_chunks: Optional[int] = None,
 ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """KLA chunkwise prefill (kla_chunk_fwd).
 
@@ -209,9 +225,14 @@ def chunk_fwd(
     kla_chunk_fwd_noalloc instead, which uses the library's fixed per-GPU
     scratch buffer (KLA_NOALLOC_SCRATCH_BYTES, 64 MiB) and allocates nothing
     (pass ``out`` and ``final_state`` to keep the call allocation-free here too).
+    ``seg_chunks`` (kla_chunk_fwd_seg): None lets the library choose whether to cut
+    long sequences into segments scanned side by side; 0 never cuts; n > 0 cuts
+    every sequence into segments of n chunks.
     """
+    if seg_chunks is not None and isinstance(workspace, str):
+        raise ValueError("kla.chunk_fwd: seg_chunks needs a workspace tensor or None")
     return _chunk_call("chunk_fwd", q, k, v, g, eta, eps, initial_state, cu_seqlens, chunk,
-                       output_final_state, cu_seqlens_host, out, final_state, workspace)
+                       output_final_state, cu_seqlens_host, out, final_state, workspace, seg_chunks)
 
 
 NOALLOC_SCRATCH_BYTES = 64 << 20  # KLA_NOALLOC_SCRATCH_BYTES in include/kla.h
@@ -240,16 +261,21 @@ def gdn_chunk_fwd(
 
 def chunk_workspace_bytes(B: int, H: int, T: int, dk: int, dv: int, chunk: int = 64,
                           dtype: torch.dtype = torch.bfloat16,
-                          cu_seqlens_host: Optional[torch.Tensor] = None) -> int:
-    """Workspace bytes kla_chunk_fwd needs (kla_chunk_workspace_bytes); 0 for
+                          cu_seqlens_host: Optional[torch.Tensor] = None,
+                          seg_chunks: Optional[int] = None) -> int:
+    """Workspace bytes kla_chunk_fwd needs (kla_chunk_workspace_bytes), or
+    kla_chunk_fwd_seg with ``seg_chunks`` (kla_chunk_seg_workspace_bytes); 0 for
     arguments it would reject.  With packed sequences pass the host int32
     cu_seqlens (B must be 1)."""
     if cu_seqlens_host is not None:
         cu = cu_seqlens_host.to(torch.int32).contiguous()
         # the device pointer is only tested for NULL here
-        return lib().kla_chunk_workspace_bytes(ctypes.c_void_p(16), cu.data_ptr(), cu.numel() - 1, B, H, T,
-                                               dk, dv, int(chunk), _DTYPES[dtype])
-    return lib().kla_chunk_workspace_bytes(None, None, B, B, H, T, dk, dv, int(chunk), _DTYPES[dtype])
+        args = (ctypes.c_void_p(16), cu.data_ptr(), cu.numel() - 1, B, H, T, dk, dv, int(chunk), _DTYPES[dtype])
+    else:
+        args = (None, None, B, B, H, T, dk, dv, int(chunk), _DTYPES[dtype])
+    if seg_chunks is not None:
+        return lib().kla_chunk_seg_workspace_bytes(*args, int(seg_chunks))
+    return lib().kla_chunk_workspace_bytes(*args)
 
 
 def pgdn_chunk_workspace_bytes(B: int, H: int, T: int, dk: int, dv: int, chunk: int = 64,

@@ -164,18 +164,77 @@ kla_status_t kla_chunk_fwd_noalloc(const void *q, const void *k, const void *v,
  * call.  Returns 0 for sizes kla_chunk_fwd would reject for both element
  * types, and when no workspace is needed (no tokens).  Callers that know the
  * dtype and cu_seqlens may use the exact kla_chunk_workspace_bytes below.
+ * For packed sequences it covers the unsegmented need (and the segmented one of
+ * a single long sequence): with less than a call's segmented need, kla_chunk_fwd
+ * runs that call unsegmented (see kla_chunk_fwd_seg).
  */
 size_t kla_chunk_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk, int num_seqs);
 
 /*
  * kla_chunk_workspace_bytes -- device workspace kla_chunk_fwd needs for these
  * arguments (the same meaning as there; host-only, no HIP call).  6,912
- * bytes per (64-token chunk, head) in bf16.  kla_gdn_chunk_fwd needs the same.  Returns 0 when no workspace is
+ * bytes per (64-token chunk, head) in bf16, plus the segments' buffers where
+ * kla_chunk_fwd cuts sequences into segments (kla_chunk_fwd_seg below).
+ * kla_gdn_chunk_fwd needs the same.  Returns 0 when no workspace is
  * needed (no tokens) and also for arguments kla_chunk_fwd would reject.
  */
 size_t kla_chunk_workspace_bytes(const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
                                  int num_seqs, int B, int H, int T, int dk, int dv, int chunk,
                                  kla_dtype_t dtype);
+
+/*
+ * kla_chunk_fwd_seg -- kla_chunk_fwd with the sequences cut into segments that
+ * are scanned side by side (the segment-parallel scan), for grids where few long
+ * sequences leave most CUs idle.
+ *
+ * The chunk update of the state is affine, S' = M_c S + D_c, and so is each chunk's
+ * output in its start state (§"Implementación": the chunkwise block solver).
+ * Every sequence is cut into segments of `seg_chunks` chunks (the last one may be
+ * shorter; a sequence of at most seg_chunks chunks stays whole), and all segments
+ * are scanned at once: a sequence's first segment from its initial state, every
+ * later one from zero, together with dk extra state columns that start from the
+ * identity with v = 0 -- their end state is the segment's transfer map M (the
+ * product of its M_c) and their outputs E give how the segment's outputs depend on
+ * its start state.  A combine kernel then chains the segments in order in fp32
+ * (S_start of segment s+1 = M_s S_start(s) + D_s, the last one the final state)
+ * and a correction kernel adds E S_start to every later segment's outputs.  The
+ * result equals kla_chunk_fwd's up to rounding.
+ *
+ *   seg_chunks  0: one segment per sequence (exactly kla_chunk_fwd's kernels);
+ *               n > 0: segments of n chunks; negative: KLA_ERR_SHAPE.
+ *   workspace   at least kla_chunk_seg_workspace_bytes(..., seg_chunks) bytes:
+ *               kla_chunk_fwd's, then per call (N + 1) ints of segment table,
+ *               E ([B, H, T, dk] in dtype), and per (segment, head) dk x dv
+ *               (end state) + dk x dk (transfer map) + dk x dv (start state)
+ *               fp32.
+ *   Other arguments, ownership and errors as kla_chunk_fwd.  seg_chunks > 0 on a
+ *   combination outside the pipelined kernels' (BF16 chunk 64 dk 64/128, F32
+ *   chunk 16 or chunk 64 with dk 16/32) returns KLA_ERR_UNSUPPORTED.
+ *
+ * kla_chunk_fwd (and kla_gdn_chunk_fwd) choose segments themselves -- BF16, chunk
+ * 64, dk 64 or 128, dv a multiple of 64, fewer than 256 workgroups of 32 state
+ * columns (N * H * dv / 32 < 256) and at least 96 chunks in the longest sequence:
+ * the shortest segments whose scan grid still fits 256 workgroups, if that cuts
+ * the longest sequence in three or more -- and only when the workspace they are
+ * given holds the segments' buffers (kla_chunk_workspace_bytes includes them);
+ * with a smaller workspace of at least the unsegmented size they run unsegmented.
+ * kla_chunk_fwd_noalloc does the same against its fixed buffer.
+ */
+kla_status_t kla_chunk_fwd_seg(const void *q, const void *k, const void *v,
+                               const void *g, const void *eta, float eps,
+                               const float *initial_state, void *o, float *final_state,
+                               const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
+                               int num_seqs, int B, int H, int T, int dk, int dv, int chunk,
+                               kla_dtype_t dtype, int seg_chunks, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
+/*
+ * kla_chunk_seg_workspace_bytes -- device workspace kla_chunk_fwd_seg needs for
+ * these arguments (host-only, no HIP call); 0 for arguments it would reject.
+ */
+size_t kla_chunk_seg_workspace_bytes(const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
+                                     int num_seqs, int B, int H, int T, int dk, int dv, int chunk,
+                                     kla_dtype_t dtype, int seg_chunks);
 
 /*
  * kla_decode_step -- one recurrent step for N sequences x H heads.
@@ -392,7 +451,7 @@ const char *kla_status_str(kla_status_t s);
 /* ABI version of this header (incremented on any incompatible change). */
 int kla_abi_version(void);
 
-#define KLA_ABI_VERSION 8
+#define KLA_ABI_VERSION 9
 
 /* Size of kla_chunk_fwd_noalloc's fixed per-GPU scratch buffer, in bytes. */
 #define KLA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)

@@ -184,6 +184,52 @@ static void workspace_queries(void) {
   (void)kla_pgdn_chunk_workspace_bytes(NULL, NULL, 1, 1, 1 << 20, 1 << 30, 128, 256, 64, KLA_DT_BF16);
 }
 
+static kla_status_t fwd_seg(Args a, int seg) {
+  return kla_chunk_fwd_seg(a.q, a.k, a.v, a.g, a.eta, a.eps, a.s0, a.o, a.sf, a.cu, a.cuh, a.N, a.B, a.H, a.T,
+                           a.dk, a.dv, a.chunk, (kla_dtype_t)a.dtype, seg, a.ws, a.wsb, NULL);
+}
+static size_t seg_bytes(Args a, int seg) {
+  return kla_chunk_seg_workspace_bytes(a.cu, a.cuh, a.N, a.B, a.H, a.T, a.dk, a.dv, a.chunk,
+                                       (kla_dtype_t)a.dtype, seg);
+}
+
+static void segmented(void) {
+  Args a = base();
+  expect("seg -1", fwd_seg(a, -1), KLA_ERR_SHAPE);
+  expect("seg INT_MIN", fwd_seg(a, INT_MIN), KLA_ERR_SHAPE);
+  a = base(); a.dtype = 7; expect("seg dtype", fwd_seg(a, 2), KLA_ERR_DTYPE);
+  a = base(); a.dtype = 1; a.chunk = 64; a.dk = 128; expect("seg general shape", fwd_seg(a, 2), KLA_ERR_UNSUPPORTED);
+  a = base(); a.q = NULL; expect("seg null", fwd_seg(a, 2), KLA_ERR_NULL);
+  a = base(); a.wsb = seg_bytes(a, 2) - 1; expect("seg ws one short", fwd_seg(a, 2), KLA_ERR_WORKSPACE);
+  a = base(); a.N = 0; a.B = 0; expect("seg nothing to do", fwd_seg(a, 2), KLA_OK);
+  a = base();
+  expect("seg 0 = plain", (long long)seg_bytes(a, 0), (long long)ws_bytes(a));
+  expect("seg 1 > plain", seg_bytes(a, 1) > ws_bytes(a), 1);
+  expect("seg bytes negative", (long long)seg_bytes(a, -3), 0);
+  expect("seg huge length = one segment each", seg_bytes(a, INT_MAX) > ws_bytes(a), 1);
+  /* the library's own choice on a long sequence */
+  a = base(); a.N = 1; a.B = 1; a.H = 16; a.T = 65536; a.dv = 256;
+  expect("auto segments", (long long)ws_bytes(a), (long long)seg_bytes(a, 342));
+  /* packed, with a heap mirror of exactly num_seqs + 1 entries */
+  const int n = 300;
+  int32_t *cu = (int32_t *)malloc(sizeof(int32_t) * (n + 1));
+  cu[0] = 0;
+  for (int i = 0; i < n; ++i) cu[i + 1] = cu[i] + (i % 7 == 0 ? 5000 : i % 3);
+  Args m = base();
+  m.cu = (const int32_t *)FAKE; m.cuh = cu; m.N = n; m.B = 1; m.T = cu[n]; m.H = 1; m.dv = 64;
+  expect("seg packed bytes", seg_bytes(m, 3) > ws_bytes(m), 1);
+  m.q = NULL; expect("seg packed reaches the pointer checks", fwd_seg(m, 3), KLA_ERR_NULL);
+  (void)ws_bytes(m);
+  free(cu);
+  /* sizes near the limits */
+  a = base(); a.N = 1; a.B = 1; a.H = 1; a.T = 1 << 30; a.dv = 256;
+  (void)ws_bytes(a);
+  (void)seg_bytes(a, 1);
+  (void)seg_bytes(a, 7);
+  a.H = 1 << 20;
+  (void)seg_bytes(a, 1);
+}
+
 static void noalloc_limits(void) {
   Args a = base();
   a.N = 4; a.B = 4; a.H = 64; a.T = 8192;
@@ -296,6 +342,7 @@ int main(void) {
   seqlens();
   workspace_queries();
   noalloc_limits();
+  segmented();
   decode();
   gdn_chunk();
   backward();
