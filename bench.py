@@ -140,7 +140,10 @@ def bench_prefill_other(steps, warmup):
     """The other two prefill workloads, each timed as one kla_chunk_fwd call per
     step: the long-context one (B=1 H=16 T=65536 dk=128 dv=256, no initial state)
     and the 32 packed sequences of log-uniform lengths (H=32, cu_seqlens, nonzero
-    initial states).  Reported beside the main line, not as the metric."""
+    initial states).  Reported beside the main line, not as the metric.  The
+    workspace is kla_chunk_workspace_bytes', so kla_chunk_fwd takes its own choice
+    of segments ("segmented": the long-context workload runs the segment-parallel
+    scan, the packed batch does not)."""
     import torch
     from gated_delta_rule_kla_amd import inputs, kla
 
@@ -156,8 +159,10 @@ def bench_prefill_other(steps, warmup):
         N = (x.cu_seqlens.numel() - 1) if x.cu_seqlens is not None else B
         o = torch.empty((B, H, T, dv), dtype=q.dtype, device=dev)
         S = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
-        ws = torch.empty(kla.chunk_workspace_bytes(B, H, T, dk, dv, x.chunk, q.dtype, cu_seqlens_host=cu_h),
-                         dtype=torch.uint8, device=dev)
+        ws_bytes = kla.chunk_workspace_bytes(B, H, T, dk, dv, x.chunk, q.dtype, cu_seqlens_host=cu_h)
+        segmented = ws_bytes > kla.chunk_workspace_bytes(B, H, T, dk, dv, x.chunk, q.dtype, cu_seqlens_host=cu_h,
+                                                         seg_chunks=0)
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
         stream = torch.cuda.current_stream(dev)
 
         def step(_i):
@@ -170,7 +175,7 @@ def bench_prefill_other(steps, warmup):
         flops, byts = prefill_algorithmic(B, H, T, dk, dv, x.chunk, 1 if s0 is not None else 0, 1, N)
         sec = ms * 1e-3
         res[inputs.CONFIGS[i]] = {
-            "ms_per_call": ms, "tokens/s": B * T / sec, "tflops": flops / sec / 1e12,
+            "ms_per_call": ms, "segmented": bool(segmented), "tokens/s": B * T / sec, "tflops": flops / sec / 1e12,
             "GB/s": byts / sec / 1e9, "hbm_frac": byts / sec / 1e9 / HBM_PEAK_GBS,
             "algorithmic_bytes_per_launch": byts, "algorithmic_flops_per_launch": flops}
         del q, k, v, g, eta, o, S, ws, s0, cu
