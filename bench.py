@@ -136,7 +136,7 @@ def bench_prefill(steps, warmup):
                 dims=(B, H, T, dk, dv, x.chunk))
 
 
-def bench_prefill_other(steps, warmup):
+def bench_prefill_other(steps, warmup, only=None):
     """The other two prefill workloads, each timed as one kla_chunk_fwd call per
     step: the long-context one (B=1 H=16 T=65536 dk=128 dv=256, no initial state)
     and the 32 packed sequences of log-uniform lengths (H=32, cu_seqlens, nonzero
@@ -149,7 +149,7 @@ def bench_prefill_other(steps, warmup):
 
     dev = torch.device("cuda:0")
     res = {}
-    for i in (2, 4):
+    for i in ((2, 4) if only is None else (only,)):
         x = _workload(i)
         B, H, T, dk, dv = x.dims
         q, k, v, g, eta = (t.to(dev) for t in (x.q, x.k, x.v, x.g, x.eta))
@@ -475,6 +475,8 @@ def main():
     ap.add_argument("--mode", choices=["all", "prefill", "decode", "backward", "prefill-other", "pgdn"],
                     default="all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", type=int, choices=[2, 4],
+                    help="prefill-other: time only this workload (2: T=65536 dv=256, 4: 32 packed sequences)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 256 MiB device copy (for HBM counter calibration)")
     args = ap.parse_args()
@@ -576,7 +578,8 @@ def main():
                         "config": {"workload": bwd["workload"]}, "roofline": bwd["roofline"]})
         out["backward"] = bwd
     if args.mode == "prefill-other":
-        out["prefill_other_workloads"] = bench_prefill_other(max(2, args.steps // 20), max(1, args.warmup // 10))
+        out["prefill_other_workloads"] = bench_prefill_other(max(2, args.steps // 20), max(1, args.warmup // 10),
+                                                             args.only)
     if args.mode in ("all", "pgdn"):
         out["pgdn"] = bench_pgdn(max(2, args.steps // 40), 1)
     if args.mode == "all":
