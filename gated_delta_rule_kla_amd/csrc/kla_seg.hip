@@ -193,7 +193,7 @@ __device__ __forceinline__ bool seg_tokens(const SegFixParams &f, int s, int &b,
 //      group g <-> contraction index 32 q + 8 g + x on both sides), the o tile from LDS
 //      the accumulator (lane (i, g): token i, columns 4 g .. 4 g + 3), written back there;
 //   3. the o rows back to memory in 16-byte pieces.
-constexpr int kSegRun = 8;  // chunks per correction workgroup
+constexpr int kSegRun = 2;  // chunks per correction workgroup (2: 150 us, 4: 155, 8: 171 on T=65536 dv=256)
 
 template <int DK, int DV>
 __global__ __launch_bounds__(64 * (DV == 64 ? 4 : DV / 32)) void kla_seg_correct_mfma_kernel(SegFixParams f) {

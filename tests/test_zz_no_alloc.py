@@ -4,7 +4,8 @@ instead of a caller workspace) against kla_chunk_fwd, through the C ABI.
 The two run the same kernels, so their outputs must agree bit for bit.  Calls
 come in a row on one GPU, each later one smaller than the one before, so a
 call that depended on what an earlier call left in the shared buffer would
-show; the oracle checks the first call's result as well."""
+show; the oracle checks the first call's result as well.  One call is cut into
+segments (the segment-parallel scan's buffers also live in the scratch)."""
 
 import numpy as np
 import pytest
@@ -36,8 +37,15 @@ def _both(x):
 
 
 def test_noalloc_matches_workspace_entry_point_on_calls_in_a_row():
+    # few long sequences: the library cuts them into segments (about 10 MB of scratch)
+    seg = inputs.make_prefill(B=1, H=2, T=6400, dk=128, dv=256, chunk=64, sigma_k=1.0, g_scale=0.1,
+                              seed=95, name="segmented")
+    assert kla.chunk_workspace_bytes(1, 2, 6400, 128, 256) > kla.chunk_workspace_bytes(1, 2, 6400, 128, 256,
+                                                                                       seg_chunks=0)
+    assert kla.chunk_workspace_bytes(1, 2, 6400, 128, 256) < kla.NOALLOC_SCRATCH_BYTES
     cases = [
         inputs.prefill_config(1),                                          # 28.3 MB of scratch
+        seg,
         inputs.make_prefill(B=2, H=3, T=333, dk=128, dv=128, chunk=64, s0_std=0.05, seed=91, name="mid"),
         inputs.make_prefill(H=2, dk=128, dv=64, chunk=64, s0_std=0.05, lengths=[5, 0, 130, 64], seed=92,
                             name="varlen"),
