@@ -267,12 +267,12 @@ __global__ __launch_bounds__(64 * (DV == 64 ? 4 : DV / 32)) void kla_seg_correct
       for (int q = 0; q < NQ; ++q) e[q] = *reinterpret_cast<const bf16x8 *>(sE + (16 * rb + li) * LDE + 32 * q + 8 * lg);
 #pragma unroll
       for (int ct = 0; ct < NCTW; ++ct) {
-        bf16 *po = sO + (16 * rb + li) * LDO + 16 * (w * NCTW + ct) + 4 * lg;
-        const bf16x4 v = *reinterpret_cast<const bf16x4 *>(po);
+        bf16 *cell = sO + (16 * rb + li) * LDO + 16 * (w * NCTW + ct) + 4 * lg;
+        const bf16x4 v = *reinterpret_cast<const bf16x4 *>(cell);
         f32x4 acc = {(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
 #pragma unroll
         for (int q = 0; q < NQ; ++q) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ct][q], e[q], acc, 0, 0, 0);
-        *reinterpret_cast<bf16x4 *>(po) = bf16x4{(bf16)acc[0], (bf16)acc[1], (bf16)acc[2], (bf16)acc[3]};
+        *reinterpret_cast<bf16x4 *>(cell) = bf16x4{(bf16)acc[0], (bf16)acc[1], (bf16)acc[2], (bf16)acc[3]};
       }
     }
     __syncthreads();
