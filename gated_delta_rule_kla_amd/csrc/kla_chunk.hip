@@ -1585,7 +1585,12 @@ __global__ __launch_bounds__(64 * (kWaves + (PG ? 1 : 0))) void kla_chunk_kernel
 template <typename E, int C, int DK, int NCT>
 struct RevShape {
   using F = ChunkShape<E, C, DK, NCT>;
-  static constexpr int NB = F::NB, DVT = F::DVT, NCW = F::NCW, NT = F::NT;
+  // four column tiles: eight waves, four chain waves of one tile each (the chain's
+  // products dominate a step: 108 MFMAs per chain wave with two tiles each against 32
+  // per P wave) and one loader for both K and Q
+  static constexpr bool W8 = NCT == 4;
+  static constexpr int NW = W8 ? 8 : kWaves;
+  static constexpr int NB = F::NB, DVT = F::DVT, NCW = W8 ? 1 : F::NCW, NT = 64 * NW;
   static constexpr int LDK = F::LDK, LDC = F::LDC, LDV = F::LDV;
   static constexpr int K_SLOT = F::K_SLOT, V_SLOT = F::V_SLOT, TP_SLOT = TpLayout<E, C>::LDS_BYTES;
   static constexpr int YP = NCT * NB * 64 * 16;  // P^T dO tiles, fp32 accumulator layout
@@ -1598,8 +1603,12 @@ struct RevShape {
   static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
+template <int NCT>
+constexpr int rev_threads() { return 64 * (NCT == 4 ? 8 : kWaves); }
+
 template <typename E, int C, int DK, int NCT>
-__global__ __launch_bounds__(64 * kWaves) void kla_chunk_rev_kernel(ChunkParams p) {
+__global__ __launch_bounds__(rev_threads<NCT>()) void kla_chunk_rev_kernel(ChunkParams p) {
+  static_assert(rev_threads<NCT>() == RevShape<E, C, DK, NCT>::NT, "workgroup size");
   using Sh = RevShape<E, C, DK, NCT>;
   using TL = TpLayout<E, C>;
   using O = Ops<E>;
@@ -1668,7 +1677,8 @@ __global__ __launch_bounds__(64 * kWaves) void kla_chunk_rev_kernel(ChunkParams 
   };
   f32x4 *sYp = reinterpret_cast<f32x4 *>(smem + Sh::OFF_YP);
 
-  if (wave == CHAIN0 || wave == CHAIN1) {
+  constexpr bool W8 = Sh::W8;
+  if (wave == CHAIN0 || wave == CHAIN1 || (W8 && wave >= LOADQ)) {
     auto chain = [&](auto ct0_c) {
       constexpr int CT0 = decltype(ct0_c)::value;
       constexpr int NCW = CT0 < NCT ? (NCT - CT0 < Sh::NCW ? NCT - CT0 : Sh::NCW) : 0;
@@ -1814,10 +1824,22 @@ __global__ __launch_bounds__(64 * kWaves) void kla_chunk_rev_kernel(ChunkParams 
         }
       }
     };
-    if (wave == CHAIN0)
-      chain(std::integral_constant<int, 0>{});
-    else
-      chain(std::integral_constant<int, Sh::NCW>{});
+    if constexpr (W8) {
+      // column tiles 0, 1 on waves 0, 1 and 2, 3 on waves 6, 7 (two SIMDs each)
+      if (wave == CHAIN0)
+        chain(std::integral_constant<int, 0>{});
+      else if (wave == CHAIN1)
+        chain(std::integral_constant<int, 1>{});
+      else if (wave == LOADQ)
+        chain(std::integral_constant<int, 2>{});
+      else
+        chain(std::integral_constant<int, 3>{});
+    } else {
+      if (wave == CHAIN0)
+        chain(std::integral_constant<int, 0>{});
+      else
+        chain(std::integral_constant<int, Sh::NCW>{});
+    }
   } else if (wave == PW0 || wave == PW1) {
     // ---- P waves: P^T dO for the rows of Y whose column block they own ----
     auto pwave = [&](auto part_c) {
@@ -1883,6 +1905,20 @@ __global__ __launch_bounds__(64 * kWaves) void kla_chunk_rev_kernel(ChunkParams 
       pwave(std::integral_constant<int, 0>{});
     else
       pwave(std::integral_constant<int, 1>{});
+  } else if (W8 && wave == LOADK) {
+    // ---- K and Q rows of the next step's chunk (one register set each, one step ahead) ----
+    RowLoad<E, DK, AllBlocks<NB>> kin, qin;
+    kin.issue(gk + tok0_of(chunk_of(0)) * DK, nrow_of(chunk_of(0)), lane);
+    qin.issue(gq + tok0_of(chunk_of(0)) * DK, nrow_of(chunk_of(0)), lane);
+    __syncthreads();
+    for (int i = -1; i <= iend; ++i) {
+      kin.put(sK(i + 1), LDK, lane, [](int, int row) { return row; });
+      qin.put(sQ(i + 1), LDK, lane, [](int, int row) { return row; });
+      kin.issue(gk + tok0_of(chunk_of(i + 2)) * DK, nrow_of(chunk_of(i + 2)), lane);
+      qin.issue(gq + tok0_of(chunk_of(i + 2)) * DK, nrow_of(chunk_of(i + 2)), lane);
+      lds_barrier();
+      lds_barrier();
+    }
   } else if (wave == LOADK) {
     // ---- K rows of the next step's chunk (two register sets, two steps ahead) ----
     RowLoad<E, DK, AllBlocks<NB>> kin[2];
