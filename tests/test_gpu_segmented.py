@@ -6,8 +6,9 @@ element by element with the oracle's token recurrence (the bf16 bar 2e-2 x max|r
 debug bar 1e-4), and with the same call unsegmented.  The paths covered: bf16 64-column tiles
 with the MFMA correction (dk 128 and 64), bf16 16- and 32-column tiles with the fp32
 correction, fp32 chunk 16 and chunk 64, packed batches with empty and one-token sequences,
-initial states, a segment length that leaves one segment per sequence, and the library's own
-choice on a grid of few long sequences.
+initial states, a segment length that leaves one segment per sequence, the library's own
+choice on a grid of few long sequences, the gated delta rule (update coefficient given) on the
+same choice, and the unsegmented fallback for a workspace without room for the segments.
 """
 
 import numpy as np
@@ -123,3 +124,29 @@ def test_seg_library_choice_on_few_long_sequences():
         eo, es = rel_err(f(o[:, h:h + 1]), o_r), rel_err(f(S[:, h:h + 1]), S_r)
         print(f"  head {h}: err_o={eo:.3e} err_S={es:.3e}")
         assert eo <= 2e-2 and es <= 2e-2, (h, eo, es)
+
+
+def test_seg_gdn_mode_and_the_unsegmented_fallback():
+    """kla_gdn_chunk_fwd takes the same choice of segments (B=1 H=4 T=8192 dv=256: eight
+    segments of 16 chunks); given a workspace of only the unsegmented size it runs unsegmented
+    instead.  Both agree, and two heads match the gated-delta-rule oracle."""
+    from oracle import gdn_forward
+    x = inputs.unit_keys(inputs.make_prefill(B=1, H=4, T=8192, dk=128, dv=256, chunk=64, g_scale=0.1,
+                                             seed=5110, name="seg-gdn"))
+    full = kla.chunk_workspace_bytes(1, 4, 8192, 128, 256)
+    plain = kla.chunk_workspace_bytes(1, 4, 8192, 128, 256, seg_chunks=0)
+    assert full > plain > 0
+    args = [t.to(DEV) for t in (x.q, x.k, x.v, x.g, x.eta)]
+    print(f"case {x.name}: segmented, then a workspace of {plain} bytes", flush=True)
+    o1, S1 = kla.gdn_chunk_fwd(*args, workspace=torch.empty(full, dtype=torch.uint8, device=DEV))
+    o0, S0 = kla.gdn_chunk_fwd(*args, workspace=torch.empty(plain, dtype=torch.uint8, device=DEV))
+    torch.cuda.synchronize()
+    o1, S1, o0, S0 = o1.cpu(), S1.cpu(), o0.cpu(), S0.cpu()
+    assert rel_err(f(o1), f(o0)) <= 2e-2 and rel_err(f(S1), f(S0)) <= 2e-2
+    for h in (0, 3):
+        o_r, S_r = gdn_forward(f(x.q[:, h:h + 1]), f(x.k[:, h:h + 1]), f(x.v[:, h:h + 1]), f(x.g[:, h:h + 1]),
+                               f(x.eta[:, h:h + 1]))
+        for o, S in ((o1, S1), (o0, S0)):
+            eo, es = rel_err(f(o[:, h:h + 1]), o_r), rel_err(f(S[:, h:h + 1]), S_r)
+            print(f"  head {h}: err_o={eo:.3e} err_S={es:.3e}")
+            assert eo <= 2e-2 and es <= 2e-2, (h, eo, es)
