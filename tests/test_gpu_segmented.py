@@ -150,3 +150,26 @@ def test_seg_gdn_mode_and_the_unsegmented_fallback():
             eo, es = rel_err(f(o[:, h:h + 1]), o_r), rel_err(f(S[:, h:h + 1]), S_r)
             print(f"  head {h}: err_o={eo:.3e} err_S={es:.3e}")
             assert eo <= 2e-2 and es <= 2e-2, (h, eo, es)
+
+
+def test_seg_dv192_six_wave_correction():
+    # dv = 192: the MFMA correction with six waves of two column tiles
+    x = inputs.make_prefill(B=2, H=2, T=520, dk=128, dv=192, chunk=64, s0_std=0.02, seed=5111,
+                            name="seg-dv192")
+    check(x, 3)
+
+
+def test_seg_final_state_aliases_initial_state():
+    """The final state may be written over the initial state: the scan reads it for the first
+    segments, and only the combine kernel, which runs after the scan, writes the final state."""
+    x = inputs.make_prefill(B=2, H=3, T=600, dk=128, dv=128, chunk=64, s0_std=0.05, seed=5112,
+                            name="seg-alias")
+    args = [t.to(DEV) for t in (x.q, x.k, x.v, x.g, x.eta)]
+    s0 = x.initial_state.to(DEV)
+    print(f"case {x.name}: in place", flush=True)
+    o_ref, S_ref = kla.chunk_fwd(*args, x.eps, s0.clone(), seg_chunks=2)
+    s_inout = s0.clone()
+    o_in, S_in = kla.chunk_fwd(*args, x.eps, s_inout, final_state=s_inout, seg_chunks=2)
+    torch.cuda.synchronize()
+    assert S_in.data_ptr() == s_inout.data_ptr()
+    assert torch.equal(o_in.cpu(), o_ref.cpu()) and torch.equal(S_in.cpu(), S_ref.cpu())
