@@ -2357,6 +2357,9 @@ hipError_t launch_chunk_fwd_seg(const ChunkArgs &a, const int32_t *cu_host, int 
   f.dv = a.dv;
   f.dtype = a.dtype;
   f.seg_chunks = L;
+  f.seg_max_chunks = 0;
+  for (int n = 0; n < (a.cu_seqlens ? a.num_seqs : 1); ++n)
+    f.seg_max_chunks = std::max(f.seg_max_chunks, seq_chunks_host(a, cu_host, n));
   f.nseg = lay.nseg;
   f.seg_d = reinterpret_cast<float *>(ws + lay.d);
   f.seg_m = reinterpret_cast<float *>(ws + lay.m);

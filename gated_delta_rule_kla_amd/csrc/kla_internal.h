@@ -117,6 +117,7 @@ struct SegFixParams {
   const int32_t *cu;     // device cu_seqlens or nullptr (dense)
   const int *seg_first;  // [nseq + 1] first segment of each sequence
   int nseq, H, T, C, dk, dv, dtype, seg_chunks;
+  int seg_max_chunks;  // chunks of the longest sequence (bounds the correction's runs)
   long long nseg;
   const float *seg_d;  // [nseg, H, dk, dv] end states (first segments: from the initial state)
   const float *seg_m;  // [nseg, H, dk, dk] transfer maps (later segments)

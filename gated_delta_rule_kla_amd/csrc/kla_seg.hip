@@ -28,6 +28,8 @@
 #include "kla_internal.h"
 #include "kla_ops.h"
 
+#include <algorithm>
+
 namespace kla {
 
 // Sequence n of a call: tokens [t0, t1) of batch row b.
@@ -181,8 +183,8 @@ __device__ __forceinline__ bool seg_tokens(const SegFixParams &f, int s, int &b,
 }
 
 // ---- correction, bf16 on MFMA --------------------------------------------------------
-// One workgroup per (later segment, head, run of kSegRun chunks) with dv / (16 NCTW)
-// waves; wave w owns NCTW column tiles (16 columns each) of o.  Per chunk (64 tokens):
+// One workgroup per (later segment, head) and grid row y, taking the segment's runs of
+// kSegRun chunks y, y + gridDim.y, ..., with dv / (16 NCTW) waves; wave w owns NCTW column tiles (16 columns each) of o.  Per chunk (64 tokens):
 //   1. the chunk's E rows and o rows into LDS, in coalesced 16-byte pieces (consecutive
 //      lanes, consecutive bytes of a row: the kernel moves 80 KB per chunk and head at
 //      dv = 256 and is bound by HBM; pieces of a few bytes per row per instruction ran it
@@ -206,14 +208,10 @@ __global__ __launch_bounds__(64 * (DV == 64 ? 4 : DV / 32)) void kla_seg_correct
   const int tid = threadIdx.x, nt = NT;
   const int lane = tid & 63, w = tid >> 6;
   const int li = lane & 15, lg = lane >> 4;
-  const int s = blockIdx.y / f.H, h = blockIdx.y % f.H;
+  const int s = blockIdx.x / f.H, h = blockIdx.x % f.H;
   int b, st0, st1;
   if (!seg_tokens(f, s, b, st0, st1)) return;
-  const long long k0 = (long long)st0 + (long long)blockIdx.x * kSegRun * C;
-  if (k0 >= st1) return;
-  const int tk0 = (int)k0, tk1 = (int)min((long long)st1, k0 + (long long)kSegRun * C);
   constexpr int dv = DV;
-  const int nrow = tk1 - tk0;
   const size_t rowbase = ((size_t)b * f.H + h) * (size_t)f.T;
   bf16x8 a[NCTW][NQ];
   {
@@ -223,91 +221,98 @@ __global__ __launch_bounds__(64 * (DV == 64 ? 4 : DV / 32)) void kla_seg_correct
 #pragma unroll
       for (int q = 0; q < NQ; ++q) a[ct][q] = G[((w * NCTW + ct) * NQ + q) * 64 + lane];
   }
-  // the run's rows of E and o as buffer ranges (rows past its end read as zero)
-  const bf16 *E = static_cast<const bf16 *>(f.eout) + (rowbase + (size_t)tk0) * DK;
-  bf16 *O = static_cast<bf16 *>(f.o) + (rowbase + (size_t)tk0) * dv;
-  const __amdgpu_buffer_rsrc_t re = buffer_rsrc(E, nrow * DK * 2);
-  const __amdgpu_buffer_rsrc_t ro = buffer_rsrc(O, nrow * dv * 2);
-  constexpr int epr = DK / 8, opr = DV / 8;  // 16-byte pieces per row
-  // a chunk's pieces per thread; the next chunk's are loaded into registers while
-  // this one is multiplied and stored
-  constexpr int NPE = (C * epr + NT - 1) / NT, NPO = (C * opr + NT - 1) / NT;
-  uint4 pe[NPE], po[NPO];
-  auto load = [&](int tb) {
+  // runs of kSegRun chunks: blockIdx.y, then every gridDim.y-th (uniform per workgroup)
+  for (long long k0 = (long long)st0 + (long long)blockIdx.y * kSegRun * C; k0 < st1;
+       k0 += (long long)gridDim.y * kSegRun * C) {
+    const int tk0 = (int)k0, tk1 = (int)min((long long)st1, k0 + (long long)kSegRun * C);
+    const int nrow = tk1 - tk0;
+    // the run's rows of E and o as buffer ranges (rows past its end read as zero)
+    const bf16 *E = static_cast<const bf16 *>(f.eout) + (rowbase + (size_t)tk0) * DK;
+    bf16 *O = static_cast<bf16 *>(f.o) + (rowbase + (size_t)tk0) * dv;
+    const __amdgpu_buffer_rsrc_t re = buffer_rsrc(E, nrow * DK * 2);
+    const __amdgpu_buffer_rsrc_t ro = buffer_rsrc(O, nrow * dv * 2);
+    constexpr int epr = DK / 8, opr = DV / 8;  // 16-byte pieces per row
+    // a chunk's pieces per thread; the next chunk's are loaded into registers while
+    // this one is multiplied and stored
+    constexpr int NPE = (C * epr + NT - 1) / NT, NPO = (C * opr + NT - 1) / NT;
+    uint4 pe[NPE], po[NPO];
+    auto load = [&](int tb) {
 #pragma unroll
-    for (int j = 0; j < NPE; ++j) {
-      const int pc = tid + nt * j;
-      pe[j] = buffer_ld16(re, ((tb + pc / epr) * DK + 8 * (pc % epr)) * 2);  // past the chunk: past the range
-    }
-#pragma unroll
-    for (int j = 0; j < NPO; ++j) {
-      const int pc = tid + nt * j;
-      po[j] = buffer_ld16(ro, ((tb + pc / opr) * dv + 8 * (pc % opr)) * 2);
-    }
-  };
-  load(0);
-  for (int tb = 0; tb < nrow; tb += C) {
-    __syncthreads();  // the previous chunk's o rows have left LDS
-#pragma unroll
-    for (int j = 0; j < NPE; ++j) {
-      const int pc = tid + nt * j;
-      if (pc < C * epr) *reinterpret_cast<uint4 *>(sE + (pc / epr) * LDE + 8 * (pc % epr)) = pe[j];
-    }
-#pragma unroll
-    for (int j = 0; j < NPO; ++j) {
-      const int pc = tid + nt * j;
-      if (pc < C * opr) *reinterpret_cast<uint4 *>(sO + (pc / opr) * LDO + 8 * (pc % opr)) = po[j];
-    }
-    if (tb + C < nrow) load(tb + C);
-    __syncthreads();
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      bf16x8 e[NQ];
-#pragma unroll
-      for (int q = 0; q < NQ; ++q) e[q] = *reinterpret_cast<const bf16x8 *>(sE + (16 * rb + li) * LDE + 32 * q + 8 * lg);
-#pragma unroll
-      for (int ct = 0; ct < NCTW; ++ct) {
-        bf16 *cell = sO + (16 * rb + li) * LDO + 16 * (w * NCTW + ct) + 4 * lg;
-        const bf16x4 v = *reinterpret_cast<const bf16x4 *>(cell);
-        f32x4 acc = {(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
-#pragma unroll
-        for (int q = 0; q < NQ; ++q) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ct][q], e[q], acc, 0, 0, 0);
-        *reinterpret_cast<bf16x4 *>(cell) = bf16x4{(bf16)acc[0], (bf16)acc[1], (bf16)acc[2], (bf16)acc[3]};
+      for (int j = 0; j < NPE; ++j) {
+        const int pc = tid + nt * j;
+        pe[j] = buffer_ld16(re, ((tb + pc / epr) * DK + 8 * (pc % epr)) * 2);  // past the chunk: past the range
       }
-    }
-    __syncthreads();
-    for (int pc = tid; pc < C * opr; pc += nt) {
-      const int r = pc / opr, c8 = pc % opr;
-      if (tb + r < nrow)
-        *reinterpret_cast<uint4 *>(O + (size_t)(tb + r) * dv + 8 * c8) = *reinterpret_cast<const uint4 *>(sO + r * LDO + 8 * c8);
+#pragma unroll
+      for (int j = 0; j < NPO; ++j) {
+        const int pc = tid + nt * j;
+        po[j] = buffer_ld16(ro, ((tb + pc / opr) * dv + 8 * (pc % opr)) * 2);
+      }
+    };
+    load(0);
+    for (int tb = 0; tb < nrow; tb += C) {
+      __syncthreads();  // the previous chunk's o rows have left LDS
+#pragma unroll
+      for (int j = 0; j < NPE; ++j) {
+        const int pc = tid + nt * j;
+        if (pc < C * epr) *reinterpret_cast<uint4 *>(sE + (pc / epr) * LDE + 8 * (pc % epr)) = pe[j];
+      }
+#pragma unroll
+      for (int j = 0; j < NPO; ++j) {
+        const int pc = tid + nt * j;
+        if (pc < C * opr) *reinterpret_cast<uint4 *>(sO + (pc / opr) * LDO + 8 * (pc % opr)) = po[j];
+      }
+      if (tb + C < nrow) load(tb + C);
+      __syncthreads();
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        bf16x8 e[NQ];
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) e[q] = *reinterpret_cast<const bf16x8 *>(sE + (16 * rb + li) * LDE + 32 * q + 8 * lg);
+#pragma unroll
+        for (int ct = 0; ct < NCTW; ++ct) {
+          bf16 *cell = sO + (16 * rb + li) * LDO + 16 * (w * NCTW + ct) + 4 * lg;
+          const bf16x4 v = *reinterpret_cast<const bf16x4 *>(cell);
+          f32x4 acc = {(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+#pragma unroll
+          for (int q = 0; q < NQ; ++q) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ct][q], e[q], acc, 0, 0, 0);
+          *reinterpret_cast<bf16x4 *>(cell) = bf16x4{(bf16)acc[0], (bf16)acc[1], (bf16)acc[2], (bf16)acc[3]};
+        }
+      }
+      __syncthreads();
+      for (int pc = tid; pc < C * opr; pc += nt) {
+        const int r = pc / opr, c8 = pc % opr;
+        if (tb + r < nrow)
+          *reinterpret_cast<uint4 *>(O + (size_t)(tb + r) * dv + 8 * c8) = *reinterpret_cast<const uint4 *>(sO + r * LDO + 8 * c8);
+      }
     }
   }
 }
 
 // ---- correction, any element type and width (fp32 arithmetic) --------------------------
-// One workgroup of 256 threads per (later segment, head, run of kSegRun chunks); each
-// thread takes elements (token, column) of the run in turn: o += sum_k E[token][k] S[k][col]
-// with S_start as fp32 rows.
+// One workgroup of 256 threads per (later segment, head) and grid row y (the runs of
+// kSegRun chunks as in the MFMA kernel); each thread takes elements (token, column) of
+// a run in turn: o += sum_k E[token][k] S[k][col], with S_start as fp32 rows.
 template <typename E>
 __global__ __launch_bounds__(256) void kla_seg_correct_simple_kernel(SegFixParams f) {
-  const int s = blockIdx.y / f.H, h = blockIdx.y % f.H;
+  const int s = blockIdx.x / f.H, h = blockIdx.x % f.H;
   int b, st0, st1;
   if (!seg_tokens(f, s, b, st0, st1)) return;
-  const long long k0 = (long long)st0 + (long long)blockIdx.x * kSegRun * f.C;
-  if (k0 >= st1) return;
-  const int tk0 = (int)k0, tk1 = (int)min((long long)st1, k0 + (long long)kSegRun * f.C);
   const int dv = f.dv, dk = f.dk;
   const size_t rowbase = ((size_t)b * f.H + h) * (size_t)f.T;
   const float *S = reinterpret_cast<const float *>(f.sfix) + ((size_t)s * f.H + h) * (size_t)dk * dv;
   const E *Ee = static_cast<const E *>(f.eout);
   E *O = static_cast<E *>(f.o);
-  const long long nel = (long long)(tk1 - tk0) * dv;
-  for (long long idx = threadIdx.x; idx < nel; idx += 256) {
-    const size_t row = rowbase + (size_t)tk0 + (size_t)(idx / dv);
-    const int col = (int)(idx % dv);
-    float acc = Elem<E>::to_f32(O[row * dv + col]);
-    for (int k = 0; k < dk; ++k) acc = fmaf(Elem<E>::to_f32(Ee[row * dk + k]), S[(size_t)k * dv + col], acc);
-    O[row * dv + col] = Elem<E>::from_f32(acc);
+  for (long long k0 = (long long)st0 + (long long)blockIdx.y * kSegRun * f.C; k0 < st1;
+       k0 += (long long)gridDim.y * kSegRun * f.C) {
+    const int tk0 = (int)k0, tk1 = (int)min((long long)st1, k0 + (long long)kSegRun * f.C);
+    const long long nel = (long long)(tk1 - tk0) * dv;
+    for (long long idx = threadIdx.x; idx < nel; idx += 256) {
+      const size_t row = rowbase + (size_t)tk0 + (size_t)(idx / dv);
+      const int col = (int)(idx % dv);
+      float acc = Elem<E>::to_f32(O[row * dv + col]);
+      for (int k = 0; k < dk; ++k) acc = fmaf(Elem<E>::to_f32(Ee[row * dk + k]), S[(size_t)k * dv + col], acc);
+      O[row * dv + col] = Elem<E>::from_f32(acc);
+    }
   }
 }
 
@@ -355,7 +360,10 @@ hipError_t launch_seg_finish(const SegFixParams &f, hipStream_t st) {
   }
   if (e != hipSuccess) return e;
   if (f.nseg <= f.nseq) return hipSuccess;  // no later segments: nothing to correct
-  const dim3 grid((unsigned)((f.seg_chunks + kSegRun - 1) / kSegRun), (unsigned)(f.nseg * f.H));
+  // x: (segment, head) (the caller keeps nseg H dv / 16 below 2^31); y: runs of kSegRun
+  // chunks of the longest segment, at most the device's 65536 (the kernels loop over the rest)
+  const int runs = (std::min(f.seg_chunks, std::max(f.seg_max_chunks, 1)) + kSegRun - 1) / kSegRun;
+  const dim3 grid((unsigned)(f.nseg * f.H), (unsigned)std::min(runs, 65535));
   if (mfma) return f.dk == 128 ? correct_mfma_t<128>(f, grid, st) : correct_mfma_t<64>(f, grid, st);
   if (f.dtype == 0)
     hipLaunchKernelGGL((kla_seg_correct_simple_kernel<bf16>), grid, dim3(256), 0, st, f);

@@ -173,3 +173,24 @@ def test_seg_final_state_aliases_initial_state():
     torch.cuda.synchronize()
     assert S_in.data_ptr() == s_inout.data_ptr()
     assert torch.equal(o_in.cpu(), o_ref.cpu()) and torch.equal(S_in.cpu(), S_ref.cpu())
+
+
+def test_seg_more_segment_heads_than_a_grid_row_holds():
+    """fp32 chunk 16, H=64, one chunk per segment over 1,100 chunks: 70,400 (segment, head)
+    pairs, more than the 65,536 a launch grid's second dimension holds.  The correction
+    takes them along the first dimension; every head matches the unsegmented call, and two
+    heads match the oracle."""
+    x = inputs.make_prefill(B=1, H=64, T=17600, dk=16, dv=16, chunk=16, dtype=torch.float32, s0_std=0.02,
+                            seed=5113, name="seg-many")
+    print(f"case {x.name} seg_chunks=1 dims={x.dims}", flush=True)
+    o, S = run(x, 1)
+    o0, S0 = run(x, 0)
+    do, ds = rel_err(f(o), f(o0)), rel_err(f(S), f(S0))
+    print(f"  vs unsegmented {do:.3e} {ds:.3e}")
+    assert do <= 1e-4 and ds <= 1e-4, (do, ds)
+    for h in (0, 63):
+        o_r, S_r = kla_forward(f(x.q[:, h:h + 1]), f(x.k[:, h:h + 1]), f(x.v[:, h:h + 1]), f(x.g[:, h:h + 1]),
+                               f(x.eta[:, h:h + 1]), x.eps, f(x.initial_state[:, h:h + 1]))
+        eo, es = rel_err(f(o[:, h:h + 1]), o_r), rel_err(f(S[:, h:h + 1]), S_r)
+        print(f"  head {h}: err_o={eo:.3e} err_S={es:.3e}")
+        assert eo <= 1e-4 and es <= 1e-4, (h, eo, es)
