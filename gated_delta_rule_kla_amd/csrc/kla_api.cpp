@@ -33,12 +33,17 @@ kla_status_t from_hip(hipError_t e) { return e == hipSuccess ? KLA_OK : KLA_ERR_
 
 // Shape, dtype, eps and cu_seqlens checks shared by kla_chunk_fwd and
 // kla_chunk_workspace_bytes.
+// Heads index the second dimension of the prep, backward and PGDN launch grids, which
+// the device caps at 65,536 workgroups.
+constexpr int kMaxHeads = 65536;
+
 kla_status_t check_chunk_shapes(float eps, const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
                                 int num_seqs, int B, int H, int T, int dk, int dv, int chunk,
                                 int dtype) {
   if (dtype != KLA_DT_BF16 && dtype != KLA_DT_F32) return KLA_ERR_DTYPE;
   if (B < 0 || H <= 0 || T < 0 || dk <= 0 || dv <= 0 || chunk <= 0 || num_seqs < 0)
     return KLA_ERR_SHAPE;
+  if (H > kMaxHeads) return KLA_ERR_SHAPE;
   if (bad_eps(eps)) return KLA_ERR_EPS;
   if (!kla::chunk_supported(dtype, dk, dv, chunk)) return KLA_ERR_UNSUPPORTED;
   if (cu_seqlens == nullptr) {

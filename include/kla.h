@@ -119,6 +119,8 @@ typedef enum {
  *
  * Supported: either dtype, chunk in {16, 64}, dk in {16, 32, 64, 128}, dv a
  * multiple of 16 in [16, 256].  Anything else returns KLA_ERR_UNSUPPORTED.
+ * H is at most 65,536 (KLA_ERR_SHAPE above: heads index a launch grid's second
+ * dimension); the same holds for every chunked entry point below.
  * The pipelined prep + scan kernels run BF16 with chunk 64 and dk in {64, 128},
  * and F32 with chunk 16 (any dk) or chunk 64 with dk in {16, 32}; the other
  * combinations run a general kernel (one workgroup per sequence, head and 16

@@ -81,6 +81,7 @@ def _decode(**kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(dtype=7), E_DTYPE),
     (dict(H=0), E_SHAPE),
+    (dict(H=65537), E_SHAPE),                    # heads beyond a launch grid's second dimension
     (dict(T=-1), E_SHAPE),
     (dict(N=3), E_SHAPE),                        # N must equal B without cu_seqlens
     (dict(eps=-1.0), E_EPS),
@@ -204,6 +205,7 @@ def test_workspace_bytes():
     assert _ws_bytes(T=129) == 2 * 4 * 3 * per
     assert _ws_bytes(T=0) == 0 and _ws_bytes(N=0, B=0) == 0
     assert _ws_bytes(dk=96) == 0                           # unsupported -> 0
+    assert _ws_bytes(H=65537) == 0 and _ws_bytes(H=65536) > 0
     # fp32 chunk 16: 16 x 16 fp32 image + 3 x 16 fp32
     assert _ws_bytes(dtype=1, chunk=16, dk=32, dv=16) == 2 * 4 * 7 * (16 * 16 * 4 + 3 * 16 * 4)
     # fp32 chunk 64: packed 64-column image (32 x 64 + 32 x 32 fp32) + 3 x 64 fp32
