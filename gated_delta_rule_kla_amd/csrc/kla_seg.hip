@@ -183,8 +183,8 @@ __device__ __forceinline__ bool seg_tokens(const SegFixParams &f, int s, int &b,
 }
 
 // ---- correction, bf16 on MFMA --------------------------------------------------------
-// One workgroup per (later segment, head) and grid row y, taking the segment's runs of
-// kSegRun chunks y, y + gridDim.y, ..., with dv / (16 NCTW) waves; wave w owns NCTW column tiles (16 columns each) of o.  Per chunk (64 tokens):
+// One workgroup per (run of kSegRun chunks, later segment, head): grid x is the run, grid
+// y the (segment, head) pair (pairs beyond gridDim.y taken in turn), dv / (16 NCTW) waves; wave w owns NCTW column tiles (16 columns each) of o.  Per chunk (64 tokens):
 //   1. the chunk's E rows and o rows into LDS, in coalesced 16-byte pieces (consecutive
 //      lanes, consecutive bytes of a row: the kernel moves 80 KB per chunk and head at
 //      dv = 256 and is bound by HBM; pieces of a few bytes per row per instruction ran it
@@ -208,22 +208,23 @@ __global__ __launch_bounds__(64 * (DV == 64 ? 4 : DV / 32)) void kla_seg_correct
   const int tid = threadIdx.x, nt = NT;
   const int lane = tid & 63, w = tid >> 6;
   const int li = lane & 15, lg = lane >> 4;
-  const int s = blockIdx.x / f.H, h = blockIdx.x % f.H;
-  int b, st0, st1;
-  if (!seg_tokens(f, s, b, st0, st1)) return;
   constexpr int dv = DV;
-  const size_t rowbase = ((size_t)b * f.H + h) * (size_t)f.T;
-  bf16x8 a[NCTW][NQ];
-  {
-    const bf16x8 *G = reinterpret_cast<const bf16x8 *>(f.sfix) + ((size_t)s * f.H + h) * (dv / 16) * NQ * 64;
+  // (segment, head) pairs: blockIdx.y, then every gridDim.y-th (uniform per workgroup)
+  for (long long sh = blockIdx.y; sh < f.nseg * f.H; sh += gridDim.y) {
+    const int s = (int)(sh / f.H), h = (int)(sh % f.H);
+    int b, st0, st1;
+    if (!seg_tokens(f, s, b, st0, st1)) continue;
+    const long long k0 = (long long)st0 + (long long)blockIdx.x * kSegRun * C;
+    if (k0 >= st1) continue;
+    const size_t rowbase = ((size_t)b * f.H + h) * (size_t)f.T;
+    bf16x8 a[NCTW][NQ];
+    {
+      const bf16x8 *G = reinterpret_cast<const bf16x8 *>(f.sfix) + ((size_t)s * f.H + h) * (dv / 16) * NQ * 64;
 #pragma unroll
-    for (int ct = 0; ct < NCTW; ++ct)
+      for (int ct = 0; ct < NCTW; ++ct)
 #pragma unroll
-      for (int q = 0; q < NQ; ++q) a[ct][q] = G[((w * NCTW + ct) * NQ + q) * 64 + lane];
-  }
-  // runs of kSegRun chunks: blockIdx.y, then every gridDim.y-th (uniform per workgroup)
-  for (long long k0 = (long long)st0 + (long long)blockIdx.y * kSegRun * C; k0 < st1;
-       k0 += (long long)gridDim.y * kSegRun * C) {
+        for (int q = 0; q < NQ; ++q) a[ct][q] = G[((w * NCTW + ct) * NQ + q) * 64 + lane];
+    }
     const int tk0 = (int)k0, tk1 = (int)min((long long)st1, k0 + (long long)kSegRun * C);
     const int nrow = tk1 - tk0;
     // the run's rows of E and o as buffer ranges (rows past its end read as zero)
@@ -289,21 +290,22 @@ __global__ __launch_bounds__(64 * (DV == 64 ? 4 : DV / 32)) void kla_seg_correct
 }
 
 // ---- correction, any element type and width (fp32 arithmetic) --------------------------
-// One workgroup of 256 threads per (later segment, head) and grid row y (the runs of
-// kSegRun chunks as in the MFMA kernel); each thread takes elements (token, column) of
-// a run in turn: o += sum_k E[token][k] S[k][col], with S_start as fp32 rows.
+// One workgroup of 256 threads per (run of kSegRun chunks, later segment, head), the
+// grid as in the MFMA kernel; each thread takes elements (token, column) of the run in
+// turn: o += sum_k E[token][k] S[k][col], with S_start as fp32 rows.
 template <typename E>
 __global__ __launch_bounds__(256) void kla_seg_correct_simple_kernel(SegFixParams f) {
-  const int s = blockIdx.x / f.H, h = blockIdx.x % f.H;
-  int b, st0, st1;
-  if (!seg_tokens(f, s, b, st0, st1)) return;
   const int dv = f.dv, dk = f.dk;
-  const size_t rowbase = ((size_t)b * f.H + h) * (size_t)f.T;
-  const float *S = reinterpret_cast<const float *>(f.sfix) + ((size_t)s * f.H + h) * (size_t)dk * dv;
   const E *Ee = static_cast<const E *>(f.eout);
   E *O = static_cast<E *>(f.o);
-  for (long long k0 = (long long)st0 + (long long)blockIdx.y * kSegRun * f.C; k0 < st1;
-       k0 += (long long)gridDim.y * kSegRun * f.C) {
+  for (long long sh = blockIdx.y; sh < f.nseg * f.H; sh += gridDim.y) {
+    const int s = (int)(sh / f.H), h = (int)(sh % f.H);
+    int b, st0, st1;
+    if (!seg_tokens(f, s, b, st0, st1)) continue;
+    const long long k0 = (long long)st0 + (long long)blockIdx.x * kSegRun * f.C;
+    if (k0 >= st1) continue;
+    const size_t rowbase = ((size_t)b * f.H + h) * (size_t)f.T;
+    const float *S = reinterpret_cast<const float *>(f.sfix) + ((size_t)s * f.H + h) * (size_t)dk * dv;
     const int tk0 = (int)k0, tk1 = (int)min((long long)st1, k0 + (long long)kSegRun * f.C);
     const long long nel = (long long)(tk1 - tk0) * dv;
     for (long long idx = threadIdx.x; idx < nel; idx += 256) {
@@ -360,10 +362,11 @@ hipError_t launch_seg_finish(const SegFixParams &f, hipStream_t st) {
   }
   if (e != hipSuccess) return e;
   if (f.nseg <= f.nseq) return hipSuccess;  // no later segments: nothing to correct
-  // x: (segment, head) (the caller keeps nseg H dv / 16 below 2^31); y: runs of kSegRun
-  // chunks of the longest segment, at most the device's 65536 (the kernels loop over the rest)
+  // x: runs of kSegRun chunks of the longest segment (consecutive workgroups stream
+  // consecutive rows); y: (segment, head) pairs, at most the device's 65,536 (the kernels
+  // take the pairs beyond gridDim.y in turn)
   const int runs = (std::min(f.seg_chunks, std::max(f.seg_max_chunks, 1)) + kSegRun - 1) / kSegRun;
-  const dim3 grid((unsigned)(f.nseg * f.H), (unsigned)std::min(runs, 65535));
+  const dim3 grid((unsigned)runs, (unsigned)std::min(f.nseg * f.H, 65535LL));
   if (mfma) return f.dk == 128 ? correct_mfma_t<128>(f, grid, st) : correct_mfma_t<64>(f, grid, st);
   if (f.dtype == 0)
     hipLaunchKernelGGL((kla_seg_correct_simple_kernel<bf16>), grid, dim3(256), 0, st, f);
