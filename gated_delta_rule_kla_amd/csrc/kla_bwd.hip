@@ -15,22 +15,25 @@
 //   O  = Diag(Gam) Q S + P U                   dA  = -T^T (dW Diag(b)) T^T   (strictly lower)
 //   S' = Gam_C S + K^T Diag(d) U               then dQ, dK, db, dgamma from A, P, X, O, S'
 //
-// Four kernels, through a caller-provided workspace:
-//   prep     (chunk, head) in parallel: b, gamma, ||k||^2, T, P and K K^T . E into the
-//            workspace.
+// The passes, through a caller-provided workspace:
 //   states   the chunk-start states, in order: the forward's own pipelined prep and
 //            scan kernels (kla_chunk.hip) in states mode, which write the state at
-//            the start of every chunk instead of the outputs.
+//            the start of every chunk instead of the outputs.  On the bf16 build the
+//            forward prep also leaves its T'^T images (with gamma, Gam, d) and a T^T
+//            image of every chunk in the workspace.
 //   dstates  dS' of every chunk, in reverse order, by the forward's machinery run as
 //            the adjoint scan (kla_chunk.hip, kla_chunk_rev_kernel); the gradient of
-//            the initial state is what is left at the start.
+//            the initial state is what is left at the start.  On the bf16 build it
+//            runs beside the states scan, on a second stream, when both fit one round
+//            of workgroups.
 //   grads    (chunk, head) in parallel: everything else from S, dS' and the chunk's
-//            inputs, streaming the state columns 16 at a time.
-// Sums are fp32 throughout.  The prep kernel's K K^T and Q K^T take the inputs as MFMA
-// operands (bf16: exact products, 16x16x32 bf16 MFMA).  The other products are 16x16x16
-// steps (Mma16 below): on the bf16 build one 16x16x16 bf16 MFMA whose operands are
-// rounded to bf16 from fp32 LDS values, on the fp32 build four 16x16x4 fp32 MFMAs.  There
-// are no atomics, so results are deterministic run to run.
+//            inputs.  bf16 (chunk 64): kla_bwd_grads2_kernel, over blocks of 64 state
+//            columns on 16x16x32 bf16 MFMA, with P, ||k||^2 and b formed from the K
+//            and Q rows.  fp32: kla_bwd_prep_kernel first writes b, gamma, ||k||^2, T,
+//            P and K K^T . E per (chunk, head), then kla_bwd_grads_kernel streams the
+//            state columns 16 at a time on fp32 MFMA (16x16x16 steps as four 16x16x4).
+// Sums are fp32 throughout.  There are no atomics, so results are deterministic run
+// to run.
 #include <mutex>
 #include <algorithm>
 
@@ -184,21 +187,11 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// One 16x16x16 product step of the scans and the gradient kernel, operands as four
-// fp32 values per lane: a[x] = A[row][k0 + 4 lg + x], b[x] = B[k0 + 4 lg + x][col].
-// The bf16 build rounds them to bf16 for one 16x16x16 bf16 MFMA (fp32 sums, 16 times
-// the fp32 MFMA rate; the inputs q, k, v and dO are bf16 already, so only derived
-// operands -- states, T, P and intermediate products -- are rounded); the fp32 build
-// runs four 16x16x4 fp32 MFMAs with the same pairing of contraction indices.
+// One 16x16x16 product step of the fp32 build's prep and gradient kernels, operands as
+// four fp32 values per lane: a[x] = A[row][k0 + 4 lg + x], b[x] = B[k0 + 4 lg + x][col],
+// run as four 16x16x4 fp32 MFMAs with the same pairing of contraction indices.  (The
+// bf16 build's gradient kernel takes its operands from bf16 LDS rows instead.)
 template <typename E> struct Mma16;
-
-template <> struct Mma16<bf16> {
-  static __device__ __forceinline__ f32x4 run(f32x4 a, f32x4 b, f32x4 c) {
-    const bf16x4 ab = {(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3]};
-    const bf16x4 bb = {(bf16)b[0], (bf16)b[1], (bf16)b[2], (bf16)b[3]};
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ab, bb, c, 0, 0, 0);
-  }
-};
 
 template <> struct Mma16<float> {
   static __device__ __forceinline__ f32x4 run(f32x4 a, f32x4 b, f32x4 c) {
@@ -213,10 +206,9 @@ __device__ __forceinline__ f32x4 gat4(const float *p, int st) { return f32x4{p[0
 __device__ __forceinline__ f32x4 vec4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
 
 // ============================================================================
-// prep: b, gamma, ||k||^2, T = (I + A)^-1 and P for one (chunk, head)
+// prep (fp32 build): b, gamma, ||k||^2, T = (I + A)^-1 and P for one (chunk, head)
 // ============================================================================
-// Four waves.  K K^T and Q K^T run on MFMA (bf16 operands are exact products
-// with fp32 sums; the fp32 build uses fp32 MFMA): the lower-triangular 16x16
+// Four waves.  K K^T and Q K^T run on fp32 MFMA: the lower-triangular 16x16
 // tiles split by row blocks {p, NB-1-p} over two waves per product, so a Gram
 // wave computes the diagonal tile -- hence the norms and b -- of every row it
 // needs.  T = (I + A)^-1 by 16x16 blocks: the diagonal blocks by column-parallel
@@ -225,21 +217,8 @@ __device__ __forceinline__ f32x4 vec4(const float *p) { return *reinterpret_cast
 // as 16x16x16 fp32 MFMA products.
 constexpr int kPT = 256;  // threads per workgroup of the prep kernel
 
+// one 16x16 tile of A B^T, rows of A and B (stride LK) from the given pointers
 template <typename E, int DK, int LK> struct PrepTile;
-
-template <int DK, int LK> struct PrepTile<bf16, DK, LK> {
-  // 16x16 tile of A B^T: rows of A and B (stride LK) from the given pointers
-  static __device__ __forceinline__ f32x4 run(const bf16 *A, const bf16 *B, int lr, int lg) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int k0 = 0; k0 < DK; k0 += 32) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8 *>(A + lr * LK + k0 + 8 * lg);
-      const bf16x8 b = *reinterpret_cast<const bf16x8 *>(B + lr * LK + k0 + 8 * lg);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
-    }
-    return acc;
-  }
-};
 
 template <int DK, int LK> struct PrepTile<float, DK, LK> {
   static __device__ __forceinline__ f32x4 run(const float *A, const float *B, int lr, int lg) {
@@ -451,7 +430,7 @@ template <typename E, int DK> struct GroupLoad {
 };
 
 // ============================================================================
-// grads: dq, dk, dv, dg, deta of one (chunk, head)
+// grads (fp32 build): dq, dk, dv, dg, deta of one (chunk, head)
 // ============================================================================
 // On 16x16x4 fp32 MFMA tiles: lane l supplies A[l%16][l/16] and B[l/16][l%16] of
 // a 16x4 by 4x16 product; accumulator element i of lane l is row 4(l/16)+i,
