@@ -22,15 +22,18 @@
 // count).  Every exponent used is of a non-positive number; the mask is
 // applied before the exponential.
 //
-// Mapping onto the chip.  One workgroup owns one (sequence, head, slice of
-// DVT = 16 NCT state columns) and walks that sequence's chunks in order.  The
-// state slice never leaves the chip: it lives in the MFMA accumulators of the
-// chain wave (fp32) for the whole sequence.  Seven role-specialised waves form
-// a software pipeline over the chunks with one LDS-only barrier per step (see
-// "Roles and LDS plan" below): the S-independent work of a chunk -- gate scan,
-// ||k||^2 and beta, K K^T and A (Gram waves), the blockwise triangular solve
-// for T' (T-solve wave) -- runs two and one steps ahead of the chain, and the
-// P waves form the causal scores and the output rows.
+// Mapping onto the chip.  Two kernels (below).  The prep kernel does the
+// S-independent work of every chunk -- gate scan, ||k||^2 and beta, K K^T and A,
+// the blockwise triangular solve for T' -- for all chunks and heads in parallel,
+// into a workspace.  In the scan kernel one workgroup owns one (sequence, head,
+// slice of DVT = 16 NCT state columns), or one segment of a sequence in segment
+// mode, and walks its chunks in order.  The state slice never leaves the chip:
+// it lives in the MFMA accumulators of the chain waves (fp32) for the whole
+// sequence.  Seven role-specialised waves form a software pipeline over the
+// chunks with one LDS-only barrier per step (see "Roles and LDS plan" below):
+// loader waves bring K, Q, the T' image and the V slice ahead of the chain, the
+// chain waves advance the state, and the P waves form the causal scores and the
+// output rows.
 //
 // Every K and Q row is read with coalesced 16-byte buffer loads and goes
 // through LDS into the MFMA operand layout: loads that give each lane its own
@@ -57,17 +60,18 @@ namespace kla {
 // ---------------------------------------------------------------------------
 // Two kernels
 // ---------------------------------------------------------------------------
-// kla_chunk_prep_kernel: the S-independent work of every chunk, all chunks in
-// parallel (a workgroup pipelines a run of consecutive chunks of one head):
-// gate scan, ||k||^2 and beta, K K^T and A, T = (I + A)^-1, T' = T Diag(beta),
-// and the causal scores P = (Q K^T) . exp(gamma_r - gamma_s) (r >= s).  It
-// writes T'^T, the row vectors gamma, Gam, d and P into a workspace, laid out
-// exactly as the scan kernel holds them in LDS and registers.
+// Prep: the S-independent work of every chunk, all chunks in parallel: gate
+// scan, ||k||^2 and beta, K K^T and A, T = (I + A)^-1, T' = T Diag(beta).  It
+// writes the packed T'^T image and the row vectors gamma, Gam, d per (chunk,
+// head) into a workspace, laid out as the scan kernel's loader expands them
+// into LDS.  bf16: kla_chunk_prep_wave_kernel, one wave per run of chunks of
+// one head; fp32: kla_chunk_prep_kernel, a workgroup of role waves pipelining
+// a run of consecutive chunks.
 //
 // kla_chunk_kernel: one workgroup per (sequence, head, slice of state
-// columns), the chunks of the sequence in order -- the state scan and the
-// output.  Because T' and P are computed once per chunk and head, the column
-// slices of a head no longer each redo them.
+// columns), the chunks of the sequence in order -- the causal scores, the
+// state scan and the output.  Because T' is computed once per chunk and head,
+// the column slices of a head do not each redo the solve.
 
 struct ChunkParams {
   const void *q, *k, *v, *g, *eta;
