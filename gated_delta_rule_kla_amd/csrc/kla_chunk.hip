@@ -2115,11 +2115,13 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t st, char *state
     if constexpr (std::is_same<E, bf16>::value && C == 64) {
       // bf16: one wave per run of consecutive slots of one head, each run
       // prefetching its next slot while it computes the current one.  Runs of
-      // one slot while the grid is at most about two rounds of the eight
-      // one-wave workgroups a CU holds (more concurrent waves hide more);
-      // longer runs beyond that, where the prefetch overlaps every round.
+      // one slot up to about sixteen rounds of the eight one-wave workgroups a
+      // CU holds (16,384 chunk-heads: 90 us against 98-107 us for runs of 2-16);
+      // longer runs beyond that, where the prefetch overlaps every round (75,008
+      // chunk-heads: 362-371 us for runs of 2-8, 431 us for runs of one).
       const long long total = (long long)p.nslot * a.H;
-      p.pslots = (int)std::min<long long>(8, std::max<long long>(1, total / (2 * 8 * 256)));
+      const long long units = total / (2 * 8 * 256);
+      p.pslots = units <= 8 ? 1 : (int)std::min<long long>(8, units / 2);
       const unsigned runs = (unsigned)((p.nslot + p.pslots - 1) / p.pslots);
       if (p.pg_w)
         hipLaunchKernelGGL((kla_chunk_prep_wave_kernel<DK, false, true>), dim3(runs, (unsigned)a.H), dim3(64), 0, st, p);
