@@ -122,3 +122,33 @@ def test_prep_images_and_decay_vectors_packed():
                 slot = n + t0 // C + c
                 off = (h * nslot + slot) * SLOT_BYTES
                 _check_chunk(ws[off:off + SLOT_BYTES], dump, (n, h, c))
+
+
+def test_prep_images_on_a_grid_with_multi_slot_runs():
+    """A packed grid of 42,000-odd chunk-heads (H=32, 40 sequences of up to 4,000 tokens), large
+    enough that each prep wave takes a run of several consecutive slots, prefetching the next
+    slot's rows while it solves the current one, with runs that cross sequence boundaries.
+    Every chunk of five sampled sequences is checked on three heads."""
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(4244)
+    lengths = [int(v) for v in rng.integers(1, 4000, size=40)]
+    lengths[7] = 0
+    x = inputs.make_prefill(H=32, dk=64, dv=16, chunk=C, lengths=lengths, seed=4245)
+    cu = x.cu_seqlens.numpy()
+    T = int(cu[-1])
+    N = len(lengths)
+    nslot = T // C + N + 1
+    assert nslot * 32 > 40960  # more than ten units of 4,096 chunk-heads: runs of several slots
+    print(f"case multi-slot runs: T={T} nslot={nslot} chunk-heads={nslot * 32}", flush=True)
+    ws, _ = _run(x, dev)
+    f = inputs.to_f64
+    for n in (0, 6, 8, 23, N - 1):
+        t0, t1 = int(cu[n]), int(cu[n + 1])
+        for h in (0, 17, 31):
+            sl = slice(t0, t1)
+            _, _, dumps = kla_chunkwise(f(x.q[0, h, sl]), f(x.k[0, h, sl]), f(x.v[0, h, sl]), f(x.g[0, h, sl]),
+                                        f(x.eta[0, h, sl]), x.eps, None, C, return_chunks=True)
+            for c, dump in enumerate(dumps):
+                slot = n + t0 // C + c
+                off = (h * nslot + slot) * SLOT_BYTES
+                _check_chunk(ws[off:off + SLOT_BYTES], dump, (n, h, c))
